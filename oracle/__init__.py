@@ -1,0 +1,200 @@
+"""fp64 CPU oracle for windowed multi-head self-attention (test infrastructure).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never does, and this
+package never imports the GPU library: the two share no code.
+
+Contents
+  * ``oracle.c`` (compiled with gcc into ``liboracle.so``): the plain per-window
+    definition -- partition / reverse maps, log-spaced offsets, the CPB table and
+    the attention itself, all in fp64.
+  * ``bruteforce.py``: full-grid attention over every token pair with a mask, for
+    tiny grids; it shares neither the partition nor the table indexing with
+    ``oracle.c`` and serves as that file's independent check.
+
+The pages followed are cited in each source file.  Every function here takes
+plain numpy arrays; mode names are strings.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+
+PART = {"cyclic": 0, "interleaved": 1}
+SIM = {"cosine": 0, "dot": 1}
+POS = {"none": 0, "table": 1, "rope2d": 2}
+
+_lib = None
+
+
+def build(force: bool = False, src: str = _SRC, out: str = _SO, defines=()) -> str:
+    """Compile ``oracle.c`` with gcc (OpenMP, IEEE arithmetic, no fast-math)."""
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + f".tmp{os.getpid()}"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+               "-fno-fast-math", "-ffp-contract=off", *[f"-D{d}" for d in defines],
+               src, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def _declare(lib):
+    i32, i64, dbl = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    vp = ctypes.c_void_p
+    lib.oracle_log_offset.restype = dbl
+    lib.oracle_log_offset.argtypes = [dbl]
+    lib.oracle_cpb_table.restype = i32
+    lib.oracle_cpb_table.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+    for fn in (lib.oracle_partition, lib.oracle_reverse):
+        fn.restype = i32
+        fn.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
+    lib.oracle_window_attn.restype = i32
+    lib.oracle_window_attn.argtypes = [i32] * 10 + [dbl, dbl] + [vp] * 7 + [i64, vp, vp]
+    lib.oracle_window_cosines.restype = i32
+    lib.oracle_window_cosines.argtypes = [i32] * 9 + [dbl, vp, vp, vp, i64, i32, vp]
+    lib.oracle_set_threads.restype = None
+    lib.oracle_set_threads.argtypes = [i32]
+    lib.oracle_max_threads.restype = i32
+    lib.oracle_max_threads.argtypes = []
+    return lib
+
+
+def load(path: str | None = None):
+    """Load (building first if needed) the oracle library.  A path other than the
+    default loads a separately built variant and is returned, not cached."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    if _lib is None:
+        build()
+        _lib = _declare(ctypes.CDLL(_SO))
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def set_threads(n: int, lib=None) -> None:
+    (lib or load()).oracle_set_threads(int(n))
+
+
+def max_threads(lib=None) -> int:
+    return int((lib or load()).oracle_max_threads())
+
+
+def log_offset(x: float, lib=None) -> float:
+    """sign(x) * log(1 + |x|)  (SwinV2 eq. 4)."""
+    return float((lib or load()).oracle_log_offset(float(x)))
+
+
+def cpb_table(M: int, w1, b1, w2, b2, lib=None) -> np.ndarray:
+    """(2M-1)^2 x heads bias table of the meta network G (SwinV2 eq. 3-4)."""
+    w1, w2 = _f64(w1), _f64(w2)
+    b1, b2 = _f64(b1), _f64(b2)
+    hidden, heads = w1.shape[0], w2.shape[0]
+    assert w1.shape == (hidden, 2) and w2.shape == (heads, hidden)
+    out = np.empty(((2 * M - 1) ** 2, heads), dtype=np.float64)
+    rc = (lib or load()).oracle_cpb_table(M, heads, hidden, _ptr(w1), _ptr(b1),
+                                          _ptr(w2), _ptr(b2), _ptr(out))
+    if rc:
+        raise ValueError(f"oracle_cpb_table: bad argument (rc={rc})")
+    return out
+
+
+def partition(x: np.ndarray, M: int, shift: int, part: str, lib=None) -> np.ndarray:
+    """Byte-exact window partition of a (B, H, W, C) array of any dtype."""
+    x = np.ascontiguousarray(x)
+    B, H, W, C = x.shape
+    out = np.empty((B * (H // M) * (W // M), M * M, C), dtype=x.dtype)
+    rc = (lib or load()).oracle_partition(_ptr(x), _ptr(out), B, H, W, C, M, shift,
+                                          PART[part], x.dtype.itemsize)
+    if rc:
+        raise ValueError("oracle_partition: bad argument")
+    return out
+
+
+def reverse(xw: np.ndarray, B: int, H: int, W: int, M: int, shift: int, part: str,
+            lib=None) -> np.ndarray:
+    """Byte-exact inverse of :func:`partition`."""
+    xw = np.ascontiguousarray(xw)
+    C = xw.shape[-1]
+    out = np.empty((B, H, W, C), dtype=xw.dtype)
+    rc = (lib or load()).oracle_reverse(_ptr(xw), _ptr(out), B, H, W, C, M, shift,
+                                        PART[part], xw.dtype.itemsize)
+    if rc:
+        raise ValueError("oracle_reverse: bad argument")
+    return out
+
+
+def window_attn(q, k, v, *, heads: int, M: int, shift: int = 0, partition: str = "cyclic",
+                sim: str = "cosine", pos: str = "none", tau=None, table=None,
+                rope_freqs=None, rope_base: float = 10000.0, tau_min: float = 0.01,
+                windows=None, return_weights: bool = False, out=None, lib=None):
+    """Windowed attention forward in fp64.
+
+    q, k, v: (B, H, W, C) arrays (converted exactly to fp64).  tau: (heads,);
+    table: ((2M-1)^2, heads); rope_freqs: (heads, 2, d/4) or None for the
+    base-``rope_base`` schedule.  ``windows``: optional global window ids to
+    compute (the rest of ``out`` stays as given, zeros by default).
+    Returns ``out`` (B, H, W, C) fp64, plus the weights
+    (n_windows, heads, N, N) when ``return_weights``.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, W, C = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    tau, table, rope_freqs = _f64(tau), _f64(table), _f64(rope_freqs)
+    if out is None:
+        out = np.zeros((B, H, W, C), dtype=np.float64)
+    win = None if windows is None else np.ascontiguousarray(windows, dtype=np.int64)
+    nwin = (B * (H // M) * (W // M)) if win is None else len(win)
+    N = M * M
+    wts = np.empty((nwin, heads, N, N), dtype=np.float64) if return_weights else None
+    rc = (lib or load()).oracle_window_attn(
+        B, H, W, C, heads, M, shift, PART[partition], SIM[sim], POS[pos],
+        float(tau_min), float(rope_base), _ptr(q), _ptr(k), _ptr(v), _ptr(tau),
+        _ptr(table), _ptr(rope_freqs), _ptr(win), 0 if win is None else len(win),
+        _ptr(out), _ptr(wts))
+    if rc:
+        raise ValueError(f"oracle_window_attn: bad argument (rc={rc})")
+    return (out, wts) if return_weights else out
+
+
+def window_cosines(q, k, *, heads: int, M: int, shift: int, partition: str, window: int,
+                   head: int, pos: str = "none", rope_freqs=None, rope_base: float = 10000.0,
+                   lib=None) -> np.ndarray:
+    """N x N cosine similarities of one (window, head)."""
+    q, k = _f64(q), _f64(k)
+    B, H, W, C = q.shape
+    N = M * M
+    out = np.empty((N, N), dtype=np.float64)
+    rc = (lib or load()).oracle_window_cosines(
+        B, H, W, C, heads, M, shift, PART[partition], POS[pos], float(rope_base),
+        _ptr(q), _ptr(k), _ptr(_f64(rope_freqs)), int(window), int(head), _ptr(out))
+    if rc:
+        raise ValueError("oracle_window_cosines: bad argument")
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return sys.platform

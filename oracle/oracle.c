@@ -1,0 +1,406 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for windowed multi-head self-attention
+ * (forward), the log-spaced continuous position bias table and the window
+ * partition / reverse maps.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the CPU
+ * baseline leg of the benchmark are the only code that may load this library.
+ * It shares no source, header, table or helper with the GPU library.
+ *
+ * Sources it follows (the pages, by title and section):
+ *   [SwinV2]  "Swin Transformer V2: Scaling Up Capacity and Resolution", paper
+ *             card: Method items 2-3, eq. 1 (softmax(QK^T/sqrt(d) + B) V),
+ *             eq. 2 (cos(q_i,k_j)/tau + B_ij, tau kept at or above 0.01),
+ *             eq. 3 (B = G(dx, dy)), eq. 4 (sign(x) log(1+|x|)), the
+ *             window-attention and continuous-bias pseudocode, the
+ *             Architecture table (G is a 2-layer ReLU MLP, 512 wide in code).
+ *   [Flash]   "FLASHSWIN: Unlocking Large Windows and Dense Tokens ...",
+ *             abstract: exact softmax attention inside each window, and
+ *             window-local 2D rotary position embedding in place of the bias.
+ *   [Iwin]    "Iwin Transformer: Hierarchical Vision Transformer using
+ *             Interleaved Windows", abstract: interleaved window attention.
+ *
+ * Where the pages leave a step open, the reading taken is stated at the step.
+ * Nothing here is blocked, fused or reordered: every window, head, query and
+ * key is visited in the plain order of the definition.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Mode codes of this library (its Python wrapper maps names onto them). */
+enum { OR_PART_CYCLIC = 0, OR_PART_INTERLEAVED = 1 };
+enum { OR_SIM_COSINE = 0, OR_SIM_DOT = 1 };
+enum { OR_POS_NONE = 0, OR_POS_TABLE = 1, OR_POS_ROPE2D = 2 };
+
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* [SwinV2] eq. 4: an offset x is mapped to sign(x) * log(1 + |x|), natural log
+ * (the page's worked example, +-2.079 for offset 7 and +-2.773 for offset 15,
+ * is ln 8 and ln 16). */
+double oracle_log_offset(double x)
+{
+    double a = log1p(fabs(x));
+    if (x > 0) return a;
+    if (x < 0) return -a;
+    return 0.0;
+}
+
+/* [SwinV2] eq. 3 + eq. 4, Method item 3: the bias for relative offset
+ * (dy, dx) = (row offset, column offset) between query and key is the meta
+ * network G applied to the log-spaced offset, G(x) = W2 relu(W1 x + b1) + b2.
+ * Readings: the offset is query position minus key position; G's first input
+ * is the column (x) offset and its second the row (y) offset; W1 is hidden x 2
+ * row-major, W2 is heads x hidden row-major; a NULL bias vector is zero.
+ * The table is stored once per relative position (Method item 3), row
+ * (dy + M-1)*(2M-1) + (dx + M-1), one column per head. */
+int oracle_cpb_table(int M, int heads, int hidden,
+                     const double* w1, const double* b1,
+                     const double* w2, const double* b2, double* table)
+{
+    if (M < 1 || heads < 1 || hidden < 1 || !w1 || !w2 || !table) return 1;
+    const int S = 2 * M - 1;
+    double* h = (double*)malloc((size_t)hidden * sizeof(double));
+    if (!h) return 2;
+    for (int dy = -(M - 1); dy <= M - 1; ++dy) {
+        for (int dx = -(M - 1); dx <= M - 1; ++dx) {
+            const double in0 = oracle_log_offset((double)dx);
+            const double in1 = oracle_log_offset((double)dy);
+            for (int j = 0; j < hidden; ++j) {
+                double a = w1[2 * j] * in0 + w1[2 * j + 1] * in1 + (b1 ? b1[j] : 0.0);
+                h[j] = a > 0.0 ? a : 0.0;                 /* ReLU between the two layers */
+            }
+            double* row = table + ((size_t)(dy + M - 1) * S + (size_t)(dx + M - 1)) * heads;
+            for (int o = 0; o < heads; ++o) {
+                double acc = b2 ? b2[o] : 0.0;
+                for (int j = 0; j < hidden; ++j) acc += w2[(size_t)o * hidden + j] * h[j];
+                row[o] = acc;
+            }
+        }
+    }
+    free(h);
+    return 0;
+}
+
+/* Shape rule shared by every entry point here: windows tile the grid exactly. */
+static int bad_shape(int B, int H, int W, int C, int M, int shift, int part)
+{
+    if (B < 0 || H < 1 || W < 1 || C < 1 || M < 1) return 1;
+    if (H % M || W % M) return 1;
+    if (shift < 0 || shift >= M) return 1;
+    if (part != OR_PART_CYCLIC && part != OR_PART_INTERLEAVED) return 1;
+    if (part == OR_PART_INTERLEAVED && shift != 0) return 1;
+    return 0;
+}
+
+/* Grid position of local token (r, c) of window (wr, wc).
+ * Cyclic ([SwinV2] "window partitioning is Swin V1's"; the shift is not shown
+ * on the page).  Reading: the grid is rolled by -shift on both axes, then cut
+ * into M x M windows in row-major window order, tokens row-major inside.
+ * Interleaved ([Iwin] abstract; the rule itself is not on the page).  Reading:
+ * window (wr, wc) gathers every (H/M)-th row starting at wr and every (W/M)-th
+ * column starting at wc, so local (r, c) is grid (wr + r*H/M, wc + c*W/M). */
+static void grid_pos(int H, int W, int M, int shift, int part,
+                     int wr, int wc, int r, int c, int* gi, int* gj)
+{
+    if (part == OR_PART_INTERLEAVED) {
+        *gi = wr + r * (H / M);
+        *gj = wc + c * (W / M);
+    } else {
+        *gi = (wr * M + r + shift) % H;
+        *gj = (wc * M + c + shift) % W;
+    }
+}
+
+/* Region of a rolled coordinate p along an axis of length L (cyclic shift s > 0):
+ * [0, L-M) -> 0, [L-M, L-s) -> 1, [L-s, L) -> 2.  Tokens rolled in from the far
+ * edge (label 2) and the ones they land next to (label 1) never attend to each
+ * other.  With s == 0 every token is region 0. */
+static int axis_region(int p, int L, int M, int s)
+{
+    if (s == 0) return 0;
+    if (p < L - M) return 0;
+    if (p < L - s) return 1;
+    return 2;
+}
+
+/* Byte-exact gather: xw[b*nW + wr*(W/M) + wc][r*M + c][:] = x[b][gi][gj][:]. */
+int oracle_partition(const void* x, void* xw, int B, int H, int W, int C,
+                     int M, int shift, int part, int elem_size)
+{
+    if (bad_shape(B, H, W, C, M, shift, part) || elem_size < 1) return 1;
+    const int nwr = H / M, nwc = W / M, N = M * M;
+    const size_t row = (size_t)C * elem_size;
+    const char* src = (const char*)x;
+    char* dst = (char*)xw;
+    for (int b = 0; b < B; ++b)
+        for (int wr = 0; wr < nwr; ++wr)
+            for (int wc = 0; wc < nwc; ++wc)
+                for (int r = 0; r < M; ++r)
+                    for (int c = 0; c < M; ++c) {
+                        int gi, gj;
+                        grid_pos(H, W, M, shift, part, wr, wc, r, c, &gi, &gj);
+                        size_t w = ((size_t)b * nwr + wr) * nwc + wc;
+                        memcpy(dst + (w * N + (size_t)r * M + c) * row,
+                               src + (((size_t)b * H + gi) * W + gj) * row, row);
+                    }
+    return 0;
+}
+
+/* Byte-exact scatter, the inverse of oracle_partition. */
+int oracle_reverse(const void* xw, void* x, int B, int H, int W, int C,
+                   int M, int shift, int part, int elem_size)
+{
+    if (bad_shape(B, H, W, C, M, shift, part) || elem_size < 1) return 1;
+    const int nwr = H / M, nwc = W / M, N = M * M;
+    const size_t row = (size_t)C * elem_size;
+    const char* src = (const char*)xw;
+    char* dst = (char*)x;
+    for (int b = 0; b < B; ++b)
+        for (int wr = 0; wr < nwr; ++wr)
+            for (int wc = 0; wc < nwc; ++wc)
+                for (int r = 0; r < M; ++r)
+                    for (int c = 0; c < M; ++c) {
+                        int gi, gj;
+                        grid_pos(H, W, M, shift, part, wr, wc, r, c, &gi, &gj);
+                        size_t w = ((size_t)b * nwr + wr) * nwc + wc;
+                        memcpy(dst + (((size_t)b * H + gi) * W + gj) * row,
+                               src + (w * N + (size_t)r * M + c) * row, row);
+                    }
+    return 0;
+}
+
+/* [Flash] abstract: window-local 2D rotary embedding (no formula on the page).
+ * Reading: channels [0, d/2) turn with the local row, [d/2, d) with the local
+ * column; inside each half, pair (2k, 2k+1), k < d/4, turns by pos * theta_k,
+ * theta_k = base^(-k/(d/4)), or the caller's per-head frequency when given
+ * (freqs = 2 x d/4: row half then column half). */
+static void rope_rotate(double* x, int d, int r, int c,
+                        const double* freqs, double base)
+{
+    const int q4 = d / 4;
+    for (int half = 0; half < 2; ++half) {
+        const int pos = half == 0 ? r : c;
+        for (int k = 0; k < q4; ++k) {
+            double theta = freqs ? freqs[half * q4 + k] : pow(base, -(double)k / (double)q4);
+            double a = (double)pos * theta;
+            double cs = cos(a), sn = sin(a);
+            double* p = x + half * (d / 2) + 2 * k;
+            double x0 = p[0], x1 = p[1];
+            p[0] = x0 * cs - x1 * sn;
+            p[1] = x0 * sn + x1 * cs;
+        }
+    }
+}
+
+/* [SwinV2] eq. 2 normalize(): x / max(||x||_2, 1e-12) (the page gives no epsilon). */
+static void unit_normalize(double* x, int d)
+{
+    double ss = 0.0;
+    for (int e = 0; e < d; ++e) ss += x[e] * x[e];
+    double n = sqrt(ss);
+    if (n < 1e-12) n = 1e-12;
+    for (int e = 0; e < d; ++e) x[e] /= n;
+}
+
+/*
+ * Windowed multi-head self-attention forward over (B, H, W, C) grids,
+ * channels last, head h owning channels [h*d, (h+1)*d), d = C / heads.
+ *
+ * Per (batch, window, head), in the pages' order:
+ *   1. gather the window's M*M tokens (grid_pos), local order t = r*M + c;
+ *   2. ROPE2D: rotate q and k by their local (r, c)          [Flash];
+ *   3. COSINE: q^ = q/max(||q||,eps), k^ likewise, logit = q^.k^ / max(tau_h, tau_min)
+ *                                                             [SwinV2] eq. 2;
+ *      DOT:    logit = q.k / sqrt(d)                          [SwinV2] eq. 1;
+ *   4. TABLE:  logit += table[(ri-rj+M-1)*(2M-1) + (ci-cj+M-1)][h]  [SwinV2] eq. 2-3;
+ *   5. cyclic shift: a key in another region than the query is excluded
+ *      outright (weight exactly 0; a finite penalty would not block it,
+ *      since |cos|/0.01 reaches 100 and the bias is unbounded);
+ *   6. softmax over the remaining keys: subtract the row max, exponentiate,
+ *      divide by the sum                                      [SwinV2] pseudocode;
+ *   7. o_i = sum_j p_ij v_j, written back to query i's grid position.
+ *
+ * windows: optional list of global window ids (b*nW + wr*(W/M) + wc) to
+ * compute; NULL means all.  Only those windows' tokens of `out` are written.
+ * weights: optional n_windows x heads x N x N array of the softmax weights.
+ * Returns 0, or 1 on a bad argument.
+ */
+int oracle_window_attn(int B, int H, int W, int C, int heads, int M, int shift,
+                       int part, int sim, int pos, double tau_min, double rope_base,
+                       const double* q, const double* k, const double* v,
+                       const double* tau, const double* table, const double* rope_freqs,
+                       const int64_t* windows, int64_t n_windows,
+                       double* out, double* weights)
+{
+    if (bad_shape(B, H, W, C, M, shift, part)) return 1;
+    if (heads < 1 || C % heads) return 1;
+    const int d = C / heads;
+    if (sim != OR_SIM_COSINE && sim != OR_SIM_DOT) return 1;
+    if (pos != OR_POS_NONE && pos != OR_POS_TABLE && pos != OR_POS_ROPE2D) return 1;
+    if (sim == OR_SIM_COSINE && !tau) return 1;
+    if (pos == OR_POS_TABLE && !table) return 1;
+    if (pos == OR_POS_ROPE2D && d % 4) return 1;
+    if (!q || !k || !v || !out) return 1;
+
+    const int nwr = H / M, nwc = W / M, N = M * M;
+    const int64_t nW = (int64_t)nwr * nwc;
+    const int64_t total = windows ? n_windows : (int64_t)B * nW;
+    if (windows) {
+        for (int64_t i = 0; i < n_windows; ++i)
+            if (windows[i] < 0 || windows[i] >= (int64_t)B * nW) return 1;
+    }
+    const int S = 2 * M - 1;
+    const double dot_scale = 1.0 / sqrt((double)d);
+    int failed = 0;
+
+    #pragma omp parallel
+    {
+        double* qs = (double*)malloc((size_t)N * d * sizeof(double));
+        double* ks = (double*)malloc((size_t)N * d * sizeof(double));
+        double* vs = (double*)malloc((size_t)N * d * sizeof(double));
+        double* lg = (double*)malloc((size_t)N * sizeof(double));
+        char* allowed = (char*)malloc((size_t)N);
+        int* gi = (int*)malloc((size_t)N * sizeof(int));
+        int* gj = (int*)malloc((size_t)N * sizeof(int));
+        int* region = (int*)malloc((size_t)N * sizeof(int));
+        if (!qs || !ks || !vs || !lg || !allowed || !gi || !gj || !region) {
+            #pragma omp atomic write
+            failed = 1;
+        } else {
+            #pragma omp for schedule(dynamic, 1)
+            for (int64_t u = 0; u < total * heads; ++u) {
+                const int64_t wi = u / heads;
+                const int h = (int)(u % heads);
+                const int64_t gw = windows ? windows[wi] : wi;
+                const int b = (int)(gw / nW);
+                const int wr = (int)((gw % nW) / nwc);
+                const int wc = (int)(gw % nwc);
+
+                /* 1. gather, with region labels in rolled coordinates */
+                for (int t = 0; t < N; ++t) {
+                    const int r = t / M, c = t % M;
+                    grid_pos(H, W, M, shift, part, wr, wc, r, c, &gi[t], &gj[t]);
+                    region[t] = (part == OR_PART_CYCLIC)
+                        ? 3 * axis_region(wr * M + r, H, M, shift) + axis_region(wc * M + c, W, M, shift)
+                        : 0;
+                    const size_t base = (((size_t)b * H + gi[t]) * W + gj[t]) * C + (size_t)h * d;
+                    for (int e = 0; e < d; ++e) {
+                        qs[(size_t)t * d + e] = q[base + e];
+                        ks[(size_t)t * d + e] = k[base + e];
+                        vs[(size_t)t * d + e] = v[base + e];
+                    }
+                    /* 2. rotary position, window-local */
+                    if (pos == OR_POS_ROPE2D) {
+                        const double* f = rope_freqs ? rope_freqs + (size_t)h * 2 * (d / 4) : NULL;
+                        rope_rotate(qs + (size_t)t * d, d, r, c, f, rope_base);
+                        rope_rotate(ks + (size_t)t * d, d, r, c, f, rope_base);
+                    }
+                    /* 3a. unit-normalise for the cosine */
+                    if (sim == OR_SIM_COSINE) {
+                        unit_normalize(qs + (size_t)t * d, d);
+                        unit_normalize(ks + (size_t)t * d, d);
+                    }
+                }
+                double inv_tau = 0.0;
+                if (sim == OR_SIM_COSINE) {
+                    double t_h = tau[h] > tau_min ? tau[h] : tau_min;   /* max(tau, 0.01) */
+                    inv_tau = 1.0 / t_h;
+                }
+
+                for (int i = 0; i < N; ++i) {
+                    const int ri = i / M, ci = i % M;
+                    double mx = -INFINITY;
+                    for (int j = 0; j < N; ++j) {
+                        const int rj = j / M, cj = j % M;
+                        double s = 0.0;
+                        for (int e = 0; e < d; ++e) s += qs[(size_t)i * d + e] * ks[(size_t)j * d + e];
+                        double l = (sim == OR_SIM_COSINE) ? s * inv_tau : s * dot_scale;
+                        if (pos == OR_POS_TABLE)
+                            l += table[((size_t)(ri - rj + M - 1) * S + (size_t)(ci - cj + M - 1)) * heads + h];
+                        lg[j] = l;
+                        allowed[j] = (char)(region[j] == region[i]);
+                        if (allowed[j] && l > mx) mx = l;
+                    }
+                    double sum = 0.0;
+                    for (int j = 0; j < N; ++j) {
+                        lg[j] = allowed[j] ? exp(lg[j] - mx) : 0.0;
+                        sum += lg[j];
+                    }
+                    for (int j = 0; j < N; ++j) lg[j] /= sum;
+                    if (weights) {
+                        double* wrow = weights + (((size_t)wi * heads + h) * N + i) * (size_t)N;
+                        for (int j = 0; j < N; ++j) wrow[j] = lg[j];
+                    }
+                    const size_t ob = (((size_t)b * H + gi[i]) * W + gj[i]) * C + (size_t)h * d;
+                    for (int e = 0; e < d; ++e) {
+                        double acc = 0.0;
+                        for (int j = 0; j < N; ++j) acc += lg[j] * vs[(size_t)j * d + e];
+                        out[ob + e] = acc;
+                    }
+                }
+            }
+        }
+        free(qs); free(ks); free(vs); free(lg); free(allowed); free(gi); free(gj); free(region);
+    }
+    return failed ? 2 : 0;
+}
+
+/* Cosine similarities q^_i . k^_j of one (window, head), N x N, for range checks
+ * ([SwinV2] eq. 2: cos lies in [-1, 1]). Same gather and rotation as above. */
+int oracle_window_cosines(int B, int H, int W, int C, int heads, int M, int shift,
+                          int part, int pos, double rope_base,
+                          const double* q, const double* k, const double* rope_freqs,
+                          int64_t window, int head, double* cosines)
+{
+    if (bad_shape(B, H, W, C, M, shift, part) || heads < 1 || C % heads) return 1;
+    const int d = C / heads, nwr = H / M, nwc = W / M, N = M * M;
+    const int64_t nW = (int64_t)nwr * nwc;
+    if (window < 0 || window >= (int64_t)B * nW || head < 0 || head >= heads) return 1;
+    if (pos == OR_POS_ROPE2D && d % 4) return 1;
+    const int b = (int)(window / nW), wr = (int)((window % nW) / nwc), wc = (int)(window % nwc);
+    double* qs = (double*)malloc((size_t)N * d * sizeof(double));
+    double* ks = (double*)malloc((size_t)N * d * sizeof(double));
+    if (!qs || !ks) { free(qs); free(ks); return 2; }
+    for (int t = 0; t < N; ++t) {
+        int r = t / M, c = t % M, i0, j0;
+        grid_pos(H, W, M, shift, part, wr, wc, r, c, &i0, &j0);
+        const size_t base = (((size_t)b * H + i0) * W + j0) * C + (size_t)head * d;
+        for (int e = 0; e < d; ++e) { qs[(size_t)t * d + e] = q[base + e]; ks[(size_t)t * d + e] = k[base + e]; }
+        if (pos == OR_POS_ROPE2D) {
+            const double* f = rope_freqs ? rope_freqs + (size_t)head * 2 * (d / 4) : NULL;
+            rope_rotate(qs + (size_t)t * d, d, r, c, f, rope_base);
+            rope_rotate(ks + (size_t)t * d, d, r, c, f, rope_base);
+        }
+        unit_normalize(qs + (size_t)t * d, d);
+        unit_normalize(ks + (size_t)t * d, d);
+    }
+    for (int i = 0; i < N; ++i)
+        for (int j = 0; j < N; ++j) {
+            double s = 0.0;
+            for (int e = 0; e < d; ++e) s += qs[(size_t)i * d + e] * ks[(size_t)j * d + e];
+            cosines[(size_t)i * N + j] = s;
+        }
+    free(qs); free(ks);
+    return 0;
+}

@@ -1,0 +1,77 @@
+"""Planted mistakes: each entry below copies oracle.c with one plausible error
+(a dropped term, a wrong sign or index, a transposed operand ...), builds the
+copy with gcc on the CPU, and runs every pin of test_oracle_pins.py against it.
+Each planted mistake must fail at least one pin; the unmodified source must
+pass them all (test_oracle_pins.py).  Nothing here touches the GPU.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+from tests.test_oracle_pins import PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, original text, planted text)
+MUTATIONS = [
+    ("log_sign", "if (x > 0) return a;", "if (x > 0) return -a;"),
+    ("log_base2", "log1p(fabs(x))", "log2(1.0 + fabs(x))"),
+    ("relu_dropped", "h[j] = a > 0.0 ? a : 0.0;", "h[j] = a;"),
+    ("g_inputs_swapped", "w1[2 * j] * in0 + w1[2 * j + 1] * in1", "w1[2 * j] * in1 + w1[2 * j + 1] * in0"),
+    ("b1_dropped", "+ (b1 ? b1[j] : 0.0)", "+ 0.0"),
+    ("bias_offset_sign", "(ri - rj + M - 1) * S + (size_t)(ci - cj + M - 1)",
+     "(rj - ri + M - 1) * S + (size_t)(cj - ci + M - 1)"),
+    ("bias_rows_cols_swapped", "(ri - rj + M - 1) * S + (size_t)(ci - cj + M - 1)",
+     "(ci - cj + M - 1) * S + (size_t)(ri - rj + M - 1)"),
+    ("bias_dropped", "l += table[", "l += 0.0 * table["),
+    ("tau_floor_dropped", "tau[h] > tau_min ? tau[h] : tau_min", "tau[h]"),
+    ("shift_direction", "*gi = (wr * M + r + shift) % H;", "*gi = (wr * M + r - shift + H) % H;"),
+    ("mask_dropped", "allowed[j] = (char)(region[j] == region[i]);", "allowed[j] = 1;"),
+    ("region_off_by_one", "if (p < L - s) return 1;", "if (p <= L - s) return 1;"),
+    ("region_first_cut", "if (p < L - M) return 0;", "if (p < L - M - 1) return 0;"),
+    ("norm_wrong", "x[e] /= n;", "x[e] /= (n + 1.0);"),
+    ("dot_scale", "1.0 / sqrt((double)d)", "1.0 / (double)d"),
+    ("rope_sign", "p[1] = x0 * sn + x1 * cs;", "p[1] = x0 * sn - x1 * cs;"),
+    ("rope_halves_swapped", "const int pos = half == 0 ? r : c;", "const int pos = half == 0 ? c : r;"),
+    ("rope_theta", "pow(base, -(double)k / (double)q4)", "pow(base, -(double)k / (double)(2 * q4))"),
+    ("qk_transposed", "s += qs[(size_t)i * d + e] * ks[(size_t)j * d + e];",
+     "s += qs[(size_t)j * d + e] * ks[(size_t)i * d + e];"),
+    ("v_index", "acc += lg[j] * vs[(size_t)j * d + e];", "acc += lg[j] * vs[(size_t)i * d + e];"),
+    ("interleaved_map", "*gi = wr + r * (H / M);", "*gi = wr * M + r;"),
+    ("softmax_unnormalised", "for (int j = 0; j < N; ++j) lg[j] /= sum;", ";"),
+]
+
+
+@pytest.fixture(scope="module")
+def workdir(tmp_path_factory):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    return tmp_path_factory.mktemp("oracle_mutants")
+
+
+def test_mutations_are_well_formed():
+    src = open(SRC).read()
+    for name, old, new in MUTATIONS:
+        assert src.count(old) >= 1, f"{name}: text not found in oracle.c"
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(workdir, name, old, new):
+    src = open(SRC).read()
+    mutant = src.replace(old, new, 1)
+    path = os.path.join(workdir, f"{name}.c")
+    with open(path, "w") as f:
+        f.write(mutant)
+    so = os.path.join(workdir, f"lib{name}.so")
+    oracle.build(force=True, src=path, out=so)
+    lib = oracle.load(so)
+    caught = []
+    for pin_name, pin in PINS.items():
+        try:
+            pin(lib)
+        except (AssertionError, ValueError):
+            caught.append(pin_name)
+    assert caught, f"planted mistake {name} passed every pin"

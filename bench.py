@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Throughput of the windowed-attention forward hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+the log-CPB table for the window size (swin_cpb_table) and the fused window
+attention over the grid, partition, shift mask and reverse map included
+(swin_window_attn_fwd).  Inputs are resident in HBM before timing starts.
+
+Timing: W untimed warm-up steps, then exactly K timed steps between two
+torch.cuda.synchronize() calls.  Cold cache by default: the steps rotate
+through enough distinct input/output sets (> 512 MB in all) that the 256 MB
+Infinity Cache cannot hold one set between its uses; --warm reuses one set.
+The attention kernel's own duration is taken from HIP events recorded on the
+launch stream around every timed launch.
+
+Prints ONE JSON line.  `value` is tokens/s over the whole job.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "window-attn fwd tokens/s + TFLOP/s (% bf16 MFMA peak), SwinV2-T M=16 256px"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, TFLOP/s
+MALL_BYTES = 256 * 2 ** 20
+KERNEL_SOURCES = ["attn_mfma.hip", "attn_valu.hip", "common.hpp"]
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "vision_transformer_windowed_partition_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(wl_name: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc counts, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{wl_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_sha") != kernel_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, x, budget_s: float):
+    """The fp64 oracle on a bounded sample of the same workload, on the host's
+    cores, in tokens/s."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    f64 = lambda t: t.to(torch.float64).numpy()
+    q, k, v = f64(x["q"]), f64(x["k"]), f64(x["v"])
+    nwin = wl.n_windows
+    t0 = time.perf_counter()
+    table = None
+    if wl.pos == "table":
+        table = oracle.cpb_table(wl.M, f64(x["w1"]), f64(x["b1"]), f64(x["w2"]), f64(x["b2"]))
+    t_table = time.perf_counter() - t0
+    kw = dict(heads=wl.heads, M=wl.M, shift=wl.shift, partition=wl.partition, sim=wl.sim, pos=wl.pos,
+              tau=f64(x["tau"]), table=table, rope_base=wl.rope_base)
+    # probe on a few windows, then size the sample to the budget
+    probe = np.linspace(0, nwin - 1, num=min(nwin, 8), dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.window_attn(q, k, v, windows=probe, **kw)
+    per_win = (time.perf_counter() - t0) / len(probe)
+    n = int(min(nwin, max(len(probe), budget_s / max(per_win, 1e-9))))
+    wins = np.unique(np.linspace(0, nwin - 1, num=n, dtype=np.int64))
+    t0 = time.perf_counter()
+    oracle.window_attn(q, k, v, windows=wins, **kw)
+    dt = time.perf_counter() - t0 + t_table
+    tokens = len(wins) * wl.N
+    sample = (f"all {nwin} windows" if len(wins) == nwin else
+              f"{len(wins)} of {nwin} windows, evenly spaced over the batch") + \
+             f" ({tokens} tokens, {dt:.1f} s incl. the CPB table)"
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": sample, "cpu": oracle.cpu_model()}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=1, help="index into synth.WORKLOADS (1 = headline)")
+    ap.add_argument("--warm", action="store_true", help="reuse one input set (cache-warm)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=8.0, help="seconds of oracle wall time")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(windows, heads and batch shard with no exchange; see the design notes)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from vision_transformer_windowed_partition_amd import binding, synth
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    x = synth.make_inputs(wl)
+
+    set_bytes = 4 * wl.tokens * wl.C * wl.elem_size
+    nsets = 1 if args.warm else max(2, math.ceil(2 * MALL_BYTES / set_bytes) + 1)
+    sets = []
+    for i in range(nsets):
+        if i == 0:
+            q, k, v = (x[n].to(dev) for n in "qkv")
+        else:   # distinct buffers with the same contents (a permuted batch would change nothing timed)
+            q, k, v = (sets[0][j].clone() for j in range(3))
+        sets.append((q, k, v, torch.empty_like(q)))
+    par = {n: x[n].to(dev) for n in ("tau", "w1", "b1", "w2", "b2")}
+    table = torch.empty(((2 * wl.M - 1) ** 2, wl.heads), dtype=torch.float32, device=dev)
+    desc = binding.make_desc(B=wl.B, H=wl.H, W=wl.W, C=wl.C, heads=wl.heads, M=wl.M, shift=wl.shift,
+                             partition=wl.partition, sim=wl.sim, pos=wl.pos, dtype=q.dtype,
+                             rope_base=wl.rope_base)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        q, k, v, o = sets[i % nsets]
+        tab = None
+        if wl.pos == "table":
+            tab = binding.swin_cpb_table(wl.M, par["w1"], par["b1"], par["w2"], par["b2"], out=table,
+                                         stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        binding.swin_window_attn_fwd(q, k, v, heads=wl.heads, M=wl.M, desc=desc, tau=par["tau"],
+                                     table=tab, out=o, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_avg = sum(kern_ms) / len(kern_ms)
+
+    if args.calib_copy:
+        a = torch.empty(2 ** 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_s = wl.tokens / (wall / args.steps)
+    alg_bytes = wl.bytes
+    kern_s = kern_avg * 1e-3
+    gbs = alg_bytes / kern_s / 1e9
+    tflops = wl.flops / kern_s / 1e12
+    peak_tf = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+    ai = wl.flops / alg_bytes
+    ridge = peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai < ridge:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(tflops / peak_tf, 4)}
+    roof["traffic"] = load_traffic(wl.name)
+    roof["kernel"] = "attn_mfma_kernel" if wl.dtype == "bf16" else "attn_valu_kernel"
+    roof["kernel_ms"] = round(kern_avg, 5)
+    roof["alg_bytes_per_launch"] = alg_bytes
+    roof["alg_flops_per_launch"] = wl.flops
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v, random-init log-CPB MLP)",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "W": wl.W, "C": wl.C, "heads": wl.heads,
+                   "M": wl.M, "shift": wl.shift, "partition": wl.partition, "sim": wl.sim,
+                   "pos": wl.pos, "cache": "warm" if args.warm else f"cold ({nsets} rotating sets)",
+                   "parallelism": "none (1 GPU)"},
+        "tflops": round(tflops, 2),
+        "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4) if wl.dtype == "bf16" else None,
+        "hbm_gbs": round(gbs, 1),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_budget)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

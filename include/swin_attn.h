@@ -1,0 +1,154 @@
+/*
+ * swin_attn.h -- C ABI of libswinattn.so: shifted-window / interleaved-window
+ * multi-head self-attention forward on one AMD Instinct MI355X (gfx950).
+ *
+ * Pages defining the operations (cited by title and section):
+ *   [SwinV2] "Swin Transformer V2: Scaling Up Capacity and Resolution",
+ *            paper card: Method items 2-3, eq. 1-4, the window-attention and
+ *            continuous-bias pseudocode, Architecture table.
+ *   [Flash]  "FLASHSWIN: Unlocking Large Windows and Dense Tokens in Swin
+ *            Vision Transformers with Memory Efficient Attention", abstract.
+ *   [Iwin]   "Iwin Transformer: Hierarchical Vision Transformer using
+ *            Interleaved Windows", abstract.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers, allocated and owned by the caller;
+ *     the library allocates no device memory and keeps no state between calls
+ *     beyond its loaded code.  `desc` is a HOST pointer, read during the call.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; results are ready when the stream is.
+ *   - Token grids are (B, H, W, C) row-major, channels last; head h owns
+ *     channels [h*d, (h+1)*d), d = C / heads.
+ *   - Window order: window (b, wr, wc) has id b*nW + wr*(W/M) + wc,
+ *     nW = (H/M)*(W/M); inside a window, token (r, c) is number r*M + c.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued.  A bad argument returns SWIN_EINVAL, a case the pages define
+ *     but this library does not build returns SWIN_EUNSUPPORTED; in both cases
+ *     nothing is written.  A failed kernel launch returns SWIN_EHIP.
+ *     swin_status_string() names a status; swin_last_error() gives the detail
+ *     of the calling thread's last failure.
+ *   - All entry points are thread-safe; no exception crosses the ABI.
+ */
+#ifndef SWIN_ATTN_H
+#define SWIN_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SWIN_ATTN_VERSION 1
+
+enum swin_status { SWIN_OK = 0, SWIN_EINVAL = 1, SWIN_EUNSUPPORTED = 2, SWIN_EHIP = 3 };
+
+/* Window partitions.
+ * CYCLIC ([SwinV2] Method: Swin V1's partition; its shift is not shown on the
+ *   page): the grid is rolled by -shift on both axes and cut into M x M
+ *   windows, so window (wr, wc) local (r, c) is grid
+ *   ((wr*M + r + shift) mod H, (wc*M + c + shift) mod W).  With shift > 0,
+ *   tokens that the roll brought from the far edge do not attend to the ones
+ *   they now sit beside: along each axis the rolled coordinate p = w*M + r
+ *   falls in region [0, L-M), [L-M, L-shift) or [L-shift, L), and a query
+ *   attends only to keys of its own region pair.  Masked weights are exactly 0.
+ * INTERLEAVED ([Iwin] abstract): window (wr, wc) holds every (H/M)-th row from
+ *   wr and every (W/M)-th column from wc: local (r, c) is grid
+ *   (wr + r*H/M, wc + c*W/M).  Requires shift == 0. */
+enum swin_partition { SWIN_PART_CYCLIC = 0, SWIN_PART_INTERLEAVED = 1 };
+
+/* Similarity.  COSINE ([SwinV2] eq. 2): cos(q_i, k_j) / max(tau_h, tau_min),
+ * each vector divided by max(||x||, 1e-12).  DOT ([SwinV2] eq. 1):
+ * q_i . k_j / sqrt(d). */
+enum swin_sim { SWIN_SIM_COSINE = 0, SWIN_SIM_DOT = 1 };
+
+/* Position information.
+ * TABLE ([SwinV2] eq. 2-3): logit += table[(ri-rj+M-1)*(2M-1) + (ci-cj+M-1)][h],
+ *   offsets taken query minus key in window-local coordinates.
+ * ROPE2D ([Flash] abstract: window-local 2D rotary embedding): before the
+ *   similarity, q and k channels [0, d/2) turn by the local row r and
+ *   [d/2, d) by the local column c; within each half, pair (2k, 2k+1),
+ *   k < d/4, turns by pos * theta_k, theta_k = rope_base^(-k/(d/4)) or the
+ *   caller's rope_freqs[h][half][k]. */
+enum swin_pos { SWIN_POS_NONE = 0, SWIN_POS_TABLE = 1, SWIN_POS_ROPE2D = 2 };
+
+enum swin_dtype { SWIN_DT_F32 = 0, SWIN_DT_BF16 = 1 };
+
+/* GRID: q, k, v, out are (B, H, W, C) and the partition is applied inside the
+ * kernel (the hot path).  WINDOWS: they are (B*nW, M*M, C), already
+ * partitioned (e.g. by swin_window_partition); the shift mask still follows
+ * each window's place in the grid. */
+enum swin_layout { SWIN_LAYOUT_GRID = 0, SWIN_LAYOUT_WINDOWS = 1 };
+
+/* Log-CPB variants.  PAPER ([SwinV2] eq. 4): inputs sign(x) ln(1+|x|) of the
+ * raw offsets, output unbounded.  (The released code's normalised log2 form
+ * and 16*sigmoid output are not built.) */
+enum swin_cpb_mode { SWIN_CPB_PAPER = 0 };
+
+typedef struct swin_attn_desc {
+    int32_t B, H, W, C, heads;  /* C % heads == 0; d = C/heads must be 32        */
+    int32_t M, shift;           /* H % M == W % M == 0; 0 <= shift < M;
+                                   shift == 0 for INTERLEAVED                     */
+    int32_t partition;          /* enum swin_partition                           */
+    int32_t sim;                /* enum swin_sim                                 */
+    int32_t pos;                /* enum swin_pos                                 */
+    int32_t dtype;              /* enum swin_dtype: q, k, v and out share it     */
+    int32_t layout;             /* enum swin_layout                              */
+    float   tau_min;            /* floor of tau, 0.01 on the pages ([SwinV2]
+                                   Method item 2); must be > 0                   */
+    float   rope_base;          /* 10000 unless rope_freqs is given; > 0        */
+} swin_attn_desc;
+
+/* Log-spaced continuous position bias table ([SwinV2] eq. 3-4, Method item 3:
+ * computed once per relative position and stored).
+ *   table[(dy+M-1)*(2M-1) + (dx+M-1)][h] = (W2 relu(W1 (f(dx), f(dy)) + b1) + b2)[h],
+ *   f(x) = sign(x) ln(1+|x|), dy, dx in [-(M-1), M-1] (query minus key; dx is
+ *   the column offset and G's first input).
+ * w1: hidden x 2, b1: hidden (or NULL = 0), w2: heads x hidden, b2: heads (or
+ * NULL = 0), all fp32 row-major on the device.  table: (2M-1)^2 x heads fp32.
+ * 1 <= M <= 64, 1 <= heads <= 64, 1 <= hidden <= 4096, cpb_mode == PAPER. */
+int swin_cpb_table(int32_t M, int32_t heads, int32_t hidden,
+                   const float* w1, const float* b1, const float* w2, const float* b2,
+                   int32_t cpb_mode, float* table, void* stream);
+
+/* Window partition (gather) of a (B, H, W, C) grid into (B*nW, M*M, C), and
+ * its inverse (scatter).  A bit-exact copy of C elements per token; dtype
+ * gives the element size.  x and xw must not overlap. */
+int swin_window_partition(const void* x, void* xw, int32_t B, int32_t H, int32_t W,
+                          int32_t C, int32_t M, int32_t shift, int32_t partition,
+                          int32_t dtype, void* stream);
+int swin_window_reverse(const void* xw, void* x, int32_t B, int32_t H, int32_t W,
+                        int32_t C, int32_t M, int32_t shift, int32_t partition,
+                        int32_t dtype, void* stream);
+
+/* Windowed multi-head self-attention forward ([SwinV2] eq. 1-2 and the
+ * window-attention pseudocode; [Flash] exact softmax attention inside the
+ * window, never materialising the N x N scores, N = M*M):
+ *   out_i = sum_j softmax_j(logit_ij) v_j over the keys j of query i's window
+ *   (and shift region), logit as set by desc->sim and desc->pos.
+ * q, k, v, out: device tensors of desc->dtype in desc->layout.  out must not
+ * overlap q, k or v.  All must be 16-byte aligned.
+ * tau: heads fp32 (required for COSINE, else ignored).
+ * table: (2M-1)^2 x heads fp32 (required for POS_TABLE, else ignored).
+ * rope_freqs: heads x 2 x (d/4) fp32, or NULL for the rope_base schedule
+ * (POS_ROPE2D only).
+ * Arithmetic: fp32 throughout for SWIN_DT_F32; for SWIN_DT_BF16 the two
+ * contractions run on bf16 matrix cores with fp32 accumulation and the
+ * softmax in fp32, output rounded to nearest even. */
+int swin_window_attn_fwd(const swin_attn_desc* desc, const void* q, const void* k,
+                         const void* v, void* out, const float* tau, const float* table,
+                         const float* rope_freqs, void* stream);
+
+/* Text for a status code (static storage). */
+const char* swin_status_string(int status);
+
+/* Detail of the calling thread's last non-OK return ("" if none). */
+const char* swin_last_error(void);
+
+/* SWIN_ATTN_VERSION of the built library. */
+int swin_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWIN_ATTN_H */

@@ -1,0 +1,138 @@
+"""Host-side checks of libswinattn.so (no GPU needed, nothing is launched):
+the library loads, exports every function include/swin_attn.h declares, and
+rejects bad arguments with the documented status before any launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from vision_transformer_windowed_partition_amd import binding
+from vision_transformer_windowed_partition_amd.binding import (SWIN_EINVAL, SWIN_EUNSUPPORTED,
+                                                               SWIN_OK, SwinAttnDesc)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swin_attn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|char\s*\*|const char\s*\*)\s*\**\s*(swin_\w+)\s*\(",
+                                 src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libswinattn.so not built")
+    return binding.lib()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(["swin_cpb_table", "swin_window_partition", "swin_window_reverse",
+                                           "swin_window_attn_fwd", "swin_status_string",
+                                           "swin_last_error", "swin_version"])
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True)
+    if out.returncode == 0:
+        for name in declared_functions():
+            assert re.search(rf"\bT {name}$", out.stdout, flags=re.M), name
+
+
+def test_version_and_status_strings(L):
+    assert binding.swin_version() == 1
+    for s in (0, 1, 2, 3):
+        assert binding.swin_status_string(s).startswith("SWIN_")
+    assert "unknown" in binding.swin_status_string(99)
+
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
+
+
+def _desc(**kw):
+    d = dict(B=1, H=16, W=16, C=64, heads=2, M=8, shift=4, partition=0, sim=0, pos=1, dtype=1,
+             layout=0, tau_min=0.01, rope_base=10000.0)
+    d.update(kw)
+    return SwinAttnDesc(*[d[f] for f, _ in SwinAttnDesc._fields_])
+
+
+def _attn(L, desc, q=FAKE, k=FAKE, v=FAKE, out=ctypes.c_void_p(0x20000000), tau=FAKE, table=FAKE):
+    return L.swin_window_attn_fwd(ctypes.byref(desc) if desc is not None else None,
+                                  q, k, v, out, tau, table, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=12), SWIN_EUNSUPPORTED),          # H % M != 0 (no padding built)
+    (dict(M=32), SWIN_EUNSUPPORTED),          # window larger than the grid
+    (dict(C=96, heads=2), SWIN_EUNSUPPORTED), # head dim 48
+    (dict(C=64, heads=3), SWIN_EINVAL),       # C % heads
+    (dict(shift=8), SWIN_EINVAL),             # shift >= M
+    (dict(shift=-1), SWIN_EINVAL),
+    (dict(partition=1, shift=4), SWIN_EINVAL),  # interleaved windows take no shift
+    (dict(partition=2), SWIN_EINVAL),
+    (dict(sim=5), SWIN_EINVAL),
+    (dict(pos=7), SWIN_EINVAL),
+    (dict(dtype=3), SWIN_EINVAL),
+    (dict(layout=2), SWIN_EINVAL),
+    (dict(tau_min=0.0), SWIN_EINVAL),
+    (dict(B=-1), SWIN_EINVAL),
+    (dict(H=0), SWIN_EINVAL),
+])
+def test_attn_rejects_bad_descriptors(L, kw, status):
+    assert _attn(L, _desc(**kw)) == status
+    assert binding.swin_last_error() != ""
+
+
+def test_attn_rejects_bad_pointers(L):
+    d = _desc()
+    assert _attn(L, None) == SWIN_EINVAL
+    assert _attn(L, d, q=None) == SWIN_EINVAL
+    assert _attn(L, d, out=None) == SWIN_EINVAL
+    assert _attn(L, d, tau=None) == SWIN_EINVAL                     # COSINE needs tau
+    assert _attn(L, d, table=None) == SWIN_EINVAL                   # TABLE needs the table
+    assert _attn(L, d, q=ctypes.c_void_p(0x10008)) == SWIN_EINVAL   # misaligned
+    assert _attn(L, d, out=ctypes.c_void_p(0x10000 + 64)) == SWIN_EINVAL   # out overlaps q
+    assert _attn(L, _desc(pos=2, rope_base=0.0)) == SWIN_EINVAL
+
+
+def test_attn_empty_batch_is_a_no_op(L):
+    assert _attn(L, _desc(B=0), q=None, k=None, v=None, out=None) == SWIN_OK
+
+
+def test_partition_rejects(L):
+    P = L.swin_window_partition
+    assert P(FAKE, ctypes.c_void_p(0x900000), 1, 12, 12, 8, 5, 0, 0, 1, None) == SWIN_EUNSUPPORTED
+    assert P(FAKE, ctypes.c_void_p(0x900000), 1, 16, 16, 8, 8, 8, 0, 1, None) == SWIN_EINVAL
+    assert P(FAKE, ctypes.c_void_p(0x900000), 1, 16, 16, 8, 8, 2, 1, 1, None) == SWIN_EINVAL
+    assert P(FAKE, FAKE, 1, 16, 16, 8, 8, 0, 0, 1, None) == SWIN_EINVAL            # x == xw
+    assert P(None, ctypes.c_void_p(0x900000), 1, 16, 16, 8, 8, 0, 0, 1, None) == SWIN_EINVAL
+    assert P(FAKE, ctypes.c_void_p(0x900000), 1, 16, 16, 8, 8, 0, 0, 9, None) == SWIN_EINVAL
+    assert P(None, None, 0, 16, 16, 8, 8, 0, 0, 1, None) == SWIN_OK               # empty
+    R = L.swin_window_reverse
+    assert R(FAKE, ctypes.c_void_p(0x900000), 1, 16, 16, 8, 8, 9, 0, 1, None) == SWIN_EINVAL
+
+
+def test_cpb_rejects(L):
+    C = L.swin_cpb_table
+    T = ctypes.c_void_p(0x900000)
+    assert C(8, 3, 512, FAKE, None, FAKE, None, 1, T, None) == SWIN_EUNSUPPORTED   # code-form log-CPB
+    assert C(8, 3, 512, FAKE, None, FAKE, None, 7, T, None) == SWIN_EINVAL
+    assert C(0, 3, 512, FAKE, None, FAKE, None, 0, T, None) == SWIN_EINVAL
+    assert C(8, 0, 512, FAKE, None, FAKE, None, 0, T, None) == SWIN_EINVAL
+    assert C(8, 3, 0, FAKE, None, FAKE, None, 0, T, None) == SWIN_EINVAL
+    assert C(8, 3, 512, None, None, FAKE, None, 0, T, None) == SWIN_EINVAL
+    assert C(8, 3, 512, FAKE, None, FAKE, None, 0, None, None) == SWIN_EINVAL
+    assert C(8, 3, 512, FAKE, None, FAKE, None, 0, FAKE, None) == SWIN_EINVAL      # table over w1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()

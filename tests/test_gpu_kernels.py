@@ -1,0 +1,79 @@
+"""GPU parity of the partition / reverse kernels (bit-exact against the
+oracle) and of the log-CPB table kernel (fp32 vs the fp64 oracle)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_helpers import f64
+from vision_transformer_windowed_partition_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    t = t.contiguous().cpu()
+    return (t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)).numpy()
+
+
+@pytest.mark.parametrize("shape,M,shift,part", [
+    ((2, 16, 24, 64), 8, 3, "cyclic"),
+    ((1, 12, 12, 8), 4, 0, "interleaved"),
+    ((3, 28, 14, 40), 7, 5, "cyclic"),
+    ((2, 16, 16, 6), 8, 4, "cyclic"),          # 12- / 24-byte rows: narrow vector moves
+    ((1, 64, 64, 96), 8, 4, "cyclic"),
+    ((0, 16, 16, 32), 8, 4, "cyclic"),         # empty batch
+])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_partition_reverse_bit_exact(shape, M, shift, part, dtype):
+    g = torch.Generator().manual_seed(1)
+    x = torch.randn(shape, generator=g).to(dtype)
+    xd = x.to(DEV)
+    xw = binding.swin_window_partition(xd, M, shift, part)
+    back = binding.swin_window_reverse(xw, shape[0], shape[1], shape[2], M, shift, part)
+    torch.cuda.synchronize()
+    want = oracle.partition(_bits(x), M, shift, part)
+    assert np.array_equal(_bits(xw), want)
+    assert np.array_equal(_bits(back), _bits(x))
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_partition_full_workloads(idx):
+    wl = synth.WORKLOADS[idx]
+    g = torch.Generator().manual_seed(idx)
+    x = torch.randint(-2 ** 15, 2 ** 15, (wl.B, wl.H, wl.W, wl.C), generator=g, dtype=torch.int16)
+    xd = x.to(DEV).view(torch.bfloat16)
+    xw = binding.swin_window_partition(xd, wl.M, wl.shift, wl.partition)
+    torch.cuda.synchronize()
+    want = oracle.partition(x.numpy(), wl.M, wl.shift, wl.partition)
+    assert np.array_equal(xw.view(torch.int16).cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("M,heads,hidden,biases", [(8, 3, 512, True), (16, 3, 512, True),
+                                                    (24, 16, 512, True), (5, 2, 37, False),
+                                                    (1, 1, 1, True), (32, 64, 4096, True)])
+def test_cpb_table(M, heads, hidden, biases):
+    g = torch.Generator().manual_seed(M)
+    w1 = 0.02 * torch.randn(hidden, 2, generator=g)
+    b1 = 0.02 * torch.randn(hidden, generator=g) if biases else None
+    w2 = 0.02 * torch.randn(heads, hidden, generator=g)
+    b2 = 0.02 * torch.randn(heads, generator=g) if biases else None
+    d = lambda t: None if t is None else t.to(DEV)
+    got = binding.swin_cpb_table(M, d(w1), d(b1), d(w2), d(b2))
+    torch.cuda.synchronize()
+    want = oracle.cpb_table(M, f64(w1), None if b1 is None else f64(b1), f64(w2),
+                            None if b2 is None else f64(b2))
+    assert got.shape == want.shape
+    np.testing.assert_allclose(got.double().cpu().numpy(), want, rtol=1e-5, atol=1e-6)
+
+
+def test_cpb_table_large_weights():
+    """Weights of trained magnitude (N(0,1)): relative fp32 accuracy."""
+    g = torch.Generator().manual_seed(3)
+    w1, b1 = torch.randn(512, 2, generator=g), torch.randn(512, generator=g)
+    w2, b2 = torch.randn(4, 512, generator=g), torch.randn(4, generator=g)
+    got = binding.swin_cpb_table(12, w1.to(DEV), b1.to(DEV), w2.to(DEV), b2.to(DEV))
+    torch.cuda.synchronize()
+    want = oracle.cpb_table(12, f64(w1), f64(b1), f64(w2), f64(b2))
+    np.testing.assert_allclose(got.double().cpu().numpy(), want, rtol=1e-5, atol=1e-4)

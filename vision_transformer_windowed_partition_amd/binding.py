@@ -1,0 +1,174 @@
+"""Python binding of libswinattn.so (C ABI in include/swin_attn.h).
+
+Argument marshalling only: each function checks that it was handed device
+tensors, takes their data pointers and the current HIP stream, and calls the
+C entry point of the same name.  Every step of the computation runs in the
+library's kernels; if the library is missing this module raises instead of
+computing anything another way.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libswinattn.so")
+
+SWIN_OK, SWIN_EINVAL, SWIN_EUNSUPPORTED, SWIN_EHIP = 0, 1, 2, 3
+PARTITION = {"cyclic": 0, "interleaved": 1}
+SIM = {"cosine": 0, "dot": 1}
+POS = {"none": 0, "table": 1, "rope2d": 2}
+DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+LAYOUT = {"grid": 0, "windows": 1}
+CPB_PAPER = 0
+
+
+class SwinAttnDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "H", "W", "C", "heads", "M", "shift", "partition", "sim", "pos", "dtype", "layout")] + \
+               [("tau_min", ctypes.c_float), ("rope_base", ctypes.c_float)]
+
+
+class SwinError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{swin_status_string(status)} -- {detail}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, vp, f = ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
+        L.swin_cpb_table.restype = i32
+        L.swin_cpb_table.argtypes = [i32, i32, i32, vp, vp, vp, vp, i32, vp, vp]
+        for fn in (L.swin_window_partition, L.swin_window_reverse):
+            fn.restype = i32
+            fn.argtypes = [vp, vp] + [i32] * 8 + [vp]
+        L.swin_window_attn_fwd.restype = i32
+        L.swin_window_attn_fwd.argtypes = [ctypes.POINTER(SwinAttnDesc)] + [vp] * 8
+        L.swin_status_string.restype = ctypes.c_char_p
+        L.swin_status_string.argtypes = [i32]
+        L.swin_last_error.restype = ctypes.c_char_p
+        L.swin_last_error.argtypes = []
+        L.swin_version.restype = i32
+        L.swin_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def swin_status_string(status: int) -> str:
+    return lib().swin_status_string(int(status)).decode()
+
+
+def swin_last_error() -> str:
+    return lib().swin_last_error().decode()
+
+
+def swin_version() -> int:
+    return int(lib().swin_version())
+
+
+def _check(rc: int) -> None:
+    if rc != SWIN_OK:
+        raise SwinError(rc, swin_last_error())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    return t.data_ptr()
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _enum(table, v):
+    return table[v] if isinstance(v, str) else int(v)
+
+
+def swin_cpb_table(M: int, w1, b1, w2, b2, *, out=None, cpb_mode: int = CPB_PAPER, stream=None):
+    """(2M-1)^2 x heads fp32 bias table from the meta network parameters."""
+    heads, hidden = w2.shape
+    for t in (w1, b1, w2, b2, out):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("CPB parameters and table must be contiguous fp32")
+    if out is None:
+        out = torch.empty(((2 * M - 1) ** 2, heads), dtype=torch.float32, device=w1.device)
+    _check(lib().swin_cpb_table(M, heads, hidden, _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
+                                cpb_mode, _ptr(out), _stream(w1, stream)))
+    return out
+
+
+def swin_window_partition(x, M: int, shift: int, partition="cyclic", *, out=None, stream=None):
+    """(B, H, W, C) grid -> (B*nW, M*M, C) windows (bit-exact gather)."""
+    B, H, W, C = x.shape
+    if out is None:
+        out = torch.empty((B * (H // max(M, 1)) * (W // max(M, 1)), M * M, C), dtype=x.dtype, device=x.device)
+    if not x.is_contiguous() or not out.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    _check(lib().swin_window_partition(_ptr(x), _ptr(out), B, H, W, C, M, shift,
+                                       _enum(PARTITION, partition), DTYPE[x.dtype], _stream(x, stream)))
+    return out
+
+
+def swin_window_reverse(xw, B: int, H: int, W: int, M: int, shift: int, partition="cyclic", *,
+                        out=None, stream=None):
+    """(B*nW, M*M, C) windows -> (B, H, W, C) grid (bit-exact scatter)."""
+    C = xw.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, W, C), dtype=xw.dtype, device=xw.device)
+    if not xw.is_contiguous() or not out.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    _check(lib().swin_window_reverse(_ptr(xw), _ptr(out), B, H, W, C, M, shift,
+                                     _enum(PARTITION, partition), DTYPE[xw.dtype], _stream(xw, stream)))
+    return out
+
+
+def make_desc(*, B, H, W, C, heads, M, shift=0, partition="cyclic", sim="cosine", pos="none",
+              dtype=torch.bfloat16, layout="grid", tau_min=0.01, rope_base=10000.0) -> SwinAttnDesc:
+    return SwinAttnDesc(B, H, W, C, heads, M, shift, _enum(PARTITION, partition), _enum(SIM, sim),
+                        _enum(POS, pos), DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype),
+                        _enum(LAYOUT, layout), float(tau_min), float(rope_base))
+
+
+def swin_window_attn_fwd(q, k, v, *, heads: int, M: int, shift: int = 0, partition="cyclic",
+                         sim="cosine", pos="none", tau=None, table=None, rope_freqs=None,
+                         tau_min: float = 0.01, rope_base: float = 10000.0, layout="grid",
+                         grid=None, out=None, desc: SwinAttnDesc | None = None, stream=None):
+    """Windowed attention forward.  q, k, v: (B, H, W, C) for layout "grid", or
+    (B*nW, M*M, C) for layout "windows" with grid=(B, H, W)."""
+    if desc is None:
+        if _enum(LAYOUT, layout) == 0:
+            B, H, W, C = q.shape
+        else:
+            B, H, W = grid
+            C = q.shape[-1]
+        desc = make_desc(B=B, H=H, W=W, C=C, heads=heads, M=M, shift=shift, partition=partition,
+                         sim=sim, pos=pos, dtype=q.dtype, layout=layout, tau_min=tau_min,
+                         rope_base=rope_base)
+    for t in (q, k, v):
+        if not t.is_contiguous() or t.dtype != q.dtype or t.shape != q.shape:
+            raise ValueError("q, k, v must be contiguous tensors of one shape and dtype")
+    for t in (tau, table, rope_freqs):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("tau, table and rope_freqs must be contiguous fp32")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().swin_window_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                      _ptr(tau), _ptr(table), _ptr(rope_freqs), _stream(q, stream)))
+    return out

@@ -1,0 +1,183 @@
+// C ABI of libswinattn.so (declared in include/swin_attn.h): argument
+// validation on the host, then one asynchronous launch on the caller's
+// stream.  Nothing is enqueued unless every argument passes.
+#include <stdint.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int hip_status(hipError_t e, const char* what)
+{
+    if (e == hipSuccess) return SWIN_OK;
+    return fail(SWIN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// Shape rules shared by partition and attention.  Returns SWIN_OK or the
+// failing status (with the detail recorded).
+int check_grid(int32_t B, int32_t H, int32_t W, int32_t C, int32_t M, int32_t shift,
+               int32_t partition)
+{
+    if (B < 0 || H < 1 || W < 1 || C < 1 || M < 1)
+        return fail(SWIN_EINVAL, "bad shape B=%d H=%d W=%d C=%d M=%d", B, H, W, C, M);
+    if (partition != SWIN_PART_CYCLIC && partition != SWIN_PART_INTERLEAVED)
+        return fail(SWIN_EINVAL, "unknown partition %d", partition);
+    if (shift < 0 || shift >= M)
+        return fail(SWIN_EINVAL, "shift %d outside [0, M=%d)", shift, M);
+    if (partition == SWIN_PART_INTERLEAVED && shift != 0)
+        return fail(SWIN_EINVAL, "interleaved windows take no shift (shift=%d)", shift);
+    if (M > H || M > W || H % M || W % M)
+        return fail(SWIN_EUNSUPPORTED, "H=%d, W=%d must be multiples of M=%d (no padding is built)", H, W, M);
+    const int64_t nwin = (int64_t)B * (H / M) * (W / M);
+    if ((int64_t)B * H * W > ((int64_t)1 << 31) - 1 || nwin * 64 > ((int64_t)1 << 31) - 1)
+        return fail(SWIN_EUNSUPPORTED, "grid too large (B*H*W=%lld)", (long long)B * H * W);
+    return SWIN_OK;
+}
+
+swin::Geometry make_geometry(int32_t B, int32_t H, int32_t W, int32_t C, int32_t heads,
+                             int32_t M, int32_t shift, int32_t partition, int32_t layout)
+{
+    swin::Geometry g;
+    g.B = B; g.H = H; g.W = W; g.C = C; g.heads = heads; g.d = C / heads;
+    g.M = M; g.shift = shift; g.part = partition; g.layout = layout;
+    g.nwr = H / M; g.nwc = W / M; g.N = M * M;
+    g.nwin = B * g.nwr * g.nwc;
+    return g;
+}
+
+int window_copy(const void* src, void* dst, int32_t B, int32_t H, int32_t W, int32_t C,
+                int32_t M, int32_t shift, int32_t partition, int32_t dtype, void* stream,
+                bool to_windows)
+{
+    int st = check_grid(B, H, W, C, M, shift, partition);
+    if (st) return st;
+    if (dtype != SWIN_DT_F32 && dtype != SWIN_DT_BF16) return fail(SWIN_EINVAL, "unknown dtype %d", dtype);
+    const size_t bytes = (size_t)B * H * W * C * (dtype == SWIN_DT_F32 ? 4 : 2);
+    if (bytes == 0) return SWIN_OK;
+    if (!src || !dst) return fail(SWIN_EINVAL, "NULL tensor pointer");
+    if (overlaps(src, bytes, dst, bytes)) return fail(SWIN_EINVAL, "source and destination overlap");
+    swin::Geometry g = make_geometry(B, H, W, C, 1, M, shift, partition, SWIN_LAYOUT_GRID);
+    return hip_status(swin::launch_window_copy(src, dst, g, dtype == SWIN_DT_F32 ? 4 : 2, to_windows,
+                                               (hipStream_t)stream),
+                      to_windows ? "swin_window_partition launch" : "swin_window_reverse launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int swin_version(void) { return SWIN_ATTN_VERSION; }
+
+const char* swin_status_string(int status)
+{
+    switch (status) {
+    case SWIN_OK: return "SWIN_OK: success";
+    case SWIN_EINVAL: return "SWIN_EINVAL: invalid argument";
+    case SWIN_EUNSUPPORTED: return "SWIN_EUNSUPPORTED: defined by the method but not built here";
+    case SWIN_EHIP: return "SWIN_EHIP: HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char* swin_last_error(void) { return g_last_error.c_str(); }
+
+int swin_cpb_table(int32_t M, int32_t heads, int32_t hidden, const float* w1, const float* b1,
+                   const float* w2, const float* b2, int32_t cpb_mode, float* table, void* stream)
+{
+    if (cpb_mode != SWIN_CPB_PAPER) {
+        if (cpb_mode == 1 || cpb_mode == 2)
+            return fail(SWIN_EUNSUPPORTED, "cpb_mode %d (released-code variant) is not built", cpb_mode);
+        return fail(SWIN_EINVAL, "unknown cpb_mode %d", cpb_mode);
+    }
+    if (M < 1 || M > 64) return fail(SWIN_EINVAL, "M=%d outside [1, 64]", M);
+    if (heads < 1 || heads > 64) return fail(SWIN_EINVAL, "heads=%d outside [1, 64]", heads);
+    if (hidden < 1 || hidden > 4096) return fail(SWIN_EINVAL, "hidden=%d outside [1, 4096]", hidden);
+    if (!w1 || !w2 || !table) return fail(SWIN_EINVAL, "NULL w1, w2 or table");
+    const size_t tb = (size_t)(2 * M - 1) * (2 * M - 1) * heads * sizeof(float);
+    if (overlaps(table, tb, w1, (size_t)hidden * 2 * 4) || overlaps(table, tb, w2, (size_t)heads * hidden * 4) ||
+        (b1 && overlaps(table, tb, b1, (size_t)hidden * 4)) || (b2 && overlaps(table, tb, b2, (size_t)heads * 4)))
+        return fail(SWIN_EINVAL, "table overlaps a parameter tensor");
+    return hip_status(swin::launch_cpb_table(M, heads, hidden, w1, b1, w2, b2, table, (hipStream_t)stream),
+                      "swin_cpb_table launch");
+}
+
+int swin_window_partition(const void* x, void* xw, int32_t B, int32_t H, int32_t W, int32_t C,
+                          int32_t M, int32_t shift, int32_t partition, int32_t dtype, void* stream)
+{
+    return window_copy(x, xw, B, H, W, C, M, shift, partition, dtype, stream, true);
+}
+
+int swin_window_reverse(const void* xw, void* x, int32_t B, int32_t H, int32_t W, int32_t C,
+                        int32_t M, int32_t shift, int32_t partition, int32_t dtype, void* stream)
+{
+    return window_copy(xw, x, B, H, W, C, M, shift, partition, dtype, stream, false);
+}
+
+int swin_window_attn_fwd(const swin_attn_desc* d, const void* q, const void* k, const void* v,
+                         void* out, const float* tau, const float* table, const float* rope_freqs,
+                         void* stream)
+{
+    if (!d) return fail(SWIN_EINVAL, "NULL descriptor");
+    int st = check_grid(d->B, d->H, d->W, d->C, d->M, d->shift, d->partition);
+    if (st) return st;
+    if (d->heads < 1 || d->C % d->heads)
+        return fail(SWIN_EINVAL, "C=%d is not a multiple of heads=%d", d->C, d->heads);
+    if (d->sim != SWIN_SIM_COSINE && d->sim != SWIN_SIM_DOT) return fail(SWIN_EINVAL, "unknown sim %d", d->sim);
+    if (d->pos != SWIN_POS_NONE && d->pos != SWIN_POS_TABLE && d->pos != SWIN_POS_ROPE2D)
+        return fail(SWIN_EINVAL, "unknown pos %d", d->pos);
+    if (d->dtype != SWIN_DT_F32 && d->dtype != SWIN_DT_BF16) return fail(SWIN_EINVAL, "unknown dtype %d", d->dtype);
+    if (d->layout != SWIN_LAYOUT_GRID && d->layout != SWIN_LAYOUT_WINDOWS)
+        return fail(SWIN_EINVAL, "unknown layout %d", d->layout);
+    if (!(d->tau_min > 0.0f) || !(d->tau_min < 3.0e38f)) return fail(SWIN_EINVAL, "tau_min must be positive and finite");
+    if (d->pos == SWIN_POS_ROPE2D && !rope_freqs && !(d->rope_base > 0.0f && d->rope_base < 3.0e38f))
+        return fail(SWIN_EINVAL, "rope_base must be positive and finite");
+    if (d->C / d->heads != 32)
+        return fail(SWIN_EUNSUPPORTED, "head dim %d: only 32 is built", d->C / d->heads);
+    if (d->M > 64) return fail(SWIN_EUNSUPPORTED, "M=%d: windows above 64 are not built", d->M);
+    const size_t es = d->dtype == SWIN_DT_F32 ? 4 : 2;
+    const size_t bytes = (size_t)d->B * d->H * d->W * d->C * es;
+    if (bytes == 0) return SWIN_OK;
+    if (!q || !k || !v || !out) return fail(SWIN_EINVAL, "NULL q, k, v or out");
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15)
+        return fail(SWIN_EINVAL, "q, k, v and out must be 16-byte aligned");
+    if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
+        return fail(SWIN_EINVAL, "out overlaps q, k or v");
+    if (d->sim == SWIN_SIM_COSINE && !tau) return fail(SWIN_EINVAL, "COSINE needs tau");
+    if (d->pos == SWIN_POS_TABLE && !table) return fail(SWIN_EINVAL, "POS_TABLE needs a table");
+
+    swin::AttnParams p;
+    p.g = make_geometry(d->B, d->H, d->W, d->C, d->heads, d->M, d->shift, d->partition, d->layout);
+    p.sim = d->sim; p.pos = d->pos; p.dtype = d->dtype;
+    p.tau_min = d->tau_min; p.rope_base = d->rope_base;
+    p.q = q; p.k = k; p.v = v; p.out = out;
+    p.tau = tau; p.table = table; p.rope_freqs = rope_freqs;
+    hipError_t e = d->dtype == SWIN_DT_F32 ? swin::launch_attn_valu(p, (hipStream_t)stream)
+                                           : swin::launch_attn_mfma(p, (hipStream_t)stream);
+    return hip_status(e, "swin_window_attn_fwd launch");
+}
+
+}  // extern "C"

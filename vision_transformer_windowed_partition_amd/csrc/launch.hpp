@@ -1,0 +1,37 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the
+// kernel translation units.  Arguments reaching these functions are already
+// validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+namespace swin {
+
+struct AttnParams {
+    Geometry g;
+    int sim, pos, dtype;
+    float tau_min, rope_base;
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    const float* tau;
+    const float* table;
+    const float* rope_freqs;
+};
+
+hipError_t launch_window_copy(const void* src, void* dst, const Geometry& g, int elem_size,
+                              bool to_windows, hipStream_t stream);
+
+hipError_t launch_cpb_table(int M, int heads, int hidden, const float* w1, const float* b1,
+                            const float* w2, const float* b2, float* table, hipStream_t stream);
+
+// fp32 (and any-shape fallback) attention on the vector ALUs.
+hipError_t launch_attn_valu(const AttnParams& p, hipStream_t stream);
+
+// bf16 attention on the matrix cores (d == 32).
+hipError_t launch_attn_mfma(const AttnParams& p, hipStream_t stream);
+
+}  // namespace swin

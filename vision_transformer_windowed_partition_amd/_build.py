@@ -18,6 +18,8 @@ FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
     # no packed-fp32 VALU instructions (v_pk_{add,mul,fma}_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs (no AGPR <-> VGPR copies around the softmax)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -175,8 +175,9 @@ int swin_window_attn_fwd(const swin_attn_desc* d, const void* q, const void* k, 
     p.tau_min = d->tau_min; p.rope_base = d->rope_base;
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.tau = tau; p.table = table; p.rope_freqs = rope_freqs;
-    hipError_t e = d->dtype == SWIN_DT_F32 ? swin::launch_attn_valu(p, (hipStream_t)stream)
-                                           : swin::launch_attn_mfma(p, (hipStream_t)stream);
+    hipError_t e = d->dtype == SWIN_DT_F32   ? swin::launch_attn_valu(p, (hipStream_t)stream)
+                 : swin::attn_small_supported(p) ? swin::launch_attn_small(p, (hipStream_t)stream)
+                                                 : swin::launch_attn_mfma(p, (hipStream_t)stream);
     return hip_status(e, "swin_window_attn_fwd launch");
 }
 

@@ -1,0 +1,508 @@
+// Window attention for windows of up to 256 tokens (M <= 16) on the gfx950
+// matrix cores, with the window's keys and values held in registers.
+//
+// Same computation as the general kernel (SwinV2 card eq. 1-2 and its
+// window-attention pseudocode, log-CPB table of eq. 3-4, cyclic-shift or
+// interleaved windows; rotary positions go to the general kernel), organised
+// for small windows: one wavefront owns (window, head, part of the queries)
+// and loads that window-head's keys and values into MFMA fragments it keeps
+// in registers for all of its query tiles.
+//   K  (keys x d): A operand of S^T = K Q^T (v_mfma_f32_16x16x32_bf16); each
+//      lane loads 16 contiguous bytes of one key from HBM.
+//   V^T (d x keys): A operand of O^T = V^T P^T; V rows are copied to a
+//      wavefront-private LDS area with contiguous 16-byte writes and read
+//      back as 8 keys of one channel per lane with fixed-offset 2-byte reads.
+// The score tile leaves the MFMA with each lane holding 8 consecutive key
+// slots of one query, the B-operand layout of P^T, so the softmax runs in
+// registers between the two products; row sums come from a third MFMA
+// against an all-ones operand.  The four wavefronts of a workgroup share one
+// head and its bias table in LDS; no workgroup barrier follows the table.
+//
+// Precision.  COSINE normally feeds the MFMA the unit-normalised k^ rounded
+// to bf16; that rounding (2^-9 of the norm) is multiplied by 1/tau, so for
+// tau < 0.1 a wavefront feeds the raw bf16 k (exact) and scales each score by
+// 1/||k_j|| in fp32 instead.  The softmax uses a static shift (cos <= 1, or
+// Cauchy-Schwarz for DOT) when the spread of the logits stays within 2^60,
+// else the running maximum per 32-key chunk.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace swin {
+
+namespace {
+
+constexpr int D = 32;
+constexpr int WAVES = 4;
+constexpr float RANGE_LIMIT = 60.0f;
+constexpr float PRECISE_TAU = 0.1f;
+
+struct SmallLayout {
+    int SR, GPR, NSP;          // slots per key row (M rounded up to 8), groups per row, real slots
+    int NQT;                   // query tiles per window-head
+    int TPW;                   // query tiles per wavefront item
+    int parts;                 // wavefront items per window-head
+    int per_head;              // items per head, padded to a multiple of WAVES
+    float inv_SR, inv_M, inv_GPR;
+};
+
+// floor(a / b) for 0 <= a < 2^16, b <= 64, from a float reciprocal: the
+// exact quotient of a + 1/2 sits at least 1/(2b) from an integer, far above
+// the rounding error of the product.
+__device__ __forceinline__ int qdiv(int a, float inv_b) { return (int)(((float)a + 0.5f) * inv_b); }
+
+// Element offset (within one image, or one window for the WINDOWS layout)
+// of local token (r, c); everything but (r, c) is wave-uniform, no branch:
+// cyclic grid: origin (wr*M + shift, wc*M + shift), steps 1, wrap at H, W;
+// interleaved: origin (wr, wc), steps (H/M, W/M), never wraps;
+// windows tensor: origin 0, steps 1, an M x M "grid".
+struct WinGeo {
+    int r0, c0, rs, cs, Hm, Wm, C;
+    __device__ __forceinline__ int tok(int r, int c) const
+    {
+        int gi = r0 + r * rs;
+        gi -= gi >= Hm ? Hm : 0;
+        int gj = c0 + c * cs;
+        gj -= gj >= Wm ? Wm : 0;
+        return (gi * Wm + gj) * C;
+    }
+};
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int NCH>
+struct Frags {                 // this wave's window-head, in MFMA operand layout
+    const bf16x8* k;           // LDS: k^ (or raw k: DOT, precise COSINE), [NCH][2][64 lanes]
+    bf16x8 v[NCH][2];          // V^T, channels 0-15 and 16-31
+    int koff[NCH];             // bias-table offset of this lane's key group: rj*S + c0
+    int rc[NCH];               // this lane's key group: rj << 8 | c0
+};
+
+struct Tile {                  // one query tile of 16 queries
+    bf16x8 qf;
+    float qscale, negm, mrun;
+    int qoff, rlo, rhi;
+    uint32_t cmask;            // allowed key columns (bit c)
+    bool exact;
+    f32x4 o0, o1, ls;
+};
+
+// One pair of query tiles against the window's keys.
+//   MASK: shift regions / padded slots; PRECISE: scores scaled by 1/||k_j||
+//   (raw k operand); EXACT: running maximum instead of the static shift.
+template <int SIM, int POS, int NCH, bool MASK, bool PRECISE, bool EXACT>
+__device__ __forceinline__ void run_pair(const Frags<NCH>& F, Tile (&T)[2], const float* bias2,
+                                         const float* kinv, int negrow, int lane, bool partial_any,
+                                         bool precise_rt)
+{
+    const int grp = lane >> 4;
+    const bool prec = PRECISE && precise_rt;
+    const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        uint32_t bits[2] = {0xffu, 0xffu};
+        if (MASK) {
+            const int rj = F.rc[c] >> 8, c0 = F.rc[c] & 0xff;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const bool rok = rj >= T[i].rlo && rj < T[i].rhi;
+                bits[i] = rok ? (T[i].cmask >> c0) & 0xffu : 0u;
+            }
+            if (!__any((bits[0] | bits[1]) != 0u)) continue;        // chunk masked for the wave
+        }
+        float kin[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+        if (prec) {
+            const f32x4 a = *(const f32x4*)(kinv + 32 * c + 8 * grp);
+            const f32x4 b = *(const f32x4*)(kinv + 32 * c + 8 * grp + 4);
+            kin[0] = a[0]; kin[1] = a[1]; kin[2] = a[2]; kin[3] = a[3];
+            kin[4] = b[0]; kin[5] = b[1]; kin[6] = b[2]; kin[7] = b[3];
+        }
+        float add[2][8];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (POS == SWIN_POS_TABLE) {
+                const float* bp = bias2 + ((MASK && bits[i] == 0u) ? negrow : F.koff[c] + T[i].qoff);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) add[i][e] = SIM == SWIN_SIM_COSINE ? bp[e] : bp[e] + T[i].negm;
+            } else {
+                const float a = (MASK && bits[i] == 0u) ? -INFINITY : T[i].negm;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) add[i][e] = a;
+            }
+        }
+        const bf16x8 ka = F.k[(c * 2 + 0) * 64 + lane];
+        const bf16x8 kb = F.k[(c * 2 + 1) * 64 + lane];
+        f32x4 sa[2], sb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            sa[i] = mfma(ka, T[i].qf, zero4);
+            sb[i] = mfma(kb, T[i].qf, zero4);
+        }
+        bf16x8 pb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { x[e] = sa[i][e]; x[e + 4] = sb[i][e]; }
+            float sc[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sc[e] = prec ? T[i].qscale * kin[e] : T[i].qscale;
+            float pr[8];
+            if (!EXACT || !T[i].exact) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(x[e], sc[e], add[i][e]));
+                if (MASK && partial_any) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pr[e] = (bits[i] >> e) & 1u ? pr[e] : 0.0f;
+                }
+            } else {
+                float xs[8], cm = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    xs[e] = fmaf(x[e], sc[e], add[i][e]);
+                    if (MASK) xs[e] = (bits[i] >> e) & 1u ? xs[e] : -INFINITY;
+                    cm = fmaxf(cm, xs[e]);
+                }
+                cm = fmaxf(cm, __shfl_xor(cm, 16));
+                cm = fmaxf(cm, __shfl_xor(cm, 32));
+                const float mnew = fmaxf(T[i].mrun, cm);
+                const float mref = mnew == -INFINITY ? 0.0f : mnew;
+                const float alpha = __builtin_amdgcn_exp2f(T[i].mrun - mref);
+                T[i].o0 *= alpha; T[i].o1 *= alpha; T[i].ls *= alpha;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(xs[e] - mref);
+                T[i].mrun = mnew;
+            }
+            pb[i] = pack_bf16x8(pr);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            T[i].o0 = mfma(F.v[c][0], pb[i], T[i].o0);
+            T[i].o1 = mfma(F.v[c][1], pb[i], T[i].o1);
+            T[i].ls = mfma(ones, pb[i], T[i].ls);
+        }
+    }
+}
+
+template <int SIM, int POS, int NCH>
+__global__ void __launch_bounds__(256)
+attn_small_kernel(AttnParams p, SmallLayout L)
+{
+    extern __shared__ __attribute__((aligned(16))) float smem_f[];
+    const Geometry& g = p.g;
+    const int M = g.M, N = g.N, S = 2 * M - 1;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int grp = lane >> 4;       // 16-lane group: k-range of the operands
+    const int li = lane & 15;        // row / column inside a 16 x 16 tile
+
+    const int tabsz = POS == SWIN_POS_TABLE ? (S * S + 8 + 3) / 4 * 4 : 0;
+    float* bias2 = smem_f;                                           // [S*S + 8] (TABLE)
+    float* red = bias2 + tabsz;                                      // [16]
+    float* kinv = red + 16 + wave * (NCH * 32);                      // [NCH*32] 1/||k|| (precise path)
+    __bf16* vst = (__bf16*)(red + 16 + WAVES * NCH * 32) + wave * (NCH * 32 * D);   // [NCH*32][D] V rows
+
+    // ---- item: one head per workgroup, one (window, query part) per wave
+    const int h = (blockIdx.x * WAVES) / L.per_head;
+    const int local = blockIdx.x * WAVES - h * L.per_head + wave;
+    const bool active = local < g.nwin * L.parts;
+    const int win = active ? local / L.parts : 0;
+    const int part = active ? local - win * L.parts : 0;
+    const float tau_eff = SIM == SWIN_SIM_COSINE ? fmaxf(p.tau[h], p.tau_min) : 1.0f;
+    const float inv_tau = 1.0f / tau_eff;
+
+    // ---- bias table of head h: reversed (consecutive keys read consecutive
+    // floats), in log2 units, shifted by its max (and by 1/tau for COSINE)
+    float bias_range = 0.0f;
+    if (POS == SWIN_POS_TABLE) {
+        float mx = -INFINITY, mn = INFINITY;
+        for (int i = tid; i < S * S; i += 256) {
+            const float v = p.table[(size_t)(S * S - 1 - i) * g.heads + h] * kLog2e;
+            bias2[i] = v;
+            mx = fmaxf(mx, v);
+            mn = fminf(mn, v);
+        }
+        if (tid < 8) bias2[S * S + tid] = -INFINITY;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            mx = fmaxf(mx, __shfl_xor(mx, off));
+            mn = fminf(mn, __shfl_xor(mn, off));
+        }
+        if (lane == 0) { red[wave] = mx; red[4 + wave] = mn; }
+        __syncthreads();
+        mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        mn = fminf(fminf(red[4], red[5]), fminf(red[6], red[7]));
+        bias_range = mx - mn;
+        const float shift = SIM == SWIN_SIM_COSINE ? mx + kLog2e / tau_eff : mx;
+        __syncthreads();
+        for (int i = tid; i < S * S; i += 256) bias2[i] -= shift;
+        __syncthreads();
+    }
+    if (!active) return;                                  // no workgroup barrier after this point
+
+    // ---- window geometry (wave-uniform)
+    WinGeo wg;
+    const int nW = g.nwr * g.nwc;
+    const int bimg = win / nW, wl = win - bimg * nW;
+    const int wr = wl / g.nwc, wc = wl - wr * g.nwc;
+    wg.C = g.C;
+    int64_t base;
+    if (g.layout == SWIN_LAYOUT_WINDOWS) {
+        base = (int64_t)win * N * g.C;
+        wg.r0 = wg.c0 = 0; wg.rs = wg.cs = 1; wg.Hm = wg.Wm = M;
+    } else {
+        base = (int64_t)bimg * g.H * g.W * g.C;
+        wg.Hm = g.H; wg.Wm = g.W;
+        if (g.part == SWIN_PART_INTERLEAVED) { wg.r0 = wr; wg.c0 = wc; wg.rs = g.nwr; wg.cs = g.nwc; }
+        else { wg.r0 = wr * M + g.shift; wg.c0 = wc * M + g.shift; wg.rs = wg.cs = 1; }
+    }
+    const bool cyc_shift = g.part == SWIN_PART_CYCLIC && g.shift > 0;
+    const bool last_r = cyc_shift && wr == g.nwr - 1;
+    const bool last_c = cyc_shift && wc == g.nwc - 1;
+    const bool padded = L.SR != M || NCH * 32 != L.NSP;
+    const bool needs_mask = last_r || last_c || padded;
+    const uint16_t* qg = (const uint16_t*)p.q + base + h * D;
+    const uint16_t* kg = (const uint16_t*)p.k + base + h * D;
+    const uint16_t* vg = (const uint16_t*)p.v + base + h * D;
+    uint16_t* og = (uint16_t*)p.out + base + h * D;
+    const bool precise = SIM == SWIN_SIM_COSINE && tau_eff < PRECISE_TAU;
+
+    // ---- K fragments: tile A of chunk c holds slots 32c + 8(r/4) + r%4,
+    // tile B the next 4 of each group of 8, so that S^T hands this lane slots
+    // 32c + 8 grp + 0..7.  V rows go to LDS (16 bytes per lane, contiguous).
+    Frags<NCH> F;
+    u32x4 kraw[NCH][2];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int s = 32 * c + 8 * (li >> 2) + (li & 3) + 4 * t;
+            const int rj = qdiv(s, L.inv_SR), cj = s - rj * L.SR;
+            kraw[c][t] = u32x4{0u, 0u, 0u, 0u};
+            if (rj < M && cj < M) kraw[c][t] = *(const u32x4*)(kg + wg.tok(rj, cj) + grp * 8);
+        }
+    {
+        u32x4 vraw[2 * NCH];
+#pragma unroll
+        for (int j = 0; j < 2 * NCH; ++j) {               // piece j*64 + lane: slot (.)/4, channels 8*(. % 4)
+            const int idx = j * 64 + lane;
+            const int s = idx >> 2, piece = idx & 3;
+            const int rj = qdiv(s, L.inv_SR), cj = s - rj * L.SR;
+            vraw[j] = u32x4{0u, 0u, 0u, 0u};
+            if (rj < M && cj < M) vraw[j] = *(const u32x4*)(vg + wg.tok(rj, cj) + piece * 8);
+        }
+        // 16-byte piece p of slot s sits at piece position p ^ (s/8 mod 4), so
+        // that the transposed reads of the four lane groups hit different banks
+#pragma unroll
+        for (int j = 0; j < 2 * NCH; ++j) {
+            const int idx = j * 64 + lane, s = idx >> 2, piece = idx & 3;
+            *(u32x4*)(vst + s * D + ((piece ^ ((s >> 3) & 3)) * 8)) = vraw[j];
+        }
+    }
+
+    // ---- V^T fragments from the wave's LDS rows: lane (li, grp) takes
+    // channel 16 dt + li of slots 32c + 8 grp + 0..7
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+            const __bf16* src = vst + (32 * c + 8 * grp) * D + (((2 * dt + (li >> 3)) ^ grp) * 8) + (li & 7);
+            bf16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = src[e * D];
+            F.v[c][dt] = v;
+        }
+        const int gam = 4 * c + grp;
+        const int rj = qdiv(gam, L.inv_GPR), c0 = (gam - rj * L.GPR) * 8;
+        F.koff[c] = rj * S + c0;
+        F.rc[c] = (rj << 8) | c0;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();                      // V rows consumed: the area takes K next
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- k: unit-normalise (COSINE), or keep raw and record 1/||k||
+    // (precise COSINE) or the largest ||k|| (DOT); fragments to LDS in
+    // operand order, one 16-byte write per lane and tile
+    bf16x8* kst = (bf16x8*)vst;
+    float kmax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            float kf[8];
+            unpack_bf16x8(kraw[c][t], kf);
+            float ss = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(kf[e], kf[e], ss);
+            ss += __shfl_xor(ss, 16);
+            ss += __shfl_xor(ss, 32);
+            bf16x8 kfrag;
+            if (SIM == SWIN_SIM_COSINE) {
+                const float inv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));   // 1 / max(||k||, 1e-12)
+                if (precise) {
+                    if (grp == 0) kinv[32 * c + 8 * (li >> 2) + (li & 3) + 4 * t] = inv;
+                    kfrag = *(const bf16x8*)&kraw[c][t];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) kf[e] *= inv;
+                    kfrag = pack_bf16x8(kf);
+                }
+            } else {
+                kmax = fmaxf(kmax, ss);
+                kfrag = *(const bf16x8*)&kraw[c][t];
+            }
+            kst[(c * 2 + t) * 64 + lane] = kfrag;
+        }
+    if (SIM == SWIN_SIM_DOT) {
+#pragma unroll
+        for (int off = 16; off > 0; off >>= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, off));
+        kmax = sqrtf(kmax);                               // largest ||k|| of the window
+    }
+    F.k = kst;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- this wave's query tiles, two at a time
+    const int tfirst = part * L.TPW;
+    const int tlast = min(tfirst + L.TPW, L.NQT);
+    for (int t0 = tfirst; t0 < tlast; t0 += 2) {
+        Tile T[2];
+        int qt[2];
+        bool qv[2];
+        u32x4 qraw[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = (t0 + i) * 16 + li;
+            qv[i] = t0 + i < tlast && t < N;
+            qt[i] = qv[i] ? t : 0;
+            const int ri = qdiv(qt[i], L.inv_M), ci = qt[i] - ri * M;
+            qraw[i] = *(const u32x4*)(qg + wg.tok(ri, ci) + grp * 8);
+        }
+        bool any_exact = false, partial = false;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int ri = qdiv(qt[i], L.inv_M), ci = qt[i] - ri * M;
+            float qf[8];
+            unpack_bf16x8(qraw[i], qf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qf[e] = qv[i] ? qf[e] : 0.0f;
+            T[i].qf = pack_bf16x8(qf);
+            float ss = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(qf[e], qf[e], ss);
+            ss += __shfl_xor(ss, 16);
+            ss += __shfl_xor(ss, 32);
+            float spread;
+            if (SIM == SWIN_SIM_COSINE) {
+                T[i].qscale = kLog2e * inv_tau * __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
+                T[i].negm = POS == SWIN_POS_TABLE ? 0.0f : -kLog2e * inv_tau;
+                spread = 2.0f * kLog2e * inv_tau + bias_range;
+            } else {
+                T[i].qscale = kLog2e * 0.17677669529663687f;          // log2(e) / sqrt(32)
+                const float c_i = sqrtf(ss) * kmax * T[i].qscale;
+                T[i].negm = -c_i;
+                spread = 2.0f * c_i + bias_range;
+            }
+            T[i].exact = __any(!(spread <= RANGE_LIMIT)) != 0;
+            any_exact = any_exact || T[i].exact;
+            T[i].mrun = -INFINITY;
+            T[i].qoff = (M - 1 - ri) * S + (M - 1 - ci);
+            T[i].rlo = 0; T[i].rhi = M;
+            int clo = 0, chi = M;
+            if (last_r) { if (ri < M - g.shift) T[i].rhi = M - g.shift; else T[i].rlo = M - g.shift; }
+            if (last_c) { if (ci < M - g.shift) chi = M - g.shift; else clo = M - g.shift; }
+            T[i].cmask = (chi >= 32 ? 0xffffffffu : ((1u << chi) - 1u)) & ~((1u << clo) - 1u);
+            // groups split by a region edge or by padding
+            if (needs_mask) partial = partial || (last_c && ((M - g.shift) & 7)) || (M & 7);
+            T[i].o0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            T[i].o1 = T[i].o0;
+            T[i].ls = T[i].o0;
+        }
+        const int negrow = S * S;
+        if (any_exact || precise)
+            run_pair<SIM, POS, NCH, true, true, true>(F, T, bias2, kinv, negrow, lane, true, precise);
+        else if (needs_mask)
+            run_pair<SIM, POS, NCH, true, false, false>(F, T, bias2, kinv, negrow, lane, partial, false);
+        else
+            run_pair<SIM, POS, NCH, false, false, false>(F, T, bias2, kinv, negrow, lane, false, false);
+
+        // ---- normalise and store: lane holds channels 4 grp..+3 and
+        // 16 + 4 grp..+3 of query li
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (!qv[i]) continue;
+            const int ri = qdiv(qt[i], L.inv_M), ci = qt[i] - ri * M;
+            const float inv = __builtin_amdgcn_rcpf(T[i].ls[0]);
+            uint16_t* dst = og + wg.tok(ri, ci) + grp * 4;
+            *(bf16x4*)dst = pack_bf16x4(T[i].o0[0] * inv, T[i].o0[1] * inv, T[i].o0[2] * inv, T[i].o0[3] * inv);
+            *(bf16x4*)(dst + 16) = pack_bf16x4(T[i].o1[0] * inv, T[i].o1[1] * inv, T[i].o1[2] * inv, T[i].o1[3] * inv);
+        }
+    }
+}
+
+template <int SIM, int POS>
+hipError_t launch_nch(const AttnParams& p, const SmallLayout& L, int nch, int grid, size_t lds, hipStream_t s)
+{
+    auto* fn = nch <= 2 ? attn_small_kernel<SIM, POS, 2>
+             : nch <= 4 ? attn_small_kernel<SIM, POS, 4>
+             : nch <= 6 ? attn_small_kernel<SIM, POS, 6>
+                        : attn_small_kernel<SIM, POS, 8>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    fn<<<grid, WAVES * 64, lds, s>>>(p, L);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_small_supported(const AttnParams& p)
+{
+    const Geometry& g = p.g;
+    const int SR = (g.M + 7) / 8 * 8;
+    return p.dtype == SWIN_DT_BF16 && p.pos != SWIN_POS_ROPE2D && g.d == D && g.M * SR <= 256 &&
+           (int64_t)g.H * g.W * g.C < ((int64_t)1 << 31);
+}
+
+hipError_t launch_attn_small(const AttnParams& p, hipStream_t stream)
+{
+    const Geometry& g = p.g;
+    if (g.nwin == 0) return hipSuccess;
+    SmallLayout L;
+    L.SR = (g.M + 7) / 8 * 8;
+    L.GPR = L.SR / 8;
+    L.NSP = g.M * L.SR;
+    L.NQT = (g.N + 15) / 16;
+    L.TPW = L.NQT > 8 ? 8 : L.NQT;
+    L.parts = (L.NQT + L.TPW - 1) / L.TPW;
+    L.per_head = (g.nwin * L.parts + WAVES - 1) / WAVES * WAVES;
+    L.inv_SR = 1.0f / (float)L.SR;
+    L.inv_M = 1.0f / (float)g.M;
+    L.inv_GPR = 1.0f / (float)L.GPR;
+    const int nch_real = (L.NSP + 31) / 32;
+    const int nch = nch_real <= 2 ? 2 : nch_real <= 4 ? 4 : nch_real <= 6 ? 6 : 8;
+    const int S = 2 * g.M - 1;
+    const int64_t grid = (int64_t)g.heads * L.per_head / WAVES;
+    size_t lds = (size_t)(16 + WAVES * nch * 32) * sizeof(float) + (size_t)WAVES * nch * 32 * D * 2;
+    if (p.pos == SWIN_POS_TABLE) lds += (size_t)((S * S + 8 + 3) / 4 * 4) * sizeof(float);
+    if (p.sim == SWIN_SIM_COSINE) {
+        if (p.pos == SWIN_POS_TABLE) return launch_nch<SWIN_SIM_COSINE, SWIN_POS_TABLE>(p, L, nch, (int)grid, lds, stream);
+        return launch_nch<SWIN_SIM_COSINE, SWIN_POS_NONE>(p, L, nch, (int)grid, lds, stream);
+    }
+    if (p.pos == SWIN_POS_TABLE) return launch_nch<SWIN_SIM_DOT, SWIN_POS_TABLE>(p, L, nch, (int)grid, lds, stream);
+    return launch_nch<SWIN_SIM_DOT, SWIN_POS_NONE>(p, L, nch, (int)grid, lds, stream);
+}
+
+}  // namespace swin

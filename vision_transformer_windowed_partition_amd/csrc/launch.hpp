@@ -31,7 +31,12 @@ hipError_t launch_cpb_table(int M, int heads, int hidden, const float* w1, const
 // fp32 (and any-shape fallback) attention on the vector ALUs.
 hipError_t launch_attn_valu(const AttnParams& p, hipStream_t stream);
 
-// bf16 attention on the matrix cores (d == 32).
+// bf16 attention on the matrix cores (d == 32), any window size.
 hipError_t launch_attn_mfma(const AttnParams& p, hipStream_t stream);
+
+// bf16 attention for windows of at most 256 key slots without rotary
+// positions, keys and values held in registers.
+bool attn_small_supported(const AttnParams& p);
+hipError_t launch_attn_small(const AttnParams& p, hipStream_t stream);
 
 }  // namespace swin

@@ -33,6 +33,8 @@ SMALL = [
     (48, 48, 48, 24, "cyclic", "dot", "none"),         # 2304 tokens per window
     (32, 32, 16, 0, "interleaved", "cosine", "table"),
     (24, 40, 8, 7, "cyclic", "dot", "none"),           # shift M-1
+    (30, 30, 10, 0, "interleaved", "cosine", "none"),  # 10 -> 16 slots per row, 6 key chunks
+    (26, 26, 13, 6, "cyclic", "dot", "table"),         # 208 of 256 slots in use
 ]
 
 

@@ -11,7 +11,9 @@
 //      lane loads 16 contiguous bytes of one key from HBM.
 //   V^T (d x keys): A operand of O^T = V^T P^T; V rows are copied to a
 //      wavefront-private LDS area with contiguous 16-byte writes and read
-//      back as 8 keys of one channel per lane with fixed-offset 2-byte reads.
+//      back transposed by ds_read_b64_tr_b16 (within each 16-lane group,
+//      lane i receives element i%4 of the 4-element vectors addressed by
+//      lanes 4j + i/4, j = 0..3), two reads per 8-key fragment.
 // The score tile leaves the MFMA with each lane holding 8 consecutive key
 // slots of one query, the B-operand layout of P^T, so the softmax runs in
 // registers between the two products; row sums come from a third MFMA
@@ -36,13 +38,41 @@ constexpr int WAVES = 4;
 constexpr float RANGE_LIMIT = 60.0f;
 constexpr float PRECISE_TAU = 0.1f;
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+// Position (in 16-byte pieces) of piece p of V slot s in the wave's LDS rows
+// is p ^ v_swizzle(s): of the transposed reads, the four 32-byte row halves a
+// 16-lane group touches fall in distinct 128-byte bank windows, and the two
+// groups of a half-wavefront in distinct 256-byte windows.
+__device__ __forceinline__ int v_swizzle(int s) { return ((s >> 1) ^ (s >> 3)) & 1 ? 2 : 0; }
+
+// Raw buffer access (gfx9 resource word 3 = 0x00020000: 32-bit data, no
+// swizzle).  A raw load whose offset is at or past the record count returns
+// zeros and a store there is dropped; tensors here stay below 2^31 bytes
+// per image, so kNoLoad is always out of range.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kNoLoad = 0x80000000u;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 load16(Rsrc r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ void store8(Rsrc r, uint32_t off, bf16x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 0);
+}
+
 struct SmallLayout {
-    int SR, GPR, NSP;          // slots per key row (M rounded up to 8), groups per row, real slots
+    int NSP;                   // key slots in use: M rows of M rounded up to 8
     int NQT;                   // query tiles per window-head
     int TPW;                   // query tiles per wavefront item
     int parts;                 // wavefront items per window-head
     int per_head;              // items per head, padded to a multiple of WAVES
-    float inv_SR, inv_M, inv_GPR;
+    float inv_M;
 };
 
 // floor(a / b) for 0 <= a < 2^16, b <= 64, from a float reciprocal: the
@@ -50,22 +80,30 @@ struct SmallLayout {
 // the rounding error of the product.
 __device__ __forceinline__ int qdiv(int a, float inv_b) { return (int)(((float)a + 0.5f) * inv_b); }
 
-// Element offset (within one image, or one window for the WINDOWS layout)
-// of local token (r, c); everything but (r, c) is wave-uniform, no branch:
+// Byte offset (within one image, or one window for the WINDOWS layout) of
+// local token (r, c) is row(r) + col(c); all but (r, c) is wave-uniform:
 // cyclic grid: origin (wr*M + shift, wc*M + shift), steps 1, wrap at H, W;
 // interleaved: origin (wr, wc), steps (H/M, W/M), never wraps;
 // windows tensor: origin 0, steps 1, an M x M "grid".
+// The wrap is min(i, i - H) in unsigned arithmetic; products use the 24-bit
+// multiplier (row and column strides stay below 2^24 bytes).
 struct WinGeo {
-    int r0, c0, rs, cs, Hm, Wm, C;
-    __device__ __forceinline__ int tok(int r, int c) const
+    uint32_t r0, c0, rs, cs, Hm, Wm, rowb, colb;
+    __device__ __forceinline__ uint32_t row(int r) const
     {
-        int gi = r0 + r * rs;
-        gi -= gi >= Hm ? Hm : 0;
-        int gj = c0 + c * cs;
-        gj -= gj >= Wm ? Wm : 0;
-        return (gi * Wm + gj) * C;
+        const uint32_t gi = r0 + __umul24((uint32_t)r, rs);
+        return __umul24(min(gi, gi - Hm), rowb);
     }
+    __device__ __forceinline__ uint32_t col(int c) const
+    {
+        const uint32_t gj = c0 + __umul24((uint32_t)c, cs);
+        return __umul24(min(gj, gj - Wm), colb);
+    }
+    __device__ __forceinline__ uint32_t tok(int r, int c) const { return row(r) + col(c); }
 };
+
+// kNoLoad unless ok (keeps the offset arithmetic unconditional: no branch)
+__device__ __forceinline__ uint32_t masked(uint32_t off, bool ok) { return off | (ok ? 0u : kNoLoad); }
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c)
 {
@@ -193,12 +231,15 @@ template <int SIM, int POS, int NCH>
 __global__ void __launch_bounds__(256)
 attn_small_kernel(AttnParams p, SmallLayout L)
 {
+    // groups of 8 key slots per key row: M <= 8 gives 8 slots per row and
+    // at most 2 chunks of 32, 9 <= M <= 16 gives 16 slots per row
+    constexpr int GPR = NCH <= 2 ? 1 : 2;
     extern __shared__ __attribute__((aligned(16))) float smem_f[];
     const Geometry& g = p.g;
     const int M = g.M, N = g.N, S = 2 * M - 1;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: item math stays scalar
     const int grp = lane >> 4;       // 16-lane group: k-range of the operands
     const int li = lane & 15;        // row / column inside a 16 x 16 tile
 
@@ -251,63 +292,82 @@ attn_small_kernel(AttnParams p, SmallLayout L)
     const int nW = g.nwr * g.nwc;
     const int bimg = win / nW, wl = win - bimg * nW;
     const int wr = wl / g.nwc, wc = wl - wr * g.nwc;
-    wg.C = g.C;
+    wg.colb = (uint32_t)g.C * 2u;
     int64_t base;
+    int span;                                             // elements of the image (or window)
     if (g.layout == SWIN_LAYOUT_WINDOWS) {
-        base = (int64_t)win * N * g.C;
+        span = N * g.C;
+        base = (int64_t)win * span;
         wg.r0 = wg.c0 = 0; wg.rs = wg.cs = 1; wg.Hm = wg.Wm = M;
     } else {
-        base = (int64_t)bimg * g.H * g.W * g.C;
+        span = g.H * g.W * g.C;
+        base = (int64_t)bimg * span;
         wg.Hm = g.H; wg.Wm = g.W;
         if (g.part == SWIN_PART_INTERLEAVED) { wg.r0 = wr; wg.c0 = wc; wg.rs = g.nwr; wg.cs = g.nwc; }
         else { wg.r0 = wr * M + g.shift; wg.c0 = wc * M + g.shift; wg.rs = wg.cs = 1; }
     }
+    wg.rowb = wg.Wm * wg.colb;
     const bool cyc_shift = g.part == SWIN_PART_CYCLIC && g.shift > 0;
     const bool last_r = cyc_shift && wr == g.nwr - 1;
     const bool last_c = cyc_shift && wc == g.nwc - 1;
-    const bool padded = L.SR != M || NCH * 32 != L.NSP;
+    const bool padded = 8 * GPR != M || NCH * 32 != L.NSP;
     const bool needs_mask = last_r || last_c || padded;
-    const uint16_t* qg = (const uint16_t*)p.q + base + h * D;
-    const uint16_t* kg = (const uint16_t*)p.k + base + h * D;
-    const uint16_t* vg = (const uint16_t*)p.v + base + h * D;
-    uint16_t* og = (uint16_t*)p.out + base + h * D;
+    // one buffer resource per tensor, starting at channel h*D of this image
+    // (window); byte offsets are 32-bit and an offset of kNoLoad reads zero
+    const uint32_t bytes = (uint32_t)(span - h * D) * 2u;
+    const Rsrc qr = make_rsrc((const uint16_t*)p.q + base + h * D, bytes);
+    const Rsrc kr = make_rsrc((const uint16_t*)p.k + base + h * D, bytes);
+    const Rsrc vr = make_rsrc((const uint16_t*)p.v + base + h * D, bytes);
+    const Rsrc orr = make_rsrc((const uint16_t*)p.out + base + h * D, bytes);
     const bool precise = SIM == SWIN_SIM_COSINE && tau_eff < PRECISE_TAU;
 
     // ---- K fragments: tile A of chunk c holds slots 32c + 8(r/4) + r%4,
     // tile B the next 4 of each group of 8, so that S^T hands this lane slots
     // 32c + 8 grp + 0..7.  V rows go to LDS (16 bytes per lane, contiguous).
+    // Key slot 8 gam + x is token (gam / GPR, 8 (gam % GPR) + x): a lane's
+    // key row advances by a fixed step per chunk, its column stays put.
     Frags<NCH> F;
     u32x4 kraw[NCH][2];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c)
+    {
+        const int rl = (li >> 2) / GPR;
+        uint32_t colk[2];
+        bool cok[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const int s = 32 * c + 8 * (li >> 2) + (li & 3) + 4 * t;
-            const int rj = qdiv(s, L.inv_SR), cj = s - rj * L.SR;
-            kraw[c][t] = u32x4{0u, 0u, 0u, 0u};
-            if (rj < M && cj < M) kraw[c][t] = *(const u32x4*)(kg + wg.tok(rj, cj) + grp * 8);
+            const int cj = 8 * ((li >> 2) % GPR) + (li & 3) + 4 * t;
+            colk[t] = wg.col(cj) + 16u * grp;
+            cok[t] = cj < M;
         }
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int rj = (4 / GPR) * c + rl;
+            const uint32_t rowk = wg.row(rj);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) kraw[c][t] = load16(kr, masked(rowk + colk[t], cok[t] && rj < M));
+        }
+    }
     {
         u32x4 vraw[2 * NCH];
+        const int rl = (lane >> 5) / GPR;
+        const int cj = 8 * ((lane >> 5) % GPR) + ((lane >> 2) & 7);
+        const uint32_t colv = wg.col(cj) + 16u * (lane & 3);
+        const bool cok = cj < M;
 #pragma unroll
         for (int j = 0; j < 2 * NCH; ++j) {               // piece j*64 + lane: slot (.)/4, channels 8*(. % 4)
-            const int idx = j * 64 + lane;
-            const int s = idx >> 2, piece = idx & 3;
-            const int rj = qdiv(s, L.inv_SR), cj = s - rj * L.SR;
-            vraw[j] = u32x4{0u, 0u, 0u, 0u};
-            if (rj < M && cj < M) vraw[j] = *(const u32x4*)(vg + wg.tok(rj, cj) + piece * 8);
+            const int rj = (2 / GPR) * j + rl;
+            vraw[j] = load16(vr, masked(wg.row(rj) + colv, cok && rj < M));
         }
-        // 16-byte piece p of slot s sits at piece position p ^ (s/8 mod 4), so
-        // that the transposed reads of the four lane groups hit different banks
 #pragma unroll
         for (int j = 0; j < 2 * NCH; ++j) {
             const int idx = j * 64 + lane, s = idx >> 2, piece = idx & 3;
-            *(u32x4*)(vst + s * D + ((piece ^ ((s >> 3) & 3)) * 8)) = vraw[j];
+            *(u32x4*)(vst + s * D + ((piece ^ v_swizzle(s)) * 8)) = vraw[j];
         }
     }
 
     // ---- V^T fragments from the wave's LDS rows: lane (li, grp) takes
-    // channel 16 dt + li of slots 32c + 8 grp + 0..7
+    // channel 16 dt + li of slots 32c + 8 grp + 0..7.  Transposed read h
+    // covers slots +4h..4h+3: lane li addresses slot + 4h + li/4, channels
+    // 16 dt + 4 (li%4) .. +3, and receives channel 16 dt + li of all four.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -315,14 +375,19 @@ attn_small_kernel(AttnParams p, SmallLayout L)
     for (int c = 0; c < NCH; ++c) {
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
-            const __bf16* src = vst + (32 * c + 8 * grp) * D + (((2 * dt + (li >> 3)) ^ grp) * 8) + (li & 7);
-            bf16x8 v;
+            i16x4 half[2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = src[e * D];
-            F.v[c][dt] = v;
+            for (int h = 0; h < 2; ++h) {
+                const int s = 32 * c + 8 * grp + 4 * h + (li >> 2);
+                const int m = li & 3;
+                const __bf16* src = vst + s * D + (((2 * dt + (m >> 1)) ^ v_swizzle(s)) * 8) + 4 * (m & 1);
+                half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)src);
+            }
+            const i16x8 v = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+            F.v[c][dt] = __builtin_bit_cast(bf16x8, v);
         }
         const int gam = 4 * c + grp;
-        const int rj = qdiv(gam, L.inv_GPR), c0 = (gam - rj * L.GPR) * 8;
+        const int rj = gam / GPR, c0 = (gam % GPR) * 8;
         F.koff[c] = rj * S + c0;
         F.rc[c] = (rj << 8) | c0;
     }
@@ -387,7 +452,7 @@ attn_small_kernel(AttnParams p, SmallLayout L)
             qv[i] = t0 + i < tlast && t < N;
             qt[i] = qv[i] ? t : 0;
             const int ri = qdiv(qt[i], L.inv_M), ci = qt[i] - ri * M;
-            qraw[i] = *(const u32x4*)(qg + wg.tok(ri, ci) + grp * 8);
+            qraw[i] = load16(qr, masked(wg.tok(ri, ci) + 16u * grp, qv[i]));
         }
         bool any_exact = false, partial = false;
 #pragma unroll
@@ -395,8 +460,6 @@ attn_small_kernel(AttnParams p, SmallLayout L)
             const int ri = qdiv(qt[i], L.inv_M), ci = qt[i] - ri * M;
             float qf[8];
             unpack_bf16x8(qraw[i], qf);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qf[e] = qv[i] ? qf[e] : 0.0f;
             T[i].qf = pack_bf16x8(qf);
             float ss = 0.0f;
 #pragma unroll
@@ -441,12 +504,11 @@ attn_small_kernel(AttnParams p, SmallLayout L)
         // 16 + 4 grp..+3 of query li
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            if (!qv[i]) continue;
             const int ri = qdiv(qt[i], L.inv_M), ci = qt[i] - ri * M;
             const float inv = __builtin_amdgcn_rcpf(T[i].ls[0]);
-            uint16_t* dst = og + wg.tok(ri, ci) + grp * 4;
-            *(bf16x4*)dst = pack_bf16x4(T[i].o0[0] * inv, T[i].o0[1] * inv, T[i].o0[2] * inv, T[i].o0[3] * inv);
-            *(bf16x4*)(dst + 16) = pack_bf16x4(T[i].o1[0] * inv, T[i].o1[1] * inv, T[i].o1[2] * inv, T[i].o1[3] * inv);
+            const uint32_t off = masked(wg.tok(ri, ci) + 8u * grp, qv[i]);
+            store8(orr, off, pack_bf16x4(T[i].o0[0] * inv, T[i].o0[1] * inv, T[i].o0[2] * inv, T[i].o0[3] * inv));
+            store8(orr, off + 32u, pack_bf16x4(T[i].o1[0] * inv, T[i].o1[1] * inv, T[i].o1[2] * inv, T[i].o1[3] * inv));
         }
     }
 }
@@ -455,7 +517,6 @@ template <int SIM, int POS>
 hipError_t launch_nch(const AttnParams& p, const SmallLayout& L, int nch, int grid, size_t lds, hipStream_t s)
 {
     auto* fn = nch <= 2 ? attn_small_kernel<SIM, POS, 2>
-             : nch <= 4 ? attn_small_kernel<SIM, POS, 4>
              : nch <= 6 ? attn_small_kernel<SIM, POS, 6>
                         : attn_small_kernel<SIM, POS, 8>;
     if (lds > 64 * 1024) {
@@ -473,7 +534,8 @@ bool attn_small_supported(const AttnParams& p)
     const Geometry& g = p.g;
     const int SR = (g.M + 7) / 8 * 8;
     return p.dtype == SWIN_DT_BF16 && p.pos != SWIN_POS_ROPE2D && g.d == D && g.M * SR <= 256 &&
-           (int64_t)g.H * g.W * g.C < ((int64_t)1 << 31);
+           (int64_t)g.H * g.W * g.C * 2 < ((int64_t)1 << 31) &&    // byte offsets of one image fit 31 bits
+           (int64_t)g.W * g.C * 2 < ((int64_t)1 << 24);            // row stride fits the 24-bit multiplier
 }
 
 hipError_t launch_attn_small(const AttnParams& p, hipStream_t stream)
@@ -481,18 +543,14 @@ hipError_t launch_attn_small(const AttnParams& p, hipStream_t stream)
     const Geometry& g = p.g;
     if (g.nwin == 0) return hipSuccess;
     SmallLayout L;
-    L.SR = (g.M + 7) / 8 * 8;
-    L.GPR = L.SR / 8;
-    L.NSP = g.M * L.SR;
+    L.NSP = g.M * ((g.M + 7) / 8 * 8);
     L.NQT = (g.N + 15) / 16;
     L.TPW = L.NQT > 8 ? 8 : L.NQT;
     L.parts = (L.NQT + L.TPW - 1) / L.TPW;
     L.per_head = (g.nwin * L.parts + WAVES - 1) / WAVES * WAVES;
-    L.inv_SR = 1.0f / (float)L.SR;
     L.inv_M = 1.0f / (float)g.M;
-    L.inv_GPR = 1.0f / (float)L.GPR;
     const int nch_real = (L.NSP + 31) / 32;
-    const int nch = nch_real <= 2 ? 2 : nch_real <= 4 ? 4 : nch_real <= 6 ? 6 : 8;
+    const int nch = nch_real <= 2 ? 2 : nch_real <= 6 ? 6 : 8;      // M <= 8, 9-12, 13-16
     const int S = 2 * g.M - 1;
     const int64_t grid = (int64_t)g.heads * L.per_head / WAVES;
     size_t lds = (size_t)(16 + WAVES * nch * 32) * sizeof(float) + (size_t)WAVES * nch * 32 * D * 2;

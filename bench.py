@@ -11,13 +11,16 @@ torch.cuda.synchronize() calls.  Cold cache by default: the steps rotate
 through enough distinct input/output sets (> 512 MB in all) that the 256 MB
 Infinity Cache cannot hold one set between its uses; --warm reuses one set.
 The attention kernel's own duration is taken from HIP events recorded on the
-launch stream around every timed launch.
+launch stream around every timed launch; the events are created with
+hipEventDisableSystemFence (timing only), so recording them adds no cache
+writeback or invalidation to the interval.
 
 Prints ONE JSON line.  `value` is tokens/s over the whole job.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -34,33 +37,79 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, TFLOP/s
 MALL_BYTES = 256 * 2 ** 20
-KERNEL_SOURCES = ["attn_mfma.hip", "attn_valu.hip", "common.hpp"]
+KERNEL_SOURCE = {"attn_small_kernel": "attn_small.hip", "attn_mfma_kernel": "attn_mfma.hip",
+                 "attn_valu_kernel": "attn_valu.hip"}
 
 
-def kernel_sha() -> str:
+def kernel_sha(kernel: str) -> str:
+    """Hash of the sources that define `kernel` (its file and the shared headers)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (KERNEL_SOURCE[kernel], "common.hpp", "launch.hpp"):
         with open(os.path.join(ROOT, "vision_transformer_windowed_partition_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(wl_name: str):
+def load_traffic(wl_name: str, kernel: str):
     """HBM bytes per launch from committed rocprofv3 --pmc counts, if they
-    were taken on the current kernel sources; else None."""
+    were taken on the current sources of `kernel`; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{wl_name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_sha") != kernel_sha():
+    if t.get("kernel") != kernel or t.get("kernel_sha") != kernel_sha(kernel):
         return None
-    return t.get("hbm_bytes_per_launch")
+    return round(t.get("hbm_bytes_per_launch"))
+
+
+class HipTimer:
+    """Pairs of HIP events on one stream, created with
+    hipEventDisableSystemFence.  Uses the HIP runtime the process already
+    loaded (torch's), found by its soname."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n: int, stream_handle: int):
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip, self.stream = hip, ctypes.c_void_p(stream_handle)
+        self.ev = []
+        for _ in range(2 * n):
+            e = ctypes.c_void_p()
+            self._ok(hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE), "create")
+            self.ev.append(e)
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"hipEvent{what} failed: {rc}")
+
+    def record(self, i: int, end: bool):
+        self._ok(self.hip.hipEventRecord(self.ev[2 * i + int(end)], self.stream), "Record")
+
+    def elapsed_ms(self) -> list[float]:
+        out = []
+        for i in range(len(self.ev) // 2):
+            self._ok(self.hip.hipEventSynchronize(self.ev[2 * i + 1]), "Synchronize")
+            ms = ctypes.c_float()
+            self._ok(self.hip.hipEventElapsedTime(ctypes.byref(ms), self.ev[2 * i], self.ev[2 * i + 1]),
+                     "ElapsedTime")
+            out.append(ms.value)
+        return out
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
 
 
 def cpu_baseline(wl, x, budget_s: float):
     """The fp64 oracle on a bounded sample of the same workload, on the host's
-    cores, in tokens/s."""
+    cores, in tokens/s: evenly spaced windows sized to about budget_s of wall
+    time, the whole sample repeated while it takes less than half of it."""
     import numpy as np
     import torch
 
@@ -83,13 +132,17 @@ def cpu_baseline(wl, x, budget_s: float):
     per_win = (time.perf_counter() - t0) / len(probe)
     n = int(min(nwin, max(len(probe), budget_s / max(per_win, 1e-9))))
     wins = np.unique(np.linspace(0, nwin - 1, num=n, dtype=np.int64))
-    t0 = time.perf_counter()
-    oracle.window_attn(q, k, v, windows=wins, **kw)
-    dt = time.perf_counter() - t0 + t_table
-    tokens = len(wins) * wl.N
+    reps, dt = 0, t_table
+    while reps == 0 or dt < 0.5 * budget_s:
+        t0 = time.perf_counter()
+        oracle.window_attn(q, k, v, windows=wins, **kw)
+        dt += time.perf_counter() - t0
+        reps += 1
+    tokens = reps * len(wins) * wl.N
     sample = (f"all {nwin} windows" if len(wins) == nwin else
               f"{len(wins)} of {nwin} windows, evenly spaced over the batch") + \
-             f" ({tokens} tokens, {dt:.1f} s incl. the CPB table)"
+             (f", {reps} passes" if reps > 1 else "") + \
+             f" ({tokens} tokens, {dt:.1f} s incl. one CPB table)"
     return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
             "sample": sample, "cpu": oracle.cpu_model()}
 
@@ -102,9 +155,11 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", type=int, default=1, help="index into synth.WORKLOADS (1 = headline)")
     ap.add_argument("--warm", action="store_true", help="reuse one input set (cache-warm)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=8.0, help="seconds of oracle wall time")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle wall time")
     ap.add_argument("--calib-copy", action="store_true",
-                    help="also run a plain 1 GiB device copy (counter calibration)")
+                    help="also run copies of known size for HBM-counter calibration: y = -x over "
+                         "2^28 fp32 (whole lines), then an interleaved window gather and its "
+                         "scatter of a 16x512x512x32 bf16 grid (64-byte pieces), 3 launches each")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -135,40 +190,49 @@ def main(argv=None) -> int:
                              partition=wl.partition, sim=wl.sim, pos=wl.pos, dtype=q.dtype,
                              rope_base=wl.rope_base)
     stream = torch.cuda.current_stream(dev)
+    kernel = binding.swin_window_attn_kernel(desc)
 
-    def step(i, ev=None):
+    def step(i, timed=None):
         q, k, v, o = sets[i % nsets]
         tab = None
         if wl.pos == "table":
             tab = binding.swin_cpb_table(wl.M, par["w1"], par["b1"], par["w2"], par["b2"], out=table,
                                          stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
+        if timed is not None:
+            timer.record(timed, False)
         binding.swin_window_attn_fwd(q, k, v, heads=wl.heads, M=wl.M, desc=desc, tau=par["tau"],
                                      table=tab, out=o, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+        if timed is not None:
+            timer.record(timed, True)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    timer = HipTimer(args.steps, stream.cuda_stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i, i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_ms = timer.elapsed_ms()
+    timer.close()
     kern_avg = sum(kern_ms) / len(kern_ms)
 
     if args.calib_copy:
-        a = torch.empty(2 ** 28, dtype=torch.float32, device=dev)
+        a = torch.zeros(2 ** 28, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
-        for _ in range(5):
-            b.copy_(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        del a, b
+        # each token's 64 bytes sits 4 KiB from the next token of its window
+        g = torch.zeros((16, 512, 512, 32), dtype=torch.bfloat16, device=dev)
+        w = binding.swin_window_partition(g, 8, 0, "interleaved")
+        for _ in range(3):
+            binding.swin_window_partition(g, 8, 0, "interleaved", out=w)
+        for _ in range(3):
+            binding.swin_window_reverse(w, 16, 512, 512, 8, 0, "interleaved", out=g)
         torch.cuda.synchronize()
 
     ms_per_step = wall * 1e3 / args.steps
@@ -186,9 +250,11 @@ def main(argv=None) -> int:
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak_tf, "unit": "TFLOP/s",
                 "frac": round(tflops / peak_tf, 4)}
-    roof["traffic"] = load_traffic(wl.name)
-    roof["kernel"] = "attn_mfma_kernel" if wl.dtype == "bf16" else "attn_valu_kernel"
+    roof["traffic"] = load_traffic(wl.name, kernel)
+    roof["kernel"] = kernel
     roof["kernel_ms"] = round(kern_avg, 5)
+    roof["kernel_ms_median"] = round(sorted(kern_ms)[len(kern_ms) // 2], 5)
+    roof["kernel_ms_min"] = round(min(kern_ms), 5)
     roof["alg_bytes_per_launch"] = alg_bytes
     roof["alg_flops_per_launch"] = wl.flops
 

@@ -138,6 +138,17 @@ int swin_window_attn_fwd(const swin_attn_desc* desc, const void* q, const void* 
                          const void* v, void* out, const float* tau, const float* table,
                          const float* rope_freqs, void* stream);
 
+/* Name of the kernel that swin_window_attn_fwd launches for desc (static
+ * storage), for matching profiler output:
+ *   "attn_valu_kernel"  SWIN_DT_F32;
+ *   "attn_small_kernel" SWIN_DT_BF16, M * roundup8(M) <= 256 key slots,
+ *                       no rotary positions;
+ *   "attn_mfma_kernel"  every other SWIN_DT_BF16 case.
+ * Only the descriptor is read; rope_base is not required (the caller may
+ * pass rope_freqs).  NULL if swin_window_attn_fwd would reject the
+ * descriptor itself; swin_last_error() then says why.  Enqueues nothing. */
+const char* swin_window_attn_kernel(const swin_attn_desc* desc);
+
 /* Text for a status code (static storage). */
 const char* swin_status_string(int status);
 

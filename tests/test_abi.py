@@ -32,7 +32,8 @@ def L():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["swin_cpb_table", "swin_window_partition", "swin_window_reverse",
-                                           "swin_window_attn_fwd", "swin_status_string",
+                                           "swin_window_attn_fwd", "swin_window_attn_kernel",
+                                           "swin_status_string",
                                            "swin_last_error", "swin_version"])
 
 
@@ -99,6 +100,27 @@ def test_attn_rejects_bad_pointers(L):
     assert _attn(L, d, q=ctypes.c_void_p(0x10008)) == SWIN_EINVAL   # misaligned
     assert _attn(L, d, out=ctypes.c_void_p(0x10000 + 64)) == SWIN_EINVAL   # out overlaps q
     assert _attn(L, _desc(pos=2, rope_base=0.0)) == SWIN_EINVAL
+
+
+def test_kernel_query_names_the_dispatch(L):
+    """Which kernel each workload shape reaches: fp32 -> vector ALUs; bf16
+    windows of at most 256 key slots (M rounded up to 8 per key row) without
+    rotary positions -> the register-resident kernel; the rest -> the
+    LDS-staged MFMA kernel."""
+    from vision_transformer_windowed_partition_amd import synth
+    want = ["attn_valu_kernel", "attn_small_kernel", "attn_small_kernel", "attn_mfma_kernel",
+            "attn_mfma_kernel"]
+    for wl, name in zip(synth.WORKLOADS, want):
+        d = binding.make_desc(B=wl.B, H=wl.H, W=wl.W, C=wl.C, heads=wl.heads, M=wl.M, shift=wl.shift,
+                              partition=wl.partition, sim=wl.sim, pos=wl.pos,
+                              dtype=binding.DTYPE_BY_NAME[wl.dtype])
+        assert binding.swin_window_attn_kernel(d) == name, wl.name
+    assert binding.swin_window_attn_kernel(_desc(M=12, H=24, W=24, dtype=1)) == "attn_small_kernel"  # 192 slots
+    assert binding.swin_window_attn_kernel(_desc(M=17, H=34, W=34, dtype=1, shift=0)) == "attn_mfma_kernel"
+    assert binding.swin_window_attn_kernel(_desc(M=8, dtype=1, pos=2)) == "attn_mfma_kernel"
+    assert L.swin_window_attn_kernel(ctypes.byref(_desc(shift=8))) is None
+    assert "shift" in binding.swin_last_error()
+    assert L.swin_window_attn_kernel(None) is None
 
 
 def test_attn_empty_batch_is_a_no_op(L):

@@ -21,6 +21,7 @@ PARTITION = {"cyclic": 0, "interleaved": 1}
 SIM = {"cosine": 0, "dot": 1}
 POS = {"none": 0, "table": 1, "rope2d": 2}
 DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+DTYPE_BY_NAME = {"f32": 0, "bf16": 1}
 LAYOUT = {"grid": 0, "windows": 1}
 CPB_PAPER = 0
 
@@ -56,6 +57,8 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = [vp, vp] + [i32] * 8 + [vp]
         L.swin_window_attn_fwd.restype = i32
         L.swin_window_attn_fwd.argtypes = [ctypes.POINTER(SwinAttnDesc)] + [vp] * 8
+        L.swin_window_attn_kernel.restype = ctypes.c_char_p
+        L.swin_window_attn_kernel.argtypes = [ctypes.POINTER(SwinAttnDesc)]
         L.swin_status_string.restype = ctypes.c_char_p
         L.swin_status_string.argtypes = [i32]
         L.swin_last_error.restype = ctypes.c_char_p
@@ -172,3 +175,12 @@ def swin_window_attn_fwd(q, k, v, *, heads: int, M: int, shift: int = 0, partiti
     _check(lib().swin_window_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                       _ptr(tau), _ptr(table), _ptr(rope_freqs), _stream(q, stream)))
     return out
+
+
+def swin_window_attn_kernel(desc: SwinAttnDesc) -> str:
+    """Name of the kernel swin_window_attn_fwd launches for desc (for
+    matching profiler output).  Raises SwinError if the descriptor is rejected."""
+    name = lib().swin_window_attn_kernel(ctypes.byref(desc))
+    if name is None:
+        raise SwinError(SWIN_EINVAL, swin_last_error())
+    return name.decode()

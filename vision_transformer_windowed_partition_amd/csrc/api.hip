@@ -137,9 +137,12 @@ int swin_window_reverse(const void* xw, void* x, int32_t B, int32_t H, int32_t W
     return window_copy(xw, x, B, H, W, C, M, shift, partition, dtype, stream, false);
 }
 
-int swin_window_attn_fwd(const swin_attn_desc* d, const void* q, const void* k, const void* v,
-                         void* out, const float* tau, const float* table, const float* rope_freqs,
-                         void* stream)
+}  // extern "C"
+
+namespace {
+
+// Checks of the descriptor alone (no pointers); SWIN_OK or the failure.
+int check_desc(const swin_attn_desc* d, bool rope_freqs_given)
 {
     if (!d) return fail(SWIN_EINVAL, "NULL descriptor");
     int st = check_grid(d->B, d->H, d->W, d->C, d->M, d->shift, d->partition);
@@ -153,11 +156,41 @@ int swin_window_attn_fwd(const swin_attn_desc* d, const void* q, const void* k, 
     if (d->layout != SWIN_LAYOUT_GRID && d->layout != SWIN_LAYOUT_WINDOWS)
         return fail(SWIN_EINVAL, "unknown layout %d", d->layout);
     if (!(d->tau_min > 0.0f) || !(d->tau_min < 3.0e38f)) return fail(SWIN_EINVAL, "tau_min must be positive and finite");
-    if (d->pos == SWIN_POS_ROPE2D && !rope_freqs && !(d->rope_base > 0.0f && d->rope_base < 3.0e38f))
+    if (d->pos == SWIN_POS_ROPE2D && !rope_freqs_given && !(d->rope_base > 0.0f && d->rope_base < 3.0e38f))
         return fail(SWIN_EINVAL, "rope_base must be positive and finite");
     if (d->C / d->heads != 32)
         return fail(SWIN_EUNSUPPORTED, "head dim %d: only 32 is built", d->C / d->heads);
     if (d->M > 64) return fail(SWIN_EUNSUPPORTED, "M=%d: windows above 64 are not built", d->M);
+    return SWIN_OK;
+}
+
+swin::AttnParams params_of(const swin_attn_desc* d)
+{
+    swin::AttnParams p{};
+    p.g = make_geometry(d->B, d->H, d->W, d->C, d->heads, d->M, d->shift, d->partition, d->layout);
+    p.sim = d->sim; p.pos = d->pos; p.dtype = d->dtype;
+    p.tau_min = d->tau_min; p.rope_base = d->rope_base;
+    return p;
+}
+
+enum class Kernel { VALU, SMALL, MFMA };
+
+Kernel kernel_for(const swin::AttnParams& p)
+{
+    if (p.dtype == SWIN_DT_F32) return Kernel::VALU;
+    return swin::attn_small_supported(p) ? Kernel::SMALL : Kernel::MFMA;
+}
+
+}  // namespace
+
+extern "C" {
+
+int swin_window_attn_fwd(const swin_attn_desc* d, const void* q, const void* k, const void* v,
+                         void* out, const float* tau, const float* table, const float* rope_freqs,
+                         void* stream)
+{
+    int st = check_desc(d, rope_freqs != nullptr);
+    if (st) return st;
     const size_t es = d->dtype == SWIN_DT_F32 ? 4 : 2;
     const size_t bytes = (size_t)d->B * d->H * d->W * d->C * es;
     if (bytes == 0) return SWIN_OK;
@@ -169,16 +202,26 @@ int swin_window_attn_fwd(const swin_attn_desc* d, const void* q, const void* k, 
     if (d->sim == SWIN_SIM_COSINE && !tau) return fail(SWIN_EINVAL, "COSINE needs tau");
     if (d->pos == SWIN_POS_TABLE && !table) return fail(SWIN_EINVAL, "POS_TABLE needs a table");
 
-    swin::AttnParams p;
-    p.g = make_geometry(d->B, d->H, d->W, d->C, d->heads, d->M, d->shift, d->partition, d->layout);
-    p.sim = d->sim; p.pos = d->pos; p.dtype = d->dtype;
-    p.tau_min = d->tau_min; p.rope_base = d->rope_base;
+    swin::AttnParams p = params_of(d);
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.tau = tau; p.table = table; p.rope_freqs = rope_freqs;
-    hipError_t e = d->dtype == SWIN_DT_F32   ? swin::launch_attn_valu(p, (hipStream_t)stream)
-                 : swin::attn_small_supported(p) ? swin::launch_attn_small(p, (hipStream_t)stream)
-                                                 : swin::launch_attn_mfma(p, (hipStream_t)stream);
+    hipError_t e;
+    switch (kernel_for(p)) {
+    case Kernel::VALU: e = swin::launch_attn_valu(p, (hipStream_t)stream); break;
+    case Kernel::SMALL: e = swin::launch_attn_small(p, (hipStream_t)stream); break;
+    default: e = swin::launch_attn_mfma(p, (hipStream_t)stream); break;
+    }
     return hip_status(e, "swin_window_attn_fwd launch");
+}
+
+const char* swin_window_attn_kernel(const swin_attn_desc* d)
+{
+    if (check_desc(d, true) != SWIN_OK) return nullptr;
+    switch (kernel_for(params_of(d))) {
+    case Kernel::VALU: return "attn_valu_kernel";
+    case Kernel::SMALL: return "attn_small_kernel";
+    default: return "attn_mfma_kernel";
+    }
 }
 
 }  // extern "C"

@@ -67,7 +67,9 @@ struct Layout {                // derived sizes, identical for every workgroup
     int GPR;                   // 8-slot groups per key row
     int NQT;                   // query tiles per window-head
     int nqb;                   // query blocks per window-head
-    int total;                 // items: (head, window, query block)
+    int nblk;                  // key blocks per window-head (unsplit)
+    int total;                 // workgroups with work
+    int P;                     // workgroups per XCD slot
 };
 
 // Per-wavefront query-tile state.
@@ -218,9 +220,7 @@ __device__ __forceinline__ void run_fast(const Stage& st, Tiles<NQ>& T, int s0, 
 }
 
 // General chunk loop: any mask, hi + lo operands, and per tile either the
-// static shift or the online normaliser.  Rare; it walks one tile at a time
-// (re-reading the fragments from LDS) to stay within the fast path's
-// register budget.
+// static shift or the online normaliser.
 template <int SIM, int POS, int NQ>
 __device__ __forceinline__ void run_general(const Stage& st, Tiles<NQ>& T, int s0, int cnt,
                                             int lane, int grp, int GPR, int SR, bool needs_mask,
@@ -228,56 +228,56 @@ __device__ __forceinline__ void run_general(const Stage& st, Tiles<NQ>& T, int s
 {
     const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
     const bf16x8 ones = ones8();
+    GroupWalk gw(s0, grp, GPR, SR);
     const int nch = cnt >> 5;
+    for (int c = 0; c < nch; ++c, gw.next()) {
+        const bf16x8 ka = st.kfrag[(c * 2 + 0) * 64 + lane];
+        const bf16x8 kb = st.kfrag[(c * 2 + 1) * 64 + lane];
+        bf16x8 ka_lo = ka, kb_lo = kb;
+        if (split_k) {
+            ka_lo = st.kfrag_lo[(c * 2 + 0) * 64 + lane];
+            kb_lo = st.kfrag_lo[(c * 2 + 1) * 64 + lane];
+        }
+        const bf16x8 va = st.vfrag[(c * 2 + 0) * 64 + lane];
+        const bf16x8 vb = st.vfrag[(c * 2 + 1) * 64 + lane];
+        const int koff = gw.rj * st.S + gw.c0;
 #pragma unroll
-    for (int qi = 0; qi < NQ; ++qi) {
-        GroupWalk gw(s0, grp, GPR, SR);
-        const bf16x8 qf = T.qf[qi], qf_lo = T.qf_lo[qi];
-        const float qscale = T.qscale[qi], negm = T.negm[qi];
-        const int qoff = T.qoff[qi];
-        const bool exact = T.exact[qi];
-        float mrun = T.mrun[qi];
-        f32x4 o0 = T.o0[qi], o1 = T.o1[qi], ls = T.ls[qi];
-        for (int c = 0; c < nch; ++c, gw.next()) {
+        for (int qi = 0; qi < NQ; ++qi) {
             uint32_t bits = 0xffu;
             if (needs_mask) {
                 bits = group_bits(T, qi, gw.rj, gw.c0);
                 if (!__any(bits != 0u)) continue;
             }
-            const bf16x8 ka = st.kfrag[(c * 2 + 0) * 64 + lane];
-            const bf16x8 kb = st.kfrag[(c * 2 + 1) * 64 + lane];
-            f32x4 sa = mfma(ka, qf, zero4);
-            f32x4 sb = mfma(kb, qf, zero4);
-            if (split_q) {
-                sa = mfma(ka, qf_lo, sa);
-                sb = mfma(kb, qf_lo, sb);
-            }
+            f32x4 sa = mfma(ka, T.qf[qi], zero4);
+            f32x4 sb = mfma(kb, T.qf[qi], zero4);
             if (split_k) {
-                const bf16x8 ka_lo = st.kfrag_lo[(c * 2 + 0) * 64 + lane];
-                const bf16x8 kb_lo = st.kfrag_lo[(c * 2 + 1) * 64 + lane];
-                sa = mfma(ka_lo, qf, sa);
-                sb = mfma(kb_lo, qf, sb);
-                if (split_q) {
-                    sa = mfma(ka_lo, qf_lo, sa);
-                    sb = mfma(kb_lo, qf_lo, sb);
+                sa = mfma(ka_lo, T.qf[qi], sa);
+                sb = mfma(kb_lo, T.qf[qi], sb);
+            }
+            if (split_q) {
+                sa = mfma(ka, T.qf_lo[qi], sa);
+                sb = mfma(kb, T.qf_lo[qi], sb);
+                if (split_k) {
+                    sa = mfma(ka_lo, T.qf_lo[qi], sa);
+                    sb = mfma(kb_lo, T.qf_lo[qi], sb);
                 }
             }
             const float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
             float add[8];
             if (POS == SWIN_POS_TABLE) {
-                const float* bp = st.bias2 + (bits == 0u ? st.negrow : gw.rj * st.S + gw.c0 + qoff);
+                const float* bp = st.bias2 + (bits == 0u ? st.negrow : koff + T.qoff[qi]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) add[e] = SIM == SWIN_SIM_COSINE ? bp[e] : bp[e] + negm;
+                for (int e = 0; e < 8; ++e) add[e] = SIM == SWIN_SIM_COSINE ? bp[e] : bp[e] + T.negm[qi];
             } else {
-                const float a = bits == 0u ? -INFINITY : negm;
+                const float a = bits == 0u ? -INFINITY : T.negm[qi];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) add[e] = a;
             }
             const bool partial = needs_mask && __any(bits != 0u && bits != 0xffu);
             float pr[8];
-            if (!exact) {
+            if (!T.exact[qi]) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(x[e], qscale, add[e]));
+                for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(x[e], T.qscale[qi], add[e]));
                 if (partial) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) pr[e] = (bits >> e) & 1u ? pr[e] : 0.0f;
@@ -287,42 +287,45 @@ __device__ __forceinline__ void run_general(const Stage& st, Tiles<NQ>& T, int s
                 float cm = -INFINITY;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    xs[e] = fmaf(x[e], qscale, add[e]);
+                    xs[e] = fmaf(x[e], T.qscale[qi], add[e]);
                     if (partial) xs[e] = (bits >> e) & 1u ? xs[e] : -INFINITY;
                     cm = fmaxf(cm, xs[e]);
                 }
                 cm = fmaxf(cm, __shfl_xor(cm, 16));
                 cm = fmaxf(cm, __shfl_xor(cm, 32));
-                const float mnew = fmaxf(mrun, cm);
+                const float mnew = fmaxf(T.mrun[qi], cm);
                 const float mref = mnew == -INFINITY ? 0.0f : mnew;
-                const float alpha = __builtin_amdgcn_exp2f(mrun - mref);
-                o0 *= alpha; o1 *= alpha; ls *= alpha;
+                const float alpha = __builtin_amdgcn_exp2f(T.mrun[qi] - mref);
+                T.o0[qi] *= alpha; T.o1[qi] *= alpha; T.ls[qi] *= alpha;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(xs[e] - mref);
-                mrun = mnew;
+                T.mrun[qi] = mnew;
             }
             const bf16x8 pb = pack_bf16x8(pr);
-            const bf16x8 va = st.vfrag[(c * 2 + 0) * 64 + lane];
-            const bf16x8 vb = st.vfrag[(c * 2 + 1) * 64 + lane];
-            o0 = mfma(va, pb, o0);
-            o1 = mfma(vb, pb, o1);
-            ls = mfma(ones, pb, ls);
+            T.o0[qi] = mfma(va, pb, T.o0[qi]);
+            T.o1[qi] = mfma(vb, pb, T.o1[qi]);
+            T.ls[qi] = mfma(ones, pb, T.ls[qi]);
         }
-        T.mrun[qi] = mrun;
-        T.o0[qi] = o0; T.o1[qi] = o1; T.ls[qi] = ls;
     }
 }
 
 template <int SIM, int POS, int NQ>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 attn_mfma_kernel(AttnParams p, Layout L)
 {
-    // Kernels that may carry k^ (or a rotated q, k) as hi + lo bf16 pairs
-    // keep an LDS area for the lo fragments.
-    constexpr bool CAN_SPLIT = SIM == SWIN_SIM_COSINE || POS == SWIN_POS_ROPE2D;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const Geometry& g = p.g;
     const int M = g.M, N = g.N, S = 2 * M - 1;
+
+    // XCD-aware order: consecutive blockIdx land on different XCDs, so give
+    // each XCD a contiguous range of work ids; the heads and query blocks of
+    // one window then share that XCD's L2.
+    const int work = (blockIdx.x & 7) * L.P + (blockIdx.x >> 3);
+    if (work >= L.total) return;
+    const int qb = work % L.nqb;
+    const int wh = work / L.nqb;
+    const int h = wh % g.heads;
+    const int win = wh / g.heads;
 
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;
@@ -332,12 +335,11 @@ attn_mfma_kernel(AttnParams p, Layout L)
     const int grp = lane >> 4;       // 16-lane group: k-range of the operands
     const int li = lane & 15;        // row / column inside a 16 x 16 tile
 
-    bf16x8* kfrag = (bf16x8*)smem;                                   // [KB/32][2][64]
-    bf16x8* kfrag_lo = kfrag + KB * 4;                               // [KB/32][2][64] (CAN_SPLIT)
-    bf16x8* vfrag = kfrag_lo + (CAN_SPLIT ? KB * 4 : 0);             // [KB/32][2][64]
-    float* red = (float*)(vfrag + KB * 4);                           // [32] reductions
-    float* bias2 = red + 32;                                         // [S*S + 8]   (TABLE)
-    float* rcs = bias2 + (POS == SWIN_POS_TABLE ? S * S + 8 : 0);    // [M][2][8] (ROPE2D)
+    bf16x8* kfrag = (bf16x8*)smem;                       // [KB/32][2][64]
+    bf16x8* vfrag = kfrag + KB * 4;                      // [KB/32][2][64]
+    float* red = (float*)(vfrag + KB * 4);               // [16] reductions
+    float* bias2 = red + 16;                             // [S*S + 8]   (TABLE)
+    float* rcs = bias2 + (POS == SWIN_POS_TABLE ? S * S + 8 : 0);   // [M][2][8] (ROPE2D)
     float* rsn = rcs + (POS == SWIN_POS_ROPE2D ? M * 16 : 0);
 
     const uint16_t* qg = (const uint16_t*)p.q;
@@ -345,36 +347,42 @@ attn_mfma_kernel(AttnParams p, Layout L)
     const uint16_t* vg = (const uint16_t*)p.v;
     uint16_t* og = (uint16_t*)p.out;
 
-    // Persistent workgroup: a contiguous range of items.  Items run head
-    // by head, then window, then query block, so a workgroup reloads its
-    // bias table rarely and meets the query blocks of one window-head back
-    // to back (their keys come from L2).
-    const int it_begin = (int)((int64_t)blockIdx.x * L.total / gridDim.x);
-    const int it_end = (int)((int64_t)(blockIdx.x + 1) * L.total / gridDim.x);
-    if (it_begin >= it_end) return;
-    const int kbs = min(KB, nthr);                       // key slots per stage: 4 pieces per thread
+    const int nW = g.nwr * g.nwc;
+    const int wloc = win % nW;
+    const int wr = wloc / g.nwc, wc = wloc % g.nwc;
+    const bool shifted = g.part == SWIN_PART_CYCLIC && g.shift > 0 &&
+                         (wr == g.nwr - 1 || wc == g.nwc - 1);
+    const bool needs_mask = shifted || L.SR != M || L.NSP != M * L.SR;
+    const float tau_eff = SIM == SWIN_SIM_COSINE ? fmaxf(p.tau[h], p.tau_min) : 1.0f;
 
-    auto decode = [&](int item, int& h, int& win, int& qb) {
-        qb = item % L.nqb;
-        const int hw = item / L.nqb;
-        win = hw % g.nwin;
-        h = hw / g.nwin;
-    };
-    auto tile_token = [&](int qb, int qi, int& t) {      // first tile of the wave, query of this lane
-        const int qt0 = qb * L.NQT / L.nqb, qt1 = (qb + 1) * L.NQT / L.nqb;
-        const int tile = qt0 + wave * NQ + qi;
-        t = tile * 16 + li;
-        return tile < qt1 && t < N;
-    };
+    // ---- this wavefront's query tiles
+    const int qt0 = qb * L.NQT / L.nqb, qt1 = (qb + 1) * L.NQT / L.nqb;
+    const int my0 = qt0 + wave * NQ;
+    const int nq = max(0, min(NQ, qt1 - my0));            // wave-uniform
 
-    // ---- global loads, issued one stage ahead of their use
+    // Every global load of the set-up is issued before its first use, so a
+    // workgroup waits for one memory round trip, not one per item.
+    // (1) this wave's query fragments (tiles past its share, or past N,
+    //     read token 0 and are zeroed later; they are never stored)
+    u32x4 qraw[NQ];
+    int qri[NQ], qci[NQ];
+    bool qvalid[NQ];
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi) {
+        const int t = (my0 + qi) * 16 + li;
+        qvalid[qi] = qi < nq && t < N;
+        const int tc = qvalid[qi] ? t : 0;
+        qri[qi] = tc / M;
+        qci[qi] = tc - qri[qi] * M;
+        qraw[qi] = *(const u32x4*)(qg + token_offset(g, win, qri[qi], qci[qi]) + h * D + grp * 8);
+    }
+
+    // (2) key/value staging, SB items of 16 bytes per thread per batch
     u32x4 kraw[SB], vraw[SB];
-    auto kv_load = [&](int h, int win, int s0, int cnt) {
-        int tid_o = tid;
-        asm volatile("" : "+v"(tid_o));
+    auto kv_load = [&](int s0, int cnt, int b0) {
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
-            const int it = j * nthr + tid_o;
+            const int it = b0 + j * nthr + tid;
             kraw[j] = u32x4{0u, 0u, 0u, 0u};
             vraw[j] = kraw[j];
             if (it < cnt * 4) {
@@ -388,27 +396,14 @@ attn_mfma_kernel(AttnParams p, Layout L)
             }
         }
     };
-    u32x4 qraw[NQ];
-    auto q_load = [&](int h, int win, int qb) {
-#pragma unroll
-        for (int qi = 0; qi < NQ; ++qi) {
-            int t;
-            const bool v = tile_token(qb, qi, t);
-            const int tc = v ? t : 0;
-            const int r = tc / M;
-            qraw[qi] = *(const u32x4*)(qg + token_offset(g, win, r, tc - r * M) + h * D + grp * 8);
-        }
-    };
-
-    // turn the loaded stage into MFMA fragments: k rotated (ROPE2D), unit
-    // normalised (COSINE), rounded to bf16 (and, when split, its remainder);
-    // v scattered transposed.  DOT tracks the stage's largest key norm.
-    auto kv_store = [&](int s0, int cnt, bool write_lo, float* kmax_slot) {
-        int tid_o = tid;
-        asm volatile("" : "+v"(tid_o));              // recompute addresses per stage
+    // turn the loaded batch into MFMA fragments: k rotated (ROPE2D), unit
+    // normalised (COSINE), rounded to bf16 (and its remainder when split);
+    // v scattered transposed.
+    auto kv_store = [&](int s0, int cnt, int b0, bool split_k, bool track_kmax) {
+        bf16x8* kfrag_lo = kfrag + (KB / 2) * 4;
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
-            const int it = j * nthr + tid_o;
+            const int it = b0 + j * nthr + tid;
             if (it >= cnt * 4) continue;                   // whole wavefronts drop out
             const int sl = it >> 2, piece = it & 3;
             const int s = s0 + sl;
@@ -436,14 +431,14 @@ attn_mfma_kernel(AttnParams p, Layout L)
                 const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) kf[e] *= inv;
-            } else if (piece == 0) {
-                atomicMax((unsigned int*)kmax_slot, __float_as_uint(sqrtf(ss)));
+            } else if (track_kmax && piece == 0) {
+                atomicMax((unsigned int*)&red[8], __float_as_uint(sqrtf(ss)));
             }
             const int c = sl >> 5, u = sl & 31, gg = u >> 3, e8 = u & 7;
             const int kidx = (c * 2 + (e8 >> 2)) * 64 + piece * 16 + gg * 4 + (e8 & 3);
             const bf16x8 khi = pack_bf16x8(kf);
             kfrag[kidx] = khi;
-            if (CAN_SPLIT && write_lo) {
+            if (split_k) {
                 float lo[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) lo[e] = kf[e] - (float)khi[e];
@@ -459,254 +454,234 @@ attn_mfma_kernel(AttnParams p, Layout L)
         }
     };
 
-    // per-head tables: bias (reversed so that consecutive keys read
-    // consecutive floats, scaled by log2 e, shifted by its max) and rotary
-    // cos/sin.  The caller has passed a barrier since their last reader.
+    // Block size: halved when k^ is carried as hi + lo.  The split for
+    // COSINE depends only on tau and is known now; for DOT + ROPE2D it waits
+    // for the norm pre-pass, which also runs before any staging.
+    constexpr bool kPrepassRope = SIM == SWIN_SIM_DOT && POS == SWIN_POS_ROPE2D;
+    const bool prepass = SIM == SWIN_SIM_DOT && (L.nblk > 1 || kPrepassRope);
+    const bool cos_split = SIM == SWIN_SIM_COSINE && tau_eff < SPLIT_TAU;
+    if (!prepass) kv_load(0, min(cos_split ? KB / 2 : KB, L.NSP), 0);
+
+    // (3) tables: bias (reversed so that consecutive keys read consecutive
+    // floats, scaled by log2 e, shifted by its max), rotary cos/sin.
     float bias_range = 0.0f;
-    auto load_tables = [&](int h, float tau_eff) {
-        if (POS == SWIN_POS_TABLE) {
-            float mx = -INFINITY, mn = INFINITY;
-            for (int i0 = 0; i0 < S * S; i0 += TB * nthr) {
-                float tv[TB];
+    if (POS == SWIN_POS_TABLE) {
+        float mx = -INFINITY, mn = INFINITY;
+        for (int i0 = 0; i0 < S * S; i0 += TB * nthr) {
+            float tv[TB];
 #pragma unroll
-                for (int j = 0; j < TB; ++j) {
-                    const int i = i0 + j * nthr + tid;
-                    tv[j] = i < S * S ? p.table[(size_t)(S * S - 1 - i) * g.heads + h] * kLog2e : 0.0f;
+            for (int j = 0; j < TB; ++j) {
+                const int i = i0 + j * nthr + tid;
+                tv[j] = i < S * S ? p.table[(size_t)(S * S - 1 - i) * g.heads + h] * kLog2e : 0.0f;
+            }
+#pragma unroll
+            for (int j = 0; j < TB; ++j) {
+                const int i = i0 + j * nthr + tid;
+                if (i < S * S) {
+                    bias2[i] = tv[j];
+                    mx = fmaxf(mx, tv[j]);
+                    mn = fminf(mn, tv[j]);
                 }
+            }
+        }
+        if (tid < 8) bias2[S * S + tid] = -INFINITY;
 #pragma unroll
-                for (int j = 0; j < TB; ++j) {
-                    const int i = i0 + j * nthr + tid;
-                    if (i < S * S) {
-                        bias2[i] = tv[j];
-                        mx = fmaxf(mx, tv[j]);
-                        mn = fminf(mn, tv[j]);
+        for (int off = 32; off > 0; off >>= 1) {
+            mx = fmaxf(mx, __shfl_xor(mx, off));
+            mn = fminf(mn, __shfl_xor(mn, off));
+        }
+        if (lane == 0) { red[wave] = mx; red[4 + wave] = mn; }
+        __syncthreads();
+        mx = red[0]; mn = red[4];
+        for (int w = 1; w < nwaves; ++w) { mx = fmaxf(mx, red[w]); mn = fminf(mn, red[4 + w]); }
+        bias_range = mx - mn;
+        const float shift = SIM == SWIN_SIM_COSINE ? mx + kLog2e / tau_eff : mx;
+        for (int i = tid; i < S * S; i += nthr) bias2[i] -= shift;
+    }
+    if (POS == SWIN_POS_ROPE2D) {
+        for (int i = tid; i < M * 16; i += nthr) {
+            const int k = i & 7, half = (i >> 3) & 1, pos = i >> 4;
+            const double th = p.rope_freqs
+                ? (double)p.rope_freqs[((size_t)h * 2 + half) * 8 + k]
+                : pow((double)p.rope_base, -(double)k / 8.0);
+            double s_, c_;
+            sincos((double)pos * th, &s_, &c_);
+            rcs[i] = (float)c_;
+            rsn[i] = (float)s_;
+        }
+    }
+    if (tid == 0) { red[8] = 0.0f; red[9] = 0.0f; }       // max key / query norm (DOT)
+    __syncthreads();
+
+    // (4) DOT over several key blocks, or after rotation: the largest key
+    // norm (and, with rotation, query norm) before any block is staged;
+    // loads in batches of SB per thread.
+    if (prepass) {
+        float kmax = 0.0f, qmax = 0.0f;
+        const int qend = min(qt1 * 16, N) - qt0 * 16;
+        const int nitems = (N + (kPrepassRope ? max(qend, 0) : 0)) * 4;
+        for (int b0 = 0; b0 < nitems; b0 += SB * nthr) {
+            u32x4 w[SB];
+#pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                const int it = b0 + j * nthr + tid;
+                w[j] = u32x4{0u, 0u, 0u, 0u};
+                if (it < nitems) {
+                    const bool isq = it >= N * 4;
+                    const int t = isq ? qt0 * 16 + ((it - N * 4) >> 2) : it >> 2;
+                    const int rj = t / M, cj = t - rj * M;
+                    w[j] = *(const u32x4*)((isq ? qg : kg) + token_offset(g, win, rj, cj) + h * D + (it & 3) * 8);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                const int it = b0 + j * nthr + tid;
+                float f[8];
+                unpack_bf16x8(w[j], f);
+                float ss = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+                ss += __shfl_xor(ss, 1);
+                ss += __shfl_xor(ss, 2);
+                if (it >= N * 4) qmax = fmaxf(qmax, sqrtf(ss));
+                else             kmax = fmaxf(kmax, sqrtf(ss));
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            kmax = fmaxf(kmax, __shfl_xor(kmax, off));
+            qmax = fmaxf(qmax, __shfl_xor(qmax, off));
+        }
+        if (lane == 0) {
+            atomicMax((unsigned int*)&red[8], __float_as_uint(kmax));
+            atomicMax((unsigned int*)&red[9], __float_as_uint(qmax));
+        }
+        __syncthreads();
+    }
+    bool split_k = cos_split, split_q = cos_split && POS == SWIN_POS_ROPE2D;
+    if (kPrepassRope) split_k = split_q = red[8] * red[9] * (kLog2e / sqrtf((float)D)) > SPLIT_BOUND;
+    const int kbs = split_k ? KB / 2 : KB;               // slots per staged block
+
+    Tiles<NQ> T;
+    bool general = false;
+    const Stage st = {kfrag, kfrag + (KB / 2) * 4, vfrag, bias2, S, S * S};
+
+    // ---- block 0 (its first batch is already in flight unless a pre-pass ran)
+    {
+        const int cnt = min(kbs, L.NSP);
+        if (prepass) kv_load(0, cnt, 0);
+        kv_store(0, cnt, 0, split_k, !prepass);
+        for (int b0 = SB * nthr; b0 < cnt * 4; b0 += SB * nthr) {
+            kv_load(0, cnt, b0);
+            kv_store(0, cnt, b0, split_k, !prepass);
+        }
+    }
+    __syncthreads();
+
+    for (int s0 = 0; s0 < L.NSP; s0 += kbs) {
+        const int cnt = min(kbs, L.NSP - s0);
+        if (s0 > 0) {
+            __syncthreads();                              // previous block consumed
+            for (int b0 = 0; b0 < cnt * 4; b0 += SB * nthr) {
+                kv_load(s0, cnt, b0);
+                kv_store(s0, cnt, b0, split_k, !prepass);
+            }
+            __syncthreads();
+        }
+
+        // ---- per query tile set-up, once the first block (and the key
+        // norm bound) is in place.
+        if (s0 == 0) {
+            const float kmax = red[8];
+#pragma unroll
+            for (int qi = 0; qi < NQ; ++qi) {
+                float qv[8];
+                unpack_bf16x8(qraw[qi], qv);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qv[e] = qvalid[qi] ? qv[e] : 0.0f;
+                if (POS == SWIN_POS_ROPE2D) {
+                    const int half = grp >> 1, pos = half ? qci[qi] : qri[qi];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int k = (grp & 1) * 4 + j;
+                        const float co = rcs[(pos * 2 + half) * 8 + k], si = rsn[(pos * 2 + half) * 8 + k];
+                        const float x0 = qv[2 * j], x1 = qv[2 * j + 1];
+                        qv[2 * j] = x0 * co - x1 * si;
+                        qv[2 * j + 1] = x0 * si + x1 * co;
                     }
                 }
-            }
-            if (tid < 8) bias2[S * S + tid] = -INFINITY;
+                T.qf[qi] = pack_bf16x8(qv);
+                float lo[8];
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) {
-                mx = fmaxf(mx, __shfl_xor(mx, off));
-                mn = fminf(mn, __shfl_xor(mn, off));
+                for (int e = 0; e < 8; ++e) lo[e] = qv[e] - (float)T.qf[qi][e];
+                T.qf_lo[qi] = pack_bf16x8(lo);
+                float ss = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss = fmaf(qv[e], qv[e], ss);
+                ss += __shfl_xor(ss, 16);
+                ss += __shfl_xor(ss, 32);
+                const float qn = sqrtf(ss);
+                float spread;
+                if (SIM == SWIN_SIM_COSINE) {
+                    T.qscale[qi] = kLog2e / (tau_eff * fmaxf(qn, 1e-12f));
+                    T.negm[qi] = POS == SWIN_POS_TABLE ? 0.0f : -kLog2e / tau_eff;
+                    spread = 2.0f * kLog2e / tau_eff + bias_range;
+                } else {
+                    T.qscale[qi] = kLog2e / sqrtf((float)D);
+                    const float c_i = qn * kmax * T.qscale[qi];
+                    T.negm[qi] = -c_i;
+                    spread = 2.0f * c_i + bias_range;
+                }
+                T.exact[qi] = __any(!(spread <= RANGE_LIMIT)) != 0;
+                general = general || T.exact[qi];
+                T.qoff[qi] = (M - 1 - qri[qi]) * S + (M - 1 - qci[qi]);
+                T.rlo[qi] = 0; T.rhi[qi] = M;
+                int clo = 0, chi = M;
+                if (shifted) {
+                    region_interval(wr, g.nwr, M, g.shift, qri[qi], T.rlo[qi], T.rhi[qi]);
+                    region_interval(wc, g.nwc, M, g.shift, qci[qi], clo, chi);
+                }
+                const uint64_t hi_bits = chi >= 64 ? ~0ull : ((1ull << chi) - 1ull);
+                T.cmask[qi] = hi_bits & ~((1ull << clo) - 1ull);
+                T.mrun[qi] = -INFINITY;
+                T.o0[qi] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                T.o1[qi] = T.o0[qi];
+                T.ls[qi] = T.o0[qi];
             }
-            if (lane == 0) { red[wave] = mx; red[8 + wave] = mn; }
-            __syncthreads();
-            mx = red[0]; mn = red[8];
-            for (int w = 1; w < nwaves; ++w) { mx = fmaxf(mx, red[w]); mn = fminf(mn, red[8 + w]); }
-            bias_range = mx - mn;
-            const float shift = SIM == SWIN_SIM_COSINE ? mx + kLog2e / tau_eff : mx;
-            for (int i = tid; i < S * S; i += nthr) bias2[i] -= shift;
+            general = general || split_k || split_q;
         }
-        if (POS == SWIN_POS_ROPE2D) {
-            for (int i = tid; i < M * 16; i += nthr) {
-                const int k = i & 7, half = (i >> 3) & 1, pos = i >> 4;
-                const double th = p.rope_freqs
-                    ? (double)p.rope_freqs[((size_t)h * 2 + half) * 8 + k]
-                    : pow((double)p.rope_base, -(double)k / 8.0);
-                double s_, c_;
-                sincos((double)pos * th, &s_, &c_);
-                rcs[i] = (float)c_;
-                rsn[i] = (float)s_;
-            }
-        }
-    };
 
-    if (tid < 2) red[16 + tid] = 0.0f;                    // per-stage max key norm slots (DOT)
-    int h_tab = -1;
-    int stage = 0;
-    {
-        int h, win, qb;
-        decode(it_begin, h, win, qb);
-        q_load(h, win, qb);
-        kv_load(h, win, 0, min(kbs, L.NSP));
+        // ---- the key chunks of this block
+        if (nq > 0) {
+            if (general)
+                run_general<SIM, POS, NQ>(st, T, s0, cnt, lane, grp, L.GPR, L.SR, needs_mask, split_k, split_q);
+            else if (needs_mask)
+                run_fast<SIM, POS, NQ, true>(st, T, s0, cnt, lane, grp, L.GPR, L.SR);
+            else
+                run_fast<SIM, POS, NQ, false>(st, T, s0, cnt, lane, grp, L.GPR, L.SR);
+        }
     }
 
-    for (int item = it_begin; item < it_end; ++item) {
-        // lane-derived values are recomputed per item rather than kept live
-        // across the whole persistent loop
-        int lane = tid & 63;
-        asm volatile("" : "+v"(lane));
-        const int grp = lane >> 4, li = lane & 15;
-        int h, win, qb;
-        decode(item, h, win, qb);
-        const int nW = g.nwr * g.nwc;
-        const int wloc = win % nW;
-        const int wr = wloc / g.nwc, wc = wloc % g.nwc;
-        const bool shifted = g.part == SWIN_PART_CYCLIC && g.shift > 0 &&
-                             (wr == g.nwr - 1 || wc == g.nwc - 1);
-        const bool needs_mask = shifted || L.SR != M || L.NSP != M * L.SR;
-        const float tau_eff = SIM == SWIN_SIM_COSINE ? fmaxf(p.tau[h], p.tau_min) : 1.0f;
-        const bool cos_split = SIM == SWIN_SIM_COSINE && tau_eff < SPLIT_TAU;
-        const bool write_lo = cos_split || POS == SWIN_POS_ROPE2D;
-        int qt0 = qb * L.NQT / L.nqb;
-        const int nq = max(0, min(NQ, (qb + 1) * L.NQT / L.nqb - (qt0 + wave * NQ)));   // wave-uniform
-
-        Tiles<NQ> T;
-        float qn[NQ];
-        float kseen = 0.0f, qmax = 0.0f;
-        bool qvalid[NQ];
-        int qtok[NQ];
-
-        for (int s0 = 0; s0 < L.NSP; s0 += kbs, ++stage) {
-            const int cnt = min(kbs, L.NSP - s0);
-            __syncthreads();                                  // LDS of the previous stage consumed
-            if (s0 == 0 && h != h_tab) {
-                load_tables(h, tau_eff);
-                h_tab = h;
-                __syncthreads();                              // tables in place before the transform
-            }
-            float* kslot = red + 16 + (stage & 1);
-            kv_store(s0, cnt, write_lo, kslot);
-            __syncthreads();
-            if (tid == 0) red[16 + ((stage + 1) & 1)] = 0.0f;  // the next stage's slot (last read a stage ago)
-            const float kmax_b = SIM == SWIN_SIM_DOT ? *kslot : 0.0f;
-
-            // prefetch the next stage: this item's next key block, or the
-            // next item's first
-            if (s0 + kbs < L.NSP) {
-                kv_load(h, win, s0 + kbs, min(kbs, L.NSP - s0 - kbs));
-            } else if (item + 1 < it_end) {
-                int h2, w2, q2;
-                decode(item + 1, h2, w2, q2);
-                kv_load(h2, w2, 0, min(kbs, L.NSP));
-            }
-
-            if (s0 == 0) {
-                // ---- query tiles of this wave: fragments, scales, masks
+    // ---- normalise and write back to the query tokens' grid positions
 #pragma unroll
-                for (int qi = 0; qi < NQ; ++qi) {
-                    int t;
-                    qvalid[qi] = tile_token(qb, qi, t) && qi < nq;
-                    qtok[qi] = qvalid[qi] ? t : 0;
-                    const int ri = qtok[qi] / M, ci = qtok[qi] - (qtok[qi] / M) * M;
-                    float qv[8];
-                    unpack_bf16x8(qraw[qi], qv);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) qv[e] = qvalid[qi] ? qv[e] : 0.0f;
-                    if (POS == SWIN_POS_ROPE2D) {
-                        const int half = grp >> 1, pos = half ? ci : ri;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int k = (grp & 1) * 4 + j;
-                            const float co = rcs[(pos * 2 + half) * 8 + k], si = rsn[(pos * 2 + half) * 8 + k];
-                            const float x0 = qv[2 * j], x1 = qv[2 * j + 1];
-                            qv[2 * j] = x0 * co - x1 * si;
-                            qv[2 * j + 1] = x0 * si + x1 * co;
-                        }
-                    }
-                    T.qf[qi] = pack_bf16x8(qv);
-                    float lo[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) lo[e] = qv[e] - (float)T.qf[qi][e];
-                    T.qf_lo[qi] = pack_bf16x8(lo);
-                    float ss = 0.0f;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) ss = fmaf(qv[e], qv[e], ss);
-                    ss += __shfl_xor(ss, 16);
-                    ss += __shfl_xor(ss, 32);
-                    qn[qi] = sqrtf(ss);
-                    qmax = fmaxf(qmax, qn[qi]);
-                    if (SIM == SWIN_SIM_COSINE) {
-                        T.qscale[qi] = kLog2e / (tau_eff * fmaxf(qn[qi], 1e-12f));
-                        T.negm[qi] = POS == SWIN_POS_TABLE ? 0.0f : -kLog2e / tau_eff;
-                        T.exact[qi] = !(2.0f * kLog2e / tau_eff + bias_range <= RANGE_LIMIT);
-                    } else {
-                        T.qscale[qi] = kLog2e / sqrtf((float)D);
-                        T.negm[qi] = 0.0f;                    // raised with the key norms seen
-                        T.exact[qi] = false;
-                    }
-                    T.qoff[qi] = (M - 1 - ri) * S + (M - 1 - ci);
-                    T.rlo[qi] = 0; T.rhi[qi] = M;
-                    int clo = 0, chi = M;
-                    if (shifted) {
-                        region_interval(wr, g.nwr, M, g.shift, ri, T.rlo[qi], T.rhi[qi]);
-                        region_interval(wc, g.nwc, M, g.shift, ci, clo, chi);
-                    }
-                    const uint64_t hi_bits = chi >= 64 ? ~0ull : ((1ull << chi) - 1ull);
-                    T.cmask[qi] = hi_bits & ~((1ull << clo) - 1ull);
-                    T.mrun[qi] = 0.0f;
-                    T.o0[qi] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                    T.o1[qi] = T.o0[qi];
-                    T.ls[qi] = T.o0[qi];
-                }
-#pragma unroll
-                for (int off = 32; off > 0; off >>= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
-                // the next item's query fragments
-                if (item + 1 < it_end) {
-                    int h2, w2, q2;
-                    decode(item + 1, h2, w2, q2);
-                    q_load(h2, w2, q2);
-                }
-            }
-
-            // ---- DOT: raise the Cauchy-Schwarz shift to the largest key
-            // norm seen so far.  A tile whose spread would pass the limit
-            // keeps its shift and continues with the running maximum.
-            if (SIM == SWIN_SIM_DOT && kmax_b > kseen) {
-                kseen = kmax_b;
-#pragma unroll
-                for (int qi = 0; qi < NQ; ++qi) {
-                    if (T.exact[qi]) continue;
-                    const float c_new = qn[qi] * kseen * T.qscale[qi];
-                    if (__any(!(2.0f * c_new + bias_range <= RANGE_LIMIT))) {
-                        T.exact[qi] = true;                   // accumulated so far with shift -negm: running max 0
-                    } else {
-                        const float f = __builtin_amdgcn_exp2f(-c_new - T.negm[qi]);   // 2^(c_old - c_new)
-                        T.o0[qi] *= f; T.o1[qi] *= f; T.ls[qi] *= f;
-                        T.negm[qi] = -c_new;
-                    }
-                }
-            }
-            bool any_exact = false;
-#pragma unroll
-            for (int qi = 0; qi < NQ; ++qi) any_exact = any_exact || T.exact[qi];
-            bool split_k = cos_split, split_q = cos_split && POS == SWIN_POS_ROPE2D;
-            if (SIM == SWIN_SIM_DOT && POS == SWIN_POS_ROPE2D)
-                split_k = split_q = qmax * kseen * (kLog2e / sqrtf((float)D)) > SPLIT_BOUND;
-            const bool general = any_exact || split_k || split_q;
-            const Stage st = {kfrag, kfrag_lo, vfrag, bias2, S, S * S};
-
-            if (nq > 0) {
-                if (general)
-                    run_general<SIM, POS, NQ>(st, T, s0, cnt, lane, grp, L.GPR, L.SR, needs_mask, split_k, split_q);
-                else if (needs_mask)
-                    run_fast<SIM, POS, NQ, true>(st, T, s0, cnt, lane, grp, L.GPR, L.SR);
-                else
-                    run_fast<SIM, POS, NQ, false>(st, T, s0, cnt, lane, grp, L.GPR, L.SR);
-            }
-        }
-
-        // ---- normalise and write back to the query tokens' grid positions
-#pragma unroll
-        for (int qi = 0; qi < NQ; ++qi) {
-            if (!qvalid[qi]) continue;
-            const int ri = qtok[qi] / M, ci = qtok[qi] - (qtok[qi] / M) * M;
-            const float inv = 1.0f / T.ls[qi][0];
-            uint16_t* dst = og + token_offset(g, win, ri, ci) + h * D + grp * 4;
-            *(bf16x4*)dst = pack_bf16x4(T.o0[qi][0] * inv, T.o0[qi][1] * inv, T.o0[qi][2] * inv, T.o0[qi][3] * inv);
-            *(bf16x4*)(dst + 16) = pack_bf16x4(T.o1[qi][0] * inv, T.o1[qi][1] * inv, T.o1[qi][2] * inv, T.o1[qi][3] * inv);
-        }
+    for (int qi = 0; qi < NQ; ++qi) {
+        if (!qvalid[qi]) continue;
+        const float inv = 1.0f / T.ls[qi][0];
+        uint16_t* dst = og + token_offset(g, win, qri[qi], qci[qi]) + h * D + grp * 4;
+        *(bf16x4*)dst = pack_bf16x4(T.o0[qi][0] * inv, T.o0[qi][1] * inv, T.o0[qi][2] * inv, T.o0[qi][3] * inv);
+        *(bf16x4*)(dst + 16) = pack_bf16x4(T.o1[qi][0] * inv, T.o1[qi][1] * inv, T.o1[qi][2] * inv, T.o1[qi][3] * inv);
     }
 }
 
 template <int SIM, int POS>
-hipError_t launch_nq(const AttnParams& p, Layout L, int nq, int threads, size_t lds, hipStream_t s)
+hipError_t launch_nq(const AttnParams& p, const Layout& L, int nq, int threads, size_t lds, hipStream_t s)
 {
     auto* fn = nq == 1 ? attn_mfma_kernel<SIM, POS, 1> : attn_mfma_kernel<SIM, POS, 2>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    // one resident wave of workgroups: as many as fit on every CU at once
-    int dev = 0, cus = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)fn, threads, lds);
-    if (e != hipSuccess) return e;
-    if (per_cu < 1) per_cu = 1;
-    const int64_t resident = (int64_t)cus * per_cu;
-    const int grid = (int)(L.total < resident ? L.total : resident);
-    fn<<<grid, threads, lds, s>>>(p, L);
+    fn<<<8 * L.P, threads, lds, s>>>(p, L);
     return hipGetLastError();
 }
 
@@ -732,16 +707,17 @@ hipError_t launch_attn_mfma(const AttnParams& p, hipStream_t stream)
     L.GPR = L.SR / 8;
     L.NQT = (g.N + 15) / 16;
     L.nqb = (L.NQT + QT_MAX * MAX_WAVES - 1) / (QT_MAX * MAX_WAVES);
+    L.nblk = (L.NSP + KB - 1) / KB;
     const int64_t total = (int64_t)g.nwin * g.heads * L.nqb;
     L.total = (int)total;
+    L.P = (int)((total + 7) / 8);
     // tiles per query block (at most), waves per workgroup, tiles per wave
     const int per_block = (L.NQT + L.nqb - 1) / L.nqb;
     int nwaves = (per_block + QT_MAX - 1) / QT_MAX;
     if (nwaves > MAX_WAVES) nwaves = MAX_WAVES;
     const int nq = (per_block + nwaves - 1) / nwaves;
     const int S = 2 * g.M - 1;
-    const bool can_split = p.sim == SWIN_SIM_COSINE || p.pos == SWIN_POS_ROPE2D;
-    size_t lds = (size_t)KB * 4 * sizeof(bf16x8) * (can_split ? 3 : 2) + 32 * sizeof(float);
+    size_t lds = (size_t)KB * 4 * sizeof(bf16x8) * 2 + 16 * sizeof(float);
     if (p.pos == SWIN_POS_TABLE) lds += (size_t)(S * S + 8) * sizeof(float);
     if (p.pos == SWIN_POS_ROPE2D) lds += (size_t)g.M * 32 * sizeof(float);
     if (p.sim == SWIN_SIM_COSINE) return launch_pos<SWIN_SIM_COSINE>(p, L, nq, 64 * nwaves, lds, stream);

@@ -1,0 +1,163 @@
+"""Summaries of rocprofv3 output for the attention kernels.
+
+Reads the CSV files rocprofv3 writes (``-f csv``): ``*_kernel_stats.csv``
+from ``--kernel-trace --stats`` and ``*_counter_collection.csv`` from
+``--pmc``.  Writes a short text summary and the measured HBM traffic per
+launch, which bench.py reports next to the algorithmic bytes.
+
+HBM traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are taken in two
+separate ``--pmc`` runs of the same command; each is scaled by what the same
+counter reads for a plain copy of a known size whose accesses have the same
+granularity as the kernel's.  bench.py ``--calib-copy`` runs two kinds:
+  * whole 128-byte lines: y = -x over 2^28 fp32 (1 GiB read, 1 GiB written);
+  * isolated 64-byte pieces: the library's interleaved window gather of a
+    16x512x512x32 bf16 grid (256 MiB; every token's 64 bytes read on its
+    own), then the matching scatter (64-byte pieces written), 3 launches each.
+The attention kernels read and write each token's head slice (32 bf16 = 64
+bytes) apart from its neighbours', so their counts take the 64-byte factors;
+the whole-line factors are reported beside them.
+
+Usage (on the files a GPU run wrote):
+    python -m vision_transformer_windowed_partition_amd.profiling \\
+        --stats DIR --fetch DIR --write DIR --kernel attn_small_kernel \\
+        --workload NAME --bench-json FILE --command-stats "..." \\
+        --command-fetch "..." --command-write "..." --out-md F.md --out-json F.json
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import statistics
+
+# torch's elementwise kernel (names truncated by rocprofv3 -T); the zero fill
+# of the source comes first, the three negations last
+LINE_KERNEL, LINE_BYTES = "vectorized_elementwise_kernel", 2 ** 30
+# the library's window copy: three gathers (64-byte reads) then three scatters
+# (64-byte writes), 2^28 bytes each way
+PIECE_KERNEL, PIECE_BYTES = "window_copy_kernel", 2 ** 28
+CALIB_LAUNCHES = 3
+
+
+def _one(pattern: str) -> str:
+    files = sorted(glob.glob(pattern))
+    if not files:
+        raise FileNotFoundError(pattern)
+    return files[0]
+
+
+def kernel_stats(stats_dir: str, kernel: str) -> dict:
+    """Row of *_kernel_stats.csv whose name contains `kernel` (the largest
+    total if several template instances match, their calls summed)."""
+    rows = [r for r in csv.DictReader(open(_one(os.path.join(stats_dir, "*kernel_stats.csv"))))
+            if kernel in r["Name"]]
+    if not rows:
+        raise KeyError(f"{kernel} not in kernel stats of {stats_dir}")
+    calls = sum(int(r["Calls"]) for r in rows)
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    return {"name": kernel, "calls": calls, "total_ns": total, "avg_ns": total / calls,
+            "min_ns": min(float(r["MinNs"]) for r in rows), "max_ns": max(float(r["MaxNs"]) for r in rows),
+            "percentage": sum(float(r["Percentage"]) for r in rows)}
+
+
+def counter_per_dispatch(pmc_dir: str, counter: str, kernel: str) -> list[float]:
+    """Values of `counter` for every dispatch of a kernel whose name contains
+    `kernel`, in dispatch order (summed over the rows of one dispatch)."""
+    per = {}
+    for r in csv.DictReader(open(_one(os.path.join(pmc_dir, "*counter_collection.csv")))):
+        if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            d = int(r["Dispatch_Id"])
+            per[d] = per.get(d, 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise KeyError(f"no {counter} for {kernel} in {pmc_dir}")
+    return [per[d] for d in sorted(per)]
+
+
+def traffic(fetch_dir: str, write_dir: str, kernel: str) -> dict:
+    """Calibrated HBM bytes per launch of `kernel` (median over dispatches),
+    scaled by the 64-byte-piece copy; the whole-line factors ride along."""
+    med = statistics.median
+    f_k = med(counter_per_dispatch(fetch_dir, "FETCH_SIZE", kernel))
+    w_k = med(counter_per_dispatch(write_dir, "WRITE_SIZE", kernel))
+    f_line = med(counter_per_dispatch(fetch_dir, "FETCH_SIZE", LINE_KERNEL)[-CALIB_LAUNCHES:])
+    w_line = med(counter_per_dispatch(write_dir, "WRITE_SIZE", LINE_KERNEL)[-CALIB_LAUNCHES:])
+    f_piece = med(counter_per_dispatch(fetch_dir, "FETCH_SIZE", PIECE_KERNEL)[-2 * CALIB_LAUNCHES:-CALIB_LAUNCHES])
+    w_piece = med(counter_per_dispatch(write_dir, "WRITE_SIZE", PIECE_KERNEL)[-CALIB_LAUNCHES:])
+    fetch_scale = PIECE_BYTES / (f_piece * 1024.0)
+    write_scale = PIECE_BYTES / (w_piece * 1024.0)
+    fetch_b = f_k * 1024.0 * fetch_scale
+    write_b = w_k * 1024.0 * write_scale
+    return {"fetch_kib": f_k, "write_kib": w_k,
+            "piece_fetch_kib": f_piece, "piece_write_kib": w_piece,
+            "line_fetch_kib": f_line, "line_write_kib": w_line,
+            "fetch_scale": fetch_scale, "write_scale": write_scale,
+            "line_fetch_scale": LINE_BYTES / (f_line * 1024.0),
+            "line_write_scale": LINE_BYTES / (w_line * 1024.0),
+            "fetch_bytes": fetch_b, "write_bytes": write_b, "hbm_bytes_per_launch": fetch_b + write_b}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--stats", required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--kernel", required=True)
+    ap.add_argument("--kernel-sha", default=None)
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--bench-json", help="file holding the JSON line bench.py printed in the stats run")
+    ap.add_argument("--command-stats", required=True)
+    ap.add_argument("--command-fetch", default="")
+    ap.add_argument("--command-write", default="")
+    ap.add_argument("--out-md", required=True)
+    ap.add_argument("--out-json")
+    a = ap.parse_args(argv)
+
+    st = kernel_stats(a.stats, a.kernel)
+    bench = None
+    if a.bench_json:
+        for line in open(a.bench_json):
+            line = line.strip()
+            if line.startswith("{") and '"metric"' in line:
+                bench = json.loads(line)
+    tr = traffic(a.fetch, a.write, a.kernel) if a.fetch and a.write else None
+
+    md = [f"# {a.kernel} on {a.workload}", "",
+          "rocprofv3 kernel trace, `--stats` summary:", "", "```", a.command_stats, "```", "",
+          "| kernel | calls | avg µs | min µs | max µs | % of GPU time |", "|---|---|---|---|---|---|",
+          f"| {st['name']} | {st['calls']} | {st['avg_ns'] / 1e3:.2f} | {st['min_ns'] / 1e3:.2f} | "
+          f"{st['max_ns'] / 1e3:.2f} | {st['percentage']:.1f} |", ""]
+    if bench is not None:
+        r = bench.get("roofline", {})
+        md += [f"bench.py in the same run: kernel average {r.get('kernel_ms', float('nan')) * 1e3:.2f} µs "
+               f"(HIP events on the launch stream), {bench['value']:.4g} {bench['unit']}, "
+               f"roofline {r.get('bound')} {r.get('achieved')} {r.get('unit')} of {r.get('peak')} "
+               f"(frac {r.get('frac')}).", ""]
+    if tr is not None:
+        md += ["HBM traffic per launch (two `--pmc` runs, medians over dispatches):", "", "```",
+               a.command_fetch, a.command_write, "```", "",
+               "| counter | kernel KiB | 64-B piece copy KiB (256 MiB known) | scale used | "
+               "whole-line copy KiB (1 GiB known) | its scale | kernel bytes |", "|---|---|---|---|---|---|---|",
+               f"| FETCH_SIZE | {tr['fetch_kib']:.0f} | {tr['piece_fetch_kib']:.0f} | {tr['fetch_scale']:.4f} | "
+               f"{tr['line_fetch_kib']:.0f} | {tr['line_fetch_scale']:.4f} | {tr['fetch_bytes'] / 1e6:.1f} MB |",
+               f"| WRITE_SIZE | {tr['write_kib']:.0f} | {tr['piece_write_kib']:.0f} | {tr['write_scale']:.4f} | "
+               f"{tr['line_write_kib']:.0f} | {tr['line_write_scale']:.4f} | {tr['write_bytes'] / 1e6:.1f} MB |", "",
+               f"Total {tr['hbm_bytes_per_launch'] / 1e6:.1f} MB per launch"
+               + (f" against {bench['roofline']['alg_bytes_per_launch'] / 1e6:.1f} MB algorithmic."
+                  if bench is not None and "alg_bytes_per_launch" in bench.get("roofline", {}) else "."), ""]
+    os.makedirs(os.path.dirname(os.path.abspath(a.out_md)), exist_ok=True)
+    with open(a.out_md, "w") as f:
+        f.write("\n".join(md))
+    if a.out_json and tr is not None:
+        rec = {"workload": a.workload, "kernel": a.kernel, "kernel_sha": a.kernel_sha,
+               "command_fetch": a.command_fetch, "command_write": a.command_write, **tr}
+        with open(a.out_json, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+    print("\n".join(md))
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())

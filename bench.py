@@ -37,14 +37,14 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, TFLOP/s
 MALL_BYTES = 256 * 2 ** 20
-KERNEL_SOURCE = {"attn_small_kernel": "attn_small.hip", "attn_mfma_kernel": "attn_mfma.hip",
-                 "attn_valu_kernel": "attn_valu.hip"}
+KERNEL_SOURCE = {"attn_small_kernel": "attn_small.hip", "attn_large_kernel": "attn_large.hip",
+                 "attn_mfma_kernel": "attn_mfma.hip", "attn_valu_kernel": "attn_valu.hip"}
 
 
 def kernel_sha(kernel: str) -> str:
     """Hash of the sources that define `kernel` (its file and the shared headers)."""
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCE[kernel], "common.hpp", "launch.hpp"):
+    for f in (KERNEL_SOURCE[kernel], "common.hpp", "launch.hpp", "tile_io.hpp"):
         with open(os.path.join(ROOT, "vision_transformer_windowed_partition_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -143,6 +143,8 @@ int swin_window_attn_fwd(const swin_attn_desc* desc, const void* q, const void* 
  *   "attn_valu_kernel"  SWIN_DT_F32;
  *   "attn_small_kernel" SWIN_DT_BF16, M * roundup8(M) <= 256 key slots,
  *                       no rotary positions;
+ *   "attn_large_kernel" SWIN_DT_BF16, M <= 32 otherwise (larger windows,
+ *                       or rotary positions);
  *   "attn_mfma_kernel"  every other SWIN_DT_BF16 case.
  * Only the descriptor is read; rope_base is not required (the caller may
  * pass rope_freqs).  NULL if swin_window_attn_fwd would reject the

@@ -105,19 +105,21 @@ def test_attn_rejects_bad_pointers(L):
 def test_kernel_query_names_the_dispatch(L):
     """Which kernel each workload shape reaches: fp32 -> vector ALUs; bf16
     windows of at most 256 key slots (M rounded up to 8 per key row) without
-    rotary positions -> the register-resident kernel; the rest -> the
-    LDS-staged MFMA kernel."""
+    rotary positions -> the register-resident kernel; other windows up to
+    M = 32 (larger, or rotary) -> the large-window kernel; beyond -> the
+    block-staged MFMA kernel."""
     from vision_transformer_windowed_partition_amd import synth
-    want = ["attn_valu_kernel", "attn_small_kernel", "attn_small_kernel", "attn_mfma_kernel",
-            "attn_mfma_kernel"]
+    want = ["attn_valu_kernel", "attn_small_kernel", "attn_small_kernel", "attn_large_kernel",
+            "attn_large_kernel"]
     for wl, name in zip(synth.WORKLOADS, want):
         d = binding.make_desc(B=wl.B, H=wl.H, W=wl.W, C=wl.C, heads=wl.heads, M=wl.M, shift=wl.shift,
                               partition=wl.partition, sim=wl.sim, pos=wl.pos,
                               dtype=binding.DTYPE_BY_NAME[wl.dtype])
         assert binding.swin_window_attn_kernel(d) == name, wl.name
     assert binding.swin_window_attn_kernel(_desc(M=12, H=24, W=24, dtype=1)) == "attn_small_kernel"  # 192 slots
-    assert binding.swin_window_attn_kernel(_desc(M=17, H=34, W=34, dtype=1, shift=0)) == "attn_mfma_kernel"
-    assert binding.swin_window_attn_kernel(_desc(M=8, dtype=1, pos=2)) == "attn_mfma_kernel"
+    assert binding.swin_window_attn_kernel(_desc(M=17, H=34, W=34, dtype=1, shift=0)) == "attn_large_kernel"
+    assert binding.swin_window_attn_kernel(_desc(M=8, dtype=1, pos=2)) == "attn_large_kernel"
+    assert binding.swin_window_attn_kernel(_desc(M=48, H=48, W=48, dtype=1, shift=0)) == "attn_mfma_kernel"
     assert L.swin_window_attn_kernel(ctypes.byref(_desc(shift=8))) is None
     assert "shift" in binding.swin_last_error()
     assert L.swin_window_attn_kernel(None) is None

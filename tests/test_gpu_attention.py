@@ -35,6 +35,8 @@ SMALL = [
     (24, 40, 8, 7, "cyclic", "dot", "none"),           # shift M-1
     (30, 30, 10, 0, "interleaved", "cosine", "none"),  # 10 -> 16 slots per row, 6 key chunks
     (26, 26, 13, 6, "cyclic", "dot", "table"),         # 208 of 256 slots in use
+    (34, 34, 17, 8, "cyclic", "dot", "none"),          # 17 -> 24 slots per row, 408 -> 416 slots
+    (48, 48, 24, 0, "interleaved", "dot", "table"),    # interleaved large windows
 ]
 
 
@@ -84,6 +86,18 @@ def test_tau_below_floor(dtype):
     x["tau"] = torch.tensor([0.001, 0.05])
     out = run_gpu(wl, gpu_inputs(x))
     compare(wl, f64(out), run_oracle(wl, x), what="tau floor")
+
+
+@pytest.mark.parametrize("pos", ["table", "rope2d"])
+def test_large_window_small_tau(pos):
+    """M = 24 with tau below 0.1: without rotation the raw k and 1/||k|| carry
+    the precision; with rotation q and k are carried as hi + lo pairs."""
+    wl = synth.small(B=1, H=48, W=48, C=64, heads=2, M=24, shift=12, sim="cosine", pos=pos,
+                     dtype="bf16", hidden=64)
+    x = synth.make_inputs(wl, seed=6)
+    x["tau"] = torch.tensor([0.03, 0.5])
+    out = run_gpu(wl, gpu_inputs(x))
+    compare(wl, f64(out), run_oracle(wl, x), what=f"large window small tau {pos}")
 
 
 @pytest.mark.parametrize("pos", ["none", "rope2d"])

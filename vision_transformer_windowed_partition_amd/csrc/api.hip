@@ -173,12 +173,14 @@ swin::AttnParams params_of(const swin_attn_desc* d)
     return p;
 }
 
-enum class Kernel { VALU, SMALL, MFMA };
+enum class Kernel { VALU, SMALL, LARGE, MFMA };
 
 Kernel kernel_for(const swin::AttnParams& p)
 {
     if (p.dtype == SWIN_DT_F32) return Kernel::VALU;
-    return swin::attn_small_supported(p) ? Kernel::SMALL : Kernel::MFMA;
+    if (swin::attn_small_supported(p)) return Kernel::SMALL;
+    if (swin::attn_large_supported(p)) return Kernel::LARGE;
+    return Kernel::MFMA;
 }
 
 }  // namespace
@@ -209,6 +211,7 @@ int swin_window_attn_fwd(const swin_attn_desc* d, const void* q, const void* k, 
     switch (kernel_for(p)) {
     case Kernel::VALU: e = swin::launch_attn_valu(p, (hipStream_t)stream); break;
     case Kernel::SMALL: e = swin::launch_attn_small(p, (hipStream_t)stream); break;
+    case Kernel::LARGE: e = swin::launch_attn_large(p, (hipStream_t)stream); break;
     default: e = swin::launch_attn_mfma(p, (hipStream_t)stream); break;
     }
     return hip_status(e, "swin_window_attn_fwd launch");
@@ -220,6 +223,7 @@ const char* swin_window_attn_kernel(const swin_attn_desc* d)
     switch (kernel_for(params_of(d))) {
     case Kernel::VALU: return "attn_valu_kernel";
     case Kernel::SMALL: return "attn_small_kernel";
+    case Kernel::LARGE: return "attn_large_kernel";
     default: return "attn_mfma_kernel";
     }
 }

@@ -28,43 +28,19 @@
 // else the running maximum per 32-key chunk.
 #include "common.hpp"
 #include "launch.hpp"
+#include "tile_io.hpp"
 
 namespace swin {
 
 namespace {
 
-constexpr int D = 32;
+using namespace tio;
+
 constexpr int WAVES = 4;
 constexpr float RANGE_LIMIT = 60.0f;
 constexpr float PRECISE_TAU = 0.1f;
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
-
-// Position (in 16-byte pieces) of piece p of V slot s in the wave's LDS rows
-// is p ^ v_swizzle(s): of the transposed reads, the four 32-byte row halves a
-// 16-lane group touches fall in distinct 128-byte bank windows, and the two
-// groups of a half-wavefront in distinct 256-byte windows.
-__device__ __forceinline__ int v_swizzle(int s) { return ((s >> 1) ^ (s >> 3)) & 1 ? 2 : 0; }
-
-// Raw buffer access (gfx9 resource word 3 = 0x00020000: 32-bit data, no
-// swizzle).  A raw load whose offset is at or past the record count returns
-// zeros and a store there is dropped; tensors here stay below 2^31 bytes
-// per image, so kNoLoad is always out of range.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-constexpr uint32_t kNoLoad = 0x80000000u;
-__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 load16(Rsrc r, uint32_t off)
-{
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-__device__ __forceinline__ void store8(Rsrc r, uint32_t off, bf16x4 v)
-{
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 0);
-}
 
 struct SmallLayout {
     int NSP;                   // key slots in use: M rows of M rounded up to 8
@@ -74,41 +50,6 @@ struct SmallLayout {
     int per_head;              // items per head, padded to a multiple of WAVES
     float inv_M;
 };
-
-// floor(a / b) for 0 <= a < 2^16, b <= 64, from a float reciprocal: the
-// exact quotient of a + 1/2 sits at least 1/(2b) from an integer, far above
-// the rounding error of the product.
-__device__ __forceinline__ int qdiv(int a, float inv_b) { return (int)(((float)a + 0.5f) * inv_b); }
-
-// Byte offset (within one image, or one window for the WINDOWS layout) of
-// local token (r, c) is row(r) + col(c); all but (r, c) is wave-uniform:
-// cyclic grid: origin (wr*M + shift, wc*M + shift), steps 1, wrap at H, W;
-// interleaved: origin (wr, wc), steps (H/M, W/M), never wraps;
-// windows tensor: origin 0, steps 1, an M x M "grid".
-// The wrap is min(i, i - H) in unsigned arithmetic; products use the 24-bit
-// multiplier (row and column strides stay below 2^24 bytes).
-struct WinGeo {
-    uint32_t r0, c0, rs, cs, Hm, Wm, rowb, colb;
-    __device__ __forceinline__ uint32_t row(int r) const
-    {
-        const uint32_t gi = r0 + __umul24((uint32_t)r, rs);
-        return __umul24(min(gi, gi - Hm), rowb);
-    }
-    __device__ __forceinline__ uint32_t col(int c) const
-    {
-        const uint32_t gj = c0 + __umul24((uint32_t)c, cs);
-        return __umul24(min(gj, gj - Wm), colb);
-    }
-    __device__ __forceinline__ uint32_t tok(int r, int c) const { return row(r) + col(c); }
-};
-
-// kNoLoad unless ok (keeps the offset arithmetic unconditional: no branch)
-__device__ __forceinline__ uint32_t masked(uint32_t off, bool ok) { return off | (ok ? 0u : kNoLoad); }
-
-__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
 template <int NCH>
 struct Frags {                 // this wave's window-head, in MFMA operand layout

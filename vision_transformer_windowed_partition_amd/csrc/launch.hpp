@@ -39,4 +39,10 @@ hipError_t launch_attn_mfma(const AttnParams& p, hipStream_t stream);
 bool attn_small_supported(const AttnParams& p);
 hipError_t launch_attn_small(const AttnParams& p, hipStream_t stream);
 
+// bf16 attention for windows of 16 < M <= 32 and for rotary positions at
+// M <= 32: one workgroup per window-head, its keys and values staged in LDS
+// once.
+bool attn_large_supported(const AttnParams& p);
+hipError_t launch_attn_large(const AttnParams& p, hipStream_t stream);
+
 }  // namespace swin

@@ -49,6 +49,12 @@ using namespace tio;
 
 constexpr int WAVES = 8;
 constexpr int NTHR = WAVES * 64;
+constexpr int KPW = 4;                 // key chunks a wavefront stages, at most (1024 slots / 32 / 8)
+constexpr int QPW = 8;                 // query tiles of a wavefront, at most (1024 queries / 16 / 8)
+#ifndef LARGE_NT
+#define LARGE_NT 2
+#endif
+constexpr int NT = LARGE_NT;           // query tiles a wavefront runs through the keys together
 constexpr float RANGE_LIMIT = 60.0f;
 constexpr float PRECISE_TAU = 0.1f;    // COSINE, no rotation: raw k and 1/||k|| below this tau
 constexpr float SPLIT_TAU = 0.1f;      // COSINE with rotation: hi + lo below this tau
@@ -59,7 +65,7 @@ struct LargeLayout {
     int GPR;                   // 8-slot groups per key row
     int NSP;                   // key slots, padded to a multiple of 32
     int NQT;                   // query tiles per window-head
-    int rounds;                // tile pairs per wavefront (same for all)
+    int rounds;                // passes of NT tiles per wavefront (same for all)
     int units;                 // window-heads
     int P;                     // work ids per XCD slot
     int kv_bytes;              // LDS bytes of the key/value area
@@ -106,9 +112,9 @@ struct GroupWalk {
 //   MASK: shift regions / padded slots; GENERAL: running maximum for tiles
 //   that need it, 1/||k_j|| scaling (precise), hi + lo products (split).
 template <int SIM, int POS, bool MASK, bool GENERAL>
-__device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[2], const float* bias2, const float* kinv,
+__device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[NT], const float* bias2, const float* kinv,
                                          int S, int SR, float inv_SR, int cb, int ce, int lane,
-                                         bool precise, bool split)
+                                         bool partial, bool precise, bool split)
 {
     const int grp = lane >> 4, li = lane & 15;
     const int negrow = S * S;
@@ -120,18 +126,20 @@ __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[2], const fl
     gw.start(bk.s0 + 32 * cb + 8 * grp, inv_SR, SR);
 #pragma unroll 2
     for (int c = cb; c < ce; ++c) {
-        bool gok[2] = {true, true};
-        uint32_t bits[2] = {0xffu, 0xffu};
+        bool gok[NT];
+        uint32_t bits[NT];
+#pragma unroll
+        for (int i = 0; i < NT; ++i) { gok[i] = true; bits[i] = 0xffu; }
         if (MASK) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < NT; ++i) {
                 bits[i] = gw.rj >= T[i].rlo && gw.rj < T[i].rhi ? (T[i].cmask >> gw.c0) & 0xffu : 0u;
                 gok[i] = bits[i] != 0u;
             }
         }
-        float add[2][8];
+        float add[NT][8];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NT; ++i) {
             if (POS == SWIN_POS_TABLE) {
                 const float* bp = bias2 + ((MASK && !gok[i]) ? negrow : gw.rj * S + gw.c0 + T[i].qoff);
 #pragma unroll
@@ -146,9 +154,9 @@ __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[2], const fl
         const bf16x8 kb = bk.k[(c * 2 + 1) * 64 + lane];
         const bf16x8 v0 = vt_frag(bk.v, c, 0, grp, li);
         const bf16x8 v1 = vt_frag(bk.v, c, 1, grp, li);
-        f32x4 sa[2], sb[2];
+        f32x4 sa[NT], sb[NT];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NT; ++i) {
             sa[i] = mfma(ka, T[i].qf, zero4);
             sb[i] = mfma(kb, T[i].qf, zero4);
         }
@@ -158,7 +166,7 @@ __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[2], const fl
                 const bf16x8 ka_lo = bk.klo[(c * 2 + 0) * 64 + lane];
                 const bf16x8 kb_lo = bk.klo[(c * 2 + 1) * 64 + lane];
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
+                for (int i = 0; i < NT; ++i) {
                     sa[i] = mfma(ka_lo, T[i].qf, sa[i]);
                     sb[i] = mfma(kb_lo, T[i].qf, sb[i]);
                     sa[i] = mfma(ka, T[i].qf_lo, sa[i]);
@@ -174,9 +182,9 @@ __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[2], const fl
                 kin[4] = b[0]; kin[5] = b[1]; kin[6] = b[2]; kin[7] = b[3];
             }
         }
-        bf16x8 pb[2];
+        bf16x8 pb[NT];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NT; ++i) {
             float x[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) { x[e] = sa[i][e]; x[e + 4] = sb[i][e]; }
@@ -185,7 +193,7 @@ __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[2], const fl
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     pr[e] = __builtin_amdgcn_exp2f(fmaf(x[e], GENERAL ? T[i].qscale * kin[e] : T[i].qscale, add[i][e]));
-                if (MASK) {
+                if (MASK && partial) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) pr[e] = (bits[i] >> e) & 1u ? pr[e] : 0.0f;
                 }
@@ -194,7 +202,7 @@ __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[2], const fl
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     xs[e] = fmaf(x[e], T[i].qscale * kin[e], add[i][e]);
-                    if (MASK) xs[e] = (bits[i] >> e) & 1u ? xs[e] : -INFINITY;
+                    if (MASK && partial) xs[e] = (bits[i] >> e) & 1u ? xs[e] : -INFINITY;
                     cm = fmaxf(cm, xs[e]);
                 }
                 cm = fmaxf(cm, __shfl_xor(cm, 16));
@@ -210,7 +218,7 @@ __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[2], const fl
             pb[i] = pack_bf16x8(pr);
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NT; ++i) {
             T[i].o0 = mfma(v0, pb[i], T[i].o0);
             T[i].o1 = mfma(v1, pb[i], T[i].o1);
             T[i].ls = mfma(ones, pb[i], T[i].ls);
@@ -321,7 +329,10 @@ attn_large_kernel(AttnParams p, LargeLayout L)
     // Wavefront w takes chunks w, w + 8, ...  Returns the largest squared
     // key norm this lane saw.
     auto stage = [&](const Block& bk, bf16x8* kdst, bf16x8* klodst, __bf16* vdst, bool with_lo) -> float {
-        for (int cb = wave; cb < bk.nch; cb += WAVES) {
+#pragma unroll
+        for (int j = 0; j < KPW; ++j) {
+            const int cb = wave + WAVES * j;
+            if (cb >= bk.nch) break;                      // wave-uniform
 #pragma unroll
             for (int j2 = 0; j2 < 2; ++j2) {
                 const int sl = 32 * cb + 16 * j2 + (lane >> 2);            // slot within the block
@@ -331,22 +342,31 @@ attn_large_kernel(AttnParams p, LargeLayout L)
                 dma16(vr, vdst + (32 * cb + 16 * j2) * D, masked(wp.wg.tok(rj, cj) + 16u * piece, rj < M && cj < M));
             }
         }
-        float kmax2 = 0.0f;
-        for (int cb = wave; cb < bk.nch; cb += WAVES) {
-            u32x4 raw[2];
-            int rr[2], cc[2];
+        // every key load of the stage in flight before the first is used
+        u32x4 raw[KPW][2];
+        int rr[KPW][2], cc[KPW][2];
+#pragma unroll
+        for (int j = 0; j < KPW; ++j) {
+            const int cb = wave + WAVES * j;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int s = bk.s0 + 32 * cb + 8 * (li >> 2) + (li & 3) + 4 * t;
-                rr[t] = qdiv(s, L.inv_SR);
-                cc[t] = s - rr[t] * SR;
-                raw[t] = load16(kr, masked(wp.wg.tok(rr[t], cc[t]) + 16u * grp, rr[t] < M && cc[t] < M));
+                rr[j][t] = qdiv(s, L.inv_SR);
+                cc[j][t] = s - rr[j][t] * SR;
+                const bool ok = cb < bk.nch && rr[j][t] < M && cc[j][t] < M;
+                raw[j][t] = load16(kr, masked(wp.wg.tok(rr[j][t], cc[j][t]) + 16u * grp, ok));
             }
+        }
+        float kmax2 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < KPW; ++j) {
+            const int cb = wave + WAVES * j;
+            if (cb >= bk.nch) break;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 float kf[8];
-                unpack_bf16x8(raw[t], kf);
-                if (POS == SWIN_POS_ROPE2D) rotate(kf, min(rr[t], M - 1), min(cc[t], M - 1));
+                unpack_bf16x8(raw[j][t], kf);
+                if (POS == SWIN_POS_ROPE2D) rotate(kf, min(rr[j][t], M - 1), min(cc[j][t], M - 1));
                 float ss = 0.0f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ss = fmaf(kf[e], kf[e], ss);
@@ -358,7 +378,7 @@ attn_large_kernel(AttnParams p, LargeLayout L)
                     const float inv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));   // 1 / max(||k||, 1e-12)
                     if (precise) {
                         if (grp == 0) kinv[bk.s0 + 32 * cb + 8 * (li >> 2) + (li & 3) + 4 * t] = inv;
-                        kdst[idx] = __builtin_bit_cast(bf16x8, raw[t]);
+                        kdst[idx] = __builtin_bit_cast(bf16x8, raw[j][t]);
                         continue;
                     }
 #pragma unroll
@@ -397,13 +417,19 @@ attn_large_kernel(AttnParams p, LargeLayout L)
         // DOT with rotation: the largest query norm too, from this wave's tiles
         if (SIM == SWIN_SIM_DOT && POS == SWIN_POS_ROPE2D) {
             float q2 = 0.0f;
-            for (int j = 0; j < 2 * L.rounds; ++j) {
+            u32x4 qraw[QPW];
+#pragma unroll
+            for (int j = 0; j < QPW; ++j) {
                 const int t = (wave + WAVES * j) * 16 + li;
                 const bool ok = t < N;
                 const int tc = ok ? t : 0;
                 const int ri = qdiv(tc, L.inv_M), ci = tc - ri * M;
+                qraw[j] = load16(qr, masked(wp.wg.tok(ri, ci) + 16u * grp, ok));
+            }
+#pragma unroll
+            for (int j = 0; j < QPW; ++j) {
                 float qv[8];
-                unpack_bf16x8(load16(qr, masked(wp.wg.tok(ri, ci) + 16u * grp, ok)), qv);
+                unpack_bf16x8(qraw[j], qv);
                 float ss = 0.0f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ss = fmaf(qv[e], qv[e], ss);
@@ -434,21 +460,40 @@ attn_large_kernel(AttnParams p, LargeLayout L)
     const int half_ch = (nch_all + 1) / 2;
     const int nblocks = split ? 2 : 1;
 
-    // ---- this wavefront's query tiles, two at a time
+    // ---- this wavefront's query tiles, two at a time; the next pair's
+    // queries load while the current pair runs
     const int qhalf = POS == SWIN_POS_ROPE2D ? 1 : 0;
+    // groups split by a region edge or by padded columns need per-key masks
+    const bool partial = (wp.last_c && ((M - g.shift) & 7)) || (M & 7);
+    auto load_pair_q = [&](int r, u32x4 (&qr2)[NT]) {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            const int t = (wave + WAVES * (NT * r + i)) * 16 + li;
+            const bool ok = t < N;
+            const int tc = ok ? t : 0;
+            const int ri = qdiv(tc, L.inv_M), ci = tc - ri * M;
+            qr2[i] = load16(qr, masked(wp.wg.tok(ri, ci) + 16u * grp, ok));
+        }
+    };
+    u32x4 qnext[NT];
+    load_pair_q(0, qnext);
     for (int r = 0; r < L.rounds; ++r) {
-        Tile T[2];
-        int qt[2];
-        bool qv[2];
+        u32x4 qcur[NT];
+#pragma unroll
+        for (int i = 0; i < NT; ++i) qcur[i] = qnext[i];
+        if (r + 1 < L.rounds) load_pair_q(r + 1, qnext);
+        Tile T[NT];
+        int qt[NT];
+        bool qv[NT];
         bool any_exact = false;
         int rlo_min = M, rhi_max = 0;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int t = (wave + WAVES * (2 * r + i)) * 16 + li;
+        for (int i = 0; i < NT; ++i) {
+            const int t = (wave + WAVES * (NT * r + i)) * 16 + li;
             qv[i] = t < N;
             qt[i] = qv[i] ? t : 0;
             const int ri = qdiv(qt[i], L.inv_M), ci = qt[i] - ri * M;
-            const u32x4 raw = load16(qr, masked(wp.wg.tok(ri, ci) + 16u * grp, qv[i]));
+            const u32x4 raw = qcur[i];
             float qf[8];
             unpack_bf16x8(raw, qf);
             if (POS == SWIN_POS_ROPE2D) rotate(qf, ri, ci);
@@ -522,17 +567,20 @@ attn_large_kernel(AttnParams p, LargeLayout L)
             const int ce = min(bk.nch, (max(0, s_hi) + 31) >> 5);
             if (cb >= ce) continue;
             if (any_exact || precise || split)
-                run_pair<SIM, POS, true, true>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, precise, split);
+                run_pair<SIM, POS, true, true>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, partial, precise,
+                                               split);
             else if (needs_mask)
-                run_pair<SIM, POS, true, false>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, false, false);
+                run_pair<SIM, POS, true, false>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, partial, false,
+                                                false);
             else
-                run_pair<SIM, POS, false, false>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, false, false);
+                run_pair<SIM, POS, false, false>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, false, false,
+                                                 false);
         }
 
         // ---- normalise and store: lane holds channels 4 grp..+3 and
         // 16 + 4 grp..+3 of query li
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NT; ++i) {
             const int ri = qdiv(qt[i], L.inv_M), ci = qt[i] - ri * M;
             const float inv = __builtin_amdgcn_rcpf(T[i].ls[0]);
             const uint32_t o = masked(wp.wg.tok(ri, ci) + 8u * grp, qv[i]);
@@ -562,7 +610,7 @@ size_t large_lds(const Geometry& g, int sim, int pos, LargeLayout* out)
     L.NSP = (g.M * L.SR + 31) / 32 * 32;
     L.NQT = (g.N + 15) / 16;
     const int tpw = (L.NQT + WAVES - 1) / WAVES;
-    L.rounds = (tpw + 1) / 2;
+    L.rounds = (tpw + NT - 1) / NT;
     L.units = g.nwin * g.heads;
     L.P = (L.units + 7) / 8;
     const int nch = L.NSP / 32, half = (nch + 1) / 2;

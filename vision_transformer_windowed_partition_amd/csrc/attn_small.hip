@@ -56,22 +56,23 @@ struct Frags {                 // this wave's window-head, in MFMA operand layou
     const bf16x8* k;           // LDS: k^ (or raw k: DOT, precise COSINE), [NCH][2][64 lanes]
     bf16x8 v[NCH][2];          // V^T, channels 0-15 and 16-31
     int koff[NCH];             // bias-table offset of this lane's key group: rj*S + c0
-    int rc[NCH];               // this lane's key group: rj << 8 | c0
 };
 
 struct Tile {                  // one query tile of 16 queries
     bf16x8 qf;
     float qscale, negm, mrun;
-    int qoff, rlo, rhi;
-    uint32_t cmask;            // allowed key columns (bit c)
+    int qoff;
+    uint32_t gmask;            // chunks whose key group of this lane is allowed (bit c)
+    uint32_t colbits;          // allowed columns of this lane's key group (bit e)
     bool exact;
     f32x4 o0, o1, ls;
 };
 
-// One pair of query tiles against the window's keys.
+// One pair of query tiles against key chunks [CB, CE) of the window (the
+// others are masked for both tiles).
 //   MASK: shift regions / padded slots; PRECISE: scores scaled by 1/||k_j||
 //   (raw k operand); EXACT: running maximum instead of the static shift.
-template <int SIM, int POS, int NCH, bool MASK, bool PRECISE, bool EXACT>
+template <int SIM, int POS, int NCH, int CB, int CE, bool MASK, bool PRECISE, bool EXACT>
 __device__ __forceinline__ void run_pair(const Frags<NCH>& F, Tile (&T)[2], const float* bias2,
                                          const float* kinv, int negrow, int lane, bool partial_any,
                                          bool precise_rt)
@@ -83,16 +84,11 @@ __device__ __forceinline__ void run_pair(const Frags<NCH>& F, Tile (&T)[2], cons
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
+    for (int c = CB; c < CE; ++c) {
         uint32_t bits[2] = {0xffu, 0xffu};
         if (MASK) {
-            const int rj = F.rc[c] >> 8, c0 = F.rc[c] & 0xff;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const bool rok = rj >= T[i].rlo && rj < T[i].rhi;
-                bits[i] = rok ? (T[i].cmask >> c0) & 0xffu : 0u;
-            }
-            if (!__any((bits[0] | bits[1]) != 0u)) continue;        // chunk masked for the wave
+            for (int i = 0; i < 2; ++i) bits[i] = (T[i].gmask >> c) & 1u ? T[i].colbits : 0u;
         }
         float kin[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
         if (prec) {
@@ -330,7 +326,6 @@ attn_small_kernel(AttnParams p, SmallLayout L)
         const int gam = 4 * c + grp;
         const int rj = gam / GPR, c0 = (gam % GPR) * 8;
         F.koff[c] = rj * S + c0;
-        F.rc[c] = (rj << 8) | c0;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();                      // V rows consumed: the area takes K next
@@ -422,11 +417,22 @@ attn_small_kernel(AttnParams p, SmallLayout L)
             any_exact = any_exact || T[i].exact;
             T[i].mrun = -INFINITY;
             T[i].qoff = (M - 1 - ri) * S + (M - 1 - ci);
-            T[i].rlo = 0; T[i].rhi = M;
-            int clo = 0, chi = M;
-            if (last_r) { if (ri < M - g.shift) T[i].rhi = M - g.shift; else T[i].rlo = M - g.shift; }
+            int rlo = 0, rhi = M, clo = 0, chi = M;
+            if (last_r) { if (ri < M - g.shift) rhi = M - g.shift; else rlo = M - g.shift; }
             if (last_c) { if (ci < M - g.shift) chi = M - g.shift; else clo = M - g.shift; }
-            T[i].cmask = (chi >= 32 ? 0xffffffffu : ((1u << chi) - 1u)) & ~((1u << clo) - 1u);
+            const uint32_t cmask = (chi >= 32 ? 0xffffffffu : ((1u << chi) - 1u)) & ~((1u << clo) - 1u);
+            // this lane's key group in chunk c: row (4/GPR) c + grp/GPR, columns
+            // 8 (grp % GPR) .. +7; allowed chunks are those whose row lies in
+            // [rlo, rhi), if the columns are allowed at all
+            {
+                constexpr int STEP = 4 / GPR, SH = STEP == 4 ? 2 : 1;
+                const int rl = grp / GPR;
+                T[i].colbits = (cmask >> (8 * (grp % GPR))) & 0xffu;
+                const int cb = max(0, (rlo - rl + STEP - 1) >> SH);
+                const int ce = min(NCH, (rhi - rl + STEP - 1) >> SH);
+                const uint32_t rows = ce > cb ? ((ce >= 32 ? 0xffffffffu : (1u << ce) - 1u) & ~((1u << cb) - 1u)) : 0u;
+                T[i].gmask = T[i].colbits ? rows : 0u;
+            }
             // groups split by a region edge or by padding
             if (needs_mask) partial = partial || (last_c && ((M - g.shift) & 7)) || (M & 7);
             T[i].o0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -435,11 +441,23 @@ attn_small_kernel(AttnParams p, SmallLayout L)
         }
         const int negrow = S * S;
         if (any_exact || precise)
-            run_pair<SIM, POS, NCH, true, true, true>(F, T, bias2, kinv, negrow, lane, true, precise);
-        else if (needs_mask)
-            run_pair<SIM, POS, NCH, true, false, false>(F, T, bias2, kinv, negrow, lane, partial, false);
-        else
-            run_pair<SIM, POS, NCH, false, false, false>(F, T, bias2, kinv, negrow, lane, false, false);
+            run_pair<SIM, POS, NCH, 0, NCH, true, true, true>(F, T, bias2, kinv, negrow, lane, true, precise);
+        else if (needs_mask) {
+            // chunks some lane of the pair may see: all, or one half of the key rows
+            uint32_t live = T[0].gmask | T[1].gmask;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) live |= (uint32_t)__shfl_xor((int)live, o);
+            live = (uint32_t)__builtin_amdgcn_readfirstlane((int)live);
+            constexpr uint32_t lo_half = (1u << (NCH / 2)) - 1u;
+            if ((live & ~lo_half) == 0u)
+                run_pair<SIM, POS, NCH, 0, NCH / 2, true, false, false>(F, T, bias2, kinv, negrow, lane, partial, false);
+            else if ((live & lo_half) == 0u)
+                run_pair<SIM, POS, NCH, NCH / 2, NCH, true, false, false>(F, T, bias2, kinv, negrow, lane, partial,
+                                                                          false);
+            else
+                run_pair<SIM, POS, NCH, 0, NCH, true, false, false>(F, T, bias2, kinv, negrow, lane, partial, false);
+        } else
+            run_pair<SIM, POS, NCH, 0, NCH, false, false, false>(F, T, bias2, kinv, negrow, lane, false, false);
 
         // ---- normalise and store: lane holds channels 4 grp..+3 and
         // 16 + 4 grp..+3 of query li

@@ -52,9 +52,15 @@ __device__ __forceinline__ RawRsrc raw_rsrc(const void* base, uint32_t bytes)
 }
 __device__ __forceinline__ void dma16(const RawRsrc& r, const void* lds, uint32_t off)
 {
-    const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds;
+    // the resource and the LDS base are wave-uniform: pin them to scalar
+    // registers, as the asm operands require
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds);
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_readfirstlane(r.w[i]);
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(m0), "v"(off), "s"(r.w) : "memory", "m0");
+                 :: "s"(m0), "v"(off), "s"(w) : "memory", "m0");
 }
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

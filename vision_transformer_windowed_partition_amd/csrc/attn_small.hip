@@ -48,6 +48,8 @@ struct SmallLayout {
     int TPW;                   // query tiles per wavefront item
     int parts;                 // wavefront items per window-head
     int per_head;              // items per head, padded to a multiple of WAVES
+    int wgs;                   // workgroups with work: heads * per_head / WAVES
+    int P;                     // work ids per XCD slot
     float inv_M;
 };
 
@@ -186,9 +188,15 @@ attn_small_kernel(AttnParams p, SmallLayout L)
     float* kinv = red + 16 + wave * (NCH * 32);                      // [NCH*32] 1/||k|| (precise path)
     __bf16* vst = (__bf16*)(red + 16 + WAVES * NCH * 32) + wave * (NCH * 32 * D);   // [NCH*32][D] V rows
 
-    // ---- item: one head per workgroup, one (window, query part) per wave
-    const int h = (blockIdx.x * WAVES) / L.per_head;
-    const int local = blockIdx.x * WAVES - h * L.per_head + wave;
+    // ---- item: one head per workgroup, one (window, query part) per wave.
+    // Work ids run window-block-major, head-minor, and each XCD takes a
+    // contiguous range of them (consecutive blockIdx land on different
+    // XCDs): the heads of a window block run back to back on one XCD, so the
+    // 128-byte lines their 64-byte head slices share are fetched once.
+    const int work = (blockIdx.x & 7) * L.P + (blockIdx.x >> 3);
+    if (work >= L.wgs) return;                            // whole workgroup, before any barrier
+    const int h = work % g.heads;
+    const int local = (work / g.heads) * WAVES + wave;
     const bool active = local < g.nwin * L.parts;
     const int win = active ? local / L.parts : 0;
     const int part = active ? local - win * L.parts : 0;
@@ -511,7 +519,11 @@ hipError_t launch_attn_small(const AttnParams& p, hipStream_t stream)
     const int nch_real = (L.NSP + 31) / 32;
     const int nch = nch_real <= 2 ? 2 : nch_real <= 6 ? 6 : 8;      // M <= 8, 9-12, 13-16
     const int S = 2 * g.M - 1;
-    const int64_t grid = (int64_t)g.heads * L.per_head / WAVES;
+    const int64_t wgs = (int64_t)g.heads * L.per_head / WAVES;
+    if (wgs > INT32_MAX - 8) return hipErrorInvalidValue;
+    L.wgs = (int)wgs;
+    L.P = (int)((wgs + 7) / 8);
+    const int64_t grid = 8 * (int64_t)L.P;
     size_t lds = (size_t)(16 + WAVES * nch * 32) * sizeof(float) + (size_t)WAVES * nch * 32 * D * 2;
     if (p.pos == SWIN_POS_TABLE) lds += (size_t)((S * S + 8 + 3) / 4 * 4) * sizeof(float);
     if (p.sim == SWIN_SIM_COSINE) {

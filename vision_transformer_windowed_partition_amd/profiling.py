@@ -5,17 +5,20 @@ from ``--kernel-trace --stats`` and ``*_counter_collection.csv`` from
 ``--pmc``.  Writes a short text summary and the measured HBM traffic per
 launch, which bench.py reports next to the algorithmic bytes.
 
-HBM traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are taken in two
-separate ``--pmc`` runs of the same command; each is scaled by what the same
-counter reads for a plain copy of a known size whose accesses have the same
-granularity as the kernel's.  bench.py ``--calib-copy`` runs two kinds:
-  * whole 128-byte lines: y = -x over 2^28 fp32 (1 GiB read, 1 GiB written);
-  * isolated 64-byte pieces: the library's interleaved window gather of a
-    16x512x512x32 bf16 grid (256 MiB; every token's 64 bytes read on its
-    own), then the matching scatter (64-byte pieces written), 3 launches each.
-The attention kernels read and write each token's head slice (32 bf16 = 64
-bytes) apart from its neighbours', so their counts take the 64-byte factors;
-the whole-line factors are reported beside them.
+HBM traffic per launch comes from two separate ``--pmc`` runs of the same
+command:
+  * reads: the L2-to-memory read requests by size, TCC_EA0_RDREQ_32B,
+    _64B and _128B (bytes = 32 n32 + 64 n64 + 128 n128).  The derived
+    FETCH_SIZE of this ROCm counts 128-byte requests through TCC_BUBBLE,
+    which does not see them: a contiguous 1 GiB copy reads as 0.5 GiB there
+    and as 1.000 GiB from the request counters;
+  * writes: WRITE_SIZE (KiB).
+Each is scaled by what it reads for a plain copy of known size, bench.py
+``--calib-copy``: y = -x over 2^28 fp32 (1 GiB read, 1 GiB written).  The
+same run also holds the library's interleaved window gather of a
+16x512x512x32 bf16 grid (every token's 64 bytes read on its own) and its
+scatter, which show the 128-byte line granularity: the gather of 256 MiB
+fetches 512 MiB.
 
 Usage (on the files a GPU run wrote):
     python -m vision_transformer_windowed_partition_amd.profiling \\
@@ -39,6 +42,7 @@ LINE_KERNEL, LINE_BYTES = "vectorized_elementwise_kernel", 2 ** 30
 # (64-byte writes), 2^28 bytes each way
 PIECE_KERNEL, PIECE_BYTES = "window_copy_kernel", 2 ** 28
 CALIB_LAUNCHES = 3
+RDREQ = {"TCC_EA0_RDREQ_32B_sum": 32, "TCC_EA0_RDREQ_64B_sum": 64, "TCC_EA0_RDREQ_128B_sum": 128}
 
 
 def _one(pattern: str) -> str:
@@ -75,33 +79,35 @@ def counter_per_dispatch(pmc_dir: str, counter: str, kernel: str) -> list[float]
     return [per[d] for d in sorted(per)]
 
 
-def traffic(fetch_dir: str, write_dir: str, kernel: str) -> dict:
-    """Calibrated HBM bytes per launch of `kernel` (median over dispatches),
-    scaled by the 64-byte-piece copy; the whole-line factors ride along."""
+def read_bytes_per_dispatch(pmc_dir: str, kernel: str) -> list[float]:
+    """L2-to-memory read bytes of every dispatch of `kernel`, from the read
+    requests by size."""
+    per = [counter_per_dispatch(pmc_dir, c, kernel) for c in RDREQ]
+    return [sum(RDREQ[c] * v[i] for c, v in zip(RDREQ, per)) for i in range(len(per[0]))]
+
+
+def traffic(rdreq_dir: str, write_dir: str, kernel: str) -> dict:
+    """Calibrated HBM bytes per launch of `kernel` (median over dispatches)."""
     med = statistics.median
-    f_k = med(counter_per_dispatch(fetch_dir, "FETCH_SIZE", kernel))
-    w_k = med(counter_per_dispatch(write_dir, "WRITE_SIZE", kernel))
-    f_line = med(counter_per_dispatch(fetch_dir, "FETCH_SIZE", LINE_KERNEL)[-CALIB_LAUNCHES:])
-    w_line = med(counter_per_dispatch(write_dir, "WRITE_SIZE", LINE_KERNEL)[-CALIB_LAUNCHES:])
-    f_piece = med(counter_per_dispatch(fetch_dir, "FETCH_SIZE", PIECE_KERNEL)[-2 * CALIB_LAUNCHES:-CALIB_LAUNCHES])
-    w_piece = med(counter_per_dispatch(write_dir, "WRITE_SIZE", PIECE_KERNEL)[-CALIB_LAUNCHES:])
-    fetch_scale = PIECE_BYTES / (f_piece * 1024.0)
-    write_scale = PIECE_BYTES / (w_piece * 1024.0)
-    fetch_b = f_k * 1024.0 * fetch_scale
-    write_b = w_k * 1024.0 * write_scale
-    return {"fetch_kib": f_k, "write_kib": w_k,
-            "piece_fetch_kib": f_piece, "piece_write_kib": w_piece,
-            "line_fetch_kib": f_line, "line_write_kib": w_line,
-            "fetch_scale": fetch_scale, "write_scale": write_scale,
-            "line_fetch_scale": LINE_BYTES / (f_line * 1024.0),
-            "line_write_scale": LINE_BYTES / (w_line * 1024.0),
-            "fetch_bytes": fetch_b, "write_bytes": write_b, "hbm_bytes_per_launch": fetch_b + write_b}
+    r_k = med(read_bytes_per_dispatch(rdreq_dir, kernel))
+    w_k = med(counter_per_dispatch(write_dir, "WRITE_SIZE", kernel)) * 1024.0
+    r_line = med(read_bytes_per_dispatch(rdreq_dir, LINE_KERNEL)[-CALIB_LAUNCHES:])
+    w_line = med(counter_per_dispatch(write_dir, "WRITE_SIZE", LINE_KERNEL)[-CALIB_LAUNCHES:]) * 1024.0
+    r_gather = med(read_bytes_per_dispatch(rdreq_dir, PIECE_KERNEL)[-2 * CALIB_LAUNCHES:-CALIB_LAUNCHES])
+    read_scale = LINE_BYTES / r_line
+    write_scale = LINE_BYTES / w_line
+    return {"read_bytes_raw": r_k, "write_bytes_raw": w_k,
+            "copy_read_bytes": r_line, "copy_write_bytes": w_line,
+            "read_scale": read_scale, "write_scale": write_scale,
+            "gather64_read_bytes": r_gather, "gather64_useful_bytes": PIECE_BYTES,
+            "read_bytes": r_k * read_scale, "write_bytes": w_k * write_scale,
+            "hbm_bytes_per_launch": r_k * read_scale + w_k * write_scale}
 
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--stats", required=True)
-    ap.add_argument("--fetch")
+    ap.add_argument("--fetch", help="directory of the --pmc run with the TCC_EA0_RDREQ_{32B,64B,128B} counters")
     ap.add_argument("--write")
     ap.add_argument("--kernel", required=True)
     ap.add_argument("--kernel-sha", default=None)
@@ -137,12 +143,14 @@ def main(argv=None) -> int:
     if tr is not None:
         md += ["HBM traffic per launch (two `--pmc` runs, medians over dispatches):", "", "```",
                a.command_fetch, a.command_write, "```", "",
-               "| counter | kernel KiB | 64-B piece copy KiB (256 MiB known) | scale used | "
-               "whole-line copy KiB (1 GiB known) | its scale | kernel bytes |", "|---|---|---|---|---|---|---|",
-               f"| FETCH_SIZE | {tr['fetch_kib']:.0f} | {tr['piece_fetch_kib']:.0f} | {tr['fetch_scale']:.4f} | "
-               f"{tr['line_fetch_kib']:.0f} | {tr['line_fetch_scale']:.4f} | {tr['fetch_bytes'] / 1e6:.1f} MB |",
-               f"| WRITE_SIZE | {tr['write_kib']:.0f} | {tr['piece_write_kib']:.0f} | {tr['write_scale']:.4f} | "
-               f"{tr['line_write_kib']:.0f} | {tr['line_write_scale']:.4f} | {tr['write_bytes'] / 1e6:.1f} MB |", "",
+               "| direction | kernel raw | contiguous copy (1 GiB known) | scale | kernel bytes |",
+               "|---|---|---|---|---|",
+               f"| read (32·n32 + 64·n64 + 128·n128) | {tr['read_bytes_raw'] / 1e6:.1f} MB | "
+               f"{tr['copy_read_bytes'] / 2**30:.4f} GiB | {tr['read_scale']:.4f} | {tr['read_bytes'] / 1e6:.1f} MB |",
+               f"| write (WRITE_SIZE) | {tr['write_bytes_raw'] / 1e6:.1f} MB | "
+               f"{tr['copy_write_bytes'] / 2**30:.4f} GiB | {tr['write_scale']:.4f} | {tr['write_bytes'] / 1e6:.1f} MB |", "",
+               f"Line granularity check: the 64-byte-piece gather of {tr['gather64_useful_bytes'] / 2**20:.0f} MiB "
+               f"reads {tr['gather64_read_bytes'] / 2**20:.0f} MiB.", "",
                f"Total {tr['hbm_bytes_per_launch'] / 1e6:.1f} MB per launch"
                + (f" against {bench['roofline']['alg_bytes_per_launch'] / 1e6:.1f} MB algorithmic."
                   if bench is not None and "alg_bytes_per_launch" in bench.get("roofline", {}) else "."), ""]

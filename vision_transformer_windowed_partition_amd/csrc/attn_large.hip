@@ -47,10 +47,13 @@ namespace {
 
 using namespace tio;
 
-constexpr int WAVES = 8;
+#ifndef LARGE_WAVES
+#define LARGE_WAVES 8
+#endif
+constexpr int WAVES = LARGE_WAVES;     // wavefronts per workgroup (one workgroup per CU)
 constexpr int NTHR = WAVES * 64;
-constexpr int KPW = 4;                 // key chunks a wavefront stages, at most (1024 slots / 32 / 8)
-constexpr int QPW = 8;                 // query tiles of a wavefront, at most (1024 queries / 16 / 8)
+constexpr int KPW = (32 + WAVES - 1) / WAVES;   // key chunks a wavefront stages, at most (1024 slots)
+constexpr int QPW = (64 + WAVES - 1) / WAVES;   // query tiles of a wavefront, at most (1024 queries)
 #ifndef LARGE_NT
 #define LARGE_NT 2
 #endif
@@ -228,7 +231,7 @@ __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[NT], const f
 }
 
 template <int SIM, int POS>
-__global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu((WAVES + 3) / 4)))
 attn_large_kernel(AttnParams p, LargeLayout L)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -253,7 +256,7 @@ attn_large_kernel(AttnParams p, LargeLayout L)
     float* bias2 = (float*)(smem + L.kv_bytes);                            // [S*S + 8]   (TABLE)
     float* rtab = bias2 + (POS == SWIN_POS_TABLE ? (S * S + 8 + 3) / 4 * 4 : 0);   // [M][2][8] cos, sin (ROPE2D)
     float* kinv = rtab + (POS == SWIN_POS_ROPE2D ? M * 32 : 0);           // [NSP]       (COSINE)
-    float* red = kinv + (SIM == SWIN_SIM_COSINE ? L.NSP : 0);             // [32]
+    float* red = kinv + (SIM == SWIN_SIM_COSINE ? L.NSP : 0);             // [4 * WAVES]
 
     const WinPlace wp = place_window(g, win);
     const uint32_t bytes = (uint32_t)(wp.span - h * D) * 2u;
@@ -268,46 +271,6 @@ attn_large_kernel(AttnParams p, LargeLayout L)
     const bool precise = SIM == SWIN_SIM_COSINE && POS != SWIN_POS_ROPE2D && tau_eff < PRECISE_TAU;
     bool split = SIM == SWIN_SIM_COSINE && POS == SWIN_POS_ROPE2D && tau_eff < SPLIT_TAU;
     const bool needs_mask = wp.last_r || wp.last_c || SR != M || L.NSP != M * SR;
-
-    // ---- tables: bias (reversed so that consecutive keys read consecutive
-    // floats, in log2 units, shifted by its max and, for COSINE, by 1/tau);
-    // rotary cos / sin per local position, half and pair
-    float bias_range = 0.0f;
-    if (POS == SWIN_POS_TABLE) {
-        float mx = -INFINITY, mn = INFINITY;
-        for (int i = tid; i < S * S; i += NTHR) {
-            const float v = p.table[(size_t)(S * S - 1 - i) * g.heads + h] * kLog2e;
-            bias2[i] = v;
-            mx = fmaxf(mx, v);
-            mn = fminf(mn, v);
-        }
-        if (tid < 8) bias2[S * S + tid] = -INFINITY;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            mx = fmaxf(mx, __shfl_xor(mx, o));
-            mn = fminf(mn, __shfl_xor(mn, o));
-        }
-        if (lane == 0) { red[wave] = mx; red[8 + wave] = mn; }
-        __syncthreads();
-        mx = red[0]; mn = red[8];
-#pragma unroll
-        for (int w = 1; w < WAVES; ++w) { mx = fmaxf(mx, red[w]); mn = fminf(mn, red[8 + w]); }
-        bias_range = mx - mn;
-        const float sh = SIM == SWIN_SIM_COSINE ? mx + kLog2e * inv_tau : mx;
-        for (int i = tid; i < S * S; i += NTHR) bias2[i] -= sh;
-    }
-    if (POS == SWIN_POS_ROPE2D) {
-        for (int i = tid; i < M * 16; i += NTHR) {
-            const int k = i & 7, half = (i >> 3) & 1, pos = i >> 4;
-            const double th = p.rope_freqs ? (double)p.rope_freqs[((size_t)h * 2 + half) * 8 + k]
-                                           : pow((double)p.rope_base, -(double)k / 8.0);
-            double s_, c_;
-            sincos((double)pos * th, &s_, &c_);
-            rtab[i * 2] = (float)c_;
-            rtab[i * 2 + 1] = (float)s_;
-        }
-    }
-    __syncthreads();
 
     // Rotate 8 channels (8 grp..8 grp+7) of a token at local (r, c): the
     // first half of the head dims turns with the row, the second with the
@@ -328,7 +291,9 @@ attn_large_kernel(AttnParams p, LargeLayout L)
     // registers (rotated, normalised, rounded; remainders when split).
     // Wavefront w takes chunks w, w + 8, ...  Returns the largest squared
     // key norm this lane saw.
-    auto stage = [&](const Block& bk, bf16x8* kdst, bf16x8* klodst, __bf16* vdst, bool with_lo) -> float {
+    u32x4 raw[KPW][2];
+    int rr[KPW][2], cc[KPW][2];
+    auto stage_issue = [&](const Block& bk, __bf16* vdst) {
 #pragma unroll
         for (int j = 0; j < KPW; ++j) {
             const int cb = wave + WAVES * j;
@@ -343,8 +308,6 @@ attn_large_kernel(AttnParams p, LargeLayout L)
             }
         }
         // every key load of the stage in flight before the first is used
-        u32x4 raw[KPW][2];
-        int rr[KPW][2], cc[KPW][2];
 #pragma unroll
         for (int j = 0; j < KPW; ++j) {
             const int cb = wave + WAVES * j;
@@ -357,6 +320,8 @@ attn_large_kernel(AttnParams p, LargeLayout L)
                 raw[j][t] = load16(kr, masked(wp.wg.tok(rr[j][t], cc[j][t]) + 16u * grp, ok));
             }
         }
+    };
+    auto stage_process = [&](const Block& bk, bf16x8* kdst, bf16x8* klodst, bool with_lo) -> float {
         float kmax2 = 0.0f;
 #pragma unroll
         for (int j = 0; j < KPW; ++j) {
@@ -406,13 +371,55 @@ attn_large_kernel(AttnParams p, LargeLayout L)
     whole.s0 = 0;
     whole.nch = nch_all;
     float kmax = 0.0f;
+    // ---- tables: bias (reversed so that consecutive keys read consecutive
+    // floats, in log2 units, shifted by its max and, for COSINE, by 1/tau);
+    // rotary cos / sin per local position, half and pair
+    float bias_range = 0.0f;
+    if (POS == SWIN_POS_TABLE) {
+        float mx = -INFINITY, mn = INFINITY;
+        for (int i = tid; i < S * S; i += NTHR) {
+            const float v = p.table[(size_t)(S * S - 1 - i) * g.heads + h] * kLog2e;
+            bias2[i] = v;
+            mx = fmaxf(mx, v);
+            mn = fminf(mn, v);
+        }
+        if (tid < 8) bias2[S * S + tid] = -INFINITY;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            mx = fmaxf(mx, __shfl_xor(mx, o));
+            mn = fminf(mn, __shfl_xor(mn, o));
+        }
+        if (lane == 0) { red[wave] = mx; red[WAVES + wave] = mn; }
+        __syncthreads();
+        mx = red[0]; mn = red[WAVES];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) { mx = fmaxf(mx, red[w]); mn = fminf(mn, red[WAVES + w]); }
+        bias_range = mx - mn;
+        const float sh = SIM == SWIN_SIM_COSINE ? mx + kLog2e * inv_tau : mx;
+        for (int i = tid; i < S * S; i += NTHR) bias2[i] -= sh;
+    }
+    if (POS == SWIN_POS_ROPE2D) {
+        for (int i = tid; i < M * 16; i += NTHR) {
+            const int k = i & 7, half = (i >> 3) & 1, pos = i >> 4;
+            // fp32 is ample: the rotated operands are rounded to bf16
+            const float th = p.rope_freqs ? p.rope_freqs[((size_t)h * 2 + half) * 8 + k]
+                                          : exp2f(-(float)k * 0.125f * log2f(p.rope_base));
+            float s_, c_;
+            sincosf((float)pos * th, &s_, &c_);
+            rtab[i * 2] = c_;
+            rtab[i * 2 + 1] = s_;
+        }
+    }
+    __syncthreads();
+
+    if (!split) stage_issue(whole, (__bf16*)(kv + L.NSP * 64));
     if (!split) {
-        float k2 = stage(whole, (bf16x8*)kv, nullptr, (__bf16*)(kv + L.NSP * 64), false);
+        float k2 = stage_process(whole, (bf16x8*)kv, nullptr, false);
         // DOT: the window's largest key norm (Cauchy-Schwarz shift, split test)
         if (SIM == SWIN_SIM_DOT) {
 #pragma unroll
             for (int o = 8; o > 0; o >>= 1) k2 = fmaxf(k2, __shfl_xor(k2, o));
-            if (lane == 0) red[16 + wave] = k2;
+            if (lane == 0) red[2 * WAVES + wave] = k2;
         }
         // DOT with rotation: the largest query norm too, from this wave's tiles
         if (SIM == SWIN_SIM_DOT && POS == SWIN_POS_ROPE2D) {
@@ -439,16 +446,16 @@ attn_large_kernel(AttnParams p, LargeLayout L)
             }
 #pragma unroll
             for (int o = 8; o > 0; o >>= 1) q2 = fmaxf(q2, __shfl_xor(q2, o));
-            if (lane == 0) red[24 + wave] = q2;
+            if (lane == 0) red[3 * WAVES + wave] = q2;
         }
         vm_wait_all();
         __syncthreads();
         if (SIM == SWIN_SIM_DOT) {
-            float k2m = red[16], q2m = red[24];
+            float k2m = red[2 * WAVES], q2m = red[3 * WAVES];
 #pragma unroll
             for (int w = 1; w < WAVES; ++w) {
-                k2m = fmaxf(k2m, red[16 + w]);
-                if (POS == SWIN_POS_ROPE2D) q2m = fmaxf(q2m, red[24 + w]);
+                k2m = fmaxf(k2m, red[2 * WAVES + w]);
+                if (POS == SWIN_POS_ROPE2D) q2m = fmaxf(q2m, red[3 * WAVES + w]);
             }
             kmax = sqrtf(k2m);
             if (POS == SWIN_POS_ROPE2D) split = kmax * sqrtf(q2m) * (kLog2e * 0.17677669529663687f) > SPLIT_BOUND;
@@ -475,13 +482,9 @@ attn_large_kernel(AttnParams p, LargeLayout L)
             qr2[i] = load16(qr, masked(wp.wg.tok(ri, ci) + 16u * grp, ok));
         }
     };
-    u32x4 qnext[NT];
-    load_pair_q(0, qnext);
     for (int r = 0; r < L.rounds; ++r) {
         u32x4 qcur[NT];
-#pragma unroll
-        for (int i = 0; i < NT; ++i) qcur[i] = qnext[i];
-        if (r + 1 < L.rounds) load_pair_q(r + 1, qnext);
+        load_pair_q(r, qcur);
         Tile T[NT];
         int qt[NT];
         bool qv[NT];
@@ -556,7 +559,8 @@ attn_large_kernel(AttnParams p, LargeLayout L)
                 bk.klo = (const bf16x8*)(kv + half_ch * 32 * 64);
                 bk.v = (const __bf16*)(kv + 2 * half_ch * 32 * 64);
                 __syncthreads();                          // the previous half is consumed
-                stage(bk, (bf16x8*)kv, (bf16x8*)(kv + half_ch * 32 * 64), (__bf16*)(kv + 2 * half_ch * 32 * 64), true);
+                stage_issue(bk, (__bf16*)(kv + 2 * half_ch * 32 * 64));
+                stage_process(bk, (bf16x8*)kv, (bf16x8*)(kv + half_ch * 32 * 64), true);
                 vm_wait_all();
                 __syncthreads();
             }
@@ -623,7 +627,7 @@ size_t large_lds(const Geometry& g, int sim, int pos, LargeLayout* out)
     if (pos == SWIN_POS_TABLE) lds += (size_t)((S * S + 8 + 3) / 4 * 4) * sizeof(float);
     if (pos == SWIN_POS_ROPE2D) lds += (size_t)g.M * 32 * sizeof(float);
     if (sim == SWIN_SIM_COSINE) lds += (size_t)L.NSP * sizeof(float);
-    lds += 32 * sizeof(float);
+    lds += 4 * WAVES * sizeof(float);
     if (out) *out = L;
     return lds;
 }

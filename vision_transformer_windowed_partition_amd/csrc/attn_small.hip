@@ -1,28 +1,32 @@
 // Window attention for windows of up to 256 tokens (M <= 16) on the gfx950
-// matrix cores, with the window's keys and values held in registers.
+// matrix cores, with each window-head's keys and values staged once in LDS.
 //
 // Same computation as the general kernel (SwinV2 card eq. 1-2 and its
 // window-attention pseudocode, log-CPB table of eq. 3-4, cyclic-shift or
-// interleaved windows; rotary positions go to the general kernel), organised
-// for small windows: one wavefront owns (window, head, part of the queries)
-// and loads that window-head's keys and values into MFMA fragments it keeps
-// in registers for all of its query tiles.
-//   K  (keys x d): A operand of S^T = K Q^T (v_mfma_f32_16x16x32_bf16); each
-//      lane loads 16 contiguous bytes of one key from HBM.
-//   V^T (d x keys): A operand of O^T = V^T P^T; V rows are copied to a
-//      wavefront-private LDS area with contiguous 16-byte writes and read
-//      back transposed by ds_read_b64_tr_b16 (within each 16-lane group,
-//      lane i receives element i%4 of the 4-element vectors addressed by
-//      lanes 4j + i/4, j = 0..3), two reads per 8-key fragment.
+// interleaved windows; rotary positions go to the large-window kernel),
+// organised for small windows.  A workgroup of four wavefronts serves one
+// head: for 9 <= M <= 16 all four share one window (each takes every fourth
+// query tile), for M <= 8 each takes a window of its own.  The wavefronts of
+// a window stage it together and then meet at the workgroup's only barrier:
+//   K^ (keys x d): A operand of S^T = K Q^T (v_mfma_f32_16x16x32_bf16); each
+//      lane loads 16 contiguous bytes of one key, the four lanes of a key
+//      unit-normalise it together, and the fragments go to LDS in operand
+//      order (one 16-byte read per lane and tile later);
+//   V  (keys x d): copied by LDS-DMA (buffer_load ... lds) into rows of 64
+//      bytes whose 16-byte pieces are XOR-swizzled through the choice of
+//      source address; A operand of O^T = V^T P^T, read back transposed by
+//      ds_read_b64_tr_b16 per chunk of 32 keys;
+//   the bias table of the head, reversed (consecutive keys read consecutive
+//      floats), in log2 units and shifted by its maximum: every wavefront
+//      reads all of it, so its extrema need no barrier, and writes a quarter.
 // The score tile leaves the MFMA with each lane holding 8 consecutive key
 // slots of one query, the B-operand layout of P^T, so the softmax runs in
 // registers between the two products; row sums come from a third MFMA
-// against an all-ones operand.  The four wavefronts of a workgroup share one
-// head and its bias table in LDS; no workgroup barrier follows the table.
+// against an all-ones operand.
 //
 // Precision.  COSINE normally feeds the MFMA the unit-normalised k^ rounded
 // to bf16; that rounding (2^-9 of the norm) is multiplied by 1/tau, so for
-// tau < 0.1 a wavefront feeds the raw bf16 k (exact) and scales each score by
+// tau < 0.1 a window feeds the raw bf16 k (exact) and scales each score by
 // 1/||k_j|| in fp32 instead.  The softmax uses a static shift (cos <= 1, or
 // Cauchy-Schwarz for DOT) when the spread of the logits stays within 2^60,
 // else the running maximum per 32-key chunk.
@@ -40,30 +44,75 @@ constexpr int WAVES = 4;
 constexpr float RANGE_LIMIT = 60.0f;
 constexpr float PRECISE_TAU = 0.1f;
 
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-
 struct SmallLayout {
     int NSP;                   // key slots in use: M rows of M rounded up to 8
-    int NQT;                   // query tiles per window-head
-    int TPW;                   // query tiles per wavefront item
-    int parts;                 // wavefront items per window-head
-    int per_head;              // items per head, padded to a multiple of WAVES
-    int wgs;                   // workgroups with work: heads * per_head / WAVES
+    int NQT;                   // query tiles of 16 per window
+    int wgs;                   // workgroups with work: heads * window blocks
     int P;                     // work ids per XCD slot
     float inv_M;
 };
 
-template <int NCH>
-struct Frags {                 // this wave's window-head, in MFMA operand layout
-    const bf16x8* k;           // LDS: k^ (or raw k: DOT, precise COSINE), [NCH][2][64 lanes]
-    bf16x8 v[NCH][2];          // V^T, channels 0-15 and 16-31
-    int koff[NCH];             // bias-table offset of this lane's key group: rj*S + c0
-};
+__device__ __forceinline__ float load_f32(Rsrc r, uint32_t off)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// sum of squares of 8 bf16 values (v_dot2_f32_bf16: products exact in fp32)
+__device__ __forceinline__ float sumsq8(const u32x4 w)
+{
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t wi = w[i];         // bit_cast of the subscript itself reads element 0
+        const bf16x2 v = __builtin_bit_cast(bf16x2, wi);
+        s = __builtin_amdgcn_fdot2_f32_bf16(v, v, s, false);
+    }
+    return s;
+}
+
+// Cross-lane steps without LDS.  v_permlane16_swap (v_permlane32_swap)
+// exchanges the odd 16-lane rows (32-lane halves) of its first operand with
+// the even ones of its second: given x twice, every lane gets back its own x
+// and that of lane ^ 16 (^ 32), in one order or the other.
+__device__ __forceinline__ float sum_x16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+template <bool MAX>
+__device__ __forceinline__ float ext2(float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); }
+// DPP row_ror:N (rotate within each row of 16 lanes)
+template <int N>
+__device__ __forceinline__ float row_ror(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
+// maximum (MAX) or minimum over the 64 lanes
+template <bool MAX>
+__device__ __forceinline__ float wave_ext(float x)
+{
+    x = ext2<MAX>(x, row_ror<8>(x));
+    x = ext2<MAX>(x, row_ror<4>(x));
+    x = ext2<MAX>(x, row_ror<2>(x));
+    x = ext2<MAX>(x, row_ror<1>(x));
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = ext2<MAX>(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return ext2<MAX>(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 struct Tile {                  // one query tile of 16 queries
     bf16x8 qf;
     float qscale, negm, mrun;
-    int qoff;
+    float cinit;               // S^T accumulator start: qscale * cinit is the softmax shift
+    int qoff;                  // bias-table offset of this lane's query and key group
     uint32_t gmask;            // chunks whose key group of this lane is allowed (bit c)
     uint32_t colbits;          // allowed columns of this lane's key group (bit e)
     bool exact;
@@ -71,22 +120,25 @@ struct Tile {                  // one query tile of 16 queries
 };
 
 // One pair of query tiles against key chunks [CB, CE) of the window (the
-// others are masked for both tiles).
+// others are masked for both tiles); K^ fragments and V rows come from LDS.
+// The key group of a lane in chunk c starts (4 / GPR) c rows further down
+// the window than in chunk 0: its bias row moves by that many table rows.
 //   MASK: shift regions / padded slots; PRECISE: scores scaled by 1/||k_j||
 //   (raw k operand); EXACT: running maximum instead of the static shift.
-template <int SIM, int POS, int NCH, int CB, int CE, bool MASK, bool PRECISE, bool EXACT>
-__device__ __forceinline__ void run_pair(const Frags<NCH>& F, Tile (&T)[2], const float* bias2,
-                                         const float* kinv, int negrow, int lane, bool partial_any,
+template <int SIM, int POS, int GPR, int CB, int CE, bool MASK, bool PRECISE, bool EXACT>
+__device__ __forceinline__ void run_pair(const bf16x8* kst, const __bf16* vst, Tile (&T)[2], const float* bias2,
+                                         const float* kinv, int S, int negrow, int lane, bool partial_any,
                                          bool precise_rt)
 {
-    const int grp = lane >> 4;
+    const int grp = lane >> 4, li = lane & 15;
     const bool prec = PRECISE && precise_rt;
-    const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
     bf16x8 ones;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 #pragma unroll
     for (int c = CB; c < CE; ++c) {
+        const bf16x8 ka = kst[(c * 2 + 0) * 64 + lane];
+        const bf16x8 kb = kst[(c * 2 + 1) * 64 + lane];
         uint32_t bits[2] = {0xffu, 0xffu};
         if (MASK) {
 #pragma unroll
@@ -103,23 +155,24 @@ __device__ __forceinline__ void run_pair(const Frags<NCH>& F, Tile (&T)[2], cons
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             if (POS == SWIN_POS_TABLE) {
-                const float* bp = bias2 + ((MASK && bits[i] == 0u) ? negrow : F.koff[c] + T[i].qoff);
+                const float* bp = bias2 + ((MASK && bits[i] == 0u) ? negrow : T[i].qoff + (4 / GPR) * c * S);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) add[i][e] = SIM == SWIN_SIM_COSINE ? bp[e] : bp[e] + T[i].negm;
+                for (int e = 0; e < 8; ++e) add[i][e] = bp[e];
             } else {
                 const float a = (MASK && bits[i] == 0u) ? -INFINITY : T[i].negm;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) add[i][e] = a;
             }
         }
-        const bf16x8 ka = F.k[(c * 2 + 0) * 64 + lane];
-        const bf16x8 kb = F.k[(c * 2 + 1) * 64 + lane];
         f32x4 sa[2], sb[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            sa[i] = mfma(ka, T[i].qf, zero4);
-            sb[i] = mfma(kb, T[i].qf, zero4);
+            const f32x4 c4 = {T[i].cinit, T[i].cinit, T[i].cinit, T[i].cinit};
+            sa[i] = mfma(ka, T[i].qf, c4);
+            sb[i] = mfma(kb, T[i].qf, c4);
         }
+        const bf16x8 v0 = vt_frag(vst, c, 0, grp, li);
+        const bf16x8 v1 = vt_frag(vst, c, 1, grp, li);
         bf16x8 pb[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -145,8 +198,12 @@ __device__ __forceinline__ void run_pair(const Frags<NCH>& F, Tile (&T)[2], cons
                     if (MASK) xs[e] = (bits[i] >> e) & 1u ? xs[e] : -INFINITY;
                     cm = fmaxf(cm, xs[e]);
                 }
-                cm = fmaxf(cm, __shfl_xor(cm, 16));
-                cm = fmaxf(cm, __shfl_xor(cm, 32));
+                {
+                    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(cm), __float_as_uint(cm), false, false);
+                    cm = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+                    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(cm), __float_as_uint(cm), false, false);
+                    cm = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+                }
                 const float mnew = fmaxf(T[i].mrun, cm);
                 const float mref = mnew == -INFINITY ? 0.0f : mnew;
                 const float alpha = __builtin_amdgcn_exp2f(T[i].mrun - mref);
@@ -159,20 +216,24 @@ __device__ __forceinline__ void run_pair(const Frags<NCH>& F, Tile (&T)[2], cons
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            T[i].o0 = mfma(F.v[c][0], pb[i], T[i].o0);
-            T[i].o1 = mfma(F.v[c][1], pb[i], T[i].o1);
+            T[i].o0 = mfma(v0, pb[i], T[i].o0);
+            T[i].o1 = mfma(v1, pb[i], T[i].o1);
             T[i].ls = mfma(ones, pb[i], T[i].ls);
         }
     }
 }
 
-template <int SIM, int POS, int NCH>
+// NCH chunks of 32 key slots per window; QW wavefronts per window.
+template <int SIM, int POS, int NCH, int QW>
 __global__ void __launch_bounds__(256)
 attn_small_kernel(AttnParams p, SmallLayout L)
 {
     // groups of 8 key slots per key row: M <= 8 gives 8 slots per row and
     // at most 2 chunks of 32, 9 <= M <= 16 gives 16 slots per row
     constexpr int GPR = NCH <= 2 ? 1 : 2;
+    constexpr int WH = WAVES / QW;                 // windows per workgroup
+    constexpr int SETS = 2 * NCH / QW;             // K tiles and 1 KB V pieces staged per wave
+    constexpr int TQ = NCH <= 2 ? 1 : 4;           // table entries per lane and wave: (2M-1)^2 <= 256 TQ
     extern __shared__ __attribute__((aligned(16))) float smem_f[];
     const Geometry& g = p.g;
     const int M = g.M, N = g.N, S = 2 * M - 1;
@@ -181,258 +242,217 @@ attn_small_kernel(AttnParams p, SmallLayout L)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: item math stays scalar
     const int grp = lane >> 4;       // 16-lane group: k-range of the operands
     const int li = lane & 15;        // row / column inside a 16 x 16 tile
+    const int wh = wave / QW;        // window of this wave within the workgroup
+    const int rank = wave - wh * QW; // rank among the waves of that window
 
     const int tabsz = POS == SWIN_POS_TABLE ? (S * S + 8 + 3) / 4 * 4 : 0;
-    float* bias2 = smem_f;                                           // [S*S + 8] (TABLE)
-    float* red = bias2 + tabsz;                                      // [16]
-    float* kinv = red + 16 + wave * (NCH * 32);                      // [NCH*32] 1/||k|| (precise path)
-    __bf16* vst = (__bf16*)(red + 16 + WAVES * NCH * 32) + wave * (NCH * 32 * D);   // [NCH*32][D] V rows
+    float* bias2 = smem_f;                                            // [S*S + 8] (TABLE)
+    float* red = bias2 + tabsz;                                       // [3 * WAVES]
+    float* kinv = red + 16 + wh * (NCH * 32);                         // [NCH*32] 1/||k|| (precise path)
+    bf16x8* kst = (bf16x8*)(red + 16 + WH * NCH * 32) + wh * (NCH * 2 * 64);       // [NCH][2][64]
+    __bf16* vst = (__bf16*)((bf16x8*)(red + 16 + WH * NCH * 32) + WH * NCH * 2 * 64) + wh * (NCH * 32 * D);
 
-    // ---- item: one head per workgroup, one (window, query part) per wave.
-    // Work ids run window-block-major, head-minor, and each XCD takes a
-    // contiguous range of them (consecutive blockIdx land on different
-    // XCDs): the heads of a window block run back to back on one XCD, so the
-    // 128-byte lines their 64-byte head slices share are fetched once.
+    // ---- item: one head per workgroup, window block-major.  Work ids run
+    // window-block-major, head-minor, and each XCD takes a contiguous range
+    // of them (consecutive blockIdx land on different XCDs): the heads of a
+    // window run back to back on one XCD, so the 128-byte lines their
+    // 64-byte head slices share are fetched once.
     const int work = (blockIdx.x & 7) * L.P + (blockIdx.x >> 3);
-    if (work >= L.wgs) return;                            // whole workgroup, before any barrier
+    if (work >= L.wgs) return;                            // whole workgroup, before the barrier
     const int h = work % g.heads;
-    const int local = (work / g.heads) * WAVES + wave;
-    const bool active = local < g.nwin * L.parts;
-    const int win = active ? local / L.parts : 0;
-    const int part = active ? local - win * L.parts : 0;
+    const int wloc = (work / g.heads) * WH + wh;
+    const bool active = wloc < g.nwin;
+    const int win = active ? wloc : 0;
     const float tau_eff = SIM == SWIN_SIM_COSINE ? fmaxf(p.tau[h], p.tau_min) : 1.0f;
     const float inv_tau = 1.0f / tau_eff;
-
-    // ---- bias table of head h: reversed (consecutive keys read consecutive
-    // floats), in log2 units, shifted by its max (and by 1/tau for COSINE)
-    float bias_range = 0.0f;
-    if (POS == SWIN_POS_TABLE) {
-        float mx = -INFINITY, mn = INFINITY;
-        for (int i = tid; i < S * S; i += 256) {
-            const float v = p.table[(size_t)(S * S - 1 - i) * g.heads + h] * kLog2e;
-            bias2[i] = v;
-            mx = fmaxf(mx, v);
-            mn = fminf(mn, v);
-        }
-        if (tid < 8) bias2[S * S + tid] = -INFINITY;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            mx = fmaxf(mx, __shfl_xor(mx, off));
-            mn = fminf(mn, __shfl_xor(mn, off));
-        }
-        if (lane == 0) { red[wave] = mx; red[4 + wave] = mn; }
-        __syncthreads();
-        mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-        mn = fminf(fminf(red[4], red[5]), fminf(red[6], red[7]));
-        bias_range = mx - mn;
-        const float shift = SIM == SWIN_SIM_COSINE ? mx + kLog2e / tau_eff : mx;
-        __syncthreads();
-        for (int i = tid; i < S * S; i += 256) bias2[i] -= shift;
-        __syncthreads();
-    }
-    if (!active) return;                                  // no workgroup barrier after this point
-
-    // ---- window geometry (wave-uniform)
-    WinGeo wg;
-    const int nW = g.nwr * g.nwc;
-    const int bimg = win / nW, wl = win - bimg * nW;
-    const int wr = wl / g.nwc, wc = wl - wr * g.nwc;
-    wg.colb = (uint32_t)g.C * 2u;
-    int64_t base;
-    int span;                                             // elements of the image (or window)
-    if (g.layout == SWIN_LAYOUT_WINDOWS) {
-        span = N * g.C;
-        base = (int64_t)win * span;
-        wg.r0 = wg.c0 = 0; wg.rs = wg.cs = 1; wg.Hm = wg.Wm = M;
-    } else {
-        span = g.H * g.W * g.C;
-        base = (int64_t)bimg * span;
-        wg.Hm = g.H; wg.Wm = g.W;
-        if (g.part == SWIN_PART_INTERLEAVED) { wg.r0 = wr; wg.c0 = wc; wg.rs = g.nwr; wg.cs = g.nwc; }
-        else { wg.r0 = wr * M + g.shift; wg.c0 = wc * M + g.shift; wg.rs = wg.cs = 1; }
-    }
-    wg.rowb = wg.Wm * wg.colb;
-    const bool cyc_shift = g.part == SWIN_PART_CYCLIC && g.shift > 0;
-    const bool last_r = cyc_shift && wr == g.nwr - 1;
-    const bool last_c = cyc_shift && wc == g.nwc - 1;
-    const bool padded = 8 * GPR != M || NCH * 32 != L.NSP;
-    const bool needs_mask = last_r || last_c || padded;
-    // one buffer resource per tensor, starting at channel h*D of this image
-    // (window); byte offsets are 32-bit and an offset of kNoLoad reads zero
-    const uint32_t bytes = (uint32_t)(span - h * D) * 2u;
-    const Rsrc qr = make_rsrc((const uint16_t*)p.q + base + h * D, bytes);
-    const Rsrc kr = make_rsrc((const uint16_t*)p.k + base + h * D, bytes);
-    const Rsrc vr = make_rsrc((const uint16_t*)p.v + base + h * D, bytes);
-    const Rsrc orr = make_rsrc((const uint16_t*)p.out + base + h * D, bytes);
     const bool precise = SIM == SWIN_SIM_COSINE && tau_eff < PRECISE_TAU;
 
-    // ---- K fragments: tile A of chunk c holds slots 32c + 8(r/4) + r%4,
-    // tile B the next 4 of each group of 8, so that S^T hands this lane slots
-    // 32c + 8 grp + 0..7.  V rows go to LDS (16 bytes per lane, contiguous).
-    // Key slot 8 gam + x is token (gam / GPR, 8 (gam % GPR) + x): a lane's
-    // key row advances by a fixed step per chunk, its column stays put.
-    Frags<NCH> F;
-    u32x4 kraw[NCH][2];
-    {
-        const int rl = (li >> 2) / GPR;
-        uint32_t colk[2];
-        bool cok[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int cj = 8 * ((li >> 2) % GPR) + (li & 3) + 4 * t;
-            colk[t] = wg.col(cj) + 16u * grp;
-            cok[t] = cj < M;
-        }
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int rj = (4 / GPR) * c + rl;
-            const uint32_t rowk = wg.row(rj);
-#pragma unroll
-            for (int t = 0; t < 2; ++t) kraw[c][t] = load16(kr, masked(rowk + colk[t], cok[t] && rj < M));
-        }
-    }
-    {
-        u32x4 vraw[2 * NCH];
-        const int rl = (lane >> 5) / GPR;
-        const int cj = 8 * ((lane >> 5) % GPR) + ((lane >> 2) & 7);
-        const uint32_t colv = wg.col(cj) + 16u * (lane & 3);
-        const bool cok = cj < M;
-#pragma unroll
-        for (int j = 0; j < 2 * NCH; ++j) {               // piece j*64 + lane: slot (.)/4, channels 8*(. % 4)
-            const int rj = (2 / GPR) * j + rl;
-            vraw[j] = load16(vr, masked(wg.row(rj) + colv, cok && rj < M));
-        }
-#pragma unroll
-        for (int j = 0; j < 2 * NCH; ++j) {
-            const int idx = j * 64 + lane, s = idx >> 2, piece = idx & 3;
-            *(u32x4*)(vst + s * D + ((piece ^ v_swizzle(s)) * 8)) = vraw[j];
-        }
-    }
+    const WinPlace wp = place_window(g, win);
+    const WinGeo& wg = wp.wg;
+    const bool padded = 8 * GPR != M || NCH * 32 != L.NSP;
+    const bool needs_mask = wp.last_r || wp.last_c || padded;
+    // one buffer resource per tensor, starting at channel h*D of this image
+    // (window); byte offsets are 32-bit and an offset of kNoLoad reads zero
+    const uint32_t bytes = (uint32_t)(wp.span - h * D) * 2u;
+    const Rsrc qr = make_rsrc((const uint16_t*)p.q + wp.base + h * D, bytes);
+    const Rsrc kr = make_rsrc((const uint16_t*)p.k + wp.base + h * D, bytes);
+    const Rsrc orr = make_rsrc((const uint16_t*)p.out + wp.base + h * D, bytes);
+    const RawRsrc vraw = raw_rsrc((const uint16_t*)p.v + wp.base + h * D, active ? bytes : 0u);
 
-    // ---- V^T fragments from the wave's LDS rows: lane (li, grp) takes
-    // channel 16 dt + li of slots 32c + 8 grp + 0..7.  Transposed read h
-    // covers slots +4h..4h+3: lane li addresses slot + 4h + li/4, channels
-    // 16 dt + 4 (li%4) .. +3, and receives channel 16 dt + li of all four.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---- issue every load of the staging at once.  Key slot 8 gam + x is
+    // token (gam / GPR, 8 (gam % GPR) + x).
+    //   K tile f = 2c + t (this wave: f = rank + QW k): tile A of chunk c
+    //   holds slots 32c + 8(r/4) + r%4, tile B the next 4 of each group of
+    //   8, so that S^T hands a lane slots 32c + 8 grp + 0..7.
+    u32x4 kraw[SETS];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-            i16x4 half[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int s = 32 * c + 8 * grp + 4 * h + (li >> 2);
-                const int m = li & 3;
-                const __bf16* src = vst + s * D + (((2 * dt + (m >> 1)) ^ v_swizzle(s)) * 8) + 4 * (m & 1);
-                half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)src);
-            }
-            const i16x8 v = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
-            F.v[c][dt] = __builtin_bit_cast(bf16x8, v);
-        }
-        const int gam = 4 * c + grp;
-        const int rj = gam / GPR, c0 = (gam % GPR) * 8;
-        F.koff[c] = rj * S + c0;
+    for (int k = 0; k < SETS; ++k) {
+        const int f = rank + QW * k, c = f >> 1, t = f & 1;
+        const int gam = 4 * c + (li >> 2);
+        const int rj = gam / GPR, cj = 8 * (gam % GPR) + (li & 3) + 4 * t;
+        kraw[k] = load16(kr, masked(wg.tok(rj, cj) + 16u * grp, active && rj < M && cj < M));
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();                      // V rows consumed: the area takes K next
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    //   V piece j (1 KB of LDS, this wave: j = rank + QW k): lane l fills
+    //   16 bytes at position 16 l, i.e. slot 16 j + l/4, LDS piece l%4,
+    //   which holds channel piece (l%4) ^ v_swizzle(slot).
+#pragma unroll
+    for (int k = 0; k < SETS; ++k) {
+        const int j = rank + QW * k;
+        const int s = 16 * j + (lane >> 2);
+        const int gam = s >> 3;
+        const int rj = gam / GPR, cj = 8 * (gam % GPR) + (s & 7);
+        const int piece = (lane & 3) ^ v_swizzle(s);
+        dma16(vraw, vst + (size_t)j * 512, masked(wg.tok(rj, cj) + 16u * piece, rj < M && cj < M));
+    }
+    //   the first two query tiles of this wave: tiles rank + QW k
+    u32x4 qpre[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int tq = rank + QW * i;
+        const int t = tq * 16 + li;
+        const bool ok = active && tq < L.NQT && t < N;
+        const int tt = ok ? t : 0;
+        const int ri = qdiv(tt, L.inv_M), ci = tt - ri * M;
+        qpre[i] = load16(qr, masked(wg.tok(ri, ci) + 16u * grp, ok));
+    }
+    //   this wave's quarter of the bias table of head h: rows (wave + 4k) 64
+    //   + lane, the last row standing in for those past the end (extrema
+    //   are unaffected, nothing is written for them)
+    float tv[TQ];
+    if (POS == SWIN_POS_TABLE) {
+        const Rsrc tr = make_rsrc(p.table, (uint32_t)(S * S * g.heads) * 4u);
+#pragma unroll
+        for (int k = 0; k < TQ; ++k) {
+            const int r = min((wave + WAVES * k) * 64 + lane, S * S - 1);
+            tv[k] = load_f32(tr, (uint32_t)__umul24((uint32_t)r, (uint32_t)g.heads) * 4u + (uint32_t)h * 4u);
+        }
+    }
+    vm_wait_all();
+
+    // ---- bias table: this wave's quarter, reversed (row r at S*S - 1 - r),
+    // in log2 units; its extrema go to red for all waves
+    if (POS == SWIN_POS_TABLE) {
+        float mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+        for (int k = 0; k < TQ; ++k) {
+            const int r = (wave + WAVES * k) * 64 + lane;
+            mx = fmaxf(mx, tv[k]);
+            mn = fminf(mn, tv[k]);
+            if (r < S * S) bias2[S * S - 1 - r] = tv[k] * kLog2e;
+        }
+        mx = wave_ext<true>(mx);
+        mn = wave_ext<false>(mn);
+        if (lane == 0) { red[WAVES + wave] = mx; red[2 * WAVES + wave] = mn; }
+        if (wave == 0 && lane < 8) bias2[S * S + lane] = -INFINITY;
+    }
 
     // ---- k: unit-normalise (COSINE), or keep raw and record 1/||k||
     // (precise COSINE) or the largest ||k|| (DOT); fragments to LDS in
     // operand order, one 16-byte write per lane and tile
-    bf16x8* kst = (bf16x8*)vst;
     float kmax = 0.0f;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            float kf[8];
-            unpack_bf16x8(kraw[c][t], kf);
-            float ss = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf(kf[e], kf[e], ss);
-            ss += __shfl_xor(ss, 16);
-            ss += __shfl_xor(ss, 32);
-            bf16x8 kfrag;
-            if (SIM == SWIN_SIM_COSINE) {
-                const float inv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));   // 1 / max(||k||, 1e-12)
-                if (precise) {
-                    if (grp == 0) kinv[32 * c + 8 * (li >> 2) + (li & 3) + 4 * t] = inv;
-                    kfrag = *(const bf16x8*)&kraw[c][t];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) kf[e] *= inv;
-                    kfrag = pack_bf16x8(kf);
-                }
+    for (int k = 0; k < SETS; ++k) {
+        const int f = rank + QW * k, c = f >> 1, t = f & 1;
+        const float ss = sum_x32(sum_x16(sumsq8(kraw[k])));
+        bf16x8 kfrag;
+        if (SIM == SWIN_SIM_COSINE) {
+            const float inv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));   // 1 / max(||k||, 1e-12)
+            if (precise) {
+                if (grp == 0) kinv[32 * c + 8 * (li >> 2) + (li & 3) + 4 * t] = inv;
+                kfrag = *(const bf16x8*)&kraw[k];
             } else {
-                kmax = fmaxf(kmax, ss);
-                kfrag = *(const bf16x8*)&kraw[c][t];
-            }
-            kst[(c * 2 + t) * 64 + lane] = kfrag;
-        }
-    if (SIM == SWIN_SIM_DOT) {
+                float kf[8];
+                unpack_bf16x8(kraw[k], kf);
 #pragma unroll
-        for (int off = 16; off > 0; off >>= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, off));
+                for (int e = 0; e < 8; ++e) kf[e] *= inv;
+                kfrag = pack_bf16x8(kf);
+            }
+        } else {
+            kmax = fmaxf(kmax, ss);
+            kfrag = *(const bf16x8*)&kraw[k];
+        }
+        kst[f * 64 + lane] = kfrag;
+    }
+    if (SIM == SWIN_SIM_DOT) {
+        kmax = wave_ext<true>(kmax);
+        if (lane == 0) red[wave] = kmax;
+    }
+    __syncthreads();                                      // K^, V, table and red complete
+    if (!active) return;
+    if (SIM == SWIN_SIM_DOT) {
+        kmax = red[wh * QW];
+#pragma unroll
+        for (int r = 1; r < QW; ++r) kmax = fmaxf(kmax, red[wh * QW + r]);
         kmax = sqrtf(kmax);                               // largest ||k|| of the window
     }
-    F.k = kst;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // table extrema (log2 units): the static shift puts the largest
+    // possible logit at 0 (COSINE: cos <= 1; DOT: Cauchy-Schwarz per query)
+    float bias_max = 0.0f, bias_range = 0.0f;
+    if (POS == SWIN_POS_TABLE) {
+        float mx = red[WAVES], mn = red[2 * WAVES];
+#pragma unroll
+        for (int r = 1; r < WAVES; ++r) { mx = fmaxf(mx, red[WAVES + r]); mn = fminf(mn, red[2 * WAVES + r]); }
+        bias_max = mx * kLog2e;
+        bias_range = (mx - mn) * kLog2e;
+    }
 
-    // ---- this wave's query tiles, two at a time
-    const int tfirst = part * L.TPW;
-    const int tlast = min(tfirst + L.TPW, L.NQT);
-    for (int t0 = tfirst; t0 < tlast; t0 += 2) {
+    // ---- this wave's query tiles rank + QW k, two at a time
+    const int kbase = (grp / GPR) * S + 8 * (grp % GPR);  // bias offset of this lane's key group in chunk 0
+    for (int k0 = 0; rank + QW * k0 < L.NQT; k0 += 2) {
         Tile T[2];
         int qt[2];
         bool qv[2];
         u32x4 qraw[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int t = (t0 + i) * 16 + li;
-            qv[i] = t0 + i < tlast && t < N;
+            const int tq = rank + QW * (k0 + i);
+            const int t = tq * 16 + li;
+            qv[i] = tq < L.NQT && t < N;
             qt[i] = qv[i] ? t : 0;
-            const int ri = qdiv(qt[i], L.inv_M), ci = qt[i] - ri * M;
-            qraw[i] = load16(qr, masked(wg.tok(ri, ci) + 16u * grp, qv[i]));
+            if (k0 == 0) qraw[i] = qpre[i];
+            else {
+                const int ri = qdiv(qt[i], L.inv_M), ci = qt[i] - ri * M;
+                qraw[i] = load16(qr, masked(wg.tok(ri, ci) + 16u * grp, qv[i]));
+            }
         }
         bool any_exact = false, partial = false;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int ri = qdiv(qt[i], L.inv_M), ci = qt[i] - ri * M;
-            float qf[8];
-            unpack_bf16x8(qraw[i], qf);
-            T[i].qf = pack_bf16x8(qf);
-            float ss = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf(qf[e], qf[e], ss);
-            ss += __shfl_xor(ss, 16);
-            ss += __shfl_xor(ss, 32);
-            float spread;
+            const u32x4 qw = qraw[i];
+            T[i].qf = __builtin_bit_cast(bf16x8, qw);
+            const float ss = sum_x32(sum_x16(sumsq8(qraw[i])));
+            float spread, shift;
             if (SIM == SWIN_SIM_COSINE) {
                 T[i].qscale = kLog2e * inv_tau * __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
-                T[i].negm = POS == SWIN_POS_TABLE ? 0.0f : -kLog2e * inv_tau;
+                T[i].negm = -kLog2e * inv_tau;
                 spread = 2.0f * kLog2e * inv_tau + bias_range;
+                shift = kLog2e * inv_tau + bias_max;
             } else {
                 T[i].qscale = kLog2e * 0.17677669529663687f;          // log2(e) / sqrt(32)
                 const float c_i = sqrtf(ss) * kmax * T[i].qscale;
                 T[i].negm = -c_i;
                 spread = 2.0f * c_i + bias_range;
+                shift = c_i + bias_max;
             }
-            T[i].exact = __any(!(spread <= RANGE_LIMIT)) != 0;
+            // TABLE: the shift enters through the accumulator of S^T (the
+            // per-key scale of the precise path rules that out there: it
+            // takes the running maximum); no table: it is the added term
+            T[i].exact = precise || __any(!(spread <= RANGE_LIMIT)) != 0;
+            T[i].cinit = POS == SWIN_POS_TABLE && !precise ? -shift / T[i].qscale : 0.0f;
             any_exact = any_exact || T[i].exact;
             T[i].mrun = -INFINITY;
-            T[i].qoff = (M - 1 - ri) * S + (M - 1 - ci);
-            int rlo = 0, rhi = M, clo = 0, chi = M;
-            if (last_r) { if (ri < M - g.shift) rhi = M - g.shift; else rlo = M - g.shift; }
-            if (last_c) { if (ci < M - g.shift) chi = M - g.shift; else clo = M - g.shift; }
-            const uint32_t cmask = (chi >= 32 ? 0xffffffffu : ((1u << chi) - 1u)) & ~((1u << clo) - 1u);
-            // this lane's key group in chunk c: row (4/GPR) c + grp/GPR, columns
-            // 8 (grp % GPR) .. +7; allowed chunks are those whose row lies in
-            // [rlo, rhi), if the columns are allowed at all
-            {
+            T[i].qoff = (M - 1 - ri) * S + (M - 1 - ci) + kbase;
+            T[i].colbits = 0xffu;
+            T[i].gmask = 0xffffffffu;
+            if (needs_mask) {
+                int rlo = 0, rhi = M, clo = 0, chi = M;
+                if (wp.last_r) { if (ri < M - g.shift) rhi = M - g.shift; else rlo = M - g.shift; }
+                if (wp.last_c) { if (ci < M - g.shift) chi = M - g.shift; else clo = M - g.shift; }
+                const uint32_t cmask = (chi >= 32 ? 0xffffffffu : ((1u << chi) - 1u)) & ~((1u << clo) - 1u);
+                // this lane's key group in chunk c: row (4/GPR) c + grp/GPR, columns
+                // 8 (grp % GPR) .. +7; allowed chunks are those whose row lies in
+                // [rlo, rhi), if the columns are allowed at all
                 constexpr int STEP = 4 / GPR, SH = STEP == 4 ? 2 : 1;
                 const int rl = grp / GPR;
                 T[i].colbits = (cmask >> (8 * (grp % GPR))) & 0xffu;
@@ -440,16 +460,16 @@ attn_small_kernel(AttnParams p, SmallLayout L)
                 const int ce = min(NCH, (rhi - rl + STEP - 1) >> SH);
                 const uint32_t rows = ce > cb ? ((ce >= 32 ? 0xffffffffu : (1u << ce) - 1u) & ~((1u << cb) - 1u)) : 0u;
                 T[i].gmask = T[i].colbits ? rows : 0u;
+                // groups split by a region edge or by padding
+                partial = partial || (wp.last_c && ((M - g.shift) & 7)) || (M & 7);
             }
-            // groups split by a region edge or by padding
-            if (needs_mask) partial = partial || (last_c && ((M - g.shift) & 7)) || (M & 7);
             T[i].o0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             T[i].o1 = T[i].o0;
             T[i].ls = T[i].o0;
         }
         const int negrow = S * S;
         if (any_exact || precise)
-            run_pair<SIM, POS, NCH, 0, NCH, true, true, true>(F, T, bias2, kinv, negrow, lane, true, precise);
+            run_pair<SIM, POS, GPR, 0, NCH, true, true, true>(kst, vst, T, bias2, kinv, S, negrow, lane, true, precise);
         else if (needs_mask) {
             // chunks some lane of the pair may see: all, or one half of the key rows
             uint32_t live = T[0].gmask | T[1].gmask;
@@ -458,14 +478,17 @@ attn_small_kernel(AttnParams p, SmallLayout L)
             live = (uint32_t)__builtin_amdgcn_readfirstlane((int)live);
             constexpr uint32_t lo_half = (1u << (NCH / 2)) - 1u;
             if ((live & ~lo_half) == 0u)
-                run_pair<SIM, POS, NCH, 0, NCH / 2, true, false, false>(F, T, bias2, kinv, negrow, lane, partial, false);
+                run_pair<SIM, POS, GPR, 0, NCH / 2, true, false, false>(kst, vst, T, bias2, kinv, S, negrow, lane,
+                                                                        partial, false);
             else if ((live & lo_half) == 0u)
-                run_pair<SIM, POS, NCH, NCH / 2, NCH, true, false, false>(F, T, bias2, kinv, negrow, lane, partial,
-                                                                          false);
+                run_pair<SIM, POS, GPR, NCH / 2, NCH, true, false, false>(kst, vst, T, bias2, kinv, S, negrow, lane,
+                                                                          partial, false);
             else
-                run_pair<SIM, POS, NCH, 0, NCH, true, false, false>(F, T, bias2, kinv, negrow, lane, partial, false);
+                run_pair<SIM, POS, GPR, 0, NCH, true, false, false>(kst, vst, T, bias2, kinv, S, negrow, lane,
+                                                                    partial, false);
         } else
-            run_pair<SIM, POS, NCH, 0, NCH, false, false, false>(F, T, bias2, kinv, negrow, lane, false, false);
+            run_pair<SIM, POS, GPR, 0, NCH, false, false, false>(kst, vst, T, bias2, kinv, S, negrow, lane, false,
+                                                                 false);
 
         // ---- normalise and store: lane holds channels 4 grp..+3 and
         // 16 + 4 grp..+3 of query li
@@ -483,9 +506,9 @@ attn_small_kernel(AttnParams p, SmallLayout L)
 template <int SIM, int POS>
 hipError_t launch_nch(const AttnParams& p, const SmallLayout& L, int nch, int grid, size_t lds, hipStream_t s)
 {
-    auto* fn = nch <= 2 ? attn_small_kernel<SIM, POS, 2>
-             : nch <= 6 ? attn_small_kernel<SIM, POS, 6>
-                        : attn_small_kernel<SIM, POS, 8>;
+    auto* fn = nch <= 2 ? attn_small_kernel<SIM, POS, 2, 1>
+             : nch <= 6 ? attn_small_kernel<SIM, POS, 6, 4>
+                        : attn_small_kernel<SIM, POS, 8, 4>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -512,19 +535,17 @@ hipError_t launch_attn_small(const AttnParams& p, hipStream_t stream)
     SmallLayout L;
     L.NSP = g.M * ((g.M + 7) / 8 * 8);
     L.NQT = (g.N + 15) / 16;
-    L.TPW = L.NQT > 8 ? 8 : L.NQT;
-    L.parts = (L.NQT + L.TPW - 1) / L.TPW;
-    L.per_head = (g.nwin * L.parts + WAVES - 1) / WAVES * WAVES;
     L.inv_M = 1.0f / (float)g.M;
     const int nch_real = (L.NSP + 31) / 32;
     const int nch = nch_real <= 2 ? 2 : nch_real <= 6 ? 6 : 8;      // M <= 8, 9-12, 13-16
+    const int wh = nch <= 2 ? WAVES : 1;                            // windows per workgroup
     const int S = 2 * g.M - 1;
-    const int64_t wgs = (int64_t)g.heads * L.per_head / WAVES;
+    const int64_t wgs = (int64_t)g.heads * ((g.nwin + wh - 1) / wh);
     if (wgs > INT32_MAX - 8) return hipErrorInvalidValue;
     L.wgs = (int)wgs;
     L.P = (int)((wgs + 7) / 8);
     const int64_t grid = 8 * (int64_t)L.P;
-    size_t lds = (size_t)(16 + WAVES * nch * 32) * sizeof(float) + (size_t)WAVES * nch * 32 * D * 2;
+    size_t lds = (size_t)(16 + wh * nch * 32) * sizeof(float) + (size_t)wh * nch * 32 * D * 2 * 2;
     if (p.pos == SWIN_POS_TABLE) lds += (size_t)((S * S + 8 + 3) / 4 * 4) * sizeof(float);
     if (p.sim == SWIN_SIM_COSINE) {
         if (p.pos == SWIN_POS_TABLE) return launch_nch<SWIN_SIM_COSINE, SWIN_POS_TABLE>(p, L, nch, (int)grid, lds, stream);

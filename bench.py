@@ -44,7 +44,7 @@ KERNEL_SOURCE = {"attn_small_kernel": "attn_small.hip", "attn_large_kernel": "at
 def kernel_sha(kernel: str) -> str:
     """Hash of the sources that define `kernel` (its file and the shared headers)."""
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCE[kernel], "common.hpp", "launch.hpp", "tile_io.hpp"):
+    for f in (KERNEL_SOURCE[kernel], "common.hpp", "launch.hpp", "tile_io.hpp", "lanes.hpp"):
         with open(os.path.join(ROOT, "vision_transformer_windowed_partition_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -32,6 +32,7 @@
 // else the running maximum per 32-key chunk.
 #include "common.hpp"
 #include "launch.hpp"
+#include "lanes.hpp"
 #include "tile_io.hpp"
 
 namespace swin {
@@ -39,6 +40,7 @@ namespace swin {
 namespace {
 
 using namespace tio;
+using namespace lanes;
 
 constexpr int WAVES = 4;
 constexpr float RANGE_LIMIT = 60.0f;
@@ -70,42 +72,6 @@ __device__ __forceinline__ float sumsq8(const u32x4 w)
         s = __builtin_amdgcn_fdot2_f32_bf16(v, v, s, false);
     }
     return s;
-}
-
-// Cross-lane steps without LDS.  v_permlane16_swap (v_permlane32_swap)
-// exchanges the odd 16-lane rows (32-lane halves) of its first operand with
-// the even ones of its second: given x twice, every lane gets back its own x
-// and that of lane ^ 16 (^ 32), in one order or the other.
-__device__ __forceinline__ float sum_x16(float x)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float sum_x32(float x)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-template <bool MAX>
-__device__ __forceinline__ float ext2(float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); }
-// DPP row_ror:N (rotate within each row of 16 lanes)
-template <int N>
-__device__ __forceinline__ float row_ror(float x)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
-}
-// maximum (MAX) or minimum over the 64 lanes
-template <bool MAX>
-__device__ __forceinline__ float wave_ext(float x)
-{
-    x = ext2<MAX>(x, row_ror<8>(x));
-    x = ext2<MAX>(x, row_ror<4>(x));
-    x = ext2<MAX>(x, row_ror<2>(x));
-    x = ext2<MAX>(x, row_ror<1>(x));
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = ext2<MAX>(__uint_as_float(r[0]), __uint_as_float(r[1]));
-    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return ext2<MAX>(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 struct Tile {                  // one query tile of 16 queries
@@ -198,12 +164,7 @@ __device__ __forceinline__ void run_pair(const bf16x8* kst, const __bf16* vst, T
                     if (MASK) xs[e] = (bits[i] >> e) & 1u ? xs[e] : -INFINITY;
                     cm = fmaxf(cm, xs[e]);
                 }
-                {
-                    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(cm), __float_as_uint(cm), false, false);
-                    cm = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-                    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(cm), __float_as_uint(cm), false, false);
-                    cm = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-                }
+                cm = max_x32(max_x16(cm));
                 const float mnew = fmaxf(T[i].mrun, cm);
                 const float mref = mnew == -INFINITY ? 0.0f : mnew;
                 const float alpha = __builtin_amdgcn_exp2f(T[i].mrun - mref);
@@ -340,8 +301,8 @@ attn_small_kernel(AttnParams p, SmallLayout L)
             mn = fminf(mn, tv[k]);
             if (r < S * S) bias2[S * S - 1 - r] = tv[k] * kLog2e;
         }
-        mx = wave_ext<true>(mx);
-        mn = wave_ext<false>(mn);
+        mx = wave_reduce<Op::Max>(mx);
+        mn = wave_reduce<Op::Min>(mn);
         if (lane == 0) { red[WAVES + wave] = mx; red[2 * WAVES + wave] = mn; }
         if (wave == 0 && lane < 8) bias2[S * S + lane] = -INFINITY;
     }
@@ -374,7 +335,7 @@ attn_small_kernel(AttnParams p, SmallLayout L)
         kst[f * 64 + lane] = kfrag;
     }
     if (SIM == SWIN_SIM_DOT) {
-        kmax = wave_ext<true>(kmax);
+        kmax = wave_reduce<Op::Max>(kmax);
         if (lane == 0) red[wave] = kmax;
     }
     __syncthreads();                                      // K^, V, table and red complete

@@ -3,51 +3,104 @@
 // network G = W2 relu(W1 (f(dx), f(dy)) + b1) + b2 with f(x) = sign(x)
 // ln(1+|x|) is evaluated once and stored, one column per head.
 //
-// One workgroup per offset: its threads evaluate the hidden layer into LDS,
-// then each wavefront reduces the output-layer dot products of a subset of
-// heads.  At most 41 MFLOP for a 47 x 47 offset grid: latency bound, run once
-// per layer and window size, never inside the attention call.
+// One wavefront per (offset, group of up to four heads): lane j evaluates
+// hidden units j, j + 64, ... of its offset and accumulates their share of
+// the group's output dot products, then a cross-lane sum finishes them.  All
+// weights a wavefront needs are requested at once (one memory latency per
+// 512 hidden units), and nothing is shared between wavefronts: no LDS, no
+// barrier.  The hidden layer is recomputed per head group (2 of the ~2 + HG
+// multiply-adds per unit).  At most 41 MFLOP for a 47 x 47 offset grid.
 #include "common.hpp"
+#include "lanes.hpp"
 #include "launch.hpp"
 
 namespace swin {
 
-__global__ void __launch_bounds__(256)
-cpb_table_kernel(int M, int heads, int hidden, const float* __restrict__ w1,
-                 const float* __restrict__ b1, const float* __restrict__ w2,
-                 const float* __restrict__ b2, float* __restrict__ table)
+namespace {
+
+constexpr int HG = 4;          // heads per wavefront
+constexpr int UPL = 8;         // hidden units per lane and pass (512 per pass)
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kNoLoad = 0x80000000u;     // beyond every record count here: reads zero
+__device__ __forceinline__ Rsrc rsrc(const void* base, uint32_t bytes)
 {
-    extern __shared__ float hid[];                 // hidden activations of this offset
-    const int S = 2 * M - 1;
-    const int row = blockIdx.x;                    // (dy + M-1)*S + (dx + M-1)
-    const int dy = row / S - (M - 1);
-    const int dx = row % S - (M - 1);
-    const float fx = dx > 0 ? log1pf((float)dx) : (dx < 0 ? -log1pf((float)-dx) : 0.0f);
-    const float fy = dy > 0 ? log1pf((float)dy) : (dy < 0 ? -log1pf((float)-dy) : 0.0f);
-    for (int j = threadIdx.x; j < hidden; j += blockDim.x) {
-        float a = fmaf(w1[2 * j], fx, fmaf(w1[2 * j + 1], fy, b1 ? b1[j] : 0.0f));
-        hid[j] = a > 0.0f ? a : 0.0f;
-    }
-    __syncthreads();
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int nwave = blockDim.x >> 6;
-    for (int o = wave; o < heads; o += nwave) {
-        const float* w = w2 + (size_t)o * hidden;
-        float acc = 0.0f;
-        for (int j = lane; j < hidden; j += 64) acc = fmaf(w[j], hid[j], acc);
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-        if (lane == 0) table[(size_t)row * heads + o] = acc + (b2 ? b2[o] : 0.0f);
-    }
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+__device__ __forceinline__ float ld1(Rsrc r, uint32_t off)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 ld2(Rsrc r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+
+__device__ __forceinline__ float signed_log1p(int x)
+{
+    return x > 0 ? log1pf((float)x) : (x < 0 ? -log1pf((float)-x) : 0.0f);
+}
+
+__global__ void __launch_bounds__(256)
+cpb_table_kernel(int M, int heads, int hidden, const float* __restrict__ w1, const float* __restrict__ b1,
+                 const float* __restrict__ w2, const float* __restrict__ b2, float* __restrict__ table,
+                 int items)
+{
+    const int lane = threadIdx.x & 63;
+    const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+    if (item >= items) return;
+    const int groups = (heads + HG - 1) / HG;
+    const int row = item / groups;                 // (dy + M-1)*S + (dx + M-1)
+    const int o0 = (item - row * groups) * HG;     // first head of the group
+    const int S = 2 * M - 1;
+    const float fx = signed_log1p(row % S - (M - 1));
+    const float fy = signed_log1p(row / S - (M - 1));
+
+    // null biases: an empty resource, whose loads read zero
+    const Rsrc r1 = rsrc(w1, (uint32_t)hidden * 8u);
+    const Rsrc rb1 = rsrc(b1, b1 ? (uint32_t)hidden * 4u : 0u);
+    const Rsrc r2 = rsrc(w2, (uint32_t)(heads * hidden) * 4u);
+    float acc[HG] = {};
+    for (int u0 = 0; u0 < hidden; u0 += 64 * UPL) {
+        u32x2 w[UPL];
+        float bb[UPL], v2[HG][UPL];
+#pragma unroll
+        for (int k = 0; k < UPL; ++k) {
+            const int u = u0 + k * 64 + lane;
+            const bool ok = u < hidden;
+            w[k] = ld2(r1, ok ? (uint32_t)u * 8u : kNoLoad);
+            bb[k] = ld1(rb1, ok ? (uint32_t)u * 4u : kNoLoad);
+#pragma unroll
+            for (int o = 0; o < HG; ++o)
+                v2[o][k] = ld1(r2, ok && o0 + o < heads ? (uint32_t)((o0 + o) * hidden + u) * 4u : kNoLoad);
+        }
+#pragma unroll
+        for (int k = 0; k < UPL; ++k) {
+            // input 0 is the column (width) offset, input 1 the row offset
+            const float a = fmaf(__uint_as_float(w[k][0]), fx, fmaf(__uint_as_float(w[k][1]), fy, bb[k]));
+            const float hk = fmaxf(a, 0.0f);
+#pragma unroll
+            for (int o = 0; o < HG; ++o) acc[o] = fmaf(v2[o][k], hk, acc[o]);
+        }
+    }
+    float mine = 0.0f;
+#pragma unroll
+    for (int o = 0; o < HG; ++o) {
+        const float s = lanes::wave_reduce<lanes::Op::Sum>(acc[o]);
+        mine = lane == o ? s : mine;
+    }
+    if (lane < HG && o0 + lane < heads)
+        table[(size_t)row * heads + o0 + lane] = mine + (b2 ? b2[o0 + lane] : 0.0f);
+}
+
+}  // namespace
 
 hipError_t launch_cpb_table(int M, int heads, int hidden, const float* w1, const float* b1,
                             const float* w2, const float* b2, float* table, hipStream_t stream)
 {
     const int S = 2 * M - 1;
-    cpb_table_kernel<<<S * S, 256, (size_t)hidden * sizeof(float), stream>>>(
-        M, heads, hidden, w1, b1, w2, b2, table);
+    const int items = S * S * ((heads + HG - 1) / HG);
+    cpb_table_kernel<<<(items + 3) / 4, 256, 0, stream>>>(M, heads, hidden, w1, b1, w2, b2, table, items);
     return hipGetLastError();
 }
 

@@ -79,10 +79,14 @@ enum swin_dtype { SWIN_DT_F32 = 0, SWIN_DT_BF16 = 1 };
  * each window's place in the grid. */
 enum swin_layout { SWIN_LAYOUT_GRID = 0, SWIN_LAYOUT_WINDOWS = 1 };
 
-/* Log-CPB variants.  PAPER ([SwinV2] eq. 4): inputs sign(x) ln(1+|x|) of the
- * raw offsets, output unbounded.  (The released code's normalised log2 form
- * and 16*sigmoid output are not built.) */
-enum swin_cpb_mode { SWIN_CPB_PAPER = 0 };
+/* Log-CPB variants, as flags.  PAPER = 0 ([SwinV2] eq. 4): inputs
+ * sign(x) ln(1+|x|) of the raw offsets, output unbounded.  The released
+ * code's forms ([SwinV2] card, "Paper vs code"):
+ *   CODE_NORM: inputs sign(u) log2(1+|u|) / log2(8) of u = 8 x / (norm_M - 1),
+ *              norm_M the pretrained window (or the window itself);
+ *   SIGMOID16: output 16 * sigmoid(G), in (0, 16).
+ * CODE_NORM | SIGMOID16 (= 3) is the released code. */
+enum swin_cpb_mode { SWIN_CPB_PAPER = 0, SWIN_CPB_CODE_NORM = 1, SWIN_CPB_SIGMOID16 = 2 };
 
 typedef struct swin_attn_desc {
     int32_t B, H, W, C, heads;  /* C % heads == 0; d = C/heads must be 32        */
@@ -105,10 +109,23 @@ typedef struct swin_attn_desc {
  *   the column offset and G's first input).
  * w1: hidden x 2, b1: hidden (or NULL = 0), w2: heads x hidden, b2: heads (or
  * NULL = 0), all fp32 row-major on the device.  table: (2M-1)^2 x heads fp32.
- * 1 <= M <= 64, 1 <= heads <= 64, 1 <= hidden <= 4096, cpb_mode == PAPER. */
+ * 1 <= M <= 64, 1 <= heads <= 64, 1 <= hidden <= 4096, 0 <= cpb_mode <= 3;
+ * under CODE_NORM the offsets are normalised by this window (M >= 2).
+ * Errors: SWIN_EINVAL for a bad size or mode, a NULL w1/w2/table, or a table
+ * overlapping a parameter; nothing is written then. */
 int swin_cpb_table(int32_t M, int32_t heads, int32_t hidden,
                    const float* w1, const float* b1, const float* w2, const float* b2,
                    int32_t cpb_mode, float* table, void* stream);
+
+/* The same table for window M with the CODE_NORM offsets normalised by
+ * norm_M - 1 instead ([SwinV2] card, Method item 3: a model trained at one
+ * window size runs at another; "Paper vs code": the code divides by the
+ * pretrained window less one).  2 <= norm_M <= 4096 when cpb_mode has
+ * CODE_NORM; otherwise norm_M is ignored.  Same arguments, layout, ownership
+ * and errors as swin_cpb_table. */
+int swin_cpb_table_ex(int32_t M, int32_t norm_M, int32_t heads, int32_t hidden,
+                      const float* w1, const float* b1, const float* w2, const float* b2,
+                      int32_t cpb_mode, float* table, void* stream);
 
 /* Window partition (gather) of a (B, H, W, C) grid into (B*nW, M*M, C), and
  * its inverse (scatter).  A bit-exact copy of C elements per token; dtype

@@ -54,6 +54,10 @@ def _declare(lib):
     lib.oracle_log_offset.argtypes = [dbl]
     lib.oracle_cpb_table.restype = i32
     lib.oracle_cpb_table.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+    lib.oracle_cpb_table_mode.restype = i32
+    lib.oracle_cpb_table_mode.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, i32, vp]
+    lib.oracle_code_offset.restype = ctypes.c_double
+    lib.oracle_code_offset.argtypes = [ctypes.c_double, i32]
     for fn in (lib.oracle_partition, lib.oracle_reverse):
         fn.restype = i32
         fn.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
@@ -101,15 +105,30 @@ def log_offset(x: float, lib=None) -> float:
     return float((lib or load()).oracle_log_offset(float(x)))
 
 
-def cpb_table(M: int, w1, b1, w2, b2, lib=None) -> np.ndarray:
-    """(2M-1)^2 x heads bias table of the meta network G (SwinV2 eq. 3-4)."""
+CPB_CODE_NORM, CPB_SIGMOID16 = 1, 2       # flags; 3 = the released code's form
+
+
+def code_offset(x: float, norm_M: int, lib=None) -> float:
+    """Released-code transform: u = 8 x / (norm_M - 1), sign(u) log2(1+|u|) / log2(8)."""
+    return float((lib or load()).oracle_code_offset(float(x), int(norm_M)))
+
+
+def cpb_table(M: int, w1, b1, w2, b2, lib=None, mode: int = 0, norm_M: int | None = None) -> np.ndarray:
+    """(2M-1)^2 x heads bias table of the meta network G (SwinV2 eq. 3-4).
+    mode 0 is the paper's form; bit 0 the released code's coordinate
+    transform (offsets normalised by norm_M - 1, default M - 1), bit 1 its
+    16 * sigmoid output bound."""
     w1, w2 = _f64(w1), _f64(w2)
     b1, b2 = _f64(b1), _f64(b2)
     hidden, heads = w1.shape[0], w2.shape[0]
     assert w1.shape == (hidden, 2) and w2.shape == (heads, hidden)
     out = np.empty(((2 * M - 1) ** 2, heads), dtype=np.float64)
-    rc = (lib or load()).oracle_cpb_table(M, heads, hidden, _ptr(w1), _ptr(b1),
-                                          _ptr(w2), _ptr(b2), _ptr(out))
+    L = lib or load()
+    if mode == 0 and norm_M is None:
+        rc = L.oracle_cpb_table(M, heads, hidden, _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(out))
+    else:
+        rc = L.oracle_cpb_table_mode(M, M if norm_M is None else norm_M, heads, hidden, _ptr(w1), _ptr(b1),
+                                     _ptr(w2), _ptr(b2), int(mode), _ptr(out))
     if rc:
         raise ValueError(f"oracle_cpb_table: bad argument (rc={rc})")
     return out

@@ -66,6 +66,27 @@ double oracle_log_offset(double x)
     return 0.0;
 }
 
+/* The released code's coordinate transform ([SwinV2] card, "Paper vs code",
+ * CPB coordinate transform): the offset is divided by (norm_M - 1), where
+ * norm_M is the pretrained window when one is set and the window itself
+ * otherwise, multiplied by 8, and mapped to sign(u) log2(1 + |u|) / log2(8).
+ * Reading: norm_M < 2 has no such transform (the divisor is zero); callers
+ * reject it. */
+double oracle_code_offset(double x, int norm_M)
+{
+    const double u = x / (double)(norm_M - 1) * 8.0;
+    const double a = log2(1.0 + fabs(u)) / log2(8.0);
+    if (u > 0) return a;
+    if (u < 0) return -a;
+    return 0.0;
+}
+
+/* CPB variants, as flags: 0 = the paper's form (eq. 3-4, output unbounded);
+ * bit 0 = the code's coordinate transform above; bit 1 = the code's bounded
+ * output 16 * sigmoid(G) ([SwinV2] card, "Paper vs code", CPB output
+ * bounded).  3 = the released code. */
+enum { OR_CPB_CODE_NORM = 1, OR_CPB_SIGMOID16 = 2 };
+
 /* [SwinV2] eq. 3 + eq. 4, Method item 3: the bias for relative offset
  * (dy, dx) = (row offset, column offset) between query and key is the meta
  * network G applied to the log-spaced offset, G(x) = W2 relu(W1 x + b1) + b2.
@@ -73,19 +94,25 @@ double oracle_log_offset(double x)
  * is the column (x) offset and its second the row (y) offset; W1 is hidden x 2
  * row-major, W2 is heads x hidden row-major; a NULL bias vector is zero.
  * The table is stored once per relative position (Method item 3), row
- * (dy + M-1)*(2M-1) + (dx + M-1), one column per head. */
-int oracle_cpb_table(int M, int heads, int hidden,
-                     const double* w1, const double* b1,
-                     const double* w2, const double* b2, double* table)
+ * (dy + M-1)*(2M-1) + (dx + M-1), one column per head.  mode selects the
+ * coordinate transform and output bound (flags above); norm_M is the window
+ * whose size less one normalises the offsets under the code's transform. */
+int oracle_cpb_table_mode(int M, int norm_M, int heads, int hidden,
+                          const double* w1, const double* b1,
+                          const double* w2, const double* b2, int mode, double* table)
 {
     if (M < 1 || heads < 1 || hidden < 1 || !w1 || !w2 || !table) return 1;
+    if (mode < 0 || mode > 3) return 1;
+    if ((mode & OR_CPB_CODE_NORM) && norm_M < 2) return 1;
     const int S = 2 * M - 1;
     double* h = (double*)malloc((size_t)hidden * sizeof(double));
     if (!h) return 2;
     for (int dy = -(M - 1); dy <= M - 1; ++dy) {
         for (int dx = -(M - 1); dx <= M - 1; ++dx) {
-            const double in0 = oracle_log_offset((double)dx);
-            const double in1 = oracle_log_offset((double)dy);
+            const double in0 = (mode & OR_CPB_CODE_NORM) ? oracle_code_offset((double)dx, norm_M)
+                                                         : oracle_log_offset((double)dx);
+            const double in1 = (mode & OR_CPB_CODE_NORM) ? oracle_code_offset((double)dy, norm_M)
+                                                         : oracle_log_offset((double)dy);
             for (int j = 0; j < hidden; ++j) {
                 double a = w1[2 * j] * in0 + w1[2 * j + 1] * in1 + (b1 ? b1[j] : 0.0);
                 h[j] = a > 0.0 ? a : 0.0;                 /* ReLU between the two layers */
@@ -94,12 +121,20 @@ int oracle_cpb_table(int M, int heads, int hidden,
             for (int o = 0; o < heads; ++o) {
                 double acc = b2 ? b2[o] : 0.0;
                 for (int j = 0; j < hidden; ++j) acc += w2[(size_t)o * hidden + j] * h[j];
-                row[o] = acc;
+                row[o] = (mode & OR_CPB_SIGMOID16) ? 16.0 / (1.0 + exp(-acc)) : acc;
             }
         }
     }
     free(h);
     return 0;
+}
+
+/* The paper's form (mode 0). */
+int oracle_cpb_table(int M, int heads, int hidden,
+                     const double* w1, const double* b1,
+                     const double* w2, const double* b2, double* table)
+{
+    return oracle_cpb_table_mode(M, M, heads, hidden, w1, b1, w2, b2, 0, table);
 }
 
 /* Shape rule shared by every entry point here: windows tile the grid exactly. */

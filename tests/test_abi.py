@@ -31,7 +31,8 @@ def L():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == sorted(["swin_cpb_table", "swin_window_partition", "swin_window_reverse",
+    assert declared_functions() == sorted(["swin_cpb_table", "swin_cpb_table_ex", "swin_window_partition",
+                                           "swin_window_reverse",
                                            "swin_window_attn_fwd", "swin_window_attn_kernel",
                                            "swin_status_string",
                                            "swin_last_error", "swin_version"])
@@ -145,8 +146,14 @@ def test_partition_rejects(L):
 def test_cpb_rejects(L):
     C = L.swin_cpb_table
     T = ctypes.c_void_p(0x900000)
-    assert C(8, 3, 512, FAKE, None, FAKE, None, 1, T, None) == SWIN_EUNSUPPORTED   # code-form log-CPB
-    assert C(8, 3, 512, FAKE, None, FAKE, None, 7, T, None) == SWIN_EINVAL
+    assert C(8, 3, 512, FAKE, None, FAKE, None, 4, T, None) == SWIN_EINVAL        # unknown mode flag
+    assert C(8, 3, 512, FAKE, None, FAKE, None, -1, T, None) == SWIN_EINVAL
+    assert C(1, 3, 512, FAKE, None, FAKE, None, 1, T, None) == SWIN_EINVAL        # code form needs M >= 2
+    X = L.swin_cpb_table_ex
+    assert X(8, 1, 3, 512, FAKE, None, FAKE, None, 3, T, None) == SWIN_EINVAL     # normalising window < 2
+    assert X(8, 5000, 3, 512, FAKE, None, FAKE, None, 1, T, None) == SWIN_EINVAL
+    assert X(8, 3, 0, 512, FAKE, None, FAKE, None, 1, T, None) == SWIN_EINVAL
+    assert X(8, 12, 3, 512, FAKE, None, FAKE, None, 3, FAKE, None) == SWIN_EINVAL  # table over w1
     assert C(0, 3, 512, FAKE, None, FAKE, None, 0, T, None) == SWIN_EINVAL
     assert C(8, 0, 512, FAKE, None, FAKE, None, 0, T, None) == SWIN_EINVAL
     assert C(8, 3, 0, FAKE, None, FAKE, None, 0, T, None) == SWIN_EINVAL

@@ -68,6 +68,25 @@ def test_cpb_table(M, heads, hidden, biases):
     np.testing.assert_allclose(got.double().cpu().numpy(), want, rtol=1e-5, atol=1e-6)
 
 
+@pytest.mark.parametrize("M,norm_M,mode", [(8, None, 1), (8, None, 2), (16, None, 3), (24, 12, 3),
+                                           (12, 24, 1), (2, None, 3), (5, 9, 3)])
+def test_cpb_table_code_forms(M, norm_M, mode):
+    """The released code's CPB forms (normalised log2 inputs, 16 sigmoid output)
+    and a table for window M normalised by another window."""
+    heads, hidden = 5, 512
+    g = torch.Generator().manual_seed(100 + M)
+    w1 = torch.randn(hidden, 2, generator=g)
+    b1 = torch.randn(hidden, generator=g)
+    w2 = 0.1 * torch.randn(heads, hidden, generator=g)
+    b2 = torch.randn(heads, generator=g)
+    got = binding.swin_cpb_table(M, w1.to(DEV), b1.to(DEV), w2.to(DEV), b2.to(DEV), cpb_mode=mode, norm_M=norm_M)
+    torch.cuda.synchronize()
+    want = oracle.cpb_table(M, f64(w1), f64(b1), f64(w2), f64(b2), mode=mode, norm_M=norm_M)
+    np.testing.assert_allclose(got.double().cpu().numpy(), want, rtol=1e-5, atol=1e-5)
+    if mode & 2:
+        assert float(got.min()) > 0.0 and float(got.max()) < 16.0
+
+
 def test_cpb_table_large_weights():
     """Weights of trained magnitude (N(0,1)): relative fp32 accuracy."""
     g = torch.Generator().manual_seed(3)

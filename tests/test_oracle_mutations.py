@@ -42,6 +42,10 @@ MUTATIONS = [
     ("v_index", "acc += lg[j] * vs[(size_t)j * d + e];", "acc += lg[j] * vs[(size_t)i * d + e];"),
     ("interleaved_map", "*gi = wr + r * (H / M);", "*gi = wr * M + r;"),
     ("softmax_unnormalised", "for (int j = 0; j < N; ++j) lg[j] /= sum;", ";"),
+    ("code_norm_scale", "x / (double)(norm_M - 1) * 8.0", "x / (double)norm_M * 8.0"),
+    ("code_norm_base", "log2(1.0 + fabs(u)) / log2(8.0)", "log2(1.0 + fabs(u)) / 3.2"),
+    ("sigmoid_scale", "16.0 / (1.0 + exp(-acc))", "8.0 / (1.0 + exp(-acc))"),
+    ("sigmoid_sign", "16.0 / (1.0 + exp(-acc))", "16.0 / (1.0 + exp(acc))"),
 ]
 
 

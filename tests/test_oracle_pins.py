@@ -2,6 +2,7 @@
 mathematics fix, never against itself.
 
   * the worked log-CPB example printed on the SwinV2 card (tests/golden);
+  * closed forms of the released code's CPB transform and output bound;
   * library routines: torch fp64 linear/ReLU for the meta network G, torch
     scaled_dot_product_attention for a single unshifted window;
   * the full-grid brute force (oracle/bruteforce.py), which shares neither the
@@ -75,6 +76,46 @@ def pin_cpb_vs_torch(lib):
     x = torch.tensor([oracle.log_offset(2, lib), oracle.log_offset(-3, lib)], dtype=torch.float64)
     want = F.linear(F.relu(F.linear(x, w1)), w2).numpy()
     np.testing.assert_allclose(tab0[(-3 + M - 1) * S + (2 + M - 1)], want, rtol=0, atol=1e-12)
+
+
+def pin_cpb_code_form(lib):
+    """SwinV2 card, Paper vs code: the released code divides each offset by
+    (norm window - 1), multiplies by 8 and maps u to sign(u) log2(1+|u|)/log2(8);
+    its output is 16 sigmoid(G).  Closed forms at norm window 9 (u = offset):
+    f(1) = 1/3, f(3) = 2/3, f(7) = 1, f(8) = log2(9)/3; 16 sigmoid of 0, ln 3,
+    -ln 3, ln 15 is 8, 12, 4, 15."""
+    for x, want in ((1, 1 / 3), (3, 2 / 3), (7, 1.0), (8, math.log2(9) / 3), (-3, -2 / 3), (0, 0.0)):
+        assert oracle.code_offset(x, 9, lib) == pytest.approx(want, abs=1e-15), (x, want)
+    assert oracle.code_offset(2, 5, lib) == pytest.approx(math.log2(5) / 3, abs=1e-15)   # u = 4
+    # the table picks the transformed offsets out through an identity first layer
+    M = 9
+    S = 2 * M - 1
+    w1 = np.array([[1.0, 0.0], [0.0, 1.0], [-1.0, 0.0]])
+    w2 = np.array([[1.0, 0.0, 0.0], [0.0, 1.0, 0.0], [0.0, 0.0, 1.0]])
+    tab = oracle.cpb_table(M, w1, None, w2, None, lib=lib, mode=oracle.CPB_CODE_NORM, norm_M=9)
+    for dy, dx in ((0, 7), (3, -1), (-8, 8), (1, -3)):
+        row = tab[(dy + M - 1) * S + (dx + M - 1)]
+        fx, fy = math.copysign(math.log2(1 + abs(dx)) / 3, dx), math.copysign(math.log2(1 + abs(dy)) / 3, dy)
+        np.testing.assert_allclose(row, [max(fx, 0), max(fy, 0), max(-fx, 0)], rtol=0, atol=1e-14)
+    # bounded output: G = b2 exactly when W2 = 0
+    b2 = np.array([0.0, math.log(3), -math.log(3), math.log(15)])
+    tab = oracle.cpb_table(3, np.ones((4, 2)), None, np.zeros((4, 4)), b2, lib=lib, mode=oracle.CPB_SIGMOID16)
+    np.testing.assert_allclose(tab, np.tile([8.0, 12.0, 4.0, 15.0], (25, 1)), rtol=0, atol=1e-13)
+    # at norm window 9 the code's inputs are the paper's divided by ln 8
+    g = torch.Generator().manual_seed(5)
+    w1 = torch.randn(16, 2, generator=g, dtype=torch.float64).numpy()
+    b1 = torch.randn(16, generator=g, dtype=torch.float64).numpy()
+    w2 = torch.randn(2, 16, generator=g, dtype=torch.float64).numpy()
+    code = oracle.cpb_table(6, w1, b1, w2, None, lib=lib, mode=oracle.CPB_CODE_NORM, norm_M=9)
+    paper = oracle.cpb_table(6, w1 / math.log(8), b1, w2, None, lib=lib)
+    np.testing.assert_allclose(code, paper, rtol=1e-12, atol=1e-13)
+    # window transfer: a window of 4 normalised by 8 is the centre of the window of 8
+    small = oracle.cpb_table(4, w1, b1, w2, None, lib=lib, mode=3, norm_M=8)
+    big = oracle.cpb_table(8, w1, b1, w2, None, lib=lib, mode=3, norm_M=8)
+    centre = big.reshape(15, 15, 2)[4:11, 4:11].reshape(49, 2)
+    np.testing.assert_allclose(small, centre, rtol=0, atol=1e-14)
+    with pytest.raises(ValueError):
+        oracle.cpb_table(4, w1, b1, w2, None, lib=lib, mode=oracle.CPB_CODE_NORM, norm_M=1)
 
 
 BRUTE_CASES = [
@@ -258,6 +299,7 @@ def pin_partition_closed_form(lib):
 PINS = {
     "worked_example": pin_worked_example,
     "cpb_vs_torch": pin_cpb_vs_torch,
+    "cpb_code_form": pin_cpb_code_form,
     "bruteforce": pin_bruteforce,
     "rope_freq_table": pin_rope_freq_table,
     "single_window_sdpa": pin_single_window_sdpa,

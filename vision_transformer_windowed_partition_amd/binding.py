@@ -24,6 +24,7 @@ DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 DTYPE_BY_NAME = {"f32": 0, "bf16": 1}
 LAYOUT = {"grid": 0, "windows": 1}
 CPB_PAPER = 0
+CPB_CODE_NORM, CPB_SIGMOID16 = 1, 2       # flags; 3 = the released code
 
 
 class SwinAttnDesc(ctypes.Structure):
@@ -52,6 +53,8 @@ def lib() -> ctypes.CDLL:
         i32, vp, f = ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
         L.swin_cpb_table.restype = i32
         L.swin_cpb_table.argtypes = [i32, i32, i32, vp, vp, vp, vp, i32, vp, vp]
+        L.swin_cpb_table_ex.restype = i32
+        L.swin_cpb_table_ex.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp]
         for fn in (L.swin_window_partition, L.swin_window_reverse):
             fn.restype = i32
             fn.argtypes = [vp, vp] + [i32] * 8 + [vp]
@@ -104,16 +107,22 @@ def _enum(table, v):
     return table[v] if isinstance(v, str) else int(v)
 
 
-def swin_cpb_table(M: int, w1, b1, w2, b2, *, out=None, cpb_mode: int = CPB_PAPER, stream=None):
-    """(2M-1)^2 x heads fp32 bias table from the meta network parameters."""
+def swin_cpb_table(M: int, w1, b1, w2, b2, *, out=None, cpb_mode: int = CPB_PAPER, norm_M=None, stream=None):
+    """(2M-1)^2 x heads fp32 bias table from the meta network parameters.
+    cpb_mode: CPB_PAPER, or the flags CPB_CODE_NORM | CPB_SIGMOID16; norm_M:
+    the window that normalises the offsets under CPB_CODE_NORM (default M)."""
     heads, hidden = w2.shape
     for t in (w1, b1, w2, b2, out):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise ValueError("CPB parameters and table must be contiguous fp32")
     if out is None:
         out = torch.empty(((2 * M - 1) ** 2, heads), dtype=torch.float32, device=w1.device)
-    _check(lib().swin_cpb_table(M, heads, hidden, _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
-                                cpb_mode, _ptr(out), _stream(w1, stream)))
+    if norm_M is None:
+        _check(lib().swin_cpb_table(M, heads, hidden, _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
+                                    cpb_mode, _ptr(out), _stream(w1, stream)))
+    else:
+        _check(lib().swin_cpb_table_ex(M, norm_M, heads, hidden, _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
+                                       cpb_mode, _ptr(out), _stream(w1, stream)))
     return out
 
 

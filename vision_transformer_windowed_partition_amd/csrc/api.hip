@@ -105,15 +105,15 @@ const char* swin_status_string(int status)
 
 const char* swin_last_error(void) { return g_last_error.c_str(); }
 
-int swin_cpb_table(int32_t M, int32_t heads, int32_t hidden, const float* w1, const float* b1,
-                   const float* w2, const float* b2, int32_t cpb_mode, float* table, void* stream)
+int swin_cpb_table_ex(int32_t M, int32_t norm_M, int32_t heads, int32_t hidden, const float* w1,
+                      const float* b1, const float* w2, const float* b2, int32_t cpb_mode, float* table,
+                      void* stream)
 {
-    if (cpb_mode != SWIN_CPB_PAPER) {
-        if (cpb_mode == 1 || cpb_mode == 2)
-            return fail(SWIN_EUNSUPPORTED, "cpb_mode %d (released-code variant) is not built", cpb_mode);
+    if (cpb_mode < 0 || cpb_mode > (SWIN_CPB_CODE_NORM | SWIN_CPB_SIGMOID16))
         return fail(SWIN_EINVAL, "unknown cpb_mode %d", cpb_mode);
-    }
     if (M < 1 || M > 64) return fail(SWIN_EINVAL, "M=%d outside [1, 64]", M);
+    if ((cpb_mode & SWIN_CPB_CODE_NORM) && (norm_M < 2 || norm_M > 4096))
+        return fail(SWIN_EINVAL, "normalising window %d outside [2, 4096]", norm_M);
     if (heads < 1 || heads > 64) return fail(SWIN_EINVAL, "heads=%d outside [1, 64]", heads);
     if (hidden < 1 || hidden > 4096) return fail(SWIN_EINVAL, "hidden=%d outside [1, 4096]", hidden);
     if (!w1 || !w2 || !table) return fail(SWIN_EINVAL, "NULL w1, w2 or table");
@@ -121,8 +121,15 @@ int swin_cpb_table(int32_t M, int32_t heads, int32_t hidden, const float* w1, co
     if (overlaps(table, tb, w1, (size_t)hidden * 2 * 4) || overlaps(table, tb, w2, (size_t)heads * hidden * 4) ||
         (b1 && overlaps(table, tb, b1, (size_t)hidden * 4)) || (b2 && overlaps(table, tb, b2, (size_t)heads * 4)))
         return fail(SWIN_EINVAL, "table overlaps a parameter tensor");
-    return hip_status(swin::launch_cpb_table(M, heads, hidden, w1, b1, w2, b2, table, (hipStream_t)stream),
+    return hip_status(swin::launch_cpb_table(M, norm_M, heads, hidden, w1, b1, w2, b2, cpb_mode, table,
+                                             (hipStream_t)stream),
                       "swin_cpb_table launch");
+}
+
+int swin_cpb_table(int32_t M, int32_t heads, int32_t hidden, const float* w1, const float* b1,
+                   const float* w2, const float* b2, int32_t cpb_mode, float* table, void* stream)
+{
+    return swin_cpb_table_ex(M, M, heads, hidden, w1, b1, w2, b2, cpb_mode, table, stream);
 }
 
 int swin_window_partition(const void* x, void* xw, int32_t B, int32_t H, int32_t W, int32_t C,

@@ -25,8 +25,8 @@ struct AttnParams {
 hipError_t launch_window_copy(const void* src, void* dst, const Geometry& g, int elem_size,
                               bool to_windows, hipStream_t stream);
 
-hipError_t launch_cpb_table(int M, int heads, int hidden, const float* w1, const float* b1,
-                            const float* w2, const float* b2, float* table, hipStream_t stream);
+hipError_t launch_cpb_table(int M, int norm_M, int heads, int hidden, const float* w1, const float* b1,
+                            const float* w2, const float* b2, int mode, float* table, hipStream_t stream);
 
 // fp32 (and any-shape fallback) attention on the vector ALUs.
 hipError_t launch_attn_valu(const AttnParams& p, hipStream_t stream);

@@ -63,6 +63,10 @@ def _declare(lib):
         fn.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
     lib.oracle_window_attn.restype = i32
     lib.oracle_window_attn.argtypes = [i32] * 10 + [dbl, dbl] + [vp] * 7 + [i64, vp, vp]
+    lib.oracle_window_attn_bwd.restype = i32
+    lib.oracle_window_attn_bwd.argtypes = [i32] * 10 + [dbl, dbl] + [vp] * 12
+    lib.oracle_cpb_table_bwd.restype = i32
+    lib.oracle_cpb_table_bwd.argtypes = [i32] * 4 + [vp] * 4 + [i32] + [vp] * 5
     lib.oracle_window_cosines.restype = i32
     lib.oracle_window_cosines.argtypes = [i32] * 9 + [dbl, vp, vp, vp, i64, i32, vp]
     lib.oracle_set_threads.restype = None
@@ -190,6 +194,49 @@ def window_attn(q, k, v, *, heads: int, M: int, shift: int = 0, partition: str =
     if rc:
         raise ValueError(f"oracle_window_attn: bad argument (rc={rc})")
     return (out, wts) if return_weights else out
+
+
+def window_attn_bwd(q, k, v, dout, *, heads: int, M: int, shift: int = 0, partition: str = "cyclic",
+                    sim: str = "cosine", pos: str = "none", tau=None, table=None,
+                    rope_freqs=None, rope_base: float = 10000.0, tau_min: float = 0.01, lib=None):
+    """Gradients of sum(dout * window_attn(...)) in fp64: a dict with dq, dk,
+    dv (B, H, W, C), dtau (heads,) for COSINE and dtable ((2M-1)^2, heads) for
+    TABLE."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, W, C = q.shape
+    assert k.shape == q.shape and v.shape == q.shape and dout.shape == q.shape
+    tau, table, rope_freqs = _f64(tau), _f64(table), _f64(rope_freqs)
+    g = {n: np.zeros((B, H, W, C), dtype=np.float64) for n in ("dq", "dk", "dv")}
+    dtau = np.zeros(heads, dtype=np.float64) if sim == "cosine" else None
+    dtable = np.zeros(((2 * M - 1) ** 2, heads), dtype=np.float64) if pos == "table" else None
+    rc = (lib or load()).oracle_window_attn_bwd(
+        B, H, W, C, heads, M, shift, PART[partition], SIM[sim], POS[pos],
+        float(tau_min), float(rope_base), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(tau),
+        _ptr(table), _ptr(rope_freqs), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+        _ptr(dtau), _ptr(dtable))
+    if rc:
+        raise ValueError(f"oracle_window_attn_bwd: bad argument (rc={rc})")
+    if dtau is not None:
+        g["dtau"] = dtau
+    if dtable is not None:
+        g["dtable"] = dtable
+    return g
+
+
+def cpb_table_bwd(M: int, w1, b1, w2, b2, dtable, lib=None, mode: int = 0, norm_M: int | None = None):
+    """Gradients (dw1, db1, dw2, db2) of sum(dtable * cpb_table(...)) in fp64."""
+    w1, w2, dtable = _f64(w1), _f64(w2), _f64(dtable)
+    b1, b2 = _f64(b1), _f64(b2)
+    hidden, heads = w1.shape[0], w2.shape[0]
+    assert dtable.shape == ((2 * M - 1) ** 2, heads)
+    dw1, db1 = np.empty((hidden, 2)), np.empty(hidden)
+    dw2, db2 = np.empty((heads, hidden)), np.empty(heads)
+    rc = (lib or load()).oracle_cpb_table_bwd(M, M if norm_M is None else norm_M, heads, hidden, _ptr(w1),
+                                              _ptr(b1), _ptr(w2), _ptr(b2), int(mode), _ptr(dtable),
+                                              _ptr(dw1), _ptr(db1), _ptr(dw2), _ptr(db2))
+    if rc:
+        raise ValueError(f"oracle_cpb_table_bwd: bad argument (rc={rc})")
+    return dw1, db1, dw2, db2
 
 
 def window_cosines(q, k, *, heads: int, M: int, shift: int, partition: str, window: int,

@@ -439,3 +439,268 @@ int oracle_window_cosines(int B, int H, int W, int C, int heads, int M, int shif
     free(qs); free(ks);
     return 0;
 }
+
+/*
+ * Backward of oracle_window_attn: given dout = dLoss/dout, the gradients of
+ * the same loss with respect to q, k, v (same layout), tau (heads) and the
+ * bias table ((2M-1)^2 x heads).  The chain rule applied to the forward steps
+ * above, in reverse, per (batch, window, head):
+ *   p = softmax over allowed keys (recomputed), o_i = sum_j p_ij v_j
+ *   dv_j   = sum_i p_ij dout_i
+ *   dp_ij  = dout_i . v_j,  D_i = sum_j p_ij dp_ij
+ *   dl_ij  = p_ij (dp_ij - D_i)             (0 for excluded keys: p_ij = 0)
+ *   TABLE:  dtable[offset(i, j)][h] += dl_ij
+ *   COSINE: ds_ij = dl_ij / tau';  dtau_h += sum dl_ij * cos_ij * (-1/tau_h^2)
+ *           when tau_h > tau_min (the floor max(tau, tau_min) passes no
+ *           gradient below it); dq^_i = sum_j ds_ij k^_j, dk^_j = sum_i ds_ij q^_i;
+ *           through x^ = x / max(||x||, eps): dx = (dx^ - x^ (x^ . dx^)) / ||x||
+ *           when ||x|| > eps, else dx^ / eps;
+ *   DOT:    dq_i = sum_j dl_ij k_j / sqrt(d), dk_j = sum_i dl_ij q_i / sqrt(d);
+ *   ROPE2D: the rotation is orthogonal, so dq = R^T dq~ (rotate by -pos).
+ * Each token belongs to one window, so dq, dk, dv are written, not summed;
+ * dtau and dtable are sums over all windows.  Any of dtau (DOT) and dtable
+ * (not TABLE) may be NULL.  Returns 0, or 1 on a bad argument.
+ */
+int oracle_window_attn_bwd(int B, int H, int W, int C, int heads, int M, int shift,
+                           int part, int sim, int pos, double tau_min, double rope_base,
+                           const double* q, const double* k, const double* v, const double* dout,
+                           const double* tau, const double* table, const double* rope_freqs,
+                           double* dq, double* dk, double* dv, double* dtau, double* dtable)
+{
+    if (bad_shape(B, H, W, C, M, shift, part)) return 1;
+    if (heads < 1 || C % heads) return 1;
+    const int d = C / heads;
+    if (sim != OR_SIM_COSINE && sim != OR_SIM_DOT) return 1;
+    if (pos != OR_POS_NONE && pos != OR_POS_TABLE && pos != OR_POS_ROPE2D) return 1;
+    if (sim == OR_SIM_COSINE && !tau) return 1;
+    if (pos == OR_POS_TABLE && !table) return 1;
+    if (pos == OR_POS_ROPE2D && d % 4) return 1;
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return 1;
+
+    const int nwr = H / M, nwc = W / M, N = M * M, S = 2 * M - 1;
+    const int64_t nW = (int64_t)nwr * nwc, total = (int64_t)B * nW;
+    const double dot_scale = 1.0 / sqrt((double)d);
+    if (dtau) for (int h = 0; h < heads; ++h) dtau[h] = 0.0;
+    if (dtable) memset(dtable, 0, (size_t)S * S * heads * sizeof(double));
+    int failed = 0;
+
+    #pragma omp parallel
+    {
+        const size_t nd = (size_t)N * d;
+        double* qx = (double*)malloc(nd * sizeof(double));    /* rotated, before normalising */
+        double* kx = (double*)malloc(nd * sizeof(double));
+        double* qs = (double*)malloc(nd * sizeof(double));    /* operands of the logits */
+        double* ks = (double*)malloc(nd * sizeof(double));
+        double* vs = (double*)malloc(nd * sizeof(double));
+        double* gs = (double*)malloc(nd * sizeof(double));    /* dout */
+        double* gq = (double*)malloc(nd * sizeof(double));
+        double* gk = (double*)malloc(nd * sizeof(double));
+        double* gv = (double*)malloc(nd * sizeof(double));
+        double* p = (double*)malloc((size_t)N * N * sizeof(double));
+        double* dl = (double*)malloc((size_t)N * N * sizeof(double));
+        int* gi = (int*)malloc((size_t)N * sizeof(int));
+        int* gj = (int*)malloc((size_t)N * sizeof(int));
+        int* region = (int*)malloc((size_t)N * sizeof(int));
+        double* my_dtau = (double*)calloc((size_t)heads, sizeof(double));
+        double* my_dtable = dtable ? (double*)calloc((size_t)S * S * heads, sizeof(double)) : NULL;
+        if (!qx || !kx || !qs || !ks || !vs || !gs || !gq || !gk || !gv || !p || !dl || !gi || !gj ||
+            !region || !my_dtau || (dtable && !my_dtable)) {
+            #pragma omp atomic write
+            failed = 1;
+        } else {
+            #pragma omp for schedule(dynamic, 1)
+            for (int64_t u = 0; u < total * heads; ++u) {
+                const int64_t gw = u / heads;
+                const int h = (int)(u % heads);
+                const int b = (int)(gw / nW);
+                const int wr = (int)((gw % nW) / nwc);
+                const int wc = (int)(gw % nwc);
+                const double* f = (pos == OR_POS_ROPE2D && rope_freqs) ? rope_freqs + (size_t)h * 2 * (d / 4) : NULL;
+
+                /* forward recomputation: gather, rotate, normalise */
+                for (int t = 0; t < N; ++t) {
+                    const int r = t / M, c = t % M;
+                    grid_pos(H, W, M, shift, part, wr, wc, r, c, &gi[t], &gj[t]);
+                    region[t] = (part == OR_PART_CYCLIC)
+                        ? 3 * axis_region(wr * M + r, H, M, shift) + axis_region(wc * M + c, W, M, shift)
+                        : 0;
+                    const size_t base = (((size_t)b * H + gi[t]) * W + gj[t]) * C + (size_t)h * d;
+                    for (int e = 0; e < d; ++e) {
+                        qx[(size_t)t * d + e] = q[base + e];
+                        kx[(size_t)t * d + e] = k[base + e];
+                        vs[(size_t)t * d + e] = v[base + e];
+                        gs[(size_t)t * d + e] = dout[base + e];
+                    }
+                    if (pos == OR_POS_ROPE2D) {
+                        rope_rotate(qx + (size_t)t * d, d, r, c, f, rope_base);
+                        rope_rotate(kx + (size_t)t * d, d, r, c, f, rope_base);
+                    }
+                    for (int e = 0; e < d; ++e) {
+                        qs[(size_t)t * d + e] = qx[(size_t)t * d + e];
+                        ks[(size_t)t * d + e] = kx[(size_t)t * d + e];
+                    }
+                    if (sim == OR_SIM_COSINE) {
+                        unit_normalize(qs + (size_t)t * d, d);
+                        unit_normalize(ks + (size_t)t * d, d);
+                    }
+                }
+                double t_h = 1.0, inv_tau = 0.0;
+                if (sim == OR_SIM_COSINE) {
+                    t_h = tau[h] > tau_min ? tau[h] : tau_min;
+                    inv_tau = 1.0 / t_h;
+                }
+                const double scale = (sim == OR_SIM_COSINE) ? inv_tau : dot_scale;
+
+                /* softmax weights, as in the forward */
+                for (int i = 0; i < N; ++i) {
+                    const int ri = i / M, ci = i % M;
+                    double mx = -INFINITY;
+                    double* pr = p + (size_t)i * N;
+                    for (int j = 0; j < N; ++j) {
+                        const int rj = j / M, cj = j % M;
+                        double s = 0.0;
+                        for (int e = 0; e < d; ++e) s += qs[(size_t)i * d + e] * ks[(size_t)j * d + e];
+                        double l = s * scale;
+                        if (pos == OR_POS_TABLE)
+                            l += table[((size_t)(ri - rj + M - 1) * S + (size_t)(ci - cj + M - 1)) * heads + h];
+                        pr[j] = (region[j] == region[i]) ? l : -INFINITY;
+                        if (pr[j] > mx) mx = pr[j];
+                    }
+                    double sum = 0.0;
+                    for (int j = 0; j < N; ++j) {
+                        pr[j] = exp(pr[j] - mx);              /* excluded keys: exp(-inf) = 0 */
+                        sum += pr[j];
+                    }
+                    for (int j = 0; j < N; ++j) pr[j] /= sum;
+                }
+
+                /* dv, dp, D, dl */
+                for (size_t x = 0; x < nd; ++x) { gv[x] = 0.0; gq[x] = 0.0; gk[x] = 0.0; }
+                for (int i = 0; i < N; ++i) {
+                    const double* pr = p + (size_t)i * N;
+                    double* dr = dl + (size_t)i * N;
+                    double Di = 0.0;
+                    for (int j = 0; j < N; ++j) {
+                        double dp = 0.0;
+                        for (int e = 0; e < d; ++e) dp += gs[(size_t)i * d + e] * vs[(size_t)j * d + e];
+                        dr[j] = dp;
+                        Di += pr[j] * dp;
+                        for (int e = 0; e < d; ++e) gv[(size_t)j * d + e] += pr[j] * gs[(size_t)i * d + e];
+                    }
+                    for (int j = 0; j < N; ++j) dr[j] = pr[j] * (dr[j] - Di);
+                }
+
+                /* bias table, tau, and the logit operands */
+                for (int i = 0; i < N; ++i) {
+                    const int ri = i / M, ci = i % M;
+                    for (int j = 0; j < N; ++j) {
+                        const int rj = j / M, cj = j % M;
+                        const double g = dl[(size_t)i * N + j];
+                        if (pos == OR_POS_TABLE && my_dtable)
+                            my_dtable[((size_t)(ri - rj + M - 1) * S + (size_t)(ci - cj + M - 1)) * heads + h] += g;
+                        if (sim == OR_SIM_COSINE && tau[h] > tau_min) {
+                            double cs = 0.0;
+                            for (int e = 0; e < d; ++e) cs += qs[(size_t)i * d + e] * ks[(size_t)j * d + e];
+                            my_dtau[h] += g * cs * (-1.0 / (tau[h] * tau[h]));
+                        }
+                        for (int e = 0; e < d; ++e) {
+                            gq[(size_t)i * d + e] += g * scale * ks[(size_t)j * d + e];
+                            gk[(size_t)j * d + e] += g * scale * qs[(size_t)i * d + e];
+                        }
+                    }
+                }
+
+                /* through the normalisation and the rotation, then scatter */
+                for (int t = 0; t < N; ++t) {
+                    const int r = t / M, c = t % M;
+                    for (int which = 0; which < 2; ++which) {
+                        double* g = (which == 0 ? gq : gk) + (size_t)t * d;
+                        const double* x = (which == 0 ? qx : kx) + (size_t)t * d;
+                        const double* xh = (which == 0 ? qs : ks) + (size_t)t * d;
+                        if (sim == OR_SIM_COSINE) {
+                            double ss = 0.0, proj = 0.0;
+                            for (int e = 0; e < d; ++e) { ss += x[e] * x[e]; proj += xh[e] * g[e]; }
+                            const double n = sqrt(ss);
+                            if (n > 1e-12) { for (int e = 0; e < d; ++e) g[e] = (g[e] - xh[e] * proj) / n; }
+                            else { for (int e = 0; e < d; ++e) g[e] = g[e] / 1e-12; }
+                        }
+                        if (pos == OR_POS_ROPE2D) rope_rotate(g, d, -r, -c, f, rope_base);
+                    }
+                    const size_t base = (((size_t)b * H + gi[t]) * W + gj[t]) * C + (size_t)h * d;
+                    for (int e = 0; e < d; ++e) {
+                        dq[base + e] = gq[(size_t)t * d + e];
+                        dk[base + e] = gk[(size_t)t * d + e];
+                        dv[base + e] = gv[(size_t)t * d + e];
+                    }
+                }
+            }
+            #pragma omp critical
+            {
+                if (dtau) for (int h = 0; h < heads; ++h) dtau[h] += my_dtau[h];
+                if (dtable) for (size_t x = 0; x < (size_t)S * S * heads; ++x) dtable[x] += my_dtable[x];
+            }
+        }
+        free(qx); free(kx); free(qs); free(ks); free(vs); free(gs); free(gq); free(gk); free(gv);
+        free(p); free(dl); free(gi); free(gj); free(region); free(my_dtau); free(my_dtable);
+    }
+    return failed ? 2 : 0;
+}
+
+/*
+ * Backward of oracle_cpb_table_mode: given dtable ((2M-1)^2 x heads), the
+ * gradients of G's parameters (dw1 hidden x 2, db1 hidden, dw2 heads x hidden,
+ * db2 heads), written.  Per table row, recompute a = W1 x + b1, hid = relu(a),
+ * g = W2 hid + b2; SIGMOID16: dg = dtable * 16 s (1 - s), s = sigmoid(g);
+ * dW2 += dg hid^T, db2 += dg, dhid = W2^T dg, da = dhid [a > 0],
+ * dW1 += da x^T, db1 += da.  db1/db2 may be NULL.  Returns 0 or 1.
+ */
+int oracle_cpb_table_bwd(int M, int norm_M, int heads, int hidden,
+                         const double* w1, const double* b1, const double* w2, const double* b2,
+                         int mode, const double* dtable,
+                         double* dw1, double* db1, double* dw2, double* db2)
+{
+    if (M < 1 || heads < 1 || hidden < 1 || !w1 || !w2 || !dtable || !dw1 || !dw2) return 1;
+    if (mode < 0 || mode > 3) return 1;
+    if ((mode & OR_CPB_CODE_NORM) && norm_M < 2) return 1;
+    const int S = 2 * M - 1;
+    double* a = (double*)malloc((size_t)hidden * sizeof(double));
+    double* dg = (double*)malloc((size_t)heads * sizeof(double));
+    if (!a || !dg) { free(a); free(dg); return 2; }
+    memset(dw1, 0, (size_t)hidden * 2 * sizeof(double));
+    memset(dw2, 0, (size_t)heads * hidden * sizeof(double));
+    if (db1) memset(db1, 0, (size_t)hidden * sizeof(double));
+    if (db2) memset(db2, 0, (size_t)heads * sizeof(double));
+    for (int dy = -(M - 1); dy <= M - 1; ++dy)
+        for (int dx = -(M - 1); dx <= M - 1; ++dx) {
+            const double in0 = (mode & OR_CPB_CODE_NORM) ? oracle_code_offset((double)dx, norm_M)
+                                                         : oracle_log_offset((double)dx);
+            const double in1 = (mode & OR_CPB_CODE_NORM) ? oracle_code_offset((double)dy, norm_M)
+                                                         : oracle_log_offset((double)dy);
+            const double* grow = dtable + ((size_t)(dy + M - 1) * S + (size_t)(dx + M - 1)) * heads;
+            for (int j = 0; j < hidden; ++j) a[j] = w1[2 * j] * in0 + w1[2 * j + 1] * in1 + (b1 ? b1[j] : 0.0);
+            for (int o = 0; o < heads; ++o) {
+                dg[o] = grow[o];
+                if (mode & OR_CPB_SIGMOID16) {
+                    double g = b2 ? b2[o] : 0.0;
+                    for (int j = 0; j < hidden; ++j) g += w2[(size_t)o * hidden + j] * (a[j] > 0.0 ? a[j] : 0.0);
+                    const double s = 1.0 / (1.0 + exp(-g));
+                    dg[o] *= 16.0 * s * (1.0 - s);
+                }
+                if (db2) db2[o] += dg[o];
+            }
+            for (int j = 0; j < hidden; ++j) {
+                const double hj = a[j] > 0.0 ? a[j] : 0.0;
+                double dh = 0.0;
+                for (int o = 0; o < heads; ++o) {
+                    dw2[(size_t)o * hidden + j] += dg[o] * hj;
+                    dh += w2[(size_t)o * hidden + j] * dg[o];
+                }
+                const double da = a[j] > 0.0 ? dh : 0.0;
+                dw1[2 * j] += da * in0;
+                dw1[2 * j + 1] += da * in1;
+                if (db1) db1[j] += da;
+            }
+        }
+    free(a); free(dg);
+    return 0;
+}

@@ -46,6 +46,21 @@ MUTATIONS = [
     ("code_norm_base", "log2(1.0 + fabs(u)) / log2(8.0)", "log2(1.0 + fabs(u)) / 3.2"),
     ("sigmoid_scale", "16.0 / (1.0 + exp(-acc))", "8.0 / (1.0 + exp(-acc))"),
     ("sigmoid_sign", "16.0 / (1.0 + exp(-acc))", "16.0 / (1.0 + exp(acc))"),
+    ("bwd_D_dropped", "dr[j] = pr[j] * (dr[j] - Di);", "dr[j] = pr[j] * dr[j];"),
+    ("bwd_dv_index", "gv[(size_t)j * d + e] += pr[j] * gs[(size_t)i * d + e];",
+     "gv[(size_t)j * d + e] += pr[j] * gs[(size_t)j * d + e];"),
+    ("bwd_norm_projection", "g[e] = (g[e] - xh[e] * proj) / n;", "g[e] = g[e] / n;"),
+    ("bwd_rope_not_transposed", "rope_rotate(g, d, -r, -c, f, rope_base);", "rope_rotate(g, d, r, c, f, rope_base);"),
+    ("bwd_dtau_sign", "(-1.0 / (tau[h] * tau[h]))", "(1.0 / (tau[h] * tau[h]))"),
+    ("bwd_dk_operand", "gk[(size_t)j * d + e] += g * scale * qs[(size_t)i * d + e];",
+     "gk[(size_t)j * d + e] += g * scale * ks[(size_t)i * d + e];"),
+    ("bwd_table_offset", "my_dtable[((size_t)(ri - rj + M - 1) * S + (size_t)(ci - cj + M - 1)) * heads + h] += g;",
+     "my_dtable[((size_t)(rj - ri + M - 1) * S + (size_t)(cj - ci + M - 1)) * heads + h] += g;"),
+    ("bwd_mask_dropped", "pr[j] = (region[j] == region[i]) ? l : -INFINITY;",
+     "pr[j] = (region[j] == region[i]) ? l : l;"),
+    ("cpb_bwd_relu_mask", "const double da = a[j] > 0.0 ? dh : 0.0;", "const double da = dh;"),
+    ("cpb_bwd_sigmoid", "dg[o] *= 16.0 * s * (1.0 - s);", "dg[o] *= 16.0 * s;"),
+    ("cpb_bwd_inputs_swapped", "dw1[2 * j] += da * in0;", "dw1[2 * j] += da * in1;"),
 ]
 
 

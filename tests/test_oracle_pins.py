@@ -3,6 +3,8 @@ mathematics fix, never against itself.
 
   * the worked log-CPB example printed on the SwinV2 card (tests/golden);
   * closed forms of the released code's CPB transform and output bound;
+  * for the backward: central differences of the (pinned) forward, and torch's
+    fp64 scaled_dot_product_attention backward for one unshifted window;
   * library routines: torch fp64 linear/ReLU for the meta network G, torch
     scaled_dot_product_attention for a single unshifted window;
   * the full-grid brute force (oracle/bruteforce.py), which shares neither the
@@ -296,6 +298,86 @@ def pin_partition_closed_form(lib):
                 assert np.array_equal(oracle.reverse(got, B, H, W, M, 0, "interleaved", lib=lib), x)
 
 
+BWD_CASES = [
+    # H, W, C, heads, M, shift, partition, sim, pos
+    (8, 8, 8, 2, 4, 2, "cyclic", "cosine", "table"),
+    (8, 8, 8, 2, 4, 1, "cyclic", "dot", "rope2d"),
+    (8, 12, 8, 2, 4, 0, "interleaved", "cosine", "rope2d"),
+    (8, 8, 4, 1, 4, 3, "cyclic", "dot", "table"),
+]
+
+
+def _fd_check(f, x, grad, idx, h=1e-6, rtol=1e-5, atol=1e-7):
+    """Central differences of the scalar f at the flat indices idx of x."""
+    flat = x.reshape(-1)
+    for i in idx:
+        old = flat[i]
+        flat[i] = old + h
+        up = f()
+        flat[i] = old - h
+        dn = f()
+        flat[i] = old
+        fd = (up - dn) / (2 * h)
+        assert abs(fd - grad.reshape(-1)[i]) <= atol + rtol * abs(fd), (i, fd, grad.reshape(-1)[i])
+
+
+def pin_bwd_finite_differences(lib):
+    """The backward equals central differences of the forward oracle's loss
+    sum(dout * out) in every input: q, k, v, tau and the bias table."""
+    rng = np.random.default_rng(21)
+    for (H, W, C, heads, M, s, part, sim, pos) in BWD_CASES:
+        q, k, v, do = (rng.standard_normal((1, H, W, C)) for _ in range(4))
+        tau = rng.uniform(0.2, 1.0, heads)
+        S = 2 * M - 1
+        table = 0.5 * rng.standard_normal((S * S, heads)) if pos == "table" else None
+        kw = dict(heads=heads, M=M, shift=s, partition=part, sim=sim, pos=pos, lib=lib)
+
+        def loss():
+            return float(np.sum(do * oracle.window_attn(q, k, v, tau=tau, table=table, **kw)))
+
+        g = oracle.window_attn_bwd(q, k, v, do, tau=tau, table=table, **kw)
+        for name, x in (("dq", q), ("dk", k), ("dv", v)):
+            _fd_check(loss, x, g[name], rng.choice(x.size, 24, replace=False))
+        if sim == "cosine":
+            _fd_check(loss, tau, g["dtau"], range(heads))
+        if pos == "table":
+            _fd_check(loss, table, g["dtable"], rng.choice(table.size, 16, replace=False))
+
+
+def pin_bwd_single_window_sdpa(lib):
+    """One unshifted window, DOT, no bias: torch's fp64 scaled_dot_product_attention
+    backward (library routine) gives the same dq, dk, dv."""
+    g = torch.Generator().manual_seed(7)
+    M, heads, d = 4, 2, 8
+    x = [torch.randn(1, M, M, heads * d, generator=g, dtype=torch.float64) for _ in range(4)]
+    q, k, v, do = x
+    got = oracle.window_attn_bwd(q.numpy(), k.numpy(), v.numpy(), do.numpy(), heads=heads, M=M, shift=0,
+                                 partition="cyclic", sim="dot", pos="none", lib=lib)
+    th = lambda t: t.reshape(1, M * M, heads, d).permute(0, 2, 1, 3).clone().requires_grad_(True)
+    tq, tk, tv = th(q), th(k), th(v)
+    out = F.scaled_dot_product_attention(tq, tk, tv)
+    out.backward(do.reshape(1, M * M, heads, d).permute(0, 2, 1, 3))
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+        want = t.grad.permute(0, 2, 1, 3).reshape(1, M, M, heads * d).numpy()
+        np.testing.assert_allclose(got[name], want, rtol=0, atol=1e-12)
+
+
+def pin_cpb_bwd_finite_differences(lib):
+    """The meta network's parameter gradients equal central differences of
+    sum(dtable * cpb_table(...)), in all four CPB forms."""
+    rng = np.random.default_rng(4)
+    M, heads, hidden = 4, 3, 12
+    w1, b1 = rng.standard_normal((hidden, 2)), rng.standard_normal(hidden)
+    w2, b2 = rng.standard_normal((heads, hidden)), rng.standard_normal(heads)
+    dt = rng.standard_normal(((2 * M - 1) ** 2, heads))
+    for mode, norm_M in ((0, None), (1, None), (2, None), (3, 7)):
+        def loss():
+            return float(np.sum(dt * oracle.cpb_table(M, w1, b1, w2, b2, lib=lib, mode=mode, norm_M=norm_M)))
+        grads = oracle.cpb_table_bwd(M, w1, b1, w2, b2, dt, lib=lib, mode=mode, norm_M=norm_M)
+        for x, gx in zip((w1, b1, w2, b2), grads):
+            _fd_check(loss, x, gx, range(x.size), atol=1e-6)
+
+
 PINS = {
     "worked_example": pin_worked_example,
     "cpb_vs_torch": pin_cpb_vs_torch,
@@ -308,6 +390,9 @@ PINS = {
     "tau_floor": pin_tau_floor,
     "b2_invariance": pin_b2_invariance,
     "partition_closed_form": pin_partition_closed_form,
+    "bwd_finite_differences": pin_bwd_finite_differences,
+    "bwd_single_window_sdpa": pin_bwd_single_window_sdpa,
+    "cpb_bwd_finite_differences": pin_cpb_bwd_finite_differences,
 }
 
 

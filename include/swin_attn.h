@@ -155,6 +155,47 @@ int swin_window_attn_fwd(const swin_attn_desc* desc, const void* q, const void* 
                          const void* v, void* out, const float* tau, const float* table,
                          const float* rope_freqs, void* stream);
 
+/* Backward of swin_window_attn_fwd: the gradients of a loss L given
+ * dout = dL/dout, by the chain rule through the same steps ([SwinV2] eq. 1-2,
+ * eq. 3-4 for the table, [Flash] for the rotary variant):
+ *   p = the forward's softmax weights, D_i = dout_i . out_i,
+ *   dv_j = sum_i p_ij dout_i,  dl_ij = p_ij (dout_i . v_j - D_i),
+ *   dtable[offset(i, j)][h] += dl_ij (summed over all windows),
+ *   COSINE: dtau_h = sum dl_ij cos_ij (-1/tau_h^2) while tau_h > tau_min
+ *           (the floor passes no gradient), and dq, dk through the unit
+ *           normalisation; DOT: dq, dk from dl / sqrt(d);
+ *   ROPE2D: dq, dk rotated back by the window-local positions.
+ * q, k, v, tau, table, rope_freqs: as given to the forward; out: the
+ * forward's output for them; dout: dL/dout.  All (B,H,W,C)-shaped tensors
+ * share desc->dtype and desc->layout and are 16-byte aligned.
+ * dq, dk, dv (outputs, same shape and dtype): written; they must not overlap
+ * an input or each other.  dtau: heads fp32 (COSINE; NULL skips it), dtable:
+ * (2M-1)^2 x heads fp32 (POS_TABLE; NULL skips it): both written (sums over
+ * the windows, accumulated with fp32 atomics, so the last bits depend on
+ * order).  Requires d = 32 and M <= 32 (SWIN_EUNSUPPORTED otherwise).
+ * Arithmetic: fp32 on the vector ALUs; bf16 gradients are rounded to
+ * nearest even once at the end. */
+int swin_window_attn_bwd(const swin_attn_desc* desc, const void* q, const void* k,
+                         const void* v, const void* out, const void* dout, const float* tau,
+                         const float* table, const float* rope_freqs, void* dq, void* dk,
+                         void* dv, float* dtau, float* dtable, void* stream);
+
+/* Backward of swin_cpb_table_ex ([SwinV2] eq. 3-4, card "Paper vs code"):
+ * from dtable ((2M-1)^2 x heads fp32) the gradients of the meta network's
+ * parameters, dw1 (hidden x 2), db1 (hidden, or NULL to skip), dw2
+ * (heads x hidden), db2 (heads, or NULL), written, fp32, device memory:
+ *   a = W1 x + b1, hid = relu(a), dg = dtable (SIGMOID16: times
+ *   T (1 - T/16), the derivative of T = 16 sigmoid(G)),
+ *   dW2 = sum dg hid^T, db2 = sum dg, dW1 = sum (W2^T dg)[a > 0] x^T,
+ *   db1 = sum (W2^T dg)[a > 0], over the table rows x.
+ * table: the forward's table (required with SIGMOID16, else may be NULL).
+ * Sizes and modes as swin_cpb_table_ex; outputs must not overlap an input or
+ * each other.  Sums use fp32 atomics (order-dependent last bits). */
+int swin_cpb_table_bwd(int32_t M, int32_t norm_M, int32_t heads, int32_t hidden,
+                       const float* w1, const float* b1, const float* w2, const float* table,
+                       const float* dtable, int32_t cpb_mode, float* dw1, float* db1,
+                       float* dw2, float* db2, void* stream);
+
 /* Name of the kernel that swin_window_attn_fwd launches for desc (static
  * storage), for matching profiler output:
  *   "attn_valu_kernel"  SWIN_DT_F32;

@@ -31,7 +31,8 @@ def L():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == sorted(["swin_cpb_table", "swin_cpb_table_ex", "swin_window_partition",
+    assert declared_functions() == sorted(["swin_cpb_table", "swin_cpb_table_ex", "swin_cpb_table_bwd",
+                                           "swin_window_attn_bwd", "swin_window_partition",
                                            "swin_window_reverse",
                                            "swin_window_attn_fwd", "swin_window_attn_kernel",
                                            "swin_status_string",
@@ -101,6 +102,44 @@ def test_attn_rejects_bad_pointers(L):
     assert _attn(L, d, q=ctypes.c_void_p(0x10008)) == SWIN_EINVAL   # misaligned
     assert _attn(L, d, out=ctypes.c_void_p(0x10000 + 64)) == SWIN_EINVAL   # out overlaps q
     assert _attn(L, _desc(pos=2, rope_base=0.0)) == SWIN_EINVAL
+
+
+def _bwd(L, desc, q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, dq=ctypes.c_void_p(0x20000000),
+         dk=ctypes.c_void_p(0x30000000), dv=ctypes.c_void_p(0x40000000), tau=FAKE, table=FAKE,
+         dtau=None, dtable=None):
+    return L.swin_window_attn_bwd(ctypes.byref(desc) if desc is not None else None, q, k, v, out, dout, tau,
+                                  table, None, dq, dk, dv, dtau, dtable, None)
+
+
+def test_backward_rejects(L):
+    d = _desc()
+    assert _bwd(L, None) == SWIN_EINVAL
+    assert _bwd(L, _desc(H=12)) == SWIN_EUNSUPPORTED
+    assert _bwd(L, _desc(H=48, W=48, M=48, shift=0)) == SWIN_EUNSUPPORTED       # M > 32
+    assert _bwd(L, d, dout=None) == SWIN_EINVAL
+    assert _bwd(L, d, out=None) == SWIN_EINVAL
+    assert _bwd(L, d, dk=None) == SWIN_EINVAL
+    assert _bwd(L, d, tau=None) == SWIN_EINVAL                                  # COSINE needs tau
+    assert _bwd(L, d, table=None) == SWIN_EINVAL                                # TABLE needs the table
+    assert _bwd(L, d, dq=ctypes.c_void_p(0x20000008)) == SWIN_EINVAL            # misaligned
+    assert _bwd(L, d, dq=ctypes.c_void_p(0x10000 + 64)) == SWIN_EINVAL          # dq overlaps q
+    assert _bwd(L, d, dv=ctypes.c_void_p(0x20000000 + 64)) == SWIN_EINVAL       # dv overlaps dq
+    assert _bwd(L, d, dtable=FAKE) == SWIN_EINVAL                               # dtable overlaps table
+    # an empty batch with no summed gradients enqueues nothing
+    assert _bwd(L, _desc(B=0), q=None, k=None, v=None, out=None, dout=None, dq=None, dk=None,
+                dv=None) == SWIN_OK
+
+
+def test_cpb_backward_rejects(L):
+    X = L.swin_cpb_table_bwd
+    A, B_, C_, D_ = (ctypes.c_void_p(0x20000000 + i * 0x1000000) for i in range(4))
+    assert X(8, 8, 3, 512, FAKE, None, FAKE, FAKE, FAKE, 4, A, B_, C_, D_, None) == SWIN_EINVAL     # mode
+    assert X(8, 8, 3, 512, FAKE, None, FAKE, None, FAKE, 2, A, B_, C_, D_, None) == SWIN_EINVAL     # no table
+    assert X(8, 1, 3, 512, FAKE, None, FAKE, FAKE, FAKE, 1, A, B_, C_, D_, None) == SWIN_EINVAL     # norm_M
+    assert X(8, 8, 3, 512, FAKE, None, FAKE, FAKE, None, 0, A, B_, C_, D_, None) == SWIN_EINVAL     # dtable
+    assert X(8, 8, 3, 512, FAKE, None, FAKE, FAKE, FAKE, 0, None, B_, C_, D_, None) == SWIN_EINVAL  # dw1
+    assert X(8, 8, 3, 512, FAKE, None, FAKE, FAKE, FAKE, 0, FAKE, B_, C_, D_, None) == SWIN_EINVAL  # dw1 = w1
+    assert X(8, 8, 3, 512, FAKE, None, FAKE, FAKE, FAKE, 0, A, A, C_, D_, None) == SWIN_EINVAL      # db1 = dw1
 
 
 def test_kernel_query_names_the_dispatch(L):

@@ -1,0 +1,126 @@
+"""GPU parity of the backward (swin_window_attn_bwd, swin_cpb_table_bwd)
+against the fp64 oracle backward, through the C ABI, on the same seeded
+inputs.
+
+Bars, derived from the arithmetic: fp32 mode computes in fp32 from exact
+inputs, so each gradient is within 1e-4 of the oracle relative to its
+largest entry and in relative Frobenius norm.  bf16 mode starts from the
+bf16 inputs (exact in the oracle) and from the forward's bf16 output (D_i =
+dout_i . out_i, out rounded to 2^-9), and rounds dq, dk, dv to bf16 once:
+relative Frobenius <= 1e-2 and max-abs <= 2e-2 of the largest entry.  dtau
+and dtable (fp32 sums over windows) take the same bars."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_helpers import f64, gpu_inputs, run_gpu
+from vision_transformer_windowed_partition_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+CASES = [
+    # H, W, M, shift, partition, sim, pos
+    (16, 16, 8, 4, "cyclic", "cosine", "table"),
+    (32, 32, 16, 8, "cyclic", "cosine", "table"),
+    (16, 24, 8, 0, "interleaved", "dot", "none"),
+    (32, 32, 32, 16, "cyclic", "dot", "rope2d"),
+    (24, 24, 24, 12, "cyclic", "cosine", "table"),
+    (14, 14, 7, 3, "cyclic", "cosine", "rope2d"),
+    (24, 24, 12, 5, "cyclic", "dot", "table"),
+    (8, 8, 1, 0, "cyclic", "cosine", "table"),          # one token per window: p = 1, dl = 0
+    (20, 20, 10, 0, "interleaved", "cosine", "none"),
+]
+
+TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 1e-2)}      # (max-abs / max|ref|, relative Frobenius)
+
+
+def _check(name, got, ref, dtype):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite"
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    err = float(np.abs(got - ref).max()) / scale
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    tmax, trel = TOL[dtype]
+    if float(np.abs(ref).max()) == 0.0:
+        assert float(np.abs(got).max()) == 0.0, f"{name}: expected zeros"
+        return
+    assert err <= tmax and rel <= trel, f"{name}: max-abs/scale {err:.3e} rel-fro {rel:.3e} > {TOL[dtype]}"
+
+
+def _run(wl, x, g, dout, table=None, table64=None):
+    out = run_gpu(wl, g, table=table)
+    got = binding.swin_window_attn_bwd(g["q"], g["k"], g["v"], out, dout.to(DEV), heads=wl.heads, M=wl.M,
+                                       shift=wl.shift, partition=wl.partition, sim=wl.sim, pos=wl.pos,
+                                       tau=g["tau"], table=table, rope_base=wl.rope_base)
+    torch.cuda.synchronize()
+    ref = oracle.window_attn_bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(dout), heads=wl.heads, M=wl.M,
+                                 shift=wl.shift, partition=wl.partition, sim=wl.sim, pos=wl.pos,
+                                 tau=f64(x["tau"]), table=table64, rope_base=wl.rope_base)
+    return got, ref
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}x{c[1]}-M{c[2]}-s{c[3]}-{c[4][:3]}-{c[5]}-{c[6]}"
+                                             for c in CASES])
+def test_backward_parity(case, dtype):
+    H, W, M, s, part, sim, pos = case
+    heads = 2
+    wl = synth.small(B=2, H=H, W=W, C=32 * heads, heads=heads, M=M, shift=s, partition=part, sim=sim, pos=pos,
+                     dtype=dtype, hidden=64)
+    x = synth.make_inputs(wl, seed=11)
+    g = gpu_inputs(x)
+    table = table64 = None
+    if pos == "table":
+        # a table with trained-size spread, so the bias gradient matters
+        gen = torch.Generator().manual_seed(5)
+        t = 0.5 * torch.randn(((2 * M - 1) ** 2, heads), generator=gen)
+        table, table64 = t.to(DEV), f64(t)
+    got, ref = _run(wl, x, g, synth.make_dout(wl), table, table64)
+    for name in ("dq", "dk", "dv"):
+        _check(f"{case} {name}", f64(got[name]), ref[name], dtype)
+    if sim == "cosine":
+        _check(f"{case} dtau", f64(got["dtau"]), ref["dtau"], dtype)
+    if pos == "table":
+        _check(f"{case} dtable", f64(got["dtable"]), ref["dtable"], dtype)
+
+
+def test_backward_tau_at_floor():
+    """tau below its floor: the clamp passes no gradient to tau."""
+    wl = synth.small(B=1, H=16, W=16, C=64, heads=2, M=8, shift=4, sim="cosine", pos="none", dtype="f32")
+    x = synth.make_inputs(wl, seed=3)
+    x["tau"] = torch.tensor([0.005, 0.5])
+    g = gpu_inputs(x)
+    got, ref = _run(wl, x, g, synth.make_dout(wl))
+    assert float(got["dtau"][0]) == 0.0 and ref["dtau"][0] == 0.0
+    _check("dtau", f64(got["dtau"]), ref["dtau"], "f32")
+    _check("dq", f64(got["dq"]), ref["dq"], "f32")
+
+
+def test_backward_empty_batch():
+    wl = synth.small(B=0, H=16, W=16, C=64, heads=2, M=8, shift=4, sim="cosine", pos="table", dtype="bf16")
+    z = torch.zeros((0, 16, 16, 64), dtype=torch.bfloat16, device=DEV)
+    tab = torch.zeros((225, 2), device=DEV)
+    got = binding.swin_window_attn_bwd(z, z, z, z, z, heads=2, M=8, shift=4, sim="cosine", pos="table",
+                                       tau=torch.ones(2, device=DEV), table=tab)
+    torch.cuda.synchronize()
+    assert got["dq"].numel() == 0
+    assert float(got["dtable"].abs().max()) == 0.0 and float(got["dtau"].abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("M,norm_M,mode,heads,hidden", [(8, None, 0, 3, 512), (16, None, 3, 3, 512),
+                                                        (24, 12, 1, 16, 512), (5, 9, 2, 2, 37),
+                                                        (12, None, 3, 20, 300)])
+def test_cpb_table_backward(M, norm_M, mode, heads, hidden):
+    gen = torch.Generator().manual_seed(M)
+    w1, b1 = torch.randn(hidden, 2, generator=gen), torch.randn(hidden, generator=gen)
+    w2, b2 = 0.1 * torch.randn(heads, hidden, generator=gen), torch.randn(heads, generator=gen)
+    dt = torch.randn(((2 * M - 1) ** 2, heads), generator=gen)
+    d = lambda t: t.to(DEV)
+    table = binding.swin_cpb_table(M, d(w1), d(b1), d(w2), d(b2), cpb_mode=mode, norm_M=norm_M)
+    got = binding.swin_cpb_table_bwd(M, d(w1), d(b1), d(w2), table, d(dt), cpb_mode=mode, norm_M=norm_M)
+    torch.cuda.synchronize()
+    ref = oracle.cpb_table_bwd(M, f64(w1), f64(b1), f64(w2), f64(b2), f64(dt), mode=mode, norm_M=norm_M)
+    for name, gv, rv in zip(("dw1", "db1", "dw2", "db2"), got, ref):
+        _check(name, f64(gv), rv, "f32")

@@ -60,6 +60,10 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = [vp, vp] + [i32] * 8 + [vp]
         L.swin_window_attn_fwd.restype = i32
         L.swin_window_attn_fwd.argtypes = [ctypes.POINTER(SwinAttnDesc)] + [vp] * 8
+        L.swin_window_attn_bwd.restype = i32
+        L.swin_window_attn_bwd.argtypes = [ctypes.POINTER(SwinAttnDesc)] + [vp] * 14
+        L.swin_cpb_table_bwd.restype = i32
+        L.swin_cpb_table_bwd.argtypes = [i32] * 4 + [vp] * 5 + [i32] + [vp] * 5
         L.swin_window_attn_kernel.restype = ctypes.c_char_p
         L.swin_window_attn_kernel.argtypes = [ctypes.POINTER(SwinAttnDesc)]
         L.swin_status_string.restype = ctypes.c_char_p
@@ -184,6 +188,57 @@ def swin_window_attn_fwd(q, k, v, *, heads: int, M: int, shift: int = 0, partiti
     _check(lib().swin_window_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                       _ptr(tau), _ptr(table), _ptr(rope_freqs), _stream(q, stream)))
     return out
+
+
+def swin_window_attn_bwd(q, k, v, out, dout, *, heads: int, M: int, shift: int = 0, partition="cyclic",
+                         sim="cosine", pos="none", tau=None, table=None, rope_freqs=None,
+                         tau_min: float = 0.01, rope_base: float = 10000.0, layout="grid", grid=None,
+                         want_dtau: bool = True, want_dtable: bool = True, desc: SwinAttnDesc | None = None,
+                         stream=None) -> dict:
+    """Backward of swin_window_attn_fwd: dq, dk, dv (like q), and dtau
+    (heads fp32, COSINE) and dtable ((2M-1)^2 x heads fp32, TABLE) when wanted."""
+    if desc is None:
+        if _enum(LAYOUT, layout) == 0:
+            B, H, W, C = q.shape
+        else:
+            B, H, W = grid
+            C = q.shape[-1]
+        desc = make_desc(B=B, H=H, W=W, C=C, heads=heads, M=M, shift=shift, partition=partition,
+                         sim=sim, pos=pos, dtype=q.dtype, layout=layout, tau_min=tau_min,
+                         rope_base=rope_base)
+    for t in (q, k, v, out, dout):
+        if not t.is_contiguous() or t.dtype != q.dtype or t.shape != q.shape:
+            raise ValueError("q, k, v, out, dout must be contiguous tensors of one shape and dtype")
+    for t in (tau, table, rope_freqs):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("tau, table and rope_freqs must be contiguous fp32")
+    g = {"dq": torch.empty_like(q), "dk": torch.empty_like(q), "dv": torch.empty_like(q)}
+    dtau = dtable = None
+    if want_dtau and _enum(SIM, sim) == 0:
+        dtau = g["dtau"] = torch.empty(heads, dtype=torch.float32, device=q.device)
+    if want_dtable and _enum(POS, pos) == 1:
+        dtable = g["dtable"] = torch.empty(((2 * M - 1) ** 2, heads), dtype=torch.float32, device=q.device)
+    _check(lib().swin_window_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+                                      _ptr(tau), _ptr(table), _ptr(rope_freqs), _ptr(g["dq"]), _ptr(g["dk"]),
+                                      _ptr(g["dv"]), _ptr(dtau), _ptr(dtable), _stream(q, stream)))
+    return g
+
+
+def swin_cpb_table_bwd(M: int, w1, b1, w2, table, dtable, *, cpb_mode: int = CPB_PAPER, norm_M=None,
+                       stream=None):
+    """Gradients (dw1, db1, dw2, db2) of the meta network from dtable; table is
+    the forward's table (needed for CPB_SIGMOID16)."""
+    heads, hidden = w2.shape
+    for t in (w1, b1, w2, table, dtable):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("CPB parameters and tables must be contiguous fp32")
+    dw1, dw2 = torch.empty_like(w1), torch.empty_like(w2)
+    db1 = torch.empty(hidden, dtype=torch.float32, device=w1.device)
+    db2 = torch.empty(heads, dtype=torch.float32, device=w1.device)
+    _check(lib().swin_cpb_table_bwd(M, M if norm_M is None else norm_M, heads, hidden, _ptr(w1), _ptr(b1),
+                                    _ptr(w2), _ptr(table), _ptr(dtable), cpb_mode, _ptr(dw1), _ptr(db1),
+                                    _ptr(dw2), _ptr(db2), _stream(w1, stream)))
+    return dw1, db1, dw2, db2
 
 
 def swin_window_attn_kernel(desc: SwinAttnDesc) -> str:

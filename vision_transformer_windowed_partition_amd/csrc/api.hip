@@ -224,6 +224,78 @@ int swin_window_attn_fwd(const swin_attn_desc* d, const void* q, const void* k, 
     return hip_status(e, "swin_window_attn_fwd launch");
 }
 
+int swin_window_attn_bwd(const swin_attn_desc* d, const void* q, const void* k, const void* v,
+                         const void* out, const void* dout, const float* tau, const float* table,
+                         const float* rope_freqs, void* dq, void* dk, void* dv, float* dtau, float* dtable,
+                         void* stream)
+{
+    int st = check_desc(d, rope_freqs != nullptr);
+    if (st) return st;
+    if (d->C != d->heads * 32) return fail(SWIN_EUNSUPPORTED, "backward: head dim %d (32 only)", d->C / d->heads);
+    if (d->M > 32) return fail(SWIN_EUNSUPPORTED, "backward: M=%d (32 at most)", d->M);
+    const size_t es = d->dtype == SWIN_DT_F32 ? 4 : 2;
+    const size_t bytes = (size_t)d->B * d->H * d->W * d->C * es;
+    if (d->sim == SWIN_SIM_COSINE && !tau) return fail(SWIN_EINVAL, "COSINE needs tau");
+    if (d->pos == SWIN_POS_TABLE && !table) return fail(SWIN_EINVAL, "POS_TABLE needs a table");
+    const void* in[5] = {q, k, v, out, dout};
+    void* g[3] = {dq, dk, dv};
+    if (bytes) {
+        uintptr_t al = 0;
+        for (const void* x : in) { if (!x) return fail(SWIN_EINVAL, "NULL q, k, v, out or dout"); al |= (uintptr_t)x; }
+        for (void* x : g) { if (!x) return fail(SWIN_EINVAL, "NULL dq, dk or dv"); al |= (uintptr_t)x; }
+        if (al & 15) return fail(SWIN_EINVAL, "tensors must be 16-byte aligned");
+        for (void* x : g) {
+            for (const void* y : in)
+                if (overlaps(x, bytes, y, bytes)) return fail(SWIN_EINVAL, "a gradient overlaps an input");
+            for (void* y : g)
+                if (x != y && overlaps(x, bytes, y, bytes)) return fail(SWIN_EINVAL, "gradients overlap");
+        }
+    }
+    const int S = 2 * d->M - 1;
+    const size_t tb = (size_t)S * S * d->heads * sizeof(float);
+    if (dtable && d->pos == SWIN_POS_TABLE && table && overlaps(dtable, tb, table, tb))
+        return fail(SWIN_EINVAL, "dtable overlaps the table");
+
+    swin::AttnParams p = params_of(d);
+    p.q = q; p.k = k; p.v = v; p.out = nullptr;
+    p.tau = tau; p.table = table; p.rope_freqs = rope_freqs;
+    return hip_status(swin::launch_attn_bwd(p, out, dout, dq, dk, dv, dtau, dtable, (hipStream_t)stream),
+                      "swin_window_attn_bwd launch");
+}
+
+int swin_cpb_table_bwd(int32_t M, int32_t norm_M, int32_t heads, int32_t hidden, const float* w1,
+                       const float* b1, const float* w2, const float* table, const float* dtable,
+                       int32_t cpb_mode, float* dw1, float* db1, float* dw2, float* db2, void* stream)
+{
+    if (cpb_mode < 0 || cpb_mode > (SWIN_CPB_CODE_NORM | SWIN_CPB_SIGMOID16))
+        return fail(SWIN_EINVAL, "unknown cpb_mode %d", cpb_mode);
+    if (M < 1 || M > 64) return fail(SWIN_EINVAL, "M=%d outside [1, 64]", M);
+    if ((cpb_mode & SWIN_CPB_CODE_NORM) && (norm_M < 2 || norm_M > 4096))
+        return fail(SWIN_EINVAL, "normalising window %d outside [2, 4096]", norm_M);
+    if (heads < 1 || heads > 64) return fail(SWIN_EINVAL, "heads=%d outside [1, 64]", heads);
+    if (hidden < 1 || hidden > 4096) return fail(SWIN_EINVAL, "hidden=%d outside [1, 4096]", hidden);
+    if (!w1 || !w2 || !dtable || !dw1 || !dw2) return fail(SWIN_EINVAL, "NULL w1, w2, dtable, dw1 or dw2");
+    if ((cpb_mode & SWIN_CPB_SIGMOID16) && !table) return fail(SWIN_EINVAL, "SIGMOID16 needs the forward table");
+    const size_t tb = (size_t)(2 * M - 1) * (2 * M - 1) * heads * sizeof(float);
+    const void* in[5] = {w1, b1, w2, table, dtable};
+    const size_t insz[5] = {(size_t)hidden * 8, (size_t)hidden * 4, (size_t)heads * hidden * 4, tb, tb};
+    float* out[4] = {dw1, db1, dw2, db2};
+    const size_t outsz[4] = {(size_t)hidden * 8, (size_t)hidden * 4, (size_t)heads * hidden * 4,
+                             (size_t)heads * 4};
+    for (int i = 0; i < 4; ++i) {
+        if (!out[i]) continue;
+        for (int j = 0; j < 5; ++j)
+            if (in[j] && overlaps(out[i], outsz[i], in[j], insz[j]))
+                return fail(SWIN_EINVAL, "a gradient overlaps an input");
+        for (int j = 0; j < 4; ++j)
+            if (j != i && out[j] && overlaps(out[i], outsz[i], out[j], outsz[j]))
+                return fail(SWIN_EINVAL, "gradients overlap");
+    }
+    return hip_status(swin::launch_cpb_table_bwd(M, norm_M, heads, hidden, w1, b1, w2, table, dtable, cpb_mode,
+                                                 dw1, db1, dw2, db2, (hipStream_t)stream),
+                      "swin_cpb_table_bwd launch");
+}
+
 const char* swin_window_attn_kernel(const swin_attn_desc* d)
 {
     if (check_desc(d, true) != SWIN_OK) return nullptr;

@@ -109,7 +109,96 @@ cpb_table_kernel(int M, int heads, int hidden, const float* __restrict__ w1, con
     }
 }
 
+// Backward of the table: gradients of G's parameters from dtable.  Per table
+// row, a = W1 x + b1, hid = relu(a); dg = dtable (SIGMOID16: times
+// dT/dG = T (1 - T/16), T the forward table); dW2 += dg hid^T, db2 += dg,
+// dhid = W2^T dg, da = dhid [a > 0], dW1 += da x^T, db1 += da.
+// Thread = hidden unit, workgroup = (256 units, BR table rows, HB heads): it
+// sums its rows in registers and adds them to the outputs with one atomic
+// per value (the outputs start at zero).  dhid is linear in dg, so the head
+// blocks' partial dW1 and db1 add up.
+constexpr int BR = 64;         // table rows per workgroup
+constexpr int HB = 16;         // heads per workgroup
+
+__global__ void __launch_bounds__(256)
+cpb_table_bwd_kernel(int M, int heads, int hidden, const float* __restrict__ w1, const float* __restrict__ b1,
+                     const float* __restrict__ w2, const float* __restrict__ table,
+                     const float* __restrict__ dtable, int mode, float norm_scale, float* __restrict__ dw1,
+                     float* __restrict__ db1, float* __restrict__ dw2, float* __restrict__ db2)
+{
+    const int u = blockIdx.x * 256 + threadIdx.x;
+    const int S = 2 * M - 1;
+    const int row0 = blockIdx.y * BR, row1 = min(row0 + BR, S * S);
+    const int o0 = blockIdx.z * HB;
+    const bool unit = u < hidden;
+    float w1x = 0.0f, w1y = 0.0f, bb = 0.0f, w2c[HB];
+#pragma unroll
+    for (int o = 0; o < HB; ++o) w2c[o] = unit && o0 + o < heads ? w2[(size_t)(o0 + o) * hidden + u] : 0.0f;
+    if (unit) { w1x = w1[2 * u]; w1y = w1[2 * u + 1]; bb = b1 ? b1[u] : 0.0f; }
+    float gw2[HB], gx = 0.0f, gy = 0.0f, gb = 0.0f, gb2 = 0.0f;
+#pragma unroll
+    for (int o = 0; o < HB; ++o) gw2[o] = 0.0f;
+    // db2 of head o0 + threadIdx.x, in the first unit block
+    const bool own_b2 = blockIdx.x == 0 && threadIdx.x < HB && o0 + threadIdx.x < heads;
+    for (int row = row0; row < row1; ++row) {
+        const float fx = cpb_input(row % S - (M - 1), mode, norm_scale);
+        const float fy = cpb_input(row / S - (M - 1), mode, norm_scale);
+        const float a = fmaf(w1x, fx, fmaf(w1y, fy, bb));
+        const float hid = fmaxf(a, 0.0f);
+        float dh = 0.0f;
+#pragma unroll
+        for (int o = 0; o < HB; ++o) {
+            if (o0 + o >= heads) break;
+            const size_t at = (size_t)row * heads + o0 + o;
+            float dg = dtable[at];
+            if (mode & SWIN_CPB_SIGMOID16) { const float t = table[at]; dg *= t * (1.0f - t * (1.0f / 16.0f)); }
+            gw2[o] = fmaf(dg, hid, gw2[o]);
+            dh = fmaf(w2c[o], dg, dh);
+            if (own_b2 && o == (int)threadIdx.x) gb2 += dg;
+        }
+        const float da = a > 0.0f ? dh : 0.0f;
+        gx = fmaf(da, fx, gx);
+        gy = fmaf(da, fy, gy);
+        gb += da;
+    }
+    if (unit) {
+#pragma unroll
+        for (int o = 0; o < HB; ++o)
+            if (o0 + o < heads) unsafeAtomicAdd(&dw2[(size_t)(o0 + o) * hidden + u], gw2[o]);
+        unsafeAtomicAdd(&dw1[2 * u], gx);
+        unsafeAtomicAdd(&dw1[2 * u + 1], gy);
+        if (db1) unsafeAtomicAdd(&db1[u], gb);
+    }
+    if (own_b2 && db2) unsafeAtomicAdd(&db2[o0 + threadIdx.x], gb2);
+}
+
+__global__ void zero4_kernel(float* a, int na, float* b, int nb, float* c, int nc, float* d, int nd)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (a && i < na) a[i] = 0.0f;
+    if (b && i < nb) b[i] = 0.0f;
+    if (c && i < nc) c[i] = 0.0f;
+    if (d && i < nd) d[i] = 0.0f;
+}
+
 }  // namespace
+
+hipError_t launch_cpb_table_bwd(int M, int norm_M, int heads, int hidden, const float* w1, const float* b1,
+                                const float* w2, const float* table, const float* dtable, int mode, float* dw1,
+                                float* db1, float* dw2, float* db2, hipStream_t stream)
+{
+    const int S = 2 * M - 1;
+    const int n = max(max(2 * hidden, heads * hidden), heads);
+    zero4_kernel<<<(n + 255) / 256, 256, 0, stream>>>(dw1, 2 * hidden, db1, hidden, dw2, heads * hidden, db2,
+                                                       heads);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const float norm_scale = norm_M > 1 ? 8.0f / (float)(norm_M - 1) : 0.0f;
+    dim3 grid((hidden + 255) / 256, (S * S + BR - 1) / BR, (heads + HB - 1) / HB);
+    cpb_table_bwd_kernel<<<grid, 256, 0, stream>>>(M, heads, hidden, w1, b1, w2, table, dtable, mode, norm_scale,
+                                                   dw1, db1, dw2, db2);
+    return hipGetLastError();
+}
 
 hipError_t launch_cpb_table(int M, int norm_M, int heads, int hidden, const float* w1, const float* b1,
                             const float* w2, const float* b2, int mode, float* table, hipStream_t stream)

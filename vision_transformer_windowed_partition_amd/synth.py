@@ -121,6 +121,14 @@ def make_inputs(wl: Workload, seed: int | None = None, tau_range=(0.1, 1.0)) -> 
     return dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), tau=tau, w1=w1, b1=b1, w2=w2, b2=b2)
 
 
+def make_dout(wl: Workload, seed: int = 1000):
+    """Gradient of a loss with respect to the attention output, for backward
+    tests: N(0, 1) of the output's shape, in the workload dtype (CPU)."""
+    g = torch.Generator().manual_seed(int(seed))
+    d = torch.randn((wl.B, wl.H, wl.W, wl.C), generator=g, dtype=torch.float32)
+    return d.to(torch_dtype(wl.dtype))
+
+
 def small(name: str = "tiny", *, B=2, H=16, W=16, C=64, heads=2, M=8, shift=4,
           partition="cyclic", sim="cosine", pos="table", dtype="f32", hidden=64) -> Workload:
     """A small workload for tests (same draw recipe)."""

@@ -156,6 +156,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warm", action="store_true", help="reuse one input set (cache-warm)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle wall time")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward step instead: swin_window_attn_bwd (dq, dk, dv, dtau, dtable) "
+                         "and swin_cpb_table_bwd, from one forward's output")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run copies of known size for HBM-counter calibration: y = -x over "
                          "2^28 fp32 (whole lines), then an interleaved window gather and its "
@@ -191,6 +194,8 @@ def main(argv=None) -> int:
                              rope_base=wl.rope_base)
     stream = torch.cuda.current_stream(dev)
     kernel = binding.swin_window_attn_kernel(desc)
+    if args.backward:
+        return bench_backward(args, wl, x, sets, nsets, par, table, desc, stream)
 
     def step(i, timed=None):
         q, k, v, o = sets[i % nsets]
@@ -282,6 +287,84 @@ def main(argv=None) -> int:
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_budget)
+    print(json.dumps(out))
+    return 0
+
+
+def bench_backward(args, wl, x, sets, nsets, par, table, desc, stream) -> int:
+    """Backward step: dq, dk, dv, dtau, dtable from (q, k, v, out, dout), then
+    the meta network's parameter gradients from dtable.  Algorithmic work per
+    (window, head): the five N x N x d contractions of the backward (scores
+    recomputed, dP, dV, dQ, dK: 10 N^2 d flops) and 8 N d elements moved
+    (read q, k, v, out, dout; write dq, dk, dv)."""
+    import torch
+
+    from vision_transformer_windowed_partition_amd import binding, synth
+
+    tab = None
+    if wl.pos == "table":
+        tab = binding.swin_cpb_table(wl.M, par["w1"], par["b1"], par["w2"], par["b2"], out=table)
+    dout = synth.make_dout(wl).to(sets[0][0].device)
+    for q, k, v, o in sets:
+        binding.swin_window_attn_fwd(q, k, v, heads=wl.heads, M=wl.M, desc=desc, tau=par["tau"], table=tab, out=o)
+    torch.cuda.synchronize()
+    kw = dict(heads=wl.heads, M=wl.M, shift=wl.shift, partition=wl.partition, sim=wl.sim, pos=wl.pos,
+              tau=par["tau"], table=tab, rope_base=wl.rope_base, desc=desc, stream=stream)
+
+    def step(i, timed=None):
+        q, k, v, o = sets[i % nsets]
+        if timed is not None:
+            timer.record(timed, False)
+        g = binding.swin_window_attn_bwd(q, k, v, o, dout, **kw)
+        if timed is not None:
+            timer.record(timed, True)
+        if wl.pos == "table":
+            binding.swin_cpb_table_bwd(wl.M, par["w1"], par["b1"], par["w2"], tab, g["dtable"], stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    timer = HipTimer(args.steps, stream.cuda_stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = timer.elapsed_ms()
+    timer.close()
+    kern_avg = sum(kern_ms) / len(kern_ms)
+    flops = int(2.5 * wl.flops)
+    alg_bytes = 2 * wl.bytes
+    kern_s = kern_avg * 1e-3
+    tflops = flops / kern_s / 1e12
+    roof = {"bound": "alu", "achieved": round(tflops, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / FP32_PEAK_TFLOPS, 4), "traffic": None, "kernel": "attn_bwd_kernel",
+            "kernel_ms": round(kern_avg, 5), "kernel_ms_median": round(sorted(kern_ms)[len(kern_ms) // 2], 5),
+            "kernel_ms_min": round(min(kern_ms), 5), "alg_bytes_per_launch": alg_bytes,
+            "alg_flops_per_launch": flops}
+    out = {
+        "metric": "window-attn bwd tokens/s (dq, dk, dv, dtau, dtable + CPB meta-network gradients)",
+        "value": round(wl.tokens / (wall / args.steps), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v/dout, random-init log-CPB MLP)",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "W": wl.W, "C": wl.C, "heads": wl.heads,
+                   "M": wl.M, "shift": wl.shift, "partition": wl.partition, "sim": wl.sim,
+                   "pos": wl.pos, "pass": "backward",
+                   "cache": "warm" if args.warm else f"cold ({nsets} rotating sets)",
+                   "parallelism": "none (1 GPU)"},
+        "tflops": round(tflops, 2),
+        "hbm_gbs": round(alg_bytes / kern_s / 1e9, 1),
+        "roofline": roof,
+    }
     print(json.dumps(out))
     return 0
 

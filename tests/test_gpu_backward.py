@@ -44,7 +44,9 @@ def _check(name, got, ref, dtype):
     rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
     tmax, trel = TOL[dtype]
     if float(np.abs(ref).max()) == 0.0:
-        assert float(np.abs(got).max()) == 0.0, f"{name}: expected zeros"
+        # e.g. one token per window: dl = dP - D vanishes exactly in the oracle;
+        # in fp32 dP (a matrix-core sum) and D (dout . out) round differently
+        assert float(np.abs(got).max()) <= 1e-5, f"{name}: expected zeros"
         return
     assert err <= tmax and rel <= trel, f"{name}: max-abs/scale {err:.3e} rel-fro {rel:.3e} > {TOL[dtype]}"
 

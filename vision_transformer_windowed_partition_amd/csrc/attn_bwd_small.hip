@@ -1,0 +1,560 @@
+// Backward of window attention on the gfx950 matrix cores, bf16, windows of
+// up to 256 tokens (M <= 16), no rotary positions.
+//
+// Gradient of the SwinV2 card's eq. 1-2 with the log-CPB table of eq. 3-4
+// over cyclic-shift or interleaved windows, per (window, head); with
+// logit_ij = (q_i . k_j) a_i c_j + b_ij (COSINE: a_i = 1/(tau' ||q_i||),
+// c_j = 1/||k_j||; DOT: a_i = c_j = 1/sqrt(d)), p the softmax over the
+// query's shift region and D_i = dout_i . out_i:
+//   dl_ij = p_ij (dout_i . v_j - D_i)
+//   dv_j  = sum_i p_ij dout_i
+//   G_i   = sum_j dl_ij c_j k_j,   dq_i = a_i (G_i - q_i (q_i . G_i) / ||q_i||^2)
+//   H_j   = sum_i dl_ij a_i q_i,   dk_j = c_j (H_j - k_j (k_j . H_j) / ||k_j||^2)
+//   (DOT: no projection terms), dtable[offset(i, j)] += dl_ij,
+//   dtau = -(1/tau) sum dl_ij cos_ij / tau while tau > tau_min.
+// q, k, v, dout stay raw (exact bf16) in LDS; the scales a_i, c_j multiply
+// in fp32, so nothing is rounded before the products but the weights.
+//
+// A workgroup of four wavefronts serves one head: for 9 <= M <= 16 one
+// window shared by the four, for M <= 8 one window each.  LDS holds the
+// window's K, V, Q and dout as 64-byte rows in key-slot order (8 slots per
+// row segment, XOR-swizzled 16-byte pieces, filled by LDS-DMA), the per-slot
+// scales, log-sum-exp and D, the head's bias table (reversed, log2 units) and
+// the workgroup's bias-gradient accumulator.  Three passes:
+//   0  query-major (like the forward): S^T = K Q^T per 32-key chunk, running
+//      maximum and sum -> log-sum-exp of each query;
+//   B  query-major: S^T and dP^T = V dout^T, dl, then
+//      G^T += K^T (dl c)^T with K^T read transposed from the K rows
+//      (ds_read_b64_tr_b16); dq, dtau and the bias gradient;
+//   A  key-major, one 16-key tile at a time: S = Q K^T and dP = dout V^T with
+//      the query rows permuted so each lane holds 8 consecutive query slots
+//      of one key (the B-operand layout of P and dS), then
+//      dV^T += dout^T P and H^T += Q^T (dl a), dout^T and Q^T read transposed.
+// All products are v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
+#include "common.hpp"
+#include "lanes.hpp"
+#include "launch.hpp"
+#include "tile_io.hpp"
+
+namespace swin {
+
+namespace {
+
+using namespace tio;
+using namespace lanes;
+
+constexpr int WAVES = 4;
+
+struct BwdLayout {
+    int NSP;                   // key slots in use: M rows of M rounded up to 8
+    int NQT;                   // query tiles of 16 tokens per window
+    int wgs;                   // workgroups with work
+    int P;                     // work ids per XCD slot
+    float inv_M;
+};
+
+struct BwdSmallArgs {
+    const void* out;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dtau;
+    float* dtable;
+};
+
+__device__ __forceinline__ bf16x8 rowfrag(const __bf16* rows, int s, int piece)
+{
+    return *(const bf16x8*)(rows + s * D + ((piece ^ v_swizzle(s)) * 8));
+}
+
+// quad reductions (lanes ^1, ^2) by DPP quad_perm
+__device__ __forceinline__ float quad_sum(float x)
+{
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));
+    return x;
+}
+
+// DPP row shifts within 16-lane rows; lanes whose source falls outside the
+// row read zero.  shl: lane i reads lane i + N; shr: lane i reads lane i - N.
+template <int N>
+__device__ __forceinline__ float row_shl(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + N, 0xf, 0xf, true));
+}
+template <int N>
+__device__ __forceinline__ float row_shr(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
+}
+
+// Slot s of a window: row (s >> 3) / GPR, column 8 ((s >> 3) % GPR) + (s & 7).
+template <int GPR>
+__device__ __forceinline__ void slot_rc(int s, int& r, int& c)
+{
+    const int gam = s >> 3;
+    r = gam / GPR;
+    c = 8 * (gam % GPR) + (s & 7);
+}
+
+template <int SIM, int POS, int NCH, int QW>
+__global__ void __launch_bounds__(256)
+attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
+{
+    constexpr int GPR = NCH <= 2 ? 1 : 2;
+    constexpr int WH = WAVES / QW;
+    constexpr int NS = NCH * 32;                   // slots per window (padded)
+    constexpr int SETS = 2 * NCH / QW;             // 1 KB row pieces per tensor and wave
+    extern __shared__ __attribute__((aligned(16))) float smem_f[];
+    const Geometry& g = p.g;
+    const int M = g.M, N = g.N, S = 2 * M - 1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = lane >> 4, li = lane & 15;
+    const int wh = wave / QW, rank = wave - wh * QW;
+
+    const int tabsz = POS == SWIN_POS_TABLE ? (S * S + 8 + 3) / 4 * 4 : 0;
+    float* bias2 = smem_f;                                     // [S*S + 8] reversed, log2 units
+    float* dtab = bias2 + tabsz;                               // [S*S] reversed, natural units
+    float* red = dtab + tabsz;                                 // [16]
+    float* scal = red + 16 + wh * (4 * NS);                    // this window's per-slot scalars
+    float* ksc = scal;                                         // [NS] c_j
+    float* qsc = ksc + NS;                                     // [NS] log2(e) a_i
+    float* lse = qsc + NS;                                     // [NS] log2-sum-exp of the logits
+    float* dd = lse + NS;                                      // [NS] D_i
+    __bf16* rows = (__bf16*)(red + 16 + WH * 4 * NS) + wh * (4 * NS * D);
+    __bf16* krow = rows;
+    __bf16* vrow = rows + NS * D;
+    __bf16* qrow = rows + 2 * NS * D;
+    __bf16* orow = rows + 3 * NS * D;
+
+    const int work = (blockIdx.x & 7) * L.P + (blockIdx.x >> 3);
+    if (work >= L.wgs) return;
+    const int h = work % g.heads;
+    const int wloc = (work / g.heads) * WH + wh;
+    const bool active = wloc < g.nwin;
+    const int win = active ? wloc : 0;
+    float tau = 1.0f;
+    if (SIM == SWIN_SIM_COSINE) tau = fmaxf(p.tau[h], p.tau_min);
+    const WinPlace wp = place_window(g, win);
+    const WinGeo& wg = wp.wg;
+    const uint32_t bytes = active ? (uint32_t)(wp.span - h * D) * 2u : 0u;
+
+    // ---- staging: the four tensors' rows by LDS-DMA; piece j of a tensor
+    // is slots 16 j .. 16 j + 15, lane l filling LDS piece l%4 of slot
+    // 16 j + l/4 with channel piece (l%4) ^ v_swizzle(slot)
+    {
+        const void* src[4] = {p.k, p.v, p.q, a.dout};
+#pragma unroll
+        for (int tsr = 0; tsr < 4; ++tsr) {
+            const RawRsrc rr = raw_rsrc((const uint16_t*)src[tsr] + wp.base + h * D, bytes);
+#pragma unroll
+            for (int k = 0; k < SETS; ++k) {
+                const int j = rank + QW * k;
+                const int s = 16 * j + (lane >> 2);
+                int r, c;
+                slot_rc<GPR>(s, r, c);
+                const int piece = (lane & 3) ^ v_swizzle(s);
+                dma16(rr, rows + (size_t)tsr * NS * D + (size_t)j * 512,
+                      masked(wg.tok(r, c) + 16u * piece, r < M && c < M));
+            }
+        }
+    }
+    //   per-slot scalars: four lanes per slot (a 16-byte piece each), slots
+    //   rank*16 + 16 QW it ...; norms of k and q, and dout . out
+    {
+        const Rsrc kr = make_rsrc((const uint16_t*)p.k + wp.base + h * D, bytes);
+        const Rsrc qr = make_rsrc((const uint16_t*)p.q + wp.base + h * D, bytes);
+        const Rsrc gr = make_rsrc((const uint16_t*)a.dout + wp.base + h * D, bytes);
+        const Rsrc orr = make_rsrc((const uint16_t*)a.out + wp.base + h * D, bytes);
+        const int piece = lane & 3;
+        for (int s0 = 16 * rank; s0 < NS; s0 += 16 * QW) {
+            const int s = s0 + (lane >> 2);
+            int r, c;
+            slot_rc<GPR>(s, r, c);
+            const uint32_t off = masked(wg.tok(r, c) + 16u * piece, r < M && c < M);
+            float kf[8], qf[8], gf[8], of[8];
+            unpack_bf16x8(load16(kr, off), kf);
+            unpack_bf16x8(load16(qr, off), qf);
+            unpack_bf16x8(load16(gr, off), gf);
+            unpack_bf16x8(load16(orr, off), of);
+            float kk = 0.0f, qq = 0.0f, go = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kk = fmaf(kf[e], kf[e], kk);
+                qq = fmaf(qf[e], qf[e], qq);
+                go = fmaf(gf[e], of[e], go);
+            }
+            kk = quad_sum(kk);
+            qq = quad_sum(qq);
+            go = quad_sum(go);
+            if (piece == 0) {
+                if (SIM == SWIN_SIM_COSINE) {
+                    ksc[s] = 1.0f / fmaxf(sqrtf(kk), 1e-12f);
+                    qsc[s] = kLog2e / (tau * fmaxf(sqrtf(qq), 1e-12f));
+                } else {
+                    ksc[s] = 1.0f;
+                    qsc[s] = kLog2e * 0.17677669529663687f;
+                }
+                dd[s] = go;
+            }
+        }
+    }
+    if (POS == SWIN_POS_TABLE) {
+        for (int i = tid; i < S * S; i += 256) {
+            bias2[S * S - 1 - i] = p.table[(size_t)i * g.heads + h] * kLog2e;
+            dtab[i] = 0.0f;
+        }
+        if (tid < 8) bias2[S * S + tid] = -INFINITY;
+    }
+    vm_wait_all();
+    __syncthreads();
+
+    const bool padded = 8 * GPR != M || NCH * 32 != L.NSP;
+    const bool needs_mask = wp.last_r || wp.last_c || padded;
+    const int negrow = S * S;
+    const int kbase = (grp / GPR) * S + 8 * (grp % GPR);   // bias offset of this lane's key group, chunk 0
+
+    // ---- pass 0: log-sum-exp of this wave's queries
+    if (active) {
+        for (int t0 = rank; t0 < L.NQT; t0 += QW) {
+            const int t = t0 * 16 + li;
+            const bool tv = t < N;
+            const int tt = tv ? t : 0;
+            const int ri = qdiv(tt, L.inv_M), ci = tt - ri * M;
+            const int qs_slot = ri * 8 * GPR + ci;
+            const bf16x8 qf = rowfrag(qrow, qs_slot, grp);
+            const float qs = qsc[qs_slot];
+            const int qoff = (M - 1 - ri) * S + (M - 1 - ci) + kbase;
+            int rlo = 0, rhi = M, clo = 0, chi = M;
+            if (wp.last_r) { if (ri < M - g.shift) rhi = M - g.shift; else rlo = M - g.shift; }
+            if (wp.last_c) { if (ci < M - g.shift) chi = M - g.shift; else clo = M - g.shift; }
+            float m = -INFINITY, l = 0.0f;
+#pragma unroll 2
+            for (int c = 0; c < NCH; ++c) {
+                const bf16x8 ka = rowfrag(krow, 32 * c + 8 * (li >> 2) + (li & 3), grp);
+                const bf16x8 kb = rowfrag(krow, 32 * c + 8 * (li >> 2) + (li & 3) + 4, grp);
+                const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+                const f32x4 sa = mfma(ka, qf, z), sb = mfma(kb, qf, z);
+                const f32x4 k0 = *(const f32x4*)(ksc + 32 * c + 8 * grp);
+                const f32x4 k1 = *(const f32x4*)(ksc + 32 * c + 8 * grp + 4);
+                const int gam = 4 * c + grp, rj = gam / GPR, cj0 = 8 * (gam % GPR);
+                float x[8];
+                float cm = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float sv = e < 4 ? sa[e] : sb[e - 4];
+                    const float kv = e < 4 ? k0[e] : k1[e - 4];
+                    const int cj = cj0 + e;
+                    const bool ok = !needs_mask || (tv && rj >= rlo && rj < rhi && cj >= clo && cj < chi &&
+                                                    rj < M && cj < M);
+                    float b = 0.0f;
+                    if (POS == SWIN_POS_TABLE) b = bias2[ok ? qoff + (4 / GPR) * c * S + e : negrow];
+                    x[e] = ok ? fmaf(sv * qs, kv, b) : -INFINITY;
+                    cm = fmaxf(cm, x[e]);
+                }
+                cm = max_x32(max_x16(cm));
+                const float mn = fmaxf(m, cm);
+                const float mref = mn == -INFINITY ? 0.0f : mn;
+                float ls = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ls += __builtin_amdgcn_exp2f(x[e] - mref);
+                l = l * __builtin_amdgcn_exp2f(m - mref) + ls;
+                m = mn;
+            }
+            l = sum_x32(sum_x16(l));
+            if (grp == 0 && tv) lse[qs_slot] = m + __builtin_amdgcn_logf(l);
+        }
+    }
+    __syncthreads();
+    if (!active) {
+        // nothing to compute; meet the final barrier
+    } else {
+        const float inv_tau = 1.0f / tau;
+        float dtau_acc = 0.0f;
+        const Rsrc dqr = make_rsrc((const uint16_t*)a.dq + wp.base + h * D, bytes);
+        const Rsrc dkr = make_rsrc((const uint16_t*)a.dk + wp.base + h * D, bytes);
+        const Rsrc dvr = make_rsrc((const uint16_t*)a.dv + wp.base + h * D, bytes);
+
+        // ---- pass B: dq of this wave's queries (query-major)
+        const bool diag = M == 16;
+        for (int t0 = rank; t0 < L.NQT; t0 += QW) {
+            const int t = t0 * 16 + li;
+            const bool tv = t < N;
+            const int tt = tv ? t : 0;
+            const int ri = qdiv(tt, L.inv_M), ci = tt - ri * M;
+            const int qs_slot = ri * 8 * GPR + ci;
+            const bf16x8 qf = rowfrag(qrow, qs_slot, grp);
+            const bf16x8 gf = rowfrag(orow, qs_slot, grp);
+            const float qs = qsc[qs_slot], lq = lse[qs_slot], Dq = dd[qs_slot];
+            const int qoff = (M - 1 - ri) * S + (M - 1 - ci) + kbase;
+            int rlo = 0, rhi = M, clo = 0, chi = M;
+            if (wp.last_r) { if (ri < M - g.shift) rhi = M - g.shift; else rlo = M - g.shift; }
+            if (wp.last_c) { if (ci < M - g.shift) chi = M - g.shift; else clo = M - g.shift; }
+            f32x4 G0 = {0.0f, 0.0f, 0.0f, 0.0f}, G1 = G0;
+#pragma unroll 2
+            for (int c = 0; c < NCH; ++c) {
+                const int sA = 32 * c + 8 * (li >> 2) + (li & 3);
+                const bf16x8 ka = rowfrag(krow, sA, grp), kb = rowfrag(krow, sA + 4, grp);
+                const bf16x8 va = rowfrag(vrow, sA, grp), vb = rowfrag(vrow, sA + 4, grp);
+                const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+                const f32x4 sa = mfma(ka, qf, z), sb = mfma(kb, qf, z);
+                const f32x4 pa = mfma(va, gf, z), pb = mfma(vb, gf, z);
+                const f32x4 k0 = *(const f32x4*)(ksc + 32 * c + 8 * grp);
+                const f32x4 k1 = *(const f32x4*)(ksc + 32 * c + 8 * grp + 4);
+                const int gam = 4 * c + grp, rj = gam / GPR, cj0 = 8 * (gam % GPR);
+                const int boff = qoff + (4 / GPR) * c * S;
+                float ds[8], dlv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float sv = e < 4 ? sa[e] : sb[e - 4];
+                    const float dpv = e < 4 ? pa[e] : pb[e - 4];
+                    const float kv = e < 4 ? k0[e] : k1[e - 4];
+                    const int cj = cj0 + e;
+                    const bool ok = tv && (!needs_mask || (rj >= rlo && rj < rhi && cj >= clo && cj < chi &&
+                                                           rj < M && cj < M));
+                    float b = 0.0f;
+                    if (POS == SWIN_POS_TABLE) b = bias2[ok ? boff + e : negrow];
+                    const float xs = sv * qs * kv;                 // log2 units, without the bias
+                    const float pr = ok ? __builtin_amdgcn_exp2f(xs + b - lq) : 0.0f;
+                    const float dl = pr * (dpv - Dq);
+                    ds[e] = dl * (SIM == SWIN_SIM_COSINE ? kv : 0.17677669529663687f);
+                    dlv[e] = dl;
+                    if (SIM == SWIN_SIM_COSINE) dtau_acc = fmaf(dl, xs, dtau_acc);
+                    if (POS == SWIN_POS_TABLE && a.dtable && !diag && ok) atomicAdd(&dtab[boff + e], dl);
+                }
+                if (POS == SWIN_POS_TABLE && a.dtable && diag) {
+                    // M == 16: the tile is one window row, lane li its column li,
+                    // so (lane li, element e) lands at boff(0) - li + e.  Row sums
+                    // along those diagonals: lane li gathers d = -li from lanes
+                    // li + e (element e) and, for li = 1..7, d = 8 - li from lanes
+                    // li - 8 + e; masked pairs carry dl = 0.
+                    float A = dlv[0] + row_shl<1>(dlv[1]) + row_shl<2>(dlv[2]) + row_shl<3>(dlv[3]) +
+                              row_shl<4>(dlv[4]) + row_shl<5>(dlv[5]) + row_shl<6>(dlv[6]) + row_shl<7>(dlv[7]);
+                    float B = row_shr<8>(dlv[0]) + row_shr<7>(dlv[1]) + row_shr<6>(dlv[2]) + row_shr<5>(dlv[3]) +
+                              row_shr<4>(dlv[4]) + row_shr<3>(dlv[5]) + row_shr<2>(dlv[6]) + row_shr<1>(dlv[7]);
+                    // The rows of lane groups 2p and 2p+1 hold the two column
+                    // halves of one key row (positions b-15..b and b-7..b+15):
+                    // group 2p keeps b - li (adding group 2p+1's A from lane
+                    // li + 8), group 2p+1 takes b + 16 - li (its B for li < 8,
+                    // else its A and group 2p's B from lane li - 8).  One
+                    // atomic per lane, no two lanes of the wave on one address.
+                    const bool even = (grp & 1) == 0;
+                    const auto sA = __builtin_amdgcn_permlane16_swap(__float_as_uint(A), __float_as_uint(A), false,
+                                                                     false);
+                    const auto sB = __builtin_amdgcn_permlane16_swap(__float_as_uint(B), __float_as_uint(B), false,
+                                                                     false);
+                    const float pA = __uint_as_float(even ? sA[1] : sA[0]);
+                    const float pB = __uint_as_float(even ? sB[1] : sB[0]);
+                    const float te = A + row_shl<8>(pA);
+                    const float to = row_shr<8>(A) + row_shr<8>(pB);
+                    const float T = even ? te : (li <= 7 ? B : to);
+                    if (even || li != 0) atomicAdd(&dtab[boff + (even ? 0 : 8)], T);
+                }
+                const bf16x8 dsb = pack_bf16x8(ds);
+                G0 = mfma(vt_frag(krow, c, 0, grp, li), dsb, G0);
+                G1 = mfma(vt_frag(krow, c, 1, grp, li), dsb, G1);
+            }
+            // lane holds channels 4 grp..+3 and 16 + 4 grp..+3 of query li
+            float q8[8], g8[8];
+            {
+                // the query's raw channels from its LDS row: piece (4 grp / 8) half (grp & 1)
+                const __bf16* qrw = qrow + qs_slot * D;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int ch = 16 * hh + 4 * grp;
+                    const __bf16* src = qrw + (((ch >> 3) ^ v_swizzle(qs_slot)) * 8) + (ch & 7);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) q8[4 * hh + e] = (float)src[e];
+                }
+                g8[0] = G0[0]; g8[1] = G0[1]; g8[2] = G0[2]; g8[3] = G0[3];
+                g8[4] = G1[0]; g8[5] = G1[1]; g8[6] = G1[2]; g8[7] = G1[3];
+            }
+            float dqv[8];
+            if (SIM == SWIN_SIM_COSINE) {
+                float qg = 0.0f, qq = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { qg = fmaf(q8[e], g8[e], qg); qq = fmaf(q8[e], q8[e], qq); }
+                qg = sum_x32(sum_x16(qg));
+                qq = sum_x32(sum_x16(qq));
+                const float nq = sqrtf(qq);
+                const float ai = inv_tau / fmaxf(nq, 1e-12f);
+                const float pj = nq > 1e-12f ? qg / qq : 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dqv[e] = ai * (g8[e] - q8[e] * pj);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dqv[e] = g8[e];
+            }
+            const uint32_t off = masked(wg.tok(ri, ci) + 8u * grp, tv);
+            store8(dqr, off, pack_bf16x4(dqv[0], dqv[1], dqv[2], dqv[3]));
+            store8(dqr, off + 32u, pack_bf16x4(dqv[4], dqv[5], dqv[6], dqv[7]));
+        }
+
+        // ---- pass A: dk, dv of this wave's 16-key tiles (key-major)
+        const int nkt = (L.NSP + 15) / 16;
+        for (int kt = rank; kt < nkt; kt += QW) {
+            const int sk = 16 * kt + li;                   // this lane's key slot
+            int rj, cj;
+            slot_rc<GPR>(sk, rj, cj);
+            const bool kv_ok = rj < M && cj < M;
+            const bf16x8 kB = rowfrag(krow, sk, grp), vB = rowfrag(vrow, sk, grp);
+            const float cj_s = ksc[sk];
+            int rlo = 0, rhi = M, clo = 0, chi = M;
+            if (wp.last_r) { if (rj < M - g.shift) rhi = M - g.shift; else rlo = M - g.shift; }
+            if (wp.last_c) { if (cj < M - g.shift) chi = M - g.shift; else clo = M - g.shift; }
+            const uint32_t cmask = ((chi >= 32 ? 0xffffffffu : ((1u << chi) - 1u)) & ~((1u << clo) - 1u)) &
+                                   ((1u << M) - 1u);
+            f32x4 V0 = {0.0f, 0.0f, 0.0f, 0.0f}, V1 = V0, H0 = V0, H1 = V0;
+#pragma unroll 2
+            for (int c = 0; c < NCH; ++c) {
+                const int sA = 32 * c + 8 * (li >> 2) + (li & 3);
+                const bf16x8 qa = rowfrag(qrow, sA, grp), qb = rowfrag(qrow, sA + 4, grp);
+                const bf16x8 ga = rowfrag(orow, sA, grp), gb = rowfrag(orow, sA + 4, grp);
+                const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+                const f32x4 sa = mfma(qa, kB, z), sb = mfma(qb, kB, z);
+                const f32x4 pa = mfma(ga, vB, z), pb = mfma(gb, vB, z);
+                // this lane's query slots: 32 c + 8 grp + e, a row segment
+                const int qs0 = 32 * c + 8 * grp;
+                const f32x4 qsA = *(const f32x4*)(qsc + qs0), qsB = *(const f32x4*)(qsc + qs0 + 4);
+                const f32x4 lA = *(const f32x4*)(lse + qs0), lB = *(const f32x4*)(lse + qs0 + 4);
+                const f32x4 dA = *(const f32x4*)(dd + qs0), dB = *(const f32x4*)(dd + qs0 + 4);
+                const int gam = 4 * c + grp, ri = gam / GPR, ci0 = 8 * (gam % GPR);
+                // query (ri, ci0 + e) against key (rj, cj): table row
+                // (ri - rj + M-1) S + (ci0 + e - cj + M-1), reversed position
+                // S*S - 1 - that, decreasing in e
+                const int rev0 = S * S - 1 - ((ri - rj + M - 1) * S + (ci0 - cj + M - 1));
+                const bool rok = kv_ok && ri < M && ri >= rlo && ri < rhi;
+                const uint32_t cbits = rok ? (cmask >> ci0) & 0xffu : 0u;
+                float pp[8], dsa[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float sv = e < 4 ? sa[e] : sb[e - 4];
+                    const float dpv = e < 4 ? pa[e] : pb[e - 4];
+                    const float qv = e < 4 ? qsA[e] : qsB[e - 4];
+                    const float lv = e < 4 ? lA[e] : lB[e - 4];
+                    const float dv_ = e < 4 ? dA[e] : dB[e - 4];
+                    const bool ok = ((cbits >> e) & 1u) != 0u;
+                    float b = 0.0f;
+                    if (POS == SWIN_POS_TABLE) b = bias2[ok ? rev0 - e : negrow];
+                    const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(sv * qv, cj_s, b) - lv) : 0.0f;
+                    pp[e] = pr;
+                    const float dl = pr * (dpv - dv_);
+                    dsa[e] = dl * (SIM == SWIN_SIM_COSINE ? qv * (1.0f / kLog2e) : 0.17677669529663687f);
+                }
+                const bf16x8 pbf = pack_bf16x8(pp), dsb = pack_bf16x8(dsa);
+                V0 = mfma(vt_frag(orow, c, 0, grp, li), pbf, V0);
+                V1 = mfma(vt_frag(orow, c, 1, grp, li), pbf, V1);
+                H0 = mfma(vt_frag(qrow, c, 0, grp, li), dsb, H0);
+                H1 = mfma(vt_frag(qrow, c, 1, grp, li), dsb, H1);
+            }
+            // lane holds channels 4 grp..+3 and 16 + 4 grp..+3 of key slot sk
+            float k8[8], h8[8], dkv[8];
+            {
+                const __bf16* krw = krow + sk * D;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int ch = 16 * hh + 4 * grp;
+                    const __bf16* src = krw + (((ch >> 3) ^ v_swizzle(sk)) * 8) + (ch & 7);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) k8[4 * hh + e] = (float)src[e];
+                }
+                h8[0] = H0[0]; h8[1] = H0[1]; h8[2] = H0[2]; h8[3] = H0[3];
+                h8[4] = H1[0]; h8[5] = H1[1]; h8[6] = H1[2]; h8[7] = H1[3];
+            }
+            if (SIM == SWIN_SIM_COSINE) {
+                float kh = 0.0f, kk = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { kh = fmaf(k8[e], h8[e], kh); kk = fmaf(k8[e], k8[e], kk); }
+                kh = sum_x32(sum_x16(kh));
+                kk = sum_x32(sum_x16(kk));
+                const float nk = sqrtf(kk);
+                const float pj = nk > 1e-12f ? kh / kk : 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dkv[e] = cj_s * (h8[e] - k8[e] * pj);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dkv[e] = h8[e];
+            }
+            const uint32_t off = masked(wg.tok(rj, cj) + 8u * grp, kv_ok);
+            store8(dkr, off, pack_bf16x4(dkv[0], dkv[1], dkv[2], dkv[3]));
+            store8(dkr, off + 32u, pack_bf16x4(dkv[4], dkv[5], dkv[6], dkv[7]));
+            store8(dvr, off, pack_bf16x4(V0[0], V0[1], V0[2], V0[3]));
+            store8(dvr, off + 32u, pack_bf16x4(V1[0], V1[1], V1[2], V1[3]));
+        }
+        if (SIM == SWIN_SIM_COSINE && a.dtau) {
+            const float s = wave_reduce<Op::Sum>(dtau_acc);
+            if (lane == 0) red[wave] = s;
+        }
+    }
+    if (SIM == SWIN_SIM_COSINE && a.dtau && !active && lane == 0) red[wave] = 0.0f;
+    __syncthreads();
+    // ---- this workgroup's share of dtau and of the table gradient
+    if (SIM == SWIN_SIM_COSINE && a.dtau && tid == 0 && p.tau[h] > p.tau_min) {
+        float s = 0.0f;
+        for (int w = 0; w < WAVES; ++w) s += red[w];
+        // sum dl cos / tau: xs = log2(e) cos / tau
+        unsafeAtomicAdd(&a.dtau[h], s * (-1.0f / (kLog2e * p.tau[h])));
+    }
+    if (POS == SWIN_POS_TABLE && a.dtable)
+        for (int i = tid; i < S * S; i += 256)
+            if (dtab[i] != 0.0f) unsafeAtomicAdd(&a.dtable[(size_t)(S * S - 1 - i) * g.heads + h], dtab[i]);
+}
+
+template <int SIM, int POS>
+hipError_t launch_nch(const AttnParams& p, const BwdSmallArgs& a, const BwdLayout& L, int nch, int grid,
+                      size_t lds, hipStream_t s)
+{
+    auto* fn = nch <= 2 ? attn_bwd_small_kernel<SIM, POS, 2, 1>
+             : nch <= 6 ? attn_bwd_small_kernel<SIM, POS, 6, 4>
+                        : attn_bwd_small_kernel<SIM, POS, 8, 4>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    fn<<<grid, WAVES * 64, lds, s>>>(p, a, L);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_bwd_small_supported(const AttnParams& p)
+{
+    const Geometry& g = p.g;
+    const int SR = (g.M + 7) / 8 * 8;
+    return p.dtype == SWIN_DT_BF16 && p.pos != SWIN_POS_ROPE2D && g.d == D && g.M * SR <= 256 &&
+           (int64_t)g.H * g.W * g.C * 2 < ((int64_t)1 << 31) && (int64_t)g.W * g.C * 2 < ((int64_t)1 << 24);
+}
+
+hipError_t launch_attn_bwd_small(const AttnParams& p, const void* out, const void* dout, void* dq, void* dk,
+                                 void* dv, float* dtau, float* dtable, hipStream_t stream)
+{
+    const Geometry& g = p.g;
+    if (g.nwin == 0) return hipSuccess;
+    BwdSmallArgs a{out, dout, dq, dk, dv, dtau, dtable};
+    BwdLayout L;
+    L.NSP = g.M * ((g.M + 7) / 8 * 8);
+    L.NQT = (g.N + 15) / 16;
+    L.inv_M = 1.0f / (float)g.M;
+    const int nch_real = (L.NSP + 31) / 32;
+    const int nch = nch_real <= 2 ? 2 : nch_real <= 6 ? 6 : 8;
+    const int wh = nch <= 2 ? WAVES : 1;
+    const int S = 2 * g.M - 1;
+    const int64_t wgs = (int64_t)g.heads * ((g.nwin + wh - 1) / wh);
+    if (wgs > INT32_MAX - 8) return hipErrorInvalidValue;
+    L.wgs = (int)wgs;
+    L.P = (int)((wgs + 7) / 8);
+    const int64_t grid = 8 * (int64_t)L.P;
+    const int ns = nch * 32;
+    size_t lds = (size_t)(16 + wh * 4 * ns) * sizeof(float) + (size_t)wh * 4 * ns * D * 2;
+    if (p.pos == SWIN_POS_TABLE) lds += (size_t)2 * ((S * S + 8 + 3) / 4 * 4) * sizeof(float);
+    if (p.sim == SWIN_SIM_COSINE) {
+        if (p.pos == SWIN_POS_TABLE) return launch_nch<SWIN_SIM_COSINE, SWIN_POS_TABLE>(p, a, L, nch, (int)grid, lds, stream);
+        return launch_nch<SWIN_SIM_COSINE, SWIN_POS_NONE>(p, a, L, nch, (int)grid, lds, stream);
+    }
+    if (p.pos == SWIN_POS_TABLE) return launch_nch<SWIN_SIM_DOT, SWIN_POS_TABLE>(p, a, L, nch, (int)grid, lds, stream);
+    return launch_nch<SWIN_SIM_DOT, SWIN_POS_NONE>(p, a, L, nch, (int)grid, lds, stream);
+}
+
+}  // namespace swin

@@ -36,6 +36,13 @@ bool attn_bwd_supported(const AttnParams& p);
 hipError_t launch_attn_bwd(const AttnParams& p, const void* out, const void* dout, void* dq, void* dk, void* dv,
                            float* dtau, float* dtable, hipStream_t stream);
 
+// Backward on the matrix cores for bf16 windows of at most 256 key slots
+// without rotary positions (called by launch_attn_bwd after it zeroes dtau
+// and dtable).
+bool attn_bwd_small_supported(const AttnParams& p);
+hipError_t launch_attn_bwd_small(const AttnParams& p, const void* out, const void* dout, void* dq, void* dk,
+                                 void* dv, float* dtau, float* dtable, hipStream_t stream);
+
 // fp32 (and any-shape fallback) attention on the vector ALUs.
 hipError_t launch_attn_valu(const AttnParams& p, hipStream_t stream);
 

@@ -126,10 +126,29 @@ cpb_table_bwd_kernel(int M, int heads, int hidden, const float* __restrict__ w1,
                      const float* __restrict__ dtable, int mode, float norm_scale, float* __restrict__ dw1,
                      float* __restrict__ db1, float* __restrict__ dw2, float* __restrict__ db2)
 {
+    __shared__ float sdg[BR * HB];                 // dg of this block's rows and heads
+    __shared__ float sfx[BR], sfy[BR];             // G's inputs for those rows
     const int u = blockIdx.x * 256 + threadIdx.x;
     const int S = 2 * M - 1;
     const int row0 = blockIdx.y * BR, row1 = min(row0 + BR, S * S);
     const int o0 = blockIdx.z * HB;
+    // dg = dtable (times dT/dG for SIGMOID16) for the block, all loads at once
+    for (int i = threadIdx.x; i < BR * HB; i += 256) {
+        const int row = row0 + i / HB, o = o0 + i % HB;
+        float dg = 0.0f;
+        if (row < row1 && o < heads) {
+            const size_t at = (size_t)row * heads + o;
+            dg = dtable[at];
+            if (mode & SWIN_CPB_SIGMOID16) { const float t = table[at]; dg *= t * (1.0f - t * (1.0f / 16.0f)); }
+        }
+        sdg[i] = dg;
+    }
+    if (threadIdx.x < BR) {
+        const int row = min(row0 + (int)threadIdx.x, S * S - 1);
+        sfx[threadIdx.x] = cpb_input(row % S - (M - 1), mode, norm_scale);
+        sfy[threadIdx.x] = cpb_input(row / S - (M - 1), mode, norm_scale);
+    }
+    __syncthreads();
     const bool unit = u < hidden;
     float w1x = 0.0f, w1y = 0.0f, bb = 0.0f, w2c[HB];
 #pragma unroll
@@ -141,17 +160,13 @@ cpb_table_bwd_kernel(int M, int heads, int hidden, const float* __restrict__ w1,
     // db2 of head o0 + threadIdx.x, in the first unit block
     const bool own_b2 = blockIdx.x == 0 && threadIdx.x < HB && o0 + threadIdx.x < heads;
     for (int row = row0; row < row1; ++row) {
-        const float fx = cpb_input(row % S - (M - 1), mode, norm_scale);
-        const float fy = cpb_input(row / S - (M - 1), mode, norm_scale);
+        const float fx = sfx[row - row0], fy = sfy[row - row0];
         const float a = fmaf(w1x, fx, fmaf(w1y, fy, bb));
         const float hid = fmaxf(a, 0.0f);
         float dh = 0.0f;
 #pragma unroll
         for (int o = 0; o < HB; ++o) {
-            if (o0 + o >= heads) break;
-            const size_t at = (size_t)row * heads + o0 + o;
-            float dg = dtable[at];
-            if (mode & SWIN_CPB_SIGMOID16) { const float t = table[at]; dg *= t * (1.0f - t * (1.0f / 16.0f)); }
+            const float dg = sdg[(row - row0) * HB + o];     // zero past the last head
             gw2[o] = fmaf(dg, hid, gw2[o]);
             dh = fmaf(w2c[o], dg, dh);
             if (own_b2 && o == (int)threadIdx.x) gb2 += dg;

@@ -397,6 +397,8 @@ hipError_t launch_attn_bwd(const AttnParams& p, const void* out, const void* dou
     if (g.nwin == 0) return hipSuccess;
     if (attn_bwd_small_supported(p))
         return launch_attn_bwd_small(p, out, dout, dq, dk, dv, a.dtau, a.dtable, stream);
+    if (attn_bwd_large_supported(p))
+        return launch_attn_bwd_large(p, out, dout, dq, dk, dv, a.dtau, a.dtable, stream);
     size_t lds = (size_t)(2 * BLK * D + 3 * g.N + TPB / 64) * sizeof(float);
     if (p.pos == SWIN_POS_TABLE) lds += (size_t)2 * S * S * sizeof(float);
     if (p.pos == SWIN_POS_ROPE2D) lds += (size_t)g.M * D * sizeof(float);

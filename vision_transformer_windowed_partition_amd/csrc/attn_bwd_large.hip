@@ -1,0 +1,563 @@
+// Backward of window attention on the gfx950 matrix cores for bf16 windows
+// too large for the small-window backward: up to 32 x 32 tokens, with the
+// rotary variant for DOT (FlashSwin abstract) and the bias table of the
+// SwinV2 card (eq. 3-4).
+//
+// Same gradient as the small-window backward (SwinV2 card eq. 1-2; with
+// logit_ij = (q~_i . k~_j) a_i c_j + b_ij, q~, k~ the rotated operands):
+//   dl_ij = p_ij (dout_i . v_j - D_i),  dv_j = sum_i p_ij dout_i,
+//   G_i = sum_j dl_ij c_j k~_j,  H_j = sum_i dl_ij a_i q~_i,
+//   COSINE: dq_i = a_i (G_i - q_i (q_i . G_i)/||q_i||^2), dk likewise with c_j;
+//   DOT:    dq~ = G / sqrt(d) ... folded: a = c = 1/sqrt(d); ROPE2D: dq = R^T dq~.
+//   dtable[offset(i, j)] += dl_ij, dtau from sum dl_ij cos_ij.
+// One workgroup of eight wavefronts per window-head, in two stages of LDS:
+//   stage 1: K~ and V rows of every key slot (64-byte rows, XOR-swizzled
+//     16-byte pieces), K rotated in fp32 and rounded once; per-slot scales
+//     and D_i = dout_i . out_i.  Query-major passes over each wavefront's
+//     query tiles (16 tokens; q~ and dout fragments straight from memory):
+//     0: log-sum-exp per query; B: dP^T = V dout^T, dl, G^T += K~^T (dl c)^T
+//     with K~^T read transposed; dq, dtau and the bias gradient.
+//   stage 2: Q~ and dout rows replace them; key-major pass A over 16-key
+//     tiles (k~, v fragments from memory): S = Q~ K~^T and dP = dout V^T with
+//     permuted query rows, then dV^T += dout^T P and H^T += Q~^T (dl a).
+// Rounding: for COSINE the operands are raw bf16 (exact) and the scales
+// multiply in fp32; rotated DOT operands are rounded to bf16 once, as in the
+// forward.  All products are v_mfma_f32_16x16x32_bf16, fp32 accumulation.
+#include "common.hpp"
+#include "lanes.hpp"
+#include "launch.hpp"
+#include "tile_io.hpp"
+
+namespace swin {
+
+namespace {
+
+using namespace tio;
+using namespace lanes;
+
+constexpr int WAVES = 8;
+constexpr int NTHR = WAVES * 64;
+
+struct LargeBwdLayout {
+    int SR;                    // slots per key row: M rounded up to 8
+    int GPR;                   // 8-slot groups per row
+    int NS;                    // slots, padded to a multiple of 32
+    int NQT;                   // query tiles of 16 tokens
+    int units;                 // window-heads
+    int P;                     // work ids per XCD slot
+    float inv_M, inv_SR, inv_GPR;
+};
+
+struct BwdLargeArgs {
+    const void* out;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dtau;
+    float* dtable;
+};
+
+__device__ __forceinline__ bf16x8 rowfrag(const __bf16* rows, int s, int piece)
+{
+    return *(const bf16x8*)(rows + s * D + ((piece ^ v_swizzle(s)) * 8));
+}
+__device__ __forceinline__ void rowstore(__bf16* rows, int s, int piece, const bf16x8& v)
+{
+    *(bf16x8*)(rows + s * D + ((piece ^ v_swizzle(s)) * 8)) = v;
+}
+
+__device__ __forceinline__ float quad_sum(float x)
+{
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));
+    return x;
+}
+
+// DPP row shifts within 16-lane rows (source outside the row reads zero)
+template <int N>
+__device__ __forceinline__ float row_shl(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + N, 0xf, 0xf, true));
+}
+template <int N>
+__device__ __forceinline__ float row_shr(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
+}
+
+__device__ __forceinline__ bf16x4 load8b(Rsrc r, uint32_t off)
+{
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+template <int SIM, int POS>
+__global__ void __launch_bounds__(NTHR)
+attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
+{
+    extern __shared__ __attribute__((aligned(16))) float smem_f[];
+    const Geometry& g = p.g;
+    const int M = g.M, N = g.N, S = 2 * M - 1, SR = L.SR, NS = L.NS;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = lane >> 4, li = lane & 15;
+
+    const int work = (blockIdx.x & 7) * L.P + (blockIdx.x >> 3);
+    if (work >= L.units) return;
+    const int win = work / g.heads;
+    const int h = work - win * g.heads;
+
+    const int tabsz = POS == SWIN_POS_TABLE ? (S * S + 8 + 3) / 4 * 4 : 0;
+    __bf16* rowA = (__bf16*)smem_f;                            // [NS][D] K~, later Q~
+    __bf16* rowB = rowA + NS * D;                              // [NS][D] V, later dout
+    float* ksc = (float*)(rowB + NS * D);                      // [NS] c_j
+    float* qsc = ksc + NS;                                     // [NS] log2(e) a_i
+    float* lse = qsc + NS;                                     // [NS]
+    float* dd = lse + NS;                                      // [NS] D_i
+    float* bias2 = dd + NS;                                    // [tabsz] reversed, log2 units
+    float* dtab = bias2 + tabsz;                               // [tabsz] reversed, natural units
+    float* rtab = dtab + tabsz;                                // [M][2][8] (cos, sin)  (ROPE2D)
+    float* red = rtab + (POS == SWIN_POS_ROPE2D ? M * 32 : 0); // [WAVES]
+
+    const WinPlace wp = place_window(g, win);
+    const WinGeo& wg = wp.wg;
+    const uint32_t bytes = (uint32_t)(wp.span - h * D) * 2u;
+    const int64_t off0 = wp.base + h * D;
+    const Rsrc qr = make_rsrc((const uint16_t*)p.q + off0, bytes);
+    const Rsrc kr = make_rsrc((const uint16_t*)p.k + off0, bytes);
+    const Rsrc vr = make_rsrc((const uint16_t*)p.v + off0, bytes);
+    const Rsrc gr = make_rsrc((const uint16_t*)a.dout + off0, bytes);
+    const Rsrc orr = make_rsrc((const uint16_t*)a.out + off0, bytes);
+    float tau = 1.0f;
+    if (SIM == SWIN_SIM_COSINE) tau = fmaxf(p.tau[h], p.tau_min);
+    const float inv_tau = 1.0f / tau;
+    const bool needs_mask = wp.last_r || wp.last_c || SR != M || NS != M * SR;
+    const int negrow = S * S;
+    constexpr float RS32 = 0.17677669529663687f;              // 1/sqrt(32)
+
+    // rotate 8 channels 8 pc..8 pc+7 of a token at (r, c) by sgn * angle:
+    // channels [0, 16) turn with the row, [16, 32) with the column
+    auto rot8 = [&](float* f, int pc, int r, int c, float sgn) {
+        const int half = pc >> 1, pos = half ? c : r;
+        const float* cs = rtab + ((pos * 2 + half) * 8 + (pc & 1) * 4) * 2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float co = cs[2 * e], si = sgn * cs[2 * e + 1];
+            const float x0 = f[2 * e], x1 = f[2 * e + 1];
+            f[2 * e] = x0 * co - x1 * si;
+            f[2 * e + 1] = x0 * si + x1 * co;
+        }
+    };
+    // inverse rotation of a lane's gradient channels 4 grp..+3 (half 0) and
+    // 16 + 4 grp..+3 (half 1): pairs k = 2 grp + m
+    auto unrot_lane = [&](float* g8, int r, int c) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int pos = hh ? c : r;
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int k = 2 * grp + m;
+                const float co = rtab[((pos * 2 + hh) * 8 + k) * 2], si = -rtab[((pos * 2 + hh) * 8 + k) * 2 + 1];
+                const float x0 = g8[4 * hh + 2 * m], x1 = g8[4 * hh + 2 * m + 1];
+                g8[4 * hh + 2 * m] = x0 * co - x1 * si;
+                g8[4 * hh + 2 * m + 1] = x0 * si + x1 * co;
+            }
+        }
+    };
+
+    // ---- tables
+    if (POS == SWIN_POS_TABLE) {
+        for (int i = tid; i < S * S; i += NTHR) {
+            bias2[S * S - 1 - i] = p.table[(size_t)i * g.heads + h] * kLog2e;
+            dtab[i] = 0.0f;
+        }
+        if (tid < 8) bias2[S * S + tid] = -INFINITY;
+    }
+    if (POS == SWIN_POS_ROPE2D) {
+        for (int i = tid; i < M * 16; i += NTHR) {
+            const int k = i & 7, half = (i >> 3) & 1, pos = i >> 4;
+            const float th = p.rope_freqs ? p.rope_freqs[((size_t)h * 2 + half) * 8 + k]
+                                          : exp2f(-(float)k * 0.125f * log2f(p.rope_base));
+            float s_, c_;
+            sincosf((float)pos * th, &s_, &c_);
+            rtab[i * 2] = c_;
+            rtab[i * 2 + 1] = s_;
+        }
+    }
+    __syncthreads();
+
+    // ---- stage a tensor's rows (rotated when `rot`) for every slot; four
+    // threads per slot, one 16-byte piece each.  Returns nothing; sq receives
+    // the squared norm of the slot (same in all four threads).
+    auto slot_of = [&](int s, int& r, int& c) { r = qdiv(s, L.inv_SR); c = s - r * SR; };
+    auto stage_rows = [&](Rsrc src, __bf16* dst, bool rot, float* norm_out, bool cosine_scale, Rsrc src2,
+                          __bf16* dst2) {
+#pragma unroll 4
+        for (int i0 = 0; i0 < NS * 4; i0 += NTHR) {
+            const int i = i0 + tid;
+            const int s = i >> 2, pc = i & 3;
+            const bool in = s < NS;
+            int r, c;
+            slot_of(in ? s : 0, r, c);
+            const bool ok = in && r < M && c < M;
+            const uint32_t off = masked(wg.tok(r, c) + 16u * pc, ok);
+            const u32x4 x = load16(src, off);
+            const u32x4 x2 = load16(src2, off);
+            float f[8];
+            unpack_bf16x8(x, f);
+            if (POS == SWIN_POS_ROPE2D && rot) rot8(f, pc, min(r, M - 1), min(c, M - 1), 1.0f);
+            float ss = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+            ss = quad_sum(ss);
+            if (in) {
+                rowstore(dst, s, pc, (POS == SWIN_POS_ROPE2D && rot) ? pack_bf16x8(f) : __builtin_bit_cast(bf16x8, x));
+                rowstore(dst2, s, pc, __builtin_bit_cast(bf16x8, x2));
+                if (norm_out && pc == 0)
+                    norm_out[s] = cosine_scale ? 1.0f / fmaxf(sqrtf(ss), 1e-12f) : 1.0f;
+            }
+        }
+    };
+
+    // ---- stage 1: K~ and V rows, c_j; a_i and D_i
+    stage_rows(kr, rowA, true, ksc, SIM == SWIN_SIM_COSINE, vr, rowB);
+#pragma unroll 4
+    for (int i0 = 0; i0 < NS * 4; i0 += NTHR) {
+        const int i = i0 + tid;
+        const int s = i >> 2, pc = i & 3;
+        const bool in = s < NS;
+        int r, c;
+        slot_of(in ? s : 0, r, c);
+        const bool ok = in && r < M && c < M;
+        const uint32_t off = masked(wg.tok(r, c) + 16u * pc, ok);
+        float qf[8], gf[8], of[8];
+        unpack_bf16x8(load16(qr, off), qf);
+        unpack_bf16x8(load16(gr, off), gf);
+        unpack_bf16x8(load16(orr, off), of);
+        float qq = 0.0f, go = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { qq = fmaf(qf[e], qf[e], qq); go = fmaf(gf[e], of[e], go); }
+        qq = quad_sum(qq);
+        go = quad_sum(go);
+        if (in && pc == 0) {
+            qsc[s] = SIM == SWIN_SIM_COSINE ? kLog2e * inv_tau / fmaxf(sqrtf(qq), 1e-12f) : kLog2e * RS32;
+            dd[s] = go;
+        }
+    }
+    __syncthreads();
+
+    const int nch = NS / 32;
+    float dtau_acc = 0.0f;
+    const Rsrc dqr = make_rsrc((const uint16_t*)a.dq + off0, bytes);
+    const Rsrc dkr = make_rsrc((const uint16_t*)a.dk + off0, bytes);
+    const Rsrc dvr = make_rsrc((const uint16_t*)a.dv + off0, bytes);
+
+    // ---- passes 0 and B over this wave's query tiles
+    const bool diag8 = (M & 7) == 0;
+    for (int t0 = wave; t0 < L.NQT; t0 += WAVES) {
+        const int t = t0 * 16 + li;
+        const bool tv = t < N;
+        const int tt = tv ? t : 0;
+        const int ri = qdiv(tt, L.inv_M), ci = tt - ri * M;
+        const int qs_slot = ri * SR + ci;
+        const uint32_t qoffb = masked(wg.tok(ri, ci) + 16u * grp, tv);
+        float qv[8];
+        unpack_bf16x8(load16(qr, qoffb), qv);
+        if (POS == SWIN_POS_ROPE2D) rot8(qv, grp, ri, ci, 1.0f);
+        const bf16x8 qf = pack_bf16x8(qv);
+        const bf16x8 gfr = __builtin_bit_cast(bf16x8, load16(gr, qoffb));
+        const float qs = qsc[qs_slot], Dq = dd[qs_slot];
+        const int qoff = (M - 1 - ri) * S + (M - 1 - ci);
+        int rlo = 0, rhi = M, clo = 0, chi = M;
+        if (wp.last_r) { if (ri < M - g.shift) rhi = M - g.shift; else rlo = M - g.shift; }
+        if (wp.last_c) { if (ci < M - g.shift) chi = M - g.shift; else clo = M - g.shift; }
+
+        // pass 0: running maximum and sum
+        float m = -INFINITY, l = 0.0f;
+        for (int c = 0; c < nch; ++c) {
+            const int sA = 32 * c + 8 * (li >> 2) + (li & 3);
+            const bf16x8 ka = rowfrag(rowA, sA, grp), kb = rowfrag(rowA, sA + 4, grp);
+            const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+            const f32x4 sa = mfma(ka, qf, z), sb = mfma(kb, qf, z);
+            const f32x4 k0 = *(const f32x4*)(ksc + 32 * c + 8 * grp);
+            const f32x4 k1 = *(const f32x4*)(ksc + 32 * c + 8 * grp + 4);
+            const int gam = 4 * c + grp, rj = qdiv(gam, L.inv_GPR), cj0 = 8 * (gam - rj * L.GPR);
+            const int boff = qoff + rj * S + cj0;
+            float x[8], cm = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float sv = e < 4 ? sa[e] : sb[e - 4];
+                const float kv = e < 4 ? k0[e] : k1[e - 4];
+                const int cj = cj0 + e;
+                const bool ok = !needs_mask || (tv && rj >= rlo && rj < rhi && cj >= clo && cj < chi && rj < M && cj < M);
+                float b = 0.0f;
+                if (POS == SWIN_POS_TABLE) b = bias2[ok ? boff + e : negrow];
+                x[e] = ok ? fmaf(sv * qs, kv, b) : -INFINITY;
+                cm = fmaxf(cm, x[e]);
+            }
+            cm = max_x32(max_x16(cm));
+            const float mn = fmaxf(m, cm);
+            const float mref = mn == -INFINITY ? 0.0f : mn;
+            float ls = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ls += __builtin_amdgcn_exp2f(x[e] - mref);
+            l = l * __builtin_amdgcn_exp2f(m - mref) + ls;
+            m = mn;
+        }
+        l = sum_x32(sum_x16(l));
+        const float lq = m + __builtin_amdgcn_logf(l);
+        if (grp == 0 && tv) lse[qs_slot] = lq;
+
+        // pass B: dq
+        f32x4 G0 = {0.0f, 0.0f, 0.0f, 0.0f}, G1 = G0;
+        for (int c = 0; c < nch; ++c) {
+            const int sA = 32 * c + 8 * (li >> 2) + (li & 3);
+            const bf16x8 ka = rowfrag(rowA, sA, grp), kb = rowfrag(rowA, sA + 4, grp);
+            const bf16x8 va = rowfrag(rowB, sA, grp), vb = rowfrag(rowB, sA + 4, grp);
+            const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+            const f32x4 sa = mfma(ka, qf, z), sb = mfma(kb, qf, z);
+            const f32x4 pa = mfma(va, gfr, z), pb = mfma(vb, gfr, z);
+            const f32x4 k0 = *(const f32x4*)(ksc + 32 * c + 8 * grp);
+            const f32x4 k1 = *(const f32x4*)(ksc + 32 * c + 8 * grp + 4);
+            const int gam = 4 * c + grp, rj = qdiv(gam, L.inv_GPR), cj0 = 8 * (gam - rj * L.GPR);
+            const int boff = qoff + rj * S + cj0;
+            float ds[8], dlv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float sv = e < 4 ? sa[e] : sb[e - 4];
+                const float dpv = e < 4 ? pa[e] : pb[e - 4];
+                const float kv = e < 4 ? k0[e] : k1[e - 4];
+                const int cj = cj0 + e;
+                const bool ok = tv && (!needs_mask || (rj >= rlo && rj < rhi && cj >= clo && cj < chi && rj < M && cj < M));
+                float b = 0.0f;
+                if (POS == SWIN_POS_TABLE) b = bias2[ok ? boff + e : negrow];
+                const float xs = sv * qs * kv;
+                const float pr = ok ? __builtin_amdgcn_exp2f(xs + b - lq) : 0.0f;
+                const float dl = pr * (dpv - Dq);
+                ds[e] = dl * (SIM == SWIN_SIM_COSINE ? kv : RS32);
+                dlv[e] = dl;
+                if (SIM == SWIN_SIM_COSINE) dtau_acc = fmaf(dl, xs, dtau_acc);
+                if (POS == SWIN_POS_TABLE && a.dtable && !diag8 && ok) atomicAdd(&dtab[boff + e], dl);
+            }
+            if (POS == SWIN_POS_TABLE && a.dtable && diag8) {
+                // M a multiple of 8: each 8-lane half of the tile is 8
+                // consecutive columns of one window row, so (lane, element e)
+                // lands at boff(lane) + e with boff falling by one per lane.
+                // Sums along those diagonals inside each half: lane j = li % 8
+                // gathers d = -j from lanes j + k (element k) and, for j >= 1,
+                // d = 8 - j from lanes j - 8 + e; terms from the other half are
+                // dropped.  Masked pairs carry dl = 0.
+                // (every lane evaluates every row shift, so that no shift is
+                // made conditional: a lane left out would read as zero)
+                const int j = li & 7;
+                const float a1 = row_shl<1>(dlv[1]), a2 = row_shl<2>(dlv[2]), a3 = row_shl<3>(dlv[3]),
+                            a4 = row_shl<4>(dlv[4]), a5 = row_shl<5>(dlv[5]), a6 = row_shl<6>(dlv[6]),
+                            a7 = row_shl<7>(dlv[7]);
+                const float b1 = row_shr<7>(dlv[1]), b2 = row_shr<6>(dlv[2]), b3 = row_shr<5>(dlv[3]),
+                            b4 = row_shr<4>(dlv[4]), b5 = row_shr<3>(dlv[5]), b6 = row_shr<2>(dlv[6]),
+                            b7 = row_shr<1>(dlv[7]);
+                const float A = dlv[0] + (j <= 6 ? a1 : 0.0f) + (j <= 5 ? a2 : 0.0f) + (j <= 4 ? a3 : 0.0f) +
+                                (j <= 3 ? a4 : 0.0f) + (j <= 2 ? a5 : 0.0f) + (j <= 1 ? a6 : 0.0f) +
+                                (j == 0 ? a7 : 0.0f);
+                const float B = (j >= 7 ? b1 : 0.0f) + (j >= 6 ? b2 : 0.0f) + (j >= 5 ? b3 : 0.0f) +
+                                (j >= 4 ? b4 : 0.0f) + (j >= 3 ? b5 : 0.0f) + (j >= 2 ? b6 : 0.0f) +
+                                (j >= 1 ? b7 : 0.0f);
+                if (tv) atomicAdd(&dtab[boff], A);
+                if (tv && j >= 1) atomicAdd(&dtab[boff + 8], B);
+            }
+            const bf16x8 dsb = pack_bf16x8(ds);
+            G0 = mfma(vt_frag(rowA, c, 0, grp, li), dsb, G0);
+            G1 = mfma(vt_frag(rowA, c, 1, grp, li), dsb, G1);
+        }
+        float g8[8] = {G0[0], G0[1], G0[2], G0[3], G1[0], G1[1], G1[2], G1[3]};
+        const uint32_t o8 = masked(wg.tok(ri, ci) + 8u * grp, tv);
+        if (SIM == SWIN_SIM_COSINE) {
+            const bf16x4 qa4 = load8b(qr, o8), qb4 = load8b(qr, o8 + 32u);
+            float q8[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { q8[e] = (float)qa4[e]; q8[e + 4] = (float)qb4[e]; }
+            float qg = 0.0f, qq = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { qg = fmaf(q8[e], g8[e], qg); qq = fmaf(q8[e], q8[e], qq); }
+            qg = sum_x32(sum_x16(qg));
+            qq = sum_x32(sum_x16(qq));
+            const float nq = sqrtf(qq);
+            const float ai = inv_tau / fmaxf(nq, 1e-12f);
+            const float pj = nq > 1e-12f ? qg / qq : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) g8[e] = ai * (g8[e] - q8[e] * pj);
+        }
+        if (POS == SWIN_POS_ROPE2D) unrot_lane(g8, ri, ci);
+        store8(dqr, o8, pack_bf16x4(g8[0], g8[1], g8[2], g8[3]));
+        store8(dqr, o8 + 32u, pack_bf16x4(g8[4], g8[5], g8[6], g8[7]));
+    }
+    __syncthreads();
+
+    // ---- stage 2: Q~ and dout rows
+    stage_rows(qr, rowA, true, nullptr, false, gr, rowB);
+    __syncthreads();
+
+    // ---- pass A: dk, dv over this wave's 16-key tiles
+    const int nkt = NS / 16;
+    for (int kt = wave; kt < nkt; kt += WAVES) {
+        const int sk = 16 * kt + li;
+        int rj, cj;
+        slot_of(sk, rj, cj);
+        const bool kv_ok = rj < M && cj < M;
+        const int rjc = min(rj, M - 1), cjc = min(cj, M - 1);
+        const uint32_t koffb = masked(wg.tok(rjc, cjc) + 16u * grp, kv_ok);
+        float kvv[8];
+        unpack_bf16x8(load16(kr, koffb), kvv);
+        if (POS == SWIN_POS_ROPE2D) rot8(kvv, grp, rjc, cjc, 1.0f);
+        const bf16x8 kB = pack_bf16x8(kvv);
+        const bf16x8 vB = __builtin_bit_cast(bf16x8, load16(vr, koffb));
+        const float cj_s = ksc[sk];
+        int rlo = 0, rhi = M, clo = 0, chi = M;
+        if (wp.last_r) { if (rj < M - g.shift) rhi = M - g.shift; else rlo = M - g.shift; }
+        if (wp.last_c) { if (cj < M - g.shift) chi = M - g.shift; else clo = M - g.shift; }
+        const uint32_t cmask = ((chi >= 32 ? 0xffffffffu : ((1u << chi) - 1u)) & ~((1u << clo) - 1u)) &
+                               (M >= 32 ? 0xffffffffu : ((1u << M) - 1u));
+        f32x4 V0 = {0.0f, 0.0f, 0.0f, 0.0f}, V1 = V0, H0 = V0, H1 = V0;
+        for (int c = 0; c < nch; ++c) {
+            const int sA = 32 * c + 8 * (li >> 2) + (li & 3);
+            const bf16x8 qa = rowfrag(rowA, sA, grp), qb = rowfrag(rowA, sA + 4, grp);
+            const bf16x8 ga = rowfrag(rowB, sA, grp), gb = rowfrag(rowB, sA + 4, grp);
+            const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+            const f32x4 sa = mfma(qa, kB, z), sb = mfma(qb, kB, z);
+            const f32x4 pa = mfma(ga, vB, z), pb = mfma(gb, vB, z);
+            const int qs0 = 32 * c + 8 * grp;
+            const f32x4 qsA = *(const f32x4*)(qsc + qs0), qsB = *(const f32x4*)(qsc + qs0 + 4);
+            const f32x4 lA = *(const f32x4*)(lse + qs0), lB = *(const f32x4*)(lse + qs0 + 4);
+            const f32x4 dA = *(const f32x4*)(dd + qs0), dB = *(const f32x4*)(dd + qs0 + 4);
+            const int gam = 4 * c + grp, ri = qdiv(gam, L.inv_GPR), ci0 = 8 * (gam - ri * L.GPR);
+            const int rev0 = S * S - 1 - ((ri - rj + M - 1) * S + (ci0 - cj + M - 1));
+            const bool rok = kv_ok && ri < M && ri >= rlo && ri < rhi;
+            const uint32_t cbits = rok ? (cmask >> ci0) & 0xffu : 0u;
+            float pp[8], dsa[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float sv = e < 4 ? sa[e] : sb[e - 4];
+                const float dpv = e < 4 ? pa[e] : pb[e - 4];
+                const float qv_ = e < 4 ? qsA[e] : qsB[e - 4];
+                const float lv = e < 4 ? lA[e] : lB[e - 4];
+                const float dv_ = e < 4 ? dA[e] : dB[e - 4];
+                const bool ok = ((cbits >> e) & 1u) != 0u;
+                float b = 0.0f;
+                if (POS == SWIN_POS_TABLE) b = bias2[ok ? rev0 - e : negrow];
+                const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(sv * qv_, cj_s, b) - lv) : 0.0f;
+                pp[e] = pr;
+                const float dl = pr * (dpv - dv_);
+                dsa[e] = dl * (SIM == SWIN_SIM_COSINE ? qv_ * (1.0f / kLog2e) : RS32);
+            }
+            const bf16x8 pbf = pack_bf16x8(pp), dsb = pack_bf16x8(dsa);
+            V0 = mfma(vt_frag(rowB, c, 0, grp, li), pbf, V0);
+            V1 = mfma(vt_frag(rowB, c, 1, grp, li), pbf, V1);
+            H0 = mfma(vt_frag(rowA, c, 0, grp, li), dsb, H0);
+            H1 = mfma(vt_frag(rowA, c, 1, grp, li), dsb, H1);
+        }
+        float h8[8] = {H0[0], H0[1], H0[2], H0[3], H1[0], H1[1], H1[2], H1[3]};
+        const uint32_t o8 = masked(wg.tok(rjc, cjc) + 8u * grp, kv_ok);
+        if (SIM == SWIN_SIM_COSINE) {
+            const bf16x4 ka4 = load8b(kr, o8), kb4 = load8b(kr, o8 + 32u);
+            float k8[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { k8[e] = (float)ka4[e]; k8[e + 4] = (float)kb4[e]; }
+            float kh = 0.0f, kk = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { kh = fmaf(k8[e], h8[e], kh); kk = fmaf(k8[e], k8[e], kk); }
+            kh = sum_x32(sum_x16(kh));
+            kk = sum_x32(sum_x16(kk));
+            const float nk = sqrtf(kk);
+            const float pj = nk > 1e-12f ? kh / kk : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h8[e] = cj_s * (h8[e] - k8[e] * pj);
+        }
+        if (POS == SWIN_POS_ROPE2D) unrot_lane(h8, rjc, cjc);
+        store8(dkr, o8, pack_bf16x4(h8[0], h8[1], h8[2], h8[3]));
+        store8(dkr, o8 + 32u, pack_bf16x4(h8[4], h8[5], h8[6], h8[7]));
+        store8(dvr, o8, pack_bf16x4(V0[0], V0[1], V0[2], V0[3]));
+        store8(dvr, o8 + 32u, pack_bf16x4(V1[0], V1[1], V1[2], V1[3]));
+    }
+
+    // ---- this window-head's share of dtau and of the table gradient
+    if (SIM == SWIN_SIM_COSINE && a.dtau) {
+        const float s = wave_reduce<Op::Sum>(dtau_acc);
+        if (lane == 0) red[wave] = s;
+    }
+    __syncthreads();
+    if (SIM == SWIN_SIM_COSINE && a.dtau && tid == 0 && p.tau[h] > p.tau_min) {
+        float s = 0.0f;
+        for (int w = 0; w < WAVES; ++w) s += red[w];
+        unsafeAtomicAdd(&a.dtau[h], s * (-1.0f / (kLog2e * p.tau[h])));
+    }
+    if (POS == SWIN_POS_TABLE && a.dtable)
+        for (int i = tid; i < S * S; i += NTHR)
+            if (dtab[i] != 0.0f) unsafeAtomicAdd(&a.dtable[(size_t)(S * S - 1 - i) * g.heads + h], dtab[i]);
+}
+
+size_t lds_bytes(const AttnParams& p, int NS)
+{
+    const int S = 2 * p.g.M - 1;
+    size_t b = (size_t)NS * D * 2 * 2 + (size_t)4 * NS * 4 + (size_t)WAVES * 4 + 64;
+    if (p.pos == SWIN_POS_TABLE) b += (size_t)2 * ((S * S + 8 + 3) / 4 * 4) * 4;
+    if (p.pos == SWIN_POS_ROPE2D) b += (size_t)p.g.M * 32 * 4;
+    return b;
+}
+
+int slots_of(const AttnParams& p)
+{
+    const int SR = (p.g.M + 7) / 8 * 8;
+    return (p.g.M * SR + 31) / 32 * 32;
+}
+
+template <int SIM, int POS>
+hipError_t launch_large(const AttnParams& p, const BwdLargeArgs& a, const LargeBwdLayout& L, size_t lds,
+                        hipStream_t s)
+{
+    auto* fn = attn_bwd_large_kernel<SIM, POS>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    fn<<<8 * L.P, NTHR, lds, s>>>(p, a, L);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_bwd_large_supported(const AttnParams& p)
+{
+    const Geometry& g = p.g;
+    return p.dtype == SWIN_DT_BF16 && g.d == D && g.M <= 32 &&
+           !(p.sim == SWIN_SIM_COSINE && p.pos == SWIN_POS_ROPE2D) &&
+           lds_bytes(p, slots_of(p)) <= 160 * 1024 &&
+           (int64_t)g.H * g.W * g.C * 2 < ((int64_t)1 << 31) && (int64_t)g.W * g.C * 2 < ((int64_t)1 << 24);
+}
+
+hipError_t launch_attn_bwd_large(const AttnParams& p, const void* out, const void* dout, void* dq, void* dk,
+                                 void* dv, float* dtau, float* dtable, hipStream_t stream)
+{
+    const Geometry& g = p.g;
+    if (g.nwin == 0) return hipSuccess;
+    BwdLargeArgs a{out, dout, dq, dk, dv, dtau, dtable};
+    LargeBwdLayout L;
+    L.SR = (g.M + 7) / 8 * 8;
+    L.GPR = L.SR / 8;
+    L.NS = slots_of(p);
+    L.NQT = (g.N + 15) / 16;
+    L.units = g.nwin * g.heads;
+    L.P = (L.units + 7) / 8;
+    L.inv_M = 1.0f / (float)g.M;
+    L.inv_SR = 1.0f / (float)L.SR;
+    L.inv_GPR = 1.0f / (float)L.GPR;
+    const size_t lds = lds_bytes(p, L.NS);
+    if (p.sim == SWIN_SIM_COSINE) {
+        if (p.pos == SWIN_POS_TABLE) return launch_large<SWIN_SIM_COSINE, SWIN_POS_TABLE>(p, a, L, lds, stream);
+        return launch_large<SWIN_SIM_COSINE, SWIN_POS_NONE>(p, a, L, lds, stream);
+    }
+    if (p.pos == SWIN_POS_TABLE) return launch_large<SWIN_SIM_DOT, SWIN_POS_TABLE>(p, a, L, lds, stream);
+    if (p.pos == SWIN_POS_ROPE2D) return launch_large<SWIN_SIM_DOT, SWIN_POS_ROPE2D>(p, a, L, lds, stream);
+    return launch_large<SWIN_SIM_DOT, SWIN_POS_NONE>(p, a, L, lds, stream);
+}
+
+}  // namespace swin

@@ -36,9 +36,13 @@ bool attn_bwd_supported(const AttnParams& p);
 hipError_t launch_attn_bwd(const AttnParams& p, const void* out, const void* dout, void* dq, void* dk, void* dv,
                            float* dtau, float* dtable, hipStream_t stream);
 
-// Backward on the matrix cores for bf16 windows of at most 256 key slots
-// without rotary positions (called by launch_attn_bwd after it zeroes dtau
-// and dtable).
+// Backward on the matrix cores (called by launch_attn_bwd after it zeroes
+// dtau and dtable): bf16 windows of at most 256 key slots without rotary
+// positions (small), else bf16 windows up to M = 32 whose staging fits LDS,
+// rotary positions with DOT only (large).
+bool attn_bwd_large_supported(const AttnParams& p);
+hipError_t launch_attn_bwd_large(const AttnParams& p, const void* out, const void* dout, void* dq, void* dk,
+                                 void* dv, float* dtau, float* dtable, hipStream_t stream);
 bool attn_bwd_small_supported(const AttnParams& p);
 hipError_t launch_attn_bwd_small(const AttnParams& p, const void* out, const void* dout, void* dq, void* dk,
                                  void* dv, float* dtau, float* dtable, hipStream_t stream);

@@ -8,6 +8,7 @@
 #include <string>
 
 #include "launch.hpp"
+#include "launch_bwd.hpp"
 
 namespace {
 

@@ -26,6 +26,7 @@
 #include "common.hpp"
 #include "lanes.hpp"
 #include "launch.hpp"
+#include "launch_bwd.hpp"
 #include "tile_io.hpp"
 
 namespace swin {

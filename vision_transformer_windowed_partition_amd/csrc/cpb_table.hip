@@ -17,6 +17,7 @@
 #include "common.hpp"
 #include "lanes.hpp"
 #include "launch.hpp"
+#include "launch_bwd.hpp"
 
 namespace swin {
 

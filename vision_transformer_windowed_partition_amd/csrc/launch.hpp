@@ -27,25 +27,6 @@ hipError_t launch_window_copy(const void* src, void* dst, const Geometry& g, int
 
 hipError_t launch_cpb_table(int M, int norm_M, int heads, int hidden, const float* w1, const float* b1,
                             const float* w2, const float* b2, int mode, float* table, hipStream_t stream);
-hipError_t launch_cpb_table_bwd(int M, int norm_M, int heads, int hidden, const float* w1, const float* b1,
-                                const float* w2, const float* table, const float* dtable, int mode, float* dw1,
-                                float* db1, float* dw2, float* db2, hipStream_t stream);
-
-// Backward of the window attention (vector ALUs; d = 32, M <= 32).
-bool attn_bwd_supported(const AttnParams& p);
-hipError_t launch_attn_bwd(const AttnParams& p, const void* out, const void* dout, void* dq, void* dk, void* dv,
-                           float* dtau, float* dtable, hipStream_t stream);
-
-// Backward on the matrix cores (called by launch_attn_bwd after it zeroes
-// dtau and dtable): bf16 windows of at most 256 key slots without rotary
-// positions (small), else bf16 windows up to M = 32 whose staging fits LDS,
-// rotary positions with DOT only (large).
-bool attn_bwd_large_supported(const AttnParams& p);
-hipError_t launch_attn_bwd_large(const AttnParams& p, const void* out, const void* dout, void* dq, void* dk,
-                                 void* dv, float* dtau, float* dtable, hipStream_t stream);
-bool attn_bwd_small_supported(const AttnParams& p);
-hipError_t launch_attn_bwd_small(const AttnParams& p, const void* out, const void* dout, void* dq, void* dk,
-                                 void* dv, float* dtau, float* dtable, hipStream_t stream);
 
 // fp32 (and any-shape fallback) attention on the vector ALUs.
 hipError_t launch_attn_valu(const AttnParams& p, hipStream_t stream);
@@ -54,7 +35,7 @@ hipError_t launch_attn_valu(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_mfma(const AttnParams& p, hipStream_t stream);
 
 // bf16 attention for windows of at most 256 key slots without rotary
-// positions, keys and values held in registers.
+// positions, each window-head's keys and values staged once in LDS.
 bool attn_small_supported(const AttnParams& p);
 hipError_t launch_attn_small(const AttnParams& p, hipStream_t stream);
 

@@ -338,11 +338,23 @@ def bench_backward(args, wl, x, sets, nsets, par, table, desc, stream) -> int:
     alg_bytes = 2 * wl.bytes
     kern_s = kern_avg * 1e-3
     tflops = flops / kern_s / 1e12
-    roof = {"bound": "alu", "achieved": round(tflops, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tflops / FP32_PEAK_TFLOPS, 4), "traffic": None, "kernel": "attn_bwd_kernel",
-            "kernel_ms": round(kern_avg, 5), "kernel_ms_median": round(sorted(kern_ms)[len(kern_ms) // 2], 5),
-            "kernel_ms_min": round(min(kern_ms), 5), "alg_bytes_per_launch": alg_bytes,
-            "alg_flops_per_launch": flops}
+    kernel = binding.swin_window_attn_bwd_kernel(desc)
+    if kernel == "attn_bwd_kernel":      # fp32 vector ALUs
+        compute, peak_tf = "alu", FP32_PEAK_TFLOPS
+    else:                                # bf16 matrix cores
+        compute, peak_tf = "mfma", BF16_PEAK_TFLOPS
+    # the ceiling is whichever of HBM and the compute peak takes longer
+    if flops / alg_bytes < peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9):
+        gbs = alg_bytes / kern_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": compute, "achieved": round(tflops, 2), "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(tflops / peak_tf, 4)}
+    roof.update({"traffic": None, "kernel": kernel, "kernel_ms": round(kern_avg, 5),
+                 "kernel_ms_median": round(sorted(kern_ms)[len(kern_ms) // 2], 5),
+                 "kernel_ms_min": round(min(kern_ms), 5), "alg_bytes_per_launch": alg_bytes,
+                 "alg_flops_per_launch": flops})
     out = {
         "metric": "window-attn bwd tokens/s (dq, dk, dv, dtau, dtable + CPB meta-network gradients)",
         "value": round(wl.tokens / (wall / args.steps), 1),

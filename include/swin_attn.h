@@ -173,8 +173,13 @@ int swin_window_attn_fwd(const swin_attn_desc* desc, const void* q, const void* 
  * (2M-1)^2 x heads fp32 (POS_TABLE; NULL skips it): both written (sums over
  * the windows, accumulated with fp32 atomics, so the last bits depend on
  * order).  Requires d = 32 and M <= 32 (SWIN_EUNSUPPORTED otherwise).
- * Arithmetic: fp32 on the vector ALUs; bf16 gradients are rounded to
- * nearest even once at the end. */
+ * Arithmetic: SWIN_DT_F32 runs in fp32 on the vector ALUs.  SWIN_DT_BF16
+ * runs its contractions on bf16 matrix cores with fp32 accumulation: the
+ * stored bf16 inputs enter as they are, the softmax weights p and the score
+ * gradients dl (and rotated q, k under ROPE2D) are rounded to bf16 as
+ * operands, scales, softmax and sums stay fp32 (COSINE with ROPE2D runs the
+ * fp32 vector path instead).  bf16 gradients are rounded to nearest even
+ * once at the end. */
 int swin_window_attn_bwd(const swin_attn_desc* desc, const void* q, const void* k,
                          const void* v, const void* out, const void* dout, const float* tau,
                          const float* table, const float* rope_freqs, void* dq, void* dk,
@@ -208,6 +213,17 @@ int swin_cpb_table_bwd(int32_t M, int32_t norm_M, int32_t heads, int32_t hidden,
  * pass rope_freqs).  NULL if swin_window_attn_fwd would reject the
  * descriptor itself; swin_last_error() then says why.  Enqueues nothing. */
 const char* swin_window_attn_kernel(const swin_attn_desc* desc);
+
+/* Name of the kernel that swin_window_attn_bwd launches for desc (static
+ * storage), beside the fill kernel that clears dtau and dtable:
+ *   "attn_bwd_small_kernel" SWIN_DT_BF16, M * roundup8(M) <= 256 key slots,
+ *                           no rotary positions;
+ *   "attn_bwd_large_kernel" SWIN_DT_BF16, M <= 32 otherwise, except COSINE
+ *                           with ROPE2D;
+ *   "attn_bwd_kernel"       SWIN_DT_F32 and every other case.
+ * NULL if swin_window_attn_bwd would reject the descriptor itself (also
+ * d != 32 or M > 32); swin_last_error() then says why.  Enqueues nothing. */
+const char* swin_window_attn_bwd_kernel(const swin_attn_desc* desc);
 
 /* Text for a status code (static storage). */
 const char* swin_status_string(int status);

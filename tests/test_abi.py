@@ -35,6 +35,7 @@ def test_header_declares_the_boundary():
                                            "swin_window_attn_bwd", "swin_window_partition",
                                            "swin_window_reverse",
                                            "swin_window_attn_fwd", "swin_window_attn_kernel",
+                                           "swin_window_attn_bwd_kernel",
                                            "swin_status_string",
                                            "swin_last_error", "swin_version"])
 
@@ -163,6 +164,30 @@ def test_kernel_query_names_the_dispatch(L):
     assert L.swin_window_attn_kernel(ctypes.byref(_desc(shift=8))) is None
     assert "shift" in binding.swin_last_error()
     assert L.swin_window_attn_kernel(None) is None
+
+
+def test_backward_kernel_query_names_the_dispatch(L):
+    """The backward's dispatch: bf16 windows of at most 256 key slots without
+    rotary positions -> the small matrix-core kernel; other bf16 windows up to
+    M = 32 except cosine with rotary positions -> the large matrix-core
+    kernel; fp32 and the rest -> the vector-ALU kernel; d != 32 or M > 32 is
+    rejected."""
+    from vision_transformer_windowed_partition_amd import synth
+    want = ["attn_bwd_kernel", "attn_bwd_small_kernel", "attn_bwd_small_kernel", "attn_bwd_large_kernel",
+            "attn_bwd_large_kernel"]
+    for wl, name in zip(synth.WORKLOADS, want):
+        d = binding.make_desc(B=wl.B, H=wl.H, W=wl.W, C=wl.C, heads=wl.heads, M=wl.M, shift=wl.shift,
+                              partition=wl.partition, sim=wl.sim, pos=wl.pos,
+                              dtype=binding.DTYPE_BY_NAME[wl.dtype])
+        assert binding.swin_window_attn_bwd_kernel(d) == name, wl.name
+    assert binding.swin_window_attn_bwd_kernel(_desc(M=12, H=24, W=24)) == "attn_bwd_small_kernel"
+    assert binding.swin_window_attn_bwd_kernel(_desc(M=8, pos=2, sim=1)) == "attn_bwd_large_kernel"
+    assert binding.swin_window_attn_bwd_kernel(_desc(M=8, pos=2, sim=0)) == "attn_bwd_kernel"
+    assert binding.swin_window_attn_bwd_kernel(_desc(M=8, dtype=0)) == "attn_bwd_kernel"
+    assert L.swin_window_attn_bwd_kernel(ctypes.byref(_desc(M=48, H=48, W=48, shift=0))) is None
+    assert "M=48" in binding.swin_last_error()
+    assert L.swin_window_attn_bwd_kernel(ctypes.byref(_desc(C=128))) is None
+    assert L.swin_window_attn_bwd_kernel(None) is None
 
 
 def test_attn_empty_batch_is_a_no_op(L):

@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.swin_cpb_table_bwd.argtypes = [i32] * 4 + [vp] * 5 + [i32] + [vp] * 5
         L.swin_window_attn_kernel.restype = ctypes.c_char_p
         L.swin_window_attn_kernel.argtypes = [ctypes.POINTER(SwinAttnDesc)]
+        L.swin_window_attn_bwd_kernel.restype = ctypes.c_char_p
+        L.swin_window_attn_bwd_kernel.argtypes = [ctypes.POINTER(SwinAttnDesc)]
         L.swin_status_string.restype = ctypes.c_char_p
         L.swin_status_string.argtypes = [i32]
         L.swin_last_error.restype = ctypes.c_char_p
@@ -247,4 +249,13 @@ def swin_window_attn_kernel(desc: SwinAttnDesc) -> str:
     name = lib().swin_window_attn_kernel(ctypes.byref(desc))
     if name is None:
         raise SwinError(SWIN_EINVAL, swin_last_error())
+    return name.decode()
+
+
+def swin_window_attn_bwd_kernel(desc: SwinAttnDesc) -> str:
+    """Name of the kernel swin_window_attn_bwd launches for desc (for
+    matching profiler output).  Raises SwinError if the descriptor is rejected."""
+    name = lib().swin_window_attn_bwd_kernel(ctypes.byref(desc))
+    if name is None:
+        raise SwinError(SWIN_EUNSUPPORTED, swin_last_error())
     return name.decode()

@@ -308,4 +308,21 @@ const char* swin_window_attn_kernel(const swin_attn_desc* d)
     }
 }
 
+const char* swin_window_attn_bwd_kernel(const swin_attn_desc* d)
+{
+    if (check_desc(d, true) != SWIN_OK) return nullptr;
+    if (d->C != d->heads * 32) {
+        fail(SWIN_EUNSUPPORTED, "backward: head dim %d (32 only)", d->C / d->heads);
+        return nullptr;
+    }
+    if (d->M > 32) {
+        fail(SWIN_EUNSUPPORTED, "backward: M=%d (32 at most)", d->M);
+        return nullptr;
+    }
+    const swin::AttnParams p = params_of(d);
+    if (swin::attn_bwd_small_supported(p)) return "attn_bwd_small_kernel";
+    if (swin::attn_bwd_large_supported(p)) return "attn_bwd_large_kernel";
+    return "attn_bwd_kernel";
+}
+
 }  // extern "C"

@@ -19,7 +19,12 @@
 // wavefront then takes query tiles wave + 8j, two at a time, through every
 // key chunk: the score tile leaves the MFMA in the B-operand layout of P^T,
 // so the softmax runs in registers between the two products; row sums come
-// from a third MFMA against an all-ones operand.
+// from a third MFMA against an all-ones operand.  For COSINE (outside the
+// precise path below) and for DOT with rotation, the staged keys carry the
+// logit scale (log2(e)/tau, or log2(e)/sqrt(d)), COSINE queries enter
+// unit-normalised, and the bias term (table entry, or the constant shift)
+// starts the accumulator of S^T: each score then costs one exp2 and half a
+// pack, no FMA.
 //
 // Key slots.  Key (rj, cj) sits in slot rj*SR + cj, SR = M rounded up to 8,
 // so each lane's 8 slots share one key row.  Padded slots and keys of another
@@ -27,9 +32,10 @@
 // its bias from a row of -inf); a pair of tiles visits only the chunks whose
 // key rows its queries may see.
 //
-// Precision.  COSINE without rotation feeds k^ rounded to bf16 (error 2^-9
-// of the norm, multiplied by 1/tau); for tau < 0.1 it feeds the raw bf16 k
-// instead, exactly, and scales each score by 1/||k_j|| in fp32.  With
+// Precision.  COSINE without rotation feeds k^ log2(e)/tau and q / ||q||,
+// each rounded to bf16 (error 2^-9 of the norm, multiplied by 1/tau); for
+// tau < 0.1 it feeds the raw bf16 q and k instead, exactly, and scales each
+// score by 1/(||q_i|| ||k_j|| tau) in fp32.  With
 // rotation the rotated operands are rounded; when that error, amplified by
 // 1/tau (COSINE, tau < 0.1) or by max||q|| max||k|| log2(e)/sqrt(d) > 20
 // (DOT), would pass the bf16 tolerance, q and k are carried as hi + lo bf16
@@ -111,6 +117,15 @@ struct GroupWalk {
     }
 };
 
+// Whether a window-head runs with the scale folded into its staged keys:
+// COSINE outside the precise path (q then enters unit-normalised), and DOT
+// with rotation (the rotated operands are rounded in any case).
+template <int SIM, int POS>
+__device__ __forceinline__ bool folded(bool precise)
+{
+    return SIM == SWIN_SIM_COSINE ? !precise : POS == SWIN_POS_ROPE2D;
+}
+
 // One pair of query tiles against chunks [cb, ce) of a staged block.
 //   MASK: shift regions / padded slots; GENERAL: running maximum for tiles
 //   that need it, 1/||k_j|| scaling (precise), hi + lo products (split).
@@ -122,6 +137,10 @@ __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[NT], const f
     const int grp = lane >> 4, li = lane & 15;
     const int negrow = S * S;
     const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    // folded scale: the staged keys carry log2(e)/tau (COSINE) or
+    // log2(e)/sqrt(d) (DOT with rotation), the bias term starts the
+    // accumulator, and S^T holds the shifted logits in log2 units
+    const bool fold = folded<SIM, POS>(GENERAL && precise);
     bf16x8 ones;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
@@ -160,8 +179,10 @@ __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[NT], const f
         f32x4 sa[NT], sb[NT];
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
-            sa[i] = mfma(ka, T[i].qf, zero4);
-            sb[i] = mfma(kb, T[i].qf, zero4);
+            const f32x4 ia = {add[i][0], add[i][1], add[i][2], add[i][3]};
+            const f32x4 ib = {add[i][4], add[i][5], add[i][6], add[i][7]};
+            sa[i] = mfma(ka, T[i].qf, fold ? ia : zero4);
+            sb[i] = mfma(kb, T[i].qf, fold ? ib : zero4);
         }
         float kin[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
         if (GENERAL) {
@@ -195,7 +216,8 @@ __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[NT], const f
             if (!GENERAL || !T[i].exact) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    pr[e] = __builtin_amdgcn_exp2f(fmaf(x[e], GENERAL ? T[i].qscale * kin[e] : T[i].qscale, add[i][e]));
+                    pr[e] = __builtin_amdgcn_exp2f(
+                        fold ? x[e] : fmaf(x[e], GENERAL ? T[i].qscale * kin[e] : T[i].qscale, add[i][e]));
                 if (MASK && partial) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) pr[e] = (bits[i] >> e) & 1u ? pr[e] : 0.0f;
@@ -204,7 +226,7 @@ __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[NT], const f
                 float xs[8], cm = -INFINITY;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    xs[e] = fmaf(x[e], T[i].qscale * kin[e], add[i][e]);
+                    xs[e] = fold ? x[e] : fmaf(x[e], T[i].qscale * kin[e], add[i][e]);
                     if (MASK && partial) xs[e] = (bits[i] >> e) & 1u ? xs[e] : -INFINITY;
                     cm = fmaxf(cm, xs[e]);
                 }
@@ -346,8 +368,12 @@ attn_large_kernel(AttnParams p, LargeLayout L)
                         kdst[idx] = __builtin_bit_cast(bf16x8, raw[j][t]);
                         continue;
                     }
+                    const float ks = inv * (kLog2e * inv_tau);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) kf[e] *= inv;
+                    for (int e = 0; e < 8; ++e) kf[e] *= ks;
+                } else if (POS == SWIN_POS_ROPE2D) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) kf[e] *= kLog2e * 0.17677669529663687f;   // log2(e) / sqrt(32)
                 }
                 const bf16x8 hi = pack_bf16x8(kf);
                 kdst[idx] = hi;
@@ -500,21 +526,26 @@ attn_large_kernel(AttnParams p, LargeLayout L)
             float qf[8];
             unpack_bf16x8(raw, qf);
             if (POS == SWIN_POS_ROPE2D) rotate(qf, ri, ci);
-            T[i].qf = qhalf ? pack_bf16x8(qf) : __builtin_bit_cast(bf16x8, raw);
+            float ss = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(qf[e], qf[e], ss);
+            ss += __shfl_xor(ss, 16);
+            ss += __shfl_xor(ss, 32);
+            const float qinv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));   // 1 / max(||q||, 1e-12)
+            if (SIM == SWIN_SIM_COSINE && !precise) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qf[e] *= qinv;
+            }
+            T[i].qf = qhalf || (SIM == SWIN_SIM_COSINE && !precise) ? pack_bf16x8(qf) : __builtin_bit_cast(bf16x8, raw);
             {
                 float lo[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) lo[e] = qf[e] - (float)T[i].qf[e];
                 T[i].qf_lo = pack_bf16x8(lo);
             }
-            float ss = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf(qf[e], qf[e], ss);
-            ss += __shfl_xor(ss, 16);
-            ss += __shfl_xor(ss, 32);
             float spread;
             if (SIM == SWIN_SIM_COSINE) {
-                T[i].qscale = kLog2e * inv_tau * __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
+                T[i].qscale = kLog2e * inv_tau * qinv;
                 T[i].negm = POS == SWIN_POS_TABLE ? 0.0f : -kLog2e * inv_tau;
                 spread = 2.0f * kLog2e * inv_tau + bias_range;
             } else {

@@ -17,19 +17,25 @@
 //      source address; A operand of O^T = V^T P^T, read back transposed by
 //      ds_read_b64_tr_b16 per chunk of 32 keys;
 //   the bias table of the head, reversed (consecutive keys read consecutive
-//      floats), in log2 units and shifted by its maximum: every wavefront
-//      reads all of it, so its extrema need no barrier, and writes a quarter.
+//      floats), in log2 units less a per-head offset every wavefront knows
+//      before the barrier; each wavefront writes a quarter and posts its
+//      extrema.
 // The score tile leaves the MFMA with each lane holding 8 consecutive key
 // slots of one query, the B-operand layout of P^T, so the softmax runs in
 // registers between the two products; row sums come from a third MFMA
-// against an all-ones operand.
+// against an all-ones operand.  For COSINE, k^ carries the head's
+// log2(e)/tau and q enters unit-normalised, and the table entries (or the
+// constant -log2(e)/tau) start the accumulator of S^T: the products leave
+// shifted logits in log2 units and each score costs one exp2 and half a
+// pack, no FMA.
 //
-// Precision.  COSINE normally feeds the MFMA the unit-normalised k^ rounded
-// to bf16; that rounding (2^-9 of the norm) is multiplied by 1/tau, so for
-// tau < 0.1 a window feeds the raw bf16 k (exact) and scales each score by
-// 1/||k_j|| in fp32 instead.  The softmax uses a static shift (cos <= 1, or
-// Cauchy-Schwarz for DOT) when the spread of the logits stays within 2^60,
-// else the running maximum per 32-key chunk.
+// Precision.  COSINE normally feeds the MFMA k^ log2(e)/tau and q / ||q||,
+// each rounded to bf16; each rounding (2^-9 of the norm) is multiplied by
+// 1/tau, so for tau < 0.1 a window feeds the raw bf16 q and k (exact) and
+// scales each score by 1/(||q_i|| ||k_j|| tau) in fp32 instead.  The softmax
+// uses a static shift (cos <= 1, or Cauchy-Schwarz for DOT) when the spread
+// of the logits stays within 2^60, else the running maximum per 32-key
+// chunk.
 #include "common.hpp"
 #include "launch.hpp"
 #include "lanes.hpp"
@@ -98,6 +104,10 @@ __device__ __forceinline__ void run_pair(const bf16x8* kst, const __bf16* vst, T
 {
     const int grp = lane >> 4, li = lane & 15;
     const bool prec = PRECISE && precise_rt;
+    // COSINE outside the precise path: k^ carries log2(e)/tau and q its unit
+    // norm, the table (or -log2(e)/tau) starts the accumulator, so S^T holds
+    // the shifted logits in log2 units and goes to exp2 as it is
+    const bool fold = SIM == SWIN_SIM_COSINE && !prec;
     bf16x8 ones;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
@@ -134,8 +144,10 @@ __device__ __forceinline__ void run_pair(const bf16x8* kst, const __bf16* vst, T
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const f32x4 c4 = {T[i].cinit, T[i].cinit, T[i].cinit, T[i].cinit};
-            sa[i] = mfma(ka, T[i].qf, c4);
-            sb[i] = mfma(kb, T[i].qf, c4);
+            const f32x4 ia = {add[i][0], add[i][1], add[i][2], add[i][3]};
+            const f32x4 ib = {add[i][4], add[i][5], add[i][6], add[i][7]};
+            sa[i] = mfma(ka, T[i].qf, fold ? ia : c4);
+            sb[i] = mfma(kb, T[i].qf, fold ? ib : c4);
         }
         const bf16x8 v0 = vt_frag(vst, c, 0, grp, li);
         const bf16x8 v1 = vt_frag(vst, c, 1, grp, li);
@@ -151,7 +163,8 @@ __device__ __forceinline__ void run_pair(const bf16x8* kst, const __bf16* vst, T
             float pr[8];
             if (!EXACT || !T[i].exact) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(x[e], sc[e], add[i][e]));
+                for (int e = 0; e < 8; ++e)
+                    pr[e] = __builtin_amdgcn_exp2f(fold ? x[e] : fmaf(x[e], sc[e], add[i][e]));
                 if (MASK && partial_any) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) pr[e] = (bits[i] >> e) & 1u ? pr[e] : 0.0f;
@@ -160,7 +173,7 @@ __device__ __forceinline__ void run_pair(const bf16x8* kst, const __bf16* vst, T
                 float xs[8], cm = -INFINITY;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    xs[e] = fmaf(x[e], sc[e], add[i][e]);
+                    xs[e] = fold ? x[e] : fmaf(x[e], sc[e], add[i][e]);
                     if (MASK) xs[e] = (bits[i] >> e) & 1u ? xs[e] : -INFINITY;
                     cm = fmaxf(cm, xs[e]);
                 }
@@ -279,9 +292,10 @@ attn_small_kernel(AttnParams p, SmallLayout L)
     //   this wave's quarter of the bias table of head h: rows (wave + 4k) 64
     //   + lane, the last row standing in for those past the end (extrema
     //   are unaffected, nothing is written for them)
-    float tv[TQ];
+    float tv[TQ], t0 = 0.0f;
     if (POS == SWIN_POS_TABLE) {
         const Rsrc tr = make_rsrc(p.table, (uint32_t)(S * S * g.heads) * 4u);
+        t0 = load_f32(tr, (uint32_t)h * 4u);                // row 0: the table's offset in LDS
 #pragma unroll
         for (int k = 0; k < TQ; ++k) {
             const int r = min((wave + WAVES * k) * 64 + lane, S * S - 1);
@@ -291,7 +305,10 @@ attn_small_kernel(AttnParams p, SmallLayout L)
     vm_wait_all();
 
     // ---- bias table: this wave's quarter, reversed (row r at S*S - 1 - r),
-    // in log2 units; its extrema go to red for all waves
+    // in log2 units less boff (row 0, and for COSINE the largest cosine
+    // logit log2(e)/tau), which every wave knows before the barrier; its
+    // extrema go to red for all waves
+    const float boff = kLog2e * (t0 + (SIM == SWIN_SIM_COSINE ? inv_tau : 0.0f));
     if (POS == SWIN_POS_TABLE) {
         float mx = -INFINITY, mn = INFINITY;
 #pragma unroll
@@ -299,7 +316,7 @@ attn_small_kernel(AttnParams p, SmallLayout L)
             const int r = (wave + WAVES * k) * 64 + lane;
             mx = fmaxf(mx, tv[k]);
             mn = fminf(mn, tv[k]);
-            if (r < S * S) bias2[S * S - 1 - r] = tv[k] * kLog2e;
+            if (r < S * S) bias2[S * S - 1 - r] = fmaf(tv[k], kLog2e, -boff);
         }
         mx = wave_reduce<Op::Max>(mx);
         mn = wave_reduce<Op::Min>(mn);
@@ -307,9 +324,9 @@ attn_small_kernel(AttnParams p, SmallLayout L)
         if (wave == 0 && lane < 8) bias2[S * S + lane] = -INFINITY;
     }
 
-    // ---- k: unit-normalise (COSINE), or keep raw and record 1/||k||
-    // (precise COSINE) or the largest ||k|| (DOT); fragments to LDS in
-    // operand order, one 16-byte write per lane and tile
+    // ---- k: unit-normalise and scale by log2(e)/tau (COSINE), or keep raw
+    // and record 1/||k|| (precise COSINE) or the largest ||k|| (DOT);
+    // fragments to LDS in operand order, one 16-byte write per lane and tile
     float kmax = 0.0f;
 #pragma unroll
     for (int k = 0; k < SETS; ++k) {
@@ -324,8 +341,9 @@ attn_small_kernel(AttnParams p, SmallLayout L)
             } else {
                 float kf[8];
                 unpack_bf16x8(kraw[k], kf);
+                const float ks = inv * (kLog2e * inv_tau);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) kf[e] *= inv;
+                for (int e = 0; e < 8; ++e) kf[e] *= ks;
                 kfrag = pack_bf16x8(kf);
             }
         } else {
@@ -346,14 +364,16 @@ attn_small_kernel(AttnParams p, SmallLayout L)
         for (int r = 1; r < QW; ++r) kmax = fmaxf(kmax, red[wh * QW + r]);
         kmax = sqrtf(kmax);                               // largest ||k|| of the window
     }
-    // table extrema (log2 units): the static shift puts the largest
-    // possible logit at 0 (COSINE: cos <= 1; DOT: Cauchy-Schwarz per query)
+    // table extrema (log2 units, as stored): the static shift puts the
+    // largest possible logit at 0 or below (COSINE: cos <= 1, and the
+    // table's offset already holds log2(e)/tau; DOT: Cauchy-Schwarz per
+    // query)
     float bias_max = 0.0f, bias_range = 0.0f;
     if (POS == SWIN_POS_TABLE) {
         float mx = red[WAVES], mn = red[2 * WAVES];
 #pragma unroll
         for (int r = 1; r < WAVES; ++r) { mx = fmaxf(mx, red[WAVES + r]); mn = fminf(mn, red[2 * WAVES + r]); }
-        bias_max = mx * kLog2e;
+        bias_max = fmaf(mx, kLog2e, -boff);
         bias_range = (mx - mn) * kLog2e;
     }
 
@@ -383,12 +403,19 @@ attn_small_kernel(AttnParams p, SmallLayout L)
             const u32x4 qw = qraw[i];
             T[i].qf = __builtin_bit_cast(bf16x8, qw);
             const float ss = sum_x32(sum_x16(sumsq8(qraw[i])));
-            float spread, shift;
+            float spread, shift = 0.0f;
             if (SIM == SWIN_SIM_COSINE) {
-                T[i].qscale = kLog2e * inv_tau * __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
+                const float qinv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));   // 1 / max(||q||, 1e-12)
+                T[i].qscale = kLog2e * inv_tau * qinv;
                 T[i].negm = -kLog2e * inv_tau;
                 spread = 2.0f * kLog2e * inv_tau + bias_range;
-                shift = kLog2e * inv_tau + bias_max;
+                if (!precise) {                                   // the MFMA takes q / ||q||
+                    float qf[8];
+                    unpack_bf16x8(qw, qf);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) qf[e] *= qinv;
+                    T[i].qf = pack_bf16x8(qf);
+                }
             } else {
                 T[i].qscale = kLog2e * 0.17677669529663687f;          // log2(e) / sqrt(32)
                 const float c_i = sqrtf(ss) * kmax * T[i].qscale;
@@ -396,11 +423,14 @@ attn_small_kernel(AttnParams p, SmallLayout L)
                 spread = 2.0f * c_i + bias_range;
                 shift = c_i + bias_max;
             }
-            // TABLE: the shift enters through the accumulator of S^T (the
-            // per-key scale of the precise path rules that out there: it
-            // takes the running maximum); no table: it is the added term
+            // DOT with a table: the shift enters through the accumulator of
+            // S^T; no table: it is the added term.  COSINE outside the
+            // precise path starts the accumulator from the stored table
+            // (or -log2(e)/tau) instead; the precise path takes the running
+            // maximum.  Spreads within RANGE_LIMIT keep every exp2 argument
+            // of the static shift in [-60, 60].
             T[i].exact = precise || __any(!(spread <= RANGE_LIMIT)) != 0;
-            T[i].cinit = POS == SWIN_POS_TABLE && !precise ? -shift / T[i].qscale : 0.0f;
+            T[i].cinit = SIM == SWIN_SIM_DOT && POS == SWIN_POS_TABLE ? -shift / T[i].qscale : 0.0f;
             any_exact = any_exact || T[i].exact;
             T[i].mrun = -INFINITY;
             T[i].qoff = (M - 1 - ri) * S + (M - 1 - ci) + kbase;

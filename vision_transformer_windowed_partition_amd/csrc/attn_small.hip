@@ -91,14 +91,15 @@ struct Tile {                  // one query tile of 16 queries
     f32x4 o0, o1, ls;
 };
 
-// One pair of query tiles against key chunks [CB, CE) of the window (the
-// others are masked for both tiles); K^ fragments and V rows come from LDS.
+// NT (one or two) query tiles against key chunks [CB, CE) of the window
+// (the others are masked for all of them); K^ fragments and V rows come
+// from LDS.
 // The key group of a lane in chunk c starts (4 / GPR) c rows further down
 // the window than in chunk 0: its bias row moves by that many table rows.
 //   MASK: shift regions / padded slots; PRECISE: scores scaled by 1/||k_j||
 //   (raw k operand); EXACT: running maximum instead of the static shift.
-template <int SIM, int POS, int GPR, int CB, int CE, bool MASK, bool PRECISE, bool EXACT>
-__device__ __forceinline__ void run_pair(const bf16x8* kst, const __bf16* vst, Tile (&T)[2], const float* bias2,
+template <int SIM, int POS, int GPR, int CB, int CE, bool MASK, bool PRECISE, bool EXACT, int NT>
+__device__ __forceinline__ void run_pair(const bf16x8* kst, const __bf16* vst, Tile* T, const float* bias2,
                                          const float* kinv, int S, int negrow, int lane, bool partial_any,
                                          bool precise_rt)
 {
@@ -111,14 +112,19 @@ __device__ __forceinline__ void run_pair(const bf16x8* kst, const __bf16* vst, T
     bf16x8 ones;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
-#pragma unroll
+    // the running-maximum variant stays rolled: its registers are not to
+    // set the kernel's occupancy
+    constexpr int UNROLL = EXACT ? 1 : CE - CB;
+#pragma unroll UNROLL
     for (int c = CB; c < CE; ++c) {
         const bf16x8 ka = kst[(c * 2 + 0) * 64 + lane];
         const bf16x8 kb = kst[(c * 2 + 1) * 64 + lane];
-        uint32_t bits[2] = {0xffu, 0xffu};
+        uint32_t bits[NT];
+#pragma unroll
+        for (int i = 0; i < NT; ++i) bits[i] = 0xffu;
         if (MASK) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) bits[i] = (T[i].gmask >> c) & 1u ? T[i].colbits : 0u;
+            for (int i = 0; i < NT; ++i) bits[i] = (T[i].gmask >> c) & 1u ? T[i].colbits : 0u;
         }
         float kin[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
         if (prec) {
@@ -127,9 +133,9 @@ __device__ __forceinline__ void run_pair(const bf16x8* kst, const __bf16* vst, T
             kin[0] = a[0]; kin[1] = a[1]; kin[2] = a[2]; kin[3] = a[3];
             kin[4] = b[0]; kin[5] = b[1]; kin[6] = b[2]; kin[7] = b[3];
         }
-        float add[2][8];
+        float add[NT][8];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NT; ++i) {
             if (POS == SWIN_POS_TABLE) {
                 const float* bp = bias2 + ((MASK && bits[i] == 0u) ? negrow : T[i].qoff + (4 / GPR) * c * S);
 #pragma unroll
@@ -140,9 +146,9 @@ __device__ __forceinline__ void run_pair(const bf16x8* kst, const __bf16* vst, T
                 for (int e = 0; e < 8; ++e) add[i][e] = a;
             }
         }
-        f32x4 sa[2], sb[2];
+        f32x4 sa[NT], sb[NT];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NT; ++i) {
             const f32x4 c4 = {T[i].cinit, T[i].cinit, T[i].cinit, T[i].cinit};
             const f32x4 ia = {add[i][0], add[i][1], add[i][2], add[i][3]};
             const f32x4 ib = {add[i][4], add[i][5], add[i][6], add[i][7]};
@@ -151,9 +157,9 @@ __device__ __forceinline__ void run_pair(const bf16x8* kst, const __bf16* vst, T
         }
         const bf16x8 v0 = vt_frag(vst, c, 0, grp, li);
         const bf16x8 v1 = vt_frag(vst, c, 1, grp, li);
-        bf16x8 pb[2];
+        bf16x8 pb[NT];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NT; ++i) {
             float x[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) { x[e] = sa[i][e]; x[e + 4] = sb[i][e]; }
@@ -189,7 +195,7 @@ __device__ __forceinline__ void run_pair(const bf16x8* kst, const __bf16* vst, T
             pb[i] = pack_bf16x8(pr);
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NT; ++i) {
             T[i].o0 = mfma(v0, pb[i], T[i].o0);
             T[i].o1 = mfma(v1, pb[i], T[i].o1);
             T[i].ls = mfma(ones, pb[i], T[i].ls);
@@ -377,8 +383,10 @@ attn_small_kernel(AttnParams p, SmallLayout L)
         bias_range = (mx - mn) * kLog2e;
     }
 
-    // ---- this wave's query tiles rank + QW k, two at a time
+    // ---- this wave's query tiles rank + QW k, two at a time; the next
+    // pair's query rows load while the current pair runs
     const int kbase = (grp / GPR) * S + 8 * (grp % GPR);  // bias offset of this lane's key group in chunk 0
+    u32x4 qnext[2] = {qpre[0], qpre[1]};
     for (int k0 = 0; rank + QW * k0 < L.NQT; k0 += 2) {
         Tile T[2];
         int qt[2];
@@ -390,11 +398,16 @@ attn_small_kernel(AttnParams p, SmallLayout L)
             const int t = tq * 16 + li;
             qv[i] = tq < L.NQT && t < N;
             qt[i] = qv[i] ? t : 0;
-            if (k0 == 0) qraw[i] = qpre[i];
-            else {
-                const int ri = qdiv(qt[i], L.inv_M), ci = qt[i] - ri * M;
-                qraw[i] = load16(qr, masked(wg.tok(ri, ci) + 16u * grp, qv[i]));
-            }
+            qraw[i] = qnext[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int tq = rank + QW * (k0 + 2 + i);
+            const int t = tq * 16 + li;
+            const bool ok = tq < L.NQT && t < N;
+            const int tt = ok ? t : 0;
+            const int ri = qdiv(tt, L.inv_M), ci = tt - ri * M;
+            qnext[i] = load16(qr, masked(wg.tok(ri, ci) + 16u * grp, ok));
         }
         bool any_exact = false, partial = false;
 #pragma unroll
@@ -459,9 +472,14 @@ attn_small_kernel(AttnParams p, SmallLayout L)
             T[i].ls = T[i].o0;
         }
         const int negrow = S * S;
-        if (any_exact || precise)
-            run_pair<SIM, POS, GPR, 0, NCH, true, true, true>(kst, vst, T, bias2, kinv, S, negrow, lane, true, precise);
-        else if (needs_mask) {
+        if (any_exact || precise) {
+            // the running maximum (rare): one tile at a time, so that its
+            // registers do not set the occupancy of the common path
+            run_pair<SIM, POS, GPR, 0, NCH, true, true, true, 1>(kst, vst, T, bias2, kinv, S, negrow, lane, true,
+                                                                 precise);
+            run_pair<SIM, POS, GPR, 0, NCH, true, true, true, 1>(kst, vst, T + 1, bias2, kinv, S, negrow, lane, true,
+                                                                 precise);
+        } else if (needs_mask) {
             // chunks some lane of the pair may see: all, or one half of the key rows
             uint32_t live = T[0].gmask | T[1].gmask;
 #pragma unroll
@@ -469,16 +487,16 @@ attn_small_kernel(AttnParams p, SmallLayout L)
             live = (uint32_t)__builtin_amdgcn_readfirstlane((int)live);
             constexpr uint32_t lo_half = (1u << (NCH / 2)) - 1u;
             if ((live & ~lo_half) == 0u)
-                run_pair<SIM, POS, GPR, 0, NCH / 2, true, false, false>(kst, vst, T, bias2, kinv, S, negrow, lane,
+                run_pair<SIM, POS, GPR, 0, NCH / 2, true, false, false, 2>(kst, vst, T, bias2, kinv, S, negrow, lane,
                                                                         partial, false);
             else if ((live & lo_half) == 0u)
-                run_pair<SIM, POS, GPR, NCH / 2, NCH, true, false, false>(kst, vst, T, bias2, kinv, S, negrow, lane,
+                run_pair<SIM, POS, GPR, NCH / 2, NCH, true, false, false, 2>(kst, vst, T, bias2, kinv, S, negrow, lane,
                                                                           partial, false);
             else
-                run_pair<SIM, POS, GPR, 0, NCH, true, false, false>(kst, vst, T, bias2, kinv, S, negrow, lane,
+                run_pair<SIM, POS, GPR, 0, NCH, true, false, false, 2>(kst, vst, T, bias2, kinv, S, negrow, lane,
                                                                     partial, false);
         } else
-            run_pair<SIM, POS, GPR, 0, NCH, false, false, false>(kst, vst, T, bias2, kinv, S, negrow, lane, false,
+            run_pair<SIM, POS, GPR, 0, NCH, false, false, false, 2>(kst, vst, T, bias2, kinv, S, negrow, lane, false,
                                                                  false);
 
         // ---- normalise and store: lane holds channels 4 grp..+3 and

@@ -6,8 +6,9 @@ package never imports the GPU library: the two share no code.
 
 Contents
   * ``oracle.c`` (compiled with gcc into ``liboracle.so``): the plain per-window
-    definition -- partition / reverse maps, log-spaced offsets, the CPB table and
-    the attention itself, all in fp64.
+    definition -- partition / reverse maps, log-spaced offsets, the CPB table,
+    the attention itself and its backward, and the attention branch's linear
+    layers and residual post-norm, all in fp64.
   * ``bruteforce.py``: full-grid attention over every token pair with a mask, for
     tiny grids; it shares neither the partition nor the table indexing with
     ``oracle.c`` and serves as that file's independent check.
@@ -69,6 +70,10 @@ def _declare(lib):
     lib.oracle_cpb_table_bwd.argtypes = [i32] * 4 + [vp] * 4 + [i32] + [vp] * 5
     lib.oracle_window_cosines.restype = i32
     lib.oracle_window_cosines.argtypes = [i32] * 9 + [dbl, vp, vp, vp, i64, i32, vp]
+    lib.oracle_linear.restype = i32
+    lib.oracle_linear.argtypes = [vp] * 4 + [i64, i32, i32]
+    lib.oracle_post_norm.restype = i32
+    lib.oracle_post_norm.argtypes = [vp] * 4 + [dbl, vp, i64, i32]
     lib.oracle_set_threads.restype = None
     lib.oracle_set_threads.argtypes = [i32]
     lib.oracle_max_threads.restype = i32
@@ -253,6 +258,50 @@ def window_cosines(q, k, *, heads: int, M: int, shift: int, partition: str, wind
     if rc:
         raise ValueError("oracle_window_cosines: bad argument")
     return out
+
+
+def linear(x, w, b=None, lib=None) -> np.ndarray:
+    """x (..., in) times w^T (w: out x in) plus b, in fp64; leading dims kept."""
+    x, w = _f64(x), _f64(w)
+    out_f, in_f = w.shape
+    assert x.shape[-1] == in_f
+    xt = np.ascontiguousarray(x.reshape(-1, in_f))
+    y = np.empty((xt.shape[0], out_f))
+    bb = None if b is None else _f64(b)
+    if bb is not None:
+        assert bb.shape == (out_f,)
+    rc = (lib or load()).oracle_linear(_ptr(xt), _ptr(w), _ptr(bb), _ptr(y), xt.shape[0], in_f, out_f)
+    if rc:
+        raise ValueError("oracle_linear: bad argument")
+    return y.reshape(*x.shape[:-1], out_f)
+
+
+def qkv_proj(x, w, b=None, lib=None):
+    """The attention branch's input projection: (q, k, v), each shaped like x,
+    from one linear layer C -> 3C whose outputs are q, k, v in that order."""
+    y = linear(x, w, b, lib=lib)
+    C = x.shape[-1]
+    assert w.shape == (3 * C, C)
+    return y[..., :C].copy(), y[..., C:2 * C].copy(), y[..., 2 * C:].copy()
+
+
+def post_norm(resid, z, gamma, beta, eps: float = 1e-5, lib=None) -> np.ndarray:
+    """resid + layer_norm(z) * gamma + beta over the last axis, in fp64."""
+    resid, z, gamma, beta = _f64(resid), _f64(z), _f64(gamma), _f64(beta)
+    C = z.shape[-1]
+    assert resid.shape == z.shape and gamma.shape == (C,) and beta.shape == (C,)
+    rt, zt = np.ascontiguousarray(resid.reshape(-1, C)), np.ascontiguousarray(z.reshape(-1, C))
+    y = np.empty_like(zt)
+    rc = (lib or load()).oracle_post_norm(_ptr(rt), _ptr(zt), _ptr(gamma), _ptr(beta), float(eps), _ptr(y),
+                                          zt.shape[0], C)
+    if rc:
+        raise ValueError("oracle_post_norm: bad argument")
+    return y.reshape(z.shape)
+
+
+def proj_post_norm(o, w, b, resid, gamma, beta, eps: float = 1e-5, lib=None) -> np.ndarray:
+    """The attention branch's output side: resid + norm_1(o w^T + b)."""
+    return post_norm(resid, linear(o, w, b, lib=lib), gamma, beta, eps, lib=lib)
 
 
 def cpu_model() -> str:

@@ -1,7 +1,8 @@
 /*
  * oracle.c -- plain fp64 CPU reference for windowed multi-head self-attention
- * (forward), the log-spaced continuous position bias table and the window
- * partition / reverse maps.
+ * (forward and backward), the log-spaced continuous position bias table, the
+ * window partition / reverse maps, and the attention branch's projections and
+ * residual post-norm.
  *
  * TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the CPU
  * baseline leg of the benchmark are the only code that may load this library.
@@ -13,7 +14,8 @@
  *             eq. 2 (cos(q_i,k_j)/tau + B_ij, tau kept at or above 0.01),
  *             eq. 3 (B = G(dx, dy)), eq. 4 (sign(x) log(1+|x|)), the
  *             window-attention and continuous-bias pseudocode, the
- *             Architecture table (G is a 2-layer ReLU MLP, 512 wide in code).
+ *             Architecture table (G is a 2-layer ReLU MLP, 512 wide in code);
+ *             Method item 1 (residual post-norm) and the block pseudocode.
  *   [Flash]   "FLASHSWIN: Unlocking Large Windows and Dense Tokens ...",
  *             abstract: exact softmax attention inside each window, and
  *             window-local 2D rotary position embedding in place of the bias.
@@ -702,5 +704,54 @@ int oracle_cpb_table_bwd(int M, int norm_M, int heads, int hidden,
             }
         }
     free(a); free(dg);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * The steps either side of the window attention in a Swin V2 block ([SwinV2]
+ * Method item 1 "Residual post-norm" and the block pseudocode; the block keeps
+ * Swin's layout, Method opening paragraph).  Readings: the attention branch
+ * maps its input features through a linear layer to queries, keys and values
+ * (C -> 3C, in that order along the output, each with a bias) and its output
+ * through a linear layer C -> C with a bias; norm_1 is a layer norm over the C
+ * channels of each token (biased variance, eps inside the square root) with a
+ * per-channel scale and shift, applied to the branch output before it is added
+ * to the main path.
+ * ------------------------------------------------------------------------- */
+
+/* y[t][n] = sum_c x[t][c] w[n][c] + b[n]  (x: T x in, w: out x in, b: out or
+ * NULL, y: T x out), every product and sum in fp64 in index order. */
+int oracle_linear(const double* x, const double* w, const double* b, double* y, int64_t T, int in, int out)
+{
+    if (T < 0 || in < 1 || out < 1 || (T > 0 && (!x || !w || !y))) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int n = 0; n < out; ++n) {
+            double s = b ? b[n] : 0.0;
+            for (int c = 0; c < in; ++c) s += x[t * in + c] * w[(size_t)n * in + c];
+            y[t * out + n] = s;
+        }
+    return 0;
+}
+
+/* y[t] = resid[t] + gamma * (z[t] - mean(z[t])) / sqrt(var(z[t]) + eps) + beta,
+ * mean and (biased) variance over the C channels of token t. */
+int oracle_post_norm(const double* resid, const double* z, const double* gamma, const double* beta,
+                     double eps, double* y, int64_t T, int C)
+{
+    if (T < 0 || C < 1 || !(eps >= 0.0) || (T > 0 && (!resid || !z || !gamma || !beta || !y))) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const double* zt = z + t * C;
+        double mean = 0.0;
+        for (int c = 0; c < C; ++c) mean += zt[c];
+        mean /= C;
+        double var = 0.0;
+        for (int c = 0; c < C; ++c) var += (zt[c] - mean) * (zt[c] - mean);
+        var /= C;
+        const double inv = 1.0 / sqrt(var + eps);
+        for (int c = 0; c < C; ++c)
+            y[t * C + c] = resid[t * C + c] + gamma[c] * (zt[c] - mean) * inv + beta[c];
+    }
     return 0;
 }

@@ -61,6 +61,13 @@ MUTATIONS = [
     ("cpb_bwd_relu_mask", "const double da = a[j] > 0.0 ? dh : 0.0;", "const double da = dh;"),
     ("cpb_bwd_sigmoid", "dg[o] *= 16.0 * s * (1.0 - s);", "dg[o] *= 16.0 * s;"),
     ("cpb_bwd_inputs_swapped", "dw1[2 * j] += da * in0;", "dw1[2 * j] += da * in1;"),
+    ("linear_transposed", "x[t * in + c] * w[(size_t)n * in + c]", "x[t * in + c] * w[(size_t)c * out + n]"),
+    ("linear_bias_dropped", "double s = b ? b[n] : 0.0;", "double s = 0.0;"),
+    ("ln_unbiased_var", "var /= C;", "var /= (C - 1);"),
+    ("ln_eps_outside", "1.0 / sqrt(var + eps)", "1.0 / (sqrt(var) + eps)"),
+    ("ln_resid_dropped", "y[t * C + c] = resid[t * C + c] + gamma[c]", "y[t * C + c] = gamma[c]"),
+    ("ln_gamma_beta_swapped", "gamma[c] * (zt[c] - mean) * inv + beta[c]", "beta[c] * (zt[c] - mean) * inv + gamma[c]"),
+    ("ln_mean_not_subtracted", "var += (zt[c] - mean) * (zt[c] - mean);", "var += zt[c] * zt[c];"),
 ]
 
 

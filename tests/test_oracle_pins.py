@@ -11,7 +11,11 @@ mathematics fix, never against itself.
     partition nor the table indexing with the oracle;
   * closed forms of the partition (torch.roll + reshape, reshape/permute);
   * invariants: rows sum to 1, cross-region weights are exactly 0, cos in
-    [-1, 1], the tau floor, invariance to a per-head constant bias (b2).
+    [-1, 1], the tau floor, invariance to a per-head constant bias (b2);
+  * the attention branch's linear layers and post-norm: a hand-worked product,
+    scaled-permutation weights, the q/k/v order, the two-channel and constant
+    closed forms of the layer norm, its shift/scale invariance, and torch's
+    fp64 linear and layer_norm.
 
 Each pin is a function of the oracle library handle so that
 tests/test_oracle_mutations.py can run the same pins against oracle builds
@@ -378,6 +382,74 @@ def pin_cpb_bwd_finite_differences(lib):
             _fd_check(loss, x, gx, range(x.size), atol=1e-6)
 
 
+def pin_linear_closed_forms(lib):
+    """Linear layers of the attention branch (SwinV2 card, Method item 1 and
+    the block pseudocode): a hand-worked product, a scaled permutation weight
+    (out != in, so a transposed operand cannot pass), and torch's fp64 linear."""
+    x = np.array([[1.0, 2.0, 3.0], [-1.0, 0.5, 4.0]])
+    w = np.array([[1.0, 0.0, -1.0], [2.0, 1.0, 0.0]])
+    b = np.array([0.5, -1.0])
+    y = oracle.linear(x, w, b, lib=lib)
+    assert np.array_equal(y, np.array([[-1.5, 3.0], [-4.5, -2.5]])), y
+    rng = np.random.default_rng(7)
+    C_in, C_out = 5, 12
+    perm = rng.permutation(np.arange(C_out) % C_in)
+    scale = rng.uniform(0.5, 2.0, C_out)
+    wp = np.zeros((C_out, C_in))
+    wp[np.arange(C_out), perm] = scale
+    bp = rng.standard_normal(C_out)
+    xp = rng.standard_normal((4, 3, C_in))
+    yp = oracle.linear(xp, wp, bp, lib=lib)
+    assert np.allclose(yp, xp[..., perm] * scale + bp, rtol=0, atol=1e-14)
+    wr, br = rng.standard_normal((C_out, C_in)), rng.standard_normal(C_out)
+    yr = oracle.linear(xp, wr, br, lib=lib)
+    ref = F.linear(torch.from_numpy(xp), torch.from_numpy(wr), torch.from_numpy(br)).numpy()
+    assert np.allclose(yr, ref, rtol=1e-13, atol=1e-13)
+
+
+def pin_qkv_split(lib):
+    """One C -> 3C layer gives q, k, v in that order: with weight [I; 2I; 3I]
+    and biases (bq, bk, bv) they are x + bq, 2x + bk, 3x + bv."""
+    rng = np.random.default_rng(3)
+    C = 8
+    x = rng.standard_normal((2, 4, 4, C))
+    w = np.concatenate([np.eye(C), 2 * np.eye(C), 3 * np.eye(C)])
+    b = rng.standard_normal(3 * C)
+    q, k, v = oracle.qkv_proj(x, w, b, lib=lib)
+    assert np.allclose(q, x + b[:C], atol=1e-15)
+    assert np.allclose(k, 2 * x + b[C:2 * C], atol=1e-15)
+    assert np.allclose(v, 3 * x + b[2 * C:], atol=1e-15)
+
+
+def pin_post_norm_closed_forms(lib):
+    """Residual post-norm (SwinV2 card, Method item 1): resid + norm_1(z).
+    Two channels [a, b] normalise to +-(a-b)/2 / sqrt((a-b)^2/4 + eps); a
+    constant token gives resid + beta; with eps = 0 the result does not change
+    under z -> alpha z + c (alpha > 0); and it equals torch's fp64 layer_norm."""
+    eps = 1e-5
+    gamma, beta = np.array([1.5, -0.25]), np.array([0.125, 2.0])
+    r = np.array([[0.5, -1.0], [3.0, 4.0]])
+    z = np.array([[2.0, -1.0], [0.25, 1.75]])
+    y = oracle.post_norm(r, z, gamma, beta, eps, lib=lib)
+    for t in range(2):
+        a, b = z[t]
+        h = (a - b) / 2.0 / math.sqrt((a - b) ** 2 / 4.0 + eps)
+        want = r[t] + gamma * np.array([h, -h]) + beta
+        assert np.allclose(y[t], want, rtol=0, atol=1e-14), (y[t], want)
+    rng = np.random.default_rng(11)
+    C = 24
+    g2, b2 = rng.uniform(0.5, 1.5, C), rng.standard_normal(C)
+    r2 = rng.standard_normal((5, C))
+    zc = np.full((5, C), 3.25)
+    assert np.allclose(oracle.post_norm(r2, zc, g2, b2, eps, lib=lib), r2 + b2, atol=1e-14)
+    z2 = rng.standard_normal((5, C)) * 3.0 + 1.0
+    y0 = oracle.post_norm(r2, z2, g2, b2, 0.0, lib=lib)
+    y1 = oracle.post_norm(r2, 2.5 * z2 - 7.0, g2, b2, 0.0, lib=lib)
+    assert np.allclose(y0, y1, rtol=0, atol=1e-12)
+    ref = r2 + F.layer_norm(torch.from_numpy(z2), (C,), torch.from_numpy(g2), torch.from_numpy(b2), eps).numpy()
+    assert np.allclose(oracle.post_norm(r2, z2, g2, b2, eps, lib=lib), ref, rtol=1e-13, atol=1e-13)
+
+
 PINS = {
     "worked_example": pin_worked_example,
     "cpb_vs_torch": pin_cpb_vs_torch,
@@ -393,6 +465,9 @@ PINS = {
     "bwd_finite_differences": pin_bwd_finite_differences,
     "bwd_single_window_sdpa": pin_bwd_single_window_sdpa,
     "cpb_bwd_finite_differences": pin_cpb_bwd_finite_differences,
+    "linear_closed_forms": pin_linear_closed_forms,
+    "qkv_split": pin_qkv_split,
+    "post_norm_closed_forms": pin_post_norm_closed_forms,
 }
 
 

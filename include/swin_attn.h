@@ -201,6 +201,36 @@ int swin_cpb_table_bwd(int32_t M, int32_t norm_M, int32_t heads, int32_t hidden,
                        const float* dtable, int32_t cpb_mode, float* dw1, float* db1,
                        float* dw2, float* db2, void* stream);
 
+/* The attention branch's input layer ([SwinV2] Method opening paragraph: the
+ * block keeps Swin's layout; block pseudocode): one linear layer C -> 3C whose
+ * outputs are queries, keys and values in that order,
+ *   [q | k | v][t] = w x[t] + b,  w: 3C x C (output rows, input columns).
+ * x: T x C (any (B, H, W, C) grid flattened), q, k, v: T x C each (outputs,
+ * written), all of `dtype` (SWIN_DT_F32 or SWIN_DT_BF16), device memory,
+ * 16-byte aligned; w of the same dtype; b: 3C fp32 or NULL (no bias).
+ * Requires C a multiple of 32, 32 <= C <= 512 (SWIN_EUNSUPPORTED otherwise);
+ * T = 0 is a no-op.  q, k, v must not overlap x, w, b or each other
+ * (SWIN_EINVAL).  Arithmetic: bf16 products on the matrix cores with fp32
+ * accumulation, bias added in fp32, rounded once to nearest even; fp32
+ * throughout for SWIN_DT_F32. */
+int swin_qkv_proj(const void* x, const void* w, const float* b, void* q, void* k, void* v,
+                  int64_t T, int32_t C, int32_t dtype, void* stream);
+
+/* The attention branch's output layer and residual post-norm ([SwinV2]
+ * Method item 1: the layer norm moves to the output of the residual branch,
+ * before the add; block pseudocode):
+ *   z[t] = w o[t] + b,   y[t] = resid[t] + gamma * (z[t] - mean) / sqrt(var + eps) + beta,
+ * mean and biased variance over the C channels of token t.
+ * o (the attention output), resid (the main path) and y (output, written):
+ * T x C of `dtype`; w: C x C of `dtype`; b (C or NULL), gamma, beta (C): fp32.
+ * All device memory, 16-byte aligned.  y may be resid itself (in place) but
+ * must not overlap any other input (SWIN_EINVAL); eps >= 0 and finite.  Same
+ * C rule as swin_qkv_proj.  Arithmetic: z in fp32 from bf16 products (or fp32),
+ * mean and variance in fp32 by two passes, y rounded once. */
+int swin_proj_post_norm(const void* o, const void* w, const float* b, const void* resid,
+                        const float* gamma, const float* beta, float eps, void* y,
+                        int64_t T, int32_t C, int32_t dtype, void* stream);
+
 /* Name of the kernel that swin_window_attn_fwd launches for desc (static
  * storage), for matching profiler output:
  *   "attn_valu_kernel"  SWIN_DT_F32;

@@ -36,6 +36,7 @@ def test_header_declares_the_boundary():
                                            "swin_window_reverse",
                                            "swin_window_attn_fwd", "swin_window_attn_kernel",
                                            "swin_window_attn_bwd_kernel",
+                                           "swin_qkv_proj", "swin_proj_post_norm",
                                            "swin_status_string",
                                            "swin_last_error", "swin_version"])
 
@@ -110,6 +111,42 @@ def _bwd(L, desc, q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, dq=ctypes.c_void_
          dtau=None, dtable=None):
     return L.swin_window_attn_bwd(ctypes.byref(desc) if desc is not None else None, q, k, v, out, dout, tau,
                                   table, None, dq, dk, dv, dtau, dtable, None)
+
+
+def _qkv(L, x=FAKE, w=ctypes.c_void_p(0x30000000), b=None, q=ctypes.c_void_p(0x40000000),
+         k=ctypes.c_void_p(0x50000000), v=ctypes.c_void_p(0x60000000), T=64, C=96, dtype=1):
+    return L.swin_qkv_proj(x, w, b, q, k, v, T, C, dtype, None)
+
+
+def _pnorm(L, o=FAKE, w=ctypes.c_void_p(0x30000000), b=None, resid=ctypes.c_void_p(0x40000000),
+           gamma=ctypes.c_void_p(0x50000000), beta=ctypes.c_void_p(0x50001000),
+           y=ctypes.c_void_p(0x60000000), eps=1e-5, T=64, C=96, dtype=1):
+    return L.swin_proj_post_norm(o, w, b, resid, gamma, beta, eps, y, T, C, dtype, None)
+
+
+def test_projection_rejects(L):
+    """Host validation of the branch's linear layers: nothing is launched."""
+    assert _qkv(L, C=80) == SWIN_EUNSUPPORTED                                   # not a multiple of 32
+    assert _qkv(L, C=544) == SWIN_EUNSUPPORTED                                  # above 512
+    assert _qkv(L, C=0) == SWIN_EINVAL
+    assert _qkv(L, T=-1) == SWIN_EINVAL
+    assert _qkv(L, dtype=2) == SWIN_EINVAL
+    assert _qkv(L, x=None) == SWIN_EINVAL
+    assert _qkv(L, v=None) == SWIN_EINVAL
+    assert _qkv(L, q=ctypes.c_void_p(0x40000008)) == SWIN_EINVAL                # misaligned
+    assert _qkv(L, b=ctypes.c_void_p(0x70000004)) == SWIN_EINVAL                # misaligned bias
+    assert _qkv(L, q=ctypes.c_void_p(0x10000 + 128)) == SWIN_EINVAL             # q overlaps x
+    assert _qkv(L, k=ctypes.c_void_p(0x40000000 + 64)) == SWIN_EINVAL           # k overlaps q
+    assert _qkv(L, x=None, w=None, q=None, k=None, v=None, T=0) == SWIN_OK      # empty: no-op
+    assert _pnorm(L, C=48) == SWIN_EUNSUPPORTED
+    assert _pnorm(L, eps=-1.0) == SWIN_EINVAL
+    assert _pnorm(L, eps=float("nan")) == SWIN_EINVAL
+    assert _pnorm(L, gamma=None) == SWIN_EINVAL
+    assert _pnorm(L, y=ctypes.c_void_p(0x10000 + 64)) == SWIN_EINVAL            # y overlaps o
+    assert _pnorm(L, y=ctypes.c_void_p(0x40000000 + 32)) == SWIN_EINVAL         # partial overlap of resid
+    assert _pnorm(L, y=ctypes.c_void_p(0x50000000 - 64)) == SWIN_EINVAL         # y overlaps gamma
+    assert _pnorm(L, beta=ctypes.c_void_p(0x50001008)) == SWIN_EINVAL           # misaligned
+    assert _pnorm(L, o=None, w=None, resid=None, gamma=None, beta=None, y=None, T=0) == SWIN_OK
 
 
 def test_backward_rejects(L):

@@ -64,6 +64,10 @@ def lib() -> ctypes.CDLL:
         L.swin_window_attn_bwd.argtypes = [ctypes.POINTER(SwinAttnDesc)] + [vp] * 14
         L.swin_cpb_table_bwd.restype = i32
         L.swin_cpb_table_bwd.argtypes = [i32] * 4 + [vp] * 5 + [i32] + [vp] * 5
+        L.swin_qkv_proj.restype = i32
+        L.swin_qkv_proj.argtypes = [vp] * 6 + [ctypes.c_int64, i32, i32, vp]
+        L.swin_proj_post_norm.restype = i32
+        L.swin_proj_post_norm.argtypes = [vp] * 6 + [ctypes.c_float, vp, ctypes.c_int64, i32, i32, vp]
         L.swin_window_attn_kernel.restype = ctypes.c_char_p
         L.swin_window_attn_kernel.argtypes = [ctypes.POINTER(SwinAttnDesc)]
         L.swin_window_attn_bwd_kernel.restype = ctypes.c_char_p
@@ -241,6 +245,47 @@ def swin_cpb_table_bwd(M: int, w1, b1, w2, table, dtable, *, cpb_mode: int = CPB
                                     _ptr(w2), _ptr(table), _ptr(dtable), cpb_mode, _ptr(dw1), _ptr(db1),
                                     _ptr(dw2), _ptr(db2), _stream(w1, stream)))
     return dw1, db1, dw2, db2
+
+
+def _proj_dtype(x):
+    if x.dtype not in DTYPE:
+        raise ValueError("features must be bf16 or fp32")
+    return DTYPE[x.dtype]
+
+
+def swin_qkv_proj(x, w, b=None, *, out=None, stream=None):
+    """(q, k, v) = split(x w^T + b) of the attention branch's input layer:
+    x (..., C), w (3C, C) in x's dtype, b (3C) fp32 or None.  Returns three
+    tensors shaped like x (or fills out=(q, k, v))."""
+    C = x.shape[-1]
+    dt = _proj_dtype(x)
+    if w.dtype != x.dtype or tuple(w.shape) != (3 * C, C) or not (x.is_contiguous() and w.is_contiguous()):
+        raise ValueError("w must be a contiguous (3C, C) tensor of x's dtype; x contiguous")
+    if b is not None and (b.dtype != torch.float32 or tuple(b.shape) != (3 * C,) or not b.is_contiguous()):
+        raise ValueError("b must be contiguous fp32 of 3C")
+    q, k, v = out if out is not None else (torch.empty_like(x), torch.empty_like(x), torch.empty_like(x))
+    _check(lib().swin_qkv_proj(_ptr(x), _ptr(w), _ptr(b), _ptr(q), _ptr(k), _ptr(v), x.numel() // C, C, dt,
+                               _stream(x, stream)))
+    return q, k, v
+
+
+def swin_proj_post_norm(o, w, b, resid, gamma, beta, *, eps: float = 1e-5, out=None, stream=None):
+    """resid + layer_norm(o w^T + b) * gamma + beta over the channels: the
+    attention branch's output layer and residual post-norm.  o, resid (..., C)
+    and w (C, C) share a dtype; b (or None), gamma, beta are fp32 (C).
+    out may be resid itself."""
+    C = o.shape[-1]
+    dt = _proj_dtype(o)
+    if (w.dtype != o.dtype or resid.dtype != o.dtype or tuple(w.shape) != (C, C) or resid.shape != o.shape
+            or not (o.is_contiguous() and w.is_contiguous() and resid.is_contiguous())):
+        raise ValueError("o, resid (same shape) and w (C, C) must be contiguous and share a dtype")
+    for t in (b, gamma, beta):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (C,) or not t.is_contiguous()):
+            raise ValueError("b, gamma and beta must be contiguous fp32 of C")
+    y = out if out is not None else torch.empty_like(o)
+    _check(lib().swin_proj_post_norm(_ptr(o), _ptr(w), _ptr(b), _ptr(resid), _ptr(gamma), _ptr(beta), float(eps),
+                                     _ptr(y), o.numel() // C, C, dt, _stream(o, stream)))
+    return y
 
 
 def swin_window_attn_kernel(desc: SwinAttnDesc) -> str:

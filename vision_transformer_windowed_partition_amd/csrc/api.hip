@@ -1,6 +1,7 @@
 // C ABI of libswinattn.so (declared in include/swin_attn.h): argument
 // validation on the host, then one asynchronous launch on the caller's
 // stream.  Nothing is enqueued unless every argument passes.
+#include <math.h>
 #include <stdint.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -9,6 +10,7 @@
 
 #include "launch.hpp"
 #include "launch_bwd.hpp"
+#include "launch_proj.hpp"
 
 namespace {
 
@@ -262,6 +264,57 @@ int swin_window_attn_bwd(const swin_attn_desc* d, const void* q, const void* k, 
     p.tau = tau; p.table = table; p.rope_freqs = rope_freqs;
     return hip_status(swin::launch_attn_bwd(p, out, dout, dq, dk, dv, dtau, dtable, (hipStream_t)stream),
                       "swin_window_attn_bwd launch");
+}
+
+int swin_qkv_proj(const void* x, const void* w, const float* b, void* q, void* k, void* v, int64_t T,
+                  int32_t C, int32_t dtype, void* stream)
+{
+    if (dtype != SWIN_DT_F32 && dtype != SWIN_DT_BF16) return fail(SWIN_EINVAL, "unknown dtype %d", dtype);
+    if (T < 0 || C < 1) return fail(SWIN_EINVAL, "bad shape T=%lld C=%d", (long long)T, C);
+    if (!swin::proj_supported(C)) return fail(SWIN_EUNSUPPORTED, "C=%d: multiples of 32 up to 512 are built", C);
+    if (T > ((int64_t)1 << 40) / C) return fail(SWIN_EUNSUPPORTED, "T=%lld too large", (long long)T);
+    if (T == 0) return SWIN_OK;
+    if (!x || !w || !q || !k || !v) return fail(SWIN_EINVAL, "NULL x, w, q, k or v");
+    if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)b | (uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15)
+        return fail(SWIN_EINVAL, "x, w, b, q, k and v must be 16-byte aligned");
+    const size_t es = dtype == SWIN_DT_F32 ? 4 : 2;
+    const size_t nx = (size_t)T * C * es, nw = (size_t)3 * C * C * es, nb = b ? (size_t)3 * C * 4 : 0;
+    void* outs[3] = {q, k, v};
+    for (int i = 0; i < 3; ++i) {
+        if (overlaps(outs[i], nx, x, nx) || overlaps(outs[i], nx, w, nw) || (b && overlaps(outs[i], nx, b, nb)))
+            return fail(SWIN_EINVAL, "an output overlaps an input");
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], nx, outs[j], nx)) return fail(SWIN_EINVAL, "q, k and v overlap");
+    }
+    swin::ProjArgs a{};
+    a.x = x; a.w = w; a.b = b; a.q = q; a.k = k; a.v = v;
+    a.T = T; a.C = C; a.dtype = dtype;
+    return hip_status(swin::launch_qkv_proj(a, (hipStream_t)stream), "swin_qkv_proj launch");
+}
+
+int swin_proj_post_norm(const void* o, const void* w, const float* b, const void* resid, const float* gamma,
+                        const float* beta, float eps, void* y, int64_t T, int32_t C, int32_t dtype, void* stream)
+{
+    if (dtype != SWIN_DT_F32 && dtype != SWIN_DT_BF16) return fail(SWIN_EINVAL, "unknown dtype %d", dtype);
+    if (T < 0 || C < 1) return fail(SWIN_EINVAL, "bad shape T=%lld C=%d", (long long)T, C);
+    if (!(eps >= 0.0f) || eps == INFINITY) return fail(SWIN_EINVAL, "eps must be finite and >= 0");
+    if (!swin::proj_supported(C)) return fail(SWIN_EUNSUPPORTED, "C=%d: multiples of 32 up to 512 are built", C);
+    if (T > ((int64_t)1 << 40) / C) return fail(SWIN_EUNSUPPORTED, "T=%lld too large", (long long)T);
+    if (T == 0) return SWIN_OK;
+    if (!o || !w || !resid || !gamma || !beta || !y) return fail(SWIN_EINVAL, "NULL o, w, resid, gamma, beta or y");
+    if (((uintptr_t)o | (uintptr_t)w | (uintptr_t)b | (uintptr_t)resid | (uintptr_t)gamma | (uintptr_t)beta |
+         (uintptr_t)y) & 15)
+        return fail(SWIN_EINVAL, "o, w, b, resid, gamma, beta and y must be 16-byte aligned");
+    const size_t es = dtype == SWIN_DT_F32 ? 4 : 2;
+    const size_t nx = (size_t)T * C * es, nw = (size_t)C * C * es, nc = (size_t)C * 4;
+    if (overlaps(y, nx, o, nx) || overlaps(y, nx, w, nw) || (b && overlaps(y, nx, b, nc)) ||
+        overlaps(y, nx, gamma, nc) || overlaps(y, nx, beta, nc))
+        return fail(SWIN_EINVAL, "y overlaps an input other than resid");
+    if (y != resid && overlaps(y, nx, resid, nx)) return fail(SWIN_EINVAL, "y overlaps resid without equalling it");
+    swin::ProjArgs a{};
+    a.x = o; a.w = w; a.b = b; a.resid = resid; a.gamma = gamma; a.beta = beta; a.eps = eps; a.y = y;
+    a.T = T; a.C = C; a.dtype = dtype;
+    return hip_status(swin::launch_proj_norm(a, (hipStream_t)stream), "swin_proj_post_norm launch");
 }
 
 int swin_cpb_table_bwd(int32_t M, int32_t norm_M, int32_t heads, int32_t hidden, const float* w1,

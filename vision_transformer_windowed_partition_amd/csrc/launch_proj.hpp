@@ -1,0 +1,28 @@
+// Launch entry of the projection kernels (proj.hip), called by api.hip after
+// the host-side validation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swin {
+
+struct ProjArgs {
+    const void* x;             // QKV: input features; NORM: attention output o (T x C)
+    const void* w;             // QKV: 3C x C; NORM: C x C (output rows, input columns)
+    const float* b;            // bias per output row, or nullptr
+    void *q, *k, *v;           // QKV outputs (T x C each)
+    const void* resid;         // NORM: main path (T x C)
+    const float *gamma, *beta; // NORM: per-channel scale and shift (C)
+    float eps;                 // NORM: added to the variance inside the root
+    void* y;                   // NORM output (T x C); may equal resid
+    int64_t T;                 // tokens
+    int C;                     // channels
+    int dtype;                 // SWIN_DT_F32 or SWIN_DT_BF16
+};
+
+bool proj_supported(int C);
+hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t stream);
+hipError_t launch_proj_norm(const ProjArgs& a, hipStream_t stream);
+
+}  // namespace swin

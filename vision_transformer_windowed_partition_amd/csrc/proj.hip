@@ -1,0 +1,309 @@
+// The linear layers on either side of the window attention in a Swin V2
+// block (SwinV2 card, Method item 1 "Residual post-norm" and the block
+// pseudocode; the block keeps Swin's layout):
+//   QKV:  [q | k | v] = x W^T + b, W: 3C x C, outputs in that order, each
+//         written to its own (T, C) tensor in the grid layout the attention
+//         reads;
+//   NORM: y = resid + norm_1(o W^T + b), W: C x C, norm_1 a layer norm over
+//         the C channels of each token (biased variance, eps inside the
+//         root) with per-channel gamma and beta.
+//
+// bf16 path (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  A workgroup of
+// four wavefronts takes BT consecutive tokens, whose input rows form one
+// contiguous block: it copies them once into LDS (rows padded by 16 bytes so
+// that the 16 rows one fragment read touches fall in distinct banks).  The
+// products are taken transposed, out^T = W x^T: the A operand is 16 weight
+// rows (output channels), read from global memory where every workgroup
+// finds them in L2, and the B operand is 16 staged token rows, so each lane
+// ends with 4 consecutive output channels of one token and stores 8 bytes.
+// The wavefronts split the 16-channel output tiles; each weight fragment
+// serves all BT / 16 token tiles.
+//   QKV adds the bias and rounds once.  NORM keeps its tiles in registers,
+//   reduces each token's sum and then its sum of squared deviations across
+//   lanes and wavefronts (two passes, exact), and writes
+//   resid + gamma (z - mean) / sqrt(var + eps) + beta, rounded once.
+//
+// fp32 path: one thread per output (QKV), one wavefront per token (NORM),
+// fp32 throughout.
+#include "common.hpp"
+#include "lanes.hpp"
+#include "launch_proj.hpp"
+#include "tile_io.hpp"
+
+namespace swin {
+
+namespace {
+
+using namespace lanes;
+using namespace tio;
+
+constexpr int PW = 4;                  // wavefronts per workgroup
+constexpr int PAD = 8;                 // bf16 elements of padding per staged row
+
+__device__ __forceinline__ void stage_rows(const __bf16* src, __bf16* xs, int C, int rows, int nt, int tid)
+{
+    const int per_row = C / 8;                        // 16-byte pieces
+    const int RS = C + PAD;
+    for (int i = tid; i < rows * per_row; i += PW * 64) {
+        const int r = i / per_row, c8 = i - r * per_row;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (r < nt) v = *(const u32x4*)(src + (size_t)r * C + 8 * c8);
+        *(u32x4*)(xs + r * RS + 8 * c8) = v;
+    }
+}
+
+// [q | k | v] = x W^T + b for BT tokens per workgroup.
+template <int BT>
+__global__ void __launch_bounds__(PW * 64) qkv_kernel(ProjArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    constexpr int RT = BT / 16;                       // token tiles
+    const int C = a.C, RS = C + PAD;
+    __bf16* xs = (__bf16*)smem;                       // [BT][RS]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = lane >> 4, li = lane & 15;
+    const int64_t t0 = (int64_t)blockIdx.x * BT;
+    const int nt = (int)min((int64_t)BT, a.T - t0);
+    stage_rows((const __bf16*)a.x + t0 * C, xs, C, BT, nt, tid);
+    __syncthreads();
+
+    const int ks = C / 32;
+    const int ntile = 3 * C / 16;
+    for (int n = wave; n < ntile; n += PW) {
+        f32x4 acc[RT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) acc[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const __bf16* wrow = (const __bf16*)a.w + (size_t)(16 * n + li) * C + 8 * grp;
+        for (int s = 0; s < ks; ++s) {
+            const bf16x8 A = *(const bf16x8*)(wrow + 32 * s);
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const bf16x8 B = *(const bf16x8*)(xs + (16 * r + li) * RS + 32 * s + 8 * grp);
+                acc[r] = mfma(A, B, acc[r]);
+            }
+        }
+        // lane holds channels 16n + 4grp .. +3 of tokens 16r + li
+        const int ch = 16 * n + 4 * grp;              // in [0, 3C)
+        const int which = ch / C, c = ch - which * C;
+        __bf16* dst = (__bf16*)(which == 0 ? a.q : which == 1 ? a.k : a.v);
+        const f32x4 bias = a.b ? *(const f32x4*)(a.b + ch) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const int t = 16 * r + li;
+            if (t < nt)
+                *(bf16x4*)(dst + (size_t)(t0 + t) * C + c) =
+                    pack_bf16x4(acc[r][0] + bias[0], acc[r][1] + bias[1], acc[r][2] + bias[2], acc[r][3] + bias[3]);
+        }
+    }
+}
+
+// y = resid + norm_1(o W^T + b) for BT tokens per workgroup; NTW bounds the
+// 16-channel tiles a wavefront holds (C <= 64 NTW).
+template <int BT, int NTW>
+__global__ void __launch_bounds__(PW * 64) norm_kernel(ProjArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    constexpr int RT = BT / 16;
+    const int C = a.C, RS = C + PAD;
+    __bf16* xs = (__bf16*)smem;                       // [BT][RS]
+    float* red = (float*)(smem + (size_t)BT * RS * 2);   // [PW][BT] per-wave partial sums
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = lane >> 4, li = lane & 15;
+    const int64_t t0 = (int64_t)blockIdx.x * BT;
+    const int nt = (int)min((int64_t)BT, a.T - t0);
+    stage_rows((const __bf16*)a.x + t0 * C, xs, C, BT, nt, tid);
+    __syncthreads();
+
+    const int ks = C / 32;
+    const int ntile = C / 16;
+    f32x4 z[NTW][RT];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+        const int n = wave + PW * j;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) z[j][r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (n >= ntile) continue;                     // wave-uniform
+        const __bf16* wrow = (const __bf16*)a.w + (size_t)(16 * n + li) * C + 8 * grp;
+        for (int s = 0; s < ks; ++s) {
+            const bf16x8 A = *(const bf16x8*)(wrow + 32 * s);
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const bf16x8 B = *(const bf16x8*)(xs + (16 * r + li) * RS + 32 * s + 8 * grp);
+                z[j][r] = mfma(A, B, z[j][r]);
+            }
+        }
+        const f32x4 bias = a.b ? *(const f32x4*)(a.b + 16 * n + 4 * grp) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int r = 0; r < RT; ++r) z[j][r] += bias;
+    }
+
+    // per-token sums over this lane's channels, then over the 4 lanes of a
+    // token (lanes li + 16 grp) and the 4 wavefronts
+    auto token_sum = [&](float (&part)[RT], float (&out)[RT]) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const float s = sum_x32(sum_x16(part[r]));
+            if (grp == 0) red[wave * BT + 16 * r + li] = s;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            float s = 0.0f;
+#pragma unroll
+            for (int w = 0; w < PW; ++w) s += red[w * BT + 16 * r + li];
+            out[r] = s;
+        }
+        __syncthreads();                              // red is reused
+    };
+    float part[RT], mean[RT], var[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        float s = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+            if (wave + PW * j < ntile) s += (z[j][r][0] + z[j][r][1]) + (z[j][r][2] + z[j][r][3]);
+        part[r] = s;
+    }
+    token_sum(part, mean);
+    const float inv_c = 1.0f / (float)C;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        mean[r] *= inv_c;
+        float s = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+            if (wave + PW * j < ntile) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float dz = z[j][r][e] - mean[r];
+                    s = fmaf(dz, dz, s);
+                }
+            }
+        part[r] = s;
+    }
+    token_sum(part, var);
+    float rstd[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) rstd[r] = 1.0f / sqrtf(fmaf(var[r], inv_c, a.eps));
+
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+        const int n = wave + PW * j;
+        if (n >= ntile) continue;
+        const int ch = 16 * n + 4 * grp;
+        const f32x4 g = *(const f32x4*)(a.gamma + ch);
+        const f32x4 be = *(const f32x4*)(a.beta + ch);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const int t = 16 * r + li;
+            if (t >= nt) continue;
+            const size_t off = (size_t)(t0 + t) * C + ch;
+            const u32x2 rw = *(const u32x2*)((const __bf16*)a.resid + off);
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t h = (e & 1) ? (rw[e >> 1] & 0xffff0000u) : (rw[e >> 1] << 16);
+                y[e] = __uint_as_float(h) + fmaf(g[e], (z[j][r][e] - mean[r]) * rstd[r], be[e]);
+            }
+            *(bf16x4*)((__bf16*)a.y + off) = pack_bf16x4(y[0], y[1], y[2], y[3]);
+        }
+    }
+}
+
+// fp32: one thread per output of [q | k | v].
+__global__ void __launch_bounds__(256) qkv_f32_kernel(ProjArgs a)
+{
+    const int C = a.C, C3 = 3 * C;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= a.T * C3) return;
+    const int64_t t = i / C3;
+    const int n = (int)(i - t * C3);
+    const float* x = (const float*)a.x + t * C;
+    const float* w = (const float*)a.w + (size_t)n * C;
+    float s = a.b ? a.b[n] : 0.0f;
+    for (int c = 0; c < C; ++c) s = fmaf(x[c], w[c], s);
+    const int which = n / C;
+    float* dst = (float*)(which == 0 ? a.q : which == 1 ? a.k : a.v);
+    dst[t * C + (n - which * C)] = s;
+}
+
+// fp32: one wavefront per token; z staged in LDS for the two passes.
+__global__ void __launch_bounds__(64) norm_f32_kernel(ProjArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    float* zs = (float*)smem;                         // [C]
+    const int C = a.C, lane = threadIdx.x;
+    const int64_t t = blockIdx.x;
+    const float* x = (const float*)a.x + t * C;
+    for (int n = lane; n < C; n += 64) {
+        const float* w = (const float*)a.w + (size_t)n * C;
+        float s = a.b ? a.b[n] : 0.0f;
+        for (int c = 0; c < C; ++c) s = fmaf(x[c], w[c], s);
+        zs[n] = s;
+    }
+    float s = 0.0f;
+    for (int n = lane; n < C; n += 64) s += zs[n];
+    const float mean = wave_reduce<Op::Sum>(s) / (float)C;
+    float q = 0.0f;
+    for (int n = lane; n < C; n += 64) q = fmaf(zs[n] - mean, zs[n] - mean, q);
+    const float rstd = 1.0f / sqrtf(wave_reduce<Op::Sum>(q) / (float)C + a.eps);
+    const float* res = (const float*)a.resid + t * C;
+    float* y = (float*)a.y + t * C;
+    for (int n = lane; n < C; n += 64) y[n] = res[n] + fmaf(a.gamma[n], (zs[n] - mean) * rstd, a.beta[n]);
+}
+
+template <typename K>
+hipError_t launch(K kernel, int64_t blocks, int threads, size_t lds, const ProjArgs& a, hipStream_t s)
+{
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    kernel<<<(int)blocks, threads, lds, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int BT>
+hipError_t launch_norm_bt(const ProjArgs& a, hipStream_t s)
+{
+    const size_t lds = (size_t)BT * (a.C + PAD) * 2 + (size_t)PW * BT * sizeof(float);
+    const int64_t blocks = (a.T + BT - 1) / BT;
+    switch ((a.C + 63) / 64) {                        // 16-channel tiles per wavefront
+    case 1: return launch(norm_kernel<BT, 1>, blocks, PW * 64, lds, a, s);
+    case 2: return launch(norm_kernel<BT, 2>, blocks, PW * 64, lds, a, s);
+    case 3: return launch(norm_kernel<BT, 3>, blocks, PW * 64, lds, a, s);
+    case 4: return launch(norm_kernel<BT, 4>, blocks, PW * 64, lds, a, s);
+    case 5: return launch(norm_kernel<BT, 5>, blocks, PW * 64, lds, a, s);
+    case 6: return launch(norm_kernel<BT, 6>, blocks, PW * 64, lds, a, s);
+    case 7: return launch(norm_kernel<BT, 7>, blocks, PW * 64, lds, a, s);
+    default: return launch(norm_kernel<BT, 8>, blocks, PW * 64, lds, a, s);
+    }
+}
+
+}  // namespace
+
+bool proj_supported(int C) { return C >= 32 && C <= 512 && C % 32 == 0; }
+
+hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t stream)
+{
+    if (a.T == 0) return hipSuccess;
+    if (a.dtype == SWIN_DT_F32)
+        return launch(qkv_f32_kernel, (a.T * 3 * a.C + 255) / 256, 256, 0, a, stream);
+    constexpr int BT = 64;
+    const size_t lds = (size_t)BT * (a.C + PAD) * 2;
+    return launch(qkv_kernel<BT>, (a.T + BT - 1) / BT, PW * 64, lds, a, stream);
+}
+
+hipError_t launch_proj_norm(const ProjArgs& a, hipStream_t stream)
+{
+    if (a.T == 0) return hipSuccess;
+    if (a.dtype == SWIN_DT_F32)
+        return launch(norm_f32_kernel, a.T, 64, (size_t)a.C * sizeof(float), a, stream);
+    // at most 64 fp32 registers of z per lane: 64 tokens up to C = 256
+    return a.C <= 256 ? launch_norm_bt<64>(a, stream) : launch_norm_bt<32>(a, stream);
+}
+
+}  // namespace swin

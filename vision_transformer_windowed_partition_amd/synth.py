@@ -129,6 +129,29 @@ def make_dout(wl: Workload, seed: int = 1000):
     return d.to(torch_dtype(wl.dtype))
 
 
+def make_branch_params(wl: Workload, seed: int = 2000, T: int | None = None) -> dict:
+    """Inputs of the attention branch's linear layers and post-norm, drawn in
+    this order (CPU, fp32): x (T, C) features, o (T, C) attention output,
+    w_qkv (3C, C) and w_proj (C, C) each randn / sqrt(C), b_qkv (3C) and
+    b_proj (C) each 0.1 randn, gamma = 1 + 0.1 randn (C), beta = 0.1 randn (C).
+    x, o and the weights are rounded to the workload dtype; the biases, gamma
+    and beta stay fp32.  T defaults to the workload's B H W tokens."""
+    g = torch.Generator().manual_seed(int(seed))
+    C = wl.C
+    T = wl.B * wl.H * wl.W if T is None else int(T)
+    dt = torch_dtype(wl.dtype)
+    x = torch.randn((T, C), generator=g)
+    o = torch.randn((T, C), generator=g)
+    w_qkv = torch.randn((3 * C, C), generator=g) / math.sqrt(C)
+    w_proj = torch.randn((C, C), generator=g) / math.sqrt(C)
+    b_qkv = 0.1 * torch.randn(3 * C, generator=g)
+    b_proj = 0.1 * torch.randn(C, generator=g)
+    gamma = 1.0 + 0.1 * torch.randn(C, generator=g)
+    beta = 0.1 * torch.randn(C, generator=g)
+    return dict(x=x.to(dt), o=o.to(dt), w_qkv=w_qkv.to(dt), w_proj=w_proj.to(dt), b_qkv=b_qkv, b_proj=b_proj,
+                gamma=gamma, beta=beta)
+
+
 def small(name: str = "tiny", *, B=2, H=16, W=16, C=64, heads=2, M=8, shift=4,
           partition="cyclic", sim="cosine", pos="table", dtype="f32", hidden=64) -> Workload:
     """A small workload for tests (same draw recipe)."""

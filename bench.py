@@ -16,6 +16,10 @@ hipEventDisableSystemFence (timing only), so recording them adds no cache
 writeback or invalidation to the interval.
 
 Prints ONE JSON line.  `value` is tokens/s over the whole job.
+
+Other modes (same protocol, their own JSON line): --backward times the
+backward step; --branch times the attention branch of a block (input
+projection, table, attention, output projection with the residual post-norm).
 """
 from __future__ import annotations
 
@@ -159,6 +163,9 @@ def main(argv=None) -> int:
     ap.add_argument("--backward", action="store_true",
                     help="time the backward step instead: swin_window_attn_bwd (dq, dk, dv, dtau, dtable) "
                          "and swin_cpb_table_bwd, from one forward's output")
+    ap.add_argument("--branch", action="store_true",
+                    help="time the whole attention branch instead: swin_qkv_proj, the CPB table, "
+                         "swin_window_attn_fwd and swin_proj_post_norm (residual post-norm)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run copies of known size for HBM-counter calibration: y = -x over "
                          "2^28 fp32 (whole lines), then an interleaved window gather and its "
@@ -196,6 +203,9 @@ def main(argv=None) -> int:
     kernel = binding.swin_window_attn_kernel(desc)
     if args.backward:
         return bench_backward(args, wl, x, sets, nsets, par, table, desc, stream)
+    if args.branch:
+        del sets
+        return bench_branch(args, wl, par, table, desc, stream)
 
     def step(i, timed=None):
         q, k, v, o = sets[i % nsets]
@@ -376,6 +386,118 @@ def bench_backward(args, wl, x, sets, nsets, par, table, desc, stream) -> int:
         "tflops": round(tflops, 2),
         "hbm_gbs": round(alg_bytes / kern_s / 1e9, 1),
         "roofline": roof,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+def _roof(flops: float, alg_bytes: float, ms: float, peak_tf: float, compute: str) -> dict:
+    """Roofline entry of one kernel: HBM if its arithmetic intensity is below
+    the ridge of its compute unit, else that unit."""
+    s = ms * 1e-3
+    if flops / alg_bytes < peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9):
+        gbs = alg_bytes / s / 1e9
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    tf = flops / s / 1e12
+    return {"bound": compute, "achieved": round(tf, 2), "peak": peak_tf, "unit": "TFLOP/s",
+            "frac": round(tf / peak_tf, 4)}
+
+
+def bench_branch(args, wl, par, table, desc, stream) -> int:
+    """Attention branch step of a Swin V2 block: q, k, v = split(x W_qkv^T +
+    b), the CPB table, the window attention, y = x + norm_1(o W_proj^T + b).
+    Algorithmic work: QKV 6 T C^2 flops and 4 T C es bytes (read x, write q,
+    k, v); attention as the forward; output layer 2 T C^2 flops and 3 T C es
+    bytes (read o and x, write y); weights counted once."""
+    import torch
+
+    from vision_transformer_windowed_partition_amd import binding, synth
+
+    dev = torch.device("cuda:0")
+    p = synth.make_branch_params(wl)
+    w = {n: p[n].to(dev) for n in ("w_qkv", "b_qkv", "w_proj", "b_proj", "gamma", "beta")}
+    T, C, es = wl.tokens, wl.C, wl.elem_size
+    set_bytes = 6 * T * C * es
+    nsets = 1 if args.warm else max(2, math.ceil(2 * MALL_BYTES / set_bytes) + 1)
+    x0 = p["x"].to(dev).reshape(wl.B, wl.H, wl.W, C)
+    sets = []
+    for i in range(nsets):
+        xs = x0 if i == 0 else x0.clone()
+        sets.append(dict(x=xs, q=torch.empty_like(xs), k=torch.empty_like(xs), v=torch.empty_like(xs),
+                         o=torch.empty_like(xs), y=torch.empty_like(xs)))
+    names = ("qkv", "attn", "norm")
+
+    def step(i, timed=None):
+        st = sets[i % nsets]
+        rec = (lambda n, end: timers[n].record(timed, end)) if timed is not None else (lambda n, end: None)
+        rec("qkv", False)
+        binding.swin_qkv_proj(st["x"], w["w_qkv"], w["b_qkv"], out=(st["q"], st["k"], st["v"]), stream=stream)
+        rec("qkv", True)
+        tab = None
+        if wl.pos == "table":
+            tab = binding.swin_cpb_table(wl.M, par["w1"], par["b1"], par["w2"], par["b2"], out=table,
+                                         stream=stream)
+        rec("attn", False)
+        binding.swin_window_attn_fwd(st["q"], st["k"], st["v"], heads=wl.heads, M=wl.M, desc=desc,
+                                     tau=par["tau"], table=tab, out=st["o"], stream=stream)
+        rec("attn", True)
+        rec("norm", False)
+        binding.swin_proj_post_norm(st["o"], w["w_proj"], w["b_proj"], st["x"], w["gamma"], w["beta"], eps=1e-5,
+                                    out=st["y"], stream=stream)
+        rec("norm", True)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    timers = {n: HipTimer(args.steps, stream.cuda_stream) for n in names}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {}
+    for n in names:
+        e = timers[n].elapsed_ms()
+        timers[n].close()
+        ms[n] = sum(e) / len(e)
+    peak_tf = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+    compute = "mfma" if wl.dtype == "bf16" else "alu"
+    work = {"qkv": (6.0 * T * C * C, 4.0 * T * C * es),
+            "attn": (float(wl.flops), float(wl.bytes)),
+            "norm": (2.0 * T * C * C, 3.0 * T * C * es)}
+    kname = {"qkv": "qkv_kernel" if wl.dtype == "bf16" else "qkv_f32_kernel",
+             "attn": binding.swin_window_attn_kernel(desc),
+             "norm": "norm_kernel" if wl.dtype == "bf16" else "norm_f32_kernel"}
+    kernels = {}
+    for n in names:
+        r = _roof(work[n][0], work[n][1], ms[n], peak_tf, compute)
+        r.update({"kernel": kname[n], "kernel_ms": round(ms[n], 5), "alg_flops_per_launch": work[n][0],
+                  "alg_bytes_per_launch": work[n][1], "traffic": None})
+        kernels[n] = r
+    dominant = max(names, key=lambda n: ms[n])
+    out = {
+        "metric": "attention branch tokens/s (QKV projection, CPB table, window attention, "
+                  "output projection + residual post-norm)",
+        "value": round(T / (wall / args.steps), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) features, randn/sqrt(C) weights, random-init log-CPB MLP)",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "W": wl.W, "C": wl.C, "heads": wl.heads,
+                   "M": wl.M, "shift": wl.shift, "partition": wl.partition, "sim": wl.sim, "pos": wl.pos,
+                   "pass": "attention branch",
+                   "cache": "warm" if args.warm else f"cold ({nsets} rotating sets)",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": kernels[dominant],
+        "kernels": kernels,
     }
     print(json.dumps(out))
     return 0

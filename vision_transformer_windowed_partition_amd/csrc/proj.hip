@@ -38,102 +38,149 @@ using namespace lanes;
 using namespace tio;
 
 constexpr int PW = 4;                  // wavefronts per workgroup
-constexpr int PAD = 8;                 // bf16 elements of padding per staged row
+constexpr int BT = 64;                 // tokens per workgroup
+constexpr int RT = BT / 16;            // token tiles
+constexpr int KC = 32;                 // input channels per staged slice
 
-__device__ __forceinline__ void stage_rows(const __bf16* src, __bf16* xs, int C, int rows, int nt, int tid)
+// LDS slot of the 16-byte piece p of staged row r (64-byte rows): the piece
+// index is XOR-ed with bits 2-3 of the row, so the 16 rows one fragment read
+// touches cover all 64 banks.
+__device__ __forceinline__ int slot(int r, int p) { return r * KC + 8 * (p ^ ((r >> 2) & 3)); }
+
+// two stages of bf16 slices: BT token rows and up to 64 NTW weight rows
+template <int NTW>
+constexpr size_t pass_lds() { return (size_t)2 * (BT + PW * NTW * 16) * KC * 2; }
+
+// Output tiles of one pass: the product of the workgroup's token rows with
+// the weight rows n0 .. n0 + nb - 1 (nb a multiple of 16, at most 64 NTW), the
+// input channels taken KC at a time.  Both operand slices go through LDS in
+// two stages: while one is read by the matrix cores, the next one's global
+// loads are in flight.  Wavefront w holds output tiles w + PW j (j < NTW) of
+// the pass for all BT tokens: z[j][r] is tokens 16r + li, channels
+// n0 + 16 (w + PW j) + 4 grp .. +3.
+template <int NTW>
+__device__ __forceinline__ void pass_product(const __bf16* x, int nt, const __bf16* w, int C, int n0, int nb,
+                                             __bf16* lds, f32x4 (&z)[NTW][RT], int tid, int wave, int lane)
 {
-    const int per_row = C / 8;                        // 16-byte pieces
-    const int RS = C + PAD;
-    for (int i = tid; i < rows * per_row; i += PW * 64) {
-        const int r = i / per_row, c8 = i - r * per_row;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (r < nt) v = *(const u32x4*)(src + (size_t)r * C + 8 * c8);
-        *(u32x4*)(xs + r * RS + 8 * c8) = v;
+    constexpr int NP = PW * NTW * 16;                     // weight rows per stage
+    const int grp = lane >> 4, li = lane & 15;
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int r = 0; r < RT; ++r) z[j][r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int XP = BT * 4 / (PW * 64);                // x pieces per thread
+    constexpr int WP = NP * 4 / (PW * 64);                // weight pieces per thread, at most
+    u32x4 xr[XP], wr[WP];
+    auto load = [&](int s) {
+#pragma unroll
+        for (int m = 0; m < XP; ++m) {
+            const int i = tid + PW * 64 * m, r = i >> 2, p = i & 3;
+            xr[m] = r < nt ? *(const u32x4*)(x + (size_t)r * C + KC * s + 8 * p) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int m = 0; m < WP; ++m) {
+            const int i = tid + PW * 64 * m, r = i >> 2, p = i & 3;
+            if (r < nb) wr[m] = *(const u32x4*)(w + (size_t)(n0 + r) * C + KC * s + 8 * p);
+        }
+    };
+    auto store = [&](__bf16* sx) {                        // stage: x rows, then weight rows
+        __bf16* sw = sx + BT * KC;
+#pragma unroll
+        for (int m = 0; m < XP; ++m) {
+            const int i = tid + PW * 64 * m;
+            *(u32x4*)(sx + slot(i >> 2, i & 3)) = xr[m];
+        }
+#pragma unroll
+        for (int m = 0; m < WP; ++m) {
+            const int i = tid + PW * 64 * m, r = i >> 2;
+            if (r < nb) *(u32x4*)(sw + slot(r, i & 3)) = wr[m];
+        }
+    };
+    const int ks = C / KC;
+    load(0);
+    store(lds);
+    __syncthreads();
+    for (int s = 0; s < ks; ++s) {
+        if (s + 1 < ks) load(s + 1);
+        const __bf16* sx = lds + (s & 1) * (BT + NP) * KC;
+        const __bf16* sw = sx + BT * KC;
+        bf16x8 B[RT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) B[r] = *(const bf16x8*)(sx + slot(16 * r + li, grp));
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+            const int m = wave + PW * j;                  // output tile within the pass
+            if (16 * m >= nb) break;                      // wave-uniform
+            const bf16x8 A = *(const bf16x8*)(sw + slot(16 * m + li, grp));
+#pragma unroll
+            for (int r = 0; r < RT; ++r) z[j][r] = mfma(A, B[r], z[j][r]);
+        }
+        if (s + 1 < ks) store(lds + ((s + 1) & 1) * (BT + NP) * KC);
+        __syncthreads();
     }
 }
 
-// [q | k | v] = x W^T + b for BT tokens per workgroup.
-template <int BT>
+// [q | k | v] = x W^T + b: 64 tokens per workgroup, output channels in
+// passes of up to 64 NTW.
+template <int NTW>
 __global__ void __launch_bounds__(PW * 64) qkv_kernel(ProjArgs a)
 {
+    constexpr int NP = PW * NTW * 16;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    constexpr int RT = BT / 16;                       // token tiles
-    const int C = a.C, RS = C + PAD;
-    __bf16* xs = (__bf16*)smem;                       // [BT][RS]
+    const int C = a.C;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = lane >> 4, li = lane & 15;
     const int64_t t0 = (int64_t)blockIdx.x * BT;
     const int nt = (int)min((int64_t)BT, a.T - t0);
-    stage_rows((const __bf16*)a.x + t0 * C, xs, C, BT, nt, tid);
-    __syncthreads();
-
-    const int ks = C / 32;
-    const int ntile = 3 * C / 16;
-    for (int n = wave; n < ntile; n += PW) {
-        f32x4 acc[RT];
+    const __bf16* x = (const __bf16*)a.x + t0 * C;
+#pragma unroll 1
+    for (int n0 = 0; n0 < 3 * C; n0 += NP) {
+        const int nb = min(NP, 3 * C - n0);
+        f32x4 z[NTW][RT];
+        pass_product<NTW>(x, nt, (const __bf16*)a.w, C, n0, nb, (__bf16*)smem, z, tid, wave, lane);
 #pragma unroll
-        for (int r = 0; r < RT; ++r) acc[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        const __bf16* wrow = (const __bf16*)a.w + (size_t)(16 * n + li) * C + 8 * grp;
-        for (int s = 0; s < ks; ++s) {
-            const bf16x8 A = *(const bf16x8*)(wrow + 32 * s);
+        for (int j = 0; j < NTW; ++j) {
+            const int m = wave + PW * j;
+            if (16 * m >= nb) break;
+            // lane holds channels ch .. ch+3 of tokens 16r + li
+            const int ch = n0 + 16 * m + 4 * grp;         // in [0, 3C)
+            const int which = ch / C, c = ch - which * C;
+            __bf16* dst = (__bf16*)(which == 0 ? a.q : which == 1 ? a.k : a.v);
+            const f32x4 bias = a.b ? *(const f32x4*)(a.b + ch) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
-                const bf16x8 B = *(const bf16x8*)(xs + (16 * r + li) * RS + 32 * s + 8 * grp);
-                acc[r] = mfma(A, B, acc[r]);
+                const int t = 16 * r + li;
+                if (t < nt)
+                    *(bf16x4*)(dst + (size_t)(t0 + t) * C + c) =
+                        pack_bf16x4(z[j][r][0] + bias[0], z[j][r][1] + bias[1], z[j][r][2] + bias[2],
+                                    z[j][r][3] + bias[3]);
             }
-        }
-        // lane holds channels 16n + 4grp .. +3 of tokens 16r + li
-        const int ch = 16 * n + 4 * grp;              // in [0, 3C)
-        const int which = ch / C, c = ch - which * C;
-        __bf16* dst = (__bf16*)(which == 0 ? a.q : which == 1 ? a.k : a.v);
-        const f32x4 bias = a.b ? *(const f32x4*)(a.b + ch) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int r = 0; r < RT; ++r) {
-            const int t = 16 * r + li;
-            if (t < nt)
-                *(bf16x4*)(dst + (size_t)(t0 + t) * C + c) =
-                    pack_bf16x4(acc[r][0] + bias[0], acc[r][1] + bias[1], acc[r][2] + bias[2], acc[r][3] + bias[3]);
         }
     }
 }
 
-// y = resid + norm_1(o W^T + b) for BT tokens per workgroup; NTW bounds the
-// 16-channel tiles a wavefront holds (C <= 64 NTW).
-template <int BT, int NTW>
+// y = resid + norm_1(o W^T + b): 64 tokens per workgroup, all C <= 64 NTW
+// output channels in one pass, held in registers through the norm.
+template <int NTW>
 __global__ void __launch_bounds__(PW * 64) norm_kernel(ProjArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    constexpr int RT = BT / 16;
-    const int C = a.C, RS = C + PAD;
-    __bf16* xs = (__bf16*)smem;                       // [BT][RS]
-    float* red = (float*)(smem + (size_t)BT * RS * 2);   // [PW][BT] per-wave partial sums
+    const int C = a.C;
+    float* red = (float*)(smem + pass_lds<NTW>());        // [PW][BT] per-wave partial sums
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = lane >> 4, li = lane & 15;
     const int64_t t0 = (int64_t)blockIdx.x * BT;
     const int nt = (int)min((int64_t)BT, a.T - t0);
-    stage_rows((const __bf16*)a.x + t0 * C, xs, C, BT, nt, tid);
-    __syncthreads();
-
-    const int ks = C / 32;
-    const int ntile = C / 16;
     f32x4 z[NTW][RT];
+    pass_product<NTW>((const __bf16*)a.x + t0 * C, nt, (const __bf16*)a.w, C, 0, C, (__bf16*)smem, z, tid, wave,
+                      lane);
+    const int ntile = C / 16;
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
         const int n = wave + PW * j;
-#pragma unroll
-        for (int r = 0; r < RT; ++r) z[j][r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        if (n >= ntile) continue;                     // wave-uniform
-        const __bf16* wrow = (const __bf16*)a.w + (size_t)(16 * n + li) * C + 8 * grp;
-        for (int s = 0; s < ks; ++s) {
-            const bf16x8 A = *(const bf16x8*)(wrow + 32 * s);
-#pragma unroll
-            for (int r = 0; r < RT; ++r) {
-                const bf16x8 B = *(const bf16x8*)(xs + (16 * r + li) * RS + 32 * s + 8 * grp);
-                z[j][r] = mfma(A, B, z[j][r]);
-            }
-        }
+        if (n >= ntile) break;
         const f32x4 bias = a.b ? *(const f32x4*)(a.b + 16 * n + 4 * grp) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int r = 0; r < RT; ++r) z[j][r] += bias;
@@ -155,7 +202,7 @@ __global__ void __launch_bounds__(PW * 64) norm_kernel(ProjArgs a)
             for (int w = 0; w < PW; ++w) s += red[w * BT + 16 * r + li];
             out[r] = s;
         }
-        __syncthreads();                              // red is reused
+        __syncthreads();                                  // red is reused
     };
     float part[RT], mean[RT], var[RT];
 #pragma unroll
@@ -191,7 +238,7 @@ __global__ void __launch_bounds__(PW * 64) norm_kernel(ProjArgs a)
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
         const int n = wave + PW * j;
-        if (n >= ntile) continue;
+        if (n >= ntile) break;
         const int ch = 16 * n + 4 * grp;
         const f32x4 g = *(const f32x4*)(a.gamma + ch);
         const f32x4 be = *(const f32x4*)(a.beta + ch);
@@ -266,23 +313,6 @@ hipError_t launch(K kernel, int64_t blocks, int threads, size_t lds, const ProjA
     return hipGetLastError();
 }
 
-template <int BT>
-hipError_t launch_norm_bt(const ProjArgs& a, hipStream_t s)
-{
-    const size_t lds = (size_t)BT * (a.C + PAD) * 2 + (size_t)PW * BT * sizeof(float);
-    const int64_t blocks = (a.T + BT - 1) / BT;
-    switch ((a.C + 63) / 64) {                        // 16-channel tiles per wavefront
-    case 1: return launch(norm_kernel<BT, 1>, blocks, PW * 64, lds, a, s);
-    case 2: return launch(norm_kernel<BT, 2>, blocks, PW * 64, lds, a, s);
-    case 3: return launch(norm_kernel<BT, 3>, blocks, PW * 64, lds, a, s);
-    case 4: return launch(norm_kernel<BT, 4>, blocks, PW * 64, lds, a, s);
-    case 5: return launch(norm_kernel<BT, 5>, blocks, PW * 64, lds, a, s);
-    case 6: return launch(norm_kernel<BT, 6>, blocks, PW * 64, lds, a, s);
-    case 7: return launch(norm_kernel<BT, 7>, blocks, PW * 64, lds, a, s);
-    default: return launch(norm_kernel<BT, 8>, blocks, PW * 64, lds, a, s);
-    }
-}
-
 }  // namespace
 
 bool proj_supported(int C) { return C >= 32 && C <= 512 && C % 32 == 0; }
@@ -292,9 +322,10 @@ hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t stream)
     if (a.T == 0) return hipSuccess;
     if (a.dtype == SWIN_DT_F32)
         return launch(qkv_f32_kernel, (a.T * 3 * a.C + 255) / 256, 256, 0, a, stream);
-    constexpr int BT = 64;
-    const size_t lds = (size_t)BT * (a.C + PAD) * 2;
-    return launch(qkv_kernel<BT>, (a.T + BT - 1) / BT, PW * 64, lds, a, stream);
+    const int64_t blocks = (a.T + BT - 1) / BT;
+    // one pass when 3C fits 5 tiles per wavefront, else passes of 4
+    if (3 * a.C <= PW * 5 * 16) return launch(qkv_kernel<5>, blocks, PW * 64, pass_lds<5>(), a, stream);
+    return launch(qkv_kernel<4>, blocks, PW * 64, pass_lds<4>(), a, stream);
 }
 
 hipError_t launch_proj_norm(const ProjArgs& a, hipStream_t stream)
@@ -302,8 +333,18 @@ hipError_t launch_proj_norm(const ProjArgs& a, hipStream_t stream)
     if (a.T == 0) return hipSuccess;
     if (a.dtype == SWIN_DT_F32)
         return launch(norm_f32_kernel, a.T, 64, (size_t)a.C * sizeof(float), a, stream);
-    // at most 64 fp32 registers of z per lane: 64 tokens up to C = 256
-    return a.C <= 256 ? launch_norm_bt<64>(a, stream) : launch_norm_bt<32>(a, stream);
+    const int64_t blocks = (a.T + BT - 1) / BT;
+    const size_t red = (size_t)PW * BT * sizeof(float);
+    switch ((a.C + 63) / 64) {                            // 16-channel tiles per wavefront
+    case 1: return launch(norm_kernel<1>, blocks, PW * 64, pass_lds<1>() + red, a, stream);
+    case 2: return launch(norm_kernel<2>, blocks, PW * 64, pass_lds<2>() + red, a, stream);
+    case 3: return launch(norm_kernel<3>, blocks, PW * 64, pass_lds<3>() + red, a, stream);
+    case 4: return launch(norm_kernel<4>, blocks, PW * 64, pass_lds<4>() + red, a, stream);
+    case 5: return launch(norm_kernel<5>, blocks, PW * 64, pass_lds<5>() + red, a, stream);
+    case 6: return launch(norm_kernel<6>, blocks, PW * 64, pass_lds<6>() + red, a, stream);
+    case 7: return launch(norm_kernel<7>, blocks, PW * 64, pass_lds<7>() + red, a, stream);
+    default: return launch(norm_kernel<8>, blocks, PW * 64, pass_lds<8>() + red, a, stream);
+    }
 }
 
 }  // namespace swin

@@ -9,18 +9,23 @@
 //         root) with per-channel gamma and beta.
 //
 // bf16 path (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  A workgroup of
-// four wavefronts takes BT consecutive tokens, whose input rows form one
-// contiguous block: it copies them once into LDS (rows padded by 16 bytes so
-// that the 16 rows one fragment read touches fall in distinct banks).  The
-// products are taken transposed, out^T = W x^T: the A operand is 16 weight
-// rows (output channels), read from global memory where every workgroup
-// finds them in L2, and the B operand is 16 staged token rows, so each lane
-// ends with 4 consecutive output channels of one token and stores 8 bytes.
-// The wavefronts split the 16-channel output tiles; each weight fragment
-// serves all BT / 16 token tiles.
-//   QKV adds the bias and rounds once.  NORM keeps its tiles in registers,
-//   reduces each token's sum and then its sum of squared deviations across
-//   lanes and wavefronts (two passes, exact), and writes
+// four wavefronts takes 64 consecutive tokens.  The products are taken
+// transposed, out^T = W x^T: the A operand is 16 weight rows (output
+// channels), the B operand 16 token rows, so each lane ends with 4
+// consecutive output channels of one token.  The input channels go 32 at a
+// time: that slice of the 64 token rows and of the pass's weight rows is
+// staged in LDS (XOR-swizzled 16-byte pieces, so the 16 rows of a fragment
+// read cover all banks), in two stages, the next slice's global loads in
+// flight while the matrix cores read the current one.  The wavefronts split
+// the pass's 16-channel output tiles; each weight fragment serves all four
+// token tiles.  Results go through LDS once more and leave as whole 16-byte
+// pieces of contiguous runs (one run per token row and output tensor):
+// stores of 8-byte pieces from different wavefronts to one line measured
+// about twice as slow.
+//   QKV takes the 3C outputs in passes of 192 channels, adds the bias and
+//   rounds once.  NORM takes all C <= 512 outputs in one pass and keeps them
+//   in registers, reduces each token's sum and then its sum of squared
+//   deviations across lanes and wavefronts (two passes, exact), and writes
 //   resid + gamma (z - mean) / sqrt(var + eps) + beta, rounded once.
 //
 // fp32 path: one thread per output (QKV), one wavefront per token (NORM),
@@ -120,6 +125,25 @@ __device__ __forceinline__ void pass_product(const __bf16* x, int nt, const __bf
     }
 }
 
+// Staged outputs (BT tokens x channels [n0, n0 + nb) of [q | k | v], row
+// stride OS) to their tensors: each destination's channels of the pass form
+// one run per token, whole rows when the pass covers the tensor, so that
+// consecutive threads write consecutive 16-byte pieces and the memory sees
+// whole lines.
+__device__ __forceinline__ void copy_out(const __bf16* ob, int OS, int n0, int nb, int C, int64_t t0, int nt,
+                                         const ProjArgs& a, int tid)
+{
+    for (int d = n0 / C; d * C < n0 + nb; ++d) {
+        const int lo = max(n0, d * C), hi = min(n0 + nb, (d + 1) * C);   // channels of [q | k | v]
+        const int run = (hi - lo) / 8;                                  // 16-byte pieces per token
+        __bf16* dst = (__bf16*)(d == 0 ? a.q : d == 1 ? a.k : a.v) + (size_t)t0 * C + (lo - d * C);
+        for (int i = tid; i < nt * run; i += PW * 64) {
+            const int t = i / run, p = i - t * run;
+            *(u32x4*)(dst + (size_t)t * C + 8 * p) = *(const u32x4*)(ob + t * OS + (lo - n0) + 8 * p);
+        }
+    }
+}
+
 // [q | k | v] = x W^T + b: 64 tokens per workgroup, output channels in
 // passes of up to 64 NTW.
 template <int NTW>
@@ -139,24 +163,26 @@ __global__ void __launch_bounds__(PW * 64) qkv_kernel(ProjArgs a)
         const int nb = min(NP, 3 * C - n0);
         f32x4 z[NTW][RT];
         pass_product<NTW>(x, nt, (const __bf16*)a.w, C, n0, nb, (__bf16*)smem, z, tid, wave, lane);
+        // the pass's outputs to LDS (the slice stages are free now), then
+        // out to q, k, v as runs of whole 16-byte pieces per token row
+        __bf16* ob = (__bf16*)smem;                       // [BT][nb + 8]
+        const int OS = nb + 8;
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
             const int m = wave + PW * j;
             if (16 * m >= nb) break;
-            // lane holds channels ch .. ch+3 of tokens 16r + li
-            const int ch = n0 + 16 * m + 4 * grp;         // in [0, 3C)
-            const int which = ch / C, c = ch - which * C;
-            __bf16* dst = (__bf16*)(which == 0 ? a.q : which == 1 ? a.k : a.v);
-            const f32x4 bias = a.b ? *(const f32x4*)(a.b + ch) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            // lane holds channels cl .. cl+3 of the pass for tokens 16r + li
+            const int cl = 16 * m + 4 * grp;
+            const f32x4 bias = a.b ? *(const f32x4*)(a.b + n0 + cl) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int r = 0; r < RT; ++r) {
-                const int t = 16 * r + li;
-                if (t < nt)
-                    *(bf16x4*)(dst + (size_t)(t0 + t) * C + c) =
-                        pack_bf16x4(z[j][r][0] + bias[0], z[j][r][1] + bias[1], z[j][r][2] + bias[2],
-                                    z[j][r][3] + bias[3]);
-            }
+            for (int r = 0; r < RT; ++r)
+                *(bf16x4*)(ob + (16 * r + li) * OS + cl) =
+                    pack_bf16x4(z[j][r][0] + bias[0], z[j][r][1] + bias[1], z[j][r][2] + bias[2],
+                                z[j][r][3] + bias[3]);
         }
+        __syncthreads();
+        copy_out(ob, OS, n0, nb, C, t0, nt, a, tid);
+        __syncthreads();                                  // ob is the next pass's first stage
     }
 }
 
@@ -234,6 +260,8 @@ __global__ void __launch_bounds__(PW * 64) norm_kernel(ProjArgs a)
     float rstd[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) rstd[r] = 1.0f / sqrtf(fmaf(var[r], inv_c, a.eps));
+    __bf16* ob = (__bf16*)smem;                           // [BT][C + 8] (the slice stages are free)
+    const int OS = C + 8;
 
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
@@ -245,8 +273,7 @@ __global__ void __launch_bounds__(PW * 64) norm_kernel(ProjArgs a)
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
             const int t = 16 * r + li;
-            if (t >= nt) continue;
-            const size_t off = (size_t)(t0 + t) * C + ch;
+            const size_t off = (size_t)(t0 + (t < nt ? t : 0)) * C + ch;
             const u32x2 rw = *(const u32x2*)((const __bf16*)a.resid + off);
             float y[4];
 #pragma unroll
@@ -254,8 +281,16 @@ __global__ void __launch_bounds__(PW * 64) norm_kernel(ProjArgs a)
                 const uint32_t h = (e & 1) ? (rw[e >> 1] & 0xffff0000u) : (rw[e >> 1] << 16);
                 y[e] = __uint_as_float(h) + fmaf(g[e], (z[j][r][e] - mean[r]) * rstd[r], be[e]);
             }
-            *(bf16x4*)((__bf16*)a.y + off) = pack_bf16x4(y[0], y[1], y[2], y[3]);
+            *(bf16x4*)(ob + t * OS + ch) = pack_bf16x4(y[0], y[1], y[2], y[3]);
         }
+    }
+    // the block's rows of y are one contiguous run: out as whole 16-byte pieces
+    __syncthreads();
+    const int run = nt * (C / 8);
+    __bf16* dst = (__bf16*)a.y + (size_t)t0 * C;
+    for (int i = tid; i < run; i += PW * 64) {
+        const int t = i / (C / 8), p = i - t * (C / 8);
+        *(u32x4*)(dst + (size_t)t * C + 8 * p) = *(const u32x4*)(ob + t * OS + 8 * p);
     }
 }
 
@@ -322,10 +357,9 @@ hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t stream)
     if (a.T == 0) return hipSuccess;
     if (a.dtype == SWIN_DT_F32)
         return launch(qkv_f32_kernel, (a.T * 3 * a.C + 255) / 256, 256, 0, a, stream);
-    const int64_t blocks = (a.T + BT - 1) / BT;
-    // one pass when 3C fits 5 tiles per wavefront, else passes of 4
-    if (3 * a.C <= PW * 5 * 16) return launch(qkv_kernel<5>, blocks, PW * 64, pass_lds<5>(), a, stream);
-    return launch(qkv_kernel<4>, blocks, PW * 64, pass_lds<4>(), a, stream);
+    // passes of 192 output channels: 3 tiles per wavefront keep the
+    // registers at 3 wavefronts per SIMD (measured faster than one pass)
+    return launch(qkv_kernel<3>, (a.T + BT - 1) / BT, PW * 64, pass_lds<3>(), a, stream);
 }
 
 hipError_t launch_proj_norm(const ProjArgs& a, hipStream_t stream)

@@ -20,8 +20,8 @@
 // the pass's 16-channel output tiles; each weight fragment serves all four
 // token tiles.  Results go through LDS once more and leave as whole 16-byte
 // pieces of contiguous runs (one run per token row and output tensor):
-// stores of 8-byte pieces from different wavefronts to one line measured
-// about twice as slow.
+// storing the 8-byte pieces straight from the lanes, several wavefronts
+// sharing each line, measured 15-25% slower.
 //   QKV takes the 3C outputs in passes of 192 channels, adds the bias and
 //   rounds once.  NORM takes all C <= 512 outputs in one pass and keeps them
 //   in registers, reduces each token's sum and then its sum of squared

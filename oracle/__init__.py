@@ -7,8 +7,9 @@ package never imports the GPU library: the two share no code.
 Contents
   * ``oracle.c`` (compiled with gcc into ``liboracle.so``): the plain per-window
     definition -- partition / reverse maps, log-spaced offsets, the CPB table,
-    the attention itself and its backward, and the attention branch's linear
-    layers and residual post-norm, all in fp64.
+    the attention itself and its backward, the attention branch's linear
+    layers and residual post-norm, and Iwin's depthwise convolution branch, all
+    in fp64.
   * ``bruteforce.py``: full-grid attention over every token pair with a mask, for
     tiny grids; it shares neither the partition nor the table indexing with
     ``oracle.c`` and serves as that file's independent check.
@@ -74,6 +75,8 @@ def _declare(lib):
     lib.oracle_linear.argtypes = [vp] * 4 + [i64, i32, i32]
     lib.oracle_post_norm.restype = i32
     lib.oracle_post_norm.argtypes = [vp] * 4 + [dbl, vp, i64, i32]
+    lib.oracle_dwconv_add.restype = i32
+    lib.oracle_dwconv_add.argtypes = [vp] * 4 + [i32] * 4
     lib.oracle_set_threads.restype = None
     lib.oracle_set_threads.argtypes = [i32]
     lib.oracle_max_threads.restype = i32
@@ -302,6 +305,19 @@ def post_norm(resid, z, gamma, beta, eps: float = 1e-5, lib=None) -> np.ndarray:
 def proj_post_norm(o, w, b, resid, gamma, beta, eps: float = 1e-5, lib=None) -> np.ndarray:
     """The attention branch's output side: resid + norm_1(o w^T + b)."""
     return post_norm(resid, linear(o, w, b, lib=lib), gamma, beta, eps, lib=lib)
+
+
+def dwconv_add(v, w, b, out, lib=None) -> np.ndarray:
+    """out + depthwise 3x3 convolution of v (B, H, W, C) with w (C, 3, 3) and
+    bias b (C) or None, zero padding, in fp64; returns a new array."""
+    v, w, o = _f64(v), _f64(w), np.array(out, dtype=np.float64, copy=True)
+    B, H, W, C = v.shape
+    assert w.shape == (C, 3, 3) and o.shape == v.shape
+    bb = None if b is None else _f64(b)
+    rc = (lib or load()).oracle_dwconv_add(_ptr(v), _ptr(w), _ptr(bb), _ptr(o), B, H, W, C)
+    if rc:
+        raise ValueError(f"oracle_dwconv_add: bad argument (rc={rc})")
+    return o
 
 
 def cpu_model() -> str:

@@ -1,8 +1,8 @@
 /*
  * oracle.c -- plain fp64 CPU reference for windowed multi-head self-attention
  * (forward and backward), the log-spaced continuous position bias table, the
- * window partition / reverse maps, and the attention branch's projections and
- * residual post-norm.
+ * window partition / reverse maps, the attention branch's projections and
+ * residual post-norm, and Iwin's depthwise convolution branch.
  *
  * TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the CPU
  * baseline leg of the benchmark are the only code that may load this library.
@@ -753,5 +753,40 @@ int oracle_post_norm(const double* resid, const double* z, const double* gamma, 
         for (int c = 0; c < C; ++c)
             y[t * C + c] = resid[t * C + c] + gamma[c] * (zt[c] - mean) * inv + beta[c];
     }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Iwin's convolution branch ([Iwin] abstract: the block couples interleaved
+ * window attention with a depthwise convolution that links each token to its
+ * local neighbours).  Reading: a 3 x 3 depthwise convolution of v over the
+ * (H, W) grid of each image, zero padding, stride 1, per-channel weights
+ * w[c][dy+1][dx+1] and an optional per-channel bias, added to the attention
+ * output:  out[b][y][x][c] += b[c] + sum_{dy,dx in -1..1} w[c][dy+1][dx+1]
+ * v[b][y+dy][x+dx][c] (terms outside the grid are 0).
+ * ------------------------------------------------------------------------- */
+int oracle_dwconv_add(const double* v, const double* w, const double* b, double* out, int B, int H, int W, int C)
+{
+    if (B < 0 || H < 1 || W < 1 || C < 1 || (B > 0 && (!v || !w || !out))) return 1;
+    const size_t plane = (size_t)H * W * C;
+    double* tmp = (double*)malloc(((size_t)B * plane + 1) * sizeof(double));
+    if (!tmp) return 2;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int bi = 0; bi < B; ++bi)
+        for (int y = 0; y < H; ++y)
+            for (int x = 0; x < W; ++x)
+                for (int c = 0; c < C; ++c) {
+                    double s = b ? b[c] : 0.0;
+                    for (int dy = -1; dy <= 1; ++dy)
+                        for (int dx = -1; dx <= 1; ++dx) {
+                            const int yy = y + dy, xx = x + dx;
+                            if (yy < 0 || yy >= H || xx < 0 || xx >= W) continue;
+                            s += w[(size_t)c * 9 + (size_t)(dy + 1) * 3 + (size_t)(dx + 1)] *
+                                 v[(size_t)bi * plane + ((size_t)yy * W + xx) * C + c];
+                        }
+                    tmp[(size_t)bi * plane + ((size_t)y * W + x) * C + c] = s;
+                }
+    for (size_t i = 0; i < (size_t)B * plane; ++i) out[i] += tmp[i];
+    free(tmp);
     return 0;
 }

@@ -68,6 +68,12 @@ MUTATIONS = [
     ("ln_resid_dropped", "y[t * C + c] = resid[t * C + c] + gamma[c]", "y[t * C + c] = gamma[c]"),
     ("ln_gamma_beta_swapped", "gamma[c] * (zt[c] - mean) * inv + beta[c]", "beta[c] * (zt[c] - mean) * inv + gamma[c]"),
     ("ln_mean_not_subtracted", "var += (zt[c] - mean) * (zt[c] - mean);", "var += zt[c] * zt[c];"),
+    ("dwconv_dy_sign", "const int yy = y + dy, xx = x + dx;", "const int yy = y - dy, xx = x + dx;"),
+    ("dwconv_kernel_transposed", "(size_t)(dy + 1) * 3 + (size_t)(dx + 1)]", "(size_t)(dx + 1) * 3 + (size_t)(dy + 1)]"),
+    ("dwconv_tap_dropped", "if (yy < 0 || yy >= H || xx < 0 || xx >= W) continue;",
+     "if (yy < 0 || yy >= H || xx < 0 || xx >= W || (dy == 1 && dx == 1)) continue;"),
+    ("dwconv_bias_dropped", "double s = b ? b[c] : 0.0;", "double s = 0.0;"),
+    ("dwconv_overwrites", "out[i] += tmp[i];", "out[i] = tmp[i];"),
 ]
 
 

@@ -15,7 +15,9 @@ mathematics fix, never against itself.
   * the attention branch's linear layers and post-norm: a hand-worked product,
     scaled-permutation weights, the q/k/v order, the two-channel and constant
     closed forms of the layer norm, its shift/scale invariance, and torch's
-    fp64 linear and layer_norm.
+    fp64 linear and layer_norm;
+  * Iwin's depthwise convolution: centre, corner and zero taps, and torch's
+    fp64 grouped conv2d.
 
 Each pin is a function of the oracle library handle so that
 tests/test_oracle_mutations.py can run the same pins against oracle builds
@@ -450,6 +452,32 @@ def pin_post_norm_closed_forms(lib):
     assert np.allclose(oracle.post_norm(r2, z2, g2, b2, eps, lib=lib), ref, rtol=1e-13, atol=1e-13)
 
 
+def pin_dwconv_closed_forms(lib):
+    """Iwin's convolution branch (Iwin abstract; reading: a 3 x 3 depthwise
+    convolution of v, zero padding, added to the attention output): a centre
+    tap adds v itself, a corner tap adds v shifted by one row and column with
+    zeros entering at the border, zero weights add the bias alone, and the
+    result equals torch's fp64 grouped conv2d."""
+    rng = np.random.default_rng(13)
+    B, H, W, C = 2, 5, 7, 4
+    v = rng.standard_normal((B, H, W, C))
+    out = rng.standard_normal((B, H, W, C))
+    b = rng.standard_normal(C)
+    w = np.zeros((C, 3, 3))
+    w[:, 1, 1] = 1.0
+    assert np.allclose(oracle.dwconv_add(v, w, None, out, lib=lib), out + v, atol=1e-15)
+    w = np.zeros((C, 3, 3))
+    w[:, 0, 0] = 2.0                                  # tap (dy, dx) = (-1, -1)
+    shifted = np.zeros_like(v)
+    shifted[:, 1:, 1:, :] = v[:, :-1, :-1, :]
+    assert np.allclose(oracle.dwconv_add(v, w, None, out, lib=lib), out + 2.0 * shifted, atol=1e-15)
+    assert np.allclose(oracle.dwconv_add(v, np.zeros((C, 3, 3)), b, out, lib=lib), out + b, atol=1e-15)
+    w = rng.standard_normal((C, 3, 3))
+    ref = F.conv2d(torch.from_numpy(v).permute(0, 3, 1, 2), torch.from_numpy(w)[:, None], torch.from_numpy(b),
+                   padding=1, groups=C).permute(0, 2, 3, 1).numpy() + out
+    assert np.allclose(oracle.dwconv_add(v, w, b, out, lib=lib), ref, rtol=1e-13, atol=1e-13)
+
+
 PINS = {
     "worked_example": pin_worked_example,
     "cpb_vs_torch": pin_cpb_vs_torch,
@@ -468,6 +496,7 @@ PINS = {
     "linear_closed_forms": pin_linear_closed_forms,
     "qkv_split": pin_qkv_split,
     "post_norm_closed_forms": pin_post_norm_closed_forms,
+    "dwconv_closed_forms": pin_dwconv_closed_forms,
 }
 
 

@@ -406,17 +406,21 @@ def _roof(flops: float, alg_bytes: float, ms: float, peak_tf: float, compute: st
 
 def bench_branch(args, wl, par, table, desc, stream) -> int:
     """Attention branch step of a Swin V2 block: q, k, v = split(x W_qkv^T +
-    b), the CPB table, the window attention, y = x + norm_1(o W_proj^T + b).
-    Algorithmic work: QKV 6 T C^2 flops and 4 T C es bytes (read x, write q,
-    k, v); attention as the forward; output layer 2 T C^2 flops and 3 T C es
-    bytes (read o and x, write y); weights counted once."""
+    b), the CPB table, the window attention, y = x + norm_1(o W_proj^T + b);
+    for interleaved windows (Iwin) the depthwise 3x3 convolution of v is added
+    to o before the output layer.  Algorithmic work: QKV 6 T C^2 flops and
+    4 T C es bytes (read x, write q, k, v); attention as the forward;
+    convolution 18 T C flops and 3 T C es bytes (read v and o, write o);
+    output layer 2 T C^2 flops and 3 T C es bytes (read o and x, write y);
+    weights counted once."""
     import torch
 
     from vision_transformer_windowed_partition_amd import binding, synth
 
     dev = torch.device("cuda:0")
     p = synth.make_branch_params(wl)
-    w = {n: p[n].to(dev) for n in ("w_qkv", "b_qkv", "w_proj", "b_proj", "gamma", "beta")}
+    w = {n: p[n].to(dev) for n in ("w_qkv", "b_qkv", "w_proj", "b_proj", "gamma", "beta", "w_dw", "b_dw")}
+    iwin = wl.partition == "interleaved"          # Iwin couples its attention with the convolution branch
     T, C, es = wl.tokens, wl.C, wl.elem_size
     set_bytes = 6 * T * C * es
     nsets = 1 if args.warm else max(2, math.ceil(2 * MALL_BYTES / set_bytes) + 1)
@@ -426,7 +430,7 @@ def bench_branch(args, wl, par, table, desc, stream) -> int:
         xs = x0 if i == 0 else x0.clone()
         sets.append(dict(x=xs, q=torch.empty_like(xs), k=torch.empty_like(xs), v=torch.empty_like(xs),
                          o=torch.empty_like(xs), y=torch.empty_like(xs)))
-    names = ("qkv", "attn", "norm")
+    names = ("qkv", "attn", "dwconv", "norm") if iwin else ("qkv", "attn", "norm")
 
     def step(i, timed=None):
         st = sets[i % nsets]
@@ -442,6 +446,10 @@ def bench_branch(args, wl, par, table, desc, stream) -> int:
         binding.swin_window_attn_fwd(st["q"], st["k"], st["v"], heads=wl.heads, M=wl.M, desc=desc,
                                      tau=par["tau"], table=tab, out=st["o"], stream=stream)
         rec("attn", True)
+        if iwin:
+            rec("dwconv", False)
+            binding.swin_dwconv_add(st["v"], w["w_dw"], w["b_dw"], st["o"], stream=stream)
+            rec("dwconv", True)
         rec("norm", False)
         binding.swin_proj_post_norm(st["o"], w["w_proj"], w["b_proj"], st["x"], w["gamma"], w["beta"], eps=1e-5,
                                     out=st["y"], stream=stream)
@@ -466,10 +474,12 @@ def bench_branch(args, wl, par, table, desc, stream) -> int:
     compute = "mfma" if wl.dtype == "bf16" else "alu"
     work = {"qkv": (6.0 * T * C * C, 4.0 * T * C * es),
             "attn": (float(wl.flops), float(wl.bytes)),
-            "norm": (2.0 * T * C * C, 3.0 * T * C * es)}
+            "norm": (2.0 * T * C * C, 3.0 * T * C * es),
+            "dwconv": (18.0 * T * C, 3.0 * T * C * es)}
     kname = {"qkv": "qkv_kernel" if wl.dtype == "bf16" else "qkv_f32_kernel",
              "attn": binding.swin_window_attn_kernel(desc),
-             "norm": "norm_kernel" if wl.dtype == "bf16" else "norm_f32_kernel"}
+             "norm": "norm_kernel" if wl.dtype == "bf16" else "norm_f32_kernel",
+             "dwconv": "dwconv_add_kernel"}
     kernels = {}
     for n in names:
         r = _roof(work[n][0], work[n][1], ms[n], peak_tf, compute)
@@ -479,7 +489,8 @@ def bench_branch(args, wl, par, table, desc, stream) -> int:
     dominant = max(names, key=lambda n: ms[n])
     out = {
         "metric": "attention branch tokens/s (QKV projection, CPB table, window attention, "
-                  "output projection + residual post-norm)",
+                  + ("depthwise 3x3 convolution of v, " if iwin else "")
+                  + "output projection + residual post-norm)",
         "value": round(T / (wall / args.steps), 1),
         "unit": "tokens/s",
         "n_gpus": 1,

@@ -231,6 +231,19 @@ int swin_proj_post_norm(const void* o, const void* w, const float* b, const void
                         const float* gamma, const float* beta, float eps, void* y,
                         int64_t T, int32_t C, int32_t dtype, void* stream);
 
+/* Iwin's convolution branch ([Iwin] abstract: the block couples interleaved
+ * window attention with a depthwise convolution that links each token to its
+ * local neighbours).  Reading: a 3 x 3 depthwise convolution of v over the
+ * (H, W) grid of each image, zero padding, added to the attention output:
+ *   out[b][y][x][c] += b[c] + sum_{dy,dx = -1..1} w[c][dy+1][dx+1] v[b][y+dy][x+dx][c].
+ * v, out: (B, H, W, C) of `dtype`, device memory, 16-byte aligned; out is read
+ * and written (in place) and must not overlap v, w or b.  w: C x 3 x 3 fp32,
+ * b: C fp32 or NULL.  Requires C a multiple of 8 (bf16) or 4 (fp32)
+ * (SWIN_EUNSUPPORTED otherwise); B = 0 is a no-op.  Arithmetic: fp32; a bf16
+ * out is rounded once more after the add. */
+int swin_dwconv_add(const void* v, const float* w, const float* b, void* out, int32_t B, int32_t H,
+                    int32_t W, int32_t C, int32_t dtype, void* stream);
+
 /* Name of the kernel that swin_window_attn_fwd launches for desc (static
  * storage), for matching profiler output:
  *   "attn_valu_kernel"  SWIN_DT_F32;

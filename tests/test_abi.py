@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
                                            "swin_window_reverse",
                                            "swin_window_attn_fwd", "swin_window_attn_kernel",
                                            "swin_window_attn_bwd_kernel",
-                                           "swin_qkv_proj", "swin_proj_post_norm",
+                                           "swin_qkv_proj", "swin_proj_post_norm", "swin_dwconv_add",
                                            "swin_status_string",
                                            "swin_last_error", "swin_version"])
 
@@ -147,6 +147,20 @@ def test_projection_rejects(L):
     assert _pnorm(L, y=ctypes.c_void_p(0x50000000 - 64)) == SWIN_EINVAL         # y overlaps gamma
     assert _pnorm(L, beta=ctypes.c_void_p(0x50001008)) == SWIN_EINVAL           # misaligned
     assert _pnorm(L, o=None, w=None, resid=None, gamma=None, beta=None, y=None, T=0) == SWIN_OK
+
+
+def test_dwconv_rejects(L):
+    """Host validation of the convolution branch: nothing is launched."""
+    out = ctypes.c_void_p(0x60000000)
+    w = ctypes.c_void_p(0x30000000)
+    assert L.swin_dwconv_add(FAKE, w, None, out, 1, 8, 8, 20, 1, None) == SWIN_EUNSUPPORTED   # 20 % 8
+    assert L.swin_dwconv_add(FAKE, w, None, out, 1, 0, 8, 32, 1, None) == SWIN_EINVAL
+    assert L.swin_dwconv_add(FAKE, w, None, out, 1, 8, 8, 32, 5, None) == SWIN_EINVAL
+    assert L.swin_dwconv_add(None, w, None, out, 1, 8, 8, 32, 1, None) == SWIN_EINVAL
+    assert L.swin_dwconv_add(FAKE, w, None, ctypes.c_void_p(0x60000008), 1, 8, 8, 32, 1, None) == SWIN_EINVAL
+    assert L.swin_dwconv_add(FAKE, w, None, ctypes.c_void_p(0x10000 + 64), 1, 8, 8, 32, 1, None) == SWIN_EINVAL
+    assert L.swin_dwconv_add(FAKE, ctypes.c_void_p(0x30000002), None, out, 1, 8, 8, 32, 1, None) == SWIN_EINVAL
+    assert L.swin_dwconv_add(None, None, None, None, 0, 8, 8, 32, 1, None) == SWIN_OK           # empty batch
 
 
 def test_backward_rejects(L):

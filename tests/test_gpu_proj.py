@@ -1,5 +1,6 @@
-"""GPU parity of the attention branch's linear layers and residual post-norm
-(swin_qkv_proj, swin_proj_post_norm) against the fp64 oracle, through the C
+"""GPU parity of the steps either side of the attention: the branch's linear
+layers and residual post-norm (swin_qkv_proj, swin_proj_post_norm) and Iwin's
+convolution branch (swin_dwconv_add), against the fp64 oracle, through the C
 ABI, on the same seeded inputs.
 
 Bars, derived from the arithmetic.  bf16 mode: the products of bf16 inputs
@@ -7,8 +8,9 @@ are exact in fp32 and summed in fp32 over at most 512 terms (relative error
 far below 2^-9), and each output is rounded to bf16 once (half an ulp,
 2^-9 relative), so every element must satisfy |got - ref| <= 2^-8 |ref| +
 1e-3 (one bf16 ulp plus a floor for values near zero, where the fp32 sum's
-own error can move the rounding).  fp32 mode: fp32 throughout, |got - ref| <=
-1e-5 |ref| + 1e-4.
+own error can move the rounding); the convolution adds nine fp32 products to
+the given bf16 output and rounds once, the same bar.  fp32 mode: fp32
+throughout, |got - ref| <= 1e-5 |ref| + 1e-4.
 """
 import numpy as np
 import pytest
@@ -134,3 +136,50 @@ def test_full_size_sampled(w):
     ry = oracle.proj_post_norm(f64(p["o"][rows]), f64(p["w_proj"]), f64(p["b_proj"]), f64(p["x"][rows]),
                                f64(p["gamma"]), f64(p["beta"]), 1e-5)
     _check(f"{wl.name} y", f64(y[torch.from_numpy(rows).to(DEV)]), ry, wl.dtype)
+
+
+DW_SHAPES = [
+    # B, H, W, C: tiles of 8 x 8 with ragged edges, one and two channel chunks
+    (2, 13, 21, 96), (1, 8, 8, 192), (1, 17, 9, 512), (3, 5, 7, 32), (1, 64, 64, 40),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,H,W,C", DW_SHAPES)
+def test_dwconv_add(B, H, W, C, dtype):
+    """Iwin's convolution branch: out += depthwise 3x3 conv of v (zero padding)."""
+    if dtype == "bf16" and C % 8:
+        pytest.skip("bf16 needs C a multiple of 8")
+    gen = torch.Generator().manual_seed(B * 1000 + H * 10 + C)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    v = torch.randn((B, H, W, C), generator=gen).to(dt)
+    out = torch.randn((B, H, W, C), generator=gen).to(dt)
+    w = torch.randn((C, 3, 3), generator=gen) / 3.0
+    b = 0.1 * torch.randn(C, generator=gen)
+    o = out.to(DEV)
+    res = binding.swin_dwconv_add(v.to(DEV), w.to(DEV), b.to(DEV), o)
+    torch.cuda.synchronize()
+    assert res.data_ptr() == o.data_ptr()
+    ref = oracle.dwconv_add(f64(v), f64(w), f64(b), f64(out))
+    _check(f"dwconv {B}x{H}x{W}x{C}", f64(o), ref, dtype)
+    o2 = out.to(DEV)
+    binding.swin_dwconv_add(v.to(DEV), w.to(DEV), None, o2)
+    torch.cuda.synchronize()
+    _check("dwconv no bias", f64(o2), oracle.dwconv_add(f64(v), f64(w), None, f64(out)), dtype)
+
+
+def test_dwconv_full_size_sampled():
+    """The interleaved workload's full grid (64 x 64 x 64 x 192, bf16), checked
+    on a sample of whole images against the oracle."""
+    wl = synth.WORKLOADS[2]
+    gen = torch.Generator().manual_seed(77)
+    v = torch.randn((wl.B, wl.H, wl.W, wl.C), generator=gen).to(torch.bfloat16)
+    out = torch.randn((wl.B, wl.H, wl.W, wl.C), generator=gen).to(torch.bfloat16)
+    w = torch.randn((wl.C, 3, 3), generator=gen) / 3.0
+    b = 0.1 * torch.randn(wl.C, generator=gen)
+    o = out.to(DEV)
+    binding.swin_dwconv_add(v.to(DEV), w.to(DEV), b.to(DEV), o)
+    torch.cuda.synchronize()
+    imgs = [0, 17, wl.B - 1]
+    ref = oracle.dwconv_add(f64(v[imgs]), f64(w), f64(b), f64(out[imgs]))
+    _check("dwconv full size", f64(o[imgs]), ref, "bf16")

@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.swin_qkv_proj.argtypes = [vp] * 6 + [ctypes.c_int64, i32, i32, vp]
         L.swin_proj_post_norm.restype = i32
         L.swin_proj_post_norm.argtypes = [vp] * 6 + [ctypes.c_float, vp, ctypes.c_int64, i32, i32, vp]
+        L.swin_dwconv_add.restype = i32
+        L.swin_dwconv_add.argtypes = [vp] * 4 + [i32] * 5 + [vp]
         L.swin_window_attn_kernel.restype = ctypes.c_char_p
         L.swin_window_attn_kernel.argtypes = [ctypes.POINTER(SwinAttnDesc)]
         L.swin_window_attn_bwd_kernel.restype = ctypes.c_char_p
@@ -286,6 +288,24 @@ def swin_proj_post_norm(o, w, b, resid, gamma, beta, *, eps: float = 1e-5, out=N
     _check(lib().swin_proj_post_norm(_ptr(o), _ptr(w), _ptr(b), _ptr(resid), _ptr(gamma), _ptr(beta), float(eps),
                                      _ptr(y), o.numel() // C, C, dt, _stream(o, stream)))
     return y
+
+
+def swin_dwconv_add(v, w, b, out, *, stream=None):
+    """out += depthwise 3x3 convolution of v (zero padding) with w (C, 3, 3)
+    fp32 and bias b (C) fp32 or None; v and out (B, H, W, C) of one dtype.
+    Returns out."""
+    if v.dim() != 4 or out.shape != v.shape or out.dtype != v.dtype:
+        raise ValueError("v and out must be (B, H, W, C) tensors of one dtype")
+    B, H, W, C = v.shape
+    if w.dtype != torch.float32 or tuple(w.shape) != (C, 3, 3) or not w.is_contiguous():
+        raise ValueError("w must be contiguous fp32 (C, 3, 3)")
+    if b is not None and (b.dtype != torch.float32 or tuple(b.shape) != (C,) or not b.is_contiguous()):
+        raise ValueError("b must be contiguous fp32 of C")
+    if not (v.is_contiguous() and out.is_contiguous()):
+        raise ValueError("v and out must be contiguous")
+    _check(lib().swin_dwconv_add(_ptr(v), _ptr(w), _ptr(b), _ptr(out), B, H, W, C, _proj_dtype(v),
+                                 _stream(v, stream)))
+    return out
 
 
 def swin_window_attn_kernel(desc: SwinAttnDesc) -> str:

@@ -317,6 +317,26 @@ int swin_proj_post_norm(const void* o, const void* w, const float* b, const void
     return hip_status(swin::launch_proj_norm(a, (hipStream_t)stream), "swin_proj_post_norm launch");
 }
 
+int swin_dwconv_add(const void* v, const float* w, const float* b, void* out, int32_t B, int32_t H, int32_t W,
+                    int32_t C, int32_t dtype, void* stream)
+{
+    if (dtype != SWIN_DT_F32 && dtype != SWIN_DT_BF16) return fail(SWIN_EINVAL, "unknown dtype %d", dtype);
+    if (B < 0 || H < 1 || W < 1 || C < 1) return fail(SWIN_EINVAL, "bad shape B=%d H=%d W=%d C=%d", B, H, W, C);
+    if (!swin::dwconv_supported(C, dtype))
+        return fail(SWIN_EUNSUPPORTED, "C=%d: multiples of 16 bytes of channels are built", C);
+    if ((int64_t)B * H * W > ((int64_t)1 << 31) - 1) return fail(SWIN_EUNSUPPORTED, "grid too large");
+    if (B == 0) return SWIN_OK;
+    if (!v || !w || !out) return fail(SWIN_EINVAL, "NULL v, w or out");
+    if (((uintptr_t)v | (uintptr_t)out) & 15) return fail(SWIN_EINVAL, "v and out must be 16-byte aligned");
+    if (((uintptr_t)w | (uintptr_t)b) & 3) return fail(SWIN_EINVAL, "w and b must be 4-byte aligned");
+    const size_t es = dtype == SWIN_DT_F32 ? 4 : 2;
+    const size_t n = (size_t)B * H * W * C * es;
+    if (overlaps(out, n, v, n) || overlaps(out, n, w, (size_t)C * 36) || (b && overlaps(out, n, b, (size_t)C * 4)))
+        return fail(SWIN_EINVAL, "out overlaps v, w or b");
+    swin::DwconvArgs a{v, w, b, out, B, H, W, C, dtype};
+    return hip_status(swin::launch_dwconv_add(a, (hipStream_t)stream), "swin_dwconv_add launch");
+}
+
 int swin_cpb_table_bwd(int32_t M, int32_t norm_M, int32_t heads, int32_t hidden, const float* w1,
                        const float* b1, const float* w2, const float* table, const float* dtable,
                        int32_t cpb_mode, float* dw1, float* db1, float* dw2, float* db2, void* stream)

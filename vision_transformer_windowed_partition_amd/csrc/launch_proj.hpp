@@ -1,5 +1,5 @@
-// Launch entry of the projection kernels (proj.hip), called by api.hip after
-// the host-side validation.
+// Launch entries of the kernels either side of the attention (proj.hip,
+// dwconv.hip), called by api.hip after the host-side validation.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,7 +21,18 @@ struct ProjArgs {
     int dtype;                 // SWIN_DT_F32 or SWIN_DT_BF16
 };
 
+struct DwconvArgs {
+    const void* v;             // (B, H, W, C) values
+    const float* w;            // C x 3 x 3 taps
+    const float* b;            // C bias, or nullptr
+    void* out;                 // (B, H, W, C) attention output, updated in place
+    int B, H, W, C;
+    int dtype;
+};
+
 bool proj_supported(int C);
+bool dwconv_supported(int C, int dtype);
+hipError_t launch_dwconv_add(const DwconvArgs& a, hipStream_t stream);
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t stream);
 hipError_t launch_proj_norm(const ProjArgs& a, hipStream_t stream);
 

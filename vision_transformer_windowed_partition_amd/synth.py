@@ -133,9 +133,11 @@ def make_branch_params(wl: Workload, seed: int = 2000, T: int | None = None) -> 
     """Inputs of the attention branch's linear layers and post-norm, drawn in
     this order (CPU, fp32): x (T, C) features, o (T, C) attention output,
     w_qkv (3C, C) and w_proj (C, C) each randn / sqrt(C), b_qkv (3C) and
-    b_proj (C) each 0.1 randn, gamma = 1 + 0.1 randn (C), beta = 0.1 randn (C).
-    x, o and the weights are rounded to the workload dtype; the biases, gamma
-    and beta stay fp32.  T defaults to the workload's B H W tokens."""
+    b_proj (C) each 0.1 randn, gamma = 1 + 0.1 randn (C), beta = 0.1 randn (C),
+    then the convolution branch's taps w_dw (C, 3, 3) = randn / 3 and bias
+    b_dw (C) = 0.1 randn.  x, o and the linear weights are rounded to the
+    workload dtype; biases, gamma, beta and the taps stay fp32.  T defaults to
+    the workload's B H W tokens."""
     g = torch.Generator().manual_seed(int(seed))
     C = wl.C
     T = wl.B * wl.H * wl.W if T is None else int(T)
@@ -148,8 +150,10 @@ def make_branch_params(wl: Workload, seed: int = 2000, T: int | None = None) -> 
     b_proj = 0.1 * torch.randn(C, generator=g)
     gamma = 1.0 + 0.1 * torch.randn(C, generator=g)
     beta = 0.1 * torch.randn(C, generator=g)
+    w_dw = torch.randn((C, 3, 3), generator=g) / 3.0
+    b_dw = 0.1 * torch.randn(C, generator=g)
     return dict(x=x.to(dt), o=o.to(dt), w_qkv=w_qkv.to(dt), w_proj=w_proj.to(dt), b_qkv=b_qkv, b_proj=b_proj,
-                gamma=gamma, beta=beta)
+                gamma=gamma, beta=beta, w_dw=w_dw, b_dw=b_dw)
 
 
 def small(name: str = "tiny", *, B=2, H=16, W=16, C=64, heads=2, M=8, shift=4,

@@ -8,8 +8,8 @@ Contents
   * ``oracle.c`` (compiled with gcc into ``liboracle.so``): the plain per-window
     definition -- partition / reverse maps, log-spaced offsets, the CPB table,
     the attention itself and its backward, the attention branch's linear
-    layers and residual post-norm, and Iwin's depthwise convolution branch, all
-    in fp64.
+    layers and residual post-norm, Iwin's depthwise convolution branch and
+    LinMapper's in-window linear mapping, all in fp64.
   * ``bruteforce.py``: full-grid attention over every token pair with a mask, for
     tiny grids; it shares neither the partition nor the table indexing with
     ``oracle.c`` and serves as that file's independent check.
@@ -77,6 +77,8 @@ def _declare(lib):
     lib.oracle_post_norm.argtypes = [vp] * 4 + [dbl, vp, i64, i32]
     lib.oracle_dwconv_add.restype = i32
     lib.oracle_dwconv_add.argtypes = [vp] * 4 + [i32] * 4
+    lib.oracle_window_linear.restype = i32
+    lib.oracle_window_linear.argtypes = [i32] * 8 + [vp] * 4
     lib.oracle_set_threads.restype = None
     lib.oracle_set_threads.argtypes = [i32]
     lib.oracle_max_threads.restype = i32
@@ -318,6 +320,25 @@ def dwconv_add(v, w, b, out, lib=None) -> np.ndarray:
     if rc:
         raise ValueError(f"oracle_dwconv_add: bad argument (rc={rc})")
     return o
+
+
+def window_linear(v, A, bias=None, *, heads: int, M: int, shift: int = 0, partition: str = "cyclic",
+                  lib=None) -> np.ndarray:
+    """Per window and head, out = A_h v (+ bias_h), cross-region pairs of
+    shifted windows excluded; v (B, H, W, C), A (heads, N, N), bias (heads, N)."""
+    v, A = _f64(v), _f64(A)
+    B, H, W, C = v.shape
+    N = M * M
+    assert A.shape == (heads, N, N)
+    bb = None if bias is None else _f64(bias)
+    if bb is not None:
+        assert bb.shape == (heads, N)
+    out = np.empty_like(v)
+    rc = (lib or load()).oracle_window_linear(B, H, W, C, heads, M, shift, PART[partition], _ptr(v), _ptr(A),
+                                              _ptr(bb), _ptr(out))
+    if rc:
+        raise ValueError("oracle_window_linear: bad argument")
+    return out
 
 
 def cpu_model() -> str:

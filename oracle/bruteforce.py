@@ -16,7 +16,9 @@ by the stride for interleaved windows).  Inside one cell they differ from the
 window-local ones by a constant, which changes neither a relative offset nor a
 rotary score.  The bias is the meta network G evaluated on each distinct
 offset (SwinV2 eq. 3-4), not a lookup in a precomputed table, and the rotary
-embedding is a complex multiply.  Nothing here is shared with ``oracle.c``.
+embedding is a complex multiply.  The same cells give the pairs of the
+in-window linear mapping (``window_linear``), with window-local indices
+computed from the grid side.  Nothing here is shared with ``oracle.c``.
 """
 from __future__ import annotations
 
@@ -134,3 +136,39 @@ def pair_allowed(H: int, W: int, M: int, shift: int, partition: str) -> np.ndarr
     cr, cc = _cell_rows(H, M, shift, partition), _cell_rows(W, M, shift, partition)
     cell = (cr[:, None] * W + cc[None, :]).reshape(H * W)
     return cell[:, None] == cell[None, :]
+
+
+def _local_index(L: int, M: int, shift: int, part: str) -> np.ndarray:
+    """Window-local row (or column) of each grid coordinate, from the grid
+    side: cyclic windows start every M rows of the grid rolled by -shift;
+    interleaved windows take one row of every H/M."""
+    idx = np.arange(L)
+    if part == "interleaved":
+        return idx // (L // M)
+    return ((idx - shift) % L) % M
+
+
+def window_linear(v, A, bias=None, *, heads: int, M: int, shift: int = 0, partition: str = "cyclic"):
+    """Full-grid form of the in-window linear mapping: token i takes
+    sum_j A_h[loc(i)][loc(j)] v_j over the tokens j of its cell (the same pairs
+    the attention allows), plus bias_h[loc(i)]."""
+    v = np.asarray(v, np.float64)
+    A = np.asarray(A, np.float64)
+    B, H, W, C = v.shape
+    d = C // heads
+    P = H * W
+    cr, cc = _cell_rows(H, M, shift, partition), _cell_rows(W, M, shift, partition)
+    cell = (cr[:, None] * W + cc[None, :]).reshape(P)
+    allowed = cell[:, None] == cell[None, :]
+    lr, lc = _local_index(H, M, shift, partition), _local_index(W, M, shift, partition)
+    loc = (lr[:, None] * M + lc[None, :]).reshape(P)
+    out = np.zeros((B, H, W, C))
+    for h in range(heads):
+        mat = np.where(allowed, A[h][loc[:, None], loc[None, :]], 0.0)      # (P, P)
+        for b in range(B):
+            vh = v[b].reshape(P, C)[:, h * d:(h + 1) * d]
+            oh = mat @ vh
+            if bias is not None:
+                oh = oh + np.asarray(bias, np.float64)[h][loc][:, None]
+            out[b].reshape(P, C)[:, h * d:(h + 1) * d] = oh
+    return out

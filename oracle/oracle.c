@@ -2,7 +2,8 @@
  * oracle.c -- plain fp64 CPU reference for windowed multi-head self-attention
  * (forward and backward), the log-spaced continuous position bias table, the
  * window partition / reverse maps, the attention branch's projections and
- * residual post-norm, and Iwin's depthwise convolution branch.
+ * residual post-norm, Iwin's depthwise convolution branch, and LinMapper's
+ * in-window linear mapping.
  *
  * TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the CPU
  * baseline leg of the benchmark are the only code that may load this library.
@@ -21,6 +22,8 @@
  *             window-local 2D rotary position embedding in place of the bias.
  *   [Iwin]    "Iwin Transformer: Hierarchical Vision Transformer using
  *             Interleaved Windows", abstract: interleaved window attention.
+ *   [What]    "What Makes for Hierarchical Vision Transformer?", abstract:
+ *             self-attention replaced by linear mapping inside each window.
  *
  * Where the pages leave a step open, the reading taken is stated at the step.
  * Nothing here is blocked, fused or reordered: every window, head, query and
@@ -788,5 +791,54 @@ int oracle_dwconv_add(const double* v, const double* w, const double* b, double*
                 }
     for (size_t i = 0; i < (size_t)B * plane; ++i) out[i] += tmp[i];
     free(tmp);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * LinMapper's aggregation inside each window ([What] abstract: self-attention
+ * replaced by a simple linear mapping layer inside each non-overlapped
+ * window, with Swin's cross-window communication kept).  Reading: per head h
+ * a learned N x N matrix A_h (N = M^2, shared by all windows) and an optional
+ * per-position bias b_h maps the window's values,
+ *   out[i] = b_h[i] + sum_j A_h[i][j] v[j],
+ * over the head's d channels, with the pairs of a shifted window's different
+ * regions excluded exactly as in the attention (region labels of the rolled
+ * grid).  Windows, regions and grid positions as in oracle_window_attn.
+ * A: heads x N x N, bias: heads x N or NULL.
+ * ------------------------------------------------------------------------- */
+int oracle_window_linear(int B, int H, int W, int C, int heads, int M, int shift, int part,
+                         const double* v, const double* A, const double* bias, double* out)
+{
+    if (bad_shape(B, H, W, C, M, shift, part)) return 1;
+    if (heads < 1 || C % heads) return 1;
+    if (B > 0 && (!v || !A || !out)) return 1;
+    const int d = C / heads, nwr = H / M, nwc = W / M, N = M * M;
+    const int64_t total = (int64_t)B * nwr * nwc;
+    memset(out, 0, (size_t)B * H * W * C * sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < total * heads; ++u) {
+        const int64_t gw = u / heads;
+        const int h = (int)(u % heads);
+        const int b = (int)(gw / ((int64_t)nwr * nwc));
+        const int wr = (int)((gw % ((int64_t)nwr * nwc)) / nwc), wc = (int)(gw % nwc);
+        for (int i = 0; i < N; ++i) {
+            int gi_i, gj_i;
+            grid_pos(H, W, M, shift, part, wr, wc, i / M, i % M, &gi_i, &gj_i);
+            const int reg_i = part == OR_PART_CYCLIC
+                ? 3 * axis_region(wr * M + i / M, H, M, shift) + axis_region(wc * M + i % M, W, M, shift) : 0;
+            double* o = out + (((size_t)b * H + gi_i) * W + gj_i) * C + (size_t)h * d;
+            for (int e = 0; e < d; ++e) o[e] = bias ? bias[(size_t)h * N + i] : 0.0;
+            for (int j = 0; j < N; ++j) {
+                const int reg_j = part == OR_PART_CYCLIC
+                    ? 3 * axis_region(wr * M + j / M, H, M, shift) + axis_region(wc * M + j % M, W, M, shift) : 0;
+                if (reg_j != reg_i) continue;
+                int gi_j, gj_j;
+                grid_pos(H, W, M, shift, part, wr, wc, j / M, j % M, &gi_j, &gj_j);
+                const double a = A[((size_t)h * N + i) * N + j];
+                const double* vj = v + (((size_t)b * H + gi_j) * W + gj_j) * C + (size_t)h * d;
+                for (int e = 0; e < d; ++e) o[e] += a * vj[e];
+            }
+        }
+    }
     return 0;
 }

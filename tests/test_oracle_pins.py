@@ -17,7 +17,10 @@ mathematics fix, never against itself.
     closed forms of the layer norm, its shift/scale invariance, and torch's
     fp64 linear and layer_norm;
   * Iwin's depthwise convolution: centre, corner and zero taps, and torch's
-    fp64 grouped conv2d.
+    fp64 grouped conv2d;
+  * LinMapper's in-window linear mapping: a full-grid brute force (its own
+    cells and window-local indices), the identity, and the attention output
+    when the matrix is the softmax weights.
 
 Each pin is a function of the oracle library handle so that
 tests/test_oracle_mutations.py can run the same pins against oracle builds
@@ -478,6 +481,36 @@ def pin_dwconv_closed_forms(lib):
     assert np.allclose(oracle.dwconv_add(v, w, b, out, lib=lib), ref, rtol=1e-13, atol=1e-13)
 
 
+def pin_window_linear(lib):
+    """LinMapper's in-window linear mapping (What Makes for Hierarchical Vision
+    Transformer?, abstract): equals the full-grid brute force (its own cells and
+    window-local indices, nothing shared with the oracle) in every partition
+    mode; the identity matrix returns v; and with A = the softmax weights of a
+    single unshifted window it reproduces the (pinned) attention output."""
+    rng = np.random.default_rng(17)
+    for (B, H, W, M, s, part) in [(2, 8, 12, 4, 2, "cyclic"), (1, 12, 12, 6, 3, "cyclic"), (1, 8, 8, 4, 0, "cyclic"),
+                                  (2, 8, 12, 4, 0, "interleaved"), (1, 9, 6, 3, 1, "cyclic")]:
+        heads, C, N = 2, 8, M * M
+        v = rng.standard_normal((B, H, W, C))
+        A = rng.standard_normal((heads, N, N))
+        b = rng.standard_normal((heads, N))
+        got = oracle.window_linear(v, A, b, heads=heads, M=M, shift=s, partition=part, lib=lib)
+        ref = bf.window_linear(v, A, b, heads=heads, M=M, shift=s, partition=part)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), (B, H, W, M, s, part)
+        eye = np.broadcast_to(np.eye(N), (heads, N, N))
+        assert np.allclose(oracle.window_linear(v, eye, None, heads=heads, M=M, shift=s, partition=part, lib=lib),
+                           v, atol=1e-15)
+    # one window over the grid: A = attention weights gives the attention output
+    M, heads, C = 4, 2, 16
+    q, k, v = (rng.standard_normal((1, M, M, C)) for _ in range(3))
+    tau = np.array([0.3, 0.7])
+    out, wts = oracle.window_attn(q, k, v, heads=heads, M=M, sim="cosine", pos="none", tau=tau,
+                                  return_weights=True, lib=lib)
+    A = np.asarray(wts).reshape(heads, M * M, M * M)
+    got = oracle.window_linear(v, A, None, heads=heads, M=M, lib=lib)
+    assert np.allclose(got, out, rtol=1e-12, atol=1e-12)
+
+
 PINS = {
     "worked_example": pin_worked_example,
     "cpb_vs_torch": pin_cpb_vs_torch,
@@ -497,6 +530,7 @@ PINS = {
     "qkv_split": pin_qkv_split,
     "post_norm_closed_forms": pin_post_norm_closed_forms,
     "dwconv_closed_forms": pin_dwconv_closed_forms,
+    "window_linear": pin_window_linear,
 }
 
 

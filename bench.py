@@ -19,7 +19,8 @@ Prints ONE JSON line.  `value` is tokens/s over the whole job.
 
 Other modes (same protocol, their own JSON line): --backward times the
 backward step; --branch times the attention branch of a block (input
-projection, table, attention, output projection with the residual post-norm).
+projection, table, attention, output projection with the residual post-norm);
+--linmapper times LinMapper's in-window linear mapping.
 """
 from __future__ import annotations
 
@@ -166,6 +167,9 @@ def main(argv=None) -> int:
     ap.add_argument("--branch", action="store_true",
                     help="time the whole attention branch instead: swin_qkv_proj, the CPB table, "
                          "swin_window_attn_fwd and swin_proj_post_norm (residual post-norm)")
+    ap.add_argument("--linmapper", action="store_true",
+                    help="time LinMapper's in-window linear mapping (swin_window_linear) on the "
+                         "workload's values instead of the attention")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run copies of known size for HBM-counter calibration: y = -x over "
                          "2^28 fp32 (whole lines), then an interleaved window gather and its "
@@ -206,6 +210,8 @@ def main(argv=None) -> int:
     if args.branch:
         del sets
         return bench_branch(args, wl, par, table, desc, stream)
+    if args.linmapper:
+        return bench_linmapper(args, wl, sets, nsets, stream)
 
     def step(i, timed=None):
         q, k, v, o = sets[i % nsets]
@@ -509,6 +515,74 @@ def bench_branch(args, wl, par, table, desc, stream) -> int:
                    "parallelism": "none (1 GPU)"},
         "roofline": kernels[dominant],
         "kernels": kernels,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+def bench_linmapper(args, wl, sets, nsets, stream) -> int:
+    """LinMapper's aggregation in place of the attention: per window and head
+    out = A_h v (+ bias), A_h an N x N matrix shared by all windows.
+    Algorithmic work per (window, head): 2 N^2 d flops, 2 N d es bytes (read v,
+    write out; the matrices, heads N^2 es bytes, counted once per launch)."""
+    import torch
+
+    from vision_transformer_windowed_partition_amd import binding
+
+    dev = torch.device("cuda:0")
+    N = wl.M * wl.M
+    gen = torch.Generator().manual_seed(3000)
+    A = (torch.randn((wl.heads, N, N), generator=gen) / math.sqrt(N)).to(sets[0][0].dtype).to(dev)
+    bias = (0.1 * torch.randn((wl.heads, N), generator=gen)).to(dev)
+
+    def step(i, timed=None):
+        q, k, v, o = sets[i % nsets]
+        if timed is not None:
+            timer.record(timed, False)
+        binding.swin_window_linear(v, A, bias, heads=wl.heads, M=wl.M, shift=wl.shift, partition=wl.partition,
+                                   out=o, stream=stream)
+        if timed is not None:
+            timer.record(timed, True)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    timer = HipTimer(args.steps, stream.cuda_stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = timer.elapsed_ms()
+    timer.close()
+    kern_avg = sum(kern_ms) / len(kern_ms)
+    es = wl.elem_size
+    flops = 2.0 * wl.tokens * N * wl.C
+    alg_bytes = 2.0 * wl.tokens * wl.C * es + wl.heads * N * N * es
+    peak_tf = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+    roof = _roof(flops, alg_bytes, kern_avg, peak_tf, "mfma" if wl.dtype == "bf16" else "alu")
+    fast = wl.dtype == "bf16" and wl.M in (8, 16)
+    roof.update({"kernel": "wlin_kernel" if fast else "wlin_valu_kernel", "kernel_ms": round(kern_avg, 5),
+                 "alg_flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes, "traffic": None})
+    out = {
+        "metric": "LinMapper in-window linear mapping tokens/s",
+        "value": round(wl.tokens / (wall / args.steps), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) values, randn/sqrt(N) window matrices)",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "W": wl.W, "C": wl.C, "heads": wl.heads,
+                   "M": wl.M, "shift": wl.shift, "partition": wl.partition, "pass": "linmapper",
+                   "cache": "warm" if args.warm else f"cold ({nsets} rotating sets)",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
     }
     print(json.dumps(out))
     return 0

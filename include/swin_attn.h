@@ -1,13 +1,16 @@
 /*
  * swin_attn.h -- C ABI of libswinattn.so: shifted-window / interleaved-window
- * multi-head self-attention forward on one AMD Instinct MI355X (gfx950).
+ * multi-head self-attention on one AMD Instinct MI355X (gfx950): forward,
+ * backward, the CPB table, and the steps around it in a block (projections,
+ * residual post-norm, Iwin's convolution, LinMapper's window mapping).
  *
  * Pages defining the operations (cited by title and section):
  *   [SwinV2] "Swin Transformer V2: Scaling Up Capacity and Resolution",
- *            paper card: Method items 2-3, eq. 1-4, the window-attention and
- *            continuous-bias pseudocode, Architecture table.
+ *            paper card: Method items 1-3, eq. 1-4, the window-attention,
+ *            continuous-bias and block pseudocode, Architecture table.
  *   [Flash]  "FLASHSWIN: Unlocking Large Windows and Dense Tokens in Swin
  *            Vision Transformers with Memory Efficient Attention", abstract.
+ *   [What]   "What Makes for Hierarchical Vision Transformer?", abstract.
  *   [Iwin]   "Iwin Transformer: Hierarchical Vision Transformer using
  *            Interleaved Windows", abstract.
  *
@@ -243,6 +246,23 @@ int swin_proj_post_norm(const void* o, const void* w, const float* b, const void
  * out is rounded once more after the add. */
 int swin_dwconv_add(const void* v, const float* w, const float* b, void* out, int32_t B, int32_t H,
                     int32_t W, int32_t C, int32_t dtype, void* stream);
+
+/* LinMapper's aggregation inside each window ([What] abstract: the
+ * self-attention of each non-overlapped window replaced by a linear mapping,
+ * Swin's cross-window communication kept).  Reading: per head h an N x N
+ * matrix A_h (N = M^2, shared by all windows) and an optional bias b_h:
+ *   out[i] = b_h[i] + sum_j A_h[i][j] v[j]
+ * over the head's channels, i, j window-local token indices (r M + c), the
+ * pairs of a shifted window's different regions excluded as in the
+ * attention.  desc as for swin_window_attn_fwd (sim, pos, tau_min and
+ * rope_base are not used).  v, out: (B, H, W, C) (or the WINDOWS layout) of
+ * desc->dtype; A: heads x N x N of the same dtype, row-major (A_h[i][j] at
+ * (h N + i) N + j); bias: heads x N fp32 or NULL.  v, A, out 16-byte aligned,
+ * out overlapping none of the inputs.  d = 32 (SWIN_EUNSUPPORTED otherwise).
+ * Arithmetic: bf16 on the matrix cores with fp32 accumulation for M = 8 and
+ * 16, fp32 on the vector ALUs otherwise; the output rounded once. */
+int swin_window_linear(const swin_attn_desc* desc, const void* v, const void* A, const float* bias,
+                       void* out, void* stream);
 
 /* Name of the kernel that swin_window_attn_fwd launches for desc (static
  * storage), for matching profiler output:

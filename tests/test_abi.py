@@ -37,6 +37,7 @@ def test_header_declares_the_boundary():
                                            "swin_window_attn_fwd", "swin_window_attn_kernel",
                                            "swin_window_attn_bwd_kernel",
                                            "swin_qkv_proj", "swin_proj_post_norm", "swin_dwconv_add",
+                                           "swin_window_linear",
                                            "swin_status_string",
                                            "swin_last_error", "swin_version"])
 
@@ -161,6 +162,21 @@ def test_dwconv_rejects(L):
     assert L.swin_dwconv_add(FAKE, w, None, ctypes.c_void_p(0x10000 + 64), 1, 8, 8, 32, 1, None) == SWIN_EINVAL
     assert L.swin_dwconv_add(FAKE, ctypes.c_void_p(0x30000002), None, out, 1, 8, 8, 32, 1, None) == SWIN_EINVAL
     assert L.swin_dwconv_add(None, None, None, None, 0, 8, 8, 32, 1, None) == SWIN_OK           # empty batch
+
+
+def test_window_linear_rejects(L):
+    """Host validation of the in-window linear mapping: nothing is launched."""
+    out = ctypes.c_void_p(0x60000000)
+    A = ctypes.c_void_p(0x30000000)
+    f = lambda d, v=FAKE, A=A, b=None, o=out: L.swin_window_linear(ctypes.byref(d) if d else None, v, A, b, o, None)
+    assert f(None) == SWIN_EINVAL
+    assert f(_desc(H=12)) == SWIN_EUNSUPPORTED                      # H % M
+    assert f(_desc(C=96, heads=2)) == SWIN_EUNSUPPORTED             # head dim 48
+    assert f(_desc(), v=None) == SWIN_EINVAL
+    assert f(_desc(), A=ctypes.c_void_p(0x30000008)) == SWIN_EINVAL # misaligned
+    assert f(_desc(), o=ctypes.c_void_p(0x10000 + 64)) == SWIN_EINVAL   # out overlaps v
+    assert f(_desc(), o=ctypes.c_void_p(0x30000000 - 64)) == SWIN_EINVAL # out overlaps A
+    assert f(_desc(B=0), v=None, A=None, o=None) == SWIN_OK         # empty batch
 
 
 def test_backward_rejects(L):

@@ -1,0 +1,84 @@
+"""GPU parity of LinMapper's in-window linear mapping (swin_window_linear)
+against the fp64 oracle, through the C ABI.
+
+Bar, from the arithmetic: bf16 products of bf16 inputs are exact in fp32 and
+summed in fp32 over at most N terms, and each output is rounded once, so
+every element is within 2^-8 |ref| + 1e-3 (one bf16 ulp, with a floor near
+zero where the fp32 sum's own error can move the rounding); fp32 within
+1e-5 |ref| + 1e-4."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_helpers import f64
+from vision_transformer_windowed_partition_amd import binding
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = {"bf16": (2.0 ** -8, 1e-3), "f32": (1e-5, 1e-4)}
+
+CASES = [
+    # B, H, W, M, shift, partition (M = 8, 16 bf16: matrix cores; others: vector ALUs)
+    (2, 16, 16, 8, 4, "cyclic"),
+    (2, 32, 32, 16, 8, "cyclic"),
+    (1, 16, 24, 8, 0, "interleaved"),
+    (1, 32, 48, 16, 0, "cyclic"),
+    (1, 12, 12, 6, 3, "cyclic"),
+    (1, 24, 24, 12, 5, "cyclic"),
+    (1, 8, 8, 8, 3, "cyclic"),            # one window row and column: every region
+]
+
+
+def _check(name, got, ref, dtype):
+    rel, absl = TOL[dtype]
+    err = np.abs(got - ref)
+    bound = rel * np.abs(ref) + absl
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert np.all(np.isfinite(got)), name
+    assert np.all(err <= bound), f"{name}: err {err[worst]:.3e} at {worst} > {bound[worst]:.3e}"
+
+
+def _inputs(B, H, W, M, heads, dtype, seed):
+    gen = torch.Generator().manual_seed(seed)
+    N = M * M
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    v = torch.randn((B, H, W, 32 * heads), generator=gen).to(dt)
+    A = (torch.randn((heads, N, N), generator=gen) / np.sqrt(N)).to(dt)
+    b = 0.1 * torch.randn((heads, N), generator=gen)
+    return v, A, b
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[1]}x{c[2]}-M{c[3]}-s{c[4]}-{c[5][:3]}" for c in CASES])
+def test_window_linear(case, dtype):
+    B, H, W, M, s, part = case
+    heads = 2
+    v, A, b = _inputs(B, H, W, M, heads, dtype, seed=H * 100 + M)
+    got = binding.swin_window_linear(v.to(DEV), A.to(DEV), b.to(DEV), heads=heads, M=M, shift=s, partition=part)
+    torch.cuda.synchronize()
+    ref = oracle.window_linear(f64(v), f64(A), f64(b), heads=heads, M=M, shift=s, partition=part)
+    _check(f"{case}", f64(got), ref, dtype)
+    got0 = binding.swin_window_linear(v.to(DEV), A.to(DEV), None, heads=heads, M=M, shift=s, partition=part)
+    torch.cuda.synchronize()
+    _check(f"{case} no bias", f64(got0), oracle.window_linear(f64(v), f64(A), None, heads=heads, M=M, shift=s,
+                                                              partition=part), dtype)
+
+
+def test_window_linear_empty():
+    v = torch.empty((0, 16, 16, 64), dtype=torch.bfloat16, device=DEV)
+    A = torch.zeros((2, 64, 64), dtype=torch.bfloat16, device=DEV)
+    assert binding.swin_window_linear(v, A, None, heads=2, M=8).numel() == 0
+
+
+@pytest.mark.parametrize("B,H,W,C,heads,M,s,part", [(64, 64, 64, 192, 6, 8, 0, "interleaved"),
+                                                    (64, 64, 64, 96, 3, 16, 8, "cyclic")])
+def test_window_linear_full_size(B, H, W, C, heads, M, s, part):
+    """The full grids of the interleaved and headline workloads, checked on
+    three whole images."""
+    v, A, b = _inputs(B, H, W, M, heads, "bf16", seed=M)
+    got = binding.swin_window_linear(v.to(DEV), A.to(DEV), b.to(DEV), heads=heads, M=M, shift=s, partition=part)
+    torch.cuda.synchronize()
+    imgs = [0, 31, B - 1]
+    ref = oracle.window_linear(f64(v[imgs]), f64(A), f64(b), heads=heads, M=M, shift=s, partition=part)
+    _check("full size", f64(got[imgs]), ref, "bf16")

@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.swin_proj_post_norm.argtypes = [vp] * 6 + [ctypes.c_float, vp, ctypes.c_int64, i32, i32, vp]
         L.swin_dwconv_add.restype = i32
         L.swin_dwconv_add.argtypes = [vp] * 4 + [i32] * 5 + [vp]
+        L.swin_window_linear.restype = i32
+        L.swin_window_linear.argtypes = [ctypes.POINTER(SwinAttnDesc)] + [vp] * 5
         L.swin_window_attn_kernel.restype = ctypes.c_char_p
         L.swin_window_attn_kernel.argtypes = [ctypes.POINTER(SwinAttnDesc)]
         L.swin_window_attn_bwd_kernel.restype = ctypes.c_char_p
@@ -306,6 +308,24 @@ def swin_dwconv_add(v, w, b, out, *, stream=None):
     _check(lib().swin_dwconv_add(_ptr(v), _ptr(w), _ptr(b), _ptr(out), B, H, W, C, _proj_dtype(v),
                                  _stream(v, stream)))
     return out
+
+
+def swin_window_linear(v, A, bias=None, *, heads: int, M: int, shift: int = 0, partition="cyclic", out=None,
+                       stream=None):
+    """LinMapper's in-window linear mapping: per window and head
+    out_i = bias_h[i] + sum_j A_h[i][j] v_j (shifted-window regions excluded).
+    v (B, H, W, C); A (heads, M*M, M*M) in v's dtype; bias (heads, M*M) fp32."""
+    B, H, W, C = v.shape
+    N = M * M
+    if A.dtype != v.dtype or tuple(A.shape) != (heads, N, N) or not (A.is_contiguous() and v.is_contiguous()):
+        raise ValueError("A must be a contiguous (heads, M*M, M*M) tensor of v's dtype")
+    if bias is not None and (bias.dtype != torch.float32 or tuple(bias.shape) != (heads, N) or not bias.is_contiguous()):
+        raise ValueError("bias must be contiguous fp32 (heads, M*M)")
+    desc = make_desc(B=B, H=H, W=W, C=C, heads=heads, M=M, shift=shift, partition=partition, sim="dot",
+                     pos="none", dtype=v.dtype)
+    o = out if out is not None else torch.empty_like(v)
+    _check(lib().swin_window_linear(ctypes.byref(desc), _ptr(v), _ptr(A), _ptr(bias), _ptr(o), _stream(v, stream)))
+    return o
 
 
 def swin_window_attn_kernel(desc: SwinAttnDesc) -> str:

@@ -337,6 +337,29 @@ int swin_dwconv_add(const void* v, const float* w, const float* b, void* out, in
     return hip_status(swin::launch_dwconv_add(a, (hipStream_t)stream), "swin_dwconv_add launch");
 }
 
+int swin_window_linear(const swin_attn_desc* d, const void* v, const void* A, const float* bias, void* out,
+                       void* stream)
+{
+    int st = check_desc(d, true);
+    if (st) return st;
+    if (d->C != d->heads * 32) return fail(SWIN_EUNSUPPORTED, "window linear: head dim %d (32 only)", d->C / d->heads);
+    const size_t es = d->dtype == SWIN_DT_F32 ? 4 : 2;
+    const size_t bytes = (size_t)d->B * d->H * d->W * d->C * es;
+    if (bytes == 0) return SWIN_OK;
+    const size_t N = (size_t)d->M * d->M;
+    const size_t abytes = (size_t)d->heads * N * N * es;
+    if (!v || !A || !out) return fail(SWIN_EINVAL, "NULL v, A or out");
+    if (((uintptr_t)v | (uintptr_t)out | (uintptr_t)A) & 15) return fail(SWIN_EINVAL, "v, A and out must be 16-byte aligned");
+    if ((uintptr_t)bias & 3) return fail(SWIN_EINVAL, "bias must be 4-byte aligned");
+    if (overlaps(out, bytes, v, bytes) || overlaps(out, bytes, A, abytes) ||
+        (bias && overlaps(out, bytes, bias, (size_t)d->heads * N * 4)))
+        return fail(SWIN_EINVAL, "out overlaps v, A or bias");
+    swin::AttnParams p = params_of(d);
+    p.v = v; p.out = out;
+    const swin::WlinArgs la{A, bias};
+    return hip_status(swin::launch_window_linear(p, la, (hipStream_t)stream), "swin_window_linear launch");
+}
+
 int swin_cpb_table_bwd(int32_t M, int32_t norm_M, int32_t heads, int32_t hidden, const float* w1,
                        const float* b1, const float* w2, const float* table, const float* dtable,
                        int32_t cpb_mode, float* dw1, float* db1, float* dw2, float* db2, void* stream)

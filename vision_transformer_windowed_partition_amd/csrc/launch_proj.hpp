@@ -1,9 +1,12 @@
-// Launch entries of the kernels either side of the attention (proj.hip,
-// dwconv.hip), called by api.hip after the host-side validation.
+// Launch entries of the kernels either side of the attention and of its
+// alternatives (proj.hip, dwconv.hip, window_linear.hip), called by api.hip
+// after the host-side validation.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "launch.hpp"
 
 namespace swin {
 
@@ -30,9 +33,16 @@ struct DwconvArgs {
     int dtype;
 };
 
+struct WlinArgs {
+    const void* A;             // heads x N x N, the features' dtype
+    const float* bias;         // heads x N, or nullptr
+};
+
 bool proj_supported(int C);
 bool dwconv_supported(int C, int dtype);
 hipError_t launch_dwconv_add(const DwconvArgs& a, hipStream_t stream);
+// p: geometry, dtype, v and out of the window mapping (launch.hpp)
+hipError_t launch_window_linear(const AttnParams& p, const WlinArgs& la, hipStream_t stream);
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t stream);
 hipError_t launch_proj_norm(const ProjArgs& a, hipStream_t stream);
 

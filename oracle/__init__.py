@@ -7,7 +7,8 @@ package never imports the GPU library: the two share no code.
 Contents
   * ``oracle.c`` (compiled with gcc into ``liboracle.so``): the plain per-window
     definition -- partition / reverse maps, log-spaced offsets, the CPB table,
-    the attention itself and its backward, the attention branch's linear
+    the attention itself (with the log-sum-exp a backward
+    reuses) and its backward, the attention branch's linear
     layers and residual post-norm, Iwin's depthwise convolution branch and
     LinMapper's in-window linear mapping, all in fp64.
   * ``bruteforce.py``: full-grid attention over every token pair with a mask, for
@@ -64,7 +65,7 @@ def _declare(lib):
         fn.restype = i32
         fn.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
     lib.oracle_window_attn.restype = i32
-    lib.oracle_window_attn.argtypes = [i32] * 10 + [dbl, dbl] + [vp] * 7 + [i64, vp, vp]
+    lib.oracle_window_attn.argtypes = [i32] * 10 + [dbl, dbl] + [vp] * 7 + [i64, vp, vp, vp]
     lib.oracle_window_attn_bwd.restype = i32
     lib.oracle_window_attn_bwd.argtypes = [i32] * 10 + [dbl, dbl] + [vp] * 12
     lib.oracle_cpb_table_bwd.restype = i32
@@ -176,15 +177,17 @@ def reverse(xw: np.ndarray, B: int, H: int, W: int, M: int, shift: int, part: st
 def window_attn(q, k, v, *, heads: int, M: int, shift: int = 0, partition: str = "cyclic",
                 sim: str = "cosine", pos: str = "none", tau=None, table=None,
                 rope_freqs=None, rope_base: float = 10000.0, tau_min: float = 0.01,
-                windows=None, return_weights: bool = False, out=None, lib=None):
+                windows=None, return_weights: bool = False, out=None, return_lse: bool = False, lib=None):
     """Windowed attention forward in fp64.
 
     q, k, v: (B, H, W, C) arrays (converted exactly to fp64).  tau: (heads,);
     table: ((2M-1)^2, heads); rope_freqs: (heads, 2, d/4) or None for the
     base-``rope_base`` schedule.  ``windows``: optional global window ids to
     compute (the rest of ``out`` stays as given, zeros by default).
-    Returns ``out`` (B, H, W, C) fp64, plus the weights
-    (n_windows, heads, N, N) when ``return_weights``.
+    Returns ``out`` (B, H, W, C) fp64, followed by the weights
+    (n_windows, heads, N, N) when ``return_weights`` and the per-query
+    natural-log log-sum-exp of the logits (n_windows, heads, N) when
+    ``return_lse``.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, W, C = q.shape
@@ -196,14 +199,16 @@ def window_attn(q, k, v, *, heads: int, M: int, shift: int = 0, partition: str =
     nwin = (B * (H // M) * (W // M)) if win is None else len(win)
     N = M * M
     wts = np.empty((nwin, heads, N, N), dtype=np.float64) if return_weights else None
+    lse = np.empty((nwin, heads, N), dtype=np.float64) if return_lse else None
     rc = (lib or load()).oracle_window_attn(
         B, H, W, C, heads, M, shift, PART[partition], SIM[sim], POS[pos],
         float(tau_min), float(rope_base), _ptr(q), _ptr(k), _ptr(v), _ptr(tau),
         _ptr(table), _ptr(rope_freqs), _ptr(win), 0 if win is None else len(win),
-        _ptr(out), _ptr(wts))
+        _ptr(out), _ptr(wts), _ptr(lse))
     if rc:
         raise ValueError(f"oracle_window_attn: bad argument (rc={rc})")
-    return (out, wts) if return_weights else out
+    res = (out,) + ((wts,) if return_weights else ()) + ((lse,) if return_lse else ())
+    return res if len(res) > 1 else out
 
 
 def window_attn_bwd(q, k, v, dout, *, heads: int, M: int, shift: int = 0, partition: str = "cyclic",

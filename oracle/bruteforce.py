@@ -70,12 +70,14 @@ def _rotate(x: np.ndarray, rows: np.ndarray, cols: np.ndarray, freqs) -> np.ndar
 def window_attn(q, k, v, *, heads: int, M: int, shift: int = 0, partition: str = "cyclic",
                 sim: str = "cosine", pos: str = "none", tau=None, mlp=None,
                 table_fn=None, rope_freqs=None, rope_base: float = 10000.0,
-                tau_min: float = 0.01, return_weights: bool = False):
+                tau_min: float = 0.01, return_weights: bool = False, return_lse: bool = False):
     """Full-grid masked attention; same meaning of arguments as the oracle.
 
     The bias comes from ``mlp = (w1, b1, w2, b2)`` (G evaluated per offset), or
     from ``table_fn(dy, dx) -> (..., heads)`` when a caller-made table is tested.
-    Returns out (B, H, W, C) and optionally the (B, heads, P, P) weights.
+    Returns out (B, H, W, C), then optionally the (B, heads, P, P) weights
+    and the (B, heads, P) natural-log log-sum-exp of each token's allowed
+    logits.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -100,6 +102,7 @@ def window_attn(q, k, v, *, heads: int, M: int, shift: int = 0, partition: str =
             bias = g[inv.ravel()].reshape(P, P, heads)
     out = np.zeros((B, H, W, C))
     wts = np.zeros((B, heads, P, P)) if return_weights else None
+    lse = np.zeros((B, heads, P)) if return_lse else None
     for h in range(heads):
         if pos == "rope2d":
             if rope_freqs is None:
@@ -128,7 +131,11 @@ def window_attn(q, k, v, *, heads: int, M: int, shift: int = 0, partition: str =
             out[b].reshape(P, C)[:, h * d:(h + 1) * d] = p @ vh
             if return_weights:
                 wts[b, h] = p
-    return (out, wts) if return_weights else out
+            if return_lse:
+                mx = logits.max(axis=1)
+                lse[b, h] = mx + np.log(np.exp(logits - mx[:, None]).sum(axis=1))
+    res = (out,) + ((wts,) if return_weights else ()) + ((lse,) if return_lse else ())
+    return res if len(res) > 1 else out
 
 
 def pair_allowed(H: int, W: int, M: int, shift: int, partition: str) -> np.ndarray:

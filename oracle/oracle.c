@@ -284,6 +284,8 @@ static void unit_normalize(double* x, int d)
  * windows: optional list of global window ids (b*nW + wr*(W/M) + wc) to
  * compute; NULL means all.  Only those windows' tokens of `out` are written.
  * weights: optional n_windows x heads x N x N array of the softmax weights.
+ * lse: optional n_windows x heads x N array: per query, the natural-log
+ *      log-sum-exp of its row of logits over the keys it may attend to.
  * Returns 0, or 1 on a bad argument.
  */
 int oracle_window_attn(int B, int H, int W, int C, int heads, int M, int shift,
@@ -291,7 +293,7 @@ int oracle_window_attn(int B, int H, int W, int C, int heads, int M, int shift,
                        const double* q, const double* k, const double* v,
                        const double* tau, const double* table, const double* rope_freqs,
                        const int64_t* windows, int64_t n_windows,
-                       double* out, double* weights)
+                       double* out, double* weights, double* lse)
 {
     if (bad_shape(B, H, W, C, M, shift, part)) return 1;
     if (heads < 1 || C % heads) return 1;
@@ -388,6 +390,9 @@ int oracle_window_attn(int B, int H, int W, int C, int heads, int M, int shift,
                         sum += lg[j];
                     }
                     for (int j = 0; j < N; ++j) lg[j] /= sum;
+                    /* log-sum-exp of the row's logits (natural log): what a
+                       backward needs to rebuild the weights */
+                    if (lse) lse[((size_t)wi * heads + h) * N + i] = mx + log(sum);
                     if (weights) {
                         double* wrow = weights + (((size_t)wi * heads + h) * N + i) * (size_t)N;
                         for (int j = 0; j < N; ++j) wrow[j] = lg[j];

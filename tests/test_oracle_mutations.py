@@ -74,6 +74,10 @@ MUTATIONS = [
      "if (yy < 0 || yy >= H || xx < 0 || xx >= W || (dy == 1 && dx == 1)) continue;"),
     ("dwconv_bias_dropped", "double s = b ? b[c] : 0.0;", "double s = 0.0;"),
     ("dwconv_overwrites", "out[i] += tmp[i];", "out[i] = tmp[i];"),
+    ("lse_max_dropped", "lse[((size_t)wi * heads + h) * N + i] = mx + log(sum);",
+     "lse[((size_t)wi * heads + h) * N + i] = log(sum);"),
+    ("lse_head_index", "lse[((size_t)wi * heads + h) * N + i] = mx + log(sum);",
+     "lse[((size_t)wi * heads + (heads - 1 - h)) * N + i] = mx + log(sum);"),
     ("wl_region_ignored", "if (reg_j != reg_i) continue;", "if (0) continue;"),
     ("wl_A_transposed", "A[((size_t)h * N + i) * N + j]", "A[((size_t)h * N + j) * N + i]"),
     ("wl_bias_index", "bias[(size_t)h * N + i]", "bias[(size_t)h * N + (N - 1 - i)]"),

@@ -167,6 +167,47 @@ def pin_bruteforce(lib):
         assert err < 1e-12, (case, err)
 
 
+def pin_lse(lib):
+    """The log-sum-exp the forward exports for a backward: on the tiny grids
+    of every mode it equals the full-grid masked attention's, token by token
+    (the oracle's (window, head, slot) order mapped to grid tokens by the
+    partition); for one unshifted window it equals torch's logsumexp of
+    logits formed here from normalised q, k, the scale and the bias."""
+    for case in BRUTE_CASES:
+        H, W, M, s, part, sim, pos = case
+        wl = synth.small(B=2, H=H, W=W, C=32, heads=2, M=M, shift=s, partition=part,
+                         sim=sim, pos=pos, hidden=16)
+        x = _inputs(wl, seed=6, tau_range=(0.05, 1.0))
+        mlp = (x["w1"], x["b1"], x["w2"], x["b2"])
+        tab = oracle.cpb_table(M, *mlp, lib=lib) if pos == "table" else None
+        _, lo = oracle.window_attn(x["q"], x["k"], x["v"], heads=2, M=M, shift=s, partition=part,
+                                   sim=sim, pos=pos, tau=x["tau"], table=tab, return_lse=True, lib=lib)
+        _, lb = bf.window_attn(x["q"], x["k"], x["v"], heads=2, M=M, shift=s, partition=part,
+                               sim=sim, pos=pos, tau=x["tau"], mlp=mlp, return_lse=True)
+        tok = oracle.partition(np.arange(2 * H * W, dtype=np.int64).reshape(2, H, W, 1), M, s, part,
+                               lib=lib)[:, :, 0]                      # (windows, N) global token ids
+        want = lb.transpose(0, 2, 1).reshape(2 * H * W, 2)[tok]      # (windows, N, heads)
+        err = np.abs(lo - want.transpose(0, 2, 1)).max()
+        assert err < 1e-12, (case, err)
+    M = 5
+    wl = synth.small(B=1, H=M, W=M, C=64, heads=2, M=M, shift=0, sim="cosine", pos="table", hidden=32)
+    x = _inputs(wl, seed=11, tau_range=(0.003, 1.0))
+    mlp = (x["w1"], x["b1"], x["w2"], x["b2"])
+    tab = oracle.cpb_table(M, *mlp, lib=lib)
+    _, lo = oracle.window_attn(x["q"], x["k"], x["v"], heads=2, M=M, sim="cosine", pos="table",
+                               tau=x["tau"], table=tab, return_lse=True, lib=lib)
+    d, N = 32, M * M
+    rr, cc = np.divmod(np.arange(N), M)
+    for h in range(2):
+        q = torch.from_numpy(x["q"].reshape(N, 64)[:, h * d:(h + 1) * d])
+        k = torch.from_numpy(x["k"].reshape(N, 64)[:, h * d:(h + 1) * d])
+        bias = torch.from_numpy(bf.meta_network(cc[:, None] - cc[None, :], rr[:, None] - rr[None, :],
+                                                *mlp)[:, :, h])
+        qn, kn = F.normalize(q, dim=-1, eps=1e-12), F.normalize(k, dim=-1, eps=1e-12)
+        logits = qn @ kn.T / max(float(x["tau"][h]), 0.01) + bias
+        np.testing.assert_allclose(lo[0, h], torch.logsumexp(logits, dim=1).numpy(), rtol=0, atol=1e-12)
+
+
 def pin_rope_freq_table(lib):
     """A per-head frequency table reaches the same result as the brute force."""
     H = W = 8
@@ -531,6 +572,7 @@ PINS = {
     "post_norm_closed_forms": pin_post_norm_closed_forms,
     "dwconv_closed_forms": pin_dwconv_closed_forms,
     "window_linear": pin_window_linear,
+    "lse": pin_lse,
 }
 
 

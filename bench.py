@@ -164,6 +164,9 @@ def main(argv=None) -> int:
     ap.add_argument("--backward", action="store_true",
                     help="time the backward step instead: swin_window_attn_bwd (dq, dk, dv, dtau, dtable) "
                          "and swin_cpb_table_bwd, from one forward's output")
+    ap.add_argument("--own-lse", action="store_true",
+                    help="with --backward: the backward recomputes the softmax statistics instead of "
+                         "taking the forward's log-sum-exp")
     ap.add_argument("--branch", action="store_true",
                     help="time the whole attention branch instead: swin_qkv_proj, the CPB table, "
                          "swin_window_attn_fwd and swin_proj_post_norm (residual post-norm)")
@@ -312,7 +315,9 @@ def bench_backward(args, wl, x, sets, nsets, par, table, desc, stream) -> int:
     the meta network's parameter gradients from dtable.  Algorithmic work per
     (window, head): the five N x N x d contractions of the backward (scores
     recomputed, dP, dV, dQ, dK: 10 N^2 d flops) and 8 N d elements moved
-    (read q, k, v, out, dout; write dq, dk, dv)."""
+    (read q, k, v, out, dout; write dq, dk, dv), plus N fp32 statistics
+    read when the forward's log-sum-exp is given (the default; --own-lse
+    recomputes them)."""
     import torch
 
     from vision_transformer_windowed_partition_amd import binding, synth
@@ -321,8 +326,15 @@ def bench_backward(args, wl, x, sets, nsets, par, table, desc, stream) -> int:
     if wl.pos == "table":
         tab = binding.swin_cpb_table(wl.M, par["w1"], par["b1"], par["w2"], par["b2"], out=table)
     dout = synth.make_dout(wl).to(sets[0][0].device)
+    use_lse = not args.own_lse
+    lses = []
     for q, k, v, o in sets:
-        binding.swin_window_attn_fwd(q, k, v, heads=wl.heads, M=wl.M, desc=desc, tau=par["tau"], table=tab, out=o)
+        if use_lse:
+            lses.append(binding.swin_window_attn_fwd_lse(q, k, v, heads=wl.heads, M=wl.M, desc=desc, tau=par["tau"],
+                                                         table=tab, out=o)[1])
+        else:
+            binding.swin_window_attn_fwd(q, k, v, heads=wl.heads, M=wl.M, desc=desc, tau=par["tau"], table=tab,
+                                         out=o)
     torch.cuda.synchronize()
     kw = dict(heads=wl.heads, M=wl.M, shift=wl.shift, partition=wl.partition, sim=wl.sim, pos=wl.pos,
               tau=par["tau"], table=tab, rope_base=wl.rope_base, desc=desc, stream=stream)
@@ -331,7 +343,7 @@ def bench_backward(args, wl, x, sets, nsets, par, table, desc, stream) -> int:
         q, k, v, o = sets[i % nsets]
         if timed is not None:
             timer.record(timed, False)
-        g = binding.swin_window_attn_bwd(q, k, v, o, dout, **kw)
+        g = binding.swin_window_attn_bwd(q, k, v, o, dout, lse=lses[i % nsets] if use_lse else None, **kw)
         if timed is not None:
             timer.record(timed, True)
         if wl.pos == "table":
@@ -351,7 +363,7 @@ def bench_backward(args, wl, x, sets, nsets, par, table, desc, stream) -> int:
     timer.close()
     kern_avg = sum(kern_ms) / len(kern_ms)
     flops = int(2.5 * wl.flops)
-    alg_bytes = 2 * wl.bytes
+    alg_bytes = 2 * wl.bytes + (wl.tokens * wl.heads * 4 if use_lse else 0)
     kern_s = kern_avg * 1e-3
     tflops = flops / kern_s / 1e12
     kernel = binding.swin_window_attn_bwd_kernel(desc)
@@ -387,6 +399,7 @@ def bench_backward(args, wl, x, sets, nsets, par, table, desc, stream) -> int:
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "W": wl.W, "C": wl.C, "heads": wl.heads,
                    "M": wl.M, "shift": wl.shift, "partition": wl.partition, "sim": wl.sim,
                    "pos": wl.pos, "pass": "backward",
+                   "softmax_stats": "forward's log-sum-exp" if use_lse else "recomputed",
                    "cache": "warm" if args.warm else f"cold ({nsets} rotating sets)",
                    "parallelism": "none (1 GPU)"},
         "tflops": round(tflops, 2),

@@ -158,6 +158,23 @@ int swin_window_attn_fwd(const swin_attn_desc* desc, const void* q, const void* 
                          const void* v, void* out, const float* tau, const float* table,
                          const float* rope_freqs, void* stream);
 
+/* swin_window_attn_fwd that also exports, per window, head and query, the
+ * log-sum-exp of the query's logits over the keys it attends to ([Flash]
+ * introduction: training with exact attention and no score matrix; the
+ * per-query softmax statistic is what lets a backward rebuild the weights
+ * without a pass of its own):
+ *   lse[(w*heads + h)*N + i] = log sum_j exp(logit_ij), natural log,
+ * w the global window id (image-major, window rows, then columns), i the
+ * query's local slot r*M + c.  lse: device fp32, n_windows x heads x N,
+ * 4-byte aligned, written; it must not overlap q, k, v or out (SWIN_EINVAL,
+ * also for NULL with a non-empty batch).  For SWIN_DT_BF16 it is formed
+ * from the same rounded weights that normalise out (the softmax's fp32 sum
+ * of bf16 weights), so the two agree; windows above M = 32 run the fp32
+ * vector kernel when lse is requested. */
+int swin_window_attn_fwd_lse(const swin_attn_desc* desc, const void* q, const void* k,
+                             const void* v, void* out, const float* tau, const float* table,
+                             const float* rope_freqs, float* lse, void* stream);
+
 /* Backward of swin_window_attn_fwd: the gradients of a loss L given
  * dout = dL/dout, by the chain rule through the same steps ([SwinV2] eq. 1-2,
  * eq. 3-4 for the table, [Flash] for the rotary variant):
@@ -187,6 +204,20 @@ int swin_window_attn_bwd(const swin_attn_desc* desc, const void* q, const void* 
                          const void* v, const void* out, const void* dout, const float* tau,
                          const float* table, const float* rope_freqs, void* dq, void* dk,
                          void* dv, float* dtau, float* dtable, void* stream);
+
+/* swin_window_attn_bwd given the forward's log-sum-exp ([Flash]
+ * introduction, as for swin_window_attn_fwd_lse): lse as written by
+ * swin_window_attn_fwd_lse for the same inputs (device fp32, n_windows x
+ * heads x N, natural log, 4-byte aligned, read only).  The matrix-core paths
+ * rebuild p_ij = exp(logit_ij - lse_i) from it and skip their own pass over
+ * the keys; the fp32 vector path (SWIN_DT_F32, and COSINE with ROPE2D)
+ * recomputes the statistics and does not read it.  Other arguments, results
+ * and errors as swin_window_attn_bwd; NULL lse with a non-empty batch is
+ * SWIN_EINVAL. */
+int swin_window_attn_bwd_lse(const swin_attn_desc* desc, const void* q, const void* k,
+                             const void* v, const void* out, const void* dout, const float* tau,
+                             const float* table, const float* rope_freqs, const float* lse, void* dq,
+                             void* dk, void* dv, float* dtau, float* dtable, void* stream);
 
 /* Backward of swin_cpb_table_ex ([SwinV2] eq. 3-4, card "Paper vs code"):
  * from dtable ((2M-1)^2 x heads fp32) the gradients of the meta network's

@@ -35,6 +35,7 @@ def test_header_declares_the_boundary():
                                            "swin_window_attn_bwd", "swin_window_partition",
                                            "swin_window_reverse",
                                            "swin_window_attn_fwd", "swin_window_attn_kernel",
+                                           "swin_window_attn_fwd_lse", "swin_window_attn_bwd_lse",
                                            "swin_window_attn_bwd_kernel",
                                            "swin_qkv_proj", "swin_proj_post_norm", "swin_dwconv_add",
                                            "swin_window_linear",
@@ -112,6 +113,24 @@ def _bwd(L, desc, q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, dq=ctypes.c_void_
          dtau=None, dtable=None):
     return L.swin_window_attn_bwd(ctypes.byref(desc) if desc is not None else None, q, k, v, out, dout, tau,
                                   table, None, dq, dk, dv, dtau, dtable, None)
+
+
+def test_lse_entries_reject(L):
+    """The log-sum-exp variants: a missing, misaligned or overlapping lse is
+    refused before anything is launched."""
+    d = _desc()
+    fwd = lambda lse, out=ctypes.c_void_p(0x20000000): L.swin_window_attn_fwd_lse(
+        ctypes.byref(d), FAKE, FAKE, FAKE, out, FAKE, FAKE, None, lse, None)
+    assert fwd(None) == SWIN_EINVAL
+    assert fwd(ctypes.c_void_p(0x30000002)) == SWIN_EINVAL                  # misaligned
+    assert fwd(ctypes.c_void_p(0x20000000 + 64)) == SWIN_EINVAL             # overlaps out
+    assert fwd(ctypes.c_void_p(0x10000 + 4096)) == SWIN_EINVAL              # overlaps q
+    bwd = lambda lse: L.swin_window_attn_bwd_lse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                                 lse, ctypes.c_void_p(0x20000000), ctypes.c_void_p(0x30000000),
+                                                 ctypes.c_void_p(0x40000000), None, None, None)
+    assert bwd(None) == SWIN_EINVAL
+    assert bwd(ctypes.c_void_p(0x50000001)) == SWIN_EINVAL                  # misaligned
+    assert L.swin_window_attn_fwd_lse(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == SWIN_EINVAL
 
 
 def _qkv(L, x=FAKE, w=ctypes.c_void_p(0x30000000), b=None, q=ctypes.c_void_p(0x40000000),

@@ -14,7 +14,16 @@ forward output induces: D_i = dout_i . out_i enters every dl_ij = p_ij (dP_ij
 dD_i E_p[cos]_i, at most sum_i |dD_i| / tau_h^2 (|cos| <= 1), and a table
 entry by at most sum_i |dD_i| (sum_j p_ij = 1); dD_i is measured against the
 oracle's fp64 forward.  These sums cancel (sum_j dl_ij = 0), so their error is
-not bounded by a fraction of their own size."""
+not bounded by a fraction of their own size.
+
+Given the forward's log-sum-exp (swin_window_attn_bwd_lse), the weights are
+rebuilt as p_ij = exp(logit_ij - lse_i): an error e_i of lse_i scales query
+i's row by exp(-e_i), which moves its share of dtau by at most
+|e_i| sum_j p_ij |dP_ij - D_i| / tau_h^2 <= |e_i| 2 ||dout_i|| max_j ||v_j|| /
+tau_h^2 (dP_ij = dout_i . v_j, ||out_i|| <= max_j ||v_j||) and a table entry
+by at most |e_i| 2 ||dout_i|| max_j ||v_j||; e_i is measured against the
+oracle's log-sum-exp and these sums join the allowance.  dq, dk, dv keep
+their bars (a row scaled by 1 + e_i is a relative error)."""
 import numpy as np
 import pytest
 import torch
@@ -59,21 +68,37 @@ def _check(name, got, ref, dtype, extra=0.0):
     assert err <= tmax and rel <= trel, f"{name}: max-abs/scale {err:.3e} rel-fro {rel:.3e} > {TOL[dtype]}"
 
 
-def _run(wl, x, g, dout, table=None, table64=None):
-    out = run_gpu(wl, g, table=table)
-    got = binding.swin_window_attn_bwd(g["q"], g["k"], g["v"], out, dout.to(DEV), heads=wl.heads, M=wl.M,
-                                       shift=wl.shift, partition=wl.partition, sim=wl.sim, pos=wl.pos,
-                                       tau=g["tau"], table=table, rope_base=wl.rope_base)
-    torch.cuda.synchronize()
+def _run(wl, x, g, dout, table=None, table64=None, lse_from=None):
+    """lse_from: None (the backward's own statistics), "gpu" (the forward's
+    exported log-sum-exp) or "oracle" (the oracle's, rounded to fp32)."""
     kw = dict(heads=wl.heads, M=wl.M, shift=wl.shift, partition=wl.partition, sim=wl.sim, pos=wl.pos,
               tau=f64(x["tau"]), table=table64, rope_base=wl.rope_base)
+    out64, lse64 = oracle.window_attn(f64(x["q"]), f64(x["k"]), f64(x["v"]), return_lse=True, **kw)
+    lse = None
+    if lse_from == "gpu":
+        out, lse = binding.swin_window_attn_fwd_lse(g["q"], g["k"], g["v"], heads=wl.heads, M=wl.M,
+                                                    shift=wl.shift, partition=wl.partition, sim=wl.sim,
+                                                    pos=wl.pos, tau=g["tau"], table=table, rope_base=wl.rope_base)
+    else:
+        out = run_gpu(wl, g, table=table)
+        if lse_from == "oracle":
+            lse = torch.from_numpy(lse64).to(DEV, torch.float32)
+    got = binding.swin_window_attn_bwd(g["q"], g["k"], g["v"], out, dout.to(DEV), heads=wl.heads, M=wl.M,
+                                       shift=wl.shift, partition=wl.partition, sim=wl.sim, pos=wl.pos,
+                                       tau=g["tau"], table=table, rope_base=wl.rope_base, lse=lse)
+    torch.cuda.synchronize()
     ref = oracle.window_attn_bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(dout), **kw)
     # forward-induced bound of the summed gradients (see the module text)
-    out64 = oracle.window_attn(f64(x["q"]), f64(x["k"]), f64(x["v"]), **kw)
     B, H, W, C = out64.shape
     d = C // wl.heads
     dD = np.abs(((f64(out) - out64) * f64(dout)).reshape(B, H, W, wl.heads, d).sum(-1))   # per token, head
     sum_dD = dD.reshape(-1, wl.heads).sum(0)
+    if lse is not None:
+        e = np.abs(f64(lse) - lse64)                                                  # (windows, heads, N)
+        gn = np.linalg.norm(f64(dout).reshape(B, H, W, wl.heads, d), axis=-1)
+        gw = oracle.partition(gn, wl.M, wl.shift, wl.partition).transpose(0, 2, 1)  # (windows, heads, N)
+        vmax = np.linalg.norm(f64(x["v"]).reshape(-1, wl.heads, d), axis=-1).max(0)
+        sum_dD = sum_dD + (e * gw).sum(axis=(0, 2)) * 2.0 * vmax
     tau_eff = np.maximum(f64(x["tau"]), 0.01)
     ref["_dtau_extra"] = sum_dD / tau_eff ** 2
     ref["_dtable_extra"] = sum_dD[None, :]
@@ -97,6 +122,33 @@ def test_backward_parity(case, dtype):
         t = 0.5 * torch.randn(((2 * M - 1) ** 2, heads), generator=gen)
         table, table64 = t.to(DEV), f64(t)
     got, ref = _run(wl, x, g, synth.make_dout(wl), table, table64)
+    for name in ("dq", "dk", "dv"):
+        _check(f"{case} {name}", f64(got[name]), ref[name], dtype)
+    if sim == "cosine":
+        _check(f"{case} dtau", f64(got["dtau"]), ref["dtau"], dtype, ref["_dtau_extra"])
+    if pos == "table":
+        _check(f"{case} dtable", f64(got["dtable"]), ref["dtable"], dtype, ref["_dtable_extra"])
+
+
+@pytest.mark.parametrize("lse_from", ["gpu", "oracle"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}x{c[1]}-M{c[2]}-s{c[3]}-{c[4][:3]}-{c[5]}-{c[6]}"
+                                             for c in CASES])
+def test_backward_with_lse(case, dtype, lse_from):
+    """swin_window_attn_bwd_lse: the forward's log-sum-exp (or the oracle's)
+    replaces the backward's own pass over the keys; same bars."""
+    H, W, M, s, part, sim, pos = case
+    heads = 2
+    wl = synth.small(B=2, H=H, W=W, C=32 * heads, heads=heads, M=M, shift=s, partition=part, sim=sim, pos=pos,
+                     dtype=dtype, hidden=64)
+    x = synth.make_inputs(wl, seed=12)
+    g = gpu_inputs(x)
+    table = table64 = None
+    if pos == "table":
+        gen = torch.Generator().manual_seed(6)
+        t = 0.5 * torch.randn(((2 * M - 1) ** 2, heads), generator=gen)
+        table, table64 = t.to(DEV), f64(t)
+    got, ref = _run(wl, x, g, synth.make_dout(wl), table, table64, lse_from=lse_from)
     for name in ("dq", "dk", "dv"):
         _check(f"{case} {name}", f64(got[name]), ref[name], dtype)
     if sim == "cosine":

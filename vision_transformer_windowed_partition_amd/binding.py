@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
         L.swin_window_attn_fwd.argtypes = [ctypes.POINTER(SwinAttnDesc)] + [vp] * 8
         L.swin_window_attn_bwd.restype = i32
         L.swin_window_attn_bwd.argtypes = [ctypes.POINTER(SwinAttnDesc)] + [vp] * 14
+        L.swin_window_attn_fwd_lse.restype = i32
+        L.swin_window_attn_fwd_lse.argtypes = [ctypes.POINTER(SwinAttnDesc)] + [vp] * 9
+        L.swin_window_attn_bwd_lse.restype = i32
+        L.swin_window_attn_bwd_lse.argtypes = [ctypes.POINTER(SwinAttnDesc)] + [vp] * 15
         L.swin_cpb_table_bwd.restype = i32
         L.swin_cpb_table_bwd.argtypes = [i32] * 4 + [vp] * 5 + [i32] + [vp] * 5
         L.swin_qkv_proj.restype = i32
@@ -200,13 +204,50 @@ def swin_window_attn_fwd(q, k, v, *, heads: int, M: int, shift: int = 0, partiti
     return out
 
 
+def swin_window_attn_fwd_lse(q, k, v, *, heads: int, M: int, shift: int = 0, partition="cyclic",
+                             sim="cosine", pos="none", tau=None, table=None, rope_freqs=None,
+                             tau_min: float = 0.01, rope_base: float = 10000.0, layout="grid",
+                             grid=None, out=None, lse=None, desc: SwinAttnDesc | None = None, stream=None):
+    """swin_window_attn_fwd that also returns the per-query natural-log
+    log-sum-exp of the logits, fp32 (n_windows, heads, M*M): (out, lse)."""
+    if desc is None:
+        if _enum(LAYOUT, layout) == 0:
+            B, H, W, C = q.shape
+        else:
+            B, H, W = grid
+            C = q.shape[-1]
+        desc = make_desc(B=B, H=H, W=W, C=C, heads=heads, M=M, shift=shift, partition=partition,
+                         sim=sim, pos=pos, dtype=q.dtype, layout=layout, tau_min=tau_min,
+                         rope_base=rope_base)
+    for t in (q, k, v):
+        if not t.is_contiguous() or t.dtype != q.dtype or t.shape != q.shape:
+            raise ValueError("q, k, v must be contiguous tensors of one shape and dtype")
+    for t in (tau, table, rope_freqs):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("tau, table and rope_freqs must be contiguous fp32")
+    nwin = desc.B * (desc.H // desc.M) * (desc.W // desc.M)
+    shape = (nwin, desc.heads, desc.M * desc.M)
+    if lse is None:
+        lse = torch.empty(shape, dtype=torch.float32, device=q.device)
+    elif lse.shape != shape or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError(f"lse must be contiguous fp32 of shape {shape}")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().swin_window_attn_fwd_lse(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                          _ptr(tau), _ptr(table), _ptr(rope_freqs), _ptr(lse),
+                                          _stream(q, stream)))
+    return out, lse
+
+
 def swin_window_attn_bwd(q, k, v, out, dout, *, heads: int, M: int, shift: int = 0, partition="cyclic",
                          sim="cosine", pos="none", tau=None, table=None, rope_freqs=None,
                          tau_min: float = 0.01, rope_base: float = 10000.0, layout="grid", grid=None,
                          want_dtau: bool = True, want_dtable: bool = True, desc: SwinAttnDesc | None = None,
-                         stream=None) -> dict:
+                         stream=None, lse=None) -> dict:
     """Backward of swin_window_attn_fwd: dq, dk, dv (like q), and dtau
-    (heads fp32, COSINE) and dtable ((2M-1)^2 x heads fp32, TABLE) when wanted."""
+    (heads fp32, COSINE) and dtable ((2M-1)^2 x heads fp32, TABLE) when wanted.
+    ``lse``: the forward's log-sum-exp from swin_window_attn_fwd_lse; when
+    given, the call goes to swin_window_attn_bwd_lse."""
     if desc is None:
         if _enum(LAYOUT, layout) == 0:
             B, H, W, C = q.shape
@@ -228,10 +269,24 @@ def swin_window_attn_bwd(q, k, v, out, dout, *, heads: int, M: int, shift: int =
         dtau = g["dtau"] = torch.empty(heads, dtype=torch.float32, device=q.device)
     if want_dtable and _enum(POS, pos) == 1:
         dtable = g["dtable"] = torch.empty(((2 * M - 1) ** 2, heads), dtype=torch.float32, device=q.device)
-    _check(lib().swin_window_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
-                                      _ptr(tau), _ptr(table), _ptr(rope_freqs), _ptr(g["dq"]), _ptr(g["dk"]),
-                                      _ptr(g["dv"]), _ptr(dtau), _ptr(dtable), _stream(q, stream)))
+    if lse is None:
+        _check(lib().swin_window_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+                                          _ptr(tau), _ptr(table), _ptr(rope_freqs), _ptr(g["dq"]), _ptr(g["dk"]),
+                                          _ptr(g["dv"]), _ptr(dtau), _ptr(dtable), _stream(q, stream)))
+    else:
+        nwin = desc.B * (desc.H // desc.M) * (desc.W // desc.M)
+        if lse.shape != (nwin, desc.heads, desc.M * desc.M) or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("lse must be the forward's contiguous fp32 (n_windows, heads, M*M)")
+        _check(lib().swin_window_attn_bwd_lse(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                              _ptr(dout), _ptr(tau), _ptr(table), _ptr(rope_freqs), _ptr(lse),
+                                              _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(dtau), _ptr(dtable),
+                                              _stream(q, stream)))
     return g
+
+
+def swin_window_attn_bwd_lse(q, k, v, out, dout, lse, **kw) -> dict:
+    """swin_window_attn_bwd given the forward's log-sum-exp (see there)."""
+    return swin_window_attn_bwd(q, k, v, out, dout, lse=lse, **kw)
 
 
 def swin_cpb_table_bwd(M: int, w1, b1, w2, table, dtable, *, cpb_mode: int = CPB_PAPER, norm_M=None,

@@ -193,13 +193,8 @@ Kernel kernel_for(const swin::AttnParams& p)
     return Kernel::MFMA;
 }
 
-}  // namespace
-
-extern "C" {
-
-int swin_window_attn_fwd(const swin_attn_desc* d, const void* q, const void* k, const void* v,
-                         void* out, const float* tau, const float* table, const float* rope_freqs,
-                         void* stream)
+int attn_fwd(const swin_attn_desc* d, const void* q, const void* k, const void* v, void* out, const float* tau,
+             const float* table, const float* rope_freqs, float* lse, void* stream)
 {
     int st = check_desc(d, rope_freqs != nullptr);
     if (st) return st;
@@ -213,12 +208,22 @@ int swin_window_attn_fwd(const swin_attn_desc* d, const void* q, const void* k, 
         return fail(SWIN_EINVAL, "out overlaps q, k or v");
     if (d->sim == SWIN_SIM_COSINE && !tau) return fail(SWIN_EINVAL, "COSINE needs tau");
     if (d->pos == SWIN_POS_TABLE && !table) return fail(SWIN_EINVAL, "POS_TABLE needs a table");
+    if (lse) {
+        const size_t lb = bytes / es / (size_t)(d->C / d->heads) * sizeof(float);   // windows x heads x N
+        if ((uintptr_t)lse & 3) return fail(SWIN_EINVAL, "lse must be 4-byte aligned");
+        if (overlaps(lse, lb, q, bytes) || overlaps(lse, lb, k, bytes) || overlaps(lse, lb, v, bytes) ||
+            overlaps(lse, lb, out, bytes))
+            return fail(SWIN_EINVAL, "lse overlaps q, k, v or out");
+    }
 
     swin::AttnParams p = params_of(d);
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.tau = tau; p.table = table; p.rope_freqs = rope_freqs;
+    p.lse = lse;
     hipError_t e;
-    switch (kernel_for(p)) {
+    Kernel kern = kernel_for(p);
+    if (lse && kern == Kernel::MFMA) kern = Kernel::VALU;      // the general kernel exports none
+    switch (kern) {
     case Kernel::VALU: e = swin::launch_attn_valu(p, (hipStream_t)stream); break;
     case Kernel::SMALL: e = swin::launch_attn_small(p, (hipStream_t)stream); break;
     case Kernel::LARGE: e = swin::launch_attn_large(p, (hipStream_t)stream); break;
@@ -227,10 +232,9 @@ int swin_window_attn_fwd(const swin_attn_desc* d, const void* q, const void* k, 
     return hip_status(e, "swin_window_attn_fwd launch");
 }
 
-int swin_window_attn_bwd(const swin_attn_desc* d, const void* q, const void* k, const void* v,
-                         const void* out, const void* dout, const float* tau, const float* table,
-                         const float* rope_freqs, void* dq, void* dk, void* dv, float* dtau, float* dtable,
-                         void* stream)
+int attn_bwd(const swin_attn_desc* d, const void* q, const void* k, const void* v, const void* out,
+             const void* dout, const float* tau, const float* table, const float* rope_freqs, const float* lse,
+             void* dq, void* dk, void* dv, float* dtau, float* dtable, void* stream)
 {
     int st = check_desc(d, rope_freqs != nullptr);
     if (st) return st;
@@ -258,12 +262,50 @@ int swin_window_attn_bwd(const swin_attn_desc* d, const void* q, const void* k, 
     const size_t tb = (size_t)S * S * d->heads * sizeof(float);
     if (dtable && d->pos == SWIN_POS_TABLE && table && overlaps(dtable, tb, table, tb))
         return fail(SWIN_EINVAL, "dtable overlaps the table");
+    if (lse && ((uintptr_t)lse & 3)) return fail(SWIN_EINVAL, "lse must be 4-byte aligned");
 
     swin::AttnParams p = params_of(d);
     p.q = q; p.k = k; p.v = v; p.out = nullptr;
     p.tau = tau; p.table = table; p.rope_freqs = rope_freqs;
+    p.lse = const_cast<float*>(lse);                          // read only by a backward
     return hip_status(swin::launch_attn_bwd(p, out, dout, dq, dk, dv, dtau, dtable, (hipStream_t)stream),
                       "swin_window_attn_bwd launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int swin_window_attn_fwd(const swin_attn_desc* d, const void* q, const void* k, const void* v,
+                         void* out, const float* tau, const float* table, const float* rope_freqs,
+                         void* stream)
+{
+    return attn_fwd(d, q, k, v, out, tau, table, rope_freqs, nullptr, stream);
+}
+
+int swin_window_attn_fwd_lse(const swin_attn_desc* d, const void* q, const void* k, const void* v,
+                             void* out, const float* tau, const float* table, const float* rope_freqs,
+                             float* lse, void* stream)
+{
+    if (!lse && d && (int64_t)d->B * d->H * d->W * d->C > 0) return fail(SWIN_EINVAL, "NULL lse");
+    return attn_fwd(d, q, k, v, out, tau, table, rope_freqs, lse, stream);
+}
+
+int swin_window_attn_bwd(const swin_attn_desc* d, const void* q, const void* k, const void* v,
+                         const void* out, const void* dout, const float* tau, const float* table,
+                         const float* rope_freqs, void* dq, void* dk, void* dv, float* dtau, float* dtable,
+                         void* stream)
+{
+    return attn_bwd(d, q, k, v, out, dout, tau, table, rope_freqs, nullptr, dq, dk, dv, dtau, dtable, stream);
+}
+
+int swin_window_attn_bwd_lse(const swin_attn_desc* d, const void* q, const void* k, const void* v,
+                             const void* out, const void* dout, const float* tau, const float* table,
+                             const float* rope_freqs, const float* lse, void* dq, void* dk, void* dv,
+                             float* dtau, float* dtable, void* stream)
+{
+    if (!lse && d && (int64_t)d->B * d->H * d->W * d->C > 0) return fail(SWIN_EINVAL, "NULL lse");
+    return attn_bwd(d, q, k, v, out, dout, tau, table, rope_freqs, lse, dq, dk, dv, dtau, dtable, stream);
 }
 
 int swin_qkv_proj(const void* x, const void* w, const float* b, void* q, void* k, void* v, int64_t T,

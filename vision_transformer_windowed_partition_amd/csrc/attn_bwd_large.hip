@@ -273,9 +273,11 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
         if (wp.last_r) { if (ri < M - g.shift) rhi = M - g.shift; else rlo = M - g.shift; }
         if (wp.last_c) { if (ci < M - g.shift) chi = M - g.shift; else clo = M - g.shift; }
 
-        // pass 0: running maximum and sum
+        // pass 0: running maximum and sum, unless the forward's log-sum-exp
+        // is given (natural log, to log2 units)
         float m = -INFINITY, l = 0.0f;
-        for (int c = 0; c < nch; ++c) {
+        const int nch0 = p.lse ? 0 : nch;
+        for (int c = 0; c < nch0; ++c) {
             const int sA = 32 * c + 8 * (li >> 2) + (li & 3);
             const bf16x8 ka = rowfrag(rowA, sA, grp), kb = rowfrag(rowA, sA + 4, grp);
             const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -305,8 +307,13 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
             l = l * __builtin_amdgcn_exp2f(m - mref) + ls;
             m = mn;
         }
-        l = sum_x32(sum_x16(l));
-        const float lq = m + __builtin_amdgcn_logf(l);
+        float lq;
+        if (p.lse) {
+            lq = tv ? p.lse[((size_t)win * g.heads + h) * N + t] * kLog2e : 0.0f;
+        } else {
+            l = sum_x32(sum_x16(l));
+            lq = m + __builtin_amdgcn_logf(l);
+        }
         if (grp == 0 && tv) lse[qs_slot] = lq;
 
         // pass B: dq

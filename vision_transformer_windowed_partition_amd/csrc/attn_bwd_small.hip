@@ -217,8 +217,15 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
     const int negrow = S * S;
     const int kbase = (grp / GPR) * S + 8 * (grp % GPR);   // bias offset of this lane's key group, chunk 0
 
-    // ---- pass 0: log-sum-exp of this wave's queries
-    if (active) {
+    // ---- pass 0: log-sum-exp of this wave's queries, or the forward's
+    // (natural log, to log2 units)
+    if (active && p.lse) {
+        const float* lin = p.lse + ((size_t)win * g.heads + h) * N;
+        for (int t = rank * 64 + lane; t < N; t += 64 * QW) {
+            const int ri = qdiv(t, L.inv_M), ci = t - ri * M;
+            lse[ri * 8 * GPR + ci] = lin[t] * kLog2e;
+        }
+    } else if (active) {
         for (int t0 = rank; t0 < L.NQT; t0 += QW) {
             const int t = t0 * 16 + li;
             const bool tv = t < N;

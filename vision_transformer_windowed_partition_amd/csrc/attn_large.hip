@@ -400,7 +400,7 @@ attn_large_kernel(AttnParams p, LargeLayout L)
     // ---- tables: bias (reversed so that consecutive keys read consecutive
     // floats, in log2 units, shifted by its max and, for COSINE, by 1/tau);
     // rotary cos / sin per local position, half and pair
-    float bias_range = 0.0f;
+    float bias_range = 0.0f, tab_shift = 0.0f;   // tab_shift: subtracted from the stored table (log2 units)
     if (POS == SWIN_POS_TABLE) {
         float mx = -INFINITY, mn = INFINITY;
         for (int i = tid; i < S * S; i += NTHR) {
@@ -423,6 +423,7 @@ attn_large_kernel(AttnParams p, LargeLayout L)
         bias_range = mx - mn;
         const float sh = SIM == SWIN_SIM_COSINE ? mx + kLog2e * inv_tau : mx;
         for (int i = tid; i < S * S; i += NTHR) bias2[i] -= sh;
+        tab_shift = sh;
     }
     if (POS == SWIN_POS_ROPE2D) {
         for (int i = tid; i < M * 16; i += NTHR) {
@@ -621,6 +622,12 @@ attn_large_kernel(AttnParams p, LargeLayout L)
             const uint32_t o = masked(wp.wg.tok(ri, ci) + 8u * grp, qv[i]);
             store8(orr, o, pack_bf16x4(T[i].o0[0] * inv, T[i].o0[1] * inv, T[i].o0[2] * inv, T[i].o0[3] * inv));
             store8(orr, o + 32u, pack_bf16x4(T[i].o1[0] * inv, T[i].o1[1] * inv, T[i].o1[2] * inv, T[i].o1[3] * inv));
+            if (p.lse && grp == 0 && qv[i]) {
+                // the exp2 arguments were the logits in log2 units less the
+                // table's shift and -negm, plus the running maximum where used
+                const float off2 = tab_shift - T[i].negm + (T[i].exact ? T[i].mrun : 0.0f);
+                p.lse[((size_t)win * g.heads + h) * N + qt[i]] = (__builtin_amdgcn_logf(T[i].ls[0]) + off2) * kLn2;
+            }
         }
     }
 }

@@ -508,6 +508,17 @@ attn_small_kernel(AttnParams p, SmallLayout L)
             const uint32_t off = masked(wg.tok(ri, ci) + 8u * grp, qv[i]);
             store8(orr, off, pack_bf16x4(T[i].o0[0] * inv, T[i].o0[1] * inv, T[i].o0[2] * inv, T[i].o0[3] * inv));
             store8(orr, off + 32u, pack_bf16x4(T[i].o1[0] * inv, T[i].o1[1] * inv, T[i].o1[2] * inv, T[i].o1[3] * inv));
+            if (p.lse && grp == 0 && qv[i]) {
+                // the exp2 arguments were the logits in log2 units less off:
+                // the stored table's offset boff (COSINE), that and the
+                // static shift c_i + bias_max (DOT with a table), or -negm;
+                // plus the running maximum where it was used
+                float off2 = POS == SWIN_POS_TABLE ? boff + (SIM == SWIN_SIM_DOT ? bias_max - T[i].negm : 0.0f)
+                                                   : -T[i].negm;
+                if (T[i].exact) off2 += T[i].mrun;
+                p.lse[((size_t)win * g.heads + h) * N + qt[i]] =
+                    (__builtin_amdgcn_logf(T[i].ls[0]) + off2) * kLn2;
+            }
         }
     }
 }

@@ -199,6 +199,7 @@ attn_valu_kernel(AttnParams p, int kc)
 #pragma unroll
             for (int e = 0; e < D; ++e) acc[e] *= inv;
             store_row<T>(og + token_offset(g, win, ri, ci) + h * D, acc);
+            if (p.lse) p.lse[((size_t)win * g.heads + h) * N + t] = (float)(m + log((double)l));
         }
     }
 }

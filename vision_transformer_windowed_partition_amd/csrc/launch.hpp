@@ -20,6 +20,10 @@ struct AttnParams {
     const float* tau;
     const float* table;
     const float* rope_freqs;
+    // per (window, head, query slot) natural-log log-sum-exp of the
+    // logits, fp32, n_windows x heads x N: written by a forward when not
+    // NULL, read by a backward when not NULL (which then skips its own pass)
+    float* lse = nullptr;
 };
 
 hipError_t launch_window_copy(const void* src, void* dst, const Geometry& g, int elem_size,

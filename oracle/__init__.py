@@ -10,7 +10,8 @@ Contents
     the attention itself (with the log-sum-exp a backward
     reuses) and its backward, the attention branch's linear
     layers and residual post-norm, Iwin's depthwise convolution branch and
-    LinMapper's in-window linear mapping, all in fp64.
+    LinMapper's in-window linear mapping, and attention over video (3D)
+    windows with their three-offset bias table, all in fp64.
   * ``bruteforce.py``: full-grid attention over every token pair with a mask, for
     tiny grids; it shares neither the partition nor the table indexing with
     ``oracle.c`` and serves as that file's independent check.
@@ -80,6 +81,10 @@ def _declare(lib):
     lib.oracle_dwconv_add.argtypes = [vp] * 4 + [i32] * 4
     lib.oracle_window_linear.restype = i32
     lib.oracle_window_linear.argtypes = [i32] * 8 + [vp] * 4
+    lib.oracle_cpb_table3d.restype = i32
+    lib.oracle_cpb_table3d.argtypes = [i32] * 4 + [vp] * 5
+    lib.oracle_window_attn3d.restype = i32
+    lib.oracle_window_attn3d.argtypes = [i32] * 13 + [dbl] + [vp] * 6
     lib.oracle_set_threads.restype = None
     lib.oracle_set_threads.argtypes = [i32]
     lib.oracle_max_threads.restype = i32
@@ -355,3 +360,35 @@ def cpu_model() -> str:
     except OSError:
         pass
     return sys.platform
+
+
+def cpb_table3d(Mt: int, M: int, w1, b1, w2, b2, lib=None) -> np.ndarray:
+    """(2Mt-1)(2M-1)^2 x heads bias table of G over the log-spaced offsets
+    (dx, dy, dt) of video windows Mt x M x M; w1 is hidden x 3."""
+    w1, w2 = _f64(w1), _f64(w2)
+    b1, b2 = _f64(b1), _f64(b2)
+    hidden, heads = w1.shape[0], w2.shape[0]
+    assert w1.shape == (hidden, 3) and w2.shape == (heads, hidden)
+    out = np.empty(((2 * Mt - 1) * (2 * M - 1) ** 2, heads), dtype=np.float64)
+    rc = (lib or load()).oracle_cpb_table3d(Mt, M, heads, hidden, _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(out))
+    if rc:
+        raise ValueError(f"oracle_cpb_table3d: bad argument (rc={rc})")
+    return out
+
+
+def window_attn3d(q, k, v, *, heads: int, Mt: int, M: int, shift_t: int = 0, shift: int = 0,
+                  partition: str = "cyclic", sim: str = "cosine", pos: str = "none", tau=None, table=None,
+                  tau_min: float = 0.01, lib=None) -> np.ndarray:
+    """Video-window attention forward in fp64 over (B, T, H, W, C) grids,
+    windows Mt x M x M (temporal shift ``shift_t``, spatial ``shift``)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, H, W, C = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    tau, table = _f64(tau), _f64(table)
+    out = np.zeros((B, T, H, W, C), dtype=np.float64)
+    rc = (lib or load()).oracle_window_attn3d(B, T, H, W, C, heads, Mt, M, shift_t, shift, PART[partition],
+                                              SIM[sim], POS[pos], float(tau_min), _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(tau), _ptr(table), _ptr(out))
+    if rc:
+        raise ValueError(f"oracle_window_attn3d: bad argument (rc={rc})")
+    return out

@@ -18,7 +18,8 @@ rotary score.  The bias is the meta network G evaluated on each distinct
 offset (SwinV2 eq. 3-4), not a lookup in a precomputed table, and the rotary
 embedding is a complex multiply.  The same cells give the pairs of the
 in-window linear mapping (``window_linear``), with window-local indices
-computed from the grid side.  Nothing here is shared with ``oracle.c``.
+computed from the grid side, and video grids (``window_attn3d``) take the same
+cell rule on a third, temporal axis.  Nothing here is shared with ``oracle.c``.
 """
 from __future__ import annotations
 
@@ -38,10 +39,14 @@ def _positions(L: int, M: int, part: str) -> np.ndarray:
     return idx / (L // M) if part == "interleaved" else idx
 
 
-def meta_network(dx: np.ndarray, dy: np.ndarray, w1, b1, w2, b2) -> np.ndarray:
-    """G(sign(dx) log(1+|dx|), sign(dy) log(1+|dy|)) for arrays of offsets -> (..., heads)."""
+def meta_network(dx: np.ndarray, dy: np.ndarray, w1, b1, w2, b2, dt=None) -> np.ndarray:
+    """G(sign(dx) log(1+|dx|), sign(dy) log(1+|dy|)[, same of dt]) for arrays of
+    offsets -> (..., heads); with dt, w1 has a third column for it."""
     f = lambda t: np.sign(t) * np.log1p(np.abs(t))
-    x = np.stack([f(np.asarray(dx, np.float64)), f(np.asarray(dy, np.float64))], axis=-1)
+    cols = [f(np.asarray(dx, np.float64)), f(np.asarray(dy, np.float64))]
+    if dt is not None:
+        cols.append(f(np.asarray(dt, np.float64)))
+    x = np.stack(cols, axis=-1)
     h = x @ np.asarray(w1, np.float64).T
     if b1 is not None:
         h = h + np.asarray(b1, np.float64)
@@ -178,4 +183,52 @@ def window_linear(v, A, bias=None, *, heads: int, M: int, shift: int = 0, partit
             if bias is not None:
                 oh = oh + np.asarray(bias, np.float64)[h][loc][:, None]
             out[b].reshape(P, C)[:, h * d:(h + 1) * d] = oh
+    return out
+
+
+def window_attn3d(q, k, v, *, heads: int, Mt: int, M: int, shift_t: int = 0, shift: int = 0,
+                  partition: str = "cyclic", sim: str = "cosine", pos: str = "none", tau=None, mlp=None,
+                  tau_min: float = 0.01):
+    """Full-grid masked attention over (B, T, H, W, C) video grids: a pair may
+    attend iff it shares the cell on every axis (the temporal axis cut like the
+    other two, with its own window Mt and shift); the bias is G evaluated on
+    the three offsets.  Same meaning of arguments as the oracle's 3D form."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, T, H, W, C = q.shape
+    d = C // heads
+    P = T * H * W
+    ct, cr, cc = (_cell_rows(T, Mt, shift_t, partition), _cell_rows(H, M, shift, partition),
+                  _cell_rows(W, M, shift, partition))
+    cell = ((ct[:, None, None] * (H + 1) + cr[None, :, None]) * (W + 1) + cc[None, None, :]).reshape(P)
+    allowed = cell[:, None] == cell[None, :]
+    pt = np.repeat(_positions(T, Mt, partition), H * W)
+    pr = np.tile(np.repeat(_positions(H, M, partition), W), T)
+    pc = np.tile(_positions(W, M, partition), T * H)
+    dt = np.rint(pt[:, None] - pt[None, :])
+    dy = np.rint(pr[:, None] - pr[None, :])
+    dx = np.rint(pc[:, None] - pc[None, :])
+    bias = None
+    if pos == "table":
+        offs, inv = np.unique(np.stack([dt.ravel(), dy.ravel(), dx.ravel()], 1), axis=0, return_inverse=True)
+        g = meta_network(offs[:, 2], offs[:, 1], *mlp, dt=offs[:, 0])      # (n_offsets, heads)
+        bias = g[inv.ravel()].reshape(P, P, heads)
+    out = np.zeros((B, T, H, W, C))
+    for h in range(heads):
+        for b in range(B):
+            qh = q[b].reshape(P, C)[:, h * d:(h + 1) * d]
+            kh = k[b].reshape(P, C)[:, h * d:(h + 1) * d]
+            vh = v[b].reshape(P, C)[:, h * d:(h + 1) * d]
+            if sim == "cosine":
+                qh = qh / np.maximum(np.linalg.norm(qh, axis=1, keepdims=True), 1e-12)
+                kh = kh / np.maximum(np.linalg.norm(kh, axis=1, keepdims=True), 1e-12)
+                logits = (qh @ kh.T) / max(float(tau[h]), tau_min)
+            else:
+                logits = (qh @ kh.T) / np.sqrt(d)
+            if bias is not None:
+                logits = logits + bias[:, :, h]
+            logits = np.where(allowed, logits, -np.inf)
+            e = np.exp(logits - logits.max(axis=1, keepdims=True))
+            out[b].reshape(P, C)[:, h * d:(h + 1) * d] = (e / e.sum(axis=1, keepdims=True)) @ vh
     return out

@@ -847,3 +847,155 @@ int oracle_window_linear(int B, int H, int W, int C, int heads, int M, int shift
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Video (3D) windows.  [SwinV2] appendix A2 fine-tunes a video model on
+ * Kinetics-400 with windows of 16^2 x 8 over 256^2 x 8 frames (and 20^2 x 8
+ * at 320^2); [Iwin] abstract transfers its 2D weights to 3D.  Neither page
+ * writes the 3D form down.  Reading: the 2D definition with a third,
+ * temporal axis treated exactly like the other two --
+ *   - tokens (B, T, H, W, C), windows of Mt x M x M, local order
+ *     (t*M + r)*M + c, window order ((b*nwt + wt)*nwr + wr)*nwc + wc;
+ *   - cyclic: every axis rolled by -its shift (shift_t on the temporal
+ *     axis), regions per axis as in 2D, a pair allowed when all three
+ *     region labels agree; interleaved: every axis interleaved, no shift;
+ *   - the bias table of G over the log-spaced offsets (dx, dy, dt), G's
+ *     first layer taking three inputs, (2Mt-1)(2M-1)^2 rows indexed
+ *     ((dt + Mt-1)(2M-1) + dy + M-1)(2M-1) + dx + M-1.
+ * With Mt = 1 (or T = Mt = 1) every step reduces to the 2D definition.
+ * ------------------------------------------------------------------------ */
+
+/* Grid coordinate of local position r in window w along one axis of length L. */
+static int axis_pos(int L, int M, int s, int part, int w, int r)
+{
+    return part == OR_PART_INTERLEAVED ? w + r * (L / M) : (w * M + r + s) % L;
+}
+
+/* [SwinV2] eq. 3-4 extended to three offsets: G(log-spaced dx, dy, dt), w1 is
+ * hidden x 3 (columns: dx, dy, dt), ReLU between the two layers. */
+int oracle_cpb_table3d(int Mt, int M, int heads, int hidden, const double* w1, const double* b1,
+                       const double* w2, const double* b2, double* table)
+{
+    if (Mt < 1 || M < 1 || heads < 1 || hidden < 1 || !w1 || !w2 || !table) return 1;
+    const int S = 2 * M - 1;
+    double* h = (double*)malloc((size_t)hidden * sizeof(double));
+    if (!h) return 2;
+    for (int dt = -(Mt - 1); dt <= Mt - 1; ++dt)
+        for (int dy = -(M - 1); dy <= M - 1; ++dy)
+            for (int dx = -(M - 1); dx <= M - 1; ++dx) {
+                const double in0 = oracle_log_offset((double)dx);
+                const double in1 = oracle_log_offset((double)dy);
+                const double in2 = oracle_log_offset((double)dt);
+                for (int j = 0; j < hidden; ++j) {
+                    const double a = w1[3 * j] * in0 + w1[3 * j + 1] * in1 + w1[3 * j + 2] * in2 +
+                                     (b1 ? b1[j] : 0.0);
+                    h[j] = a > 0.0 ? a : 0.0;
+                }
+                double* row = table + (((size_t)(dt + Mt - 1) * S + (size_t)(dy + M - 1)) * S +
+                                       (size_t)(dx + M - 1)) * heads;
+                for (int o = 0; o < heads; ++o) {
+                    double acc = b2 ? b2[o] : 0.0;
+                    for (int j = 0; j < hidden; ++j) acc += w2[(size_t)o * hidden + j] * h[j];
+                    row[o] = acc;
+                }
+            }
+    free(h);
+    return 0;
+}
+
+/* Windowed attention over (B, T, H, W, C) video grids, windows Mt x M x M
+ * (reading above); logit, bias, exclusion and softmax as in
+ * oracle_window_attn.  pos: NONE or TABLE (no rotary form in 3D). */
+int oracle_window_attn3d(int B, int T, int H, int W, int C, int heads, int Mt, int M,
+                         int shift_t, int shift, int part, int sim, int pos, double tau_min,
+                         const double* q, const double* k, const double* v,
+                         const double* tau, const double* table, double* out)
+{
+    if (bad_shape(B, H, W, C, M, shift, part)) return 1;
+    if (T < 1 || Mt < 1 || T % Mt || shift_t < 0 || shift_t >= Mt) return 1;
+    if (part == OR_PART_INTERLEAVED && shift_t != 0) return 1;
+    if (heads < 1 || C % heads) return 1;
+    if (sim != OR_SIM_COSINE && sim != OR_SIM_DOT) return 1;
+    if (pos != OR_POS_NONE && pos != OR_POS_TABLE) return 1;
+    if (sim == OR_SIM_COSINE && !tau) return 1;
+    if (pos == OR_POS_TABLE && !table) return 1;
+    if (!q || !k || !v || !out) return 1;
+    const int d = C / heads;
+    const int nwt = T / Mt, nwr = H / M, nwc = W / M, N = Mt * M * M, S = 2 * M - 1;
+    const int64_t nW = (int64_t)nwt * nwr * nwc, total = (int64_t)B * nW;
+    const double dot_scale = 1.0 / sqrt((double)d);
+    int failed = 0;
+
+    #pragma omp parallel
+    {
+        double* qs = (double*)malloc((size_t)N * d * sizeof(double));
+        double* ks = (double*)malloc((size_t)N * d * sizeof(double));
+        double* vs = (double*)malloc((size_t)N * d * sizeof(double));
+        double* lg = (double*)malloc((size_t)N * sizeof(double));
+        size_t* gofs = (size_t*)malloc((size_t)N * sizeof(size_t));
+        int* region = (int*)malloc((size_t)N * sizeof(int));
+        if (!qs || !ks || !vs || !lg || !gofs || !region) {
+            #pragma omp atomic write
+            failed = 1;
+        } else {
+            #pragma omp for schedule(dynamic, 1)
+            for (int64_t u = 0; u < total * heads; ++u) {
+                const int64_t wi = u / heads;
+                const int h = (int)(u % heads);
+                const int b = (int)(wi / nW);
+                const int wt = (int)((wi % nW) / ((int64_t)nwr * nwc));
+                const int wr = (int)((wi % ((int64_t)nwr * nwc)) / nwc);
+                const int wc = (int)(wi % nwc);
+                /* gather, with region labels per axis in rolled coordinates */
+                for (int i = 0; i < N; ++i) {
+                    const int t = i / (M * M), r = (i / M) % M, c = i % M;
+                    const int gt = axis_pos(T, Mt, shift_t, part, wt, t);
+                    const int gi = axis_pos(H, M, shift, part, wr, r);
+                    const int gj = axis_pos(W, M, shift, part, wc, c);
+                    region[i] = part == OR_PART_CYCLIC
+                        ? 9 * axis_region(wt * Mt + t, T, Mt, shift_t) + 3 * axis_region(wr * M + r, H, M, shift) +
+                          axis_region(wc * M + c, W, M, shift)
+                        : 0;
+                    gofs[i] = ((((size_t)b * T + gt) * H + gi) * W + gj) * C + (size_t)h * d;
+                    for (int e = 0; e < d; ++e) {
+                        qs[(size_t)i * d + e] = q[gofs[i] + e];
+                        ks[(size_t)i * d + e] = k[gofs[i] + e];
+                        vs[(size_t)i * d + e] = v[gofs[i] + e];
+                    }
+                    if (sim == OR_SIM_COSINE) {
+                        unit_normalize(qs + (size_t)i * d, d);
+                        unit_normalize(ks + (size_t)i * d, d);
+                    }
+                }
+                const double inv_tau = sim == OR_SIM_COSINE ? 1.0 / (tau[h] > tau_min ? tau[h] : tau_min) : 0.0;
+                for (int i = 0; i < N; ++i) {
+                    const int ti = i / (M * M), ri = (i / M) % M, ci = i % M;
+                    double mx = -INFINITY;
+                    for (int j = 0; j < N; ++j) {
+                        const int tj = j / (M * M), rj = (j / M) % M, cj = j % M;
+                        double s = 0.0;
+                        for (int e = 0; e < d; ++e) s += qs[(size_t)i * d + e] * ks[(size_t)j * d + e];
+                        double l = sim == OR_SIM_COSINE ? s * inv_tau : s * dot_scale;
+                        if (pos == OR_POS_TABLE)
+                            l += table[((((size_t)(ti - tj + Mt - 1) * S + (size_t)(ri - rj + M - 1)) * S) +
+                                        (size_t)(ci - cj + M - 1)) * heads + h];
+                        lg[j] = region[j] == region[i] ? l : -INFINITY;
+                        if (lg[j] > mx) mx = lg[j];
+                    }
+                    double sum = 0.0;
+                    for (int j = 0; j < N; ++j) {
+                        lg[j] = lg[j] == -INFINITY ? 0.0 : exp(lg[j] - mx);
+                        sum += lg[j];
+                    }
+                    for (int e = 0; e < d; ++e) {
+                        double acc = 0.0;
+                        for (int j = 0; j < N; ++j) acc += lg[j] * vs[(size_t)j * d + e];
+                        out[gofs[i] + e] = acc / sum;
+                    }
+                }
+            }
+        }
+        free(qs); free(ks); free(vs); free(lg); free(gofs); free(region);
+    }
+    return failed ? 2 : 0;
+}

@@ -18,7 +18,7 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_helpers import f64, gpu_inputs, gpu_table
+from tests.gpu_helpers import compare, f64, gpu_inputs, gpu_table
 from vision_transformer_windowed_partition_amd import binding, synth
 
 pytestmark = pytest.mark.gpu
@@ -80,8 +80,15 @@ def _run(wl, x, tau=None):
     out, lse = binding.swin_window_attn_fwd_lse(g["q"], g["k"], g["v"], **kw)
     plain = binding.swin_window_attn_fwd(g["q"], g["k"], g["v"], **kw)
     torch.cuda.synchronize()
-    assert torch.equal(out, plain), "the output written with the log-sum-exp differs from the plain forward's"
     tau64 = f64(x["tau"] if tau is None else tau)
+    if wl.dtype == "bf16" and wl.M > 32:
+        # the general matrix-core kernel exports no statistic: the vector
+        # kernel runs instead, its output within the forward's own bars
+        compare(wl, f64(out), oracle.window_attn(f64(x["q"]), f64(x["k"]), f64(x["v"]), heads=wl.heads, M=wl.M,
+                                                 shift=wl.shift, partition=wl.partition, sim=wl.sim, pos=wl.pos,
+                                                 tau=tau64, table=table64, rope_base=wl.rope_base), what="M > 32")
+    else:
+        assert torch.equal(out, plain), "the output written with the log-sum-exp differs from the plain forward's"
     ref = _lse_ref(wl, x, table64, tau64)
     got = f64(lse)
     assert got.shape == ref.shape

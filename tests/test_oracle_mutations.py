@@ -74,6 +74,12 @@ MUTATIONS = [
      "if (yy < 0 || yy >= H || xx < 0 || xx >= W || (dy == 1 && dx == 1)) continue;"),
     ("dwconv_bias_dropped", "double s = b ? b[c] : 0.0;", "double s = 0.0;"),
     ("dwconv_overwrites", "out[i] += tmp[i];", "out[i] = tmp[i];"),
+    ("v3_shift_t_direction", "(w * M + r + s) % L;", "(w * M + r - s + L) % L;"),
+    ("v3_region_t_dropped", "? 9 * axis_region(wt * Mt + t, T, Mt, shift_t) +", "? 0 * axis_region(wt * Mt + t, T, Mt, shift_t) +"),
+    ("v3_bias_t_sign", "(size_t)(ti - tj + Mt - 1)", "(size_t)(tj - ti + Mt - 1)"),
+    ("v3_dt_input", "w1[3 * j + 2] * in2", "w1[3 * j + 2] * in1"),
+    ("v3_interleaved_t", "return part == OR_PART_INTERLEAVED ? w + r * (L / M) : (w * M + r + s) % L;",
+     "return part == OR_PART_INTERLEAVED ? w * M + r : (w * M + r + s) % L;"),
     ("lse_max_dropped", "lse[((size_t)wi * heads + h) * N + i] = mx + log(sum);",
      "lse[((size_t)wi * heads + h) * N + i] = log(sum);"),
     ("lse_head_index", "lse[((size_t)wi * heads + h) * N + i] = mx + log(sum);",

@@ -208,6 +208,61 @@ def pin_lse(lib):
         np.testing.assert_allclose(lo[0, h], torch.logsumexp(logits, dim=1).numpy(), rtol=0, atol=1e-12)
 
 
+VIDEO_CASES = [
+    # T, H, W, Mt, M, shift_t, shift, partition, sim, pos
+    (4, 8, 8, 2, 4, 1, 2, "cyclic", "cosine", "table"),      # every axis shifted
+    (6, 6, 6, 3, 3, 1, 0, "cyclic", "dot", "table"),         # temporal shift only
+    (4, 8, 8, 4, 4, 0, 2, "cyclic", "cosine", "none"),       # one temporal window, spatial shift
+    (4, 8, 12, 2, 4, 0, 0, "interleaved", "cosine", "table"),
+    (4, 4, 4, 4, 2, 2, 1, "cyclic", "dot", "none"),
+]
+
+
+def _video_inputs(case, seed, B=2, C=16, heads=2, hidden=8):
+    T, H, W, Mt, M, st, s, part, sim, pos = case
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((B, T, H, W, C)) for _ in range(3))
+    tau = rng.uniform(0.05, 1.0, heads)
+    mlp = (rng.standard_normal((hidden, 3)), rng.standard_normal(hidden), 0.3 * rng.standard_normal((heads, hidden)),
+           rng.standard_normal(heads))
+    return q, k, v, tau, mlp
+
+
+def pin_video_bruteforce(lib):
+    """Video (3D) windows: the oracle == full-grid masked attention whose pairs
+    share a cell on all three axes, bias from G on the three offsets."""
+    for case in VIDEO_CASES:
+        T, H, W, Mt, M, st, s, part, sim, pos = case
+        q, k, v, tau, mlp = _video_inputs(case, seed=T * 10 + M)
+        tab = oracle.cpb_table3d(Mt, M, *mlp, lib=lib) if pos == "table" else None
+        o = oracle.window_attn3d(q, k, v, heads=2, Mt=Mt, M=M, shift_t=st, shift=s, partition=part, sim=sim,
+                                 pos=pos, tau=tau, table=tab, lib=lib)
+        b = bf.window_attn3d(q, k, v, heads=2, Mt=Mt, M=M, shift_t=st, shift=s, partition=part, sim=sim,
+                             pos=pos, tau=tau, mlp=mlp)
+        err = np.abs(o - b).max()
+        assert err < 1e-12, (case, err)
+
+
+def pin_video_reduces_to_2d(lib):
+    """One-frame temporal windows (Mt = 1) are the 2D definition applied to
+    every frame, and the 3D table's dt = 0 slice is the 2D table of G's
+    first two input columns (log(1 + 0) = 0)."""
+    case = (3, 8, 8, 1, 4, 0, 2, "cyclic", "cosine", "table")
+    q, k, v, tau, (w1, b1, w2, b2) = _video_inputs(case, seed=3)
+    tab3 = oracle.cpb_table3d(1, 4, w1, b1, w2, b2, lib=lib)
+    tab2 = oracle.cpb_table(4, w1[:, :2], b1, w2, b2, lib=lib)
+    np.testing.assert_allclose(tab3, tab2, rtol=0, atol=1e-13)
+    o3 = oracle.window_attn3d(q, k, v, heads=2, Mt=1, M=4, shift=2, sim="cosine", pos="table", tau=tau,
+                              table=tab3, lib=lib)
+    B, T, H, W, C = q.shape
+    o2 = oracle.window_attn(q.reshape(B * T, H, W, C), k.reshape(B * T, H, W, C), v.reshape(B * T, H, W, C),
+                            heads=2, M=4, shift=2, sim="cosine", pos="table", tau=tau, table=tab2, lib=lib)
+    np.testing.assert_allclose(o3.reshape(B * T, H, W, C), o2, rtol=0, atol=1e-13)
+    Mt, M = 3, 4
+    t3 = oracle.cpb_table3d(Mt, M, w1, b1, w2, b2, lib=lib).reshape(2 * Mt - 1, (2 * M - 1) ** 2, 2)
+    np.testing.assert_allclose(t3[Mt - 1], oracle.cpb_table(M, w1[:, :2], b1, w2, b2, lib=lib), rtol=0, atol=1e-13)
+
+
 def pin_rope_freq_table(lib):
     """A per-head frequency table reaches the same result as the brute force."""
     H = W = 8
@@ -573,6 +628,8 @@ PINS = {
     "dwconv_closed_forms": pin_dwconv_closed_forms,
     "window_linear": pin_window_linear,
     "lse": pin_lse,
+    "video_bruteforce": pin_video_bruteforce,
+    "video_reduces_to_2d": pin_video_reduces_to_2d,
 }
 
 

@@ -173,6 +173,9 @@ def main(argv=None) -> int:
     ap.add_argument("--linmapper", action="store_true",
                     help="time LinMapper's in-window linear mapping (swin_window_linear) on the "
                          "workload's values instead of the attention")
+    ap.add_argument("--video", action="store_true",
+                    help="time video (3D) window attention instead: swin_window_attn3d_fwd on the video "
+                         "workload (16^2 x 8 windows), its table from swin_cpb_table3d")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run copies of known size for HBM-counter calibration: y = -x over "
                          "2^28 fp32 (whole lines), then an interleaved window gather and its "
@@ -188,6 +191,8 @@ def main(argv=None) -> int:
 
     from vision_transformer_windowed_partition_amd import binding, synth
 
+    if args.video:
+        return bench_video(args)
     wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     x = synth.make_inputs(wl)
@@ -593,6 +598,79 @@ def bench_linmapper(args, wl, sets, nsets, stream) -> int:
         "data": "synthetic (seeded N(0,1) values, randn/sqrt(N) window matrices)",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "W": wl.W, "C": wl.C, "heads": wl.heads,
                    "M": wl.M, "shift": wl.shift, "partition": wl.partition, "pass": "linmapper",
+                   "cache": "warm" if args.warm else f"cold ({nsets} rotating sets)",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+def bench_video(args) -> int:
+    """Video (3D) window attention: swin_window_attn3d_fwd with the table from
+    swin_cpb_table3d in each step.  Algorithmic work as for 2D windows: 4 N C
+    flops per token (N = Mt M^2) and q, k, v read and o written once."""
+    import torch
+
+    from vision_transformer_windowed_partition_amd import binding, synth
+
+    wl = synth.VIDEO_WORKLOADS[0]
+    dev = torch.device("cuda:0")
+    x = synth.make_video_inputs(wl)
+    set_bytes = wl.bytes
+    nsets = 1 if args.warm else max(2, math.ceil(2 * MALL_BYTES / set_bytes) + 1)
+    sets = []
+    for i in range(nsets):
+        qkv = tuple(x[n].to(dev) for n in "qkv") if i == 0 else tuple(t.clone() for t in sets[0][:3])
+        sets.append(qkv + (torch.empty_like(qkv[0]),))
+    par = {n: x[n].to(dev) for n in ("tau", "w1", "b1", "w2", "b2")}
+    table = torch.empty(((2 * wl.Mt - 1) * (2 * wl.M - 1) ** 2, wl.heads), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, timed=None):
+        q, k, v, o = sets[i % nsets]
+        tab = binding.swin_cpb_table3d(wl.Mt, wl.M, par["w1"], par["b1"], par["w2"], par["b2"], out=table,
+                                       stream=stream)
+        if timed is not None:
+            timer.record(timed, False)
+        binding.swin_window_attn3d_fwd(q, k, v, heads=wl.heads, Mt=wl.Mt, M=wl.M, shift_t=wl.shift_t,
+                                       shift=wl.shift, partition=wl.partition, sim=wl.sim, pos=wl.pos,
+                                       tau=par["tau"], table=tab, out=o, stream=stream)
+        if timed is not None:
+            timer.record(timed, True)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    timer = HipTimer(args.steps, stream.cuda_stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = timer.elapsed_ms()
+    timer.close()
+    kern_avg = sum(kern_ms) / len(kern_ms)
+    roof = _roof(wl.flops, wl.bytes, kern_avg, FP32_PEAK_TFLOPS, "alu")
+    roof.update({"kernel": "attn_video_kernel", "kernel_ms": round(kern_avg, 5),
+                 "alg_flops_per_launch": wl.flops, "alg_bytes_per_launch": wl.bytes, "traffic": None})
+    out = {
+        "metric": "video window-attn fwd tokens/s",
+        "value": round(wl.tokens / (wall / args.steps), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v, random-init 3-input log-CPB MLP)",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "W": wl.W, "C": wl.C,
+                   "heads": wl.heads, "Mt": wl.Mt, "M": wl.M, "shift_t": wl.shift_t, "shift": wl.shift,
+                   "partition": wl.partition, "sim": wl.sim, "pos": wl.pos, "pass": "video",
                    "cache": "warm" if args.warm else f"cold ({nsets} rotating sets)",
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,

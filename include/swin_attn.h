@@ -219,6 +219,38 @@ int swin_window_attn_bwd_lse(const swin_attn_desc* desc, const void* q, const vo
                              const float* table, const float* rope_freqs, const float* lse, void* dq,
                              void* dk, void* dv, float* dtau, float* dtable, void* stream);
 
+/* Bias table of video (3D) windows Mt x M x M ([SwinV2] eq. 3-4 with a third
+ * offset; appendix A2 fine-tunes on video with 16^2 x 8 windows, the page
+ * gives no 3D form): row ((dt + Mt-1)(2M-1) + dy + M-1)(2M-1) + dx + M-1 of
+ * table ((2Mt-1)(2M-1)^2 x heads fp32, written) holds
+ *   G(x) = W2 relu(W1 x + b1) + b2,  x = sign(d) log(1 + |d|) of (dx, dy, dt),
+ * w1: hidden x 3 (columns dx, dy, dt), b1: hidden or NULL, w2: heads x hidden,
+ * b2: heads or NULL; device fp32, the table must not overlap them.  Each
+ * value is a fp32 sum over hidden.  1 <= Mt, M <= 64, 1 <= heads <= 64,
+ * 1 <= hidden <= 4096 (SWIN_EINVAL otherwise). */
+int swin_cpb_table3d(int32_t Mt, int32_t M, int32_t heads, int32_t hidden, const float* w1,
+                     const float* b1, const float* w2, const float* b2, float* table, void* stream);
+
+/* Window attention over video (3D) windows: swin_window_attn_fwd's logit,
+ * bias, exclusion and softmax ([SwinV2] eq. 1-2 and the window-attention
+ * pseudocode) over (B, T, H, W, C) grids, channels last, windows of
+ * Mt x M x M tokens.  desc gives B, H, W, C, heads, M, shift, partition, sim,
+ * pos (NONE or TABLE; ROPE2D is SWIN_EUNSUPPORTED), dtype and tau_min, with
+ * layout GRID; T frames, temporal window Mt (T % Mt == 0) and temporal shift
+ * shift_t (0 <= shift_t < Mt, 0 for interleaved windows) come as arguments.
+ * Reading ([SwinV2] appendix A2, [Iwin] abstract: video models, no 3D form on
+ * the pages): the temporal axis is rolled (or interleaved) like the other
+ * two, pairs whose shift regions differ on any axis are excluded, and the
+ * bias is swin_cpb_table3d's table, indexed by the offsets (dt, dy, dx).
+ * q, k, v, out: device tensors of desc->dtype, 16-byte aligned, out not
+ * overlapping q, k or v; tau: heads fp32 (COSINE); table: as written by
+ * swin_cpb_table3d (TABLE).  Vector-ALU kernel: similarities and logits in
+ * fp64, exponentials and sums in fp32, output rounded once.  The head's
+ * table must fit LDS next to a 64-key chunk (SWIN_EUNSUPPORTED otherwise). */
+int swin_window_attn3d_fwd(const swin_attn_desc* desc, int32_t T, int32_t Mt, int32_t shift_t,
+                           const void* q, const void* k, const void* v, void* out, const float* tau,
+                           const float* table, void* stream);
+
 /* Backward of swin_cpb_table_ex ([SwinV2] eq. 3-4, card "Paper vs code"):
  * from dtable ((2M-1)^2 x heads fp32) the gradients of the meta network's
  * parameters, dw1 (hidden x 2), db1 (hidden, or NULL to skip), dw2

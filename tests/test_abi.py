@@ -36,6 +36,7 @@ def test_header_declares_the_boundary():
                                            "swin_window_reverse",
                                            "swin_window_attn_fwd", "swin_window_attn_kernel",
                                            "swin_window_attn_fwd_lse", "swin_window_attn_bwd_lse",
+                                           "swin_cpb_table3d", "swin_window_attn3d_fwd",
                                            "swin_window_attn_bwd_kernel",
                                            "swin_qkv_proj", "swin_proj_post_norm", "swin_dwconv_add",
                                            "swin_window_linear",
@@ -131,6 +132,32 @@ def test_lse_entries_reject(L):
     assert bwd(None) == SWIN_EINVAL
     assert bwd(ctypes.c_void_p(0x50000001)) == SWIN_EINVAL                  # misaligned
     assert L.swin_window_attn_fwd_lse(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == SWIN_EINVAL
+
+
+def test_video_entries_reject(L):
+    """Video windows: bad temporal geometry, rotary positions, the windows
+    layout, missing tensors and misalignment are refused before any launch."""
+    f = lambda d=None, T=4, Mt=2, st=1, q=FAKE, out=ctypes.c_void_p(0x20000000), tau=FAKE, table=FAKE: \
+        L.swin_window_attn3d_fwd(ctypes.byref(d if d is not None else _desc()), T, Mt, st, q, FAKE, FAKE, out, tau,
+                                 table, None)
+    assert f(T=5) == SWIN_EINVAL                          # T % Mt
+    assert f(T=0) == SWIN_EINVAL
+    assert f(st=2) == SWIN_EINVAL                         # shift_t >= Mt
+    assert f(st=-1) == SWIN_EINVAL
+    assert f(d=_desc(partition=1, shift=0), st=1) == SWIN_EINVAL      # interleaved takes no shift
+    assert f(d=_desc(pos=2)) == SWIN_EUNSUPPORTED         # no rotary form in 3D
+    assert f(d=_desc(layout=1)) == SWIN_EUNSUPPORTED
+    assert f(Mt=65, T=65, st=0) == SWIN_EUNSUPPORTED
+    assert f(q=None) == SWIN_EINVAL
+    assert f(tau=None) == SWIN_EINVAL                     # COSINE needs tau
+    assert f(table=None) == SWIN_EINVAL                   # TABLE needs the table
+    assert f(q=ctypes.c_void_p(0x10008)) == SWIN_EINVAL   # misaligned
+    assert f(out=ctypes.c_void_p(0x10000 + 64)) == SWIN_EINVAL       # out overlaps q
+    t3 = lambda Mt=2, M=4, heads=2, hidden=8, table=ctypes.c_void_p(0x20000000): L.swin_cpb_table3d(
+        Mt, M, heads, hidden, FAKE, None, ctypes.c_void_p(0x30000000), None, table, None)
+    assert t3(Mt=0) == SWIN_EINVAL and t3(M=65) == SWIN_EINVAL and t3(heads=0) == SWIN_EINVAL
+    assert t3(hidden=0) == SWIN_EINVAL and t3(table=None) == SWIN_EINVAL
+    assert t3(table=ctypes.c_void_p(0x10000 + 16)) == SWIN_EINVAL      # overlaps w1
 
 
 def _qkv(L, x=FAKE, w=ctypes.c_void_p(0x30000000), b=None, q=ctypes.c_void_p(0x40000000),

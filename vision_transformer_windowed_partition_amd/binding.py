@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
         L.swin_window_attn_fwd.argtypes = [ctypes.POINTER(SwinAttnDesc)] + [vp] * 8
         L.swin_window_attn_bwd.restype = i32
         L.swin_window_attn_bwd.argtypes = [ctypes.POINTER(SwinAttnDesc)] + [vp] * 14
+        L.swin_cpb_table3d.restype = i32
+        L.swin_cpb_table3d.argtypes = [i32] * 4 + [vp] * 6
+        L.swin_window_attn3d_fwd.restype = i32
+        L.swin_window_attn3d_fwd.argtypes = [ctypes.POINTER(SwinAttnDesc), i32, i32, i32] + [vp] * 7
         L.swin_window_attn_fwd_lse.restype = i32
         L.swin_window_attn_fwd_lse.argtypes = [ctypes.POINTER(SwinAttnDesc)] + [vp] * 9
         L.swin_window_attn_bwd_lse.restype = i32
@@ -237,6 +241,41 @@ def swin_window_attn_fwd_lse(q, k, v, *, heads: int, M: int, shift: int = 0, par
                                           _ptr(tau), _ptr(table), _ptr(rope_freqs), _ptr(lse),
                                           _stream(q, stream)))
     return out, lse
+
+
+def swin_cpb_table3d(Mt: int, M: int, w1, b1, w2, b2, *, out=None, stream=None):
+    """((2Mt-1)(2M-1)^2, heads) fp32 bias table of video windows; w1 is (hidden, 3)."""
+    hidden, heads = w1.shape[0], w2.shape[0]
+    for t in (w1, b1, w2, b2):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("w1, b1, w2, b2 must be contiguous fp32")
+    if w1.shape != (hidden, 3) or w2.shape != (heads, hidden):
+        raise ValueError("w1 must be (hidden, 3) and w2 (heads, hidden)")
+    if out is None:
+        out = torch.empty(((2 * Mt - 1) * (2 * M - 1) ** 2, heads), dtype=torch.float32, device=w1.device)
+    _check(lib().swin_cpb_table3d(Mt, M, heads, hidden, _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(out),
+                                  _stream(w1, stream)))
+    return out
+
+
+def swin_window_attn3d_fwd(q, k, v, *, heads: int, Mt: int, M: int, shift_t: int = 0, shift: int = 0,
+                           partition="cyclic", sim="cosine", pos="none", tau=None, table=None,
+                           tau_min: float = 0.01, out=None, stream=None):
+    """Video-window attention forward: q, k, v (B, T, H, W, C), windows Mt x M x M."""
+    for t in (q, k, v):
+        if not t.is_contiguous() or t.dtype != q.dtype or t.shape != q.shape or t.dim() != 5:
+            raise ValueError("q, k, v must be contiguous (B, T, H, W, C) tensors of one shape and dtype")
+    for t in (tau, table):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("tau and table must be contiguous fp32")
+    B, T, H, W, C = q.shape
+    desc = make_desc(B=B, H=H, W=W, C=C, heads=heads, M=M, shift=shift, partition=partition, sim=sim, pos=pos,
+                     dtype=q.dtype, tau_min=tau_min)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().swin_window_attn3d_fwd(ctypes.byref(desc), T, Mt, shift_t, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                        _ptr(tau), _ptr(table), _stream(q, stream)))
+    return out
 
 
 def swin_window_attn_bwd(q, k, v, out, dout, *, heads: int, M: int, shift: int = 0, partition="cyclic",

@@ -11,6 +11,7 @@
 #include "launch.hpp"
 #include "launch_bwd.hpp"
 #include "launch_proj.hpp"
+#include "launch_video.hpp"
 
 namespace {
 
@@ -289,6 +290,59 @@ int swin_window_attn_fwd_lse(const swin_attn_desc* d, const void* q, const void*
 {
     if (!lse && d && (int64_t)d->B * d->H * d->W * d->C > 0) return fail(SWIN_EINVAL, "NULL lse");
     return attn_fwd(d, q, k, v, out, tau, table, rope_freqs, lse, stream);
+}
+
+int swin_cpb_table3d(int32_t Mt, int32_t M, int32_t heads, int32_t hidden, const float* w1, const float* b1,
+                     const float* w2, const float* b2, float* table, void* stream)
+{
+    if (M < 1 || M > 64) return fail(SWIN_EINVAL, "M=%d outside [1, 64]", M);
+    if (Mt < 1 || Mt > 64) return fail(SWIN_EINVAL, "Mt=%d outside [1, 64]", Mt);
+    if (heads < 1 || heads > 64) return fail(SWIN_EINVAL, "heads=%d outside [1, 64]", heads);
+    if (hidden < 1 || hidden > 4096) return fail(SWIN_EINVAL, "hidden=%d outside [1, 4096]", hidden);
+    if (!w1 || !w2 || !table) return fail(SWIN_EINVAL, "NULL w1, w2 or table");
+    const size_t tb = (size_t)(2 * Mt - 1) * (2 * M - 1) * (2 * M - 1) * heads * sizeof(float);
+    if (overlaps(table, tb, w1, (size_t)hidden * 3 * 4) || overlaps(table, tb, w2, (size_t)heads * hidden * 4) ||
+        (b1 && overlaps(table, tb, b1, (size_t)hidden * 4)) || (b2 && overlaps(table, tb, b2, (size_t)heads * 4)))
+        return fail(SWIN_EINVAL, "table overlaps a parameter tensor");
+    return hip_status(swin::launch_cpb_table3d(Mt, M, heads, hidden, w1, b1, w2, b2, table, (hipStream_t)stream),
+                      "swin_cpb_table3d launch");
+}
+
+int swin_window_attn3d_fwd(const swin_attn_desc* d, int32_t T, int32_t Mt, int32_t shift_t, const void* q,
+                           const void* k, const void* v, void* out, const float* tau, const float* table,
+                           void* stream)
+{
+    int st = check_desc(d, false);
+    if (st) return st;
+    if (d->pos == SWIN_POS_ROPE2D) return fail(SWIN_EUNSUPPORTED, "video windows: no rotary form");
+    if (d->layout != SWIN_LAYOUT_GRID) return fail(SWIN_EUNSUPPORTED, "video windows: grid layout only");
+    if (T < 1 || Mt < 1 || T % Mt) return fail(SWIN_EINVAL, "T=%d is not a positive multiple of Mt=%d", T, Mt);
+    if (Mt > 64) return fail(SWIN_EUNSUPPORTED, "Mt=%d: temporal windows above 64 are not built", Mt);
+    if (shift_t < 0 || shift_t >= Mt) return fail(SWIN_EINVAL, "shift_t=%d outside [0, Mt)", shift_t);
+    if (d->partition == SWIN_PART_INTERLEAVED && shift_t != 0)
+        return fail(SWIN_EINVAL, "interleaved windows take no shift");
+    const size_t es = d->dtype == SWIN_DT_F32 ? 4 : 2;
+    const size_t bytes = (size_t)d->B * T * d->H * d->W * d->C * es;
+    if (d->sim == SWIN_SIM_COSINE && !tau) return fail(SWIN_EINVAL, "COSINE needs tau");
+    if (d->pos == SWIN_POS_TABLE && !table) return fail(SWIN_EINVAL, "POS_TABLE needs a table");
+    swin::VideoArgs a{};
+    a.B = d->B; a.T = T; a.H = d->H; a.W = d->W; a.C = d->C; a.heads = d->heads;
+    a.Mt = Mt; a.M = d->M; a.shift_t = shift_t; a.shift = d->shift; a.part = d->partition;
+    a.sim = d->sim; a.pos = d->pos; a.dtype = d->dtype; a.tau_min = d->tau_min;
+    a.nwt = T / Mt; a.nwr = d->H / d->M; a.nwc = d->W / d->M; a.N = Mt * d->M * d->M;
+    const int64_t nwin = (int64_t)d->B * a.nwt * a.nwr * a.nwc;
+    if (nwin > INT32_MAX) return fail(SWIN_EUNSUPPORTED, "too many windows");
+    a.nwin = (int)nwin;
+    if (swin::video_lds(a, nullptr) == 0)
+        return fail(SWIN_EUNSUPPORTED, "Mt=%d, M=%d: the bias table does not fit LDS", Mt, d->M);
+    if (bytes == 0) return SWIN_OK;
+    if (!q || !k || !v || !out) return fail(SWIN_EINVAL, "NULL q, k, v or out");
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15)
+        return fail(SWIN_EINVAL, "q, k, v and out must be 16-byte aligned");
+    if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
+        return fail(SWIN_EINVAL, "out overlaps q, k or v");
+    a.q = q; a.k = k; a.v = v; a.out = out; a.tau = tau; a.table = table;
+    return hip_status(swin::launch_attn_video(a, (hipStream_t)stream), "swin_window_attn3d_fwd launch");
 }
 
 int swin_window_attn_bwd(const swin_attn_desc* d, const void* q, const void* k, const void* v,

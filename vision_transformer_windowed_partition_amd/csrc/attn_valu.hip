@@ -17,6 +17,7 @@
 // another shift region; softmax; weighted sum of v.
 #include "common.hpp"
 #include "launch.hpp"
+#include "rows.hpp"
 
 namespace swin {
 
@@ -24,37 +25,6 @@ namespace {
 
 constexpr int D = 32;
 constexpr int KC_MAX = 256;   // keys per LDS chunk
-
-template <typename T> __device__ __forceinline__ void load_row(const T* p, float* f);
-template <> __device__ __forceinline__ void load_row<float>(const float* p, float* f)
-{
-    const float4* v = (const float4*)p;
-#pragma unroll
-    for (int i = 0; i < D / 4; ++i) {
-        float4 x = v[i];
-        f[4 * i] = x.x; f[4 * i + 1] = x.y; f[4 * i + 2] = x.z; f[4 * i + 3] = x.w;
-    }
-}
-template <> __device__ __forceinline__ void load_row<uint16_t>(const uint16_t* p, float* f)
-{
-    const u32x4* v = (const u32x4*)p;
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) unpack_bf16x8(v[i], f + 8 * i);
-}
-
-template <typename T> __device__ __forceinline__ void store_row(T* p, const float* f);
-template <> __device__ __forceinline__ void store_row<float>(float* p, const float* f)
-{
-    float4* v = (float4*)p;
-#pragma unroll
-    for (int i = 0; i < D / 4; ++i) v[i] = make_float4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
-}
-template <> __device__ __forceinline__ void store_row<uint16_t>(uint16_t* p, const float* f)
-{
-    bf16x8* v = (bf16x8*)p;
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) v[i] = pack_bf16x8(f + 8 * i);
-}
 
 // Rotate channel pairs by the window-local position: [0, D/2) by row r,
 // [D/2, D) by column c; cs/sn tables are [pos][half][D/4].
@@ -125,7 +95,7 @@ attn_valu_kernel(AttnParams p, int kc)
         float q[D], acc[D];
         double scale = 0.0;
         if (valid) {
-            load_row<T>(qg + token_offset(g, win, ri, ci) + h * D, q);
+            load_row32<T>(qg + token_offset(g, win, ri, ci) + h * D, q);
             if (POS == SWIN_POS_ROPE2D) rope_apply(q, ri, ci, cs, sn);
             if (SIM == SWIN_SIM_COSINE) {
                 double ss = 0.0;
@@ -154,8 +124,8 @@ attn_valu_kernel(AttnParams p, int kc)
                 const int j = j0 + tid, rj = j / M, cj = j % M;
                 float kr[D], vr[D];
                 const int64_t off = token_offset(g, win, rj, cj) + h * D;
-                load_row<T>(kg + off, kr);
-                load_row<T>(vg + off, vr);
+                load_row32<T>(kg + off, kr);
+                load_row32<T>(vg + off, vr);
                 if (POS == SWIN_POS_ROPE2D) rope_apply(kr, rj, cj, cs, sn);
                 if (SIM == SWIN_SIM_COSINE) {
                     double ss = 0.0;
@@ -198,7 +168,7 @@ attn_valu_kernel(AttnParams p, int kc)
             const float inv = 1.0f / l;
 #pragma unroll
             for (int e = 0; e < D; ++e) acc[e] *= inv;
-            store_row<T>(og + token_offset(g, win, ri, ci) + h * D, acc);
+            store_row32<T>(og + token_offset(g, win, ri, ci) + h * D, acc);
             if (p.lse) p.lse[((size_t)win * g.heads + h) * N + t] = (float)(m + log((double)l));
         }
     }

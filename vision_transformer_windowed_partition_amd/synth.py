@@ -160,3 +160,73 @@ def small(name: str = "tiny", *, B=2, H=16, W=16, C=64, heads=2, M=8, shift=4,
           partition="cyclic", sim="cosine", pos="table", dtype="f32", hidden=64) -> Workload:
     """A small workload for tests (same draw recipe)."""
     return Workload(name, B, H, W, C, heads, M, shift, partition, sim, pos, dtype, hidden)
+
+
+@dataclass(frozen=True)
+class VideoWorkload:
+    """A video (3D) window workload: (B, T, H, W, C) tokens, windows Mt x M x M."""
+    name: str
+    B: int
+    T: int
+    H: int
+    W: int
+    C: int
+    heads: int
+    Mt: int
+    M: int
+    shift_t: int
+    shift: int
+    partition: str
+    sim: str
+    pos: str                # "none" | "table"
+    dtype: str
+    hidden: int = 512
+
+    @property
+    def N(self) -> int:
+        return self.Mt * self.M * self.M
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.T * self.H * self.W
+
+    @property
+    def elem_size(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def flops(self) -> int:
+        """4 N C flops per token (QK^T and PV, dense within the window)."""
+        return 4 * self.tokens * self.N * self.C
+
+    @property
+    def bytes(self) -> int:
+        """q, k, v read once and o written once."""
+        return 4 * self.tokens * self.C * self.elem_size
+
+
+# The SwinV2 video fine-tuning shape (appendix A2: 256^2 x 8 frames, 16^2 x 8
+# windows) at the first stage of a Tiny backbone (4 x 4 patches: a 64 x 64
+# grid per frame, C = 96, 3 heads), 8 clips.
+VIDEO_WORKLOADS = [
+    VideoWorkload("swinv2t_k400_8x256px_w16x8", 8, 8, 64, 64, 96, 3, 8, 16, 0, 8, "cyclic", "cosine", "table",
+                  "bf16"),
+]
+
+
+def make_video_inputs(wl: VideoWorkload, seed: int = 0, tau_range=(0.1, 1.0)) -> dict:
+    """q, k, v (B, T, H, W, C) N(0, 1) in the workload dtype; tau as for the 2D
+    workloads; the meta network w1 (hidden, 3), b1, w2, b2 at 0.02 N(0, 1)."""
+    g = torch.Generator().manual_seed(int(seed))
+    shape = (wl.B, wl.T, wl.H, wl.W, wl.C)
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    lo, hi = math.log(tau_range[0]), math.log(tau_range[1])
+    tau = torch.exp(torch.rand(wl.heads, generator=g, dtype=torch.float32) * (hi - lo) + lo).clamp_min(0.01)
+    w1 = 0.02 * torch.randn(wl.hidden, 3, generator=g, dtype=torch.float32)
+    b1 = 0.02 * torch.randn(wl.hidden, generator=g, dtype=torch.float32)
+    w2 = 0.02 * torch.randn(wl.heads, wl.hidden, generator=g, dtype=torch.float32)
+    b2 = 0.02 * torch.randn(wl.heads, generator=g, dtype=torch.float32)
+    dt = torch_dtype(wl.dtype)
+    return dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), tau=tau, w1=w1, b1=b1, w2=w2, b2=b2)

@@ -652,8 +652,13 @@ def bench_video(args) -> int:
     kern_ms = timer.elapsed_ms()
     timer.close()
     kern_avg = sum(kern_ms) / len(kern_ms)
-    roof = _roof(wl.flops, wl.bytes, kern_avg, FP32_PEAK_TFLOPS, "alu")
-    roof.update({"kernel": "attn_video_kernel", "kernel_ms": round(kern_avg, 5),
+    desc = binding.make_desc(B=wl.B, H=wl.H, W=wl.W, C=wl.C, heads=wl.heads, M=wl.M, shift=wl.shift,
+                             partition=wl.partition, sim=wl.sim, pos=wl.pos, dtype=sets[0][0].dtype)
+    kernel = binding.swin_window_attn3d_kernel(desc, wl.T, wl.Mt)
+    mfma = kernel == "attn_video_mfma_kernel"
+    roof = _roof(wl.flops, wl.bytes, kern_avg, BF16_PEAK_TFLOPS if mfma else FP32_PEAK_TFLOPS,
+                 "mfma" if mfma else "alu")
+    roof.update({"kernel": kernel, "kernel_ms": round(kern_avg, 5),
                  "alg_flops_per_launch": wl.flops, "alg_bytes_per_launch": wl.bytes, "traffic": None})
     out = {
         "metric": "video window-attn fwd tokens/s",

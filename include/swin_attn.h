@@ -244,12 +244,21 @@ int swin_cpb_table3d(int32_t Mt, int32_t M, int32_t heads, int32_t hidden, const
  * bias is swin_cpb_table3d's table, indexed by the offsets (dt, dy, dx).
  * q, k, v, out: device tensors of desc->dtype, 16-byte aligned, out not
  * overlapping q, k or v; tau: heads fp32 (COSINE); table: as written by
- * swin_cpb_table3d (TABLE).  Vector-ALU kernel: similarities and logits in
- * fp64, exponentials and sums in fp32, output rounded once.  The head's
- * table must fit LDS next to a 64-key chunk (SWIN_EUNSUPPORTED otherwise). */
+ * swin_cpb_table3d (TABLE).  bf16 with M = 8 or 16 runs on the matrix cores
+ * (the products on bf16 operands with fp32 accumulation, COSINE's unit q and
+ * k scaled by 1/tau rounded to bf16 unless tau < 0.1, the weights rounded to
+ * bf16 before P V, softmax in fp32 with a running maximum); everything else
+ * on the vector ALUs (similarities and logits in fp64, exponentials and sums
+ * in fp32), where the head's table must fit LDS next to a 64-key chunk
+ * (SWIN_EUNSUPPORTED otherwise).  The output is rounded once. */
 int swin_window_attn3d_fwd(const swin_attn_desc* desc, int32_t T, int32_t Mt, int32_t shift_t,
                            const void* q, const void* k, const void* v, void* out, const float* tau,
                            const float* table, void* stream);
+
+/* Name of the kernel swin_window_attn3d_fwd runs for desc and the temporal
+ * sizes ("attn_video_mfma_kernel" or "attn_video_kernel"; "" for a NULL or
+ * malformed descriptor).  A static string; no device work. */
+const char* swin_window_attn3d_kernel(const swin_attn_desc* desc, int32_t T, int32_t Mt);
 
 /* Backward of swin_cpb_table_ex ([SwinV2] eq. 3-4, card "Paper vs code"):
  * from dtable ((2M-1)^2 x heads fp32) the gradients of the meta network's

@@ -37,6 +37,7 @@ def test_header_declares_the_boundary():
                                            "swin_window_attn_fwd", "swin_window_attn_kernel",
                                            "swin_window_attn_fwd_lse", "swin_window_attn_bwd_lse",
                                            "swin_cpb_table3d", "swin_window_attn3d_fwd",
+                                           "swin_window_attn3d_kernel",
                                            "swin_window_attn_bwd_kernel",
                                            "swin_qkv_proj", "swin_proj_post_norm", "swin_dwconv_add",
                                            "swin_window_linear",

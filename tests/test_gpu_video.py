@@ -26,7 +26,10 @@ CASES = [
     (6, 12, 12, 3, 6, 1, 3, "cyclic", "cosine", "none"),      # 108-token windows
     (2, 8, 8, 1, 8, 0, 4, "cyclic", "cosine", "table"),       # one frame a window: the 2D attention per frame
     (8, 32, 32, 8, 16, 0, 8, "cyclic", "cosine", "table"),    # the pages' 16^2 x 8 windows (2048 tokens)
+    (6, 16, 16, 3, 8, 1, 4, "cyclic", "cosine", "table"),     # 3 query frames on 4 wavefronts, every axis shifted
+    (4, 32, 32, 2, 16, 1, 8, "cyclic", "dot", "none"),
 ]
+# bf16 with M = 8 or 16 runs on the matrix cores, the rest on the vector ALUs
 
 
 def _compare(got, ref, dtype, what):
@@ -62,6 +65,31 @@ def test_video_parity(case, dtype):
     ref = oracle.window_attn3d(f64(q), f64(k), f64(v), heads=2, Mt=Mt, M=M, shift_t=st, shift=s, partition=part,
                                sim=sim, pos=pos, tau=f64(tau), table=None if table is None else f64(table))
     _compare(f64(out), ref, dtype, str(case))
+
+
+@pytest.mark.parametrize("M", [8, 16])
+def test_video_small_tau(M):
+    """COSINE with tau below 0.1 for one head: the matrix-core kernel keeps
+    raw k with 1/||k|| in fp32 instead of rounding k / ||k|| / tau."""
+    case = (4, 2 * M, 2 * M, 2, M, 1, M // 2, "cyclic", "cosine", "table")
+    q, k, v, tau, table = _inputs(case, "bf16", seed=M)
+    tau = torch.tensor([0.03, 0.5])
+    d = lambda t: t.to(DEV)
+    out = binding.swin_window_attn3d_fwd(d(q), d(k), d(v), heads=2, Mt=2, M=M, shift_t=1, shift=M // 2,
+                                         sim="cosine", pos="table", tau=d(tau), table=d(table))
+    torch.cuda.synchronize()
+    ref = oracle.window_attn3d(f64(q), f64(k), f64(v), heads=2, Mt=2, M=M, shift_t=1, shift=M // 2, sim="cosine",
+                               pos="table", tau=f64(tau), table=f64(table))
+    _compare(f64(out), ref, "bf16", f"small tau M={M}")
+
+
+def test_video_kernel_choice():
+    d = lambda **kw: binding.make_desc(**{**dict(B=1, H=32, W=32, C=64, heads=2, M=16, shift=8, sim="cosine",
+                                                  pos="table", dtype=torch.bfloat16), **kw})
+    assert binding.swin_window_attn3d_kernel(d(), 8, 8) == "attn_video_mfma_kernel"
+    assert binding.swin_window_attn3d_kernel(d(M=8, shift=4), 8, 4) == "attn_video_mfma_kernel"
+    assert binding.swin_window_attn3d_kernel(d(dtype=torch.float32), 8, 8) == "attn_video_kernel"
+    assert binding.swin_window_attn3d_kernel(d(M=4, shift=2), 8, 8) == "attn_video_kernel"
 
 
 def test_video_one_frame_windows_match_2d():

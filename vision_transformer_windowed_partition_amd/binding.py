@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.swin_cpb_table3d.argtypes = [i32] * 4 + [vp] * 6
         L.swin_window_attn3d_fwd.restype = i32
         L.swin_window_attn3d_fwd.argtypes = [ctypes.POINTER(SwinAttnDesc), i32, i32, i32] + [vp] * 7
+        L.swin_window_attn3d_kernel.restype = ctypes.c_char_p
+        L.swin_window_attn3d_kernel.argtypes = [ctypes.POINTER(SwinAttnDesc), i32, i32]
         L.swin_window_attn_fwd_lse.restype = i32
         L.swin_window_attn_fwd_lse.argtypes = [ctypes.POINTER(SwinAttnDesc)] + [vp] * 9
         L.swin_window_attn_bwd_lse.restype = i32
@@ -276,6 +278,11 @@ def swin_window_attn3d_fwd(q, k, v, *, heads: int, Mt: int, M: int, shift_t: int
     _check(lib().swin_window_attn3d_fwd(ctypes.byref(desc), T, Mt, shift_t, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                         _ptr(tau), _ptr(table), _stream(q, stream)))
     return out
+
+
+def swin_window_attn3d_kernel(desc: SwinAttnDesc, T: int, Mt: int) -> str:
+    """Name of the kernel swin_window_attn3d_fwd runs for this descriptor."""
+    return lib().swin_window_attn3d_kernel(ctypes.byref(desc), T, Mt).decode()
 
 
 def swin_window_attn_bwd(q, k, v, out, dout, *, heads: int, M: int, shift: int = 0, partition="cyclic",

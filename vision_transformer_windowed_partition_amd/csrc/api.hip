@@ -342,7 +342,18 @@ int swin_window_attn3d_fwd(const swin_attn_desc* d, int32_t T, int32_t Mt, int32
     if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
         return fail(SWIN_EINVAL, "out overlaps q, k or v");
     a.q = q; a.k = k; a.v = v; a.out = out; a.tau = tau; a.table = table;
-    return hip_status(swin::launch_attn_video(a, (hipStream_t)stream), "swin_window_attn3d_fwd launch");
+    const hipError_t e = swin::video_mfma_supported(a) ? swin::launch_attn_video_mfma(a, (hipStream_t)stream)
+                                                       : swin::launch_attn_video(a, (hipStream_t)stream);
+    return hip_status(e, "swin_window_attn3d_fwd launch");
+}
+
+const char* swin_window_attn3d_kernel(const swin_attn_desc* d, int32_t T, int32_t Mt)
+{
+    if (!d || T < 1 || Mt < 1 || d->heads < 1 || d->M < 1) return "";
+    swin::VideoArgs a{};
+    a.B = d->B; a.T = T; a.H = d->H; a.W = d->W; a.C = d->C; a.heads = d->heads;
+    a.Mt = Mt; a.M = d->M; a.part = d->partition; a.sim = d->sim; a.pos = d->pos; a.dtype = d->dtype;
+    return swin::video_mfma_supported(a) ? "attn_video_mfma_kernel" : "attn_video_kernel";
 }
 
 int swin_window_attn_bwd(const swin_attn_desc* d, const void* q, const void* k, const void* v,

@@ -1,0 +1,342 @@
+// Video (3D) window attention on the gfx950 matrix cores: bf16 tensors, d = 32,
+// windows Mt x M x M with M = 8 or 16 (the reading of the video form is the
+// one the vector-ALU kernel in attn_video.hip follows: the SwinV2 card's
+// window attention, eq. 1-2 and the window-attention pseudocode, with a
+// temporal axis treated like the other two and the bias G(dx, dy, dt) of
+// eq. 3-4 from a (2Mt-1)(2M-1)^2 x heads table).
+//
+// A workgroup of four wavefronts owns one (window, head, query frame) for
+// M = 16, or (window, head, four query frames) for M = 8, one frame a
+// wavefront; either way each wavefront keeps four query tiles of 16 queries
+// live for the whole window: their q fragments, their running maxima and
+// their fp32 accumulators for O^T and the row sums.  The workgroup then
+// walks the window's key frames: per key frame it stages that frame's M x M
+// keys (unit-normalised and scaled by log2(e)/tau for COSINE, raw otherwise)
+// as MFMA A-fragments and its values by LDS-DMA, together with the table
+// slice of the time offset between each query frame and the key frame (a
+// (2M-1)^2 slice, in log2 units), and every wavefront runs its tiles over
+// the frame's 32-key chunks: S^T = K^ Q^T (the slice entries, or the scale,
+// enter as the accumulator or one FMA), the online normaliser per chunk
+// (running maximum, accumulators rescaled when it grows), P^T rounded to
+// bf16 and O^T += V^T P^T, row sums by a third product against ones.  A key
+// frame in another temporal shift region than a wavefront's query frame is
+// skipped by that wavefront; within a frame, spatial shift regions mask
+// 8-key groups (and single keys where a region edge splits a group).
+#include "common.hpp"
+#include "lanes.hpp"
+#include "launch_video.hpp"
+#include "tile_io.hpp"
+
+namespace swin {
+
+namespace {
+
+using namespace tio;
+using namespace lanes;
+
+constexpr int WAVES = 4;
+constexpr int TPW = 4;                 // query tiles a wavefront keeps live
+constexpr float PRECISE_TAU = 0.1f;    // COSINE below this: raw k and 1/||k|| in fp32
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float sumsq8(const u32x4 w)
+{
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t wi = w[i];
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wi), __builtin_bit_cast(bf16x2, wi), s,
+                                            false);
+    }
+    return s;
+}
+
+__device__ __forceinline__ int axis_pos(int L, int M, int s, int part, int w, int r)
+{
+    return part == SWIN_PART_INTERLEAVED ? w + r * (L / M) : (w * M + r + s) % L;
+}
+
+struct VTile {
+    bf16x8 qf;                 // q (unit for COSINE outside the precise path) as the B operand
+    f32x4 o0, o1, ls;          // O^T channels 0-15 and 16-31, row sums
+    float mrun;                // running maximum, log2 units
+    float qscale;              // per-score scale when not folded into K^
+    int qoff;                  // this lane's bias offset in a slice, chunk 0
+    uint32_t colbits;          // allowed key columns of this lane's 8-key group
+    int rlo, rhi;              // allowed key rows (spatial shift regions)
+};
+
+// One 32-key chunk c of the staged key frame for two tiles.
+template <int SIM, int POS, int M>
+__device__ __forceinline__ void chunk(const bf16x8* kst, const __bf16* vst, const float* bias2, const float* kinv,
+                                      VTile* T, int c, int lane, bool mask, bool fold, bool prec)
+{
+    constexpr int GPR = M / 8, S = 2 * M - 1;
+    const int grp = lane >> 4, li = lane & 15;
+    const int rj = (4 / GPR) * c + grp / GPR;          // key row of this lane's group
+    uint32_t bits[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) bits[i] = !mask ? 0xffu : (rj >= T[i].rlo && rj < T[i].rhi ? T[i].colbits : 0u);
+    if (mask && !__any((bits[0] | bits[1]) != 0u)) return;          // chunk masked for the whole wave
+    const bf16x8 ka = kst[(c * 2 + 0) * 64 + lane];
+    const bf16x8 kb = kst[(c * 2 + 1) * 64 + lane];
+    float kin[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+    if (prec) {
+        const f32x4 x0 = *(const f32x4*)(kinv + 32 * c + 8 * grp);
+        const f32x4 x1 = *(const f32x4*)(kinv + 32 * c + 8 * grp + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { kin[e] = x0[e]; kin[e + 4] = x1[e]; }
+    }
+    bf16x8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        float add[8];
+        if (POS == SWIN_POS_TABLE) {
+            const float* bp = bias2 + (bits[i] == 0u ? S * S : T[i].qoff + (4 / GPR) * c * S);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) add[e] = bp[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) add[e] = bits[i] == 0u ? -INFINITY : 0.0f;
+        }
+        const f32x4 za = {add[0], add[1], add[2], add[3]}, zb = {add[4], add[5], add[6], add[7]};
+        const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        const f32x4 sa = mfma(ka, T[i].qf, fold ? za : zero);
+        const f32x4 sb = mfma(kb, T[i].qf, fold ? zb : zero);
+        float x[8], cm = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float s = e < 4 ? sa[e] : sb[e - 4];
+            x[e] = fold ? s : fmaf(s, T[i].qscale * kin[e], add[e]);
+            if (mask) x[e] = (bits[i] >> e) & 1u ? x[e] : -INFINITY;
+            cm = fmaxf(cm, x[e]);
+        }
+        cm = max_x32(max_x16(cm));
+        const float mnew = fmaxf(T[i].mrun, cm);
+        const float mref = mnew == -INFINITY ? 0.0f : mnew;
+        const float alpha = __builtin_amdgcn_exp2f(T[i].mrun - mref);
+        T[i].o0 *= alpha; T[i].o1 *= alpha; T[i].ls *= alpha;
+        T[i].mrun = mnew;
+        float pr[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(x[e] - mref);
+        pb[i] = pack_bf16x8(pr);
+    }
+    const bf16x8 v0 = vt_frag(vst, c, 0, grp, li);
+    const bf16x8 v1 = vt_frag(vst, c, 1, grp, li);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        T[i].o0 = mfma(v0, pb[i], T[i].o0);
+        T[i].o1 = mfma(v1, pb[i], T[i].o1);
+        T[i].ls = mfma(ones, pb[i], T[i].ls);
+    }
+}
+
+template <int SIM, int POS, int M>
+__global__ void __launch_bounds__(256) attn_video_mfma_kernel(VideoArgs a, int units, int per_xcd)
+{
+    constexpr int NS = M * M, NCH = NS / 32, GPR = M / 8, S = 2 * M - 1;
+    constexpr int QF = M == 8 ? 4 : 1;           // query frames a workgroup owns
+    constexpr int SETS = 2 * NCH / WAVES;        // K tiles and 1 KB V pieces a wave stages
+    constexpr int SLICE = S * S + 8;             // a table slice and its row of -inf
+    __shared__ __attribute__((aligned(16))) bf16x8 kst[2 * NCH * 64];
+    __shared__ __attribute__((aligned(16))) __bf16 vst[NS * D];
+    __shared__ __attribute__((aligned(16))) float kinv[NS];
+    __shared__ __attribute__((aligned(16))) float bias2[POS == SWIN_POS_TABLE ? QF * SLICE : 1];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = lane >> 4, li = lane & 15;
+    const int work = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (work >= units) return;                   // whole workgroup, before any barrier
+    const int Mt = a.Mt;
+    const int fblocks = (Mt + QF - 1) / QF;
+    const int fb = work % fblocks, wh = work / fblocks;
+    const int h = wh % a.heads, win = wh / a.heads;
+    const int nW = a.nwt * a.nwr * a.nwc;
+    const int b = win / nW, wl = win - b * nW;
+    const int wt = wl / (a.nwr * a.nwc), wr = (wl / a.nwc) % a.nwr, wc = wl % a.nwc;
+    const bool cyc = a.part == SWIN_PART_CYCLIC;
+
+    // frame addressing: rows and columns as in the 2D kernels, frames by base
+    WinGeo wg;
+    wg.colb = (uint32_t)a.C * 2u;
+    wg.Hm = a.H; wg.Wm = a.W;
+    if (cyc) { wg.r0 = wr * M + a.shift; wg.c0 = wc * M + a.shift; wg.rs = wg.cs = 1; }
+    else { wg.r0 = wr; wg.c0 = wc; wg.rs = a.nwr; wg.cs = a.nwc; }
+    wg.rowb = a.W * wg.colb;
+    const int64_t frame_elems = (int64_t)a.H * a.W * a.C;
+    const uint32_t bytes = (uint32_t)(frame_elems - h * D) * 2u;
+    auto frame_base = [&](int t) -> int64_t {
+        return ((int64_t)b * a.T + axis_pos(a.T, Mt, a.shift_t, a.part, wt, t)) * frame_elems + h * D;
+    };
+    const bool last_r = cyc && a.shift > 0 && wr == a.nwr - 1;
+    const bool last_c = cyc && a.shift > 0 && wc == a.nwc - 1;
+    const bool mask = last_r || last_c;
+
+    const float tau_eff = SIM == SWIN_SIM_COSINE ? fmaxf(a.tau[h], a.tau_min) : 1.0f;
+    const float inv_tau = 1.0f / tau_eff;
+    const bool prec = SIM == SWIN_SIM_COSINE && tau_eff < PRECISE_TAU;
+    const bool fold = SIM == SWIN_SIM_COSINE && !prec;
+
+    // ---- this wave's query frame and tiles
+    const int ti = QF == 1 ? fb : fb * QF + wave;
+    const bool active = ti < Mt;
+    const int tiq = active ? ti : 0;
+    int tlo = 0, thi = Mt;
+    if (cyc) region_interval(wt, a.nwt, Mt, a.shift_t, tiq, tlo, thi);
+    VTile T[TPW];
+    {
+        const Rsrc qr = make_rsrc((const uint16_t*)a.q + frame_base(tiq), bytes);
+        u32x4 qraw[TPW];
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+            const int tq = QF == 1 ? wave + WAVES * k : k;
+            const int t = 16 * tq + li, ri = t / M, ci = t % M;
+            qraw[k] = load16(qr, masked(wg.tok(ri, ci) + 16u * grp, active));
+        }
+        const int kbase = (grp / GPR) * S + 8 * (grp % GPR);
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+            const int tq = QF == 1 ? wave + WAVES * k : k;
+            const int t = 16 * tq + li, ri = t / M, ci = t % M;
+            const float ss = sum_x32(sum_x16(sumsq8(qraw[k])));
+            const float qinv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));       // 1 / max(||q||, 1e-12)
+            T[k].qf = __builtin_bit_cast(bf16x8, qraw[k]);
+            if (fold) {
+                float qf[8];
+                unpack_bf16x8(qraw[k], qf);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qf[e] *= qinv;
+                T[k].qf = pack_bf16x8(qf);
+            }
+            T[k].qscale = SIM == SWIN_SIM_COSINE ? kLog2e * inv_tau * qinv : kLog2e * 0.17677669529663687f;
+            T[k].o0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            T[k].o1 = T[k].o0;
+            T[k].ls = T[k].o0;
+            T[k].mrun = -INFINITY;
+            T[k].qoff = (M - 1 - ri) * S + (M - 1 - ci) + kbase;
+            int clo = 0, chi = M;
+            T[k].rlo = 0; T[k].rhi = M;
+            if (last_r) { if (ri < M - a.shift) T[k].rhi = M - a.shift; else T[k].rlo = M - a.shift; }
+            if (last_c) { if (ci < M - a.shift) chi = M - a.shift; else clo = M - a.shift; }
+            const uint32_t cmask = ((1u << chi) - 1u) & ~((1u << clo) - 1u);
+            T[k].colbits = (cmask >> (8 * (grp % GPR))) & 0xffu;
+        }
+    }
+    if (POS == SWIN_POS_TABLE && tid < 8 * QF) bias2[(tid >> 3) * SLICE + S * S + (tid & 7)] = -INFINITY;
+
+    // ---- key frames
+    for (int tj = 0; tj < Mt; ++tj) {
+        __syncthreads();                         // the previous frame's LDS is consumed
+        const int64_t kb0 = frame_base(tj);
+        const Rsrc kr = make_rsrc((const uint16_t*)a.k + kb0, bytes);
+        const RawRsrc vraw = raw_rsrc((const uint16_t*)a.v + kb0, bytes);
+        u32x4 kraw[SETS];
+#pragma unroll
+        for (int k = 0; k < SETS; ++k) {
+            const int f = wave + WAVES * k, c = f >> 1, t = f & 1;
+            const int gam = 4 * c + (li >> 2);
+            const int rj = gam / GPR, cj = 8 * (gam % GPR) + (li & 3) + 4 * t;
+            kraw[k] = load16(kr, wg.tok(rj, cj) + 16u * grp);
+        }
+#pragma unroll
+        for (int k = 0; k < SETS; ++k) {
+            const int j = wave + WAVES * k;
+            const int s = 16 * j + (lane >> 2);
+            const int rj = s / M, cj = s % M;
+            const int piece = (lane & 3) ^ v_swizzle(s);
+            dma16(vraw, vst + (size_t)j * 512, wg.tok(rj, cj) + 16u * piece);
+        }
+        if (POS == SWIN_POS_TABLE) {
+            // slices of the offsets ti - tj, reversed (row r at S*S - 1 - r), log2 units
+            for (int i = tid; i < QF * S * S; i += WAVES * 64) {
+                const int q = i / (S * S), r = i - q * (S * S);
+                const int tq = QF == 1 ? fb : min(fb * QF + q, Mt - 1);
+                const int row = (tq - tj + Mt - 1) * (S * S) + r;
+                bias2[q * SLICE + S * S - 1 - r] = a.table[(size_t)row * a.heads + h] * kLog2e;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < SETS; ++k) {
+            const int f = wave + WAVES * k, c = f >> 1, t = f & 1;
+            const float ss = sum_x32(sum_x16(sumsq8(kraw[k])));
+            bf16x8 kfrag = __builtin_bit_cast(bf16x8, kraw[k]);
+            if (SIM == SWIN_SIM_COSINE) {
+                const float inv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
+                if (prec) {
+                    if (grp == 0) kinv[32 * c + 8 * (li >> 2) + (li & 3) + 4 * t] = inv;
+                } else {
+                    float kf[8];
+                    unpack_bf16x8(kraw[k], kf);
+                    const float sc = inv * (kLog2e * inv_tau);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) kf[e] *= sc;
+                    kfrag = pack_bf16x8(kf);
+                }
+            }
+            kst[f * 64 + lane] = kfrag;
+        }
+        vm_wait_all();
+        __syncthreads();                         // K^, V and the slices complete
+        if (!active || tj < tlo || tj >= thi) continue;
+        const float* slice = bias2 + (QF == 1 ? 0 : wave * SLICE);
+#pragma unroll
+        for (int p = 0; p < TPW / 2; ++p) {
+#pragma unroll 1
+            for (int c = 0; c < NCH; ++c)
+                chunk<SIM, POS, M>(kst, vst, slice, kinv, T + 2 * p, c, lane, mask, fold, prec);
+        }
+    }
+
+    // ---- normalise and store: lane holds channels 4 grp..+3 and 16 + 4 grp..+3 of query li
+    if (!active) return;
+    const Rsrc orr = make_rsrc((const uint16_t*)a.out + frame_base(tiq), bytes);
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+        const int tq = QF == 1 ? wave + WAVES * k : k;
+        const int t = 16 * tq + li, ri = t / M, ci = t % M;
+        const float inv = __builtin_amdgcn_rcpf(T[k].ls[0]);
+        const uint32_t off = wg.tok(ri, ci) + 8u * grp;
+        store8(orr, off, pack_bf16x4(T[k].o0[0] * inv, T[k].o0[1] * inv, T[k].o0[2] * inv, T[k].o0[3] * inv));
+        store8(orr, off + 32u, pack_bf16x4(T[k].o1[0] * inv, T[k].o1[1] * inv, T[k].o1[2] * inv, T[k].o1[3] * inv));
+    }
+}
+
+template <int SIM, int POS>
+hipError_t launch_m(const VideoArgs& a, int units, int per_xcd, hipStream_t s)
+{
+    const unsigned grid = 8u * (unsigned)per_xcd;
+    if (a.M == 16) attn_video_mfma_kernel<SIM, POS, 16><<<grid, 256, 0, s>>>(a, units, per_xcd);
+    else attn_video_mfma_kernel<SIM, POS, 8><<<grid, 256, 0, s>>>(a, units, per_xcd);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool video_mfma_supported(const VideoArgs& a)
+{
+    return a.dtype == SWIN_DT_BF16 && (a.M == 8 || a.M == 16) && a.C / a.heads == D &&
+           (a.pos == SWIN_POS_NONE || a.pos == SWIN_POS_TABLE) &&
+           (int64_t)a.H * a.W * a.C * 2 < ((int64_t)1 << 31) && (int64_t)a.W * a.C * 2 < ((int64_t)1 << 24);
+}
+
+hipError_t launch_attn_video_mfma(const VideoArgs& a, hipStream_t stream)
+{
+    if (a.nwin == 0) return hipSuccess;
+    const int qf = a.M == 8 ? 4 : 1;
+    const int64_t units = (int64_t)a.nwin * a.heads * ((a.Mt + qf - 1) / qf);
+    if (units > INT32_MAX - 8) return hipErrorInvalidValue;
+    const int per_xcd = (int)((units + 7) / 8);
+    if (a.sim == SWIN_SIM_COSINE)
+        return a.pos == SWIN_POS_TABLE ? launch_m<SWIN_SIM_COSINE, SWIN_POS_TABLE>(a, (int)units, per_xcd, stream)
+                                       : launch_m<SWIN_SIM_COSINE, SWIN_POS_NONE>(a, (int)units, per_xcd, stream);
+    return a.pos == SWIN_POS_TABLE ? launch_m<SWIN_SIM_DOT, SWIN_POS_TABLE>(a, (int)units, per_xcd, stream)
+                                   : launch_m<SWIN_SIM_DOT, SWIN_POS_NONE>(a, (int)units, per_xcd, stream);
+}
+
+}  // namespace swin

@@ -29,6 +29,10 @@ struct VideoArgs {
 // LDS bytes the kernel needs with kc keys staged at a time (0 if no kc fits).
 size_t video_lds(const VideoArgs& a, int* kc);
 hipError_t launch_attn_video(const VideoArgs& a, hipStream_t stream);
+
+// The same on the matrix cores: bf16, M = 8 or 16, no rotary positions.
+bool video_mfma_supported(const VideoArgs& a);
+hipError_t launch_attn_video_mfma(const VideoArgs& a, hipStream_t stream);
 hipError_t launch_cpb_table3d(int Mt, int M, int heads, int hidden, const float* w1, const float* b1,
                               const float* w2, const float* b2, float* table, hipStream_t stream);
 

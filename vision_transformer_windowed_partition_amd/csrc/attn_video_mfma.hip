@@ -22,6 +22,12 @@
 // frame in another temporal shift region than a wavefront's query frame is
 // skipped by that wavefront; within a frame, spatial shift regions mask
 // 8-key groups (and single keys where a region edge splits a group).
+// Normaliser: each frame's logits are bounded above from the slice's largest
+// entry and |cos| <= 1 (COSINE) or Cauchy-Schwarz with the frame's largest
+// ||k|| (DOT); when that bound lies within 60 (base 2) of the lowest
+// possible logit, the frame is exponentiated against it (the accumulators
+// rescaled once if it raises the reference), else against a running maximum
+// per 32-key chunk, which has no range condition.
 #include "common.hpp"
 #include "lanes.hpp"
 #include "launch_video.hpp"
@@ -37,6 +43,7 @@ using namespace lanes;
 constexpr int WAVES = 4;
 constexpr int TPW = 4;                 // query tiles a wavefront keeps live
 constexpr float PRECISE_TAU = 0.1f;    // COSINE below this: raw k and 1/||k|| in fp32
+constexpr float RANGE_LIMIT = 60.0f;   // widest logit spread (base 2) a fixed reference may take
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -60,17 +67,19 @@ __device__ __forceinline__ int axis_pos(int L, int M, int s, int part, int w, in
 struct VTile {
     bf16x8 qf;                 // q (unit for COSINE outside the precise path) as the B operand
     f32x4 o0, o1, ls;          // O^T channels 0-15 and 16-31, row sums
-    float mrun;                // running maximum, log2 units
+    float mrun;                // reference of the accumulators (running maximum or bound), log2 units
     float qscale;              // per-score scale when not folded into K^
+    float qnorm;               // ||q||
     int qoff;                  // this lane's bias offset in a slice, chunk 0
     uint32_t colbits;          // allowed key columns of this lane's 8-key group
     int rlo, rhi;              // allowed key rows (spatial shift regions)
 };
 
-// One 32-key chunk c of the staged key frame for two tiles.
+// One 32-key chunk c of the staged key frame for two tiles; exact
+// (wave-uniform): the running maximum, else the tiles' fixed references.
 template <int SIM, int POS, int M>
 __device__ __forceinline__ void chunk(const bf16x8* kst, const __bf16* vst, const float* bias2, const float* kinv,
-                                      VTile* T, int c, int lane, bool mask, bool fold, bool prec)
+                                      VTile* T, int c, int lane, bool mask, bool fold, bool prec, bool exact)
 {
     constexpr int GPR = M / 8, S = 2 * M - 1;
     const int grp = lane >> 4, li = lane & 15;
@@ -115,12 +124,15 @@ __device__ __forceinline__ void chunk(const bf16x8* kst, const __bf16* vst, cons
             if (mask) x[e] = (bits[i] >> e) & 1u ? x[e] : -INFINITY;
             cm = fmaxf(cm, x[e]);
         }
-        cm = max_x32(max_x16(cm));
-        const float mnew = fmaxf(T[i].mrun, cm);
-        const float mref = mnew == -INFINITY ? 0.0f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(T[i].mrun - mref);
-        T[i].o0 *= alpha; T[i].o1 *= alpha; T[i].ls *= alpha;
-        T[i].mrun = mnew;
+        float mref = T[i].mrun;
+        if (exact) {
+            cm = max_x32(max_x16(cm));
+            const float mnew = fmaxf(T[i].mrun, cm);
+            mref = mnew == -INFINITY ? 0.0f : mnew;
+            const float alpha = __builtin_amdgcn_exp2f(T[i].mrun - mref);
+            T[i].o0 *= alpha; T[i].o1 *= alpha; T[i].ls *= alpha;
+            T[i].mrun = mnew;
+        }
         float pr[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(x[e] - mref);
@@ -147,6 +159,7 @@ __global__ void __launch_bounds__(256) attn_video_mfma_kernel(VideoArgs a, int u
     __shared__ __attribute__((aligned(16))) __bf16 vst[NS * D];
     __shared__ __attribute__((aligned(16))) float kinv[NS];
     __shared__ __attribute__((aligned(16))) float bias2[POS == SWIN_POS_TABLE ? QF * SLICE : 1];
+    __shared__ float red[WAVES * (2 * QF + 1)];  // per wave: slice extrema per query frame, largest ||k||^2
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -215,6 +228,7 @@ __global__ void __launch_bounds__(256) attn_video_mfma_kernel(VideoArgs a, int u
                 T[k].qf = pack_bf16x8(qf);
             }
             T[k].qscale = SIM == SWIN_SIM_COSINE ? kLog2e * inv_tau * qinv : kLog2e * 0.17677669529663687f;
+            T[k].qnorm = sqrtf(ss);
             T[k].o0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             T[k].o1 = T[k].o0;
             T[k].ls = T[k].o0;
@@ -237,6 +251,7 @@ __global__ void __launch_bounds__(256) attn_video_mfma_kernel(VideoArgs a, int u
         const Rsrc kr = make_rsrc((const uint16_t*)a.k + kb0, bytes);
         const RawRsrc vraw = raw_rsrc((const uint16_t*)a.v + kb0, bytes);
         u32x4 kraw[SETS];
+        float kmax2 = 0.0f;
 #pragma unroll
         for (int k = 0; k < SETS; ++k) {
             const int f = wave + WAVES * k, c = f >> 1, t = f & 1;
@@ -253,12 +268,22 @@ __global__ void __launch_bounds__(256) attn_video_mfma_kernel(VideoArgs a, int u
             dma16(vraw, vst + (size_t)j * 512, wg.tok(rj, cj) + 16u * piece);
         }
         if (POS == SWIN_POS_TABLE) {
-            // slices of the offsets ti - tj, reversed (row r at S*S - 1 - r), log2 units
-            for (int i = tid; i < QF * S * S; i += WAVES * 64) {
-                const int q = i / (S * S), r = i - q * (S * S);
+            // slices of the offsets ti - tj, reversed (row r at S*S - 1 - r),
+            // log2 units, and their extrema
+#pragma unroll
+            for (int q = 0; q < QF; ++q) {
                 const int tq = QF == 1 ? fb : min(fb * QF + q, Mt - 1);
-                const int row = (tq - tj + Mt - 1) * (S * S) + r;
-                bias2[q * SLICE + S * S - 1 - r] = a.table[(size_t)row * a.heads + h] * kLog2e;
+                const float* trow = a.table + (size_t)(tq - tj + Mt - 1) * (S * S) * a.heads + h;
+                float mx = -INFINITY, mn = INFINITY;
+                for (int r = tid; r < S * S; r += WAVES * 64) {
+                    const float val = trow[(size_t)r * a.heads] * kLog2e;
+                    bias2[q * SLICE + S * S - 1 - r] = val;
+                    mx = fmaxf(mx, val);
+                    mn = fminf(mn, val);
+                }
+                mx = wave_reduce<Op::Max>(mx);
+                mn = wave_reduce<Op::Min>(mn);
+                if (lane == 0) { red[wave * (2 * QF + 1) + 2 * q] = mx; red[wave * (2 * QF + 1) + 2 * q + 1] = mn; }
             }
         }
 #pragma unroll
@@ -280,16 +305,52 @@ __global__ void __launch_bounds__(256) attn_video_mfma_kernel(VideoArgs a, int u
                 }
             }
             kst[f * 64 + lane] = kfrag;
+            kmax2 = fmaxf(kmax2, ss);
+        }
+        if (SIM == SWIN_SIM_DOT) {
+            kmax2 = wave_reduce<Op::Max>(kmax2);
+            if (lane == 0) red[wave * (2 * QF + 1) + 2 * QF] = kmax2;
         }
         vm_wait_all();
-        __syncthreads();                         // K^, V and the slices complete
+        __syncthreads();                         // K^, V, the slices and their extrema complete
         if (!active || tj < tlo || tj >= thi) continue;
         const float* slice = bias2 + (QF == 1 ? 0 : wave * SLICE);
+        // this frame's bound on every logit of a query (log2 units) and the spread below it
+        const int qs = QF == 1 ? 0 : wave;
+        float bmx = 0.0f, bmn = 0.0f, kmax = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            if (POS == SWIN_POS_TABLE) {
+                const float x = red[w * (2 * QF + 1) + 2 * qs], y = red[w * (2 * QF + 1) + 2 * qs + 1];
+                bmx = w == 0 ? x : fmaxf(bmx, x);
+                bmn = w == 0 ? y : fminf(bmn, y);
+            }
+            if (SIM == SWIN_SIM_DOT) kmax = fmaxf(kmax, red[w * (2 * QF + 1) + 2 * QF]);
+        }
+        kmax = sqrtf(kmax);
+        bool wide = false;
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+            const float c = SIM == SWIN_SIM_COSINE ? kLog2e * inv_tau : T[k].qnorm * kmax * T[k].qscale;
+            wide = wide || !(2.0f * c + (bmx - bmn) <= RANGE_LIMIT);
+        }
+        const bool exact = __any(wide);
+        if (!exact) {
+#pragma unroll
+            for (int k = 0; k < TPW; ++k) {
+                // raise the reference to the frame's bound (rescale once)
+                const float c = SIM == SWIN_SIM_COSINE ? kLog2e * inv_tau : T[k].qnorm * kmax * T[k].qscale;
+                const float ref = fmaxf(T[k].mrun, c + bmx);
+                const float alpha = __builtin_amdgcn_exp2f(T[k].mrun - ref);
+                T[k].o0 *= alpha; T[k].o1 *= alpha; T[k].ls *= alpha;
+                T[k].mrun = ref;
+            }
+        }
 #pragma unroll
         for (int p = 0; p < TPW / 2; ++p) {
 #pragma unroll 1
             for (int c = 0; c < NCH; ++c)
-                chunk<SIM, POS, M>(kst, vst, slice, kinv, T + 2 * p, c, lane, mask, fold, prec);
+                chunk<SIM, POS, M>(kst, vst, slice, kinv, T + 2 * p, c, lane, mask, fold, prec, exact);
         }
     }
 

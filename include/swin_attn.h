@@ -226,7 +226,7 @@ int swin_window_attn_bwd_lse(const swin_attn_desc* desc, const void* q, const vo
  *   G(x) = W2 relu(W1 x + b1) + b2,  x = sign(d) log(1 + |d|) of (dx, dy, dt),
  * w1: hidden x 3 (columns dx, dy, dt), b1: hidden or NULL, w2: heads x hidden,
  * b2: heads or NULL; device fp32, the table must not overlap them.  Each
- * value is a fp32 sum over hidden.  1 <= Mt, M <= 64, 1 <= heads <= 64,
+ * value is a fp32 sum over hidden (64 partial sums, then across them).  1 <= Mt, M <= 64, 1 <= heads <= 64,
  * 1 <= hidden <= 4096 (SWIN_EINVAL otherwise). */
 int swin_cpb_table3d(int32_t Mt, int32_t M, int32_t heads, int32_t hidden, const float* w1,
                      const float* b1, const float* w2, const float* b2, float* table, void* stream);
@@ -249,8 +249,8 @@ int swin_cpb_table3d(int32_t Mt, int32_t M, int32_t heads, int32_t hidden, const
  * k scaled by 1/tau rounded to bf16 unless tau < 0.1, the weights rounded to
  * bf16 before P V, softmax in fp32 with a running maximum); everything else
  * on the vector ALUs (similarities and logits in fp64, exponentials and sums
- * in fp32), where the head's table must fit LDS next to a 64-key chunk
- * (SWIN_EUNSUPPORTED otherwise).  The output is rounded once. */
+ * in fp32), where the head's whole table must fit LDS next to a 64-key
+ * chunk (SWIN_EUNSUPPORTED otherwise).  The output is rounded once. */
 int swin_window_attn3d_fwd(const swin_attn_desc* desc, int32_t T, int32_t Mt, int32_t shift_t,
                            const void* q, const void* k, const void* v, void* out, const float* tau,
                            const float* table, void* stream);

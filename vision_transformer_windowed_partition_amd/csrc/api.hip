@@ -333,7 +333,8 @@ int swin_window_attn3d_fwd(const swin_attn_desc* d, int32_t T, int32_t Mt, int32
     const int64_t nwin = (int64_t)d->B * a.nwt * a.nwr * a.nwc;
     if (nwin > INT32_MAX) return fail(SWIN_EUNSUPPORTED, "too many windows");
     a.nwin = (int)nwin;
-    if (swin::video_lds(a, nullptr) == 0)
+    const bool mfma = swin::video_mfma_supported(a);
+    if (!mfma && swin::video_lds(a, nullptr) == 0)
         return fail(SWIN_EUNSUPPORTED, "Mt=%d, M=%d: the bias table does not fit LDS", Mt, d->M);
     if (bytes == 0) return SWIN_OK;
     if (!q || !k || !v || !out) return fail(SWIN_EINVAL, "NULL q, k, v or out");
@@ -342,8 +343,8 @@ int swin_window_attn3d_fwd(const swin_attn_desc* d, int32_t T, int32_t Mt, int32
     if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
         return fail(SWIN_EINVAL, "out overlaps q, k or v");
     a.q = q; a.k = k; a.v = v; a.out = out; a.tau = tau; a.table = table;
-    const hipError_t e = swin::video_mfma_supported(a) ? swin::launch_attn_video_mfma(a, (hipStream_t)stream)
-                                                       : swin::launch_attn_video(a, (hipStream_t)stream);
+    const hipError_t e = mfma ? swin::launch_attn_video_mfma(a, (hipStream_t)stream)
+                              : swin::launch_attn_video(a, (hipStream_t)stream);
     return hip_status(e, "swin_window_attn3d_fwd launch");
 }
 

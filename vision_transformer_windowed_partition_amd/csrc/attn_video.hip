@@ -18,6 +18,7 @@
 // cosine logit reaches 100 at tau's floor), exponentials and the value sums
 // fp32.  The N x N scores are never stored.
 #include "common.hpp"
+#include "lanes.hpp"
 #include "launch_video.hpp"
 #include "rows.hpp"
 
@@ -181,26 +182,38 @@ hipError_t launch_sim(const VideoArgs& a, dim3 grid, int threads, int kc, size_t
 
 int video_threads(const VideoArgs& a) { return a.N >= 512 ? 512 : (a.N + 63) / 64 * 64; }
 
-// G over the log-spaced offsets (dx, dy, dt) of table row i, head h: one
-// thread per (row, head), fp32.
+// G over the log-spaced offsets (dx, dy, dt) of one table row for a group of
+// up to four heads: one wavefront, lane j evaluating hidden units j, j + 64,
+// ... and accumulating their share of the group's output sums, which a
+// cross-lane sum finishes; fp32.
+constexpr int CPB_HG = 4;
+
 __global__ void __launch_bounds__(256) cpb3d_kernel(int Mt, int M, int heads, int hidden, const float* w1,
                                                     const float* b1, const float* w2, const float* b2,
-                                                    float* table, int rows)
+                                                    float* table, int items)
 {
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= rows * heads) return;
-    const int row = idx / heads, h = idx - row * heads;
+    const int lane = threadIdx.x & 63;
+    const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+    if (item >= items) return;
+    const int groups = (heads + CPB_HG - 1) / CPB_HG;
+    const int row = item / groups, h0 = (item - row * groups) * CPB_HG;
     const int S = 2 * M - 1;
     const int dx = row % S - (M - 1), dy = (row / S) % S - (M - 1), dt = row / (S * S) - (Mt - 1);
     const auto lg = [](int x) { return copysignf(log1pf(fabsf((float)x)), (float)x); };
     const float in0 = lg(dx), in1 = lg(dy), in2 = lg(dt);
-    float acc = b2 ? b2[h] : 0.0f;
-    for (int j = 0; j < hidden; ++j) {
-        float z = fmaf(w1[3 * j], in0, fmaf(w1[3 * j + 1], in1, fmaf(w1[3 * j + 2], in2, b1 ? b1[j] : 0.0f)));
-        z = fmaxf(z, 0.0f);
-        acc = fmaf(w2[(size_t)h * hidden + j], z, acc);
+    float acc[CPB_HG] = {};
+    for (int j = lane; j < hidden; j += 64) {
+        const float z = fmaxf(fmaf(w1[3 * j], in0, fmaf(w1[3 * j + 1], in1, fmaf(w1[3 * j + 2], in2,
+                                                                                 b1 ? b1[j] : 0.0f))), 0.0f);
+#pragma unroll
+        for (int o = 0; o < CPB_HG; ++o)
+            if (h0 + o < heads) acc[o] = fmaf(w2[(size_t)(h0 + o) * hidden + j], z, acc[o]);
     }
-    table[(size_t)row * heads + h] = acc;
+#pragma unroll
+    for (int o = 0; o < CPB_HG; ++o) {
+        const float g = lanes::wave_reduce<lanes::Op::Sum>(acc[o]);
+        if (lane == 0 && h0 + o < heads) table[(size_t)row * heads + h0 + o] = g + (b2 ? b2[h0 + o] : 0.0f);
+    }
 }
 
 }  // namespace
@@ -236,10 +249,10 @@ hipError_t launch_cpb_table3d(int Mt, int M, int heads, int hidden, const float*
                               const float* w2, const float* b2, float* table, hipStream_t stream)
 {
     const int S = 2 * M - 1;
-    const int rows = (2 * Mt - 1) * S * S;
-    const int64_t n = (int64_t)rows * heads;
-    if (n == 0) return hipSuccess;
-    cpb3d_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(Mt, M, heads, hidden, w1, b1, w2, b2, table, rows);
+    const int64_t items = (int64_t)(2 * Mt - 1) * S * S * ((heads + CPB_HG - 1) / CPB_HG);
+    if (items == 0) return hipSuccess;
+    cpb3d_kernel<<<(unsigned)((items + 3) / 4), 256, 0, stream>>>(Mt, M, heads, hidden, w1, b1, w2, b2, table,
+                                                                  (int)items);
     return hipGetLastError();
 }
 

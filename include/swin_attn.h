@@ -1,13 +1,15 @@
 /*
  * swin_attn.h -- C ABI of libswinattn.so: shifted-window / interleaved-window
- * multi-head self-attention on one AMD Instinct MI355X (gfx950): forward,
- * backward, the CPB table, and the steps around it in a block (projections,
+ * multi-head self-attention on one AMD Instinct MI355X (gfx950): forward
+ * (optionally exporting the softmax statistics), backward, the CPB table,
+ * video (3D) windows, and the steps around it in a block (projections,
  * residual post-norm, Iwin's convolution, LinMapper's window mapping).
  *
  * Pages defining the operations (cited by title and section):
  *   [SwinV2] "Swin Transformer V2: Scaling Up Capacity and Resolution",
  *            paper card: Method items 1-3, eq. 1-4, the window-attention,
- *            continuous-bias and block pseudocode, Architecture table.
+ *            continuous-bias and block pseudocode, Architecture table,
+ *            appendix A2 (video fine-tuning).
  *   [Flash]  "FLASHSWIN: Unlocking Large Windows and Dense Tokens in Swin
  *            Vision Transformers with Memory Efficient Attention", abstract.
  *   [What]   "What Makes for Hierarchical Vision Transformer?", abstract.
@@ -20,8 +22,8 @@
  *     beyond its loaded code.  `desc` is a HOST pointer, read during the call.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on it and returns; results are ready when the stream is.
- *   - Token grids are (B, H, W, C) row-major, channels last; head h owns
- *     channels [h*d, (h+1)*d), d = C / heads.
+ *   - Token grids are (B, H, W, C) row-major, channels last (video grids
+ *     (B, T, H, W, C)); head h owns channels [h*d, (h+1)*d), d = C / heads.
  *   - Window order: window (b, wr, wc) has id b*nW + wr*(W/M) + wc,
  *     nW = (H/M)*(W/M); inside a window, token (r, c) is number r*M + c.
  *   - Errors: arguments are validated on the host before anything is

@@ -84,7 +84,7 @@ def _declare(lib):
     lib.oracle_cpb_table3d.restype = i32
     lib.oracle_cpb_table3d.argtypes = [i32] * 4 + [vp] * 5
     lib.oracle_window_attn3d.restype = i32
-    lib.oracle_window_attn3d.argtypes = [i32] * 13 + [dbl] + [vp] * 6
+    lib.oracle_window_attn3d.argtypes = [i32] * 13 + [dbl] + [vp] * 5 + [vp, i64, vp]
     lib.oracle_set_threads.restype = None
     lib.oracle_set_threads.argtypes = [i32]
     lib.oracle_max_threads.restype = i32
@@ -378,17 +378,21 @@ def cpb_table3d(Mt: int, M: int, w1, b1, w2, b2, lib=None) -> np.ndarray:
 
 def window_attn3d(q, k, v, *, heads: int, Mt: int, M: int, shift_t: int = 0, shift: int = 0,
                   partition: str = "cyclic", sim: str = "cosine", pos: str = "none", tau=None, table=None,
-                  tau_min: float = 0.01, lib=None) -> np.ndarray:
+                  tau_min: float = 0.01, windows=None, lib=None) -> np.ndarray:
     """Video-window attention forward in fp64 over (B, T, H, W, C) grids,
-    windows Mt x M x M (temporal shift ``shift_t``, spatial ``shift``)."""
+    windows Mt x M x M (temporal shift ``shift_t``, spatial ``shift``).
+    ``windows``: optional global window ids to compute (the rest of the
+    output stays zero)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, T, H, W, C = q.shape
     assert k.shape == q.shape and v.shape == q.shape
     tau, table = _f64(tau), _f64(table)
     out = np.zeros((B, T, H, W, C), dtype=np.float64)
+    win = None if windows is None else np.ascontiguousarray(windows, dtype=np.int64)
     rc = (lib or load()).oracle_window_attn3d(B, T, H, W, C, heads, Mt, M, shift_t, shift, PART[partition],
                                               SIM[sim], POS[pos], float(tau_min), _ptr(q), _ptr(k), _ptr(v),
-                                              _ptr(tau), _ptr(table), _ptr(out))
+                                              _ptr(tau), _ptr(table), _ptr(win), 0 if win is None else len(win),
+                                              _ptr(out))
     if rc:
         raise ValueError(f"oracle_window_attn3d: bad argument (rc={rc})")
     return out

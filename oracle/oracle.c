@@ -905,11 +905,14 @@ int oracle_cpb_table3d(int Mt, int M, int heads, int hidden, const double* w1, c
 
 /* Windowed attention over (B, T, H, W, C) video grids, windows Mt x M x M
  * (reading above); logit, bias, exclusion and softmax as in
- * oracle_window_attn.  pos: NONE or TABLE (no rotary form in 3D). */
+ * oracle_window_attn.  pos: NONE or TABLE (no rotary form in 3D).  windows:
+ * optional list of global window ids to compute (NULL: all); only their
+ * tokens of `out` are written. */
 int oracle_window_attn3d(int B, int T, int H, int W, int C, int heads, int Mt, int M,
                          int shift_t, int shift, int part, int sim, int pos, double tau_min,
                          const double* q, const double* k, const double* v,
-                         const double* tau, const double* table, double* out)
+                         const double* tau, const double* table, const int64_t* windows, int64_t n_windows,
+                         double* out)
 {
     if (bad_shape(B, H, W, C, M, shift, part)) return 1;
     if (T < 1 || Mt < 1 || T % Mt || shift_t < 0 || shift_t >= Mt) return 1;
@@ -922,7 +925,10 @@ int oracle_window_attn3d(int B, int T, int H, int W, int C, int heads, int Mt, i
     if (!q || !k || !v || !out) return 1;
     const int d = C / heads;
     const int nwt = T / Mt, nwr = H / M, nwc = W / M, N = Mt * M * M, S = 2 * M - 1;
-    const int64_t nW = (int64_t)nwt * nwr * nwc, total = (int64_t)B * nW;
+    const int64_t nW = (int64_t)nwt * nwr * nwc, total = windows ? n_windows : (int64_t)B * nW;
+    if (windows)
+        for (int64_t i = 0; i < n_windows; ++i)
+            if (windows[i] < 0 || windows[i] >= (int64_t)B * nW) return 1;
     const double dot_scale = 1.0 / sqrt((double)d);
     int failed = 0;
 
@@ -940,7 +946,7 @@ int oracle_window_attn3d(int B, int T, int H, int W, int C, int heads, int Mt, i
         } else {
             #pragma omp for schedule(dynamic, 1)
             for (int64_t u = 0; u < total * heads; ++u) {
-                const int64_t wi = u / heads;
+                const int64_t wi = windows ? windows[u / heads] : u / heads;
                 const int h = (int)(u % heads);
                 const int b = (int)(wi / nW);
                 const int wt = (int)((wi % nW) / ((int64_t)nwr * nwc));

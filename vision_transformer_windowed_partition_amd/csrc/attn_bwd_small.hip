@@ -16,13 +16,17 @@
 // in fp32, so nothing is rounded before the products but the weights.
 //
 // A workgroup of four wavefronts serves one head: for 9 <= M <= 16 one
-// window shared by the four, for M <= 8 one window each.  LDS holds the
-// window's K, V, Q and dout as 64-byte rows in key-slot order (8 slots per
-// row segment, XOR-swizzled 16-byte pieces, filled by LDS-DMA), the per-slot
-// scales, log-sum-exp and D, the head's bias table (reversed, log2 units) and
-// the workgroup's bias-gradient accumulator.  Three passes:
+// window shared by the four, for M <= 8 one window each.  LDS holds two of
+// the window's tensors as 64-byte rows in key-slot order (8 slots per row
+// segment, XOR-swizzled 16-byte pieces, filled by LDS-DMA): K and V for
+// passes 0 and B, then Q and dout, staged into the same space, for pass A;
+// a pass takes the fragments of its own tiles of the other two straight from
+// memory.  Beside them: the per-slot scales, log-sum-exp and D, the head's
+// bias table (reversed, log2 units) and the workgroup's bias-gradient
+// accumulator.  Three passes:
 //   0  query-major (like the forward): S^T = K Q^T per 32-key chunk, running
-//      maximum and sum -> log-sum-exp of each query;
+//      maximum and sum -> log-sum-exp of each query (skipped when the
+//      forward's is given);
 //   B  query-major: S^T and dP^T = V dout^T, dl, then
 //      G^T += K^T (dl c)^T with K^T read transposed from the K rows
 //      (ds_read_b64_tr_b16); dq, dtau and the bias gradient;
@@ -124,11 +128,16 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
     float* qsc = ksc + NS;                                     // [NS] log2(e) a_i
     float* lse = qsc + NS;                                     // [NS] log2-sum-exp of the logits
     float* dd = lse + NS;                                      // [NS] D_i
-    __bf16* rows = (__bf16*)(red + 16 + WH * 4 * NS) + wh * (4 * NS * D);
+    // PHASED (one window shared by four wavefronts): two row buffers, K and V
+    // for passes 0 and B, then Q and dout for pass A; else all four at once
+    // (LDS is not what limits those workgroups)
+    constexpr bool PHASED = QW > 1;
+    constexpr int NROWS = PHASED ? 2 : 4;
+    __bf16* rows = (__bf16*)(red + 16 + WH * 4 * NS) + wh * (NROWS * NS * D);
     __bf16* krow = rows;
     __bf16* vrow = rows + NS * D;
-    __bf16* qrow = rows + 2 * NS * D;
-    __bf16* orow = rows + 3 * NS * D;
+    __bf16* qrow = rows + (PHASED ? 0 : 2 * NS * D);
+    __bf16* orow = rows + (PHASED ? NS * D : 3 * NS * D);
 
     const int work = (blockIdx.x & 7) * L.P + (blockIdx.x >> 3);
     if (work >= L.wgs) return;
@@ -145,10 +154,10 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
     // ---- staging: the four tensors' rows by LDS-DMA; piece j of a tensor
     // is slots 16 j .. 16 j + 15, lane l filling LDS piece l%4 of slot
     // 16 j + l/4 with channel piece (l%4) ^ v_swizzle(slot)
-    {
-        const void* src[4] = {p.k, p.v, p.q, a.dout};
+    auto stage_rows = [&](const void* t0, const void* t1, __bf16* dst) {
+        const void* src[2] = {t0, t1};
 #pragma unroll
-        for (int tsr = 0; tsr < 4; ++tsr) {
+        for (int tsr = 0; tsr < 2; ++tsr) {
             const RawRsrc rr = raw_rsrc((const uint16_t*)src[tsr] + wp.base + h * D, bytes);
 #pragma unroll
             for (int k = 0; k < SETS; ++k) {
@@ -157,11 +166,41 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                 int r, c;
                 slot_rc<GPR>(s, r, c);
                 const int piece = (lane & 3) ^ v_swizzle(s);
-                dma16(rr, rows + (size_t)tsr * NS * D + (size_t)j * 512,
+                dma16(rr, dst + (size_t)tsr * NS * D + (size_t)j * 512,
                       masked(wg.tok(r, c) + 16u * piece, r < M && c < M));
             }
         }
-    }
+    };
+    stage_rows(p.k, p.v, krow);
+    if (!PHASED) stage_rows(p.q, a.dout, qrow);
+    // a row's 8-channel piece straight from memory (zeros for padded slots):
+    // the fragments of the tensors not in LDS during a pass
+    const Rsrc qg = make_rsrc((const uint16_t*)p.q + wp.base + h * D, bytes);
+    const Rsrc dg = make_rsrc((const uint16_t*)a.dout + wp.base + h * D, bytes);
+    const Rsrc kg = make_rsrc((const uint16_t*)p.k + wp.base + h * D, bytes);
+    const Rsrc vg = make_rsrc((const uint16_t*)p.v + wp.base + h * D, bytes);
+    auto gfrag = [&](const Rsrc& r, int s, int piece) -> bf16x8 {
+        int rr, cc;
+        slot_rc<GPR>(s, rr, cc);
+        return __builtin_bit_cast(bf16x8, load16(r, masked(wg.tok(rr, cc) + 16u * piece, rr < M && cc < M)));
+    };
+    // channels 4 grp..+3 and 16 + 4 grp..+3 of slot s, as floats, from an
+    // LDS row (piece (4 grp / 8), half grp & 1) or from memory
+    auto lquad = [&](const __bf16* rw, int s, float* f) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int ch = 16 * hh + 4 * grp;
+            const __bf16* src = rw + s * D + (((ch >> 3) ^ v_swizzle(s)) * 8) + (ch & 7);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[4 * hh + e] = (float)src[e];
+        }
+    };
+    auto gquad = [&](const Rsrc& r, int s, float* f) {
+        const bf16x8 lo = gfrag(r, s, grp >> 1), hi = gfrag(r, s, 2 + (grp >> 1));
+        const int o = 4 * (grp & 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { f[e] = (float)lo[o + e]; f[4 + e] = (float)hi[o + e]; }
+    };
     //   per-slot scalars: four lanes per slot (a 16-byte piece each), slots
     //   rank*16 + 16 QW it ...; norms of k and q, and dout . out
     {
@@ -232,7 +271,7 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             const int tt = tv ? t : 0;
             const int ri = qdiv(tt, L.inv_M), ci = tt - ri * M;
             const int qs_slot = ri * 8 * GPR + ci;
-            const bf16x8 qf = rowfrag(qrow, qs_slot, grp);
+            const bf16x8 qf = PHASED ? gfrag(qg, qs_slot, grp) : rowfrag(qrow, qs_slot, grp);
             const float qs = qsc[qs_slot];
             const int qoff = (M - 1 - ri) * S + (M - 1 - ci) + kbase;
             int rlo = 0, rhi = M, clo = 0, chi = M;
@@ -276,15 +315,12 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
         }
     }
     __syncthreads();
-    if (!active) {
-        // nothing to compute; meet the final barrier
-    } else {
-        const float inv_tau = 1.0f / tau;
-        float dtau_acc = 0.0f;
-        const Rsrc dqr = make_rsrc((const uint16_t*)a.dq + wp.base + h * D, bytes);
-        const Rsrc dkr = make_rsrc((const uint16_t*)a.dk + wp.base + h * D, bytes);
-        const Rsrc dvr = make_rsrc((const uint16_t*)a.dv + wp.base + h * D, bytes);
-
+    const float inv_tau = 1.0f / tau;
+    float dtau_acc = 0.0f;
+    const Rsrc dqr = make_rsrc((const uint16_t*)a.dq + wp.base + h * D, bytes);
+    const Rsrc dkr = make_rsrc((const uint16_t*)a.dk + wp.base + h * D, bytes);
+    const Rsrc dvr = make_rsrc((const uint16_t*)a.dv + wp.base + h * D, bytes);
+    if (active) {
         // ---- pass B: dq of this wave's queries (query-major)
         const bool diag = M == 16;
         for (int t0 = rank; t0 < L.NQT; t0 += QW) {
@@ -293,8 +329,8 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             const int tt = tv ? t : 0;
             const int ri = qdiv(tt, L.inv_M), ci = tt - ri * M;
             const int qs_slot = ri * 8 * GPR + ci;
-            const bf16x8 qf = rowfrag(qrow, qs_slot, grp);
-            const bf16x8 gf = rowfrag(orow, qs_slot, grp);
+            const bf16x8 qf = PHASED ? gfrag(qg, qs_slot, grp) : rowfrag(qrow, qs_slot, grp);
+            const bf16x8 gf = PHASED ? gfrag(dg, qs_slot, grp) : rowfrag(orow, qs_slot, grp);
             const float qs = qsc[qs_slot], lq = lse[qs_slot], Dq = dd[qs_slot];
             const int qoff = (M - 1 - ri) * S + (M - 1 - ci) + kbase;
             int rlo = 0, rhi = M, clo = 0, chi = M;
@@ -367,15 +403,8 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             // lane holds channels 4 grp..+3 and 16 + 4 grp..+3 of query li
             float q8[8], g8[8];
             {
-                // the query's raw channels from its LDS row: piece (4 grp / 8) half (grp & 1)
-                const __bf16* qrw = qrow + qs_slot * D;
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int ch = 16 * hh + 4 * grp;
-                    const __bf16* src = qrw + (((ch >> 3) ^ v_swizzle(qs_slot)) * 8) + (ch & 7);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) q8[4 * hh + e] = (float)src[e];
-                }
+                if (PHASED) gquad(qg, qs_slot, q8);        // the query's raw channels
+                else lquad(qrow, qs_slot, q8);
                 g8[0] = G0[0]; g8[1] = G0[1]; g8[2] = G0[2]; g8[3] = G0[3];
                 g8[4] = G1[0]; g8[5] = G1[1]; g8[6] = G1[2]; g8[7] = G1[3];
             }
@@ -399,7 +428,15 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             store8(dqr, off, pack_bf16x4(dqv[0], dqv[1], dqv[2], dqv[3]));
             store8(dqr, off + 32u, pack_bf16x4(dqv[4], dqv[5], dqv[6], dqv[7]));
         }
-
+    }
+    if (PHASED) {
+        // ---- Q and dout rows replace K and V
+        __syncthreads();
+        stage_rows(p.q, a.dout, qrow);
+        vm_wait_all();
+        __syncthreads();
+    }
+    if (active) {
         // ---- pass A: dk, dv of this wave's 16-key tiles (key-major)
         const int nkt = (L.NSP + 15) / 16;
         for (int kt = rank; kt < nkt; kt += QW) {
@@ -407,7 +444,8 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             int rj, cj;
             slot_rc<GPR>(sk, rj, cj);
             const bool kv_ok = rj < M && cj < M;
-            const bf16x8 kB = rowfrag(krow, sk, grp), vB = rowfrag(vrow, sk, grp);
+            const bf16x8 kB = PHASED ? gfrag(kg, sk, grp) : rowfrag(krow, sk, grp);
+            const bf16x8 vB = PHASED ? gfrag(vg, sk, grp) : rowfrag(vrow, sk, grp);
             const float cj_s = ksc[sk];
             int rlo = 0, rhi = M, clo = 0, chi = M;
             if (wp.last_r) { if (rj < M - g.shift) rhi = M - g.shift; else rlo = M - g.shift; }
@@ -460,14 +498,8 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             // lane holds channels 4 grp..+3 and 16 + 4 grp..+3 of key slot sk
             float k8[8], h8[8], dkv[8];
             {
-                const __bf16* krw = krow + sk * D;
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int ch = 16 * hh + 4 * grp;
-                    const __bf16* src = krw + (((ch >> 3) ^ v_swizzle(sk)) * 8) + (ch & 7);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) k8[4 * hh + e] = (float)src[e];
-                }
+                if (PHASED) gquad(kg, sk, k8);             // the key's raw channels
+                else lquad(krow, sk, k8);
                 h8[0] = H0[0]; h8[1] = H0[1]; h8[2] = H0[2]; h8[3] = H0[3];
                 h8[4] = H1[0]; h8[5] = H1[1]; h8[6] = H1[2]; h8[7] = H1[3];
             }
@@ -555,7 +587,8 @@ hipError_t launch_attn_bwd_small(const AttnParams& p, const void* out, const voi
     L.P = (int)((wgs + 7) / 8);
     const int64_t grid = 8 * (int64_t)L.P;
     const int ns = nch * 32;
-    size_t lds = (size_t)(16 + wh * 4 * ns) * sizeof(float) + (size_t)wh * 4 * ns * D * 2;
+    const int nrows = wh == 1 ? 2 : 4;                              // phased when four waves share a window
+    size_t lds = (size_t)(16 + wh * 4 * ns) * sizeof(float) + (size_t)wh * nrows * ns * D * 2;
     if (p.pos == SWIN_POS_TABLE) lds += (size_t)2 * ((S * S + 8 + 3) / 4 * 4) * sizeof(float);
     if (p.sim == SWIN_SIM_COSINE) {
         if (p.pos == SWIN_POS_TABLE) return launch_nch<SWIN_SIM_COSINE, SWIN_POS_TABLE>(p, a, L, nch, (int)grid, lds, stream);

@@ -8,17 +8,17 @@
 // A workgroup of four wavefronts owns one (window, head, query frame) for
 // M = 16, or (window, head, four query frames) for M = 8, one frame a
 // wavefront; either way each wavefront keeps four query tiles of 16 queries
-// live for the whole window: their q fragments, their running maxima and
-// their fp32 accumulators for O^T and the row sums.  The workgroup then
+// live for the whole window: their q fragments, their normaliser references
+// and their fp32 accumulators for O^T and the row sums.  The workgroup then
 // walks the window's key frames: per key frame it stages that frame's M x M
 // keys (unit-normalised and scaled by log2(e)/tau for COSINE, raw otherwise)
 // as MFMA A-fragments and its values by LDS-DMA, together with the table
 // slice of the time offset between each query frame and the key frame (a
 // (2M-1)^2 slice, in log2 units), and every wavefront runs its tiles over
 // the frame's 32-key chunks: S^T = K^ Q^T (the slice entries, or the scale,
-// enter as the accumulator or one FMA), the online normaliser per chunk
-// (running maximum, accumulators rescaled when it grows), P^T rounded to
-// bf16 and O^T += V^T P^T, row sums by a third product against ones.  A key
+// enter as the accumulator or one FMA), the weights against the normaliser's
+// reference (below), P^T rounded to bf16 and O^T += V^T P^T, row sums by a
+// third product against ones.  A key
 // frame in another temporal shift region than a wavefront's query frame is
 // skipped by that wavefront; within a frame, spatial shift regions mask
 // 8-key groups (and single keys where a region edge splits a group).

@@ -166,3 +166,19 @@ def test_lse_empty_and_rejects():
     z = torch.zeros((0, 16, 16, 64), dtype=torch.bfloat16, device=DEV)
     out, lse = binding.swin_window_attn_fwd_lse(z, z, z, heads=2, M=8, shift=4, sim="dot", pos="none")
     assert out.numel() == 0 and lse.shape == (0, 2, 64)
+
+
+@pytest.mark.parametrize("M,pos", [(16, "table"), (24, "table"), (8, "none")])
+def test_lse_windows_layout_matches_grid(M, pos):
+    """The statistic of pre-partitioned windows (layout "windows") is the grid
+    layout's, bit for bit: same windows, same order, same arithmetic."""
+    wl = synth.small(B=2, H=2 * M, W=2 * M, C=64, heads=2, M=M, shift=M // 2, pos=pos, dtype="bf16", hidden=64)
+    g = gpu_inputs(synth.make_inputs(wl, seed=9))
+    table = gpu_table(wl, g) if pos == "table" else None
+    kw = dict(heads=wl.heads, M=M, shift=wl.shift, sim="cosine", pos=pos, tau=g["tau"], table=table)
+    _, lse_grid = binding.swin_window_attn_fwd_lse(g["q"], g["k"], g["v"], **kw)
+    part = {n: binding.swin_window_partition(g[n], M, wl.shift) for n in "qkv"}
+    _, lse_win = binding.swin_window_attn_fwd_lse(part["q"], part["k"], part["v"], layout="windows",
+                                                  grid=(wl.B, wl.H, wl.W), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(lse_grid, lse_win)

@@ -1,0 +1,79 @@
+"""Seeded random geometries through the C ABI against the fp64 oracle: the
+forward (every kernel the dispatcher can pick), the exported log-sum-exp and
+the backward, over window sizes, shifts, partitions, similarity and position
+modes and both dtypes the fixed cases do not reach.  Bars as in the fixed
+tests: forward fp32 max-abs 1e-5, bf16 max-abs 2e-2 and relative Frobenius
+1e-2; backward per test_gpu_backward (without the summed gradients, whose
+allowance needs the forward's error, checked there)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_helpers import compare, f64, gpu_inputs, gpu_table, run_gpu, run_oracle
+from vision_transformer_windowed_partition_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _case(seed):
+    rng = np.random.default_rng(seed)
+    M = int(rng.choice([2, 3, 4, 5, 6, 7, 8, 9, 11, 12, 13, 16, 17, 20, 24, 32, 40]))
+    nr, nc = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+    if M > 16:
+        nr, nc = min(nr, 2), min(nc, 2)
+    part = "interleaved" if rng.random() < 0.3 else "cyclic"
+    shift = 0 if part == "interleaved" or nr * nc == 1 else int(rng.integers(0, M))
+    sim = "cosine" if rng.random() < 0.6 else "dot"
+    pos = str(rng.choice(["none", "table", "rope2d"]))
+    dtype = "bf16" if rng.random() < 0.7 else "f32"
+    heads = int(rng.integers(1, 4))
+    B = int(rng.integers(1, 3))
+    return dict(B=B, H=nr * M, W=nc * M, C=32 * heads, heads=heads, M=M, shift=shift, partition=part, sim=sim,
+                pos=pos, dtype=dtype)
+
+
+SEEDS = list(range(40))
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_forward(seed):
+    kw = _case(seed)
+    wl = synth.small(**kw, hidden=64)
+    x = synth.make_inputs(wl, seed=1000 + seed)
+    g = gpu_inputs(x)
+    out = run_gpu(wl, g)
+    compare(wl, f64(out), run_oracle(wl, x), what=f"seed {seed}: {kw}")
+
+
+@pytest.mark.parametrize("seed", SEEDS[:20])
+def test_random_backward(seed):
+    kw = _case(seed)
+    if kw["M"] > 32:
+        pytest.skip("the backward is built for M <= 32")
+    wl = synth.small(**kw, hidden=64)
+    x = synth.make_inputs(wl, seed=2000 + seed)
+    g = gpu_inputs(x)
+    table = gpu_table(wl, g) if wl.pos == "table" else None
+    out, lse = (binding.swin_window_attn_fwd_lse(g["q"], g["k"], g["v"], heads=wl.heads, M=wl.M, shift=wl.shift,
+                                                 partition=wl.partition, sim=wl.sim, pos=wl.pos, tau=g["tau"],
+                                                 table=table, rope_base=wl.rope_base))
+    dout = synth.make_dout(wl, seed=3000 + seed)
+    got = binding.swin_window_attn_bwd(g["q"], g["k"], g["v"], out, dout.to(DEV), heads=wl.heads, M=wl.M,
+                                       shift=wl.shift, partition=wl.partition, sim=wl.sim, pos=wl.pos, tau=g["tau"],
+                                       table=table, rope_base=wl.rope_base, lse=lse)
+    torch.cuda.synchronize()
+    table64 = None if table is None else oracle.cpb_table(wl.M, f64(x["w1"]), f64(x["b1"]), f64(x["w2"]),
+                                                          f64(x["b2"]))
+    ref = oracle.window_attn_bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(dout), heads=wl.heads, M=wl.M,
+                                 shift=wl.shift, partition=wl.partition, sim=wl.sim, pos=wl.pos, tau=f64(x["tau"]),
+                                 table=table64, rope_base=wl.rope_base)
+    tmax, trel = (1e-4, 1e-4) if wl.dtype == "f32" else (2e-2, 1e-2)
+    for name in ("dq", "dk", "dv"):
+        a, r = f64(got[name]), ref[name]
+        scale = max(float(np.abs(r).max()), 1e-30)
+        err = float(np.abs(a - r).max()) / scale
+        rel = float(np.linalg.norm(a - r) / max(np.linalg.norm(r), 1e-30))
+        assert np.all(np.isfinite(a)), name
+        assert err <= tmax and rel <= trel, f"seed {seed} {kw} {name}: {err:.3e} {rel:.3e}"

@@ -142,3 +142,33 @@ def test_video_workload_sampled():
     got = f64(out)
     _compare(got[mask], ref[mask], wl.dtype, wl.name)
     assert mask.sum() == len(wins) * wl.N * wl.C
+
+
+def _random_case(seed):
+    rng = np.random.default_rng(seed)
+    M = int(rng.choice([2, 4, 5, 8, 8, 16, 16]))
+    Mt = int(rng.choice([1, 2, 3, 4]))
+    nt, nr, nc = int(rng.integers(1, 3)), int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    part = "interleaved" if rng.random() < 0.3 else "cyclic"
+    st = 0 if part == "interleaved" or nt == 1 else int(rng.integers(0, Mt))
+    s = 0 if part == "interleaved" or nr * nc == 1 else int(rng.integers(0, M))
+    sim = "cosine" if rng.random() < 0.6 else "dot"
+    pos = "table" if rng.random() < 0.6 else "none"
+    return (nt * Mt, nr * M, nc * M, Mt, M, st, s, part, sim, pos)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("seed", range(12))
+def test_video_random(seed, dtype):
+    """Seeded random video geometries (both kernels for bf16: M = 8, 16 on the
+    matrix cores, others on the vector ALUs)."""
+    case = _random_case(seed)
+    T, H, W, Mt, M, st, s, part, sim, pos = case
+    q, k, v, tau, table = _inputs(case, dtype, seed=500 + seed, B=2)
+    d = lambda t: None if t is None else t.to(DEV)
+    out = binding.swin_window_attn3d_fwd(d(q), d(k), d(v), heads=2, Mt=Mt, M=M, shift_t=st, shift=s, partition=part,
+                                         sim=sim, pos=pos, tau=d(tau), table=d(table))
+    torch.cuda.synchronize()
+    ref = oracle.window_attn3d(f64(q), f64(k), f64(v), heads=2, Mt=Mt, M=M, shift_t=st, shift=s, partition=part,
+                               sim=sim, pos=pos, tau=f64(tau), table=None if table is None else f64(table))
+    _compare(f64(out), ref, dtype, f"seed {seed}: {case}")

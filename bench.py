@@ -183,7 +183,7 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
               "(windows, heads and batch shard with no exchange; see the design notes)", file=sys.stderr)
         return 2
 

@@ -43,7 +43,8 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, TFLOP/s
 MALL_BYTES = 256 * 2 ** 20
 KERNEL_SOURCE = {"attn_small_kernel": "attn_small.hip", "attn_large_kernel": "attn_large.hip",
-                 "attn_mfma_kernel": "attn_mfma.hip", "attn_valu_kernel": "attn_valu.hip"}
+                 "attn_mfma_kernel": "attn_mfma.hip", "attn_valu_kernel": "attn_valu.hip",
+                 "attn_video_mfma_kernel": "attn_video_mfma.hip"}
 
 
 def kernel_sha(kernel: str) -> str:
@@ -250,19 +251,7 @@ def main(argv=None) -> int:
     kern_avg = sum(kern_ms) / len(kern_ms)
 
     if args.calib_copy:
-        a = torch.zeros(2 ** 28, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            torch.neg(a, out=b)
-        del a, b
-        # each token's 64 bytes sits 4 KiB from the next token of its window
-        g = torch.zeros((16, 512, 512, 32), dtype=torch.bfloat16, device=dev)
-        w = binding.swin_window_partition(g, 8, 0, "interleaved")
-        for _ in range(3):
-            binding.swin_window_partition(g, 8, 0, "interleaved", out=w)
-        for _ in range(3):
-            binding.swin_window_reverse(w, 16, 512, 512, 8, 0, "interleaved", out=g)
-        torch.cuda.synchronize()
+        run_calib_copies(dev)
 
     ms_per_step = wall * 1e3 / args.steps
     tokens_s = wl.tokens / (wall / args.steps)
@@ -606,6 +595,27 @@ def bench_linmapper(args, wl, sets, nsets, stream) -> int:
     return 0
 
 
+def run_calib_copies(dev) -> None:
+    """Copies of known size for HBM-counter calibration (see --calib-copy)."""
+    import torch
+
+    from vision_transformer_windowed_partition_amd import binding
+
+    a = torch.zeros(2 ** 28, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)
+    del a, b
+    # each token's 64 bytes sits 4 KiB from the next token of its window
+    g = torch.zeros((16, 512, 512, 32), dtype=torch.bfloat16, device=dev)
+    w = binding.swin_window_partition(g, 8, 0, "interleaved")
+    for _ in range(3):
+        binding.swin_window_partition(g, 8, 0, "interleaved", out=w)
+    for _ in range(3):
+        binding.swin_window_reverse(w, 16, 512, 512, 8, 0, "interleaved", out=g)
+    torch.cuda.synchronize()
+
+
 def bench_video(args) -> int:
     """Video (3D) window attention: swin_window_attn3d_fwd with the table from
     swin_cpb_table3d in each step.  Algorithmic work as for 2D windows: 4 N C
@@ -652,6 +662,8 @@ def bench_video(args) -> int:
     kern_ms = timer.elapsed_ms()
     timer.close()
     kern_avg = sum(kern_ms) / len(kern_ms)
+    if args.calib_copy:
+        run_calib_copies(dev)
     desc = binding.make_desc(B=wl.B, H=wl.H, W=wl.W, C=wl.C, heads=wl.heads, M=wl.M, shift=wl.shift,
                              partition=wl.partition, sim=wl.sim, pos=wl.pos, dtype=sets[0][0].dtype)
     kernel = binding.swin_window_attn3d_kernel(desc, wl.T, wl.Mt)
@@ -659,7 +671,8 @@ def bench_video(args) -> int:
     roof = _roof(wl.flops, wl.bytes, kern_avg, BF16_PEAK_TFLOPS if mfma else FP32_PEAK_TFLOPS,
                  "mfma" if mfma else "alu")
     roof.update({"kernel": kernel, "kernel_ms": round(kern_avg, 5),
-                 "alg_flops_per_launch": wl.flops, "alg_bytes_per_launch": wl.bytes, "traffic": None})
+                 "alg_flops_per_launch": wl.flops, "alg_bytes_per_launch": wl.bytes,
+                 "traffic": load_traffic(wl.name, kernel) if kernel in KERNEL_SOURCE else None})
     out = {
         "metric": "video window-attn fwd tokens/s",
         "value": round(wl.tokens / (wall / args.steps), 1),

@@ -570,7 +570,8 @@ def bench_linmapper(args, wl, sets, nsets, stream) -> int:
     peak_tf = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
     roof = _roof(flops, alg_bytes, kern_avg, peak_tf, "mfma" if wl.dtype == "bf16" else "alu")
     fast = wl.dtype == "bf16" and wl.M in (8, 16)
-    roof.update({"kernel": "wlin_kernel" if fast else "wlin_valu_kernel", "kernel_ms": round(kern_avg, 5),
+    kname = ("wlin16_kernel" if wl.M == 16 else "wlin_kernel") if fast else "wlin_valu_kernel"
+    roof.update({"kernel": kname, "kernel_ms": round(kern_avg, 5),
                  "alg_flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes, "traffic": None})
     out = {
         "metric": "LinMapper in-window linear mapping tokens/s",

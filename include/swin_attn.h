@@ -87,10 +87,14 @@ enum swin_layout { SWIN_LAYOUT_GRID = 0, SWIN_LAYOUT_WINDOWS = 1 };
 /* Log-CPB variants, as flags.  PAPER = 0 ([SwinV2] eq. 4): inputs
  * sign(x) ln(1+|x|) of the raw offsets, output unbounded.  The released
  * code's forms ([SwinV2] card, "Paper vs code"):
- *   CODE_NORM: inputs sign(u) log2(1+|u|) / log2(8) of u = 8 x / (norm_M - 1),
- *              norm_M the pretrained window (or the window itself);
+ *   CODE_NORM: the code's coordinate table: inputs sign(u) log2(1+|u|) /
+ *              log2(8) of u = 8 x / (norm_M - 1), norm_M the pretrained
+ *              window (or the window itself), with the row offset as G's
+ *              first input (the page does not give the order; the SwinV2
+ *              port in transformers stacks (row, column) offsets);
  *   SIGMOID16: output 16 * sigmoid(G), in (0, 16).
- * CODE_NORM | SIGMOID16 (= 3) is the released code. */
+ * CODE_NORM | SIGMOID16 (= 3) is the released code's table, so trained
+ * meta-network weights of that code load unchanged. */
 enum swin_cpb_mode { SWIN_CPB_PAPER = 0, SWIN_CPB_CODE_NORM = 1, SWIN_CPB_SIGMOID16 = 2 };
 
 typedef struct swin_attn_desc {
@@ -111,7 +115,8 @@ typedef struct swin_attn_desc {
  * computed once per relative position and stored).
  *   table[(dy+M-1)*(2M-1) + (dx+M-1)][h] = (W2 relu(W1 (f(dx), f(dy)) + b1) + b2)[h],
  *   f(x) = sign(x) ln(1+|x|), dy, dx in [-(M-1), M-1] (query minus key; dx is
- *   the column offset and G's first input).
+ *   the column offset and G's first input in the paper's form; CODE_NORM
+ *   feeds (dy, dx) instead, see swin_cpb_mode).
  * w1: hidden x 2, b1: hidden (or NULL = 0), w2: heads x hidden, b2: heads (or
  * NULL = 0), all fp32 row-major on the device.  table: (2M-1)^2 x heads fp32.
  * 1 <= M <= 64, 1 <= heads <= 64, 1 <= hidden <= 4096, 0 <= cpb_mode <= 3;

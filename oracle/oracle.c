@@ -87,16 +87,34 @@ double oracle_code_offset(double x, int norm_M)
 }
 
 /* CPB variants, as flags: 0 = the paper's form (eq. 3-4, output unbounded);
- * bit 0 = the code's coordinate transform above; bit 1 = the code's bounded
- * output 16 * sigmoid(G) ([SwinV2] card, "Paper vs code", CPB output
- * bounded).  3 = the released code. */
+ * bit 0 = the code's coordinate table: the transform above, with the row
+ * offset as G's first input; bit 1 = the code's bounded output
+ * 16 * sigmoid(G) ([SwinV2] card, "Paper vs code", CPB output bounded).
+ * 3 = the released code. */
 enum { OR_CPB_CODE_NORM = 1, OR_CPB_SIGMOID16 = 2 };
+
+/* G's two inputs for offset (dy, dx) under `mode`.  The paper writes
+ * G(dx, dy) (eq. 3): the column offset first.  The page does not say in
+ * which order the released code stacks its coordinate table; reading: the
+ * row offset first, as the SwinV2 port importable beside this oracle
+ * (transformers' Swinv2SelfAttention) builds its table from a row-major
+ * meshgrid of (row, column) offsets. */
+static void cpb_inputs(int dy, int dx, int mode, int norm_M, double* in0, double* in1)
+{
+    if (mode & OR_CPB_CODE_NORM) {
+        *in0 = oracle_code_offset((double)dy, norm_M);
+        *in1 = oracle_code_offset((double)dx, norm_M);
+    } else {
+        *in0 = oracle_log_offset((double)dx);
+        *in1 = oracle_log_offset((double)dy);
+    }
+}
 
 /* [SwinV2] eq. 3 + eq. 4, Method item 3: the bias for relative offset
  * (dy, dx) = (row offset, column offset) between query and key is the meta
  * network G applied to the log-spaced offset, G(x) = W2 relu(W1 x + b1) + b2.
- * Readings: the offset is query position minus key position; G's first input
- * is the column (x) offset and its second the row (y) offset; W1 is hidden x 2
+ * Readings: the offset is query position minus key position; G's inputs are
+ * ordered as cpb_inputs says (paper form: column offset first); W1 is hidden x 2
  * row-major, W2 is heads x hidden row-major; a NULL bias vector is zero.
  * The table is stored once per relative position (Method item 3), row
  * (dy + M-1)*(2M-1) + (dx + M-1), one column per head.  mode selects the
@@ -114,10 +132,8 @@ int oracle_cpb_table_mode(int M, int norm_M, int heads, int hidden,
     if (!h) return 2;
     for (int dy = -(M - 1); dy <= M - 1; ++dy) {
         for (int dx = -(M - 1); dx <= M - 1; ++dx) {
-            const double in0 = (mode & OR_CPB_CODE_NORM) ? oracle_code_offset((double)dx, norm_M)
-                                                         : oracle_log_offset((double)dx);
-            const double in1 = (mode & OR_CPB_CODE_NORM) ? oracle_code_offset((double)dy, norm_M)
-                                                         : oracle_log_offset((double)dy);
+            double in0, in1;
+            cpb_inputs(dy, dx, mode, norm_M, &in0, &in1);
             for (int j = 0; j < hidden; ++j) {
                 double a = w1[2 * j] * in0 + w1[2 * j + 1] * in1 + (b1 ? b1[j] : 0.0);
                 h[j] = a > 0.0 ? a : 0.0;                 /* ReLU between the two layers */
@@ -682,10 +698,8 @@ int oracle_cpb_table_bwd(int M, int norm_M, int heads, int hidden,
     if (db2) memset(db2, 0, (size_t)heads * sizeof(double));
     for (int dy = -(M - 1); dy <= M - 1; ++dy)
         for (int dx = -(M - 1); dx <= M - 1; ++dx) {
-            const double in0 = (mode & OR_CPB_CODE_NORM) ? oracle_code_offset((double)dx, norm_M)
-                                                         : oracle_log_offset((double)dx);
-            const double in1 = (mode & OR_CPB_CODE_NORM) ? oracle_code_offset((double)dy, norm_M)
-                                                         : oracle_log_offset((double)dy);
+            double in0, in1;
+            cpb_inputs(dy, dx, mode, norm_M, &in0, &in1);
             const double* grow = dtable + ((size_t)(dy + M - 1) * S + (size_t)(dx + M - 1)) * heads;
             for (int j = 0; j < hidden; ++j) a[j] = w1[2 * j] * in0 + w1[2 * j + 1] * in1 + (b1 ? b1[j] : 0.0);
             for (int o = 0; o < heads; ++o) {

@@ -44,6 +44,8 @@ MUTATIONS = [
     ("softmax_unnormalised", "for (int j = 0; j < N; ++j) lg[j] /= sum;", ";"),
     ("code_norm_scale", "x / (double)(norm_M - 1) * 8.0", "x / (double)norm_M * 8.0"),
     ("code_norm_base", "log2(1.0 + fabs(u)) / log2(8.0)", "log2(1.0 + fabs(u)) / 3.2"),
+    ("code_inputs_paper_order", "*in0 = oracle_code_offset((double)dy, norm_M);\n        *in1 = oracle_code_offset((double)dx, norm_M);",
+     "*in0 = oracle_code_offset((double)dx, norm_M);\n        *in1 = oracle_code_offset((double)dy, norm_M);"),
     ("sigmoid_scale", "16.0 / (1.0 + exp(-acc))", "8.0 / (1.0 + exp(-acc))"),
     ("sigmoid_sign", "16.0 / (1.0 + exp(-acc))", "16.0 / (1.0 + exp(acc))"),
     ("bwd_D_dropped", "dr[j] = pr[j] * (dr[j] - Di);", "dr[j] = pr[j] * dr[j];"),

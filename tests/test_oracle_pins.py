@@ -98,27 +98,34 @@ def pin_cpb_code_form(lib):
     for x, want in ((1, 1 / 3), (3, 2 / 3), (7, 1.0), (8, math.log2(9) / 3), (-3, -2 / 3), (0, 0.0)):
         assert oracle.code_offset(x, 9, lib) == pytest.approx(want, abs=1e-15), (x, want)
     assert oracle.code_offset(2, 5, lib) == pytest.approx(math.log2(5) / 3, abs=1e-15)   # u = 4
-    # the table picks the transformed offsets out through an identity first layer
+    # the table picks the transformed offsets out through an identity first
+    # layer: the code's table feeds the row offset first, the paper's form the
+    # column offset
     M = 9
     S = 2 * M - 1
     w1 = np.array([[1.0, 0.0], [0.0, 1.0], [-1.0, 0.0]])
     w2 = np.array([[1.0, 0.0, 0.0], [0.0, 1.0, 0.0], [0.0, 0.0, 1.0]])
     tab = oracle.cpb_table(M, w1, None, w2, None, lib=lib, mode=oracle.CPB_CODE_NORM, norm_M=9)
+    tab_paper = oracle.cpb_table(M, w1, None, w2, None, lib=lib)
     for dy, dx in ((0, 7), (3, -1), (-8, 8), (1, -3)):
         row = tab[(dy + M - 1) * S + (dx + M - 1)]
         fx, fy = math.copysign(math.log2(1 + abs(dx)) / 3, dx), math.copysign(math.log2(1 + abs(dy)) / 3, dy)
-        np.testing.assert_allclose(row, [max(fx, 0), max(fy, 0), max(-fx, 0)], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(row, [max(fy, 0), max(fx, 0), max(-fy, 0)], rtol=0, atol=1e-14)
+        px, py = math.copysign(math.log1p(abs(dx)), dx), math.copysign(math.log1p(abs(dy)), dy)
+        np.testing.assert_allclose(tab_paper[(dy + M - 1) * S + (dx + M - 1)], [max(px, 0), max(py, 0), max(-px, 0)],
+                                   rtol=0, atol=1e-14)
     # bounded output: G = b2 exactly when W2 = 0
     b2 = np.array([0.0, math.log(3), -math.log(3), math.log(15)])
     tab = oracle.cpb_table(3, np.ones((4, 2)), None, np.zeros((4, 4)), b2, lib=lib, mode=oracle.CPB_SIGMOID16)
     np.testing.assert_allclose(tab, np.tile([8.0, 12.0, 4.0, 15.0], (25, 1)), rtol=0, atol=1e-13)
-    # at norm window 9 the code's inputs are the paper's divided by ln 8
+    # at norm window 9 the code's inputs are the paper's divided by ln 8, in
+    # the other order (W1's columns swapped)
     g = torch.Generator().manual_seed(5)
     w1 = torch.randn(16, 2, generator=g, dtype=torch.float64).numpy()
     b1 = torch.randn(16, generator=g, dtype=torch.float64).numpy()
     w2 = torch.randn(2, 16, generator=g, dtype=torch.float64).numpy()
     code = oracle.cpb_table(6, w1, b1, w2, None, lib=lib, mode=oracle.CPB_CODE_NORM, norm_M=9)
-    paper = oracle.cpb_table(6, w1 / math.log(8), b1, w2, None, lib=lib)
+    paper = oracle.cpb_table(6, np.ascontiguousarray(w1[:, ::-1]) / math.log(8), b1, w2, None, lib=lib)
     np.testing.assert_allclose(code, paper, rtol=1e-12, atol=1e-13)
     # window transfer: a window of 4 normalised by 8 is the centre of the window of 8
     small = oracle.cpb_table(4, w1, b1, w2, None, lib=lib, mode=3, norm_M=8)
@@ -128,6 +135,46 @@ def pin_cpb_code_form(lib):
     with pytest.raises(ValueError):
         oracle.cpb_table(4, w1, b1, w2, None, lib=lib, mode=oracle.CPB_CODE_NORM, norm_M=1)
 
+
+
+def _swinv2_port_table(M, pretrained_M, w1, b1, w2):
+    """16 sigmoid(G(coordinate table)) as transformers' SwinV2 port computes it
+    (its second layer has no bias), flattened to ((2M-1)^2, heads).  The port
+    forms its coordinate table in fp32; G runs here in fp64."""
+    from transformers.models.swinv2 import modeling_swinv2 as m
+    heads = w2.shape[0]
+    cfg = m.Swinv2Config(embed_dim=heads * 4, num_heads=[heads], depths=[1], window_size=M)
+    att = m.Swinv2SelfAttention(cfg, heads * 4, heads, M, pretrained_window_size=[pretrained_M] * 2)
+    mlp = att.continuous_position_bias_mlp.double()
+    with torch.no_grad():
+        mlp[0].weight.copy_(torch.from_numpy(w1))
+        mlp[0].bias.copy_(torch.from_numpy(b1))
+        mlp[2].weight.copy_(torch.from_numpy(w2))
+        tab = 16 * torch.sigmoid(mlp(att.relative_coords_table.double())).view(-1, heads)
+        idx = att.relative_position_index
+    # its index maps (query, key) pairs to table rows (dy + M-1)(2M-1) + (dx + M-1)
+    coords = torch.stack(torch.meshgrid(torch.arange(M), torch.arange(M), indexing="ij")).flatten(1)
+    rel = coords[:, :, None] - coords[:, None, :]
+    assert torch.equal(idx, (rel[0] + M - 1) * (2 * M - 1) + rel[1] + M - 1)
+    return tab.numpy()
+
+
+def pin_cpb_released_code(lib):
+    """SwinV2 card, Paper vs code (CPB coordinate transform, CPB output
+    bounded): mode 3 equals the released code's table as the SwinV2 port in
+    transformers computes it, with the same G, for windows 8, 12 and 16, with
+    and without a pretrained window that normalises the offsets."""
+    pytest.importorskip("transformers")
+    g = torch.Generator().manual_seed(21)
+    hidden, heads = 512, 3
+    w1 = (torch.randn(hidden, 2, generator=g, dtype=torch.float64)).numpy()
+    b1 = (torch.randn(hidden, generator=g, dtype=torch.float64)).numpy()
+    w2 = (0.05 * torch.randn(heads, hidden, generator=g, dtype=torch.float64)).numpy()
+    for M, pre in ((8, 0), (12, 0), (16, 0), (16, 8), (12, 16)):
+        want = _swinv2_port_table(M, pre, w1, b1, w2)
+        got = oracle.cpb_table(M, w1, b1, w2, None, lib=lib, mode=3, norm_M=pre if pre > 0 else M)
+        # the port's fp32 coordinates move the fp64 result by a few 1e-7
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-6, err_msg=f"M={M} pretrained={pre}")
 
 BRUTE_CASES = [
     # H, W, M, shift, partition, sim, pos
@@ -611,6 +658,7 @@ PINS = {
     "worked_example": pin_worked_example,
     "cpb_vs_torch": pin_cpb_vs_torch,
     "cpb_code_form": pin_cpb_code_form,
+    "cpb_released_code": pin_cpb_released_code,
     "bruteforce": pin_bruteforce,
     "rope_freq_table": pin_rope_freq_table,
     "single_window_sdpa": pin_single_window_sdpa,

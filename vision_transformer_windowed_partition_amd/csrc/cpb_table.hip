@@ -3,8 +3,10 @@
 // network G = W2 relu(W1 (f(dx), f(dy)) + b1) + b2 with f(x) = sign(x)
 // ln(1+|x|) is evaluated once and stored, one column per head.  The
 // released code's variants (SwinV2 card, Paper vs code) are flags of `mode`:
-// CODE_NORM maps an offset x to u = 8 x / (norm_M - 1), then to
-// sign(u) log2(1+|u|) / log2(8); SIGMOID16 bounds the output to
+// CODE_NORM is the code's coordinate table, an offset x mapped to
+// u = 8 x / (norm_M - 1), then to sign(u) log2(1+|u|) / log2(8), with the
+// row offset as G's first input (the page leaves the order open; the SwinV2
+// port in transformers stacks (row, column)); SIGMOID16 bounds the output to
 // 16 sigmoid(G).
 //
 // One wavefront per (offset, group of up to four heads): lane j evaluates
@@ -55,6 +57,18 @@ __device__ __forceinline__ float cpb_input(int x, int mode, float norm_scale)
     return u > 0.0f ? a : (u < 0.0f ? -a : 0.0f);
 }
 
+// G's two inputs for table row (dy + M-1)(2M-1) + (dx + M-1): (f(dx), f(dy))
+// in the paper's form, (f(dy), f(dx)) in the code's coordinate table
+__device__ __forceinline__ void cpb_inputs(int row, int M, int mode, float norm_scale, float& in0, float& in1)
+{
+    const int S = 2 * M - 1;
+    const float fx = cpb_input(row % S - (M - 1), mode, norm_scale);
+    const float fy = cpb_input(row / S - (M - 1), mode, norm_scale);
+    const bool code = (mode & SWIN_CPB_CODE_NORM) != 0;
+    in0 = code ? fy : fx;
+    in1 = code ? fx : fy;
+}
+
 __global__ void __launch_bounds__(256)
 cpb_table_kernel(int M, int heads, int hidden, const float* __restrict__ w1, const float* __restrict__ b1,
                  const float* __restrict__ w2, const float* __restrict__ b2, float* __restrict__ table,
@@ -66,9 +80,8 @@ cpb_table_kernel(int M, int heads, int hidden, const float* __restrict__ w1, con
     const int groups = (heads + HG - 1) / HG;
     const int row = item / groups;                 // (dy + M-1)*S + (dx + M-1)
     const int o0 = (item - row * groups) * HG;     // first head of the group
-    const int S = 2 * M - 1;
-    const float fx = cpb_input(row % S - (M - 1), mode, norm_scale);
-    const float fy = cpb_input(row / S - (M - 1), mode, norm_scale);
+    float in0, in1;
+    cpb_inputs(row, M, mode, norm_scale, in0, in1);
 
     // null biases: an empty resource, whose loads read zero
     const Rsrc r1 = rsrc(w1, (uint32_t)hidden * 8u);
@@ -90,8 +103,7 @@ cpb_table_kernel(int M, int heads, int hidden, const float* __restrict__ w1, con
         }
 #pragma unroll
         for (int k = 0; k < UPL; ++k) {
-            // input 0 is the column (width) offset, input 1 the row offset
-            const float a = fmaf(__uint_as_float(w[k][0]), fx, fmaf(__uint_as_float(w[k][1]), fy, bb[k]));
+            const float a = fmaf(__uint_as_float(w[k][0]), in0, fmaf(__uint_as_float(w[k][1]), in1, bb[k]));
             const float hk = fmaxf(a, 0.0f);
 #pragma unroll
             for (int o = 0; o < HG; ++o) acc[o] = fmaf(v2[o][k], hk, acc[o]);
@@ -128,7 +140,7 @@ cpb_table_bwd_kernel(int M, int heads, int hidden, const float* __restrict__ w1,
                      float* __restrict__ db1, float* __restrict__ dw2, float* __restrict__ db2)
 {
     __shared__ float sdg[BR * HB];                 // dg of this block's rows and heads
-    __shared__ float sfx[BR], sfy[BR];             // G's inputs for those rows
+    __shared__ float sin0[BR], sin1[BR];           // G's inputs for those rows
     const int u = blockIdx.x * 256 + threadIdx.x;
     const int S = 2 * M - 1;
     const int row0 = blockIdx.y * BR, row1 = min(row0 + BR, S * S);
@@ -146,23 +158,22 @@ cpb_table_bwd_kernel(int M, int heads, int hidden, const float* __restrict__ w1,
     }
     if (threadIdx.x < BR) {
         const int row = min(row0 + (int)threadIdx.x, S * S - 1);
-        sfx[threadIdx.x] = cpb_input(row % S - (M - 1), mode, norm_scale);
-        sfy[threadIdx.x] = cpb_input(row / S - (M - 1), mode, norm_scale);
+        cpb_inputs(row, M, mode, norm_scale, sin0[threadIdx.x], sin1[threadIdx.x]);
     }
     __syncthreads();
     const bool unit = u < hidden;
-    float w1x = 0.0f, w1y = 0.0f, bb = 0.0f, w2c[HB];
+    float w10 = 0.0f, w11 = 0.0f, bb = 0.0f, w2c[HB];
 #pragma unroll
     for (int o = 0; o < HB; ++o) w2c[o] = unit && o0 + o < heads ? w2[(size_t)(o0 + o) * hidden + u] : 0.0f;
-    if (unit) { w1x = w1[2 * u]; w1y = w1[2 * u + 1]; bb = b1 ? b1[u] : 0.0f; }
-    float gw2[HB], gx = 0.0f, gy = 0.0f, gb = 0.0f, gb2 = 0.0f;
+    if (unit) { w10 = w1[2 * u]; w11 = w1[2 * u + 1]; bb = b1 ? b1[u] : 0.0f; }
+    float gw2[HB], g0 = 0.0f, g1 = 0.0f, gb = 0.0f, gb2 = 0.0f;
 #pragma unroll
     for (int o = 0; o < HB; ++o) gw2[o] = 0.0f;
     // db2 of head o0 + threadIdx.x, in the first unit block
     const bool own_b2 = blockIdx.x == 0 && threadIdx.x < HB && o0 + threadIdx.x < heads;
     for (int row = row0; row < row1; ++row) {
-        const float fx = sfx[row - row0], fy = sfy[row - row0];
-        const float a = fmaf(w1x, fx, fmaf(w1y, fy, bb));
+        const float x0 = sin0[row - row0], x1 = sin1[row - row0];
+        const float a = fmaf(w10, x0, fmaf(w11, x1, bb));
         const float hid = fmaxf(a, 0.0f);
         float dh = 0.0f;
 #pragma unroll
@@ -173,16 +184,16 @@ cpb_table_bwd_kernel(int M, int heads, int hidden, const float* __restrict__ w1,
             if (own_b2 && o == (int)threadIdx.x) gb2 += dg;
         }
         const float da = a > 0.0f ? dh : 0.0f;
-        gx = fmaf(da, fx, gx);
-        gy = fmaf(da, fy, gy);
+        g0 = fmaf(da, x0, g0);
+        g1 = fmaf(da, x1, g1);
         gb += da;
     }
     if (unit) {
 #pragma unroll
         for (int o = 0; o < HB; ++o)
             if (o0 + o < heads) unsafeAtomicAdd(&dw2[(size_t)(o0 + o) * hidden + u], gw2[o]);
-        unsafeAtomicAdd(&dw1[2 * u], gx);
-        unsafeAtomicAdd(&dw1[2 * u + 1], gy);
+        unsafeAtomicAdd(&dw1[2 * u], g0);
+        unsafeAtomicAdd(&dw1[2 * u + 1], g1);
         if (db1) unsafeAtomicAdd(&db1[u], gb);
     }
     if (own_b2 && db2) unsafeAtomicAdd(&db2[o0 + threadIdx.x], gb2);

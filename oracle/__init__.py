@@ -69,6 +69,8 @@ def _declare(lib):
     lib.oracle_window_attn.argtypes = [i32] * 10 + [dbl, dbl] + [vp] * 7 + [i64, vp, vp, vp]
     lib.oracle_window_attn_bwd.restype = i32
     lib.oracle_window_attn_bwd.argtypes = [i32] * 10 + [dbl, dbl] + [vp] * 12
+    lib.oracle_window_attn_bwd_given.restype = i32
+    lib.oracle_window_attn_bwd_given.argtypes = [i32] * 10 + [dbl, dbl] + [vp] * 14
     lib.oracle_cpb_table_bwd.restype = i32
     lib.oracle_cpb_table_bwd.argtypes = [i32] * 4 + [vp] * 4 + [i32] + [vp] * 5
     lib.oracle_window_cosines.restype = i32
@@ -218,21 +220,30 @@ def window_attn(q, k, v, *, heads: int, M: int, shift: int = 0, partition: str =
 
 def window_attn_bwd(q, k, v, dout, *, heads: int, M: int, shift: int = 0, partition: str = "cyclic",
                     sim: str = "cosine", pos: str = "none", tau=None, table=None,
-                    rope_freqs=None, rope_base: float = 10000.0, tau_min: float = 0.01, lib=None):
+                    rope_freqs=None, rope_base: float = 10000.0, tau_min: float = 0.01,
+                    out=None, lse=None, lib=None):
     """Gradients of sum(dout * window_attn(...)) in fp64: a dict with dq, dk,
     dv (B, H, W, C), dtau (heads,) for COSINE and dtable ((2M-1)^2, heads) for
-    TABLE."""
+    TABLE.  out (B, H, W, C) and lse (windows, heads, N) are optional forward
+    statistics as a caller holds them: D_i = dout_i . out_i and
+    p_ij = exp(logit_ij - lse_i) then come from them instead of the recomputed
+    softmax (the same values for the exact forward)."""
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, H, W, C = q.shape
     assert k.shape == q.shape and v.shape == q.shape and dout.shape == q.shape
     tau, table, rope_freqs = _f64(tau), _f64(table), _f64(rope_freqs)
+    out, lse = _f64(out), _f64(lse)
+    if out is not None:
+        assert out.shape == q.shape
+    if lse is not None:
+        assert lse.shape == (B * (H // M) * (W // M), heads, M * M)
     g = {n: np.zeros((B, H, W, C), dtype=np.float64) for n in ("dq", "dk", "dv")}
     dtau = np.zeros(heads, dtype=np.float64) if sim == "cosine" else None
     dtable = np.zeros(((2 * M - 1) ** 2, heads), dtype=np.float64) if pos == "table" else None
-    rc = (lib or load()).oracle_window_attn_bwd(
+    rc = (lib or load()).oracle_window_attn_bwd_given(
         B, H, W, C, heads, M, shift, PART[partition], SIM[sim], POS[pos],
         float(tau_min), float(rope_base), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(tau),
-        _ptr(table), _ptr(rope_freqs), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+        _ptr(table), _ptr(rope_freqs), _ptr(out), _ptr(lse), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
         _ptr(dtau), _ptr(dtable))
     if rc:
         raise ValueError(f"oracle_window_attn_bwd: bad argument (rc={rc})")

@@ -486,12 +486,22 @@ int oracle_window_cosines(int B, int H, int W, int C, int heads, int M, int shif
  * Each token belongs to one window, so dq, dk, dv are written, not summed;
  * dtau and dtable are sums over all windows.  Any of dtau (DOT) and dtable
  * (not TABLE) may be NULL.  Returns 0, or 1 on a bad argument.
+ *
+ * Given forward statistics (FLASHSWIN abstract: exact attention whose weights
+ * are never stored, so a backward rebuilds them from what the forward kept):
+ * when `out` (B, H, W, C, the forward's output as the caller holds it) is
+ * given, D_i = dout_i . out_i replaces sum_j p_ij dp_ij (the two are equal for
+ * the exact output); when `lse` (windows x heads x N, natural log, window-
+ * local query order) is given, p_ij = exp(l_ij - lse_i) over the allowed keys
+ * replaces the softmax (equal for the exact log-sum-exp).  These are the
+ * gradients a backward computes from the statistics it is handed.
  */
-int oracle_window_attn_bwd(int B, int H, int W, int C, int heads, int M, int shift,
-                           int part, int sim, int pos, double tau_min, double rope_base,
-                           const double* q, const double* k, const double* v, const double* dout,
-                           const double* tau, const double* table, const double* rope_freqs,
-                           double* dq, double* dk, double* dv, double* dtau, double* dtable)
+int oracle_window_attn_bwd_given(int B, int H, int W, int C, int heads, int M, int shift,
+                                 int part, int sim, int pos, double tau_min, double rope_base,
+                                 const double* q, const double* k, const double* v, const double* dout,
+                                 const double* tau, const double* table, const double* rope_freqs,
+                                 const double* out, const double* lse,
+                                 double* dq, double* dk, double* dv, double* dtau, double* dtable)
 {
     if (bad_shape(B, H, W, C, M, shift, part)) return 1;
     if (heads < 1 || C % heads) return 1;
@@ -519,6 +529,7 @@ int oracle_window_attn_bwd(int B, int H, int W, int C, int heads, int M, int shi
         double* ks = (double*)malloc(nd * sizeof(double));
         double* vs = (double*)malloc(nd * sizeof(double));
         double* gs = (double*)malloc(nd * sizeof(double));    /* dout */
+        double* os = (double*)malloc(nd * sizeof(double));    /* the given forward output */
         double* gq = (double*)malloc(nd * sizeof(double));
         double* gk = (double*)malloc(nd * sizeof(double));
         double* gv = (double*)malloc(nd * sizeof(double));
@@ -529,7 +540,7 @@ int oracle_window_attn_bwd(int B, int H, int W, int C, int heads, int M, int shi
         int* region = (int*)malloc((size_t)N * sizeof(int));
         double* my_dtau = (double*)calloc((size_t)heads, sizeof(double));
         double* my_dtable = dtable ? (double*)calloc((size_t)S * S * heads, sizeof(double)) : NULL;
-        if (!qx || !kx || !qs || !ks || !vs || !gs || !gq || !gk || !gv || !p || !dl || !gi || !gj ||
+        if (!qx || !kx || !qs || !ks || !vs || !gs || !os || !gq || !gk || !gv || !p || !dl || !gi || !gj ||
             !region || !my_dtau || (dtable && !my_dtable)) {
             #pragma omp atomic write
             failed = 1;
@@ -556,6 +567,7 @@ int oracle_window_attn_bwd(int B, int H, int W, int C, int heads, int M, int shi
                         kx[(size_t)t * d + e] = k[base + e];
                         vs[(size_t)t * d + e] = v[base + e];
                         gs[(size_t)t * d + e] = dout[base + e];
+                        os[(size_t)t * d + e] = out ? out[base + e] : 0.0;
                     }
                     if (pos == OR_POS_ROPE2D) {
                         rope_rotate(qx + (size_t)t * d, d, r, c, f, rope_base);
@@ -592,6 +604,12 @@ int oracle_window_attn_bwd(int B, int H, int W, int C, int heads, int M, int shi
                         pr[j] = (region[j] == region[i]) ? l : -INFINITY;
                         if (pr[j] > mx) mx = pr[j];
                     }
+                    if (lse) {
+                        /* the weights rebuilt from the given log-sum-exp */
+                        const double li = lse[((size_t)gw * heads + h) * N + i];
+                        for (int j = 0; j < N; ++j) pr[j] = exp(pr[j] - li);
+                        continue;
+                    }
                     double sum = 0.0;
                     for (int j = 0; j < N; ++j) {
                         pr[j] = exp(pr[j] - mx);              /* excluded keys: exp(-inf) = 0 */
@@ -612,6 +630,10 @@ int oracle_window_attn_bwd(int B, int H, int W, int C, int heads, int M, int shi
                         dr[j] = dp;
                         Di += pr[j] * dp;
                         for (int e = 0; e < d; ++e) gv[(size_t)j * d + e] += pr[j] * gs[(size_t)i * d + e];
+                    }
+                    if (out) {
+                        Di = 0.0;
+                        for (int e = 0; e < d; ++e) Di += gs[(size_t)i * d + e] * os[(size_t)i * d + e];
                     }
                     for (int j = 0; j < N; ++j) dr[j] = pr[j] * (dr[j] - Di);
                 }
@@ -666,10 +688,22 @@ int oracle_window_attn_bwd(int B, int H, int W, int C, int heads, int M, int shi
                 if (dtable) for (size_t x = 0; x < (size_t)S * S * heads; ++x) dtable[x] += my_dtable[x];
             }
         }
-        free(qx); free(kx); free(qs); free(ks); free(vs); free(gs); free(gq); free(gk); free(gv);
+        free(qx); free(kx); free(qs); free(ks); free(vs); free(gs); free(os); free(gq); free(gk); free(gv);
         free(p); free(dl); free(gi); free(gj); free(region); free(my_dtau); free(my_dtable);
     }
     return failed ? 2 : 0;
+}
+
+/* The backward with its own statistics: the softmax recomputed, D_i from it. */
+int oracle_window_attn_bwd(int B, int H, int W, int C, int heads, int M, int shift,
+                           int part, int sim, int pos, double tau_min, double rope_base,
+                           const double* q, const double* k, const double* v, const double* dout,
+                           const double* tau, const double* table, const double* rope_freqs,
+                           double* dq, double* dk, double* dv, double* dtau, double* dtable)
+{
+    return oracle_window_attn_bwd_given(B, H, W, C, heads, M, shift, part, sim, pos, tau_min, rope_base,
+                                        q, k, v, dout, tau, table, rope_freqs, NULL, NULL,
+                                        dq, dk, dv, dtau, dtable);
 }
 
 /*

@@ -345,3 +345,41 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         binding.lib()
+
+
+def test_binding_checks_sizes_before_the_call():
+    """The Python binding rejects tensors whose sizes disagree with the
+    descriptor before anything reaches the library (CPU tensors: the check runs
+    before the device-pointer check, so a size error is what raises)."""
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros((2, 16, 16, 64), dtype=bf)
+    tau, table = torch.ones(2), torch.zeros((225, 2))
+    base = dict(heads=2, M=8, shift=4, sim="cosine", pos="table")
+    with pytest.raises(ValueError, match="tau must hold 2"):
+        binding.swin_window_attn_fwd(q, q, q, tau=torch.ones(1), table=table, **base)
+    with pytest.raises(ValueError, match="table must hold 450"):
+        binding.swin_window_attn_fwd(q, q, q, tau=tau, table=torch.zeros((224, 2)), **base)
+    with pytest.raises(ValueError, match="rope_freqs must hold 32"):
+        binding.swin_window_attn_fwd(q, q, q, heads=2, M=8, sim="dot", pos="rope2d", rope_freqs=torch.zeros(31))
+    with pytest.raises(ValueError, match="out must be"):
+        binding.swin_window_attn_fwd(q, q, q, tau=tau, table=table, out=torch.zeros((2, 16, 16, 64)), **base)
+    with pytest.raises(ValueError, match="out must be"):
+        binding.swin_window_attn_fwd_lse(q, q, q, tau=tau, table=table, out=torch.zeros((2, 16, 16, 32), dtype=bf),
+                                         **base)
+    # pre-partitioned windows: q's element count must match the grid it is paired with
+    qw = torch.zeros((8, 64, 64), dtype=bf)
+    with pytest.raises(ValueError, match="descriptor's grid"):
+        binding.swin_window_attn_fwd(qw, qw, qw, tau=tau, table=table, layout="windows", grid=(2, 16, 24), **base)
+    with pytest.raises(ValueError, match="tau must hold 2"):
+        binding.swin_window_attn_bwd(q, q, q, q, q, tau=torch.ones(3), table=table, **base)
+    with pytest.raises(ValueError, match="table must hold 450"):
+        binding.swin_window_attn_bwd(q, q, q, q, q, tau=tau, table=torch.zeros(10), **base)
+    # video windows: the table covers (2Mt-1)(2M-1)^2 offsets
+    qv = torch.zeros((1, 4, 16, 16, 64), dtype=bf)
+    with pytest.raises(ValueError, match="table must hold 1350"):
+        binding.swin_window_attn3d_fwd(qv, qv, qv, heads=2, Mt=2, M=8, sim="cosine", pos="table", tau=tau,
+                                       table=torch.zeros((225, 2)))
+    # correctly sized CPU tensors get past the size checks and stop at the device check
+    with pytest.raises(ValueError, match="GPU"):
+        binding.swin_window_attn_fwd(q, q, q, tau=tau, table=table, **base)

@@ -27,6 +27,8 @@ CASES = [
     (1, 12, 12, 6, 3, "cyclic"),
     (1, 24, 24, 12, 5, "cyclic"),
     (1, 8, 8, 8, 3, "cyclic"),            # one window row and column: every region
+    (1, 48, 32, 16, 8, "cyclic"),         # 6 windows: M = 16 groups of four with a partial, shifted last group
+    (3, 32, 32, 16, 8, "cyclic"),         # 12 windows over 3 images: groups cross images, shifted
 ]
 
 

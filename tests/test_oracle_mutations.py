@@ -49,6 +49,10 @@ MUTATIONS = [
     ("sigmoid_scale", "16.0 / (1.0 + exp(-acc))", "8.0 / (1.0 + exp(-acc))"),
     ("sigmoid_sign", "16.0 / (1.0 + exp(-acc))", "16.0 / (1.0 + exp(acc))"),
     ("bwd_D_dropped", "dr[j] = pr[j] * (dr[j] - Di);", "dr[j] = pr[j] * dr[j];"),
+    ("bwd_given_lse_sign", "pr[j] = exp(pr[j] - li);", "pr[j] = exp(li - pr[j]);"),
+    ("bwd_given_lse_index", "lse[((size_t)gw * heads + h) * N + i];", "lse[((size_t)gw * heads + h) * N + (N - 1 - i)];"),
+    ("bwd_given_D_from_v", "Di += gs[(size_t)i * d + e] * os[(size_t)i * d + e];",
+     "Di += gs[(size_t)i * d + e] * vs[(size_t)i * d + e];"),
     ("bwd_dv_index", "gv[(size_t)j * d + e] += pr[j] * gs[(size_t)i * d + e];",
      "gv[(size_t)j * d + e] += pr[j] * gs[(size_t)j * d + e];"),
     ("bwd_norm_projection", "g[e] = (g[e] - xh[e] * proj) / n;", "g[e] = g[e] / n;"),

@@ -514,6 +514,52 @@ def pin_bwd_single_window_sdpa(lib):
         np.testing.assert_allclose(got[name], want, rtol=0, atol=1e-12)
 
 
+
+def pin_bwd_given_statistics(lib):
+    """The backward handed the forward's statistics (FLASHSWIN abstract: the
+    weights are rebuilt, not stored): given the exact output and log-sum-exp
+    it equals the backward with its own softmax (itself pinned by finite
+    differences and torch's SDPA backward); a log-sum-exp raised by c scales
+    every gradient by exp(-c) when the output is given (p_ij scales, D_i does
+    not); a changed output moves only D_i, so dv does not change."""
+    rng = np.random.default_rng(12)
+    for (H, W, M, s, part, sim, pos) in ((8, 8, 4, 2, "cyclic", "cosine", "table"),
+                                          (8, 12, 4, 0, "interleaved", "dot", "rope2d"),
+                                          (12, 12, 6, 3, "cyclic", "dot", "table")):
+        B, heads, C = 2, 2, 16
+        q, k, v, do = (rng.standard_normal((B, H, W, C)) for _ in range(4))
+        kw = dict(heads=heads, M=M, shift=s, partition=part, sim=sim, pos=pos, lib=lib,
+                  tau=np.array([0.3, 0.07]) if sim == "cosine" else None,
+                  table=rng.standard_normal(((2 * M - 1) ** 2, heads)) if pos == "table" else None)
+        out, lse = oracle.window_attn(q, k, v, return_lse=True, **kw)
+        plain = oracle.window_attn_bwd(q, k, v, do, **kw)
+        given = oracle.window_attn_bwd(q, k, v, do, out=out, lse=lse, **kw)
+        for name in plain:
+            np.testing.assert_allclose(given[name], plain[name], rtol=1e-10, atol=1e-12, err_msg=name)
+        c = rng.uniform(-0.5, 0.5, size=lse.shape)
+        shifted = oracle.window_attn_bwd(q, k, v, do, out=out, lse=lse + c, **kw)
+        scale_tok = np.exp(-c)                                   # per (window, head, query)
+        # dv_j = sum_i p_ij dout_i, so rows scaled by exp(-c_i) give the dv of
+        # dout_i scaled by exp(-c_i)
+        dsc = oracle.reverse(np.repeat(scale_tok.transpose(0, 2, 1), C // heads, axis=2),
+                             B, H, W, M, s, part)
+        want_dv = oracle.window_attn_bwd(q, k, v, do * dsc, out=out * 0.0, lse=lse, **kw)["dv"]
+        np.testing.assert_allclose(shifted["dv"], want_dv, rtol=1e-10, atol=1e-12)
+        moved = oracle.window_attn_bwd(q, k, v, do, out=out + rng.standard_normal(out.shape), lse=lse, **kw)
+        np.testing.assert_allclose(moved["dv"], given["dv"], rtol=0, atol=1e-13)
+        assert np.abs(moved["dq"] - given["dq"]).max() > 1e-3
+    # a constant raise of the log-sum-exp scales every gradient by exp(-c)
+    H = W = 8
+    M, s, heads, C = 4, 2, 2, 16
+    q, k, v, do = (rng.standard_normal((1, H, W, C)) for _ in range(4))
+    kw = dict(heads=heads, M=M, shift=s, partition="cyclic", sim="cosine", pos="table", lib=lib,
+              tau=np.array([0.2, 0.5]), table=rng.standard_normal(((2 * M - 1) ** 2, heads)))
+    out, lse = oracle.window_attn(q, k, v, return_lse=True, **kw)
+    base = oracle.window_attn_bwd(q, k, v, do, out=out, lse=lse, **kw)
+    up = oracle.window_attn_bwd(q, k, v, do, out=out, lse=lse + 0.7, **kw)
+    for name in base:
+        np.testing.assert_allclose(up[name], math.exp(-0.7) * base[name], rtol=1e-10, atol=1e-13, err_msg=name)
+
 def pin_cpb_bwd_finite_differences(lib):
     """The meta network's parameter gradients equal central differences of
     sum(dtable * cpb_table(...)), in all four CPB forms."""
@@ -669,6 +715,7 @@ PINS = {
     "partition_closed_form": pin_partition_closed_form,
     "bwd_finite_differences": pin_bwd_finite_differences,
     "bwd_single_window_sdpa": pin_bwd_single_window_sdpa,
+    "bwd_given_statistics": pin_bwd_given_statistics,
     "cpb_bwd_finite_differences": pin_cpb_bwd_finite_differences,
     "linear_closed_forms": pin_linear_closed_forms,
     "qkv_split": pin_qkv_split,

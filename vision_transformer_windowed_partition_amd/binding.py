@@ -1,8 +1,10 @@
 """Python binding of libswinattn.so (C ABI in include/swin_attn.h).
 
 Argument marshalling only: each function checks that it was handed device
-tensors, takes their data pointers and the current HIP stream, and calls the
-C entry point of the same name.  Every step of the computation runs in the
+tensors of the sizes its descriptor implies (so a mismatch raises ValueError
+here instead of sending a kernel past the end of a tensor), takes their data
+pointers and the current HIP stream, and calls the C entry point of the same
+name.  Every step of the computation runs in the
 library's kernels; if the library is missing this module raises instead of
 computing anything another way.
 """
@@ -131,6 +133,39 @@ def _enum(table, v):
     return table[v] if isinstance(v, str) else int(v)
 
 
+def _check_attn(desc: SwinAttnDesc, q, tau, table, rope_freqs, out=None, *, T: int = 1, Mt: int = 1) -> None:
+    """Sizes of what a window-attention call reads and writes, checked against
+    the descriptor before the C call, so a mismatch raises here instead of
+    sending a kernel past the end of a tensor.  T, Mt: video frames and
+    temporal window (1 for the 2D calls)."""
+    dev = q.device
+    if q.numel() != desc.B * T * desc.H * desc.W * desc.C:
+        raise ValueError(f"q holds {q.numel()} elements; the descriptor's grid needs "
+                         f"{desc.B * T * desc.H * desc.W * desc.C}")
+    if desc.layout == LAYOUT["grid"] and T == 1 and tuple(q.shape) != (desc.B, desc.H, desc.W, desc.C):
+        raise ValueError(f"q must be (B, H, W, C) = {(desc.B, desc.H, desc.W, desc.C)}, got {tuple(q.shape)}")
+    heads, M = desc.heads, desc.M
+    d = desc.C // heads if heads > 0 else 0
+    need = []
+    if desc.sim == SIM["cosine"]:
+        need.append(("tau", tau, heads))
+    if desc.pos == POS["table"]:
+        need.append(("table", table, (2 * Mt - 1) * (2 * M - 1) ** 2 * heads))
+    if desc.pos == POS["rope2d"] and rope_freqs is not None:
+        need.append(("rope_freqs", rope_freqs, heads * 2 * (d // 4)))
+    for name, t, n in need:
+        if t is None:
+            continue                    # the library rejects a missing required pointer
+        if t.numel() != n:
+            raise ValueError(f"{name} must hold {n} fp32 values, got {t.numel()}")
+    for t in (tau, table, rope_freqs):
+        if t is not None and t.device != dev:
+            raise ValueError("tau, table and rope_freqs must be on q's device")
+    if out is not None:
+        if out.shape != q.shape or out.dtype != q.dtype or out.device != dev or not out.is_contiguous():
+            raise ValueError("out must be a contiguous tensor of q's shape, dtype and device")
+
+
 def swin_cpb_table(M: int, w1, b1, w2, b2, *, out=None, cpb_mode: int = CPB_PAPER, norm_M=None, stream=None):
     """(2M-1)^2 x heads fp32 bias table from the meta network parameters.
     cpb_mode: CPB_PAPER, or the flags CPB_CODE_NORM | CPB_SIGMOID16; norm_M:
@@ -198,11 +233,12 @@ def swin_window_attn_fwd(q, k, v, *, heads: int, M: int, shift: int = 0, partiti
                          sim=sim, pos=pos, dtype=q.dtype, layout=layout, tau_min=tau_min,
                          rope_base=rope_base)
     for t in (q, k, v):
-        if not t.is_contiguous() or t.dtype != q.dtype or t.shape != q.shape:
-            raise ValueError("q, k, v must be contiguous tensors of one shape and dtype")
+        if not t.is_contiguous() or t.dtype != q.dtype or t.shape != q.shape or t.device != q.device:
+            raise ValueError("q, k, v must be contiguous tensors of one shape, dtype and device")
     for t in (tau, table, rope_freqs):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise ValueError("tau, table and rope_freqs must be contiguous fp32")
+    _check_attn(desc, q, tau, table, rope_freqs, out)
     if out is None:
         out = torch.empty_like(q)
     _check(lib().swin_window_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
@@ -226,12 +262,13 @@ def swin_window_attn_fwd_lse(q, k, v, *, heads: int, M: int, shift: int = 0, par
                          sim=sim, pos=pos, dtype=q.dtype, layout=layout, tau_min=tau_min,
                          rope_base=rope_base)
     for t in (q, k, v):
-        if not t.is_contiguous() or t.dtype != q.dtype or t.shape != q.shape:
-            raise ValueError("q, k, v must be contiguous tensors of one shape and dtype")
+        if not t.is_contiguous() or t.dtype != q.dtype or t.shape != q.shape or t.device != q.device:
+            raise ValueError("q, k, v must be contiguous tensors of one shape, dtype and device")
     for t in (tau, table, rope_freqs):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise ValueError("tau, table and rope_freqs must be contiguous fp32")
-    nwin = desc.B * (desc.H // desc.M) * (desc.W // desc.M)
+    _check_attn(desc, q, tau, table, rope_freqs, out)
+    nwin = desc.B * (desc.H // max(desc.M, 1)) * (desc.W // max(desc.M, 1))
     shape = (nwin, desc.heads, desc.M * desc.M)
     if lse is None:
         lse = torch.empty(shape, dtype=torch.float32, device=q.device)
@@ -273,6 +310,7 @@ def swin_window_attn3d_fwd(q, k, v, *, heads: int, Mt: int, M: int, shift_t: int
     B, T, H, W, C = q.shape
     desc = make_desc(B=B, H=H, W=W, C=C, heads=heads, M=M, shift=shift, partition=partition, sim=sim, pos=pos,
                      dtype=q.dtype, tau_min=tau_min)
+    _check_attn(desc, q, tau, table, None, out, T=T, Mt=Mt)
     if out is None:
         out = torch.empty_like(q)
     _check(lib().swin_window_attn3d_fwd(ctypes.byref(desc), T, Mt, shift_t, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
@@ -309,6 +347,10 @@ def swin_window_attn_bwd(q, k, v, out, dout, *, heads: int, M: int, shift: int =
     for t in (tau, table, rope_freqs):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise ValueError("tau, table and rope_freqs must be contiguous fp32")
+    _check_attn(desc, q, tau, table, rope_freqs)
+    for t in (k, v, out, dout):
+        if t.device != q.device:
+            raise ValueError("q, k, v, out, dout must be on one device")
     g = {"dq": torch.empty_like(q), "dk": torch.empty_like(q), "dv": torch.empty_like(q)}
     dtau = dtable = None
     if want_dtau and _enum(SIM, sim) == 0:
@@ -320,7 +362,7 @@ def swin_window_attn_bwd(q, k, v, out, dout, *, heads: int, M: int, shift: int =
                                           _ptr(tau), _ptr(table), _ptr(rope_freqs), _ptr(g["dq"]), _ptr(g["dk"]),
                                           _ptr(g["dv"]), _ptr(dtau), _ptr(dtable), _stream(q, stream)))
     else:
-        nwin = desc.B * (desc.H // desc.M) * (desc.W // desc.M)
+        nwin = desc.B * (desc.H // max(desc.M, 1)) * (desc.W // max(desc.M, 1))
         if lse.shape != (nwin, desc.heads, desc.M * desc.M) or lse.dtype != torch.float32 or not lse.is_contiguous():
             raise ValueError("lse must be the forward's contiguous fp32 (n_windows, heads, M*M)")
         _check(lib().swin_window_attn_bwd_lse(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out),

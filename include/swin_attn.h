@@ -167,7 +167,7 @@ int swin_window_attn_fwd(const swin_attn_desc* desc, const void* q, const void* 
 
 /* swin_window_attn_fwd that also exports, per window, head and query, the
  * log-sum-exp of the query's logits over the keys it attends to ([Flash]
- * introduction: training with exact attention and no score matrix; the
+ * Abstract: training with exact attention and no score matrix; the
  * per-query softmax statistic is what lets a backward rebuild the weights
  * without a pass of its own):
  *   lse[(w*heads + h)*N + i] = log sum_j exp(logit_ij), natural log,
@@ -213,7 +213,7 @@ int swin_window_attn_bwd(const swin_attn_desc* desc, const void* q, const void* 
                          void* dv, float* dtau, float* dtable, void* stream);
 
 /* swin_window_attn_bwd given the forward's log-sum-exp ([Flash]
- * introduction, as for swin_window_attn_fwd_lse): lse as written by
+ * Abstract, as for swin_window_attn_fwd_lse): lse as written by
  * swin_window_attn_fwd_lse for the same inputs (device fp32, n_windows x
  * heads x N, natural log, 4-byte aligned, read only).  The matrix-core paths
  * rebuild p_ij = exp(logit_ij - lse_i) from it and skip their own pass over

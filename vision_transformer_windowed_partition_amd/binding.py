@@ -133,16 +133,17 @@ def _enum(table, v):
     return table[v] if isinstance(v, str) else int(v)
 
 
-def _check_attn(desc: SwinAttnDesc, q, tau, table, rope_freqs, out=None, *, T: int = 1, Mt: int = 1) -> None:
+def _check_attn(desc: SwinAttnDesc, q, tau, table, rope_freqs, out=None, *, T=None, Mt: int = 1) -> None:
     """Sizes of what a window-attention call reads and writes, checked against
     the descriptor before the C call, so a mismatch raises here instead of
     sending a kernel past the end of a tensor.  T, Mt: video frames and
-    temporal window (1 for the 2D calls)."""
+    temporal window (T None for the 2D calls)."""
     dev = q.device
-    if q.numel() != desc.B * T * desc.H * desc.W * desc.C:
+    frames = 1 if T is None else T
+    if q.numel() != desc.B * frames * desc.H * desc.W * desc.C:
         raise ValueError(f"q holds {q.numel()} elements; the descriptor's grid needs "
-                         f"{desc.B * T * desc.H * desc.W * desc.C}")
-    if desc.layout == LAYOUT["grid"] and T == 1 and tuple(q.shape) != (desc.B, desc.H, desc.W, desc.C):
+                         f"{desc.B * frames * desc.H * desc.W * desc.C}")
+    if desc.layout == LAYOUT["grid"] and T is None and tuple(q.shape) != (desc.B, desc.H, desc.W, desc.C):
         raise ValueError(f"q must be (B, H, W, C) = {(desc.B, desc.H, desc.W, desc.C)}, got {tuple(q.shape)}")
     heads, M = desc.heads, desc.M
     d = desc.C // heads if heads > 0 else 0

@@ -104,9 +104,78 @@ def traffic(rdreq_dir: str, write_dir: str, kernel: str) -> dict:
             "hbm_bytes_per_launch": r_k * read_scale + w_k * write_scale}
 
 
+# Matrix-core counters of one --pmc run: what each kernel issued and how long
+# the MFMA pipes were busy.  GRBM_GUI_ACTIVE comes back summed over the
+# chip's 8 XCDs (its per-dispatch value divided by the dispatch's duration is
+# 8x the clock), so the GPU's busy cycles are that sum / 8, as rocprofv3's own
+# MfmaUtil takes the largest instance.  Every matrix instruction in these
+# kernels is v_mfma_f32_16x16x32_bf16: 16384 flops, 16 busy cycles of one SIMD
+# at the bf16 dense rate (1024 flops per SIMD and clock, 4 SIMDs per CU).
+MFMA_COUNTERS = ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+N_XCD, N_SIMD, FLOPS_PER_MFMA, PEAK_BF16 = 8, 1024, 16384, 2.5e15
+
+
+def dispatch_durations(pmc_dir: str, kernel: str) -> list[float]:
+    """Start-to-end seconds of every dispatch of `kernel` in a --pmc run."""
+    per = {}
+    for r in csv.DictReader(open(_one(os.path.join(pmc_dir, "*counter_collection.csv")))):
+        if kernel in r["Kernel_Name"]:
+            per[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    return [per[d] for d in sorted(per)]
+
+
+def mfma_summary(pmc_dir: str, kernel: str, alg_flops: float | None = None) -> dict:
+    """Medians over the dispatches of `kernel` of the MFMA_COUNTERS and what
+    follows from them: MFMA-pipe utilisation (busy cycles over the SIMDs'
+    cycles, rocprofv3's MfmaUtil), vector instructions per MFMA, and the
+    executed and algorithmic flop rates over the counted cycles at the
+    measured clock, as fractions of the 2.5 PFLOP/s bf16 peak."""
+    med = statistics.median
+    v = {c: med(counter_per_dispatch(pmc_dir, c, kernel)) for c in MFMA_COUNTERS}
+    dur = med(dispatch_durations(pmc_dir, kernel))
+    cycles = v["GRBM_GUI_ACTIVE"] / N_XCD
+    out = dict(v)
+    out.update(dispatch_s=dur, gpu_cycles=cycles, clock_ghz=cycles / dur / 1e9,
+               mfma_util=v["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * N_SIMD),
+               busy_cycles_per_mfma=v["SQ_VALU_MFMA_BUSY_CYCLES"] / max(v["SQ_INSTS_MFMA"], 1.0),
+               valu_per_mfma=v["SQ_INSTS_VALU"] / max(v["SQ_INSTS_MFMA"], 1.0),
+               executed_flops=v["SQ_INSTS_MFMA"] * FLOPS_PER_MFMA)
+    out["executed_frac"] = out["executed_flops"] / dur / PEAK_BF16
+    if alg_flops:
+        out["alg_flops"] = alg_flops
+        out["alg_frac"] = alg_flops / dur / PEAK_BF16
+    return out
+
+
+def mfma_markdown(kernel: str, workload: str, command: str, m: dict) -> list[str]:
+    md = [f"# Matrix-core counters: {kernel} on {workload}", "",
+          "One `--pmc` pass (medians over the dispatches of the kernel):", "", "```", command, "```", "",
+          "| counter | value per launch |", "|---|---|"]
+    md += [f"| {c} | {m[c]:.4g} |" for c in MFMA_COUNTERS]
+    md += ["", "Derived (GRBM_GUI_ACTIVE is summed over 8 XCDs; every matrix instruction is "
+           "v_mfma_f32_16x16x32_bf16, 16384 flops):", "",
+           "| quantity | value |", "|---|---|",
+           f"| GPU cycles (GRBM_GUI_ACTIVE / 8) | {m['gpu_cycles']:.4g} |",
+           f"| dispatch duration under counters | {m['dispatch_s'] * 1e6:.1f} µs |",
+           f"| clock (cycles / duration) | {m['clock_ghz']:.2f} GHz |",
+           f"| busy cycles per MFMA | {m['busy_cycles_per_mfma']:.2f} |",
+           f"| **MFMA utilisation** = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs) | "
+           f"**{m['mfma_util']:.3f}** |",
+           f"| vector instructions per MFMA (SQ_INSTS_VALU / SQ_INSTS_MFMA) | {m['valu_per_mfma']:.2f} |",
+           f"| executed MFMA flops / duration / 2.5 PFLOP/s | {m['executed_frac']:.3f} |"]
+    if "alg_frac" in m:
+        md += [f"| algorithmic flops ({m['alg_flops'] / 1e9:.1f} GFLOP) / duration / 2.5 PFLOP/s | "
+               f"{m['alg_frac']:.3f} |"]
+    md += ["", "The utilisation and the executed-flop fraction agree when the busy cycles per MFMA are 16 "
+           "and the clock is 2.4 GHz; the executed flops exceed the algorithmic ones by the padded key "
+           "slots, the row-sum products and, where taken, the hi + lo operand products. The duration here "
+           "is the counter pass's, longer than an unprofiled launch's.", ""]
+    return md
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--stats", required=True)
+    ap.add_argument("--stats", help="directory of the --kernel-trace --stats run (not needed with --mfma)")
     ap.add_argument("--fetch", help="directory of the --pmc run with the TCC_EA0_RDREQ_{32B,64B,128B} counters")
     ap.add_argument("--write")
     ap.add_argument("--kernel", required=True)
@@ -118,7 +187,22 @@ def main(argv=None) -> int:
     ap.add_argument("--command-write", default="")
     ap.add_argument("--out-md", required=True)
     ap.add_argument("--out-json")
+    ap.add_argument("--mfma", help="directory of a --pmc run of MFMA_COUNTERS: write only its summary")
     a = ap.parse_args(argv)
+
+    if a.mfma:
+        alg = None
+        if a.bench_json:
+            for line in open(a.bench_json):
+                if line.strip().startswith("{") and '"metric"' in line:
+                    alg = json.loads(line)["roofline"].get("alg_flops_per_launch")
+        m = mfma_summary(a.mfma, a.kernel, alg)
+        md = mfma_markdown(a.kernel, a.workload, a.command_stats, m)
+        os.makedirs(os.path.dirname(os.path.abspath(a.out_md)), exist_ok=True)
+        with open(a.out_md, "w") as f:
+            f.write("\n".join(md))
+        print("\n".join(md))
+        return 0
 
     st = kernel_stats(a.stats, a.kernel)
     bench = None

@@ -19,7 +19,8 @@ Prints ONE JSON line.  `value` is tokens/s over the whole job.
 
 Other modes (same protocol, their own JSON line): --backward times the
 backward step; --branch times the attention branch of a block (input
-projection, table, attention, output projection with the residual post-norm);
+projection, table, attention, output projection with the residual post-norm;
+--fused takes the input projection inside the attention kernel);
 --linmapper times LinMapper's in-window linear mapping.
 """
 from __future__ import annotations
@@ -171,6 +172,9 @@ def main(argv=None) -> int:
     ap.add_argument("--branch", action="store_true",
                     help="time the whole attention branch instead: swin_qkv_proj, the CPB table, "
                          "swin_window_attn_fwd and swin_proj_post_norm (residual post-norm)")
+    ap.add_argument("--fused", action="store_true",
+                    help="with --branch: the input layer fused into the attention (swin_qkv_window_attn_fwd) "
+                         "instead of swin_qkv_proj then swin_window_attn_fwd")
     ap.add_argument("--linmapper", action="store_true",
                     help="time LinMapper's in-window linear mapping (swin_window_linear) on the "
                          "workload's values instead of the attention")
@@ -443,22 +447,34 @@ def bench_branch(args, wl, par, table, desc, stream) -> int:
         xs = x0 if i == 0 else x0.clone()
         sets.append(dict(x=xs, q=torch.empty_like(xs), k=torch.empty_like(xs), v=torch.empty_like(xs),
                          o=torch.empty_like(xs), y=torch.empty_like(xs)))
-    names = ("qkv", "attn", "dwconv", "norm") if iwin else ("qkv", "attn", "norm")
+    fused = args.fused
+    if fused and iwin:
+        raise SystemExit("bench.py: --fused covers the attention branch without the convolution of v")
+    first = ("qkv_attn",) if fused else ("qkv", "attn")
+    names = first + (("dwconv", "norm") if iwin else ("norm",))
 
     def step(i, timed=None):
         st = sets[i % nsets]
         rec = (lambda n, end: timers[n].record(timed, end)) if timed is not None else (lambda n, end: None)
-        rec("qkv", False)
-        binding.swin_qkv_proj(st["x"], w["w_qkv"], w["b_qkv"], out=(st["q"], st["k"], st["v"]), stream=stream)
-        rec("qkv", True)
         tab = None
         if wl.pos == "table":
             tab = binding.swin_cpb_table(wl.M, par["w1"], par["b1"], par["w2"], par["b2"], out=table,
                                          stream=stream)
-        rec("attn", False)
-        binding.swin_window_attn_fwd(st["q"], st["k"], st["v"], heads=wl.heads, M=wl.M, desc=desc,
-                                     tau=par["tau"], table=tab, out=st["o"], stream=stream)
-        rec("attn", True)
+        if fused:
+            rec("qkv_attn", False)
+            binding.swin_qkv_window_attn_fwd(st["x"], w["w_qkv"], w["b_qkv"], heads=wl.heads, M=wl.M,
+                                             shift=wl.shift, partition=wl.partition, sim=wl.sim, pos=wl.pos,
+                                             tau=par["tau"], table=tab, out=st["o"], stream=stream)
+            rec("qkv_attn", True)
+        else:
+            rec("qkv", False)
+            binding.swin_qkv_proj(st["x"], w["w_qkv"], w["b_qkv"], out=(st["q"], st["k"], st["v"]),
+                                  stream=stream)
+            rec("qkv", True)
+            rec("attn", False)
+            binding.swin_window_attn_fwd(st["q"], st["k"], st["v"], heads=wl.heads, M=wl.M, desc=desc,
+                                         tau=par["tau"], table=tab, out=st["o"], stream=stream)
+            rec("attn", True)
         if iwin:
             rec("dwconv", False)
             binding.swin_dwconv_add(st["v"], w["w_dw"], w["b_dw"], st["o"], stream=stream)
@@ -487,10 +503,12 @@ def bench_branch(args, wl, par, table, desc, stream) -> int:
     compute = "mfma" if wl.dtype == "bf16" else "alu"
     work = {"qkv": (6.0 * T * C * C, 4.0 * T * C * es),
             "attn": (float(wl.flops), float(wl.bytes)),
+            "qkv_attn": (6.0 * T * C * C + float(wl.flops), 2.0 * T * C * es),
             "norm": (2.0 * T * C * C, 3.0 * T * C * es),
             "dwconv": (18.0 * T * C, 3.0 * T * C * es)}
     kname = {"qkv": "qkv_kernel" if wl.dtype == "bf16" else "qkv_f32_kernel",
              "attn": binding.swin_window_attn_kernel(desc),
+             "qkv_attn": "attn_fused_kernel",
              "norm": "norm_kernel" if wl.dtype == "bf16" else "norm_f32_kernel",
              "dwconv": "dwconv_add_kernel"}
     kernels = {}
@@ -502,6 +520,8 @@ def bench_branch(args, wl, par, table, desc, stream) -> int:
     dominant = max(names, key=lambda n: ms[n])
     out = {
         "metric": "attention branch tokens/s (QKV projection, CPB table, window attention, "
+                  if not fused else
+                  "attention branch tokens/s (CPB table, window attention with the QKV projection fused in, "
                   + ("depthwise 3x3 convolution of v, " if iwin else "")
                   + "output projection + residual post-norm)",
         "value": round(T / (wall / args.steps), 1),
@@ -517,7 +537,7 @@ def bench_branch(args, wl, par, table, desc, stream) -> int:
         "data": "synthetic (seeded N(0,1) features, randn/sqrt(C) weights, random-init log-CPB MLP)",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "W": wl.W, "C": wl.C, "heads": wl.heads,
                    "M": wl.M, "shift": wl.shift, "partition": wl.partition, "sim": wl.sim, "pos": wl.pos,
-                   "pass": "attention branch",
+                   "pass": "attention branch" + (" (fused input layer)" if fused else ""),
                    "cache": "warm" if args.warm else f"cold ({nsets} rotating sets)",
                    "parallelism": "none (1 GPU)"},
         "roofline": kernels[dominant],

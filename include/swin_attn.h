@@ -298,6 +298,24 @@ int swin_cpb_table_bwd(int32_t M, int32_t norm_M, int32_t heads, int32_t hidden,
 int swin_qkv_proj(const void* x, const void* w, const float* b, void* q, void* k, void* v,
                   int64_t T, int32_t C, int32_t dtype, void* stream);
 
+/* The attention branch's input layer fused into the window attention
+ * ([SwinV2] Method item 1 and the block pseudocode: window_attention(features)
+ * maps the features through one linear layer to q, k, v and attends within
+ * windows): q, k, v = split(x w_qkv^T + b_qkv) as swin_qkv_proj computes
+ * them, then swin_window_attn_fwd over them, without q, k, v leaving the
+ * chip.  desc as for swin_window_attn_fwd, GRID layout; x, out: (B, H, W, C)
+ * bf16; w_qkv: 3C x C bf16 (rows: q, k, v outputs); b_qkv: 3C fp32 or NULL;
+ * tau, table as for swin_window_attn_fwd.  Device memory; x, w_qkv, out
+ * 16-byte aligned; out must not overlap x, w_qkv or b_qkv (SWIN_EINVAL).
+ * Built for bf16, 9 <= M <= 16, no rotary positions, d = 32 and C a multiple
+ * of 32 up to 192; other descriptors return SWIN_EUNSUPPORTED (use
+ * swin_qkv_proj and swin_window_attn_fwd).  Arithmetic: q, k, v in fp32 from
+ * bf16 products, rounded once to bf16 for the matrix-core attention (as
+ * hi + lo pairs where a rounded operand would pass the bf16 tolerance:
+ * COSINE with tau < 0.1, DOT with a logit bound above 20 in log2 units). */
+int swin_qkv_window_attn_fwd(const swin_attn_desc* desc, const void* x, const void* w_qkv, const float* b_qkv,
+                             void* out, const float* tau, const float* table, void* stream);
+
 /* The attention branch's output layer and residual post-norm ([SwinV2]
  * Method item 1: the layer norm moves to the output of the residual branch,
  * before the add; block pseudocode):

@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
                                            "swin_cpb_table3d", "swin_window_attn3d_fwd",
                                            "swin_window_attn3d_kernel",
                                            "swin_window_attn_bwd_kernel",
-                                           "swin_qkv_proj", "swin_proj_post_norm", "swin_dwconv_add",
+                                           "swin_qkv_proj", "swin_qkv_window_attn_fwd", "swin_proj_post_norm",
+                                           "swin_dwconv_add",
                                            "swin_window_linear",
                                            "swin_status_string",
                                            "swin_last_error", "swin_version"])
@@ -195,6 +196,30 @@ def test_projection_rejects(L):
     assert _pnorm(L, y=ctypes.c_void_p(0x50000000 - 64)) == SWIN_EINVAL         # y overlaps gamma
     assert _pnorm(L, beta=ctypes.c_void_p(0x50001008)) == SWIN_EINVAL           # misaligned
     assert _pnorm(L, o=None, w=None, resid=None, gamma=None, beta=None, y=None, T=0) == SWIN_OK
+
+
+def _fused(L, d=None, x=ctypes.c_void_p(0x10000), w=ctypes.c_void_p(0x30000000), b=None,
+           out=ctypes.c_void_p(0x40000000), tau=FAKE, table=FAKE, **kw):
+    desc = d if d is not None else _desc(**{**dict(B=1, H=32, W=32, C=96, heads=3, M=16, shift=8), **kw})
+    return L.swin_qkv_window_attn_fwd(ctypes.byref(desc), x, w, b, out, tau, table, None)
+
+
+def test_fused_input_layer_rejects(L):
+    """Host validation of the fused input layer + attention: nothing is launched."""
+    assert _fused(L, dtype=0) == SWIN_EUNSUPPORTED                              # fp32
+    assert _fused(L, M=8, H=16, W=16, shift=4) == SWIN_EUNSUPPORTED             # M <= 8
+    assert _fused(L, M=24, H=48, W=48, shift=12) == SWIN_EUNSUPPORTED           # M > 16
+    assert _fused(L, pos=2) == SWIN_EUNSUPPORTED                                # rotary positions
+    assert _fused(L, C=512, heads=16) == SWIN_EUNSUPPORTED                      # C > 192
+    assert _fused(L, layout=1) == SWIN_EUNSUPPORTED                             # windows layout
+    assert _fused(L, shift=16) == SWIN_EINVAL                                   # bad descriptor
+    assert _fused(L, x=None) == SWIN_EINVAL
+    assert _fused(L, w=ctypes.c_void_p(0x30000008)) == SWIN_EINVAL              # misaligned
+    assert _fused(L, b=ctypes.c_void_p(0x50000002)) == SWIN_EINVAL              # misaligned bias
+    assert _fused(L, out=ctypes.c_void_p(0x10000 + 4096)) == SWIN_EINVAL        # out overlaps x
+    assert _fused(L, tau=None) == SWIN_EINVAL                                   # COSINE needs tau
+    assert _fused(L, table=None) == SWIN_EINVAL                                 # TABLE needs a table
+    assert _fused(L, B=0, x=None, w=None, out=None) == SWIN_OK                  # empty: no-op
 
 
 def test_dwconv_rejects(L):

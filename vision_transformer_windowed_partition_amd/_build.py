@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libswinattn.so")
-SOURCES = ["api.hip", "partition.hip", "cpb_table.hip", "attn_valu.hip", "attn_mfma.hip", "attn_small.hip", "attn_large.hip", "attn_bwd.hip", "attn_bwd_small.hip", "attn_bwd_large.hip", "proj.hip", "dwconv.hip", "window_linear.hip", "attn_video.hip", "attn_video_mfma.hip"]
+SOURCES = ["api.hip", "partition.hip", "cpb_table.hip", "attn_valu.hip", "attn_mfma.hip", "attn_small.hip", "attn_large.hip", "attn_bwd.hip", "attn_bwd_small.hip", "attn_bwd_large.hip", "proj.hip", "attn_fused.hip", "dwconv.hip", "window_linear.hip", "attn_video.hip", "attn_video_mfma.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

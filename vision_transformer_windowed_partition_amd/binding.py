@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.swin_cpb_table_bwd.argtypes = [i32] * 4 + [vp] * 5 + [i32] + [vp] * 5
         L.swin_qkv_proj.restype = i32
         L.swin_qkv_proj.argtypes = [vp] * 6 + [ctypes.c_int64, i32, i32, vp]
+        L.swin_qkv_window_attn_fwd.restype = i32
+        L.swin_qkv_window_attn_fwd.argtypes = [ctypes.POINTER(SwinAttnDesc)] + [vp] * 7
         L.swin_proj_post_norm.restype = i32
         L.swin_proj_post_norm.argtypes = [vp] * 6 + [ctypes.c_float, vp, ctypes.c_int64, i32, i32, vp]
         L.swin_dwconv_add.restype = i32
@@ -415,6 +417,33 @@ def swin_qkv_proj(x, w, b=None, *, out=None, stream=None):
     _check(lib().swin_qkv_proj(_ptr(x), _ptr(w), _ptr(b), _ptr(q), _ptr(k), _ptr(v), x.numel() // C, C, dt,
                                _stream(x, stream)))
     return q, k, v
+
+
+def swin_qkv_window_attn_fwd(x, w_qkv, b_qkv=None, *, heads: int, M: int, shift: int = 0, partition="cyclic",
+                             sim="cosine", pos="none", tau=None, table=None, tau_min: float = 0.01, out=None,
+                             stream=None):
+    """Window attention of q, k, v = split(x w_qkv^T + b_qkv), the input layer
+    fused in: x (B, H, W, C) bf16, w_qkv (3C, C) bf16, b_qkv (3C,) fp32 or
+    None; returns the attention output (B, H, W, C)."""
+    if x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous (B, H, W, C) tensor")
+    B, H, W, C = x.shape
+    if w_qkv.shape != (3 * C, C) or w_qkv.dtype != x.dtype or not w_qkv.is_contiguous() or w_qkv.device != x.device:
+        raise ValueError("w_qkv must be a contiguous (3C, C) tensor of x's dtype and device")
+    if b_qkv is not None and (b_qkv.shape != (3 * C,) or b_qkv.dtype != torch.float32 or not b_qkv.is_contiguous()
+                              or b_qkv.device != x.device):
+        raise ValueError("b_qkv must be contiguous fp32 of 3C on x's device")
+    for t in (tau, table):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("tau and table must be contiguous fp32")
+    desc = make_desc(B=B, H=H, W=W, C=C, heads=heads, M=M, shift=shift, partition=partition, sim=sim, pos=pos,
+                     dtype=x.dtype, tau_min=tau_min)
+    _check_attn(desc, x, tau, table, None, out)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib().swin_qkv_window_attn_fwd(ctypes.byref(desc), _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(out),
+                                          _ptr(tau), _ptr(table), _stream(x, stream)))
+    return out
 
 
 def swin_proj_post_norm(o, w, b, resid, gamma, beta, *, eps: float = 1e-5, out=None, stream=None):

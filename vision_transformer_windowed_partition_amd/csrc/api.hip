@@ -400,6 +400,33 @@ int swin_qkv_proj(const void* x, const void* w, const float* b, void* q, void* k
     return hip_status(swin::launch_qkv_proj(a, (hipStream_t)stream), "swin_qkv_proj launch");
 }
 
+int swin_qkv_window_attn_fwd(const swin_attn_desc* d, const void* x, const void* w_qkv, const float* b_qkv,
+                             void* out, const float* tau, const float* table, void* stream)
+{
+    int st = check_desc(d, false);
+    if (st) return st;
+    if (d->layout != SWIN_LAYOUT_GRID) return fail(SWIN_EUNSUPPORTED, "the fused input layer needs the GRID layout");
+    swin::AttnParams p = params_of(d);
+    if (!swin::attn_fused_supported(p))
+        return fail(SWIN_EUNSUPPORTED, "fused input layer: bf16, 9 <= M <= 16, no rotary positions, "
+                                       "C a multiple of 32 up to 192 are built");
+    const size_t bytes = (size_t)d->B * d->H * d->W * d->C * 2;
+    if (bytes == 0) return SWIN_OK;
+    if (!x || !w_qkv || !out) return fail(SWIN_EINVAL, "NULL x, w_qkv or out");
+    if (((uintptr_t)x | (uintptr_t)w_qkv | (uintptr_t)out) & 15)
+        return fail(SWIN_EINVAL, "x, w_qkv and out must be 16-byte aligned");
+    if ((uintptr_t)b_qkv & 3) return fail(SWIN_EINVAL, "b_qkv must be 4-byte aligned");
+    if (d->sim == SWIN_SIM_COSINE && !tau) return fail(SWIN_EINVAL, "COSINE needs tau");
+    if (d->pos == SWIN_POS_TABLE && !table) return fail(SWIN_EINVAL, "POS_TABLE needs a table");
+    const size_t nw = (size_t)3 * d->C * d->C * 2, nb = (size_t)3 * d->C * 4;
+    if (overlaps(out, bytes, x, bytes) || overlaps(out, bytes, w_qkv, nw) || (b_qkv && overlaps(out, bytes, b_qkv, nb)))
+        return fail(SWIN_EINVAL, "out overlaps x, w_qkv or b_qkv");
+    p.out = out;
+    p.tau = tau; p.table = table;
+    swin::FusedArgs a{x, w_qkv, b_qkv};
+    return hip_status(swin::launch_attn_fused(p, a, (hipStream_t)stream), "swin_qkv_window_attn_fwd launch");
+}
+
 int swin_proj_post_norm(const void* o, const void* w, const float* b, const void* resid, const float* gamma,
                         const float* beta, float eps, void* y, int64_t T, int32_t C, int32_t dtype, void* stream)
 {

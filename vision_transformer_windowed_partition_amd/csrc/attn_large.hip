@@ -396,7 +396,34 @@ attn_large_kernel(AttnParams p, LargeLayout L)
     whole.v = (const __bf16*)(kv + L.NSP * 64);
     whole.s0 = 0;
     whole.nch = nch_all;
+    auto load_pair_q = [&](int r, u32x4 (&qr2)[NT]) {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            const int t = (wave + WAVES * (NT * r + i)) * 16 + li;
+            const bool ok = t < N;
+            const int tc = ok ? t : 0;
+            const int ri = qdiv(tc, L.inv_M), ci = tc - ri * M;
+            qr2[i] = load16(qr, masked(wp.wg.tok(ri, ci) + 16u * grp, ok));
+        }
+    };
     float kmax = 0.0f;
+    // ---- every load of the staging in flight first: keys (registers),
+    // values (LDS-DMA), the queries of the DOT + rotation norm test and the
+    // first pair of query tiles; the tables are set up meanwhile
+    if (!split) stage_issue(whole, (__bf16*)(kv + L.NSP * 64));
+    u32x4 qraw[SIM == SWIN_SIM_DOT && POS == SWIN_POS_ROPE2D ? QPW : 1];
+    if (SIM == SWIN_SIM_DOT && POS == SWIN_POS_ROPE2D && !split) {
+#pragma unroll
+        for (int j = 0; j < QPW; ++j) {
+            const int t = (wave + WAVES * j) * 16 + li;
+            const bool ok = t < N;
+            const int tc = ok ? t : 0;
+            const int ri = qdiv(tc, L.inv_M), ci = tc - ri * M;
+            qraw[j] = load16(qr, masked(wp.wg.tok(ri, ci) + 16u * grp, ok));
+        }
+    }
+    u32x4 qnext[NT];
+    load_pair_q(0, qnext);
     // ---- tables: bias (reversed so that consecutive keys read consecutive
     // floats, in log2 units, shifted by its max and, for COSINE, by 1/tau);
     // rotary cos / sin per local position, half and pair
@@ -439,7 +466,6 @@ attn_large_kernel(AttnParams p, LargeLayout L)
     }
     __syncthreads();
 
-    if (!split) stage_issue(whole, (__bf16*)(kv + L.NSP * 64));
     if (!split) {
         float k2 = stage_process(whole, (bf16x8*)kv, nullptr, false);
         // DOT: the window's largest key norm (Cauchy-Schwarz shift, split test)
@@ -451,15 +477,6 @@ attn_large_kernel(AttnParams p, LargeLayout L)
         // DOT with rotation: the largest query norm too, from this wave's tiles
         if (SIM == SWIN_SIM_DOT && POS == SWIN_POS_ROPE2D) {
             float q2 = 0.0f;
-            u32x4 qraw[QPW];
-#pragma unroll
-            for (int j = 0; j < QPW; ++j) {
-                const int t = (wave + WAVES * j) * 16 + li;
-                const bool ok = t < N;
-                const int tc = ok ? t : 0;
-                const int ri = qdiv(tc, L.inv_M), ci = tc - ri * M;
-                qraw[j] = load16(qr, masked(wp.wg.tok(ri, ci) + 16u * grp, ok));
-            }
 #pragma unroll
             for (int j = 0; j < QPW; ++j) {
                 float qv[8];
@@ -499,19 +516,11 @@ attn_large_kernel(AttnParams p, LargeLayout L)
     const int qhalf = POS == SWIN_POS_ROPE2D ? 1 : 0;
     // groups split by a region edge or by padded columns need per-key masks
     const bool partial = (wp.last_c && ((M - g.shift) & 7)) || (M & 7);
-    auto load_pair_q = [&](int r, u32x4 (&qr2)[NT]) {
-#pragma unroll
-        for (int i = 0; i < NT; ++i) {
-            const int t = (wave + WAVES * (NT * r + i)) * 16 + li;
-            const bool ok = t < N;
-            const int tc = ok ? t : 0;
-            const int ri = qdiv(tc, L.inv_M), ci = tc - ri * M;
-            qr2[i] = load16(qr, masked(wp.wg.tok(ri, ci) + 16u * grp, ok));
-        }
-    };
     for (int r = 0; r < L.rounds; ++r) {
         u32x4 qcur[NT];
-        load_pair_q(r, qcur);
+#pragma unroll
+        for (int i = 0; i < NT; ++i) qcur[i] = qnext[i];
+        if (r + 1 < L.rounds) load_pair_q(r + 1, qnext);
         Tile T[NT];
         int qt[NT];
         bool qv[NT];

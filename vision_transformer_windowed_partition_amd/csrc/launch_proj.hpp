@@ -1,5 +1,5 @@
 // Launch entries of the kernels either side of the attention and of its
-// alternatives (proj.hip, dwconv.hip, window_linear.hip), called by api.hip
+// alternatives (proj.hip, attn_fused.hip, dwconv.hip, window_linear.hip), called by api.hip
 // after the host-side validation.
 #pragma once
 
@@ -38,7 +38,17 @@ struct WlinArgs {
     const float* bias;         // heads x N, or nullptr
 };
 
+struct FusedArgs {
+    const void* x;             // (B, H, W, C) features
+    const void* w;             // 3C x C input-layer weight (rows q, k, v)
+    const float* b;            // 3C bias, or nullptr
+};
+
 bool proj_supported(int C);
+// window attention with the input layer fused in (attn_fused.hip): p holds
+// the geometry, modes, tau, table and out (p.q, p.k, p.v unused)
+bool attn_fused_supported(const AttnParams& p);
+hipError_t launch_attn_fused(const AttnParams& p, const FusedArgs& a, hipStream_t stream);
 bool dwconv_supported(int C, int dtype);
 hipError_t launch_dwconv_add(const DwconvArgs& a, hipStream_t stream);
 // p: geometry, dtype, v and out of the window mapping (launch.hpp)

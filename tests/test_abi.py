@@ -308,9 +308,10 @@ def test_kernel_query_names_the_dispatch(L):
 def test_backward_kernel_query_names_the_dispatch(L):
     """The backward's dispatch: bf16 windows of at most 256 key slots without
     rotary positions -> the small matrix-core kernel; other bf16 windows up to
-    M = 32 except cosine with rotary positions -> the large matrix-core
-    kernel; fp32 and the rest -> the vector-ALU kernel; d != 32 or M > 32 is
-    rejected."""
+    M = 32 whose rows fit in LDS (cosine with rotary positions also keeps the
+    remainders of its rotated rows, which fit up to M = 24) -> the large
+    matrix-core kernel; fp32 and the rest -> the vector-ALU kernel; d != 32
+    or M > 32 is rejected."""
     from vision_transformer_windowed_partition_amd import synth
     want = ["attn_bwd_kernel", "attn_bwd_small_kernel", "attn_bwd_small_kernel", "attn_bwd_large_kernel",
             "attn_bwd_large_kernel"]
@@ -321,7 +322,10 @@ def test_backward_kernel_query_names_the_dispatch(L):
         assert binding.swin_window_attn_bwd_kernel(d) == name, wl.name
     assert binding.swin_window_attn_bwd_kernel(_desc(M=12, H=24, W=24)) == "attn_bwd_small_kernel"
     assert binding.swin_window_attn_bwd_kernel(_desc(M=8, pos=2, sim=1)) == "attn_bwd_large_kernel"
-    assert binding.swin_window_attn_bwd_kernel(_desc(M=8, pos=2, sim=0)) == "attn_bwd_kernel"
+    assert binding.swin_window_attn_bwd_kernel(_desc(M=8, pos=2, sim=0)) == "attn_bwd_large_kernel"
+    assert binding.swin_window_attn_bwd_kernel(_desc(M=24, H=48, W=48, shift=12, pos=2, sim=0)) == \
+        "attn_bwd_large_kernel"
+    assert binding.swin_window_attn_bwd_kernel(_desc(M=32, H=32, W=32, shift=16, pos=2, sim=0)) == "attn_bwd_kernel"
     assert binding.swin_window_attn_bwd_kernel(_desc(M=8, dtype=0)) == "attn_bwd_kernel"
     assert L.swin_window_attn_bwd_kernel(ctypes.byref(_desc(M=48, H=48, W=48, shift=0))) is None
     assert "M=48" in binding.swin_last_error()

@@ -132,6 +132,27 @@ def test_backward_with_lse(case, dtype, lse_from):
         _check(f"{case} dtable", f64(got["dtable"]), ref["dtable"], dtype)
 
 
+@pytest.mark.parametrize("M,shift,tau", [(12, 6, (0.02, 0.5)), (24, 12, (0.3, 0.05)), (7, 3, (0.01, 0.004))])
+def test_backward_cosine_rope(M, shift, tau):
+    """Cosine attention with rotary positions on the matrix cores (the large
+    backward): the cosine is taken of the rotated operands, the score
+    products from hi + lo pairs; tau from the floor up.  Given the forward's
+    log-sum-exp and not."""
+    heads = 2
+    wl = synth.small(B=1, H=2 * M, W=2 * M, C=32 * heads, heads=heads, M=M, shift=shift, sim="cosine",
+                     pos="rope2d", dtype="bf16", hidden=64)
+    x = synth.make_inputs(wl, seed=40 + M)
+    x["tau"] = torch.tensor(tau)
+    g = gpu_inputs(x)
+    desc = binding.make_desc(B=wl.B, H=wl.H, W=wl.W, C=wl.C, heads=heads, M=M, shift=shift, sim="cosine",
+                             pos="rope2d", dtype=torch.bfloat16)
+    assert binding.swin_window_attn_bwd_kernel(desc) == "attn_bwd_large_kernel"
+    for lse_from in (None, "gpu"):
+        got, ref = _run(wl, x, g, synth.make_dout(wl), lse_from=lse_from)
+        for name in ("dq", "dk", "dv", "dtau"):
+            _check(f"M={M} tau={tau} lse={lse_from} {name}", f64(got[name]), ref[name], "bf16")
+
+
 def test_backward_tau_at_floor():
     """tau below its floor: the clamp passes no gradient to tau."""
     wl = synth.small(B=1, H=16, W=16, C=64, heads=2, M=8, shift=4, sim="cosine", pos="none", dtype="f32")

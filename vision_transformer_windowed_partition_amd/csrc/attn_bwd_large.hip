@@ -1,7 +1,7 @@
 // Backward of window attention on the gfx950 matrix cores for bf16 windows
 // too large for the small-window backward: up to 32 x 32 tokens, with the
-// rotary variant for DOT (FlashSwin abstract) and the bias table of the
-// SwinV2 card (eq. 3-4).
+// window-local rotary positions (FlashSwin abstract) and the bias table of
+// the SwinV2 card (eq. 3-4).
 //
 // Same gradient as the small-window backward (SwinV2 card eq. 1-2; with
 // logit_ij = (q~_i . k~_j) a_i c_j + b_ij, q~, k~ the rotated operands):
@@ -21,8 +21,12 @@
 //     tiles (k~, v fragments from memory): S = Q~ K~^T and dP = dout V^T with
 //     permuted query rows, then dV^T += dout^T P and H^T += Q~^T (dl a).
 // Rounding: for COSINE the operands are raw bf16 (exact) and the scales
-// multiply in fp32; rotated DOT operands are rounded to bf16 once, as in the
-// forward.  All products are v_mfma_f32_16x16x32_bf16, fp32 accumulation.
+// multiply in fp32; rotated operands are rounded to bf16 once, as in the
+// forward, and for COSINE with rotation the score products take hi + lo
+// pairs (the rotated rows' remainders in LDS, the tile's in registers), the
+// cosine's normalisation being taken on the rotated operand (rotation keeps
+// the norm).  All products are
+// v_mfma_f32_16x16x32_bf16, fp32 accumulation.
 #include "common.hpp"
 #include "lanes.hpp"
 #include "launch.hpp"
@@ -119,6 +123,10 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
     float* dtab = bias2 + tabsz;                               // [tabsz] reversed, natural units
     float* rtab = dtab + tabsz;                                // [M][2][8] (cos, sin)  (ROPE2D)
     float* red = rtab + (POS == SWIN_POS_ROPE2D ? M * 32 : 0); // [WAVES]
+    // COSINE with rotation: the remainders of the rounded rotated rows (K~,
+    // later Q~), 16-byte aligned after red
+    __bf16* rowL = (__bf16*)(((uintptr_t)(red + WAVES) + 15) & ~(uintptr_t)15);   // [NS][D]
+    constexpr bool CR = SIM == SWIN_SIM_COSINE && POS == SWIN_POS_ROPE2D;
 
     const WinPlace wp = place_window(g, win);
     const WinGeo& wg = wp.wg;
@@ -132,6 +140,11 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
     float tau = 1.0f;
     if (SIM == SWIN_SIM_COSINE) tau = fmaxf(p.tau[h], p.tau_min);
     const float inv_tau = 1.0f / tau;
+    // COSINE with rotation: rounded rotated operands would move a logit by
+    // up to 2^-8 / tau, which dtau (a sum that cancels over each query's
+    // keys) does not absorb, so the score products take hi + lo pairs (three
+    // products) from rowL and the query remainders
+    const bool split = CR;
     const bool needs_mask = wp.last_r || wp.last_c || SR != M || NS != M * SR;
     const int negrow = S * S;
     constexpr float RS32 = 0.17677669529663687f;              // 1/sqrt(32)
@@ -149,22 +162,25 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
             f[2 * e + 1] = x0 * si + x1 * co;
         }
     };
-    // inverse rotation of a lane's gradient channels 4 grp..+3 (half 0) and
-    // 16 + 4 grp..+3 (half 1): pairs k = 2 grp + m
-    auto unrot_lane = [&](float* g8, int r, int c) {
+    // rotation (sgn = 1) or its inverse (sgn = -1) of a lane's channels
+    // 4 grp..+3 (half 0) and 16 + 4 grp..+3 (half 1): pairs k = 2 grp + m
+    auto turn_lane = [&](float* g8, int r, int c, float sgn) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int pos = hh ? c : r;
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int k = 2 * grp + m;
-                const float co = rtab[((pos * 2 + hh) * 8 + k) * 2], si = -rtab[((pos * 2 + hh) * 8 + k) * 2 + 1];
+                const float co = rtab[((pos * 2 + hh) * 8 + k) * 2];
+                const float si = sgn * rtab[((pos * 2 + hh) * 8 + k) * 2 + 1];
                 const float x0 = g8[4 * hh + 2 * m], x1 = g8[4 * hh + 2 * m + 1];
                 g8[4 * hh + 2 * m] = x0 * co - x1 * si;
                 g8[4 * hh + 2 * m + 1] = x0 * si + x1 * co;
             }
         }
     };
+    auto unrot_lane = [&](float* g8, int r, int c) { turn_lane(g8, r, c, -1.0f); };
+    auto rot_lane = [&](float* g8, int r, int c) { turn_lane(g8, r, c, 1.0f); };
 
     // ---- tables
     if (POS == SWIN_POS_TABLE) {
@@ -212,7 +228,14 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
             for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
             ss = quad_sum(ss);
             if (in) {
-                rowstore(dst, s, pc, (POS == SWIN_POS_ROPE2D && rot) ? pack_bf16x8(f) : __builtin_bit_cast(bf16x8, x));
+                const bf16x8 hi = (POS == SWIN_POS_ROPE2D && rot) ? pack_bf16x8(f) : __builtin_bit_cast(bf16x8, x);
+                if (CR && split && rot) {
+                    float lo[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) lo[e] = f[e] - (float)hi[e];
+                    rowstore(rowL, s, pc, pack_bf16x8(lo));
+                }
+                rowstore(dst, s, pc, hi);
                 rowstore(dst2, s, pc, __builtin_bit_cast(bf16x8, x2));
                 if (norm_out && pc == 0)
                     norm_out[s] = cosine_scale ? 1.0f / fmaxf(sqrtf(ss), 1e-12f) : 1.0f;
@@ -266,6 +289,26 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
         unpack_bf16x8(load16(qr, qoffb), qv);
         if (POS == SWIN_POS_ROPE2D) rot8(qv, grp, ri, ci, 1.0f);
         const bf16x8 qf = pack_bf16x8(qv);
+        bf16x8 qf_lo = qf;
+        if (CR && split) {
+            float lo[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) lo[e] = qv[e] - (float)qf[e];
+            qf_lo = pack_bf16x8(lo);
+        }
+        // S^T for the 8 keys of this lane's group in chunk c (hi + lo when split)
+        auto scores = [&](int sA, f32x4& sa, f32x4& sb) {
+            const bf16x8 ka = rowfrag(rowA, sA, grp), kb = rowfrag(rowA, sA + 4, grp);
+            const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+            sa = mfma(ka, qf, z);
+            sb = mfma(kb, qf, z);
+            if (CR && split) {
+                sa = mfma(rowfrag(rowL, sA, grp), qf, sa);
+                sb = mfma(rowfrag(rowL, sA + 4, grp), qf, sb);
+                sa = mfma(ka, qf_lo, sa);
+                sb = mfma(kb, qf_lo, sb);
+            }
+        };
         const bf16x8 gfr = __builtin_bit_cast(bf16x8, load16(gr, qoffb));
         const float qs = qsc[qs_slot], Dq = dd[qs_slot];
         const int qoff = (M - 1 - ri) * S + (M - 1 - ci);
@@ -279,9 +322,8 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
         const int nch0 = p.lse ? 0 : nch;
         for (int c = 0; c < nch0; ++c) {
             const int sA = 32 * c + 8 * (li >> 2) + (li & 3);
-            const bf16x8 ka = rowfrag(rowA, sA, grp), kb = rowfrag(rowA, sA + 4, grp);
-            const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-            const f32x4 sa = mfma(ka, qf, z), sb = mfma(kb, qf, z);
+            f32x4 sa, sb;
+            scores(sA, sa, sb);
             const f32x4 k0 = *(const f32x4*)(ksc + 32 * c + 8 * grp);
             const f32x4 k1 = *(const f32x4*)(ksc + 32 * c + 8 * grp + 4);
             const int gam = 4 * c + grp, rj = qdiv(gam, L.inv_GPR), cj0 = 8 * (gam - rj * L.GPR);
@@ -320,10 +362,10 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
         f32x4 G0 = {0.0f, 0.0f, 0.0f, 0.0f}, G1 = G0;
         for (int c = 0; c < nch; ++c) {
             const int sA = 32 * c + 8 * (li >> 2) + (li & 3);
-            const bf16x8 ka = rowfrag(rowA, sA, grp), kb = rowfrag(rowA, sA + 4, grp);
             const bf16x8 va = rowfrag(rowB, sA, grp), vb = rowfrag(rowB, sA + 4, grp);
             const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-            const f32x4 sa = mfma(ka, qf, z), sb = mfma(kb, qf, z);
+            f32x4 sa, sb;
+            scores(sA, sa, sb);
             const f32x4 pa = mfma(va, gfr, z), pb = mfma(vb, gfr, z);
             const f32x4 k0 = *(const f32x4*)(ksc + 32 * c + 8 * grp);
             const f32x4 k1 = *(const f32x4*)(ksc + 32 * c + 8 * grp + 4);
@@ -384,6 +426,7 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
             float q8[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) { q8[e] = (float)qa4[e]; q8[e + 4] = (float)qb4[e]; }
+            if (CR) rot_lane(q8, ri, ci);                     // the normalised operand is the rotated q
             float qg = 0.0f, qq = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) { qg = fmaf(q8[e], g8[e], qg); qq = fmaf(q8[e], q8[e], qq); }
@@ -418,6 +461,13 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
         unpack_bf16x8(load16(kr, koffb), kvv);
         if (POS == SWIN_POS_ROPE2D) rot8(kvv, grp, rjc, cjc, 1.0f);
         const bf16x8 kB = pack_bf16x8(kvv);
+        bf16x8 kB_lo = kB;
+        if (CR && split) {
+            float lo[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) lo[e] = kvv[e] - (float)kB[e];
+            kB_lo = pack_bf16x8(lo);
+        }
         const bf16x8 vB = __builtin_bit_cast(bf16x8, load16(vr, koffb));
         const float cj_s = ksc[sk];
         int rlo = 0, rhi = M, clo = 0, chi = M;
@@ -431,7 +481,13 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
             const bf16x8 qa = rowfrag(rowA, sA, grp), qb = rowfrag(rowA, sA + 4, grp);
             const bf16x8 ga = rowfrag(rowB, sA, grp), gb = rowfrag(rowB, sA + 4, grp);
             const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-            const f32x4 sa = mfma(qa, kB, z), sb = mfma(qb, kB, z);
+            f32x4 sa = mfma(qa, kB, z), sb = mfma(qb, kB, z);
+            if (CR && split) {
+                sa = mfma(rowfrag(rowL, sA, grp), kB, sa);
+                sb = mfma(rowfrag(rowL, sA + 4, grp), kB, sb);
+                sa = mfma(qa, kB_lo, sa);
+                sb = mfma(qb, kB_lo, sb);
+            }
             const f32x4 pa = mfma(ga, vB, z), pb = mfma(gb, vB, z);
             const int qs0 = 32 * c + 8 * grp;
             const f32x4 qsA = *(const f32x4*)(qsc + qs0), qsB = *(const f32x4*)(qsc + qs0 + 4);
@@ -470,6 +526,7 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
             float k8[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) { k8[e] = (float)ka4[e]; k8[e + 4] = (float)kb4[e]; }
+            if (CR) rot_lane(k8, rjc, cjc);
             float kh = 0.0f, kk = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) { kh = fmaf(k8[e], h8[e], kh); kk = fmaf(k8[e], k8[e], kk); }
@@ -509,6 +566,7 @@ size_t lds_bytes(const AttnParams& p, int NS)
     size_t b = (size_t)NS * D * 2 * 2 + (size_t)4 * NS * 4 + (size_t)WAVES * 4 + 64;
     if (p.pos == SWIN_POS_TABLE) b += (size_t)2 * ((S * S + 8 + 3) / 4 * 4) * 4;
     if (p.pos == SWIN_POS_ROPE2D) b += (size_t)p.g.M * 32 * 4;
+    if (p.sim == SWIN_SIM_COSINE && p.pos == SWIN_POS_ROPE2D) b += 16 + (size_t)NS * D * 2;   // remainder rows
     return b;
 }
 
@@ -537,7 +595,6 @@ bool attn_bwd_large_supported(const AttnParams& p)
 {
     const Geometry& g = p.g;
     return p.dtype == SWIN_DT_BF16 && g.d == D && g.M <= 32 &&
-           !(p.sim == SWIN_SIM_COSINE && p.pos == SWIN_POS_ROPE2D) &&
            lds_bytes(p, slots_of(p)) <= 160 * 1024 &&
            (int64_t)g.H * g.W * g.C * 2 < ((int64_t)1 << 31) && (int64_t)g.W * g.C * 2 < ((int64_t)1 << 24);
 }
@@ -561,6 +618,7 @@ hipError_t launch_attn_bwd_large(const AttnParams& p, const void* out, const voi
     const size_t lds = lds_bytes(p, L.NS);
     if (p.sim == SWIN_SIM_COSINE) {
         if (p.pos == SWIN_POS_TABLE) return launch_large<SWIN_SIM_COSINE, SWIN_POS_TABLE>(p, a, L, lds, stream);
+        if (p.pos == SWIN_POS_ROPE2D) return launch_large<SWIN_SIM_COSINE, SWIN_POS_ROPE2D>(p, a, L, lds, stream);
         return launch_large<SWIN_SIM_COSINE, SWIN_POS_NONE>(p, a, L, lds, stream);
     }
     if (p.pos == SWIN_POS_TABLE) return launch_large<SWIN_SIM_DOT, SWIN_POS_TABLE>(p, a, L, lds, stream);

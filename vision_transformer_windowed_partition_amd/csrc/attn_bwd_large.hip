@@ -10,7 +10,8 @@
 //   COSINE: dq_i = a_i (G_i - q_i (q_i . G_i)/||q_i||^2), dk likewise with c_j;
 //   DOT:    dq~ = G / sqrt(d) ... folded: a = c = 1/sqrt(d); ROPE2D: dq = R^T dq~.
 //   dtable[offset(i, j)] += dl_ij, dtau from sum dl_ij cos_ij.
-// One workgroup of eight wavefronts per window-head, in two stages of LDS:
+// One workgroup of sixteen wavefronts (four per SIMD) per window-head, in two
+// stages of LDS:
 //   stage 1: K~ and V rows of every key slot (64-byte rows, XOR-swizzled
 //     16-byte pieces), K rotated in fp32 and rounded once; per-slot scales
 //     and D_i = dout_i . out_i.  Query-major passes over each wavefront's
@@ -40,7 +41,10 @@ namespace {
 using namespace tio;
 using namespace lanes;
 
-constexpr int WAVES = 8;
+#ifndef LBWD_WAVES
+#define LBWD_WAVES 16
+#endif
+constexpr int WAVES = LBWD_WAVES;
 constexpr int NTHR = WAVES * 64;
 
 struct LargeBwdLayout {

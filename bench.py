@@ -178,9 +178,10 @@ def main(argv=None) -> int:
     ap.add_argument("--linmapper", action="store_true",
                     help="time LinMapper's in-window linear mapping (swin_window_linear) on the "
                          "workload's values instead of the attention")
-    ap.add_argument("--video", action="store_true",
-                    help="time video (3D) window attention instead: swin_window_attn3d_fwd on the video "
-                         "workload (16^2 x 8 windows), its table from swin_cpb_table3d")
+    ap.add_argument("--video", type=int, nargs="?", const=0, default=None, metavar="IDX",
+                    help="time video (3D) window attention instead: swin_window_attn3d_fwd on "
+                         "synth.VIDEO_WORKLOADS[IDX] (0: 256^2 x 8 frames, 16^2 x 8 windows; 1: 320^2 x 8 "
+                         "frames, 20^2 x 8 windows), its table from swin_cpb_table3d")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run copies of known size for HBM-counter calibration: y = -x over "
                          "2^28 fp32 (whole lines), then an interleaved window gather and its "
@@ -196,7 +197,7 @@ def main(argv=None) -> int:
 
     from vision_transformer_windowed_partition_amd import binding, synth
 
-    if args.video:
+    if args.video is not None:
         return bench_video(args)
     wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -645,7 +646,7 @@ def bench_video(args) -> int:
 
     from vision_transformer_windowed_partition_amd import binding, synth
 
-    wl = synth.VIDEO_WORKLOADS[0]
+    wl = synth.VIDEO_WORKLOADS[args.video]
     dev = torch.device("cuda:0")
     x = synth.make_video_inputs(wl)
     set_bytes = wl.bytes

@@ -251,7 +251,7 @@ int swin_cpb_table3d(int32_t Mt, int32_t M, int32_t heads, int32_t hidden, const
  * bias is swin_cpb_table3d's table, indexed by the offsets (dt, dy, dx).
  * q, k, v, out: device tensors of desc->dtype, 16-byte aligned, out not
  * overlapping q, k or v; tau: heads fp32 (COSINE); table: as written by
- * swin_cpb_table3d (TABLE).  bf16 with M = 8 or 16 runs on the matrix cores
+ * swin_cpb_table3d (TABLE).  bf16 with M <= 22 runs on the matrix cores
  * (the products on bf16 operands with fp32 accumulation, COSINE's unit q and
  * k scaled by 1/tau rounded to bf16 unless tau < 0.1, the weights rounded to
  * bf16 before P V, softmax in fp32 with a running maximum); everything else

@@ -28,8 +28,14 @@ CASES = [
     (8, 32, 32, 8, 16, 0, 8, "cyclic", "cosine", "table"),    # the pages' 16^2 x 8 windows (2048 tokens)
     (6, 16, 16, 3, 8, 1, 4, "cyclic", "cosine", "table"),     # 3 query frames on 4 wavefronts, every axis shifted
     (4, 32, 32, 2, 16, 1, 8, "cyclic", "dot", "none"),
+    (4, 40, 40, 2, 20, 1, 10, "cyclic", "cosine", "table"),   # 20^2 x 2 windows: 8 wavefronts, 24-slot key rows
+    (2, 22, 44, 2, 22, 0, 11, "cyclic", "dot", "table"),      # the largest matrix-core window
+    (4, 24, 24, 2, 12, 1, 6, "cyclic", "cosine", "table"),    # 12-key rows padded to 16 slots
+    (2, 34, 34, 1, 17, 0, 8, "cyclic", "cosine", "none"),     # odd rows in 24 slots, one frame a window
+    (4, 10, 15, 2, 5, 1, 2, "cyclic", "dot", "table"),        # 5-key rows padded to 8 slots
+    (2, 36, 36, 2, 18, 0, 0, "interleaved", "cosine", "table"),
 ]
-# bf16 with M = 8 or 16 runs on the matrix cores, the rest on the vector ALUs
+# bf16 runs on the matrix cores (M <= 22), fp32 on the vector ALUs
 
 
 def _compare(got, ref, dtype, what):
@@ -67,7 +73,7 @@ def test_video_parity(case, dtype):
     _compare(f64(out), ref, dtype, str(case))
 
 
-@pytest.mark.parametrize("M", [8, 16])
+@pytest.mark.parametrize("M", [8, 16, 20])
 def test_video_small_tau(M):
     """COSINE with tau below 0.1 for one head: the matrix-core kernel keeps
     raw k with 1/||k|| in fp32 instead of rounding k / ||k|| / tau."""
@@ -89,7 +95,9 @@ def test_video_kernel_choice():
     assert binding.swin_window_attn3d_kernel(d(), 8, 8) == "attn_video_mfma_kernel"
     assert binding.swin_window_attn3d_kernel(d(M=8, shift=4), 8, 4) == "attn_video_mfma_kernel"
     assert binding.swin_window_attn3d_kernel(d(dtype=torch.float32), 8, 8) == "attn_video_kernel"
-    assert binding.swin_window_attn3d_kernel(d(M=4, shift=2), 8, 8) == "attn_video_kernel"
+    assert binding.swin_window_attn3d_kernel(d(M=4, shift=2), 8, 8) == "attn_video_mfma_kernel"
+    assert binding.swin_window_attn3d_kernel(d(H=40, W=40, M=20, shift=10), 8, 8) == "attn_video_mfma_kernel"
+    assert binding.swin_window_attn3d_kernel(d(H=46, W=46, M=23, shift=11), 2, 2) == "attn_video_kernel"
 
 
 def test_video_one_frame_windows_match_2d():
@@ -121,10 +129,12 @@ def test_cpb_table3d(Mt, M, heads, hidden):
                                atol=1e-4)
 
 
-def test_video_workload_sampled():
-    """The video workload at full size (the launch the bench times), its
+@pytest.mark.parametrize("idx", range(len(synth.VIDEO_WORKLOADS)),
+                         ids=[w.name for w in synth.VIDEO_WORKLOADS])
+def test_video_workload_sampled(idx):
+    """The video workloads at full size (the launch the bench times), the
     table from swin_cpb_table3d; the oracle computes sampled windows."""
-    wl = synth.VIDEO_WORKLOADS[0]
+    wl = synth.VIDEO_WORKLOADS[idx]
     x = synth.make_video_inputs(wl)
     g = {k: v.to(DEV) for k, v in x.items()}
     table = binding.swin_cpb_table3d(wl.Mt, wl.M, g["w1"], g["b1"], g["w2"], g["b2"])
@@ -146,7 +156,7 @@ def test_video_workload_sampled():
 
 def _random_case(seed):
     rng = np.random.default_rng(seed)
-    M = int(rng.choice([2, 4, 5, 8, 8, 16, 16]))
+    M = int(rng.choice([2, 4, 5, 8, 8, 11, 16, 16, 19, 20]))
     Mt = int(rng.choice([1, 2, 3, 4]))
     nt, nr, nc = int(rng.integers(1, 3)), int(rng.integers(1, 3)), int(rng.integers(1, 3))
     part = "interleaved" if rng.random() < 0.3 else "cyclic"
@@ -160,8 +170,8 @@ def _random_case(seed):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("seed", range(12))
 def test_video_random(seed, dtype):
-    """Seeded random video geometries (both kernels for bf16: M = 8, 16 on the
-    matrix cores, others on the vector ALUs)."""
+    """Seeded random video geometries (bf16 on the matrix cores, fp32 on the
+    vector ALUs)."""
     case = _random_case(seed)
     T, H, W, Mt, M, st, s, part, sim, pos = case
     q, k, v, tau, table = _inputs(case, dtype, seed=500 + seed, B=2)

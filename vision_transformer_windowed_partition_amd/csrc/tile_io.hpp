@@ -50,17 +50,25 @@ __device__ __forceinline__ RawRsrc raw_rsrc(const void* base, uint32_t bytes)
     const uint64_t a = (uint64_t)(uintptr_t)base;
     return RawRsrc{u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u}};
 }
-__device__ __forceinline__ void dma16(const RawRsrc& r, const void* lds, uint32_t off)
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+// lds: the LDS byte address (wave-uniform)
+__device__ __forceinline__ void dma16_at(const RawRsrc& r, uint32_t lds, uint32_t off)
 {
     // the resource and the LDS base are wave-uniform: pin them to scalar
     // registers, as the asm operands require
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
     u32x4 w;
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_readfirstlane(r.w[i]);
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :: "s"(m0), "v"(off), "s"(w) : "memory", "m0");
+}
+__device__ __forceinline__ void dma16(const RawRsrc& r, const void* lds, uint32_t off)
+{
+    dma16_at(r, lds_addr(lds), off);
 }
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

@@ -205,11 +205,15 @@ class VideoWorkload:
         return 4 * self.tokens * self.C * self.elem_size
 
 
-# The SwinV2 video fine-tuning shape (appendix A2: 256^2 x 8 frames, 16^2 x 8
-# windows) at the first stage of a Tiny backbone (4 x 4 patches: a 64 x 64
-# grid per frame, C = 96, 3 heads), 8 clips.
+# The SwinV2 video fine-tuning shapes (appendix A2, Kinetics-400 stages 1
+# and 2: 256^2 x 8 frames with 16^2 x 8 windows, 320^2 x 8 frames with
+# 20^2 x 8 windows) at the first stage of a Tiny backbone (4 x 4 patches: a
+# 64 x 64 or 80 x 80 grid per frame, C = 96, 3 heads), 8 clips, the spatial
+# shift M/2 of a shifted block.
 VIDEO_WORKLOADS = [
     VideoWorkload("swinv2t_k400_8x256px_w16x8", 8, 8, 64, 64, 96, 3, 8, 16, 0, 8, "cyclic", "cosine", "table",
+                  "bf16"),
+    VideoWorkload("swinv2t_k400_8x320px_w20x8", 8, 8, 80, 80, 96, 3, 8, 20, 0, 10, "cyclic", "cosine", "table",
                   "bf16"),
 ]
 

@@ -103,7 +103,10 @@ __device__ __forceinline__ void slot_rc(int s, int& r, int& c)
     c = 8 * (gam % GPR) + (s & 7);
 }
 
-template <int SIM, int POS, int NCH, int QW>
+template <bool B> struct Flag { static constexpr bool value = B; };
+
+// DIAG: M = 16 with a table (the bias gradient by diagonal sums)
+template <int SIM, int POS, int NCH, int QW, bool DIAG>
 __global__ void __launch_bounds__(256)
 attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
 {
@@ -277,6 +280,7 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             int rlo = 0, rhi = M, clo = 0, chi = M;
             if (wp.last_r) { if (ri < M - g.shift) rhi = M - g.shift; else rlo = M - g.shift; }
             if (wp.last_c) { if (ci < M - g.shift) chi = M - g.shift; else clo = M - g.shift; }
+            const uint32_t cmask = (((1u << chi) - 1u) & ~((1u << clo) - 1u));
             float m = -INFINITY, l = 0.0f;
 #pragma unroll 2
             for (int c = 0; c < NCH; ++c) {
@@ -287,15 +291,15 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                 const f32x4 k0 = *(const f32x4*)(ksc + 32 * c + 8 * grp);
                 const f32x4 k1 = *(const f32x4*)(ksc + 32 * c + 8 * grp + 4);
                 const int gam = 4 * c + grp, rj = gam / GPR, cj0 = 8 * (gam % GPR);
+                const uint32_t bits = !needs_mask ? 0xffu
+                                    : tv && rj >= rlo && rj < rhi && rj < M ? (cmask >> cj0) & 0xffu : 0u;
                 float x[8];
                 float cm = -INFINITY;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float sv = e < 4 ? sa[e] : sb[e - 4];
                     const float kv = e < 4 ? k0[e] : k1[e - 4];
-                    const int cj = cj0 + e;
-                    const bool ok = !needs_mask || (tv && rj >= rlo && rj < rhi && cj >= clo && cj < chi &&
-                                                    rj < M && cj < M);
+                    const bool ok = ((bits >> e) & 1u) != 0u;
                     float b = 0.0f;
                     if (POS == SWIN_POS_TABLE) b = bias2[ok ? qoff + (4 / GPR) * c * S + e : negrow];
                     x[e] = ok ? fmaf(sv * qs, kv, b) : -INFINITY;
@@ -320,12 +324,13 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
     const Rsrc dqr = make_rsrc((const uint16_t*)a.dq + wp.base + h * D, bytes);
     const Rsrc dkr = make_rsrc((const uint16_t*)a.dk + wp.base + h * D, bytes);
     const Rsrc dvr = make_rsrc((const uint16_t*)a.dv + wp.base + h * D, bytes);
-    if (active) {
-        // ---- pass B: dq of this wave's queries (query-major)
-        const bool diag = M == 16;
+    // ---- pass B: dq of this wave's queries (query-major); MASK: the
+    // window has shift regions or padded slots (else every pair counts)
+    auto pass_b = [&](auto mflag) {
+        constexpr bool MASK = decltype(mflag)::value;
         for (int t0 = rank; t0 < L.NQT; t0 += QW) {
             const int t = t0 * 16 + li;
-            const bool tv = t < N;
+            const bool tv = !MASK || t < N;
             const int tt = tv ? t : 0;
             const int ri = qdiv(tt, L.inv_M), ci = tt - ri * M;
             const int qs_slot = ri * 8 * GPR + ci;
@@ -336,6 +341,7 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             int rlo = 0, rhi = M, clo = 0, chi = M;
             if (wp.last_r) { if (ri < M - g.shift) rhi = M - g.shift; else rlo = M - g.shift; }
             if (wp.last_c) { if (ci < M - g.shift) chi = M - g.shift; else clo = M - g.shift; }
+            const uint32_t cmask = (((1u << chi) - 1u) & ~((1u << clo) - 1u));
             f32x4 G0 = {0.0f, 0.0f, 0.0f, 0.0f}, G1 = G0;
 #pragma unroll 2
             for (int c = 0; c < NCH; ++c) {
@@ -349,31 +355,34 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                 const f32x4 k1 = *(const f32x4*)(ksc + 32 * c + 8 * grp + 4);
                 const int gam = 4 * c + grp, rj = gam / GPR, cj0 = 8 * (gam % GPR);
                 const int boff = qoff + (4 / GPR) * c * S;
+                // allowed keys of this lane's 8-key group (bit e: key column cj0 + e)
+                const uint32_t bits = !MASK ? 0xffu : tv && rj >= rlo && rj < rhi && rj < M ? (cmask >> cj0) & 0xffu
+                                                                                             : 0u;
                 float ds[8], dlv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float sv = e < 4 ? sa[e] : sb[e - 4];
                     const float dpv = e < 4 ? pa[e] : pb[e - 4];
                     const float kv = e < 4 ? k0[e] : k1[e - 4];
-                    const int cj = cj0 + e;
-                    const bool ok = tv && (!needs_mask || (rj >= rlo && rj < rhi && cj >= clo && cj < chi &&
-                                                           rj < M && cj < M));
+                    const bool ok = !MASK || ((bits >> e) & 1u) != 0u;
                     float b = 0.0f;
-                    if (POS == SWIN_POS_TABLE) b = bias2[ok ? boff + e : negrow];
+                    if (POS == SWIN_POS_TABLE) b = bias2[ok ? boff + e : negrow];     // -inf when excluded
                     const float xs = sv * qs * kv;                 // log2 units, without the bias
-                    const float pr = ok ? __builtin_amdgcn_exp2f(xs + b - lq) : 0.0f;
+                    float arg = xs + b - lq;
+                    if (POS != SWIN_POS_TABLE && MASK) arg = ok ? arg : -INFINITY;
+                    const float pr = __builtin_amdgcn_exp2f(arg);
                     const float dl = pr * (dpv - Dq);
                     ds[e] = dl * (SIM == SWIN_SIM_COSINE ? kv : 0.17677669529663687f);
                     dlv[e] = dl;
                     if (SIM == SWIN_SIM_COSINE) dtau_acc = fmaf(dl, xs, dtau_acc);
-                    if (POS == SWIN_POS_TABLE && a.dtable && !diag && ok) atomicAdd(&dtab[boff + e], dl);
+                    if (POS == SWIN_POS_TABLE && !DIAG && a.dtable && ok) atomicAdd(&dtab[boff + e], dl);
                 }
-                if (POS == SWIN_POS_TABLE && a.dtable && diag) {
+                if (POS == SWIN_POS_TABLE && DIAG && a.dtable) {
                     // M == 16: the tile is one window row, lane li its column li,
                     // so (lane li, element e) lands at boff(0) - li + e.  Row sums
                     // along those diagonals: lane li gathers d = -li from lanes
                     // li + e (element e) and, for li = 1..7, d = 8 - li from lanes
-                    // li - 8 + e; masked pairs carry dl = 0.
+                    // li - 8 + e; excluded pairs carry dl = 0.
                     float A = dlv[0] + row_shl<1>(dlv[1]) + row_shl<2>(dlv[2]) + row_shl<3>(dlv[3]) +
                               row_shl<4>(dlv[4]) + row_shl<5>(dlv[5]) + row_shl<6>(dlv[6]) + row_shl<7>(dlv[7]);
                     float B = row_shr<8>(dlv[0]) + row_shr<7>(dlv[1]) + row_shr<6>(dlv[2]) + row_shr<5>(dlv[3]) +
@@ -428,6 +437,10 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             store8(dqr, off, pack_bf16x4(dqv[0], dqv[1], dqv[2], dqv[3]));
             store8(dqr, off + 32u, pack_bf16x4(dqv[4], dqv[5], dqv[6], dqv[7]));
         }
+    };
+    if (active) {
+        if (needs_mask) pass_b(Flag<true>{});
+        else pass_b(Flag<false>{});
     }
     if (PHASED) {
         // ---- Q and dout rows replace K and V
@@ -436,8 +449,9 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
         vm_wait_all();
         __syncthreads();
     }
-    if (active) {
-        // ---- pass A: dk, dv of this wave's 16-key tiles (key-major)
+    // ---- pass A: dk, dv of this wave's 16-key tiles (key-major)
+    auto pass_a = [&](auto mflag) {
+        constexpr bool MASK = decltype(mflag)::value;
         const int nkt = (L.NSP + 15) / 16;
         for (int kt = rank; kt < nkt; kt += QW) {
             const int sk = 16 * kt + li;                   // this lane's key slot
@@ -481,10 +495,12 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                     const float qv = e < 4 ? qsA[e] : qsB[e - 4];
                     const float lv = e < 4 ? lA[e] : lB[e - 4];
                     const float dv_ = e < 4 ? dA[e] : dB[e - 4];
-                    const bool ok = ((cbits >> e) & 1u) != 0u;
+                    const bool ok = !MASK || ((cbits >> e) & 1u) != 0u;
                     float b = 0.0f;
                     if (POS == SWIN_POS_TABLE) b = bias2[ok ? rev0 - e : negrow];
-                    const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(sv * qv, cj_s, b) - lv) : 0.0f;
+                    // (the select also covers padded query slots, whose statistics are unset)
+                    const float arg = fmaf(sv * qv, cj_s, b) - lv;
+                    const float pr = __builtin_amdgcn_exp2f(!MASK || ok ? arg : -INFINITY);
                     pp[e] = pr;
                     const float dl = pr * (dpv - dv_);
                     dsa[e] = dl * (SIM == SWIN_SIM_COSINE ? qv * (1.0f / kLog2e) : 0.17677669529663687f);
@@ -523,6 +539,10 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             store8(dvr, off, pack_bf16x4(V0[0], V0[1], V0[2], V0[3]));
             store8(dvr, off + 32u, pack_bf16x4(V1[0], V1[1], V1[2], V1[3]));
         }
+    };
+    if (active) {
+        if (needs_mask) pass_a(Flag<true>{});
+        else pass_a(Flag<false>{});
         if (SIM == SWIN_SIM_COSINE && a.dtau) {
             const float s = wave_reduce<Op::Sum>(dtau_acc);
             if (lane == 0) red[wave] = s;
@@ -546,9 +566,10 @@ template <int SIM, int POS>
 hipError_t launch_nch(const AttnParams& p, const BwdSmallArgs& a, const BwdLayout& L, int nch, int grid,
                       size_t lds, hipStream_t s)
 {
-    auto* fn = nch <= 2 ? attn_bwd_small_kernel<SIM, POS, 2, 1>
-             : nch <= 6 ? attn_bwd_small_kernel<SIM, POS, 6, 4>
-                        : attn_bwd_small_kernel<SIM, POS, 8, 4>;
+    auto* fn = nch <= 2 ? attn_bwd_small_kernel<SIM, POS, 2, 1, false>
+             : nch <= 6 ? attn_bwd_small_kernel<SIM, POS, 6, 4, false>
+             : p.g.M == 16 && POS == SWIN_POS_TABLE ? attn_bwd_small_kernel<SIM, POS, 8, 4, true>
+                        : attn_bwd_small_kernel<SIM, POS, 8, 4, false>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;

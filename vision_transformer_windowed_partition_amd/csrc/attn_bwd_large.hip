@@ -9,7 +9,8 @@
 //   G_i = sum_j dl_ij c_j k~_j,  H_j = sum_i dl_ij a_i q~_i,
 //   COSINE: dq_i = a_i (G_i - q_i (q_i . G_i)/||q_i||^2), dk likewise with c_j;
 //   DOT:    dq~ = G / sqrt(d) ... folded: a = c = 1/sqrt(d); ROPE2D: dq = R^T dq~.
-//   dtable[offset(i, j)] += dl_ij, dtau from sum dl_ij cos_ij.
+//   dtable[offset(i, j)] += dl_ij (summed per workgroup in LDS as 64-bit
+//   fixed point), dtau from sum dl_ij cos_ij.
 // One workgroup of sixteen wavefronts (four per SIMD) per window-head, in two
 // stages of LDS:
 //   stage 1: K~ and V rows of every key slot (64-byte rows, XOR-swizzled
@@ -29,6 +30,7 @@
 // the norm).  All products are
 // v_mfma_f32_16x16x32_bf16, fp32 accumulation.
 #include "common.hpp"
+#include "fixed_sum.hpp"
 #include "lanes.hpp"
 #include "launch.hpp"
 #include "launch_bwd.hpp"
@@ -124,8 +126,9 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
     float* lse = qsc + NS;                                     // [NS]
     float* dd = lse + NS;                                      // [NS] D_i
     float* bias2 = dd + NS;                                    // [tabsz] reversed, log2 units
-    float* dtab = bias2 + tabsz;                               // [tabsz] reversed, natural units
-    float* rtab = dtab + tabsz;                                // [M][2][8] (cos, sin)  (ROPE2D)
+    // [tabsz] reversed, natural units, 64-bit fixed point
+    fixed::acc_t* dtab = (fixed::acc_t*)(bias2 + tabsz);
+    float* rtab = (float*)(dtab + tabsz);                      // [M][2][8] (cos, sin)  (ROPE2D)
     float* red = rtab + (POS == SWIN_POS_ROPE2D ? M * 32 : 0); // [WAVES]
     // COSINE with rotation: the remainders of the rounded rotated rows (K~,
     // later Q~), 16-byte aligned after red
@@ -190,7 +193,7 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
     if (POS == SWIN_POS_TABLE) {
         for (int i = tid; i < S * S; i += NTHR) {
             bias2[S * S - 1 - i] = p.table[(size_t)i * g.heads + h] * kLog2e;
-            dtab[i] = 0.0f;
+            dtab[i] = 0ull;
         }
         if (tid < 8) bias2[S * S + tid] = -INFINITY;
     }
@@ -319,6 +322,11 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
         int rlo = 0, rhi = M, clo = 0, chi = M;
         if (wp.last_r) { if (ri < M - g.shift) rhi = M - g.shift; else rlo = M - g.shift; }
         if (wp.last_c) { if (ci < M - g.shift) chi = M - g.shift; else clo = M - g.shift; }
+        // allowed key columns of this query, and those of a lane's 8-key group
+        const uint32_t cmask = (chi >= 32 ? 0xffffffffu : (1u << chi) - 1u) & ~((1u << clo) - 1u);
+        auto group_bits = [&](int rj, int cj0) -> uint32_t {
+            return !needs_mask ? 0xffu : tv && rj >= rlo && rj < rhi && rj < M ? (cmask >> cj0) & 0xffu : 0u;
+        };
 
         // pass 0: running maximum and sum, unless the forward's log-sum-exp
         // is given (natural log, to log2 units)
@@ -332,13 +340,13 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
             const f32x4 k1 = *(const f32x4*)(ksc + 32 * c + 8 * grp + 4);
             const int gam = 4 * c + grp, rj = qdiv(gam, L.inv_GPR), cj0 = 8 * (gam - rj * L.GPR);
             const int boff = qoff + rj * S + cj0;
+            const uint32_t bits = group_bits(rj, cj0);
             float x[8], cm = -INFINITY;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float sv = e < 4 ? sa[e] : sb[e - 4];
                 const float kv = e < 4 ? k0[e] : k1[e - 4];
-                const int cj = cj0 + e;
-                const bool ok = !needs_mask || (tv && rj >= rlo && rj < rhi && cj >= clo && cj < chi && rj < M && cj < M);
+                const bool ok = ((bits >> e) & 1u) != 0u;
                 float b = 0.0f;
                 if (POS == SWIN_POS_TABLE) b = bias2[ok ? boff + e : negrow];
                 x[e] = ok ? fmaf(sv * qs, kv, b) : -INFINITY;
@@ -375,23 +383,23 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
             const f32x4 k1 = *(const f32x4*)(ksc + 32 * c + 8 * grp + 4);
             const int gam = 4 * c + grp, rj = qdiv(gam, L.inv_GPR), cj0 = 8 * (gam - rj * L.GPR);
             const int boff = qoff + rj * S + cj0;
+            const uint32_t bits = tv ? group_bits(rj, cj0) : 0u;
             float ds[8], dlv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float sv = e < 4 ? sa[e] : sb[e - 4];
                 const float dpv = e < 4 ? pa[e] : pb[e - 4];
                 const float kv = e < 4 ? k0[e] : k1[e - 4];
-                const int cj = cj0 + e;
-                const bool ok = tv && (!needs_mask || (rj >= rlo && rj < rhi && cj >= clo && cj < chi && rj < M && cj < M));
+                const bool ok = ((bits >> e) & 1u) != 0u;
                 float b = 0.0f;
                 if (POS == SWIN_POS_TABLE) b = bias2[ok ? boff + e : negrow];
                 const float xs = sv * qs * kv;
-                const float pr = ok ? __builtin_amdgcn_exp2f(xs + b - lq) : 0.0f;
+                const float pr = __builtin_amdgcn_exp2f(ok ? xs + b - lq : -INFINITY);
                 const float dl = pr * (dpv - Dq);
                 ds[e] = dl * (SIM == SWIN_SIM_COSINE ? kv : RS32);
                 dlv[e] = dl;
                 if (SIM == SWIN_SIM_COSINE) dtau_acc = fmaf(dl, xs, dtau_acc);
-                if (POS == SWIN_POS_TABLE && a.dtable && !diag8 && ok) atomicAdd(&dtab[boff + e], dl);
+                if (POS == SWIN_POS_TABLE && a.dtable && !diag8 && ok) fixed::add(&dtab[boff + e], dl);
             }
             if (POS == SWIN_POS_TABLE && a.dtable && diag8) {
                 // M a multiple of 8: each 8-lane half of the tile is 8
@@ -416,8 +424,8 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
                 const float B = (j >= 7 ? b1 : 0.0f) + (j >= 6 ? b2 : 0.0f) + (j >= 5 ? b3 : 0.0f) +
                                 (j >= 4 ? b4 : 0.0f) + (j >= 3 ? b5 : 0.0f) + (j >= 2 ? b6 : 0.0f) +
                                 (j >= 1 ? b7 : 0.0f);
-                if (tv) atomicAdd(&dtab[boff], A);
-                if (tv && j >= 1) atomicAdd(&dtab[boff + 8], B);
+                if (tv) fixed::add(&dtab[boff], A);
+                if (tv && j >= 1) fixed::add(&dtab[boff + 8], B);
             }
             const bf16x8 dsb = pack_bf16x8(ds);
             G0 = mfma(vt_frag(rowA, c, 0, grp, li), dsb, G0);
@@ -512,7 +520,7 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
                 const bool ok = ((cbits >> e) & 1u) != 0u;
                 float b = 0.0f;
                 if (POS == SWIN_POS_TABLE) b = bias2[ok ? rev0 - e : negrow];
-                const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(sv * qv_, cj_s, b) - lv) : 0.0f;
+                const float pr = __builtin_amdgcn_exp2f(ok ? fmaf(sv * qv_, cj_s, b) - lv : -INFINITY);
                 pp[e] = pr;
                 const float dl = pr * (dpv - dv_);
                 dsa[e] = dl * (SIM == SWIN_SIM_COSINE ? qv_ * (1.0f / kLog2e) : RS32);
@@ -561,14 +569,15 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
     }
     if (POS == SWIN_POS_TABLE && a.dtable)
         for (int i = tid; i < S * S; i += NTHR)
-            if (dtab[i] != 0.0f) unsafeAtomicAdd(&a.dtable[(size_t)(S * S - 1 - i) * g.heads + h], dtab[i]);
+            if (dtab[i] != 0ull)
+                unsafeAtomicAdd(&a.dtable[(size_t)(S * S - 1 - i) * g.heads + h], fixed::from_fixed(dtab[i]));
 }
 
 size_t lds_bytes(const AttnParams& p, int NS)
 {
     const int S = 2 * p.g.M - 1;
     size_t b = (size_t)NS * D * 2 * 2 + (size_t)4 * NS * 4 + (size_t)WAVES * 4 + 64;
-    if (p.pos == SWIN_POS_TABLE) b += (size_t)2 * ((S * S + 8 + 3) / 4 * 4) * 4;
+    if (p.pos == SWIN_POS_TABLE) b += (size_t)3 * ((S * S + 8 + 3) / 4 * 4) * 4;   // bias2, dtab
     if (p.pos == SWIN_POS_ROPE2D) b += (size_t)p.g.M * 32 * 4;
     if (p.sim == SWIN_SIM_COSINE && p.pos == SWIN_POS_ROPE2D) b += 16 + (size_t)NS * D * 2;   // remainder rows
     return b;

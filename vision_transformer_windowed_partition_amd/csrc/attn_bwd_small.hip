@@ -23,7 +23,7 @@
 // a pass takes the fragments of its own tiles of the other two straight from
 // memory.  Beside them: the per-slot scales, log-sum-exp and D, the head's
 // bias table (reversed, log2 units) and the workgroup's bias-gradient
-// accumulator.  Three passes:
+// accumulator (64-bit fixed point, integer LDS atomics).  Three passes:
 //   0  query-major (like the forward): S^T = K Q^T per 32-key chunk, running
 //      maximum and sum -> log-sum-exp of each query (skipped when the
 //      forward's is given);
@@ -36,6 +36,7 @@
 //      dV^T += dout^T P and H^T += Q^T (dl a), dout^T and Q^T read transposed.
 // All products are v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
 #include "common.hpp"
+#include "fixed_sum.hpp"
 #include "lanes.hpp"
 #include "launch.hpp"
 #include "launch_bwd.hpp"
@@ -124,8 +125,9 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
 
     const int tabsz = POS == SWIN_POS_TABLE ? (S * S + 8 + 3) / 4 * 4 : 0;
     float* bias2 = smem_f;                                     // [S*S + 8] reversed, log2 units
-    float* dtab = bias2 + tabsz;                               // [S*S] reversed, natural units
-    float* red = dtab + tabsz;                                 // [16]
+    // [S*S] reversed, natural units, 64-bit fixed point
+    fixed::acc_t* dtab = (fixed::acc_t*)(bias2 + tabsz);
+    float* red = (float*)(dtab + tabsz);                       // [16]
     float* scal = red + 16 + wh * (4 * NS);                    // this window's per-slot scalars
     float* ksc = scal;                                         // [NS] c_j
     float* qsc = ksc + NS;                                     // [NS] log2(e) a_i
@@ -247,7 +249,7 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
     if (POS == SWIN_POS_TABLE) {
         for (int i = tid; i < S * S; i += 256) {
             bias2[S * S - 1 - i] = p.table[(size_t)i * g.heads + h] * kLog2e;
-            dtab[i] = 0.0f;
+            dtab[i] = 0ull;
         }
         if (tid < 8) bias2[S * S + tid] = -INFINITY;
     }
@@ -375,7 +377,7 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                     ds[e] = dl * (SIM == SWIN_SIM_COSINE ? kv : 0.17677669529663687f);
                     dlv[e] = dl;
                     if (SIM == SWIN_SIM_COSINE) dtau_acc = fmaf(dl, xs, dtau_acc);
-                    if (POS == SWIN_POS_TABLE && !DIAG && a.dtable && ok) atomicAdd(&dtab[boff + e], dl);
+                    if (POS == SWIN_POS_TABLE && !DIAG && a.dtable && ok) fixed::add(&dtab[boff + e], dl);
                 }
                 if (POS == SWIN_POS_TABLE && DIAG && a.dtable) {
                     // M == 16: the tile is one window row, lane li its column li,
@@ -403,7 +405,7 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                     const float te = A + row_shl<8>(pA);
                     const float to = row_shr<8>(A) + row_shr<8>(pB);
                     const float T = even ? te : (li <= 7 ? B : to);
-                    if (even || li != 0) atomicAdd(&dtab[boff + (even ? 0 : 8)], T);
+                    if (even || li != 0) fixed::add(&dtab[boff + (even ? 0 : 8)], T);
                 }
                 const bf16x8 dsb = pack_bf16x8(ds);
                 G0 = mfma(vt_frag(krow, c, 0, grp, li), dsb, G0);
@@ -559,7 +561,8 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
     }
     if (POS == SWIN_POS_TABLE && a.dtable)
         for (int i = tid; i < S * S; i += 256)
-            if (dtab[i] != 0.0f) unsafeAtomicAdd(&a.dtable[(size_t)(S * S - 1 - i) * g.heads + h], dtab[i]);
+            if (dtab[i] != 0ull)
+                unsafeAtomicAdd(&a.dtable[(size_t)(S * S - 1 - i) * g.heads + h], fixed::from_fixed(dtab[i]));
 }
 
 template <int SIM, int POS>
@@ -610,7 +613,7 @@ hipError_t launch_attn_bwd_small(const AttnParams& p, const void* out, const voi
     const int ns = nch * 32;
     const int nrows = wh == 1 ? 2 : 4;                              // phased when four waves share a window
     size_t lds = (size_t)(16 + wh * 4 * ns) * sizeof(float) + (size_t)wh * nrows * ns * D * 2;
-    if (p.pos == SWIN_POS_TABLE) lds += (size_t)2 * ((S * S + 8 + 3) / 4 * 4) * sizeof(float);
+    if (p.pos == SWIN_POS_TABLE) lds += (size_t)3 * ((S * S + 8 + 3) / 4 * 4) * sizeof(float);   // bias2, dtab
     if (p.sim == SWIN_SIM_COSINE) {
         if (p.pos == SWIN_POS_TABLE) return launch_nch<SWIN_SIM_COSINE, SWIN_POS_TABLE>(p, a, L, nch, (int)grid, lds, stream);
         return launch_nch<SWIN_SIM_COSINE, SWIN_POS_NONE>(p, a, L, nch, (int)grid, lds, stream);

@@ -372,6 +372,7 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
 
         // pass B: dq
         f32x4 G0 = {0.0f, 0.0f, 0.0f, 0.0f}, G1 = G0;
+        float dts = 0.0f;                                  // sum over keys of dS~ s (dtau without a_i)
         for (int c = 0; c < nch; ++c) {
             const int sA = 32 * c + 8 * (li >> 2) + (li & 3);
             const bf16x8 va = rowfrag(rowB, sA, grp), vb = rowfrag(rowB, sA + 4, grp);
@@ -393,12 +394,14 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
                 const bool ok = ((bits >> e) & 1u) != 0u;
                 float b = 0.0f;
                 if (POS == SWIN_POS_TABLE) b = bias2[ok ? boff + e : negrow];
-                const float xs = sv * qs * kv;
-                const float pr = __builtin_amdgcn_exp2f(ok ? xs + b - lq : -INFINITY);
+                // logit (log2 units) = s a_i c_j + b, a_i c_j = qs kv (DOT: kv = 1)
+                const float arg = fmaf(sv, SIM == SWIN_SIM_COSINE ? qs * kv : qs, b) - lq;
+                const float pr = __builtin_amdgcn_exp2f(ok ? arg : -INFINITY);
                 const float dl = pr * (dpv - Dq);
-                ds[e] = dl * (SIM == SWIN_SIM_COSINE ? kv : RS32);
+                // COSINE: dS~ = dl c_j (dq's a_i after the sum); DOT: dl (1/sqrt(d) after)
+                ds[e] = SIM == SWIN_SIM_COSINE ? dl * kv : dl;
                 dlv[e] = dl;
-                if (SIM == SWIN_SIM_COSINE) dtau_acc = fmaf(dl, xs, dtau_acc);
+                if (SIM == SWIN_SIM_COSINE) dts = fmaf(ds[e], sv, dts);
                 if (POS == SWIN_POS_TABLE && a.dtable && !diag8 && ok) fixed::add(&dtab[boff + e], dl);
             }
             if (POS == SWIN_POS_TABLE && a.dtable && diag8) {
@@ -431,7 +434,11 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
             G0 = mfma(vt_frag(rowA, c, 0, grp, li), dsb, G0);
             G1 = mfma(vt_frag(rowA, c, 1, grp, li), dsb, G1);
         }
-        float g8[8] = {G0[0], G0[1], G0[2], G0[3], G1[0], G1[1], G1[2], G1[3]};
+        // sum dl (log2-unit logit without the bias) = qs sum dS~ s
+        if (SIM == SWIN_SIM_COSINE) dtau_acc = fmaf(dts, qs, dtau_acc);
+        const float gs = SIM == SWIN_SIM_COSINE ? 1.0f : RS32;
+        float g8[8] = {G0[0] * gs, G0[1] * gs, G0[2] * gs, G0[3] * gs,
+                       G1[0] * gs, G1[1] * gs, G1[2] * gs, G1[3] * gs};
         const uint32_t o8 = masked(wg.tok(ri, ci) + 8u * grp, tv);
         if (SIM == SWIN_SIM_COSINE) {
             const bf16x4 qa4 = load8b(qr, o8), qb4 = load8b(qr, o8 + 32u);
@@ -500,13 +507,14 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
                 sa = mfma(qa, kB_lo, sa);
                 sb = mfma(qb, kB_lo, sb);
             }
-            const f32x4 pa = mfma(ga, vB, z), pb = mfma(gb, vB, z);
             const int qs0 = 32 * c + 8 * grp;
+            const f32x4 dA = *(const f32x4*)(dd + qs0), dB = *(const f32x4*)(dd + qs0 + 4);
+            const f32x4 pa = mfma(ga, vB, z), pb = mfma(gb, vB, z);
             const f32x4 qsA = *(const f32x4*)(qsc + qs0), qsB = *(const f32x4*)(qsc + qs0 + 4);
             const f32x4 lA = *(const f32x4*)(lse + qs0), lB = *(const f32x4*)(lse + qs0 + 4);
-            const f32x4 dA = *(const f32x4*)(dd + qs0), dB = *(const f32x4*)(dd + qs0 + 4);
             const int gam = 4 * c + grp, ri = qdiv(gam, L.inv_GPR), ci0 = 8 * (gam - ri * L.GPR);
-            const int rev0 = S * S - 1 - ((ri - rj + M - 1) * S + (ci0 - cj + M - 1));
+            // reversed table position of query (ri, ci0 + 7) against key (rj, cj)
+            const int rev7 = S * S - 8 - ((ri - rj + M - 1) * S + (ci0 - cj + M - 1));
             const bool rok = kv_ok && ri < M && ri >= rlo && ri < rhi;
             const uint32_t cbits = rok ? (cmask >> ci0) & 0xffu : 0u;
             float pp[8], dsa[8];
@@ -516,14 +524,14 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
                 const float dpv = e < 4 ? pa[e] : pb[e - 4];
                 const float qv_ = e < 4 ? qsA[e] : qsB[e - 4];
                 const float lv = e < 4 ? lA[e] : lB[e - 4];
-                const float dv_ = e < 4 ? dA[e] : dB[e - 4];
                 const bool ok = ((cbits >> e) & 1u) != 0u;
                 float b = 0.0f;
-                if (POS == SWIN_POS_TABLE) b = bias2[ok ? rev0 - e : negrow];
+                if (POS == SWIN_POS_TABLE) b = bias2[ok ? rev7 + (7 - e) : negrow];
                 const float pr = __builtin_amdgcn_exp2f(ok ? fmaf(sv * qv_, cj_s, b) - lv : -INFINITY);
                 pp[e] = pr;
-                const float dl = pr * (dpv - dv_);
-                dsa[e] = dl * (SIM == SWIN_SIM_COSINE ? qv_ * (1.0f / kLog2e) : RS32);
+                const float dl = pr * (dpv - (e < 4 ? dA[e] : dB[e - 4]));
+                // dS~ = dl log2(e) a_i (COSINE) or dl (DOT); the constant after the sum
+                dsa[e] = SIM == SWIN_SIM_COSINE ? dl * qv_ : dl;
             }
             const bf16x8 pbf = pack_bf16x8(pp), dsb = pack_bf16x8(dsa);
             V0 = mfma(vt_frag(rowB, c, 0, grp, li), pbf, V0);
@@ -531,7 +539,9 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
             H0 = mfma(vt_frag(rowA, c, 0, grp, li), dsb, H0);
             H1 = mfma(vt_frag(rowA, c, 1, grp, li), dsb, H1);
         }
-        float h8[8] = {H0[0], H0[1], H0[2], H0[3], H1[0], H1[1], H1[2], H1[3]};
+        const float hs = SIM == SWIN_SIM_COSINE ? 1.0f / kLog2e : RS32;
+        float h8[8] = {H0[0] * hs, H0[1] * hs, H0[2] * hs, H0[3] * hs,
+                       H1[0] * hs, H1[1] * hs, H1[2] * hs, H1[3] * hs};
         const uint32_t o8 = masked(wg.tok(rjc, cjc) + 8u * grp, kv_ok);
         if (SIM == SWIN_SIM_COSINE) {
             const bf16x4 ka4 = load8b(kr, o8), kb4 = load8b(kr, o8 + 32u);

@@ -345,6 +345,7 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             if (wp.last_c) { if (ci < M - g.shift) chi = M - g.shift; else clo = M - g.shift; }
             const uint32_t cmask = (((1u << chi) - 1u) & ~((1u << clo) - 1u));
             f32x4 G0 = {0.0f, 0.0f, 0.0f, 0.0f}, G1 = G0;
+            float dts = 0.0f;                              // sum over keys of dS~ s (dtau without a_i)
 #pragma unroll 2
             for (int c = 0; c < NCH; ++c) {
                 const int sA = 32 * c + 8 * (li >> 2) + (li & 3);
@@ -369,14 +370,15 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                     const bool ok = !MASK || ((bits >> e) & 1u) != 0u;
                     float b = 0.0f;
                     if (POS == SWIN_POS_TABLE) b = bias2[ok ? boff + e : negrow];     // -inf when excluded
-                    const float xs = sv * qs * kv;                 // log2 units, without the bias
-                    float arg = xs + b - lq;
+                    // logit (log2 units) = s a_i c_j + b, a_i c_j = qs kv (DOT: kv = 1)
+                    float arg = fmaf(sv, SIM == SWIN_SIM_COSINE ? qs * kv : qs, b) - lq;
                     if (POS != SWIN_POS_TABLE && MASK) arg = ok ? arg : -INFINITY;
                     const float pr = __builtin_amdgcn_exp2f(arg);
                     const float dl = pr * (dpv - Dq);
-                    ds[e] = dl * (SIM == SWIN_SIM_COSINE ? kv : 0.17677669529663687f);
+                    // COSINE: dS~ = dl c_j (dq's a_i after the sum); DOT: dl (1/sqrt(d) after)
+                    ds[e] = SIM == SWIN_SIM_COSINE ? dl * kv : dl;
                     dlv[e] = dl;
-                    if (SIM == SWIN_SIM_COSINE) dtau_acc = fmaf(dl, xs, dtau_acc);
+                    if (SIM == SWIN_SIM_COSINE) dts = fmaf(ds[e], sv, dts);
                     if (POS == SWIN_POS_TABLE && !DIAG && a.dtable && ok) fixed::add(&dtab[boff + e], dl);
                 }
                 if (POS == SWIN_POS_TABLE && DIAG && a.dtable) {
@@ -411,6 +413,8 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                 G0 = mfma(vt_frag(krow, c, 0, grp, li), dsb, G0);
                 G1 = mfma(vt_frag(krow, c, 1, grp, li), dsb, G1);
             }
+            // sum dl (log2-unit logit without the bias) = qs sum dS~ s
+            if (SIM == SWIN_SIM_COSINE) dtau_acc = fmaf(dts, qs, dtau_acc);
             // lane holds channels 4 grp..+3 and 16 + 4 grp..+3 of query li
             float q8[8], g8[8];
             {
@@ -433,7 +437,7 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                 for (int e = 0; e < 8; ++e) dqv[e] = ai * (g8[e] - q8[e] * pj);
             } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) dqv[e] = g8[e];
+                for (int e = 0; e < 8; ++e) dqv[e] = g8[e] * 0.17677669529663687f;
             }
             const uint32_t off = masked(wg.tok(ri, ci) + 8u * grp, tv);
             store8(dqr, off, pack_bf16x4(dqv[0], dqv[1], dqv[2], dqv[3]));
@@ -474,19 +478,19 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                 const int sA = 32 * c + 8 * (li >> 2) + (li & 3);
                 const bf16x8 qa = rowfrag(qrow, sA, grp), qb = rowfrag(qrow, sA + 4, grp);
                 const bf16x8 ga = rowfrag(orow, sA, grp), gb = rowfrag(orow, sA + 4, grp);
+                // this lane's query slots: 32 c + 8 grp + e, a row segment
+                const int qs0 = 32 * c + 8 * grp;
+                const f32x4 dA = *(const f32x4*)(dd + qs0), dB = *(const f32x4*)(dd + qs0 + 4);
                 const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
                 const f32x4 sa = mfma(qa, kB, z), sb = mfma(qb, kB, z);
                 const f32x4 pa = mfma(ga, vB, z), pb = mfma(gb, vB, z);
-                // this lane's query slots: 32 c + 8 grp + e, a row segment
-                const int qs0 = 32 * c + 8 * grp;
                 const f32x4 qsA = *(const f32x4*)(qsc + qs0), qsB = *(const f32x4*)(qsc + qs0 + 4);
                 const f32x4 lA = *(const f32x4*)(lse + qs0), lB = *(const f32x4*)(lse + qs0 + 4);
-                const f32x4 dA = *(const f32x4*)(dd + qs0), dB = *(const f32x4*)(dd + qs0 + 4);
                 const int gam = 4 * c + grp, ri = gam / GPR, ci0 = 8 * (gam % GPR);
                 // query (ri, ci0 + e) against key (rj, cj): table row
                 // (ri - rj + M-1) S + (ci0 + e - cj + M-1), reversed position
                 // S*S - 1 - that, decreasing in e
-                const int rev0 = S * S - 1 - ((ri - rj + M - 1) * S + (ci0 - cj + M - 1));
+                const int rev7 = S * S - 8 - ((ri - rj + M - 1) * S + (ci0 - cj + M - 1));   // rev. pos. of e = 7
                 const bool rok = kv_ok && ri < M && ri >= rlo && ri < rhi;
                 const uint32_t cbits = rok ? (cmask >> ci0) & 0xffu : 0u;
                 float pp[8], dsa[8];
@@ -496,16 +500,16 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                     const float dpv = e < 4 ? pa[e] : pb[e - 4];
                     const float qv = e < 4 ? qsA[e] : qsB[e - 4];
                     const float lv = e < 4 ? lA[e] : lB[e - 4];
-                    const float dv_ = e < 4 ? dA[e] : dB[e - 4];
                     const bool ok = !MASK || ((cbits >> e) & 1u) != 0u;
                     float b = 0.0f;
-                    if (POS == SWIN_POS_TABLE) b = bias2[ok ? rev0 - e : negrow];
+                    if (POS == SWIN_POS_TABLE) b = bias2[ok ? rev7 + (7 - e) : negrow];
                     // (the select also covers padded query slots, whose statistics are unset)
                     const float arg = fmaf(sv * qv, cj_s, b) - lv;
                     const float pr = __builtin_amdgcn_exp2f(!MASK || ok ? arg : -INFINITY);
                     pp[e] = pr;
-                    const float dl = pr * (dpv - dv_);
-                    dsa[e] = dl * (SIM == SWIN_SIM_COSINE ? qv * (1.0f / kLog2e) : 0.17677669529663687f);
+                    const float dl = pr * (dpv - (e < 4 ? dA[e] : dB[e - 4]));
+                    // dS~ = dl log2(e) a_i (COSINE) or dl (DOT); the constant after the sum
+                    dsa[e] = SIM == SWIN_SIM_COSINE ? dl * qv : dl;
                 }
                 const bf16x8 pbf = pack_bf16x8(pp), dsb = pack_bf16x8(dsa);
                 V0 = mfma(vt_frag(orow, c, 0, grp, li), pbf, V0);
@@ -518,8 +522,10 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             {
                 if (PHASED) gquad(kg, sk, k8);             // the key's raw channels
                 else lquad(krow, sk, k8);
-                h8[0] = H0[0]; h8[1] = H0[1]; h8[2] = H0[2]; h8[3] = H0[3];
-                h8[4] = H1[0]; h8[5] = H1[1]; h8[6] = H1[2]; h8[7] = H1[3];
+                // the constant of dS~: 1/log2(e) (COSINE) or 1/sqrt(d) (DOT)
+                const float hs = SIM == SWIN_SIM_COSINE ? 1.0f / kLog2e : 0.17677669529663687f;
+                h8[0] = H0[0] * hs; h8[1] = H0[1] * hs; h8[2] = H0[2] * hs; h8[3] = H0[3] * hs;
+                h8[4] = H1[0] * hs; h8[5] = H1[1] * hs; h8[6] = H1[2] * hs; h8[7] = H1[3] * hs;
             }
             if (SIM == SWIN_SIM_COSINE) {
                 float kh = 0.0f, kk = 0.0f;

@@ -154,6 +154,13 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
     const bool split = CR;
     const bool needs_mask = wp.last_r || wp.last_c || SR != M || NS != M * SR;
     const int negrow = S * S;
+    // lane offsets of the chunk loops' LDS fragments (the swizzles do not
+    // change from chunk to chunk: chunk c adds 32 c D elements)
+    const int offA = row_off(8 * (li >> 2) + (li & 3), grp);   // A rows sA (and sA + 4: + 4 D)
+    const int vo0 = vt_off(0, grp, li), vo1 = vt_off(1, grp, li);
+    auto fragA = [&](const __bf16* rows, int c, int second) -> bf16x8 {
+        return *(const bf16x8*)(rows + offA + (32 * c + 4 * second) * D);
+    };
     constexpr float RS32 = 0.17677669529663687f;              // 1/sqrt(32)
 
     // rotate 8 channels 8 pc..8 pc+7 of a token at (r, c) by sgn * angle:
@@ -304,14 +311,14 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
             qf_lo = pack_bf16x8(lo);
         }
         // S^T for the 8 keys of this lane's group in chunk c (hi + lo when split)
-        auto scores = [&](int sA, f32x4& sa, f32x4& sb) {
-            const bf16x8 ka = rowfrag(rowA, sA, grp), kb = rowfrag(rowA, sA + 4, grp);
+        auto scores = [&](int c, f32x4& sa, f32x4& sb) {
+            const bf16x8 ka = fragA(rowA, c, 0), kb = fragA(rowA, c, 1);
             const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
             sa = mfma(ka, qf, z);
             sb = mfma(kb, qf, z);
             if (CR && split) {
-                sa = mfma(rowfrag(rowL, sA, grp), qf, sa);
-                sb = mfma(rowfrag(rowL, sA + 4, grp), qf, sb);
+                sa = mfma(fragA(rowL, c, 0), qf, sa);
+                sb = mfma(fragA(rowL, c, 1), qf, sb);
                 sa = mfma(ka, qf_lo, sa);
                 sb = mfma(kb, qf_lo, sb);
             }
@@ -333,9 +340,8 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
         float m = -INFINITY, l = 0.0f;
         const int nch0 = p.lse ? 0 : nch;
         for (int c = 0; c < nch0; ++c) {
-            const int sA = 32 * c + 8 * (li >> 2) + (li & 3);
             f32x4 sa, sb;
-            scores(sA, sa, sb);
+            scores(c, sa, sb);
             const f32x4 k0 = *(const f32x4*)(ksc + 32 * c + 8 * grp);
             const f32x4 k1 = *(const f32x4*)(ksc + 32 * c + 8 * grp + 4);
             const int gam = 4 * c + grp, rj = qdiv(gam, L.inv_GPR), cj0 = 8 * (gam - rj * L.GPR);
@@ -374,11 +380,10 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
         f32x4 G0 = {0.0f, 0.0f, 0.0f, 0.0f}, G1 = G0;
         float dts = 0.0f;                                  // sum over keys of dS~ s (dtau without a_i)
         for (int c = 0; c < nch; ++c) {
-            const int sA = 32 * c + 8 * (li >> 2) + (li & 3);
-            const bf16x8 va = rowfrag(rowB, sA, grp), vb = rowfrag(rowB, sA + 4, grp);
+            const bf16x8 va = fragA(rowB, c, 0), vb = fragA(rowB, c, 1);
             const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
             f32x4 sa, sb;
-            scores(sA, sa, sb);
+            scores(c, sa, sb);
             const f32x4 pa = mfma(va, gfr, z), pb = mfma(vb, gfr, z);
             const f32x4 k0 = *(const f32x4*)(ksc + 32 * c + 8 * grp);
             const f32x4 k1 = *(const f32x4*)(ksc + 32 * c + 8 * grp + 4);
@@ -431,8 +436,8 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
                 if (tv && j >= 1) fixed::add(&dtab[boff + 8], B);
             }
             const bf16x8 dsb = pack_bf16x8(ds);
-            G0 = mfma(vt_frag(rowA, c, 0, grp, li), dsb, G0);
-            G1 = mfma(vt_frag(rowA, c, 1, grp, li), dsb, G1);
+            G0 = mfma(vt_frag_at(rowA + 32 * c * D + vo0), dsb, G0);
+            G1 = mfma(vt_frag_at(rowA + 32 * c * D + vo1), dsb, G1);
         }
         // sum dl (log2-unit logit without the bias) = qs sum dS~ s
         if (SIM == SWIN_SIM_COSINE) dtau_acc = fmaf(dts, qs, dtau_acc);
@@ -496,14 +501,13 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
                                (M >= 32 ? 0xffffffffu : ((1u << M) - 1u));
         f32x4 V0 = {0.0f, 0.0f, 0.0f, 0.0f}, V1 = V0, H0 = V0, H1 = V0;
         for (int c = 0; c < nch; ++c) {
-            const int sA = 32 * c + 8 * (li >> 2) + (li & 3);
-            const bf16x8 qa = rowfrag(rowA, sA, grp), qb = rowfrag(rowA, sA + 4, grp);
-            const bf16x8 ga = rowfrag(rowB, sA, grp), gb = rowfrag(rowB, sA + 4, grp);
+            const bf16x8 qa = fragA(rowA, c, 0), qb = fragA(rowA, c, 1);
+            const bf16x8 ga = fragA(rowB, c, 0), gb = fragA(rowB, c, 1);
             const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
             f32x4 sa = mfma(qa, kB, z), sb = mfma(qb, kB, z);
             if (CR && split) {
-                sa = mfma(rowfrag(rowL, sA, grp), kB, sa);
-                sb = mfma(rowfrag(rowL, sA + 4, grp), kB, sb);
+                sa = mfma(fragA(rowL, c, 0), kB, sa);
+                sb = mfma(fragA(rowL, c, 1), kB, sb);
                 sa = mfma(qa, kB_lo, sa);
                 sb = mfma(qb, kB_lo, sb);
             }
@@ -515,6 +519,7 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
             const int gam = 4 * c + grp, ri = qdiv(gam, L.inv_GPR), ci0 = 8 * (gam - ri * L.GPR);
             // reversed table position of query (ri, ci0 + 7) against key (rj, cj)
             const int rev7 = S * S - 8 - ((ri - rj + M - 1) * S + (ci0 - cj + M - 1));
+            const float* brow = bias2 + rev7;
             const bool rok = kv_ok && ri < M && ri >= rlo && ri < rhi;
             const uint32_t cbits = rok ? (cmask >> ci0) & 0xffu : 0u;
             float pp[8], dsa[8];
@@ -526,7 +531,7 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
                 const float lv = e < 4 ? lA[e] : lB[e - 4];
                 const bool ok = ((cbits >> e) & 1u) != 0u;
                 float b = 0.0f;
-                if (POS == SWIN_POS_TABLE) b = bias2[ok ? rev7 + (7 - e) : negrow];
+                if (POS == SWIN_POS_TABLE) b = needs_mask ? bias2[ok ? rev7 + (7 - e) : negrow] : brow[7 - e];
                 const float pr = __builtin_amdgcn_exp2f(ok ? fmaf(sv * qv_, cj_s, b) - lv : -INFINITY);
                 pp[e] = pr;
                 const float dl = pr * (dpv - (e < 4 ? dA[e] : dB[e - 4]));
@@ -534,10 +539,10 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
                 dsa[e] = SIM == SWIN_SIM_COSINE ? dl * qv_ : dl;
             }
             const bf16x8 pbf = pack_bf16x8(pp), dsb = pack_bf16x8(dsa);
-            V0 = mfma(vt_frag(rowB, c, 0, grp, li), pbf, V0);
-            V1 = mfma(vt_frag(rowB, c, 1, grp, li), pbf, V1);
-            H0 = mfma(vt_frag(rowA, c, 0, grp, li), dsb, H0);
-            H1 = mfma(vt_frag(rowA, c, 1, grp, li), dsb, H1);
+            V0 = mfma(vt_frag_at(rowB + 32 * c * D + vo0), pbf, V0);
+            V1 = mfma(vt_frag_at(rowB + 32 * c * D + vo1), pbf, V1);
+            H0 = mfma(vt_frag_at(rowA + 32 * c * D + vo0), dsb, H0);
+            H1 = mfma(vt_frag_at(rowA + 32 * c * D + vo1), dsb, H1);
         }
         const float hs = SIM == SWIN_SIM_COSINE ? 1.0f / kLog2e : RS32;
         float h8[8] = {H0[0] * hs, H0[1] * hs, H0[2] * hs, H0[3] * hs,

@@ -260,6 +260,13 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
     const bool needs_mask = wp.last_r || wp.last_c || padded;
     const int negrow = S * S;
     const int kbase = (grp / GPR) * S + 8 * (grp % GPR);   // bias offset of this lane's key group, chunk 0
+    // lane offsets of the chunk loops' LDS fragments (the swizzles do not
+    // change from chunk to chunk: chunk c adds 32 c D elements)
+    const int offA = row_off(8 * (li >> 2) + (li & 3), grp);   // A rows sA (and sA + 4: + 4 D)
+    const int vo0 = vt_off(0, grp, li), vo1 = vt_off(1, grp, li);
+    auto fragA = [&](const __bf16* rows, int c, int second) -> bf16x8 {
+        return *(const bf16x8*)(rows + offA + (32 * c + 4 * second) * D);
+    };
 
     // ---- pass 0: log-sum-exp of this wave's queries, or the forward's
     // (natural log, to log2 units)
@@ -286,8 +293,7 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             float m = -INFINITY, l = 0.0f;
 #pragma unroll 2
             for (int c = 0; c < NCH; ++c) {
-                const bf16x8 ka = rowfrag(krow, 32 * c + 8 * (li >> 2) + (li & 3), grp);
-                const bf16x8 kb = rowfrag(krow, 32 * c + 8 * (li >> 2) + (li & 3) + 4, grp);
+                const bf16x8 ka = fragA(krow, c, 0), kb = fragA(krow, c, 1);
                 const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
                 const f32x4 sa = mfma(ka, qf, z), sb = mfma(kb, qf, z);
                 const f32x4 k0 = *(const f32x4*)(ksc + 32 * c + 8 * grp);
@@ -348,9 +354,8 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             float dts = 0.0f;                              // sum over keys of dS~ s (dtau without a_i)
 #pragma unroll 2
             for (int c = 0; c < NCH; ++c) {
-                const int sA = 32 * c + 8 * (li >> 2) + (li & 3);
-                const bf16x8 ka = rowfrag(krow, sA, grp), kb = rowfrag(krow, sA + 4, grp);
-                const bf16x8 va = rowfrag(vrow, sA, grp), vb = rowfrag(vrow, sA + 4, grp);
+                const bf16x8 ka = fragA(krow, c, 0), kb = fragA(krow, c, 1);
+                const bf16x8 va = fragA(vrow, c, 0), vb = fragA(vrow, c, 1);
                 const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
                 const f32x4 sa = mfma(ka, qf, z), sb = mfma(kb, qf, z);
                 const f32x4 pa = mfma(va, gf, z), pb = mfma(vb, gf, z);
@@ -358,6 +363,7 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                 const f32x4 k1 = *(const f32x4*)(ksc + 32 * c + 8 * grp + 4);
                 const int gam = 4 * c + grp, rj = gam / GPR, cj0 = 8 * (gam % GPR);
                 const int boff = qoff + (4 / GPR) * c * S;
+                const float* brow = bias2 + boff;
                 // allowed keys of this lane's 8-key group (bit e: key column cj0 + e)
                 const uint32_t bits = !MASK ? 0xffu : tv && rj >= rlo && rj < rhi && rj < M ? (cmask >> cj0) & 0xffu
                                                                                              : 0u;
@@ -369,7 +375,7 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                     const float kv = e < 4 ? k0[e] : k1[e - 4];
                     const bool ok = !MASK || ((bits >> e) & 1u) != 0u;
                     float b = 0.0f;
-                    if (POS == SWIN_POS_TABLE) b = bias2[ok ? boff + e : negrow];     // -inf when excluded
+                    if (POS == SWIN_POS_TABLE) b = MASK ? bias2[ok ? boff + e : negrow] : brow[e];   // -inf: excluded
                     // logit (log2 units) = s a_i c_j + b, a_i c_j = qs kv (DOT: kv = 1)
                     float arg = fmaf(sv, SIM == SWIN_SIM_COSINE ? qs * kv : qs, b) - lq;
                     if (POS != SWIN_POS_TABLE && MASK) arg = ok ? arg : -INFINITY;
@@ -410,8 +416,8 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                     if (even || li != 0) fixed::add(&dtab[boff + (even ? 0 : 8)], T);
                 }
                 const bf16x8 dsb = pack_bf16x8(ds);
-                G0 = mfma(vt_frag(krow, c, 0, grp, li), dsb, G0);
-                G1 = mfma(vt_frag(krow, c, 1, grp, li), dsb, G1);
+                G0 = mfma(vt_frag_at(krow + 32 * c * D + vo0), dsb, G0);
+                G1 = mfma(vt_frag_at(krow + 32 * c * D + vo1), dsb, G1);
             }
             // sum dl (log2-unit logit without the bias) = qs sum dS~ s
             if (SIM == SWIN_SIM_COSINE) dtau_acc = fmaf(dts, qs, dtau_acc);
@@ -475,9 +481,8 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             f32x4 V0 = {0.0f, 0.0f, 0.0f, 0.0f}, V1 = V0, H0 = V0, H1 = V0;
 #pragma unroll 2
             for (int c = 0; c < NCH; ++c) {
-                const int sA = 32 * c + 8 * (li >> 2) + (li & 3);
-                const bf16x8 qa = rowfrag(qrow, sA, grp), qb = rowfrag(qrow, sA + 4, grp);
-                const bf16x8 ga = rowfrag(orow, sA, grp), gb = rowfrag(orow, sA + 4, grp);
+                const bf16x8 qa = fragA(qrow, c, 0), qb = fragA(qrow, c, 1);
+                const bf16x8 ga = fragA(orow, c, 0), gb = fragA(orow, c, 1);
                 // this lane's query slots: 32 c + 8 grp + e, a row segment
                 const int qs0 = 32 * c + 8 * grp;
                 const f32x4 dA = *(const f32x4*)(dd + qs0), dB = *(const f32x4*)(dd + qs0 + 4);
@@ -491,6 +496,7 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                 // (ri - rj + M-1) S + (ci0 + e - cj + M-1), reversed position
                 // S*S - 1 - that, decreasing in e
                 const int rev7 = S * S - 8 - ((ri - rj + M - 1) * S + (ci0 - cj + M - 1));   // rev. pos. of e = 7
+                const float* brow = bias2 + rev7;
                 const bool rok = kv_ok && ri < M && ri >= rlo && ri < rhi;
                 const uint32_t cbits = rok ? (cmask >> ci0) & 0xffu : 0u;
                 float pp[8], dsa[8];
@@ -502,7 +508,7 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                     const float lv = e < 4 ? lA[e] : lB[e - 4];
                     const bool ok = !MASK || ((cbits >> e) & 1u) != 0u;
                     float b = 0.0f;
-                    if (POS == SWIN_POS_TABLE) b = bias2[ok ? rev7 + (7 - e) : negrow];
+                    if (POS == SWIN_POS_TABLE) b = MASK ? bias2[ok ? rev7 + (7 - e) : negrow] : brow[7 - e];
                     // (the select also covers padded query slots, whose statistics are unset)
                     const float arg = fmaf(sv * qv, cj_s, b) - lv;
                     const float pr = __builtin_amdgcn_exp2f(!MASK || ok ? arg : -INFINITY);
@@ -512,10 +518,10 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                     dsa[e] = SIM == SWIN_SIM_COSINE ? dl * qv : dl;
                 }
                 const bf16x8 pbf = pack_bf16x8(pp), dsb = pack_bf16x8(dsa);
-                V0 = mfma(vt_frag(orow, c, 0, grp, li), pbf, V0);
-                V1 = mfma(vt_frag(orow, c, 1, grp, li), pbf, V1);
-                H0 = mfma(vt_frag(qrow, c, 0, grp, li), dsb, H0);
-                H1 = mfma(vt_frag(qrow, c, 1, grp, li), dsb, H1);
+                V0 = mfma(vt_frag_at(orow + 32 * c * D + vo0), pbf, V0);
+                V1 = mfma(vt_frag_at(orow + 32 * c * D + vo1), pbf, V1);
+                H0 = mfma(vt_frag_at(qrow + 32 * c * D + vo0), dsb, H0);
+                H1 = mfma(vt_frag_at(qrow + 32 * c * D + vo1), dsb, H1);
             }
             // lane holds channels 4 grp..+3 and 16 + 4 grp..+3 of key slot sk
             float k8[8], h8[8], dkv[8];

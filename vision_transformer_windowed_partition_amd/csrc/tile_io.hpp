@@ -159,6 +159,27 @@ __device__ __forceinline__ bf16x8 vt_frag(const __bf16* vst, int c, int dt, int 
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// The same with the lane's addresses taken apart: the swizzle of slot
+// 32 c + 8 grp + 4 h + li/4 depends on neither c nor h, so the fragment of
+// chunk c is read at vt_off(dt, grp, li) + 32 c D elements (the second
+// transposed read 4 D further), and a loop over chunks needs one base.
+__device__ __forceinline__ int vt_off(int dt, int grp, int li)
+{
+    const int s = 8 * grp + (li >> 2), m = li & 3;
+    return s * D + (((2 * dt + (m >> 1)) ^ v_swizzle(s)) * 8) + 4 * (m & 1);
+}
+__device__ __forceinline__ bf16x8 vt_frag_at(const __bf16* p)
+{
+    i16x4 half[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p + 4 * h * D));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// Element offset of 16-byte piece `piece` of slot s in swizzled 64-byte
+// rows; unchanged in its swizzle for s + 32 c, and for s + 4 when s % 8 < 4.
+__device__ __forceinline__ int row_off(int s, int piece) { return s * D + ((piece ^ v_swizzle(s)) * 8); }
+
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -378,8 +378,9 @@ const char* swin_window_attn_kernel(const swin_attn_desc* desc);
  * storage), beside the fill kernel that clears dtau and dtable:
  *   "attn_bwd_small_kernel" SWIN_DT_BF16, M * roundup8(M) <= 256 key slots,
  *                           no rotary positions;
- *   "attn_bwd_large_kernel" SWIN_DT_BF16, M <= 32 otherwise, except COSINE
- *                           with ROPE2D;
+ *   "attn_bwd_large_kernel" SWIN_DT_BF16, M <= 32 otherwise, when the
+ *                           window's rows fit LDS (COSINE with ROPE2D, which
+ *                           also stages the remainders, up to M = 24);
  *   "attn_bwd_kernel"       SWIN_DT_F32 and every other case.
  * NULL if swin_window_attn_bwd would reject the descriptor itself (also
  * d != 32 or M > 32); swin_last_error() then says why.  Enqueues nothing. */

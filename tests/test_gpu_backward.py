@@ -191,3 +191,43 @@ def test_cpb_table_backward(M, norm_M, mode, heads, hidden):
     ref = oracle.cpb_table_bwd(M, f64(w1), f64(b1), f64(w2), f64(b2), f64(dt), mode=mode, norm_M=norm_M)
     for name, gv, rv in zip(("dw1", "db1", "dw2", "db2"), got, ref):
         _check(name, f64(gv), rv, "f32")
+
+
+LSE_CASES = [
+    # H, W, M, shift, partition, sim, pos
+    (48, 32, 16, 0, "cyclic", "dot", "table"),         # diagonal bias sums, no shift regions
+    (26, 39, 13, 6, "cyclic", "cosine", "none"),       # padded slots (16-slot rows)
+    (27, 18, 9, 4, "cyclic", "dot", "table"),
+    (22, 22, 11, 0, "interleaved", "cosine", "table"),
+    (30, 45, 15, 7, "cyclic", "cosine", "table"),
+    (24, 24, 12, 6, "cyclic", "dot", "none"),
+]
+
+
+@pytest.mark.parametrize("case", LSE_CASES, ids=[f"{c[0]}x{c[1]}-M{c[2]}-s{c[3]}-{c[4][:3]}-{c[5]}-{c[6]}"
+                                                 for c in LSE_CASES])
+def test_backward_small_given_lse(case):
+    """The small-window backward given the forward's log-sum-exp on window
+    sizes 9 to 16 (padded key rows, shift regions, interleaved windows,
+    dot and cosine, with and without the table), at the bf16 bars."""
+    H, W, M, s, part, sim, pos = case
+    heads = 2
+    wl = synth.small(B=2, H=H, W=W, C=32 * heads, heads=heads, M=M, shift=s, partition=part, sim=sim, pos=pos,
+                     dtype="bf16", hidden=64)
+    desc = binding.make_desc(B=wl.B, H=H, W=W, C=wl.C, heads=heads, M=M, shift=s, partition=part, sim=sim, pos=pos,
+                             dtype=torch.bfloat16)
+    assert binding.swin_window_attn_bwd_kernel(desc) == "attn_bwd_small_kernel"
+    x = synth.make_inputs(wl, seed=60 + M)
+    g = gpu_inputs(x)
+    table = table64 = None
+    if pos == "table":
+        gen = torch.Generator().manual_seed(7 + M)
+        t = 0.5 * torch.randn(((2 * M - 1) ** 2, heads), generator=gen)
+        table, table64 = t.to(DEV), f64(t)
+    got, ref = _run(wl, x, g, synth.make_dout(wl), table, table64, lse_from="gpu")
+    for name in ("dq", "dk", "dv"):
+        _check(f"{case} {name}", f64(got[name]), ref[name], "bf16")
+    if sim == "cosine":
+        _check(f"{case} dtau", f64(got["dtau"]), ref["dtau"], "bf16")
+    if pos == "table":
+        _check(f"{case} dtable", f64(got["dtable"]), ref["dtable"], "bf16")

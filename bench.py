@@ -48,10 +48,15 @@ KERNEL_SOURCE = {"attn_small_kernel": "attn_small.hip", "attn_large_kernel": "at
                  "attn_video_mfma_kernel": "attn_video_mfma.hip"}
 
 
+# headers a kernel's file includes beyond the shared ones
+KERNEL_HEADERS = {"attn_small_kernel": ("small_core.hpp",)}
+
+
 def kernel_sha(kernel: str) -> str:
-    """Hash of the sources that define `kernel` (its file and the shared headers)."""
+    """Hash of the sources that define `kernel` (its file and the headers it includes)."""
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCE[kernel], "common.hpp", "launch.hpp", "tile_io.hpp", "lanes.hpp"):
+    for f in (KERNEL_SOURCE[kernel], *KERNEL_HEADERS.get(kernel, ()), "common.hpp", "launch.hpp", "tile_io.hpp",
+              "lanes.hpp"):
         with open(os.path.join(ROOT, "vision_transformer_windowed_partition_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -199,7 +199,9 @@ int swin_window_attn_fwd_lse(const swin_attn_desc* desc, const void* q, const vo
  * an input or each other.  dtau: heads fp32 (COSINE; NULL skips it), dtable:
  * (2M-1)^2 x heads fp32 (POS_TABLE; NULL skips it): both written (sums over
  * the windows, accumulated with fp32 atomics, so the last bits depend on
- * order).  Requires d = 32 and M <= 32 (SWIN_EUNSUPPORTED otherwise).
+ * order).  Requires d = 32 and M <= 64, with the per-query statistics and
+ * (POS_TABLE) the table and its gradient fitting the vector kernel's LDS:
+ * POS_TABLE up to M = 55 (SWIN_EUNSUPPORTED otherwise).
  * Arithmetic: SWIN_DT_F32 runs in fp32 on the vector ALUs.  SWIN_DT_BF16
  * runs its contractions on bf16 matrix cores with fp32 accumulation: the
  * stored bf16 inputs enter as they are, the softmax weights p and the score
@@ -383,7 +385,8 @@ const char* swin_window_attn_kernel(const swin_attn_desc* desc);
  *                           also stages the remainders, up to M = 24);
  *   "attn_bwd_kernel"       SWIN_DT_F32 and every other case.
  * NULL if swin_window_attn_bwd would reject the descriptor itself (also
- * d != 32 or M > 32); swin_last_error() then says why.  Enqueues nothing. */
+ * d != 32, M > 64 or LDS); swin_last_error() then says why.  Enqueues
+ * nothing. */
 const char* swin_window_attn_bwd_kernel(const swin_attn_desc* desc);
 
 /* Text for a status code (static storage). */

@@ -255,7 +255,8 @@ def test_backward_rejects(L):
     d = _desc()
     assert _bwd(L, None) == SWIN_EINVAL
     assert _bwd(L, _desc(H=12)) == SWIN_EUNSUPPORTED
-    assert _bwd(L, _desc(H=48, W=48, M=48, shift=0)) == SWIN_EUNSUPPORTED       # M > 32
+    assert _bwd(L, _desc(H=56, W=56, M=56, shift=0)) == SWIN_EUNSUPPORTED       # table and statistics past LDS
+    assert _bwd(L, _desc(H=72, W=72, M=72, shift=0)) == SWIN_EUNSUPPORTED       # M > 64
     assert _bwd(L, d, dout=None) == SWIN_EINVAL
     assert _bwd(L, d, out=None) == SWIN_EINVAL
     assert _bwd(L, d, dk=None) == SWIN_EINVAL
@@ -310,8 +311,9 @@ def test_backward_kernel_query_names_the_dispatch(L):
     rotary positions -> the small matrix-core kernel; other bf16 windows up to
     M = 32 whose rows fit in LDS (cosine with rotary positions also keeps the
     remainders of its rotated rows, which fit up to M = 24) -> the large
-    matrix-core kernel; fp32 and the rest -> the vector-ALU kernel; d != 32
-    or M > 32 is rejected."""
+    matrix-core kernel; fp32 and the rest -> the vector-ALU kernel (M <= 64
+    where its statistics and table fit LDS); d != 32 and the rest are
+    rejected."""
     from vision_transformer_windowed_partition_amd import synth
     want = ["attn_bwd_kernel", "attn_bwd_small_kernel", "attn_bwd_small_kernel", "attn_bwd_large_kernel",
             "attn_bwd_large_kernel"]
@@ -327,8 +329,10 @@ def test_backward_kernel_query_names_the_dispatch(L):
         "attn_bwd_large_kernel"
     assert binding.swin_window_attn_bwd_kernel(_desc(M=32, H=32, W=32, shift=16, pos=2, sim=0)) == "attn_bwd_kernel"
     assert binding.swin_window_attn_bwd_kernel(_desc(M=8, dtype=0)) == "attn_bwd_kernel"
-    assert L.swin_window_attn_bwd_kernel(ctypes.byref(_desc(M=48, H=48, W=48, shift=0))) is None
-    assert "M=48" in binding.swin_last_error()
+    assert binding.swin_window_attn_bwd_kernel(_desc(M=48, H=48, W=48, shift=0)) == "attn_bwd_kernel"
+    assert binding.swin_window_attn_bwd_kernel(_desc(M=64, H=64, W=64, shift=0, pos=0)) == "attn_bwd_kernel"
+    assert L.swin_window_attn_bwd_kernel(ctypes.byref(_desc(M=56, H=56, W=56, shift=0))) is None
+    assert "M=56" in binding.swin_last_error()
     assert L.swin_window_attn_bwd_kernel(ctypes.byref(_desc(C=128))) is None
     assert L.swin_window_attn_bwd_kernel(None) is None
 

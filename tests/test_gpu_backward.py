@@ -231,3 +231,31 @@ def test_backward_small_given_lse(case):
         _check(f"{case} dtau", f64(got["dtau"]), ref["dtau"], "bf16")
     if pos == "table":
         _check(f"{case} dtable", f64(got["dtable"]), ref["dtable"], "bf16")
+
+
+@pytest.mark.parametrize("M,shift,sim,pos,dtype,lse_from", [(48, 24, "cosine", "table", "bf16", "gpu"),
+                                                            (40, 0, "dot", "rope2d", "f32", None),
+                                                            (64, 32, "cosine", "none", "bf16", None)])
+def test_backward_windows_past_32(M, shift, sim, pos, dtype, lse_from):
+    """Windows above 32 x 32 (the forward's key-blocked range) on the
+    vector-ALU backward, one window a head, at the bars of the dtype."""
+    heads = 2
+    wl = synth.small(B=1, H=M, W=M, C=32 * heads, heads=heads, M=M, shift=shift, sim=sim, pos=pos, dtype=dtype,
+                     hidden=64)
+    desc = binding.make_desc(B=1, H=M, W=M, C=wl.C, heads=heads, M=M, shift=shift, sim=sim, pos=pos,
+                             dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+    assert binding.swin_window_attn_bwd_kernel(desc) == "attn_bwd_kernel"
+    x = synth.make_inputs(wl, seed=M)
+    g = gpu_inputs(x)
+    table = table64 = None
+    if pos == "table":
+        gen = torch.Generator().manual_seed(M)
+        t = 0.5 * torch.randn(((2 * M - 1) ** 2, heads), generator=gen)
+        table, table64 = t.to(DEV), f64(t)
+    got, ref = _run(wl, x, g, synth.make_dout(wl), table, table64, lse_from=lse_from)
+    for name in ("dq", "dk", "dv"):
+        _check(f"M={M} {name}", f64(got[name]), ref[name], dtype)
+    if sim == "cosine":
+        _check(f"M={M} dtau", f64(got["dtau"]), ref["dtau"], dtype)
+    if pos == "table":
+        _check(f"M={M} dtable", f64(got["dtable"]), ref["dtable"], dtype)

@@ -50,8 +50,6 @@ def test_random_forward(seed):
 @pytest.mark.parametrize("seed", SEEDS[:20])
 def test_random_backward(seed):
     kw = _case(seed)
-    if kw["M"] > 32:
-        pytest.skip("the backward is built for M <= 32")
     wl = synth.small(**kw, hidden=64)
     x = synth.make_inputs(wl, seed=2000 + seed)
     g = gpu_inputs(x)

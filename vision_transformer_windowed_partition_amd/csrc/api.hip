@@ -240,7 +240,8 @@ int attn_bwd(const swin_attn_desc* d, const void* q, const void* k, const void* 
     int st = check_desc(d, rope_freqs != nullptr);
     if (st) return st;
     if (d->C != d->heads * 32) return fail(SWIN_EUNSUPPORTED, "backward: head dim %d (32 only)", d->C / d->heads);
-    if (d->M > 32) return fail(SWIN_EUNSUPPORTED, "backward: M=%d (32 at most)", d->M);
+    if (!swin::attn_bwd_supported(params_of(d)))
+        return fail(SWIN_EUNSUPPORTED, "backward: M=%d (up to 64, where the statistics and table fit LDS)", d->M);
     const size_t es = d->dtype == SWIN_DT_F32 ? 4 : 2;
     const size_t bytes = (size_t)d->B * d->H * d->W * d->C * es;
     if (d->sim == SWIN_SIM_COSINE && !tau) return fail(SWIN_EINVAL, "COSINE needs tau");
@@ -546,8 +547,8 @@ const char* swin_window_attn_bwd_kernel(const swin_attn_desc* d)
         fail(SWIN_EUNSUPPORTED, "backward: head dim %d (32 only)", d->C / d->heads);
         return nullptr;
     }
-    if (d->M > 32) {
-        fail(SWIN_EUNSUPPORTED, "backward: M=%d (32 at most)", d->M);
+    if (!swin::attn_bwd_supported(params_of(d))) {
+        fail(SWIN_EUNSUPPORTED, "backward: M=%d (up to 64, where the statistics and table fit LDS)", d->M);
         return nullptr;
     }
     const swin::AttnParams p = params_of(d);

@@ -1,5 +1,5 @@
 // Backward of window attention on the vector ALUs, any dtype, windows of up
-// to 32 x 32 tokens.
+// to 64 x 64 tokens whose per-query statistics and table fit LDS.
 //
 // The forward is the SwinV2 card's eq. 1-2 with the log-CPB table of eq. 3-4,
 // cyclic-shift or interleaved windows, and the FlashSwin abstract's
@@ -378,7 +378,21 @@ hipError_t dispatch_sim(const AttnParams& p, const BwdArgs& a, dim3 grid, size_t
 
 }  // namespace
 
-bool attn_bwd_supported(const AttnParams& p) { return p.g.d == D && p.g.M <= 32; }
+// LDS of the vector-ALU kernel: two operand blocks, three per-query
+// statistics, and the table and its gradient (TABLE) or the angles (ROPE2D)
+size_t attn_bwd_lds(const AttnParams& p)
+{
+    const int S = 2 * p.g.M - 1;
+    size_t lds = (size_t)(2 * BLK * D + 3 * p.g.N + TPB / 64) * sizeof(float);
+    if (p.pos == SWIN_POS_TABLE) lds += (size_t)2 * S * S * sizeof(float);
+    if (p.pos == SWIN_POS_ROPE2D) lds += (size_t)p.g.M * D * sizeof(float);
+    return lds;
+}
+
+bool attn_bwd_supported(const AttnParams& p)
+{
+    return p.g.d == D && p.g.M <= 64 && attn_bwd_lds(p) <= 160 * 1024;
+}
 
 hipError_t launch_attn_bwd(const AttnParams& p, const void* out, const void* dout, void* dq, void* dk, void* dv,
                            float* dtau, float* dtable, hipStream_t stream)
@@ -400,9 +414,7 @@ hipError_t launch_attn_bwd(const AttnParams& p, const void* out, const void* dou
         return launch_attn_bwd_small(p, out, dout, dq, dk, dv, a.dtau, a.dtable, stream);
     if (attn_bwd_large_supported(p))
         return launch_attn_bwd_large(p, out, dout, dq, dk, dv, a.dtau, a.dtable, stream);
-    size_t lds = (size_t)(2 * BLK * D + 3 * g.N + TPB / 64) * sizeof(float);
-    if (p.pos == SWIN_POS_TABLE) lds += (size_t)2 * S * S * sizeof(float);
-    if (p.pos == SWIN_POS_ROPE2D) lds += (size_t)g.M * D * sizeof(float);
+    const size_t lds = attn_bwd_lds(p);
     dim3 grid(g.nwin, g.heads);
     if (p.dtype == SWIN_DT_F32) return dispatch_sim<float>(p, a, grid, lds, stream);
     return dispatch_sim<uint16_t>(p, a, grid, lds, stream);

@@ -10,7 +10,8 @@ hipError_t launch_cpb_table_bwd(int M, int norm_M, int heads, int hidden, const 
                                 const float* w2, const float* table, const float* dtable, int mode, float* dw1,
                                 float* db1, float* dw2, float* db2, hipStream_t stream);
 
-// Backward of the window attention (vector ALUs; d = 32, M <= 32).
+// Backward of the window attention (vector ALUs; d = 32, M <= 64 where the
+// statistics and table fit LDS; the matrix-core kernels take bf16 M <= 32).
 bool attn_bwd_supported(const AttnParams& p);
 hipError_t launch_attn_bwd(const AttnParams& p, const void* out, const void* dout, void* dq, void* dk, void* dv,
                            float* dtau, float* dtable, hipStream_t stream);

@@ -87,6 +87,8 @@ def _declare(lib):
     lib.oracle_cpb_table3d.argtypes = [i32] * 4 + [vp] * 5
     lib.oracle_window_attn3d.restype = i32
     lib.oracle_window_attn3d.argtypes = [i32] * 13 + [dbl] + [vp] * 5 + [vp, i64, vp]
+    lib.oracle_table_resize.restype = i32
+    lib.oracle_table_resize.argtypes = [i32] * 3 + [vp] * 2
     lib.oracle_set_threads.restype = None
     lib.oracle_set_threads.argtypes = [i32]
     lib.oracle_max_threads.restype = i32
@@ -153,6 +155,19 @@ def cpb_table(M: int, w1, b1, w2, b2, lib=None, mode: int = 0, norm_M: int | Non
                                      _ptr(w2), _ptr(b2), int(mode), _ptr(out))
     if rc:
         raise ValueError(f"oracle_cpb_table: bad argument (rc={rc})")
+    return out
+
+
+def table_resize(table, Ms: int, Md: int, lib=None) -> np.ndarray:
+    """A Swin V1 (2Ms-1)^2 x heads bias table resampled bi-cubically to
+    (2Md-1)^2 x heads (SwinV2 card, Problem and tab. 1)."""
+    t = _f64(table)
+    heads = t.shape[1]
+    assert t.shape == ((2 * Ms - 1) ** 2, heads)
+    out = np.empty(((2 * Md - 1) ** 2, heads), dtype=np.float64)
+    rc = (lib or load()).oracle_table_resize(Ms, Md, heads, _ptr(t), _ptr(out))
+    if rc:
+        raise ValueError(f"oracle_table_resize: bad argument (rc={rc})")
     return out
 
 

@@ -1053,3 +1053,57 @@ int oracle_window_attn3d(int B, int T, int H, int W, int C, int heads, int Mt, i
     }
     return failed ? 2 : 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * Swin V1 bias table at a new window size ([SwinV2] Problem and tab. 1: the
+ * earlier model's parameterised (2M-1)^2 x heads table, interpolated
+ * bi-cubically when the window changes; log-CPB replaces it).  Reading (the
+ * page names the method only): each head's table is an image, rows dy,
+ * columns dx, resampled from (2Ms-1)^2 to (2Md-1)^2 by separable cubic
+ * convolution with Keys' kernel, a = -0.75; output sample x sits at source
+ * coordinate (x + 1/2) Ss / Sd - 1/2 (sample centres aligned), and taps
+ * outside the table take its border value.
+ * ------------------------------------------------------------------------- */
+static double keys_cubic(double t)
+{
+    const double a = -0.75;
+    const double u = fabs(t);
+    if (u <= 1.0) return ((a + 2.0) * u - (a + 3.0)) * u * u + 1.0;
+    if (u < 2.0) return ((a * u - 5.0 * a) * u + 8.0 * a) * u - 4.0 * a;
+    return 0.0;
+}
+
+/* source taps i0 - 1 .. i0 + 2 of output sample o and their weights */
+static void resize_taps(int o, int Ss, int Sd, int* idx, double* w)
+{
+    const double s = ((double)o + 0.5) * (double)Ss / (double)Sd - 0.5;
+    const double f = floor(s);
+    const int i0 = (int)f;
+    for (int m = 0; m < 4; ++m) {
+        const int i = i0 - 1 + m;
+        idx[m] = i < 0 ? 0 : i > Ss - 1 ? Ss - 1 : i;
+        w[m] = keys_cubic(s - (double)i);
+    }
+}
+
+int oracle_table_resize(int Ms, int Md, int heads, const double* src, double* dst)
+{
+    if (Ms < 1 || Md < 1 || heads < 1 || !src || !dst) return 1;
+    const int Ss = 2 * Ms - 1, Sd = 2 * Md - 1;
+    for (int y = 0; y < Sd; ++y) {
+        int iy[4], ix[4];
+        double wy[4], wx[4];
+        resize_taps(y, Ss, Sd, iy, wy);
+        for (int x = 0; x < Sd; ++x) {
+            resize_taps(x, Ss, Sd, ix, wx);
+            for (int h = 0; h < heads; ++h) {
+                double acc = 0.0;
+                for (int m = 0; m < 4; ++m)
+                    for (int n = 0; n < 4; ++n)
+                        acc += wy[m] * wx[n] * src[((size_t)iy[m] * Ss + (size_t)ix[n]) * heads + h];
+                dst[((size_t)y * Sd + (size_t)x) * heads + h] = acc;
+            }
+        }
+    }
+    return 0;
+}

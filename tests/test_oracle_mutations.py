@@ -17,6 +17,13 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
 # (name, original text, planted text)
 MUTATIONS = [
+    ("resize_keys_a", "const double a = -0.75;", "const double a = -0.5;"),
+    ("resize_corners_aligned", "((double)o + 0.5) * (double)Ss / (double)Sd - 0.5",
+     "(double)o * (double)(Ss - 1) / (double)(Sd > 1 ? Sd - 1 : 1)"),
+    ("resize_border_zero", "idx[m] = i < 0 ? 0 : i > Ss - 1 ? Ss - 1 : i;\n        w[m] = keys_cubic(s - (double)i);",
+     "idx[m] = i < 0 ? 0 : i > Ss - 1 ? Ss - 1 : i;\n        w[m] = (i < 0 || i > Ss - 1) ? 0.0 : keys_cubic(s - (double)i);"),
+    ("resize_rows_cols", "src[((size_t)iy[m] * Ss + (size_t)ix[n]) * heads + h]",
+     "src[((size_t)ix[n] * Ss + (size_t)iy[m]) * heads + h]"),
     ("log_sign", "if (x > 0) return a;", "if (x > 0) return -a;"),
     ("log_base2", "log1p(fabs(x))", "log2(1.0 + fabs(x))"),
     ("relu_dropped", "h[j] = a > 0.0 ? a : 0.0;", "h[j] = a;"),

@@ -700,6 +700,41 @@ def pin_window_linear(lib):
     assert np.allclose(got, out, rtol=1e-12, atol=1e-12)
 
 
+def pin_table_resize(lib):
+    """Swin V1 table at a new window size (SwinV2 card, Problem and tab. 1:
+    bicubic interpolation; the reading: Keys' cubic convolution, a = -0.75,
+    sample centres aligned, border replicated).  Pins: the same convolution
+    in torch's fp64 bicubic resampling (up and down), the identity at the
+    same size, constants kept (the four weights sum to 1), and Keys' kernel
+    at its knots (w(0) = 1, w(1) = w(2) = 0), and on a linear ramp inside
+    the table the kernel's first moment in closed form: with s = i + t,
+    sum_m w(t - m) m = t - (2a + 1) t (1 - t) (1 - 2t), so a = -0.75 lifts a
+    ramp by t (1 - t) (1 - 2t) / 2 (a = -0.5 would reproduce it)."""
+    import torch
+    rng = np.random.default_rng(7)
+    for Ms, Md, H in ((7, 12, 3), (12, 7, 2), (8, 24, 4), (2, 5, 1), (16, 9, 2)):
+        t = rng.standard_normal(((2 * Ms - 1) ** 2, H))
+        got = oracle.table_resize(t, Ms, Md, lib)
+        img = torch.from_numpy(t).T.reshape(1, H, 2 * Ms - 1, 2 * Ms - 1)
+        want = torch.nn.functional.interpolate(img, size=(2 * Md - 1, 2 * Md - 1), mode="bicubic",
+                                               align_corners=False).reshape(H, -1).T.numpy()
+        assert np.abs(got - want).max() <= 1e-12, (Ms, Md)
+    t = rng.standard_normal((13 ** 2, 2))
+    assert np.array_equal(oracle.table_resize(t, 7, 7, lib), t)
+    const = np.full((9 ** 2, 3), 2.5)
+    assert np.abs(oracle.table_resize(const, 5, 11, lib) - 2.5).max() <= 1e-14
+    # a ramp in dx, away from the border
+    Ms, Md = 8, 15
+    Ss, Sd = 2 * Ms - 1, 2 * Md - 1
+    ramp = np.tile(np.arange(Ss, dtype=np.float64), Ss).reshape(-1, 1)
+    got = oracle.table_resize(ramp, Ms, Md, lib).reshape(Sd, Sd)
+    for x in range(Sd):
+        s = (x + 0.5) * Ss / Sd - 0.5
+        if 1.0 <= s <= Ss - 3.0:
+            t = s - math.floor(s)
+            assert got[Sd // 2, x] == pytest.approx(s + 0.5 * t * (1 - t) * (1 - 2 * t), abs=1e-12), x
+
+
 PINS = {
     "worked_example": pin_worked_example,
     "cpb_vs_torch": pin_cpb_vs_torch,
@@ -725,6 +760,7 @@ PINS = {
     "lse": pin_lse,
     "video_bruteforce": pin_video_bruteforce,
     "video_reduces_to_2d": pin_video_reduces_to_2d,
+    "table_resize": pin_table_resize,
 }
 
 

@@ -137,6 +137,21 @@ int swin_cpb_table_ex(int32_t M, int32_t norm_M, int32_t heads, int32_t hidden,
                       const float* w1, const float* b1, const float* w2, const float* b2,
                       int32_t cpb_mode, float* table, void* stream);
 
+/* A parameterised (Swin V1) bias table carried to another window size by
+ * bicubic interpolation, the transfer log-CPB replaces ([SwinV2] card,
+ * Problem and tab. 1).  Each head's (2*M_src-1) x (2*M_src-1) table, rows
+ * dy and columns dx in the layout swin_cpb_table writes, is resampled to
+ * (2*M_dst-1) x (2*M_dst-1): separable cubic convolution with Keys' kernel,
+ * a = -0.75, output sample x at source coordinate (x + 1/2) S_src/S_dst - 1/2,
+ * taps past the border taking the border value (the page names the method
+ * only; this is the common reading).  Weights and sums in fp32.
+ * src: (2*M_src-1)^2 x heads fp32, dst: (2*M_dst-1)^2 x heads fp32, device
+ * memory owned by the caller, dst not overlapping src; 1 <= M_src, M_dst <= 64,
+ * 1 <= heads <= 64.  Errors: SWIN_EINVAL for a bad size, a NULL pointer or an
+ * overlap (nothing is written then). */
+int swin_cpb_table_resize(int32_t M_src, int32_t M_dst, int32_t heads, const float* src, float* dst,
+                          void* stream);
+
 /* Window partition (gather) of a (B, H, W, C) grid into (B*nW, M*M, C), and
  * its inverse (scatter).  A bit-exact copy of C elements per token; dtype
  * gives the element size.  x and xw must not overlap. */

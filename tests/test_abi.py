@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
                                            "swin_window_attn_fwd_lse", "swin_window_attn_bwd_lse",
                                            "swin_cpb_table3d", "swin_window_attn3d_fwd",
                                            "swin_window_attn3d_kernel",
-                                           "swin_window_attn_bwd_kernel",
+                                           "swin_window_attn_bwd_kernel", "swin_cpb_table_resize",
                                            "swin_qkv_proj", "swin_qkv_window_attn_fwd", "swin_proj_post_norm",
                                            "swin_dwconv_add",
                                            "swin_window_linear",
@@ -371,6 +371,13 @@ def test_cpb_rejects(L):
     assert C(8, 3, 512, None, None, FAKE, None, 0, T, None) == SWIN_EINVAL
     assert C(8, 3, 512, FAKE, None, FAKE, None, 0, None, None) == SWIN_EINVAL
     assert C(8, 3, 512, FAKE, None, FAKE, None, 0, FAKE, None) == SWIN_EINVAL      # table over w1
+    R = L.swin_cpb_table_resize
+    assert R(0, 8, 3, FAKE, T, None) == SWIN_EINVAL                                # window sizes
+    assert R(8, 65, 3, FAKE, T, None) == SWIN_EINVAL
+    assert R(8, 12, 0, FAKE, T, None) == SWIN_EINVAL                               # heads
+    assert R(8, 12, 3, None, T, None) == SWIN_EINVAL
+    assert R(8, 12, 3, FAKE, None, None) == SWIN_EINVAL
+    assert R(8, 12, 3, FAKE, FAKE, None) == SWIN_EINVAL                            # dst over src
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -96,3 +96,18 @@ def test_cpb_table_large_weights():
     torch.cuda.synchronize()
     want = oracle.cpb_table(12, f64(w1), f64(b1), f64(w2), f64(b2))
     np.testing.assert_allclose(got.double().cpu().numpy(), want, rtol=1e-5, atol=1e-4)
+
+
+@pytest.mark.parametrize("Ms,Md,heads", [(7, 12, 3), (12, 7, 2), (8, 8, 4), (16, 24, 16), (2, 32, 1), (24, 16, 6)])
+def test_cpb_table_resize(Ms, Md, heads):
+    """swin_cpb_table_resize (a Swin V1 table carried to another window size
+    by bicubic interpolation) against the fp64 oracle: fp32 weights and sums
+    over 16 taps, within 1e-5 relative and 1e-5 absolute."""
+    gen = torch.Generator().manual_seed(Ms * 100 + Md)
+    t = torch.randn(((2 * Ms - 1) ** 2, heads), generator=gen)
+    got = binding.swin_cpb_table_resize(t.to(DEV), Ms, Md)
+    torch.cuda.synchronize()
+    want = oracle.table_resize(t.double().numpy(), Ms, Md)
+    np.testing.assert_allclose(got.cpu().double().numpy(), want, rtol=1e-5, atol=1e-5)
+    if Ms == Md:
+        assert torch.equal(got.cpu(), t)

@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.swin_cpb_table.argtypes = [i32, i32, i32, vp, vp, vp, vp, i32, vp, vp]
         L.swin_cpb_table_ex.restype = i32
         L.swin_cpb_table_ex.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp]
+        L.swin_cpb_table_resize.restype = i32
+        L.swin_cpb_table_resize.argtypes = [i32, i32, i32, vp, vp, vp]
         for fn in (L.swin_window_partition, L.swin_window_reverse):
             fn.restype = i32
             fn.argtypes = [vp, vp] + [i32] * 8 + [vp]
@@ -185,6 +187,24 @@ def swin_cpb_table(M: int, w1, b1, w2, b2, *, out=None, cpb_mode: int = CPB_PAPE
     else:
         _check(lib().swin_cpb_table_ex(M, norm_M, heads, hidden, _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
                                        cpb_mode, _ptr(out), _stream(w1, stream)))
+    return out
+
+
+def swin_cpb_table_resize(table, M_src: int, M_dst: int, *, out=None, stream=None):
+    """A (2*M_src-1)^2 x heads fp32 bias table resampled bi-cubically to
+    (2*M_dst-1)^2 x heads (the Swin V1 transfer between window sizes)."""
+    if table.dtype != torch.float32 or not table.is_contiguous() or table.dim() != 2:
+        raise ValueError("the table must be a contiguous 2D fp32 tensor")
+    heads = table.shape[1]
+    if table.shape[0] != (2 * M_src - 1) ** 2:
+        raise ValueError(f"table rows {table.shape[0]} != (2*{M_src}-1)^2")
+    if out is None:
+        out = torch.empty(((2 * M_dst - 1) ** 2, heads), dtype=torch.float32, device=table.device)
+    elif out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != ((2 * M_dst - 1) ** 2, heads):
+        raise ValueError("out must be a contiguous fp32 ((2*M_dst-1)^2, heads) tensor")
+    if out.device != table.device:
+        raise ValueError("table and out must be on one device")
+    _check(lib().swin_cpb_table_resize(M_src, M_dst, heads, _ptr(table), _ptr(out), _stream(table, stream)))
     return out
 
 

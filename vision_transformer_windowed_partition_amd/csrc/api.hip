@@ -136,6 +136,19 @@ int swin_cpb_table(int32_t M, int32_t heads, int32_t hidden, const float* w1, co
     return swin_cpb_table_ex(M, M, heads, hidden, w1, b1, w2, b2, cpb_mode, table, stream);
 }
 
+int swin_cpb_table_resize(int32_t M_src, int32_t M_dst, int32_t heads, const float* src, float* dst, void* stream)
+{
+    if (M_src < 1 || M_src > 64 || M_dst < 1 || M_dst > 64)
+        return fail(SWIN_EINVAL, "windows %d -> %d outside [1, 64]", M_src, M_dst);
+    if (heads < 1 || heads > 64) return fail(SWIN_EINVAL, "heads=%d outside [1, 64]", heads);
+    if (!src || !dst) return fail(SWIN_EINVAL, "NULL src or dst");
+    const size_t ns = (size_t)(2 * M_src - 1) * (2 * M_src - 1) * heads * sizeof(float);
+    const size_t nd = (size_t)(2 * M_dst - 1) * (2 * M_dst - 1) * heads * sizeof(float);
+    if (overlaps(dst, nd, src, ns)) return fail(SWIN_EINVAL, "dst overlaps src");
+    return hip_status(swin::launch_table_resize(M_src, M_dst, heads, src, dst, (hipStream_t)stream),
+                      "swin_cpb_table_resize launch");
+}
+
 int swin_window_partition(const void* x, void* xw, int32_t B, int32_t H, int32_t W, int32_t C,
                           int32_t M, int32_t shift, int32_t partition, int32_t dtype, void* stream)
 {

@@ -238,4 +238,55 @@ hipError_t launch_cpb_table(int M, int norm_M, int heads, int hidden, const floa
     return hipGetLastError();
 }
 
+// ---- a Swin V1 bias table at a new window size: each head's (2Ms-1)^2
+// table resampled bi-cubically to (2Md-1)^2 (SwinV2 card, Problem and tab. 1),
+// by separable cubic convolution with Keys' kernel (a = -0.75), sample
+// centres aligned and the border replicated.  One thread per output entry and
+// head; weights and sums in fp32.
+namespace {
+
+__device__ __forceinline__ float keys_w(float t)
+{
+    constexpr float a = -0.75f;
+    const float u = fabsf(t);
+    if (u <= 1.0f) return ((a + 2.0f) * u - (a + 3.0f)) * u * u + 1.0f;
+    if (u < 2.0f) return ((a * u - 5.0f * a) * u + 8.0f * a) * u - 4.0f * a;
+    return 0.0f;
+}
+
+__global__ void __launch_bounds__(256)
+table_resize_kernel(int Ss, int Sd, int heads, const float* src, float* dst)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= Sd * Sd * heads) return;
+    const int h = i % heads, yx = i / heads, y = yx / Sd, x = yx - y * Sd;
+    const float scale = (float)Ss / (float)Sd;
+    const float sy = ((float)y + 0.5f) * scale - 0.5f, sx = ((float)x + 0.5f) * scale - 0.5f;
+    const int y0 = (int)floorf(sy), x0 = (int)floorf(sx);
+    float acc = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int iy = min(max(y0 - 1 + m, 0), Ss - 1);
+        const float wy = keys_w(sy - (float)(y0 - 1 + m));
+        float row = 0.0f;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int ix = min(max(x0 - 1 + n, 0), Ss - 1);
+            row = fmaf(keys_w(sx - (float)(x0 - 1 + n)), src[((size_t)iy * Ss + ix) * heads + h], row);
+        }
+        acc = fmaf(wy, row, acc);
+    }
+    dst[i] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_table_resize(int Ms, int Md, int heads, const float* src, float* dst, hipStream_t stream)
+{
+    const int Ss = 2 * Ms - 1, Sd = 2 * Md - 1;
+    const int n = Sd * Sd * heads;
+    table_resize_kernel<<<(n + 255) / 256, 256, 0, stream>>>(Ss, Sd, heads, src, dst);
+    return hipGetLastError();
+}
+
 }  // namespace swin

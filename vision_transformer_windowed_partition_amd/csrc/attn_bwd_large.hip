@@ -97,6 +97,9 @@ __device__ __forceinline__ float row_shr(float x)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
 }
 
+template <bool B> struct Flag { static constexpr bool value = B; };
+template <int V> struct Mode { static constexpr int value = V; };
+
 __device__ __forceinline__ bf16x4 load8b(Rsrc r, uint32_t off)
 {
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
@@ -379,66 +382,97 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
         // pass B: dq
         f32x4 G0 = {0.0f, 0.0f, 0.0f, 0.0f}, G1 = G0;
         float dts = 0.0f;                                  // sum over keys of dS~ s (dtau without a_i)
-        for (int c = 0; c < nch; ++c) {
-            const bf16x8 va = fragA(rowB, c, 0), vb = fragA(rowB, c, 1);
-            const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-            f32x4 sa, sb;
-            scores(c, sa, sb);
-            const f32x4 pa = mfma(va, gfr, z), pb = mfma(vb, gfr, z);
-            const f32x4 k0 = *(const f32x4*)(ksc + 32 * c + 8 * grp);
-            const f32x4 k1 = *(const f32x4*)(ksc + 32 * c + 8 * grp + 4);
-            const int gam = 4 * c + grp, rj = qdiv(gam, L.inv_GPR), cj0 = 8 * (gam - rj * L.GPR);
-            const int boff = qoff + rj * S + cj0;
-            const uint32_t bits = tv ? group_bits(rj, cj0) : 0u;
-            float ds[8], dlv[8];
+        // MASK false: no padded slot, shift region or tail query in the
+        // window, so every pair is kept and the loop carries no selects
+        // TM: bias-gradient sums, 0 none, 1 one LDS atomic per element,
+        // 2 diagonal sums (M a multiple of 8)
+        auto pass_b = [&](auto mflag, auto tflag) {
+            constexpr bool MASK = decltype(mflag)::value;
+            constexpr int TM = decltype(tflag)::value;
+            for (int c = 0; c < nch; ++c) {
+                const bf16x8 va = fragA(rowB, c, 0), vb = fragA(rowB, c, 1);
+                const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+                f32x4 sa, sb;
+                scores(c, sa, sb);
+                const f32x4 pa = mfma(va, gfr, z), pb = mfma(vb, gfr, z);
+                const f32x4 k0 = *(const f32x4*)(ksc + 32 * c + 8 * grp);
+                const f32x4 k1 = *(const f32x4*)(ksc + 32 * c + 8 * grp + 4);
+                const int gam = 4 * c + grp, rj = qdiv(gam, L.inv_GPR), cj0 = 8 * (gam - rj * L.GPR);
+                const int boff = qoff + rj * S + cj0;
+                const uint32_t bits = MASK ? (tv ? group_bits(rj, cj0) : 0u) : 0xffu;
+                float ds[8], dlv[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float sv = e < 4 ? sa[e] : sb[e - 4];
-                const float dpv = e < 4 ? pa[e] : pb[e - 4];
-                const float kv = e < 4 ? k0[e] : k1[e - 4];
-                const bool ok = ((bits >> e) & 1u) != 0u;
-                float b = 0.0f;
-                if (POS == SWIN_POS_TABLE) b = bias2[ok ? boff + e : negrow];
-                // logit (log2 units) = s a_i c_j + b, a_i c_j = qs kv (DOT: kv = 1)
-                const float arg = fmaf(sv, SIM == SWIN_SIM_COSINE ? qs * kv : qs, b) - lq;
-                const float pr = __builtin_amdgcn_exp2f(ok ? arg : -INFINITY);
-                const float dl = pr * (dpv - Dq);
-                // COSINE: dS~ = dl c_j (dq's a_i after the sum); DOT: dl (1/sqrt(d) after)
-                ds[e] = SIM == SWIN_SIM_COSINE ? dl * kv : dl;
-                dlv[e] = dl;
-                if (SIM == SWIN_SIM_COSINE) dts = fmaf(ds[e], sv, dts);
-                if (POS == SWIN_POS_TABLE && a.dtable && !diag8 && ok) fixed::add(&dtab[boff + e], dl);
+                for (int e = 0; e < 8; ++e) {
+                    const float sv = e < 4 ? sa[e] : sb[e - 4];
+                    const float dpv = e < 4 ? pa[e] : pb[e - 4];
+                    const float kv = e < 4 ? k0[e] : k1[e - 4];
+                    const bool ok = !MASK || ((bits >> e) & 1u) != 0u;
+                    float b = 0.0f;
+                    if (POS == SWIN_POS_TABLE) b = MASK ? bias2[ok ? boff + e : negrow] : bias2[boff + e];
+                    // logit (log2 units) = s a_i c_j + b, a_i c_j = qs kv (DOT: kv = 1)
+                    const float arg = fmaf(sv, SIM == SWIN_SIM_COSINE ? qs * kv : qs, b) - lq;
+                    const float pr = __builtin_amdgcn_exp2f(!MASK || ok ? arg : -INFINITY);
+                    const float dl = pr * (dpv - Dq);
+                    // COSINE: dS~ = dl c_j (dq's a_i after the sum); DOT: dl (1/sqrt(d) after)
+                    ds[e] = SIM == SWIN_SIM_COSINE ? dl * kv : dl;
+                    dlv[e] = dl;
+                    if (SIM == SWIN_SIM_COSINE) dts = fmaf(ds[e], sv, dts);
+                    if (TM == 1 && (!MASK || ok)) fixed::add(&dtab[boff + e], dl);
+                }
+                if (TM == 2) {
+                    // M a multiple of 8: each 8-lane half of the tile is 8
+                    // consecutive columns of one window row, so (lane, element e)
+                    // lands at boff(lane) + e with boff falling by one per lane.
+                    // Sums along those diagonals inside each half: lane j = li % 8
+                    // gathers d = -j from lanes j + k (element k) and, for j >= 1,
+                    // d = 8 - j from lanes j - 8 + e; terms from the other half are
+                    // dropped.  Masked pairs carry dl = 0.
+                    // Element k of a lane at position j moves k lanes down for the
+                    // first sum and 8 - k lanes up for the second; it stays in its
+                    // half for the first when j >= k and for the second otherwise,
+                    // so each lane splits it before the moves and the shifted
+                    // values only add (a lane shifted in from outside the 16-lane
+                    // row reads zero).  Every lane evaluates every row shift, so
+                    // that no shift is made conditional.
+                    const int j = li & 7;
+                    float x[8], y[8];
+#pragma unroll
+                    for (int k = 1; k < 8; ++k) {
+                        x[k] = j >= k ? dlv[k] : 0.0f;
+                        y[k] = j >= k ? 0.0f : dlv[k];
+                    }
+                    float A = dlv[0];
+                    A += row_shl<1>(x[1]);
+                    A += row_shl<2>(x[2]);
+                    A += row_shl<3>(x[3]);
+                    A += row_shl<4>(x[4]);
+                    A += row_shl<5>(x[5]);
+                    A += row_shl<6>(x[6]);
+                    A += row_shl<7>(x[7]);
+                    float B = row_shr<7>(y[1]);
+                    B += row_shr<6>(y[2]);
+                    B += row_shr<5>(y[3]);
+                    B += row_shr<4>(y[4]);
+                    B += row_shr<3>(y[5]);
+                    B += row_shr<2>(y[6]);
+                    B += row_shr<1>(y[7]);
+                    if (!MASK || tv) fixed::add(&dtab[boff], A);
+                    // B is zero at j = 0 (every source is outside the half); the
+                    // add is kept there so the sum is not branched around
+                    if (!MASK || tv) fixed::add(&dtab[boff + 8], B);
+                }
+                const bf16x8 dsb = pack_bf16x8(ds);
+                G0 = mfma(vt_frag_at(rowA + 32 * c * D + vo0), dsb, G0);
+                G1 = mfma(vt_frag_at(rowA + 32 * c * D + vo1), dsb, G1);
             }
-            if (POS == SWIN_POS_TABLE && a.dtable && diag8) {
-                // M a multiple of 8: each 8-lane half of the tile is 8
-                // consecutive columns of one window row, so (lane, element e)
-                // lands at boff(lane) + e with boff falling by one per lane.
-                // Sums along those diagonals inside each half: lane j = li % 8
-                // gathers d = -j from lanes j + k (element k) and, for j >= 1,
-                // d = 8 - j from lanes j - 8 + e; terms from the other half are
-                // dropped.  Masked pairs carry dl = 0.
-                // (every lane evaluates every row shift, so that no shift is
-                // made conditional: a lane left out would read as zero)
-                const int j = li & 7;
-                const float a1 = row_shl<1>(dlv[1]), a2 = row_shl<2>(dlv[2]), a3 = row_shl<3>(dlv[3]),
-                            a4 = row_shl<4>(dlv[4]), a5 = row_shl<5>(dlv[5]), a6 = row_shl<6>(dlv[6]),
-                            a7 = row_shl<7>(dlv[7]);
-                const float b1 = row_shr<7>(dlv[1]), b2 = row_shr<6>(dlv[2]), b3 = row_shr<5>(dlv[3]),
-                            b4 = row_shr<4>(dlv[4]), b5 = row_shr<3>(dlv[5]), b6 = row_shr<2>(dlv[6]),
-                            b7 = row_shr<1>(dlv[7]);
-                const float A = dlv[0] + (j <= 6 ? a1 : 0.0f) + (j <= 5 ? a2 : 0.0f) + (j <= 4 ? a3 : 0.0f) +
-                                (j <= 3 ? a4 : 0.0f) + (j <= 2 ? a5 : 0.0f) + (j <= 1 ? a6 : 0.0f) +
-                                (j == 0 ? a7 : 0.0f);
-                const float B = (j >= 7 ? b1 : 0.0f) + (j >= 6 ? b2 : 0.0f) + (j >= 5 ? b3 : 0.0f) +
-                                (j >= 4 ? b4 : 0.0f) + (j >= 3 ? b5 : 0.0f) + (j >= 2 ? b6 : 0.0f) +
-                                (j >= 1 ? b7 : 0.0f);
-                if (tv) fixed::add(&dtab[boff], A);
-                if (tv && j >= 1) fixed::add(&dtab[boff + 8], B);
-            }
-            const bf16x8 dsb = pack_bf16x8(ds);
-            G0 = mfma(vt_frag_at(rowA + 32 * c * D + vo0), dsb, G0);
-            G1 = mfma(vt_frag_at(rowA + 32 * c * D + vo1), dsb, G1);
-        }
+        };
+        auto pass_b_masks = [&](auto tflag) {
+            if (needs_mask) pass_b(Flag<true>{}, tflag);
+            else pass_b(Flag<false>{}, tflag);
+        };
+        if (POS != SWIN_POS_TABLE || !a.dtable) pass_b_masks(Mode<0>{});
+        else if (diag8) pass_b_masks(Mode<2>{});
+        else pass_b_masks(Mode<1>{});
         // sum dl (log2-unit logit without the bias) = qs sum dS~ s
         if (SIM == SWIN_SIM_COSINE) dtau_acc = fmaf(dts, qs, dtau_acc);
         const float gs = SIM == SWIN_SIM_COSINE ? 1.0f : RS32;
@@ -500,50 +534,56 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
         const uint32_t cmask = ((chi >= 32 ? 0xffffffffu : ((1u << chi) - 1u)) & ~((1u << clo) - 1u)) &
                                (M >= 32 ? 0xffffffffu : ((1u << M) - 1u));
         f32x4 V0 = {0.0f, 0.0f, 0.0f, 0.0f}, V1 = V0, H0 = V0, H1 = V0;
-        for (int c = 0; c < nch; ++c) {
-            const bf16x8 qa = fragA(rowA, c, 0), qb = fragA(rowA, c, 1);
-            const bf16x8 ga = fragA(rowB, c, 0), gb = fragA(rowB, c, 1);
-            const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-            f32x4 sa = mfma(qa, kB, z), sb = mfma(qb, kB, z);
-            if (CR && split) {
-                sa = mfma(fragA(rowL, c, 0), kB, sa);
-                sb = mfma(fragA(rowL, c, 1), kB, sb);
-                sa = mfma(qa, kB_lo, sa);
-                sb = mfma(qb, kB_lo, sb);
-            }
-            const int qs0 = 32 * c + 8 * grp;
-            const f32x4 dA = *(const f32x4*)(dd + qs0), dB = *(const f32x4*)(dd + qs0 + 4);
-            const f32x4 pa = mfma(ga, vB, z), pb = mfma(gb, vB, z);
-            const f32x4 qsA = *(const f32x4*)(qsc + qs0), qsB = *(const f32x4*)(qsc + qs0 + 4);
-            const f32x4 lA = *(const f32x4*)(lse + qs0), lB = *(const f32x4*)(lse + qs0 + 4);
-            const int gam = 4 * c + grp, ri = qdiv(gam, L.inv_GPR), ci0 = 8 * (gam - ri * L.GPR);
-            // reversed table position of query (ri, ci0 + 7) against key (rj, cj)
-            const int rev7 = S * S - 8 - ((ri - rj + M - 1) * S + (ci0 - cj + M - 1));
-            const float* brow = bias2 + rev7;
-            const bool rok = kv_ok && ri < M && ri >= rlo && ri < rhi;
-            const uint32_t cbits = rok ? (cmask >> ci0) & 0xffu : 0u;
-            float pp[8], dsa[8];
+        auto pass_a = [&](auto mflag) {
+            constexpr bool MASK = decltype(mflag)::value;
+            for (int c = 0; c < nch; ++c) {
+                const bf16x8 qa = fragA(rowA, c, 0), qb = fragA(rowA, c, 1);
+                const bf16x8 ga = fragA(rowB, c, 0), gb = fragA(rowB, c, 1);
+                const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+                f32x4 sa = mfma(qa, kB, z), sb = mfma(qb, kB, z);
+                if (CR && split) {
+                    sa = mfma(fragA(rowL, c, 0), kB, sa);
+                    sb = mfma(fragA(rowL, c, 1), kB, sb);
+                    sa = mfma(qa, kB_lo, sa);
+                    sb = mfma(qb, kB_lo, sb);
+                }
+                const int qs0 = 32 * c + 8 * grp;
+                const f32x4 dA = *(const f32x4*)(dd + qs0), dB = *(const f32x4*)(dd + qs0 + 4);
+                const f32x4 pa = mfma(ga, vB, z), pb = mfma(gb, vB, z);
+                const f32x4 qsA = *(const f32x4*)(qsc + qs0), qsB = *(const f32x4*)(qsc + qs0 + 4);
+                const f32x4 lA = *(const f32x4*)(lse + qs0), lB = *(const f32x4*)(lse + qs0 + 4);
+                const int gam = 4 * c + grp, ri = qdiv(gam, L.inv_GPR), ci0 = 8 * (gam - ri * L.GPR);
+                // reversed table position of query (ri, ci0 + 7) against key (rj, cj)
+                const int rev7 = S * S - 8 - ((ri - rj + M - 1) * S + (ci0 - cj + M - 1));
+                const float* brow = bias2 + rev7;
+                const bool rok = kv_ok && ri < M && ri >= rlo && ri < rhi;
+                const uint32_t cbits = MASK ? (rok ? (cmask >> ci0) & 0xffu : 0u) : 0xffu;
+                float pp[8], dsa[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float sv = e < 4 ? sa[e] : sb[e - 4];
-                const float dpv = e < 4 ? pa[e] : pb[e - 4];
-                const float qv_ = e < 4 ? qsA[e] : qsB[e - 4];
-                const float lv = e < 4 ? lA[e] : lB[e - 4];
-                const bool ok = ((cbits >> e) & 1u) != 0u;
-                float b = 0.0f;
-                if (POS == SWIN_POS_TABLE) b = needs_mask ? bias2[ok ? rev7 + (7 - e) : negrow] : brow[7 - e];
-                const float pr = __builtin_amdgcn_exp2f(ok ? fmaf(sv * qv_, cj_s, b) - lv : -INFINITY);
-                pp[e] = pr;
-                const float dl = pr * (dpv - (e < 4 ? dA[e] : dB[e - 4]));
-                // dS~ = dl log2(e) a_i (COSINE) or dl (DOT); the constant after the sum
-                dsa[e] = SIM == SWIN_SIM_COSINE ? dl * qv_ : dl;
+                for (int e = 0; e < 8; ++e) {
+                    const float sv = e < 4 ? sa[e] : sb[e - 4];
+                    const float dpv = e < 4 ? pa[e] : pb[e - 4];
+                    const float qv_ = e < 4 ? qsA[e] : qsB[e - 4];
+                    const float lv = e < 4 ? lA[e] : lB[e - 4];
+                    const bool ok = !MASK || ((cbits >> e) & 1u) != 0u;
+                    float b = 0.0f;
+                    if (POS == SWIN_POS_TABLE) b = MASK ? bias2[ok ? rev7 + (7 - e) : negrow] : brow[7 - e];
+                    const float arg = fmaf(sv * qv_, cj_s, b) - lv;
+                    const float pr = __builtin_amdgcn_exp2f(!MASK || ok ? arg : -INFINITY);
+                    pp[e] = pr;
+                    const float dl = pr * (dpv - (e < 4 ? dA[e] : dB[e - 4]));
+                    // dS~ = dl log2(e) a_i (COSINE) or dl (DOT); the constant after the sum
+                    dsa[e] = SIM == SWIN_SIM_COSINE ? dl * qv_ : dl;
+                }
+                const bf16x8 pbf = pack_bf16x8(pp), dsb = pack_bf16x8(dsa);
+                V0 = mfma(vt_frag_at(rowB + 32 * c * D + vo0), pbf, V0);
+                V1 = mfma(vt_frag_at(rowB + 32 * c * D + vo1), pbf, V1);
+                H0 = mfma(vt_frag_at(rowA + 32 * c * D + vo0), dsb, H0);
+                H1 = mfma(vt_frag_at(rowA + 32 * c * D + vo1), dsb, H1);
             }
-            const bf16x8 pbf = pack_bf16x8(pp), dsb = pack_bf16x8(dsa);
-            V0 = mfma(vt_frag_at(rowB + 32 * c * D + vo0), pbf, V0);
-            V1 = mfma(vt_frag_at(rowB + 32 * c * D + vo1), pbf, V1);
-            H0 = mfma(vt_frag_at(rowA + 32 * c * D + vo0), dsb, H0);
-            H1 = mfma(vt_frag_at(rowA + 32 * c * D + vo1), dsb, H1);
-        }
+        };
+        if (needs_mask) pass_a(Flag<true>{});
+        else pass_a(Flag<false>{});
         const float hs = SIM == SWIN_SIM_COSINE ? 1.0f / kLog2e : RS32;
         float h8[8] = {H0[0] * hs, H0[1] * hs, H0[2] * hs, H0[3] * hs,
                        H1[0] * hs, H1[1] * hs, H1[2] * hs, H1[3] * hs};

@@ -201,6 +201,8 @@ LSE_CASES = [
     (22, 22, 11, 0, "interleaved", "cosine", "table"),
     (30, 45, 15, 7, "cyclic", "cosine", "table"),
     (24, 24, 12, 6, "cyclic", "dot", "none"),
+    (32, 48, 16, 8, "cyclic", "dot", "table"),         # whole-group exclusions, half-range chunk loops
+    (48, 32, 16, 4, "cyclic", "cosine", "table"),      # column split inside a group: every pair masked
 ]
 
 
@@ -225,6 +227,49 @@ def test_backward_small_given_lse(case):
         t = 0.5 * torch.randn(((2 * M - 1) ** 2, heads), generator=gen)
         table, table64 = t.to(DEV), f64(t)
     got, ref = _run(wl, x, g, synth.make_dout(wl), table, table64, lse_from="gpu")
+    for name in ("dq", "dk", "dv"):
+        _check(f"{case} {name}", f64(got[name]), ref[name], "bf16")
+    if sim == "cosine":
+        _check(f"{case} dtau", f64(got["dtau"]), ref["dtau"], "bf16")
+    if pos == "table":
+        _check(f"{case} dtable", f64(got["dtable"]), ref["dtable"], "bf16")
+
+
+LARGE_REGION_CASES = [
+    # H, W, M, shift, sim, pos: 2 x 1 or 1 x 2 windows, so one window has one
+    # split (rows or columns) and the other both
+    (64, 32, 32, 16, "dot", "rope2d"),      # column groups without a table; corner: row halves + groups
+    (32, 64, 32, 16, "dot", "rope2d"),      # row halves alone; corner
+    (24, 48, 24, 12, "cosine", "rope2d"),   # row halves with hi + lo scores; corner: per-pair masks
+    (24, 48, 24, 12, "cosine", "table"),    # row halves alone; corner: halves + per-pair masks
+    (48, 24, 24, 12, "cosine", "table"),    # column split inside a group: per-pair masks
+    (48, 48, 24, 8, "dot", "table"),        # 2 x 2: plain, column groups, row halves, both
+]
+
+
+@pytest.mark.parametrize("lse_from", [None, "gpu"])
+@pytest.mark.parametrize("case", LARGE_REGION_CASES,
+                         ids=[f"{c[0]}x{c[1]}-M{c[2]}-s{c[3]}-{c[4]}-{c[5]}" for c in LARGE_REGION_CASES])
+def test_backward_large_shift_regions(case, lse_from):
+    """The large-window backward on shifted windows of the last row and
+    column: exclusions by whole 8-slot groups, chunk loops restricted to the
+    query's (or key's) row region, and per-pair masks where the column split
+    falls inside a group; bf16 bars."""
+    H, W, M, s, sim, pos = case
+    heads = 2
+    wl = synth.small(B=1, H=H, W=W, C=32 * heads, heads=heads, M=M, shift=s, sim=sim, pos=pos, dtype="bf16",
+                     hidden=64)
+    desc = binding.make_desc(B=1, H=H, W=W, C=wl.C, heads=heads, M=M, shift=s, sim=sim, pos=pos,
+                             dtype=torch.bfloat16)
+    assert binding.swin_window_attn_bwd_kernel(desc) == "attn_bwd_large_kernel"
+    x = synth.make_inputs(wl, seed=90 + M + s)
+    g = gpu_inputs(x)
+    table = table64 = None
+    if pos == "table":
+        gen = torch.Generator().manual_seed(9 + M)
+        t = 0.5 * torch.randn(((2 * M - 1) ** 2, heads), generator=gen)
+        table, table64 = t.to(DEV), f64(t)
+    got, ref = _run(wl, x, g, synth.make_dout(wl), table, table64, lse_from=lse_from)
     for name in ("dq", "dk", "dv"):
         _check(f"{case} {name}", f64(got[name]), ref[name], "bf16")
     if sim == "cosine":

@@ -97,7 +97,6 @@ __device__ __forceinline__ float row_shr(float x)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
 }
 
-template <bool B> struct Flag { static constexpr bool value = B; };
 template <int V> struct Mode { static constexpr int value = V; };
 
 __device__ __forceinline__ bf16x4 load8b(Rsrc r, uint32_t off)
@@ -156,6 +155,30 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
     // products) from rowL and the query remainders
     const bool split = CR;
     const bool needs_mask = wp.last_r || wp.last_c || SR != M || NS != M * SR;
+    // With no padded slot (M a multiple of 8) the exclusions of a shifted
+    // window fall on whole 8-slot groups when the column split M - shift is
+    // a multiple of 8: a lane's group (8 keys of one key row against one
+    // query, or 8 queries of one query row against one key) is kept or
+    // dropped as a whole, and a dropped group reads the table's -inf row (or
+    // adds -inf without a table): mask mode 2, one select per group instead
+    // of one per pair (mode 1).  When the row split lands on a chunk
+    // boundary, the tiles of a last-row window see only the chunks of their
+    // own region (c_lo, c_hi below) and need no row masks.
+    const int rsplit = M - g.shift;
+    const bool unpadded = SR == M && NS == M * SR;
+    const bool half_rows = unpadded && wp.last_r && (rsplit * M) % 32 == 0;
+    const bool group_masks = unpadded && (!wp.last_c || (rsplit & 7) == 0);
+    const int mask_mode = !needs_mask ? 0 : (half_rows && !wp.last_c) ? 0 : group_masks ? 2 : 1;
+    // chunk range of a tile whose first slot is s0 (query tile in pass B,
+    // key tile in pass A)
+    auto chunk_range = [&](int s0, int& c_lo, int& c_hi) {
+        c_lo = 0;
+        c_hi = NS / 32;
+        if (half_rows) {
+            if (s0 < rsplit * M) c_hi = rsplit * M / 32;
+            else c_lo = rsplit * M / 32;
+        }
+    };
     const int negrow = S * S;
     // lane offsets of the chunk loops' LDS fragments (the swizzles do not
     // change from chunk to chunk: chunk c adds 32 c D elements)
@@ -386,10 +409,13 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
         // window, so every pair is kept and the loop carries no selects
         // TM: bias-gradient sums, 0 none, 1 one LDS atomic per element,
         // 2 diagonal sums (M a multiple of 8)
+        int cb_lo, cb_hi;
+        chunk_range(16 * t0, cb_lo, cb_hi);
         auto pass_b = [&](auto mflag, auto tflag) {
-            constexpr bool MASK = decltype(mflag)::value;
+            constexpr int MK = decltype(mflag)::value;
+            constexpr bool MASK = MK == 1;
             constexpr int TM = decltype(tflag)::value;
-            for (int c = 0; c < nch; ++c) {
+            for (int c = cb_lo; c < cb_hi; ++c) {
                 const bf16x8 va = fragA(rowB, c, 0), vb = fragA(rowB, c, 1);
                 const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
                 f32x4 sa, sb;
@@ -400,6 +426,8 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
                 const int gam = 4 * c + grp, rj = qdiv(gam, L.inv_GPR), cj0 = 8 * (gam - rj * L.GPR);
                 const int boff = qoff + rj * S + cj0;
                 const uint32_t bits = MASK ? (tv ? group_bits(rj, cj0) : 0u) : 0xffu;
+                const bool gok = MK != 2 || (rj >= rlo && rj < rhi && ((cmask >> cj0) & 1u));
+                const int bidx = MK == 2 && !gok ? negrow : boff;
                 float ds[8], dlv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -408,7 +436,8 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
                     const float kv = e < 4 ? k0[e] : k1[e - 4];
                     const bool ok = !MASK || ((bits >> e) & 1u) != 0u;
                     float b = 0.0f;
-                    if (POS == SWIN_POS_TABLE) b = MASK ? bias2[ok ? boff + e : negrow] : bias2[boff + e];
+                    if (POS == SWIN_POS_TABLE) b = MASK ? bias2[ok ? boff + e : negrow] : bias2[bidx + e];
+                    else if (MK == 2) b = gok ? 0.0f : -INFINITY;
                     // logit (log2 units) = s a_i c_j + b, a_i c_j = qs kv (DOT: kv = 1)
                     const float arg = fmaf(sv, SIM == SWIN_SIM_COSINE ? qs * kv : qs, b) - lq;
                     const float pr = __builtin_amdgcn_exp2f(!MASK || ok ? arg : -INFINITY);
@@ -467,8 +496,9 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
             }
         };
         auto pass_b_masks = [&](auto tflag) {
-            if (needs_mask) pass_b(Flag<true>{}, tflag);
-            else pass_b(Flag<false>{}, tflag);
+            if (mask_mode == 1) pass_b(Mode<1>{}, tflag);
+            else if (mask_mode == 2) pass_b(Mode<2>{}, tflag);
+            else pass_b(Mode<0>{}, tflag);
         };
         if (POS != SWIN_POS_TABLE || !a.dtable) pass_b_masks(Mode<0>{});
         else if (diag8) pass_b_masks(Mode<2>{});
@@ -534,9 +564,12 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
         const uint32_t cmask = ((chi >= 32 ? 0xffffffffu : ((1u << chi) - 1u)) & ~((1u << clo) - 1u)) &
                                (M >= 32 ? 0xffffffffu : ((1u << M) - 1u));
         f32x4 V0 = {0.0f, 0.0f, 0.0f, 0.0f}, V1 = V0, H0 = V0, H1 = V0;
+        int ca_lo, ca_hi;
+        chunk_range(16 * kt, ca_lo, ca_hi);
         auto pass_a = [&](auto mflag) {
-            constexpr bool MASK = decltype(mflag)::value;
-            for (int c = 0; c < nch; ++c) {
+            constexpr int MK = decltype(mflag)::value;
+            constexpr bool MASK = MK == 1;
+            for (int c = ca_lo; c < ca_hi; ++c) {
                 const bf16x8 qa = fragA(rowA, c, 0), qb = fragA(rowA, c, 1);
                 const bf16x8 ga = fragA(rowB, c, 0), gb = fragA(rowB, c, 1);
                 const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -555,7 +588,8 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
                 const int gam = 4 * c + grp, ri = qdiv(gam, L.inv_GPR), ci0 = 8 * (gam - ri * L.GPR);
                 // reversed table position of query (ri, ci0 + 7) against key (rj, cj)
                 const int rev7 = S * S - 8 - ((ri - rj + M - 1) * S + (ci0 - cj + M - 1));
-                const float* brow = bias2 + rev7;
+                const bool gok = MK != 2 || (ri >= rlo && ri < rhi && ((cmask >> ci0) & 1u));
+                const float* brow = bias2 + (MK == 2 && !gok ? negrow : rev7);
                 const bool rok = kv_ok && ri < M && ri >= rlo && ri < rhi;
                 const uint32_t cbits = MASK ? (rok ? (cmask >> ci0) & 0xffu : 0u) : 0xffu;
                 float pp[8], dsa[8];
@@ -568,6 +602,7 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
                     const bool ok = !MASK || ((cbits >> e) & 1u) != 0u;
                     float b = 0.0f;
                     if (POS == SWIN_POS_TABLE) b = MASK ? bias2[ok ? rev7 + (7 - e) : negrow] : brow[7 - e];
+                    else if (MK == 2) b = gok ? 0.0f : -INFINITY;
                     const float arg = fmaf(sv * qv_, cj_s, b) - lv;
                     const float pr = __builtin_amdgcn_exp2f(!MASK || ok ? arg : -INFINITY);
                     pp[e] = pr;
@@ -582,8 +617,9 @@ attn_bwd_large_kernel(AttnParams p, BwdLargeArgs a, LargeBwdLayout L)
                 H1 = mfma(vt_frag_at(rowA + 32 * c * D + vo1), dsb, H1);
             }
         };
-        if (needs_mask) pass_a(Flag<true>{});
-        else pass_a(Flag<false>{});
+        if (mask_mode == 1) pass_a(Mode<1>{});
+        else if (mask_mode == 2) pass_a(Mode<2>{});
+        else pass_a(Mode<0>{});
         const float hs = SIM == SWIN_SIM_COSINE ? 1.0f / kLog2e : RS32;
         float h8[8] = {H0[0] * hs, H0[1] * hs, H0[2] * hs, H0[3] * hs,
                        H1[0] * hs, H1[1] * hs, H1[2] * hs, H1[3] * hs};

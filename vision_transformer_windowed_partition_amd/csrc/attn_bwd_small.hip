@@ -105,6 +105,7 @@ __device__ __forceinline__ void slot_rc(int s, int& r, int& c)
 }
 
 template <bool B> struct Flag { static constexpr bool value = B; };
+template <int V> struct Mode { static constexpr int value = V; };
 
 // DIAG: M = 16 with a table (the bias gradient by diagonal sums)
 template <int SIM, int POS, int NCH, int QW, bool DIAG>
@@ -258,6 +259,18 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
 
     const bool padded = 8 * GPR != M || NCH * 32 != L.NSP;
     const bool needs_mask = wp.last_r || wp.last_c || padded;
+    // Exclusions of a shifted window fall on whole 8-slot groups when nothing
+    // is padded and the column split M - shift is a multiple of 8: a lane's
+    // group (8 keys of one key row against one query, or 8 queries of one
+    // query row against one key) is then kept or dropped as a whole, and a
+    // dropped group reads the table's -inf row (mask mode 2, one select per
+    // group instead of one per pair; mode 1 masks every pair).  With M = 16
+    // and shift 8 a tile is one row and a 32-slot chunk two rows, so in a
+    // window of the last row every tile sees only one half of the chunks
+    // (HALF: the loop runs over that half).
+    const bool group_masks = POS == SWIN_POS_TABLE && !padded && (!wp.last_c || ((M - g.shift) & 7) == 0);
+    const bool half_rows = NCH == 8 && M == 16 && !padded && wp.last_r && g.shift == 8;
+    const int mask_mode = !needs_mask ? 0 : !group_masks ? 1 : (half_rows && !wp.last_c) ? 0 : 2;
     const int negrow = S * S;
     const int kbase = (grp / GPR) * S + 8 * (grp % GPR);   // bias offset of this lane's key group, chunk 0
     // lane offsets of the chunk loops' LDS fragments (the swizzles do not
@@ -334,8 +347,10 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
     const Rsrc dvr = make_rsrc((const uint16_t*)a.dv + wp.base + h * D, bytes);
     // ---- pass B: dq of this wave's queries (query-major); MASK: the
     // window has shift regions or padded slots (else every pair counts)
-    auto pass_b = [&](auto mflag) {
-        constexpr bool MASK = decltype(mflag)::value;
+    auto pass_b = [&](auto mflag, auto hflag) {
+        constexpr int MK = decltype(mflag)::value;
+        constexpr bool MASK = MK == 1;
+        constexpr bool HALF = decltype(hflag)::value;
         for (int t0 = rank; t0 < L.NQT; t0 += QW) {
             const int t = t0 * 16 + li;
             const bool tv = !MASK || t < N;
@@ -352,8 +367,11 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             const uint32_t cmask = (((1u << chi) - 1u) & ~((1u << clo) - 1u));
             f32x4 G0 = {0.0f, 0.0f, 0.0f, 0.0f}, G1 = G0;
             float dts = 0.0f;                              // sum over keys of dS~ s (dtau without a_i)
+            // HALF: key rows [rlo, rhi) are chunks [rlo / 2, rhi / 2)
+            const int c_beg = HALF ? rlo >> 1 : 0;
 #pragma unroll 2
-            for (int c = 0; c < NCH; ++c) {
+            for (int cc = 0; cc < (HALF ? NCH / 2 : NCH); ++cc) {
+                const int c = c_beg + cc;
                 const bf16x8 ka = fragA(krow, c, 0), kb = fragA(krow, c, 1);
                 const bf16x8 va = fragA(vrow, c, 0), vb = fragA(vrow, c, 1);
                 const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -363,7 +381,7 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                 const f32x4 k1 = *(const f32x4*)(ksc + 32 * c + 8 * grp + 4);
                 const int gam = 4 * c + grp, rj = gam / GPR, cj0 = 8 * (gam % GPR);
                 const int boff = qoff + (4 / GPR) * c * S;
-                const float* brow = bias2 + boff;
+                const float* brow = bias2 + (MK == 2 && !(rj >= rlo && rj < rhi && ((cmask >> cj0) & 1u)) ? negrow : boff);
                 // allowed keys of this lane's 8-key group (bit e: key column cj0 + e)
                 const uint32_t bits = !MASK ? 0xffu : tv && rj >= rlo && rj < rhi && rj < M ? (cmask >> cj0) & 0xffu
                                                                                              : 0u;
@@ -412,8 +430,11 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                     const float pB = __uint_as_float(even ? sB[1] : sB[0]);
                     const float te = A + row_shl<8>(pA);
                     const float to = row_shr<8>(A) + row_shr<8>(pB);
-                    const float T = even ? te : (li <= 7 ? B : to);
-                    if (even || li != 0) fixed::add(&dtab[boff + (even ? 0 : 8)], T);
+                    const float T = __builtin_unpredictable(even) ? te : (__builtin_unpredictable(li <= 7) ? B : to);
+                    // T is zero for lane 0 of an odd group (every source of its
+                    // B lies outside the row); its add is kept so that no part
+                    // of the sum sits under a branch
+                    fixed::add(&dtab[boff + (even ? 0 : 8)], T);
                 }
                 const bf16x8 dsb = pack_bf16x8(ds);
                 G0 = mfma(vt_frag_at(krow + 32 * c * D + vo0), dsb, G0);
@@ -451,8 +472,12 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
         }
     };
     if (active) {
-        if (needs_mask) pass_b(Flag<true>{});
-        else pass_b(Flag<false>{});
+        if (mask_mode == 1) pass_b(Mode<1>{}, Flag<false>{});
+        else if (half_rows) {
+            if (mask_mode == 2) pass_b(Mode<2>{}, Flag<true>{});
+            else pass_b(Mode<0>{}, Flag<true>{});
+        } else if (mask_mode == 2) pass_b(Mode<2>{}, Flag<false>{});
+        else pass_b(Mode<0>{}, Flag<false>{});
     }
     if (PHASED) {
         // ---- Q and dout rows replace K and V
@@ -462,8 +487,10 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
         __syncthreads();
     }
     // ---- pass A: dk, dv of this wave's 16-key tiles (key-major)
-    auto pass_a = [&](auto mflag) {
-        constexpr bool MASK = decltype(mflag)::value;
+    auto pass_a = [&](auto mflag, auto hflag) {
+        constexpr int MK = decltype(mflag)::value;
+        constexpr bool MASK = MK == 1;
+        constexpr bool HALF = decltype(hflag)::value;
         const int nkt = (L.NSP + 15) / 16;
         for (int kt = rank; kt < nkt; kt += QW) {
             const int sk = 16 * kt + li;                   // this lane's key slot
@@ -479,8 +506,11 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             const uint32_t cmask = ((chi >= 32 ? 0xffffffffu : ((1u << chi) - 1u)) & ~((1u << clo) - 1u)) &
                                    ((1u << M) - 1u);
             f32x4 V0 = {0.0f, 0.0f, 0.0f, 0.0f}, V1 = V0, H0 = V0, H1 = V0;
+            // HALF: query rows [rlo, rhi) are chunks [rlo / 2, rhi / 2)
+            const int c_beg = HALF ? rlo >> 1 : 0;
 #pragma unroll 2
-            for (int c = 0; c < NCH; ++c) {
+            for (int cc = 0; cc < (HALF ? NCH / 2 : NCH); ++cc) {
+                const int c = c_beg + cc;
                 const bf16x8 qa = fragA(qrow, c, 0), qb = fragA(qrow, c, 1);
                 const bf16x8 ga = fragA(orow, c, 0), gb = fragA(orow, c, 1);
                 // this lane's query slots: 32 c + 8 grp + e, a row segment
@@ -496,7 +526,8 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                 // (ri - rj + M-1) S + (ci0 + e - cj + M-1), reversed position
                 // S*S - 1 - that, decreasing in e
                 const int rev7 = S * S - 8 - ((ri - rj + M - 1) * S + (ci0 - cj + M - 1));   // rev. pos. of e = 7
-                const float* brow = bias2 + rev7;
+                const float* brow =
+                    bias2 + (MK == 2 && !(ri >= rlo && ri < rhi && ((cmask >> ci0) & 1u)) ? negrow : rev7);
                 const bool rok = kv_ok && ri < M && ri >= rlo && ri < rhi;
                 const uint32_t cbits = rok ? (cmask >> ci0) & 0xffu : 0u;
                 float pp[8], dsa[8];
@@ -555,8 +586,12 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
         }
     };
     if (active) {
-        if (needs_mask) pass_a(Flag<true>{});
-        else pass_a(Flag<false>{});
+        if (mask_mode == 1) pass_a(Mode<1>{}, Flag<false>{});
+        else if (half_rows) {
+            if (mask_mode == 2) pass_a(Mode<2>{}, Flag<true>{});
+            else pass_a(Mode<0>{}, Flag<true>{});
+        } else if (mask_mode == 2) pass_a(Mode<2>{}, Flag<false>{});
+        else pass_a(Mode<0>{}, Flag<false>{});
         if (SIM == SWIN_SIM_COSINE && a.dtau) {
             const float s = wave_reduce<Op::Sum>(dtau_acc);
             if (lane == 0) red[wave] = s;

@@ -59,7 +59,11 @@ struct SmallLayout {
 };
 
 // NCH chunks of 32 key slots per window; QW wavefronts per window.
-template <int SIM, int POS, int NCH, int QW>
+// RT: query tiles that are whole window rows, so that a tile's row offsets
+// are the same for every lane (scalar) and its columns the lane's own:
+// 1 for M = 16 (tile tq is row tq, query column li), 2 for M = 8 (rows
+// 2 tq and 2 tq + 1, column li % 8); 0 for other M.
+template <int SIM, int POS, int NCH, int QW, int RT>
 __global__ void __launch_bounds__(256)
 attn_small_kernel(AttnParams p, SmallLayout L)
 {
@@ -114,18 +118,38 @@ attn_small_kernel(AttnParams p, SmallLayout L)
     const Rsrc orr = make_rsrc((const uint16_t*)p.out + wp.base + h * D, bytes);
     const RawRsrc vraw = raw_rsrc((const uint16_t*)p.v + wp.base + h * D, active ? bytes : 0u);
 
+    // RT: the lane's query column offset (its column within every tile), and
+    // the byte offset of query tile tq's row for this lane
+    const uint32_t qcol = RT == 1 ? wg.col(li) : RT == 2 ? wg.col(li & 7) : 0u;
+    auto qrow_of = [&](int tq) -> uint32_t {
+        if (RT == 1) return wg.row(tq);
+        const uint32_t r0 = wg.row(2 * tq), r1 = wg.row(2 * tq + 1);
+        return (li & 8) ? r1 : r0;
+    };
+
     // ---- issue every load of the staging at once.  Key slot 8 gam + x is
     // token (gam / GPR, 8 (gam % GPR) + x).
     //   K tile f = 2c + t (this wave: f = rank + QW k): tile A of chunk c
     //   holds slots 32c + 8(r/4) + r%4, tile B the next 4 of each group of
     //   8, so that S^T hands a lane slots 32c + 8 grp + 0..7.
     u32x4 kraw[SETS];
+    // RT 1: a K tile f = rank + QW k holds rows 2c, 2c + 1 (lanes li / 8) at
+    // the lane's columns 8 ((li / 4) % 2) + li % 4 + 4 (f % 2), the same for
+    // every k; a V piece j is row j at columns 8 (l / 32) + (l / 4) % 8
+    const uint32_t kcol = RT == 1 ? wg.col(8 * ((li >> 2) & 1) + (li & 3) + 4 * (rank & 1)) + 16u * grp : 0u;
+    const uint32_t vcol = RT == 1 ? wg.col(8 * (lane >> 5) + ((lane >> 2) & 7)) +
+                                        16u * ((lane & 3) ^ v_swizzle(lane >> 2)) : 0u;
 #pragma unroll
     for (int k = 0; k < SETS; ++k) {
         const int f = rank + QW * k, c = f >> 1, t = f & 1;
         const int gam = 4 * c + (li >> 2);
         const int rj = gam / GPR, cj = 8 * (gam % GPR) + (li & 3) + 4 * t;
-        kraw[k] = load16(kr, masked(wg.tok(rj, cj) + 16u * grp, active && rj < M && cj < M));
+        if (RT == 1) {
+            // rows 2c and 2c + 1 (lanes li / 8), columns of the lane's group
+            const uint32_t r0 = wg.row(2 * c), r1 = wg.row(2 * c + 1);
+            kraw[k] = load16(kr, masked(((li & 8) ? r1 : r0) + kcol, active));
+        } else
+            kraw[k] = load16(kr, masked(wg.tok(rj, cj) + 16u * grp, active && rj < M && cj < M));
     }
     //   V piece j (1 KB of LDS, this wave: j = rank + QW k): lane l fills
     //   16 bytes at position 16 l, i.e. slot 16 j + l/4, LDS piece l%4,
@@ -137,7 +161,10 @@ attn_small_kernel(AttnParams p, SmallLayout L)
         const int gam = s >> 3;
         const int rj = gam / GPR, cj = 8 * (gam % GPR) + (s & 7);
         const int piece = (lane & 3) ^ v_swizzle(s);
-        dma16(vraw, vst + (size_t)j * 512, masked(wg.tok(rj, cj) + 16u * piece, rj < M && cj < M));
+        if (RT == 1)
+            dma16(vraw, vst + (size_t)j * 512, wg.row(j) + vcol);
+        else
+            dma16(vraw, vst + (size_t)j * 512, masked(wg.tok(rj, cj) + 16u * piece, rj < M && cj < M));
     }
     //   the first two query tiles of this wave: tiles rank + QW k
     u32x4 qpre[2];
@@ -146,9 +173,13 @@ attn_small_kernel(AttnParams p, SmallLayout L)
         const int tq = rank + QW * i;
         const int t = tq * 16 + li;
         const bool ok = active && tq < L.NQT && t < N;
-        const int tt = ok ? t : 0;
-        const int ri = qdiv(tt, L.inv_M), ci = tt - ri * M;
-        qpre[i] = load16(qr, masked(wg.tok(ri, ci) + 16u * grp, ok));
+        if (RT) {
+            qpre[i] = load16(qr, masked(qrow_of(tq) + qcol + 16u * grp, active && tq < L.NQT));
+        } else {
+            const int tt = ok ? t : 0;
+            const int ri = qdiv(tt, L.inv_M), ci = tt - ri * M;
+            qpre[i] = load16(qr, masked(wg.tok(ri, ci) + 16u * grp, ok));
+        }
     }
     //   this wave's quarter of the bias table of head h: rows (wave + 4k) 64
     //   + lane, the last row standing in for those past the end (extrema
@@ -260,14 +291,20 @@ attn_small_kernel(AttnParams p, SmallLayout L)
             const int tq = rank + QW * (k0 + 2 + i);
             const int t = tq * 16 + li;
             const bool ok = tq < L.NQT && t < N;
-            const int tt = ok ? t : 0;
-            const int ri = qdiv(tt, L.inv_M), ci = tt - ri * M;
-            qnext[i] = load16(qr, masked(wg.tok(ri, ci) + 16u * grp, ok));
+            if (RT) {
+                qnext[i] = load16(qr, masked(qrow_of(tq) + qcol + 16u * grp, tq < L.NQT));
+            } else {
+                const int tt = ok ? t : 0;
+                const int ri = qdiv(tt, L.inv_M), ci = tt - ri * M;
+                qnext[i] = load16(qr, masked(wg.tok(ri, ci) + 16u * grp, ok));
+            }
         }
         bool any_exact = false, partial = false;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int ri = qdiv(qt[i], L.inv_M), ci = qt[i] - ri * M;
+            const int tq = qv[i] ? rank + QW * (k0 + i) : 0;
+            const int ri = RT == 1 ? tq : RT == 2 ? 2 * tq + (li >> 3) : qdiv(qt[i], L.inv_M);
+            const int ci = RT == 1 ? li : RT == 2 ? (li & 7) : qt[i] - ri * M;
             const u32x4 qw = qraw[i];
             T[i].qf = __builtin_bit_cast(bf16x8, qw);
             const float ss = sum_x32(sum_x16(sumsq8(qraw[i])));
@@ -358,9 +395,15 @@ attn_small_kernel(AttnParams p, SmallLayout L)
         // 16 + 4 grp..+3 of query li
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int ri = qdiv(qt[i], L.inv_M), ci = qt[i] - ri * M;
+            const int tq = rank + QW * (k0 + i);
+            uint32_t off;
+            if (RT) {
+                off = masked(qrow_of(tq) + qcol + 8u * grp, tq < L.NQT);
+            } else {
+                const int ri = qdiv(qt[i], L.inv_M), ci = qt[i] - ri * M;
+                off = masked(wg.tok(ri, ci) + 8u * grp, qv[i]);
+            }
             const float inv = __builtin_amdgcn_rcpf(T[i].ls[0]);
-            const uint32_t off = masked(wg.tok(ri, ci) + 8u * grp, qv[i]);
             store8(orr, off, pack_bf16x4(T[i].o0[0] * inv, T[i].o0[1] * inv, T[i].o0[2] * inv, T[i].o0[3] * inv));
             store8(orr, off + 32u, pack_bf16x4(T[i].o1[0] * inv, T[i].o1[1] * inv, T[i].o1[2] * inv, T[i].o1[3] * inv));
             if (p.lse && grp == 0 && qv[i]) {
@@ -381,9 +424,11 @@ attn_small_kernel(AttnParams p, SmallLayout L)
 template <int SIM, int POS>
 hipError_t launch_nch(const AttnParams& p, const SmallLayout& L, int nch, int grid, size_t lds, hipStream_t s)
 {
-    auto* fn = nch <= 2 ? attn_small_kernel<SIM, POS, 2, 1>
-             : nch <= 6 ? attn_small_kernel<SIM, POS, 6, 4>
-                        : attn_small_kernel<SIM, POS, 8, 4>;
+    const int M = p.g.M;
+    auto* fn = nch <= 2 ? (M == 8 ? attn_small_kernel<SIM, POS, 2, 1, 2> : attn_small_kernel<SIM, POS, 2, 1, 0>)
+             : nch <= 6 ? attn_small_kernel<SIM, POS, 6, 4, 0>
+             : M == 16  ? attn_small_kernel<SIM, POS, 8, 4, 1>
+                        : attn_small_kernel<SIM, POS, 8, 4, 0>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;

@@ -107,8 +107,10 @@ __device__ __forceinline__ void slot_rc(int s, int& r, int& c)
 template <bool B> struct Flag { static constexpr bool value = B; };
 template <int V> struct Mode { static constexpr int value = V; };
 
-// DIAG: M = 16 with a table (the bias gradient by diagonal sums)
-template <int SIM, int POS, int NCH, int QW, bool DIAG>
+// DIAG: M = 16 with a table (the bias gradient by diagonal sums).
+// RT: M = 16, so a 16-slot piece, a query tile and a key tile are each one
+// window row (row offsets scalar, the lane's column its own).
+template <int SIM, int POS, int NCH, int QW, bool DIAG, bool RT>
 __global__ void __launch_bounds__(256)
 attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
 {
@@ -160,6 +162,10 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
     // ---- staging: the four tensors' rows by LDS-DMA; piece j of a tensor
     // is slots 16 j .. 16 j + 15, lane l filling LDS piece l%4 of slot
     // 16 j + l/4 with channel piece (l%4) ^ v_swizzle(slot)
+    // RT: the lane's column offsets, as a query or key (li) and as a staging
+    // lane (l / 4, with its swizzled piece)
+    const uint32_t lcol = RT ? wg.col(li) : 0u;
+    const uint32_t scol = RT ? wg.col(lane >> 2) + 16u * ((lane & 3) ^ v_swizzle(lane >> 2)) : 0u;
     auto stage_rows = [&](const void* t0, const void* t1, __bf16* dst) {
         const void* src[2] = {t0, t1};
 #pragma unroll
@@ -172,8 +178,11 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
                 int r, c;
                 slot_rc<GPR>(s, r, c);
                 const int piece = (lane & 3) ^ v_swizzle(s);
-                dma16(rr, dst + (size_t)tsr * NS * D + (size_t)j * 512,
-                      masked(wg.tok(r, c) + 16u * piece, r < M && c < M));
+                if (RT)
+                    dma16(rr, dst + (size_t)tsr * NS * D + (size_t)j * 512, wg.row(j) + scol);
+                else
+                    dma16(rr, dst + (size_t)tsr * NS * D + (size_t)j * 512,
+                          masked(wg.tok(r, c) + 16u * piece, r < M && c < M));
             }
         }
     };
@@ -201,6 +210,10 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             for (int e = 0; e < 4; ++e) f[4 * hh + e] = (float)src[e];
         }
     };
+    // RT: the same from the token offset of the lane's row and column
+    auto tfrag = [&](const Rsrc& r, uint32_t tok, int piece) -> bf16x8 {
+        return __builtin_bit_cast(bf16x8, load16(r, tok + 16u * piece));
+    };
     auto gquad = [&](const Rsrc& r, int s, float* f) {
         const bf16x8 lo = gfrag(r, s, grp >> 1), hi = gfrag(r, s, 2 + (grp >> 1));
         const int o = 4 * (grp & 1);
@@ -219,7 +232,8 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             const int s = s0 + (lane >> 2);
             int r, c;
             slot_rc<GPR>(s, r, c);
-            const uint32_t off = masked(wg.tok(r, c) + 16u * piece, r < M && c < M);
+            const uint32_t off = RT ? wg.row(s0 >> 4) + wg.col(lane >> 2) + 16u * piece
+                                    : masked(wg.tok(r, c) + 16u * piece, r < M && c < M);
             float kf[8], qf[8], gf[8], of[8];
             unpack_bf16x8(load16(kr, off), kf);
             unpack_bf16x8(load16(qr, off), qf);
@@ -355,10 +369,11 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             const int t = t0 * 16 + li;
             const bool tv = !MASK || t < N;
             const int tt = tv ? t : 0;
-            const int ri = qdiv(tt, L.inv_M), ci = tt - ri * M;
+            const int ri = RT ? t0 : qdiv(tt, L.inv_M), ci = RT ? li : tt - ri * M;
             const int qs_slot = ri * 8 * GPR + ci;
-            const bf16x8 qf = PHASED ? gfrag(qg, qs_slot, grp) : rowfrag(qrow, qs_slot, grp);
-            const bf16x8 gf = PHASED ? gfrag(dg, qs_slot, grp) : rowfrag(orow, qs_slot, grp);
+            const uint32_t qtok = RT ? wg.row(t0) + lcol : 0u;
+            const bf16x8 qf = RT ? tfrag(qg, qtok, grp) : PHASED ? gfrag(qg, qs_slot, grp) : rowfrag(qrow, qs_slot, grp);
+            const bf16x8 gf = RT ? tfrag(dg, qtok, grp) : PHASED ? gfrag(dg, qs_slot, grp) : rowfrag(orow, qs_slot, grp);
             const float qs = qsc[qs_slot], lq = lse[qs_slot], Dq = dd[qs_slot];
             const int qoff = (M - 1 - ri) * S + (M - 1 - ci) + kbase;
             int rlo = 0, rhi = M, clo = 0, chi = M;
@@ -445,7 +460,12 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             // lane holds channels 4 grp..+3 and 16 + 4 grp..+3 of query li
             float q8[8], g8[8];
             {
-                if (PHASED) gquad(qg, qs_slot, q8);        // the query's raw channels
+                if (RT) {                                  // the query's raw channels
+                    const bf16x8 lo = tfrag(qg, qtok, grp >> 1), hi = tfrag(qg, qtok, 2 + (grp >> 1));
+                    const int o = 4 * (grp & 1);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { q8[e] = (float)lo[o + e]; q8[4 + e] = (float)hi[o + e]; }
+                } else if (PHASED) gquad(qg, qs_slot, q8);
                 else lquad(qrow, qs_slot, q8);
                 g8[0] = G0[0]; g8[1] = G0[1]; g8[2] = G0[2]; g8[3] = G0[3];
                 g8[4] = G1[0]; g8[5] = G1[1]; g8[6] = G1[2]; g8[7] = G1[3];
@@ -466,7 +486,7 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) dqv[e] = g8[e] * 0.17677669529663687f;
             }
-            const uint32_t off = masked(wg.tok(ri, ci) + 8u * grp, tv);
+            const uint32_t off = RT ? qtok + 8u * grp : masked(wg.tok(ri, ci) + 8u * grp, tv);
             store8(dqr, off, pack_bf16x4(dqv[0], dqv[1], dqv[2], dqv[3]));
             store8(dqr, off + 32u, pack_bf16x4(dqv[4], dqv[5], dqv[6], dqv[7]));
         }
@@ -496,9 +516,11 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             const int sk = 16 * kt + li;                   // this lane's key slot
             int rj, cj;
             slot_rc<GPR>(sk, rj, cj);
+            if (RT) { rj = kt; cj = li; }
             const bool kv_ok = rj < M && cj < M;
-            const bf16x8 kB = PHASED ? gfrag(kg, sk, grp) : rowfrag(krow, sk, grp);
-            const bf16x8 vB = PHASED ? gfrag(vg, sk, grp) : rowfrag(vrow, sk, grp);
+            const uint32_t ktok = RT ? wg.row(kt) + lcol : 0u;
+            const bf16x8 kB = RT ? tfrag(kg, ktok, grp) : PHASED ? gfrag(kg, sk, grp) : rowfrag(krow, sk, grp);
+            const bf16x8 vB = RT ? tfrag(vg, ktok, grp) : PHASED ? gfrag(vg, sk, grp) : rowfrag(vrow, sk, grp);
             const float cj_s = ksc[sk];
             int rlo = 0, rhi = M, clo = 0, chi = M;
             if (wp.last_r) { if (rj < M - g.shift) rhi = M - g.shift; else rlo = M - g.shift; }
@@ -557,7 +579,12 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
             // lane holds channels 4 grp..+3 and 16 + 4 grp..+3 of key slot sk
             float k8[8], h8[8], dkv[8];
             {
-                if (PHASED) gquad(kg, sk, k8);             // the key's raw channels
+                if (RT) {                                  // the key's raw channels
+                    const bf16x8 lo = tfrag(kg, ktok, grp >> 1), hi = tfrag(kg, ktok, 2 + (grp >> 1));
+                    const int o = 4 * (grp & 1);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { k8[e] = (float)lo[o + e]; k8[4 + e] = (float)hi[o + e]; }
+                } else if (PHASED) gquad(kg, sk, k8);
                 else lquad(krow, sk, k8);
                 // the constant of dS~: 1/log2(e) (COSINE) or 1/sqrt(d) (DOT)
                 const float hs = SIM == SWIN_SIM_COSINE ? 1.0f / kLog2e : 0.17677669529663687f;
@@ -578,7 +605,7 @@ attn_bwd_small_kernel(AttnParams p, BwdSmallArgs a, BwdLayout L)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) dkv[e] = h8[e];
             }
-            const uint32_t off = masked(wg.tok(rj, cj) + 8u * grp, kv_ok);
+            const uint32_t off = RT ? ktok + 8u * grp : masked(wg.tok(rj, cj) + 8u * grp, kv_ok);
             store8(dkr, off, pack_bf16x4(dkv[0], dkv[1], dkv[2], dkv[3]));
             store8(dkr, off + 32u, pack_bf16x4(dkv[4], dkv[5], dkv[6], dkv[7]));
             store8(dvr, off, pack_bf16x4(V0[0], V0[1], V0[2], V0[3]));
@@ -616,10 +643,11 @@ template <int SIM, int POS>
 hipError_t launch_nch(const AttnParams& p, const BwdSmallArgs& a, const BwdLayout& L, int nch, int grid,
                       size_t lds, hipStream_t s)
 {
-    auto* fn = nch <= 2 ? attn_bwd_small_kernel<SIM, POS, 2, 1, false>
-             : nch <= 6 ? attn_bwd_small_kernel<SIM, POS, 6, 4, false>
-             : p.g.M == 16 && POS == SWIN_POS_TABLE ? attn_bwd_small_kernel<SIM, POS, 8, 4, true>
-                        : attn_bwd_small_kernel<SIM, POS, 8, 4, false>;
+    auto* fn = nch <= 2 ? attn_bwd_small_kernel<SIM, POS, 2, 1, false, false>
+             : nch <= 6 ? attn_bwd_small_kernel<SIM, POS, 6, 4, false, false>
+             : p.g.M == 16 ? (POS == SWIN_POS_TABLE ? attn_bwd_small_kernel<SIM, POS, 8, 4, true, true>
+                                                    : attn_bwd_small_kernel<SIM, POS, 8, 4, false, true>)
+                        : attn_bwd_small_kernel<SIM, POS, 8, 4, false, false>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;

@@ -129,7 +129,8 @@ __device__ __forceinline__ bool folded(bool precise)
 // One pair of query tiles against chunks [cb, ce) of a staged block.
 //   MASK: shift regions / padded slots; GENERAL: running maximum for tiles
 //   that need it, 1/||k_j|| scaling (precise), hi + lo products (split).
-template <int SIM, int POS, bool MASK, bool GENERAL>
+//   NU: tiles of the pair in use (1 for a wavefront's odd last tile).
+template <int SIM, int POS, bool MASK, bool GENERAL, int NU>
 __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[NT], const float* bias2, const float* kinv,
                                          int S, int SR, float inv_SR, int cb, int ce, int lane,
                                          bool partial, bool precise, bool split)
@@ -151,17 +152,17 @@ __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[NT], const f
         bool gok[NT];
         uint32_t bits[NT];
 #pragma unroll
-        for (int i = 0; i < NT; ++i) { gok[i] = true; bits[i] = 0xffu; }
+        for (int i = 0; i < NU; ++i) { gok[i] = true; bits[i] = 0xffu; }
         if (MASK) {
 #pragma unroll
-            for (int i = 0; i < NT; ++i) {
+            for (int i = 0; i < NU; ++i) {
                 bits[i] = gw.rj >= T[i].rlo && gw.rj < T[i].rhi ? (T[i].cmask >> gw.c0) & 0xffu : 0u;
                 gok[i] = bits[i] != 0u;
             }
         }
         float add[NT][8];
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
+        for (int i = 0; i < NU; ++i) {
             if (POS == SWIN_POS_TABLE) {
                 const float* bp = bias2 + ((MASK && !gok[i]) ? negrow : gw.rj * S + gw.c0 + T[i].qoff);
 #pragma unroll
@@ -178,7 +179,7 @@ __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[NT], const f
         const bf16x8 v1 = vt_frag(bk.v, c, 1, grp, li);
         f32x4 sa[NT], sb[NT];
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
+        for (int i = 0; i < NU; ++i) {
             const f32x4 ia = {add[i][0], add[i][1], add[i][2], add[i][3]};
             const f32x4 ib = {add[i][4], add[i][5], add[i][6], add[i][7]};
             sa[i] = mfma(ka, T[i].qf, fold ? ia : zero4);
@@ -190,7 +191,7 @@ __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[NT], const f
                 const bf16x8 ka_lo = bk.klo[(c * 2 + 0) * 64 + lane];
                 const bf16x8 kb_lo = bk.klo[(c * 2 + 1) * 64 + lane];
 #pragma unroll
-                for (int i = 0; i < NT; ++i) {
+                for (int i = 0; i < NU; ++i) {
                     sa[i] = mfma(ka_lo, T[i].qf, sa[i]);
                     sb[i] = mfma(kb_lo, T[i].qf, sb[i]);
                     sa[i] = mfma(ka, T[i].qf_lo, sa[i]);
@@ -208,7 +209,7 @@ __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[NT], const f
         }
         bf16x8 pb[NT];
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
+        for (int i = 0; i < NU; ++i) {
             float x[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) { x[e] = sa[i][e]; x[e + 4] = sb[i][e]; }
@@ -243,7 +244,7 @@ __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[NT], const f
             pb[i] = pack_bf16x8(pr);
         }
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
+        for (int i = 0; i < NU; ++i) {
             T[i].o0 = mfma(v0, pb[i], T[i].o0);
             T[i].o1 = mfma(v1, pb[i], T[i].o1);
             T[i].ls = mfma(ones, pb[i], T[i].ls);
@@ -589,6 +590,8 @@ attn_large_kernel(AttnParams p, LargeLayout L)
         rlo_min = __builtin_amdgcn_readfirstlane(rlo_min);
         rhi_max = __builtin_amdgcn_readfirstlane(rhi_max);
         const bool live = rhi_max > rlo_min;              // some tile of the pair has queries
+        // whether the pair's second tile holds queries (wave-uniform)
+        const bool two = NT == 2 && (wave + WAVES * (NT * r + 1)) * 16 < N;
 
         for (int b = 0; b < nblocks; ++b) {
             Block bk = whole;
@@ -612,14 +615,22 @@ attn_large_kernel(AttnParams p, LargeLayout L)
             const int ce = min(bk.nch, (max(0, s_hi) + 31) >> 5);
             if (cb >= ce) continue;
             if (any_exact || precise || split)
-                run_pair<SIM, POS, true, true>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, partial, precise,
-                                               split);
-            else if (needs_mask)
-                run_pair<SIM, POS, true, false>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, partial, false,
-                                                false);
+                run_pair<SIM, POS, true, true, NT>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, partial,
+                                                   precise, split);
+            else if (!two) {
+                // the wavefront's last tile is alone: run it by itself
+                if (needs_mask)
+                    run_pair<SIM, POS, true, false, 1>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, partial,
+                                                       false, false);
+                else
+                    run_pair<SIM, POS, false, false, 1>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, false,
+                                                        false, false);
+            } else if (needs_mask)
+                run_pair<SIM, POS, true, false, NT>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, partial, false,
+                                                    false);
             else
-                run_pair<SIM, POS, false, false>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, false, false,
-                                                 false);
+                run_pair<SIM, POS, false, false, NT>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, false, false,
+                                                     false);
         }
 
         // ---- normalise and store: lane holds channels 4 grp..+3 and

@@ -413,7 +413,7 @@ attn_large_kernel(AttnParams p, LargeLayout L)
     // first pair of query tiles; the tables are set up meanwhile
     if (!split) stage_issue(whole, (__bf16*)(kv + L.NSP * 64));
     u32x4 qraw[SIM == SWIN_SIM_DOT && POS == SWIN_POS_ROPE2D ? QPW : 1];
-    if (SIM == SWIN_SIM_DOT && POS == SWIN_POS_ROPE2D && !split) {
+    if (SIM == SWIN_SIM_DOT && POS == SWIN_POS_ROPE2D) {             // (split is only set below for DOT)
 #pragma unroll
         for (int j = 0; j < QPW; ++j) {
             const int t = (wave + WAVES * j) * 16 + li;
@@ -423,8 +423,13 @@ attn_large_kernel(AttnParams p, LargeLayout L)
             qraw[j] = load16(qr, masked(wp.wg.tok(ri, ci) + 16u * grp, ok));
         }
     }
+    // DOT with rotation keeps those query rows for the tiles (a second read
+    // of Q would come partly from HBM again: the window's K, V and Q pass
+    // the L2 between the norm test and the last pair); others load a pair
+    // ahead
+    constexpr bool QKEEP = SIM == SWIN_SIM_DOT && POS == SWIN_POS_ROPE2D;
     u32x4 qnext[NT];
-    load_pair_q(0, qnext);
+    if (!QKEEP) load_pair_q(0, qnext);
     // ---- tables: bias (reversed so that consecutive keys read consecutive
     // floats, in log2 units, shifted by its max and, for COSINE, by 1/tau);
     // rotary cos / sin per local position, half and pair
@@ -519,9 +524,17 @@ attn_large_kernel(AttnParams p, LargeLayout L)
     const bool partial = (wp.last_c && ((M - g.shift) & 7)) || (M & 7);
     for (int r = 0; r < L.rounds; ++r) {
         u32x4 qcur[NT];
+        if (QKEEP) {
+            // this round's rows are qraw[0..NT); the rest move down a pair
 #pragma unroll
-        for (int i = 0; i < NT; ++i) qcur[i] = qnext[i];
-        if (r + 1 < L.rounds) load_pair_q(r + 1, qnext);
+            for (int i = 0; i < NT; ++i) qcur[i] = qraw[i];
+#pragma unroll
+            for (int j = 0; j + NT < QPW; ++j) qraw[j] = qraw[j + NT];
+        } else {
+#pragma unroll
+            for (int i = 0; i < NT; ++i) qcur[i] = qnext[i];
+            if (r + 1 < L.rounds) load_pair_q(r + 1, qnext);
+        }
         Tile T[NT];
         int qt[NT];
         bool qv[NT];

@@ -7,7 +7,10 @@ attention over the grid, partition, shift mask and reverse map included
 (swin_window_attn_fwd).  Inputs are resident in HBM before timing starts.
 
 Timing: W untimed warm-up steps, then exactly K timed steps between two
-torch.cuda.synchronize() calls.  Cold cache by default: the steps rotate
+torch.cuda.synchronize() calls.  The defaults (200 warm-up, 500 timed)
+measure the steady state: the GPU's clocks settle over the first hundred or
+so launches of the path, and the first 50 steps after 10 run about 10%
+slower than the same steps later.  Cold cache by default: the steps rotate
 through enough distinct input/output sets (> 512 MB in all) that the 256 MB
 Infinity Cache cannot hold one set between its uses; --warm reuses one set.
 The attention kernel's own duration is taken from HIP events recorded on the
@@ -162,8 +165,8 @@ def cpu_baseline(wl, x, budget_s: float):
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", type=int, default=1, help="index into synth.WORKLOADS (1 = headline)")
     ap.add_argument("--warm", action="store_true", help="reuse one input set (cache-warm)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -69,10 +69,6 @@ struct BwdLargeArgs {
     float* dtable;
 };
 
-__device__ __forceinline__ bf16x8 rowfrag(const __bf16* rows, int s, int piece)
-{
-    return *(const bf16x8*)(rows + s * D + ((piece ^ v_swizzle(s)) * 8));
-}
 __device__ __forceinline__ void rowstore(__bf16* rows, int s, int piece, const bf16x8& v)
 {
     *(bf16x8*)(rows + s * D + ((piece ^ v_swizzle(s)) * 8)) = v;

@@ -81,9 +81,10 @@ struct VTile {
 // groups, group 4c + grp of the lane being row gam / GPR, columns
 // 8 (gam % GPR) .. +7.
 //
-// One 32-key chunk c of the staged key frame for two tiles; exact
-// (wave-uniform): the running maximum, else the tiles' fixed references.
-template <int SIM, int POS, int SR>
+// One 32-key chunk c of the staged key frame for NU tiles (two, or one when
+// the pair's second tile lies past the frame); exact (wave-uniform): the
+// running maximum, else the tiles' fixed references.
+template <int SIM, int POS, int SR, int NU>
 __device__ __forceinline__ void chunk(const bf16x8* kst, const __bf16* vst, const float* bias2, const float* kinv,
                                       VTile* T, int c, int lane, int S, bool mask, bool fold, bool prec,
                                       bool exact)
@@ -95,11 +96,11 @@ __device__ __forceinline__ void chunk(const bf16x8* kst, const __bf16* vst, cons
     const int rj = gam / GPR, cj0 = 8 * (gam - rj * GPR);   // this lane's key group
     uint32_t bits[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NU; ++i) {
         const uint32_t cb = ALIGNED ? T[i].cbits : (T[i].cbits >> cj0) & 0xffu;
         bits[i] = !mask ? 0xffu : (rj >= T[i].rlo && rj < T[i].rhi ? cb : 0u);
     }
-    if (mask && !__any((bits[0] | bits[1]) != 0u)) return;          // chunk masked for the whole wave
+    if (mask && !__any((bits[0] | (NU > 1 ? bits[1] : 0u)) != 0u)) return;   // chunk masked for the whole wave
     const bf16x8 ka = kst[(c * 2 + 0) * 64 + lane];
     const bf16x8 kb = kst[(c * 2 + 1) * 64 + lane];
     float kin[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
@@ -114,7 +115,7 @@ __device__ __forceinline__ void chunk(const bf16x8* kst, const __bf16* vst, cons
     for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
     bf16x8 pb[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NU; ++i) {
         float add[8];
         if (POS == SWIN_POS_TABLE) {
             const int boff = T[i].qoff + (ALIGNED ? (4 / GPR) * c * S : rj * S + cj0);
@@ -154,7 +155,7 @@ __device__ __forceinline__ void chunk(const bf16x8* kst, const __bf16* vst, cons
     const bf16x8 v0 = vt_frag(vst, c, 0, grp, li);
     const bf16x8 v1 = vt_frag(vst, c, 1, grp, li);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NU; ++i) {
         T[i].o0 = mfma(v0, pb[i], T[i].o0);
         T[i].o1 = mfma(v1, pb[i], T[i].o1);
         T[i].ls = mfma(ones, pb[i], T[i].ls);
@@ -400,9 +401,16 @@ attn_video_mfma_kernel(VideoArgs a, int units, int per_xcd)
 #pragma unroll
         for (int pp = 0; pp < TPW / 2; ++pp) {
             if (!__any(tval[2 * pp] || tval[2 * pp + 1])) continue;    // (SR = 24: tiles past the window)
+            // (SR = 24: a lone tile past the frame's last runs by itself)
+            if (SR != 24 || __any(tval[2 * pp + 1])) {
 #pragma unroll 1
-            for (int c = 0; c < NCH; ++c)
-                chunk<SIM, POS, SR>(kst, vst, slice, kinv, T + 2 * pp, c, lane, S, mask, fold, prec, exact);
+                for (int c = 0; c < NCH; ++c)
+                    chunk<SIM, POS, SR, 2>(kst, vst, slice, kinv, T + 2 * pp, c, lane, S, mask, fold, prec, exact);
+            } else {
+#pragma unroll 1
+                for (int c = 0; c < NCH; ++c)
+                    chunk<SIM, POS, SR, 1>(kst, vst, slice, kinv, T + 2 * pp, c, lane, S, mask, fold, prec, exact);
+            }
         }
     }
 

@@ -203,6 +203,7 @@ LSE_CASES = [
     (24, 24, 12, 6, "cyclic", "dot", "none"),
     (32, 48, 16, 8, "cyclic", "dot", "table"),         # whole-group exclusions, half-range chunk loops
     (48, 32, 16, 4, "cyclic", "cosine", "table"),      # column split inside a group: every pair masked
+    (32, 48, 16, 8, "cyclic", "cosine", "none"),       # half-range loops without a table (per-pair masks)
 ]
 
 

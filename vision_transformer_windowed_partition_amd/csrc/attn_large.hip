@@ -39,8 +39,11 @@
 // rotation the rotated operands are rounded; when that error, amplified by
 // 1/tau (COSINE, tau < 0.1) or by max||q|| max||k|| log2(e)/sqrt(d) > 20
 // (DOT), would pass the bf16 tolerance, q and k are carried as hi + lo bf16
-// pairs and every score takes four products; the keys are then staged in two
-// halves, once per tile pair.  The softmax uses a static shift (cos <= 1, or
+// pairs and every score takes three products (hi hi, lo hi, hi lo: lo lo is
+// below 2^-18 of |q||k|, the order of the remainders' own rounding); the
+// keys are then staged in two halves per tile pair, and consecutive pairs
+// take the halves in opposite order, so the half a pair ends with is the one
+// the next pair starts with and is staged once for both.  The softmax uses a static shift (cos <= 1, or
 // Cauchy-Schwarz for DOT) when the spread of a row's logits stays within
 // 2^60, else the running maximum per 32-key chunk.
 #include "common.hpp"
@@ -196,8 +199,6 @@ __device__ __forceinline__ void run_pair(const Block& bk, Tile (&T)[NT], const f
                     sb[i] = mfma(kb_lo, T[i].qf, sb[i]);
                     sa[i] = mfma(ka, T[i].qf_lo, sa[i]);
                     sb[i] = mfma(kb, T[i].qf_lo, sb[i]);
-                    sa[i] = mfma(ka_lo, T[i].qf_lo, sa[i]);
-                    sb[i] = mfma(kb_lo, T[i].qf_lo, sb[i]);
                 }
             }
             if (precise) {
@@ -513,7 +514,10 @@ attn_large_kernel(AttnParams p, LargeLayout L)
     } else if (SIM == SWIN_SIM_DOT) {
         kmax = 0.0f;                                      // (COSINE only reaches here)
     }
-    // split: keys in two halves with their remainders, staged per tile pair
+    // split: keys in two halves with their remainders, staged per tile pair;
+    // round r takes them in the order 0, 1 (r even) or 1, 0 (r odd), so its
+    // first half is still in LDS from round r - 1 (the online normaliser
+    // does not depend on the order of the keys)
     const int half_ch = (nch_all + 1) / 2;
     const int nblocks = split ? 2 : 1;
 
@@ -606,20 +610,23 @@ attn_large_kernel(AttnParams p, LargeLayout L)
         // whether the pair's second tile holds queries (wave-uniform)
         const bool two = NT == 2 && (wave + WAVES * (NT * r + 1)) * 16 < N;
 
-        for (int b = 0; b < nblocks; ++b) {
+        for (int bi = 0; bi < nblocks; ++bi) {
             Block bk = whole;
             if (split) {
-                // stage this half (every wave takes part), with remainders
+                const int b = (r & 1) ? 1 - bi : bi;
                 bk.nch = b == 0 ? half_ch : nch_all - half_ch;
                 bk.s0 = b * half_ch * 32;
                 bk.k = (const bf16x8*)kv;
                 bk.klo = (const bf16x8*)(kv + half_ch * 32 * 64);
                 bk.v = (const __bf16*)(kv + 2 * half_ch * 32 * 64);
-                __syncthreads();                          // the previous half is consumed
-                stage_issue(bk, (__bf16*)(kv + 2 * half_ch * 32 * 64));
-                stage_process(bk, (bf16x8*)kv, (bf16x8*)(kv + half_ch * 32 * 64), true);
-                vm_wait_all();
-                __syncthreads();
+                if (r == 0 || bi == 1) {
+                    // stage this half (every wave takes part), with remainders
+                    __syncthreads();                      // the previous half is consumed
+                    stage_issue(bk, (__bf16*)(kv + 2 * half_ch * 32 * 64));
+                    stage_process(bk, (bf16x8*)kv, (bf16x8*)(kv + half_ch * 32 * 64), true);
+                    vm_wait_all();
+                    __syncthreads();
+                }
             }
             if (!live) continue;
             // chunks of this block holding those key rows

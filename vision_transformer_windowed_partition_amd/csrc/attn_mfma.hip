@@ -254,13 +254,9 @@ __device__ __forceinline__ void run_general(const Stage& st, Tiles<NQ>& T, int s
                 sa = mfma(ka_lo, T.qf[qi], sa);
                 sb = mfma(kb_lo, T.qf[qi], sb);
             }
-            if (split_q) {
+            if (split_q) {                                // lo lo (< 2^-18 |q||k|) is left out
                 sa = mfma(ka, T.qf_lo[qi], sa);
                 sb = mfma(kb, T.qf_lo[qi], sb);
-                if (split_k) {
-                    sa = mfma(ka_lo, T.qf_lo[qi], sa);
-                    sb = mfma(kb_lo, T.qf_lo[qi], sb);
-                }
             }
             const float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
             float add[8];

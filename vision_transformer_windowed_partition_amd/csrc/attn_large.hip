@@ -41,9 +41,9 @@
 // (DOT), would pass the bf16 tolerance, q and k are carried as hi + lo bf16
 // pairs and every score takes three products (hi hi, lo hi, hi lo: lo lo is
 // below 2^-18 of |q||k|, the order of the remainders' own rounding); the
-// keys are then staged in two halves per tile pair, and consecutive pairs
-// take the halves in opposite order, so the half a pair ends with is the one
-// the next pair starts with and is staged once for both.  The softmax uses a static shift (cos <= 1, or
+// keys are then staged in two halves, each run by two tile pairs of every
+// wavefront, and consecutive cycles of two pairs take the halves in opposite
+// order, so the half a cycle ends with is staged once for the next as well.  The softmax uses a static shift (cos <= 1, or
 // Cauchy-Schwarz for DOT) when the spread of a row's logits stays within
 // 2^60, else the running maximum per 32-key chunk.
 #include "common.hpp"
@@ -514,19 +514,29 @@ attn_large_kernel(AttnParams p, LargeLayout L)
     } else if (SIM == SWIN_SIM_DOT) {
         kmax = 0.0f;                                      // (COSINE only reaches here)
     }
-    // split: keys in two halves with their remainders, staged per tile pair;
-    // round r takes them in the order 0, 1 (r even) or 1, 0 (r odd), so its
-    // first half is still in LDS from round r - 1 (the online normaliser
-    // does not depend on the order of the keys)
+    // split: keys in two halves with their remainders, staged per cycle of
+    // two tile pairs (below)
     const int half_ch = (nch_all + 1) / 2;
-    const int nblocks = split ? 2 : 1;
 
     // ---- this wavefront's query tiles, two at a time; the next pair's
     // queries load while the current pair runs
     const int qhalf = POS == SWIN_POS_ROPE2D ? 1 : 0;
     // groups split by a region edge or by padded columns need per-key masks
     const bool partial = (wp.last_c && ((M - g.shift) & 7)) || (M & 7);
-    for (int r = 0; r < L.rounds; ++r) {
+    // One pair's tile state: the queries' rows (rotated, normalised, rounded),
+    // scales, masks and accumulators; rlo_min / rhi_max: the key rows some
+    // query of the pair may see (wave-uniform).
+    struct Pair {
+        Tile T[NT];
+        int qt[NT];
+        bool qv[NT];
+        bool any_exact, live, two;
+        int rlo_min, rhi_max;
+    };
+    auto setup = [&](int r, Pair& P) {
+        Tile (&T)[NT] = P.T;
+        int (&qt)[NT] = P.qt;
+        bool (&qv)[NT] = P.qv;
         u32x4 qcur[NT];
         if (QKEEP) {
             // this round's rows are qraw[0..NT); the rest move down a pair
@@ -539,9 +549,6 @@ attn_large_kernel(AttnParams p, LargeLayout L)
             for (int i = 0; i < NT; ++i) qcur[i] = qnext[i];
             if (r + 1 < L.rounds) load_pair_q(r + 1, qnext);
         }
-        Tile T[NT];
-        int qt[NT];
-        bool qv[NT];
         bool any_exact = false;
         int rlo_min = M, rhi_max = 0;
 #pragma unroll
@@ -606,53 +613,43 @@ attn_large_kernel(AttnParams p, LargeLayout L)
         }
         rlo_min = __builtin_amdgcn_readfirstlane(rlo_min);
         rhi_max = __builtin_amdgcn_readfirstlane(rhi_max);
-        const bool live = rhi_max > rlo_min;              // some tile of the pair has queries
+        P.live = rhi_max > rlo_min;                       // some tile of the pair has queries
         // whether the pair's second tile holds queries (wave-uniform)
-        const bool two = NT == 2 && (wave + WAVES * (NT * r + 1)) * 16 < N;
+        P.two = NT == 2 && (wave + WAVES * (NT * r + 1)) * 16 < N;
+        P.any_exact = any_exact;
+        P.rlo_min = rlo_min;
+        P.rhi_max = rhi_max;
 
-        for (int bi = 0; bi < nblocks; ++bi) {
-            Block bk = whole;
-            if (split) {
-                const int b = (r & 1) ? 1 - bi : bi;
-                bk.nch = b == 0 ? half_ch : nch_all - half_ch;
-                bk.s0 = b * half_ch * 32;
-                bk.k = (const bf16x8*)kv;
-                bk.klo = (const bf16x8*)(kv + half_ch * 32 * 64);
-                bk.v = (const __bf16*)(kv + 2 * half_ch * 32 * 64);
-                if (r == 0 || bi == 1) {
-                    // stage this half (every wave takes part), with remainders
-                    __syncthreads();                      // the previous half is consumed
-                    stage_issue(bk, (__bf16*)(kv + 2 * half_ch * 32 * 64));
-                    stage_process(bk, (bf16x8*)kv, (bf16x8*)(kv + half_ch * 32 * 64), true);
-                    vm_wait_all();
-                    __syncthreads();
-                }
-            }
-            if (!live) continue;
-            // chunks of this block holding those key rows
-            const int s_lo = rlo_min * SR - bk.s0, s_hi = rhi_max * SR - bk.s0;
-            const int cb = max(0, s_lo) >> 5;
-            const int ce = min(bk.nch, (max(0, s_hi) + 31) >> 5);
-            if (cb >= ce) continue;
-            if (any_exact || precise || split)
-                run_pair<SIM, POS, true, true, NT>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, partial,
-                                                   precise, split);
-            else if (!two) {
-                // the wavefront's last tile is alone: run it by itself
-                if (needs_mask)
-                    run_pair<SIM, POS, true, false, 1>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, partial,
-                                                       false, false);
-                else
-                    run_pair<SIM, POS, false, false, 1>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, false,
-                                                        false, false);
-            } else if (needs_mask)
-                run_pair<SIM, POS, true, false, NT>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, partial, false,
-                                                    false);
+    };
+    // the pair against the chunks of block bk its queries can see
+    auto run = [&](Pair& P, const Block& bk) {
+        if (!P.live) return;
+        const int s_lo = P.rlo_min * SR - bk.s0, s_hi = P.rhi_max * SR - bk.s0;
+        const int cb = max(0, s_lo) >> 5;
+        const int ce = min(bk.nch, (max(0, s_hi) + 31) >> 5);
+        if (cb >= ce) return;
+        if (P.any_exact || precise || split)
+            run_pair<SIM, POS, true, true, NT>(bk, P.T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, partial,
+                                               precise, split);
+        else if (!P.two) {
+            // the wavefront's last tile is alone: run it by itself
+            if (needs_mask)
+                run_pair<SIM, POS, true, false, 1>(bk, P.T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, partial,
+                                                   false, false);
             else
-                run_pair<SIM, POS, false, false, NT>(bk, T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, false, false,
-                                                     false);
-        }
-
+                run_pair<SIM, POS, false, false, 1>(bk, P.T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, false,
+                                                    false, false);
+        } else if (needs_mask)
+            run_pair<SIM, POS, true, false, NT>(bk, P.T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, partial, false,
+                                                false);
+        else
+            run_pair<SIM, POS, false, false, NT>(bk, P.T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, false, false,
+                                                 false);
+    };
+    auto store = [&](Pair& P) {
+        Tile (&T)[NT] = P.T;
+        int (&qt)[NT] = P.qt;
+        bool (&qv)[NT] = P.qv;
         // ---- normalise and store: lane holds channels 4 grp..+3 and
         // 16 + 4 grp..+3 of query li
 #pragma unroll
@@ -668,6 +665,47 @@ attn_large_kernel(AttnParams p, LargeLayout L)
                 const float off2 = tab_shift - T[i].negm + (T[i].exact ? T[i].mrun : 0.0f);
                 p.lse[((size_t)win * g.heads + h) * N + qt[i]] = (__builtin_amdgcn_logf(T[i].ls[0]) + off2) * kLn2;
             }
+        }
+    };
+
+    if (!split) {
+        for (int r = 0; r < L.rounds; ++r) {
+            Pair P;
+            setup(r, P);
+            run(P, whole);
+            store(P);
+        }
+    } else {
+        // two pairs per staging cycle: cycle c runs pairs 2c and 2c + 1 over
+        // the halves in the order 0, 1 (c even) or 1, 0 (c odd), so its
+        // first half is still in LDS from cycle c - 1 (the online normaliser
+        // does not depend on the order of the keys)
+        for (int r = 0; r < L.rounds; r += 2) {
+            const bool second = r + 1 < L.rounds;
+            Pair P0, P1;
+            setup(r, P0);
+            if (second) setup(r + 1, P1);
+            for (int bi = 0; bi < 2; ++bi) {
+                const int b = ((r >> 1) & 1) ? 1 - bi : bi;
+                Block bk = whole;
+                bk.nch = b == 0 ? half_ch : nch_all - half_ch;
+                bk.s0 = b * half_ch * 32;
+                bk.k = (const bf16x8*)kv;
+                bk.klo = (const bf16x8*)(kv + half_ch * 32 * 64);
+                bk.v = (const __bf16*)(kv + 2 * half_ch * 32 * 64);
+                if (r == 0 || bi == 1) {
+                    // stage this half (every wave takes part), with remainders
+                    __syncthreads();                      // the previous half is consumed
+                    stage_issue(bk, (__bf16*)(kv + 2 * half_ch * 32 * 64));
+                    stage_process(bk, (bf16x8*)kv, (bf16x8*)(kv + half_ch * 32 * 64), true);
+                    vm_wait_all();
+                    __syncthreads();
+                }
+                run(P0, bk);
+                if (second) run(P1, bk);
+            }
+            store(P0);
+            if (second) store(P1);
         }
     }
 }

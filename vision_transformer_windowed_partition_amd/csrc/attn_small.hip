@@ -372,21 +372,7 @@ attn_small_kernel(AttnParams p, SmallLayout L)
             run_pair<SIM, POS, GPR, 0, NCH, true, true, true, 1>(kst, vst, T + 1, bias2, kinv, S, negrow, lane, true,
                                                                  precise);
         } else if (needs_mask) {
-            // chunks some lane of the pair may see: all, or one half of the key rows
-            uint32_t live = T[0].gmask | T[1].gmask;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) live |= (uint32_t)__shfl_xor((int)live, o);
-            live = (uint32_t)__builtin_amdgcn_readfirstlane((int)live);
-            constexpr uint32_t lo_half = (1u << (NCH / 2)) - 1u;
-            if ((live & ~lo_half) == 0u)
-                run_pair<SIM, POS, GPR, 0, NCH / 2, true, false, false, 2>(kst, vst, T, bias2, kinv, S, negrow, lane,
-                                                                        partial, false);
-            else if ((live & lo_half) == 0u)
-                run_pair<SIM, POS, GPR, NCH / 2, NCH, true, false, false, 2>(kst, vst, T, bias2, kinv, S, negrow, lane,
-                                                                          partial, false);
-            else
-                run_pair<SIM, POS, GPR, 0, NCH, true, false, false, 2>(kst, vst, T, bias2, kinv, S, negrow, lane,
-                                                                    partial, false);
+            run_masked_pair<SIM, POS, GPR, NCH>(kst, vst, T, bias2, kinv, S, negrow, lane, partial);
         } else
             run_pair<SIM, POS, GPR, 0, NCH, false, false, false, 2>(kst, vst, T, bias2, kinv, S, negrow, lane, false,
                                                                  false);

@@ -4,6 +4,8 @@
 // products on the matrix cores, the softmax in registers between them).
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "lanes.hpp"
 #include "tile_io.hpp"
@@ -170,6 +172,38 @@ __device__ __forceinline__ void run_pair(const bf16x8* kst, const __bf16* vst, T
             T[i].ls = mfma(ones, pb[i], T[i].ls);
         }
     }
+}
+
+// A pair of query tiles over a window with shift regions or padded slots:
+// only the chunks some lane of the pair may see (all, or one half of the key
+// rows), and a loop of its own for windows whose region edges fall on 8-slot
+// group boundaries (partial false), which then needs no per-key selects.
+// partial must be uniform over the wavefront.
+template <int SIM, int POS, int GPR, int NCH>
+__device__ __forceinline__ void run_masked_pair(const bf16x8* kst, const __bf16* vst, Tile* T, const float* bias2,
+                                                const float* kinv, int S, int negrow, int lane, bool partial)
+{
+    uint32_t live = T[0].gmask | T[1].gmask;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) live |= (uint32_t)__shfl_xor((int)live, o);
+    live = (uint32_t)__builtin_amdgcn_readfirstlane((int)live);
+    constexpr uint32_t lo_half = (1u << (NCH / 2)) - 1u;
+    auto go = [&](auto part) {
+        constexpr bool PART = decltype(part)::value;
+        if ((live & ~lo_half) == 0u)
+            run_pair<SIM, POS, GPR, 0, NCH / 2, true, false, false, 2>(kst, vst, T, bias2, kinv, S, negrow, lane,
+                                                                    PART, false);
+        else if ((live & lo_half) == 0u)
+            run_pair<SIM, POS, GPR, NCH / 2, NCH, true, false, false, 2>(kst, vst, T, bias2, kinv, S, negrow, lane,
+                                                                      PART, false);
+        else
+            run_pair<SIM, POS, GPR, 0, NCH, true, false, false, 2>(kst, vst, T, bias2, kinv, S, negrow, lane, PART,
+                                                                false);
+    };
+    if (__builtin_amdgcn_readfirstlane((int)partial))
+        go(std::integral_constant<bool, true>());
+    else
+        go(std::integral_constant<bool, false>());
 }
 
 }  // namespace core

@@ -523,6 +523,7 @@ attn_large_kernel(AttnParams p, LargeLayout L)
     const int qhalf = POS == SWIN_POS_ROPE2D ? 1 : 0;
     // groups split by a region edge or by padded columns need per-key masks
     const bool partial = (wp.last_c && ((M - g.shift) & 7)) || (M & 7);
+    const bool partial_s = __builtin_amdgcn_readfirstlane((int)partial) != 0;   // uniform
     // One pair's tile state: the queries' rows (rotated, normalised, rounded),
     // scales, masks and accumulators; rlo_min / rhi_max: the key rows some
     // query of the pair may see (wave-uniform).
@@ -633,14 +634,22 @@ attn_large_kernel(AttnParams p, LargeLayout L)
                                                precise, split);
         else if (!P.two) {
             // the wavefront's last tile is alone: run it by itself
-            if (needs_mask)
-                run_pair<SIM, POS, true, false, 1>(bk, P.T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, partial,
+            if (needs_mask && partial_s)
+                run_pair<SIM, POS, true, false, 1>(bk, P.T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, true,
+                                                   false, false);
+            else if (needs_mask)
+                run_pair<SIM, POS, true, false, 1>(bk, P.T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, false,
                                                    false, false);
             else
                 run_pair<SIM, POS, false, false, 1>(bk, P.T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, false,
                                                     false, false);
-        } else if (needs_mask)
-            run_pair<SIM, POS, true, false, NT>(bk, P.T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, partial, false,
+        } else if (needs_mask && partial_s)
+            run_pair<SIM, POS, true, false, NT>(bk, P.T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, true, false,
+                                                false);
+        else if (needs_mask)
+            // region edges on 8-slot group boundaries: a loop without
+            // per-key selects
+            run_pair<SIM, POS, true, false, NT>(bk, P.T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, false, false,
                                                 false);
         else
             run_pair<SIM, POS, false, false, NT>(bk, P.T, bias2, kinv, S, SR, L.inv_SR, cb, ce, lane, false, false,

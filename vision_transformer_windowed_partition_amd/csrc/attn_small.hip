@@ -55,6 +55,7 @@ struct SmallLayout {
     int NQT;                   // query tiles of 16 per window
     int wgs;                   // workgroups with work: heads * window blocks
     int P;                     // work ids per XCD slot
+    int hpair;                 // M <= 8, no table, even heads: a workgroup takes two windows of a head pair
     float inv_M;
 };
 
@@ -98,8 +99,17 @@ attn_small_kernel(AttnParams p, SmallLayout L)
     // 64-byte head slices share are fetched once.
     const int work = (blockIdx.x & 7) * L.P + (blockIdx.x >> 3);
     if (work >= L.wgs) return;                            // whole workgroup, before the barrier
-    const int h = work % g.heads;
-    const int wloc = (work / g.heads) * WH + wh;
+    int h, wloc;
+    if (WH > 1 && L.hpair) {
+        // two windows x heads 2j, 2j + 1: the wavefronts reading the two
+        // 64-byte halves of each 128-byte line run together on one CU
+        const int hp = g.heads >> 1;
+        h = 2 * (work % hp) + (wh & 1);
+        wloc = (work / hp) * 2 + (wh >> 1);
+    } else {
+        h = work % g.heads;
+        wloc = (work / g.heads) * WH + wh;
+    }
     const bool active = wloc < g.nwin;
     const int win = active ? wloc : 0;
     const float tau_eff = SIM == SWIN_SIM_COSINE ? fmaxf(p.tau[h], p.tau_min) : 1.0f;
@@ -446,7 +456,10 @@ hipError_t launch_attn_small(const AttnParams& p, hipStream_t stream)
     const int nch = nch_real <= 2 ? 2 : nch_real <= 6 ? 6 : 8;      // M <= 8, 9-12, 13-16
     const int wh = nch <= 2 ? WAVES : 1;                            // windows per workgroup
     const int S = 2 * g.M - 1;
-    const int64_t wgs = (int64_t)g.heads * ((g.nwin + wh - 1) / wh);
+    // M <= 8 without a table (whose LDS copy is one head's): head pairs
+    L.hpair = wh > 1 && p.pos != SWIN_POS_TABLE && g.heads % 2 == 0 ? 1 : 0;
+    const int64_t wgs = L.hpair ? (int64_t)(g.heads / 2) * ((g.nwin + 1) / 2)
+                                : (int64_t)g.heads * ((g.nwin + wh - 1) / wh);
     if (wgs > INT32_MAX - 8) return hipErrorInvalidValue;
     L.wgs = (int)wgs;
     L.P = (int)((wgs + 7) / 8);

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from tests.gpu_helpers import (compare, f64, gpu_inputs, gpu_table, run_gpu, run_oracle,
                                sample_windows, window_token_mask)
 from vision_transformer_windowed_partition_amd import binding, synth
@@ -164,3 +165,57 @@ def test_empty_batch_writes_nothing():
                                        tau=torch.ones(2, device="cuda:0"))
     torch.cuda.synchronize()
     assert out.shape == q.shape
+
+
+# Windows of up to 8 x 8 without a table and with an even head count run as
+# workgroups of two windows x a head pair: odd window counts (the last
+# workgroup's second window inactive), two heads (one pair), padded rows
+# (M = 6, 7), shifts, interleaving, dot and cosine.
+HEAD_PAIRS = [
+    # (B, H, W, M, shift, partition, sim, heads)
+    (1, 24, 40, 8, 4, "cyclic", "dot", 2),           # 15 windows
+    (1, 21, 35, 7, 3, "cyclic", "cosine", 4),        # 15 windows, 7 -> 8 slots per key row
+    (3, 16, 24, 8, 0, "interleaved", "cosine", 6),   # 18 windows over 3 images
+    (1, 18, 30, 6, 2, "cyclic", "dot", 4),           # 15 windows, 36 of 48 slots
+    (1, 8, 8, 8, 0, "cyclic", "dot", 2),             # one window
+]
+
+
+@pytest.mark.parametrize("case", HEAD_PAIRS, ids=[f"B{c[0]}-{c[1]}x{c[2]}-M{c[3]}-s{c[4]}-{c[5][:3]}-{c[6]}-h{c[7]}"
+                                                  for c in HEAD_PAIRS])
+def test_head_pair_workgroups(case):
+    B, H, W, M, s, part, sim, heads = case
+    wl = synth.small(B=B, H=H, W=W, C=32 * heads, heads=heads, M=M, shift=s, partition=part, sim=sim, pos="none",
+                     dtype="bf16", hidden=64)
+    x = synth.make_inputs(wl, seed=11)
+    g = gpu_inputs(x)
+    kw = dict(heads=heads, M=M, shift=s, partition=part, sim=sim, pos="none", tau=g["tau"])
+    desc = binding.make_desc(B=B, H=H, W=W, C=wl.C, heads=heads, M=M, shift=s, partition=part, sim=sim,
+                             pos="none", dtype=g["q"].dtype)
+    assert binding.swin_window_attn_kernel(desc) == "attn_small_kernel"
+    out, lse = binding.swin_window_attn_fwd_lse(g["q"], g["k"], g["v"], **kw)
+    plain = binding.swin_window_attn_fwd(g["q"], g["k"], g["v"], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain)
+    ref, ref_lse = oracle.window_attn(f64(x["q"]), f64(x["k"]), f64(x["v"]), heads=heads, M=M, shift=s,
+                                      partition=part, sim=sim, pos="none", tau=f64(x["tau"]), return_lse=True)
+    compare(wl, f64(out), ref, what=str(case))
+    # log-sum-exp: the bf16 bar of the exported statistic (logit error from
+    # the rounded operands, 2^-8 of the logit scale's bound, plus fp32 sums)
+    d = 32
+    if sim == "cosine":
+        scale = (1.0 / np.maximum(f64(x["tau"]), 0.01))[None, :, None]
+    else:
+        qn = np.linalg.norm(f64(x["q"]).reshape(B, H, W, heads, d), axis=-1)
+        kn = np.linalg.norm(f64(x["k"]).reshape(B, H, W, heads, d), axis=-1)
+        qw = oracle.partition(qn, M, s, part).transpose(0, 2, 1)
+        kwin = oracle.partition(kn, M, s, part).transpose(0, 2, 1)
+        scale = qw * kwin.max(axis=2, keepdims=True) / np.sqrt(d)
+    err = np.abs(f64(lse) - ref_lse)
+    assert np.all(err <= 2.0 ** -8 * scale + 2.0 ** -8 + 1e-5 * np.abs(ref_lse)), float(err.max())
+    # pre-partitioned windows give the grid layout's result bit for bit
+    parts = {n: binding.swin_window_partition(g[n], M, s, part) for n in "qkv"}
+    wout = binding.swin_window_attn_fwd(parts["q"], parts["k"], parts["v"], layout="windows", grid=(B, H, W), **kw)
+    back = binding.swin_window_reverse(wout, B, H, W, M, s, part)
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16), out.view(torch.int16))

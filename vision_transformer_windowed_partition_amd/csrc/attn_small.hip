@@ -6,7 +6,10 @@
 // interleaved windows; rotary positions go to the large-window kernel),
 // organised for small windows.  A workgroup of four wavefronts serves one
 // head: for 9 <= M <= 16 all four share one window (each takes every fourth
-// query tile), for M <= 8 each takes a window of its own.  The wavefronts of
+// query tile), for M <= 8 each takes a window of its own (without a table
+// and with an even head count, two windows of a head pair instead, so the
+// two 64-byte halves of each 128-byte line are read together on one CU).
+// The wavefronts of
 // a window stage it together and then meet at the workgroup's only barrier:
 //   K^ (keys x d): A operand of S^T = K Q^T (v_mfma_f32_16x16x32_bf16); each
 //      lane loads 16 contiguous bytes of one key, the four lanes of a key
@@ -92,7 +95,7 @@ attn_small_kernel(AttnParams p, SmallLayout L)
     bf16x8* kst = (bf16x8*)(red + 16 + WH * NCH * 32) + wh * (NCH * 2 * 64);       // [NCH][2][64]
     __bf16* vst = (__bf16*)((bf16x8*)(red + 16 + WH * NCH * 32) + WH * NCH * 2 * 64) + wh * (NCH * 32 * D);
 
-    // ---- item: one head per workgroup, window block-major.  Work ids run
+    // ---- item: one head (or head pair) per workgroup, window block-major.  Work ids run
     // window-block-major, head-minor, and each XCD takes a contiguous range
     // of them (consecutive blockIdx land on different XCDs): the heads of a
     // window run back to back on one XCD, so the 128-byte lines their
